@@ -1,0 +1,217 @@
+/*
+ * fmoe.h -- C ABI of libfmoe: the quantized Mixture-of-Experts expert forward at
+ * decode time, for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes comes from the Flash-MoE pages:
+ *  [P1] "397B MoE en MacBook: Motor Flash-MoE a 4,4 t/s" (aibit.im)
+ *  [P2] "Flash-MoE: Ausfuehren eines 397B-Parameter-Qwen-Modells auf dem MacBook
+ *       Pro mit reinem C/Metal" (openclawradar.com)
+ * Per layer it takes the hidden state, picks K of the layer's experts by softmax
+ * top-K ([P2] "Pipeline-Leistung"; 512 experts, K=4 plus one shared expert in
+ * [P2] "Technische Implementierung"), runs each chosen expert's SwiGLU
+ * feed-forward on 4-bit or 2-bit group-affine quantized weights
+ * (weight = code*scale + bias, evaluated as fma(code, scale*x, bias*x):
+ * [P1] "2. Kernel de desquantizacion optimizado con FMA", [P2]
+ * "FMA-optimierter Dequant-Kernel"), and combines the outputs with their routing
+ * weights, the sigmoid-gated shared expert and the residual ([P2]
+ * "Metal-Compute-Shader": fused MoE combination + residual + sigmoid gate).
+ *
+ * ---------------------------------------------------------------- conventions
+ * Pointers. Every array argument of an entry point that enqueues GPU work is a
+ * DEVICE pointer (HBM, e.g. hipMalloc or a torch tensor's data_ptr()); the pack
+ * and unpack helpers without "_device" in their name take HOST pointers. fp32
+ * arrays are row-major and contiguous and must be 16-byte aligned; quantized
+ * blobs and workspaces must be 256-byte aligned.
+ *
+ * Ownership. The caller allocates and frees everything: blobs, activations and
+ * workspaces. The library keeps no device state and never allocates or frees
+ * device memory. Blobs are read-only during a call.
+ *
+ * Asynchrony. A device entry point validates its arguments on the host, enqueues
+ * its kernels on `stream` (a hipStream_t; NULL means the null stream) and
+ * returns. It never synchronises, so it can be captured in a HIP graph. Results
+ * are valid once the caller has synchronised the stream; a device fault surfaces
+ * there, not as a status.
+ *
+ * Errors. Validation is synchronous and complete before the first launch: on
+ * any status other than FMOE_OK nothing was enqueued and no output was written.
+ * FMOE_ERR_LAUNCH reports a launch the HIP runtime refused (earlier kernels of
+ * the same call may have been enqueued). No C++ exception crosses this ABI.
+ *
+ * Determinism. Identical inputs give bitwise identical outputs and routing:
+ * every reduction runs in a fixed order and no floating-point atomics are used.
+ *
+ * Re-entrancy. Calls are re-entrant; calls that may run concurrently need
+ * distinct workspaces and outputs.
+ *
+ * Supported set. bits in {4, 2}; group == 64; every quantized matrix has cols
+ * in {256, 512, 1024, 2048, 4096} (so hidden and inter are in that set) and
+ * rows >= 1; 1 <= top_k <= FMOE_MAX_TOPK; 1 <= n_experts <= FMOE_MAX_EXPERTS;
+ * 1 <= n_tokens <= FMOE_MAX_TOKENS. The tuned shape is hidden 4096, inter 1024,
+ * 512 experts, top_k 4.
+ *
+ * ---------------------------------------------------------------- blob layout
+ * A quantized matrix W [rows][cols] is stored as `rows` row records. A row
+ * record holds cols/64 groups of 64 codes and, after the codes, one 32-bit
+ * word per group: (bf16 scale << 16) | bf16 bias.
+ *   4-bit: record = [first halves of all groups: 16 B each]
+ *                   [second halves of all groups: 16 B each][scale/bias words]
+ *          (36 bytes per group). In the 16-byte half h of group g, byte k of
+ *          32-bit word w holds column 64g+32h+8w+k in its low nibble and column
+ *          64g+32h+8w+4+k in its high nibble.
+ *   2-bit: record = [groups: 16 B each][scale/bias words] (20 bytes per group).
+ *          Byte k of word w of group g holds column 64g+16w+4q+k in bits 2q..2q+1.
+ * An expert blob is [gate row 0][up row 0][gate row 1][up row 1]...
+ * [gate row inter-1][up row inter-1] (records over hidden columns) followed by
+ * the `hidden` row records of down (records over inter columns). A bank of
+ * experts is n_experts expert blobs at a stride of fmoe_expert_bytes().
+ * Use the pack functions; the layout may change between library versions.
+ */
+#ifndef FMOE_H_
+#define FMOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FMOE_GROUP 64
+#define FMOE_MAX_TOPK 8
+#define FMOE_MAX_TOKENS 64
+#define FMOE_MAX_EXPERTS 1024
+
+typedef enum fmoe_status {
+  FMOE_OK = 0,
+  FMOE_ERR_NULL = 1,      /* a required pointer is NULL                                   */
+  FMOE_ERR_SHAPE = 2,     /* rows/cols/hidden/inter/group unsupported or inconsistent     */
+  FMOE_ERR_ALIGN = 3,     /* fp32 array not 16-B aligned, or blob not 256-B aligned       */
+  FMOE_ERR_BITS = 4,      /* bits not 4 (q4 entry), not 2 (q2 entry), not in {2,4} else  */
+  FMOE_ERR_ROUTING = 5,   /* top_k < 1, top_k > n_experts, top_k > FMOE_MAX_TOPK,
+                             or n_experts outside [1, FMOE_MAX_EXPERTS]                    */
+  FMOE_ERR_BATCH = 6,     /* n_tokens < 1 or n_tokens > FMOE_MAX_TOKENS, or n_layers < 1  */
+  FMOE_ERR_WORKSPACE = 7, /* workspace NULL or smaller than the matching *_bytes() query  */
+  FMOE_ERR_LAUNCH = 8,    /* the HIP runtime refused a kernel launch                      */
+  FMOE_ERR_ALIAS = 9      /* an input aliases an output or the workspace it must not      */
+} fmoe_status;
+
+/* One packed quantized matrix (see "blob layout"). */
+typedef struct fmoe_qmat {
+  const void *blob; /* device, 256-B aligned, fmoe_qmat_bytes(bits, rows, cols, group) bytes */
+  int32_t rows, cols, bits, group;
+} fmoe_qmat;
+
+/* One packed SwiGLU expert: gate and up [inter][hidden], down [hidden][inter]. */
+typedef struct fmoe_expert {
+  const void *blob; /* device, 256-B aligned, fmoe_expert_bytes(bits, hidden, inter, group) */
+  int32_t hidden, inter, bits, group;
+} fmoe_expert;
+
+/* One MoE layer. */
+typedef struct fmoe_layer {
+  const float *router;      /* device fp32 [n_experts][hidden], row-major                   */
+  const float *shared_gate; /* device fp32 [hidden]; the shared expert's gate is
+                               sigmoid(shared_gate . x). Ignored when shared == NULL.      */
+  const void *bank;         /* device: n_experts expert blobs, stride fmoe_expert_bytes()   */
+  const void *shared;       /* device: one expert blob, or NULL for a layer without a
+                               shared expert                                               */
+  int32_t n_experts, top_k, hidden, inter, bits, group;
+} fmoe_layer;
+
+/* ------------------------------------------------------------------ sizes */
+
+/* Bytes of one packed matrix; 0 if the arguments are outside the supported set. */
+size_t fmoe_qmat_bytes(int bits, int rows, int cols, int group);
+/* Bytes of one packed expert (4, 4096, 1024, 64 -> 7,077,888 = 6.75 MiB); 0 if unsupported. */
+size_t fmoe_expert_bytes(int bits, int hidden, int inter, int group);
+/* Workspace of fmoe_expert_ffn for one token; 0 if unsupported. */
+size_t fmoe_expert_workspace_bytes(const fmoe_expert *E);
+/* Workspace of fmoe_moe_layer for n_tokens tokens; 0 if unsupported. */
+size_t fmoe_workspace_bytes(const fmoe_layer *L, int n_tokens);
+/* Workspace of fmoe_moe_stack for n_tokens tokens (every layer shaped like L); 0 if unsupported. */
+size_t fmoe_stack_workspace_bytes(const fmoe_layer *L, int n_tokens);
+
+/* ------------------------------------------------------------------ packing
+ * Canonical input (host or device, as named): codes uint8 [rows][cols], one
+ * unsigned code in [0, 2^bits) per element (higher bits must be zero, else
+ * FMOE_ERR_SHAPE from the host packers; the device packers mask them off);
+ * scale and bias uint16 [rows][cols/group], bf16 bit patterns. blob_out
+ * receives fmoe_qmat_bytes() bytes. */
+fmoe_status fmoe_pack_qmat(int bits, int rows, int cols, int group, const uint8_t *codes,
+                           const uint16_t *scale, const uint16_t *bias, void *blob_out);
+fmoe_status fmoe_unpack_qmat(int bits, int rows, int cols, int group, const void *blob,
+                             uint8_t *codes, uint16_t *scale, uint16_t *bias);
+/* codes/scale/bias[0..2] = gate [inter][hidden], up [inter][hidden], down [hidden][inter]. */
+fmoe_status fmoe_pack_expert(int bits, int hidden, int inter, int group, const uint8_t *const codes[3],
+                             const uint16_t *const scale[3], const uint16_t *const bias[3],
+                             void *blob_out);
+fmoe_status fmoe_unpack_expert(int bits, int hidden, int inter, int group, const void *blob,
+                               uint8_t *const codes[3], uint16_t *const scale[3],
+                               uint16_t *const bias[3]);
+/* Device twins: all pointers are device pointers; work is enqueued on `stream`. */
+fmoe_status fmoe_pack_qmat_device(int bits, int rows, int cols, int group, const uint8_t *codes,
+                                  const uint16_t *scale, const uint16_t *bias, void *blob_out,
+                                  void *stream);
+fmoe_status fmoe_pack_expert_device(int bits, int hidden, int inter, int group,
+                                    const uint8_t *const codes[3], const uint16_t *const scale[3],
+                                    const uint16_t *const bias[3], void *blob_out, void *stream);
+
+/* ------------------------------------------------------------------ compute */
+
+/* y[r] = sum_c (code[r][c]*scale[r][c/64] + bias[r][c/64]) * x[c] for a 4-bit matrix
+ * ([P2] "FMA-optimierter Dequant-Kernel"; [P2] "Metal-Compute-Shader": 4-bit dequantized
+ * matrix-vector multiplication). x: device fp32 [cols]; y: device fp32 [rows], must not
+ * overlap x. FMOE_ERR_BITS unless W->bits == 4. */
+fmoe_status fmoe_q4_matvec(const fmoe_qmat *W, const float *x, float *y, void *stream);
+/* The same for a 2-bit matrix ([P2] "Metal-Compute-Shader": 2-bit dequantized matvec).
+ * FMOE_ERR_BITS unless W->bits == 2. */
+fmoe_status fmoe_q2_matvec(const fmoe_qmat *W, const float *x, float *y, void *stream);
+
+/* One SwiGLU expert on one token: out = down( silu(gate x) * (up x) ), silu(z) = z/(1+e^-z)
+ * ([P2] "Metal-Compute-Shader": fused SwiGLU activation). x: device fp32 [hidden];
+ * out: device fp32 [hidden], must not overlap x; ws: device, >= fmoe_expert_workspace_bytes. */
+fmoe_status fmoe_expert_ffn(const fmoe_expert *E, const float *x, float *out, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/* One MoE layer for n_tokens independent tokens t:
+ *   logits = router x_t; p = softmax(logits); T = the top_k experts by p (descending,
+ *   lower index first on a tie); w_j = p[T_j] / sum_{i in T} p[i];
+ *   out_t = residual_t + sum_j w_j E_{T_j}(x_t) + sigmoid(shared_gate . x_t) E_shared(x_t)
+ * ([P2] "Pipeline-Leistung", "Technische Implementierung", "Metal-Compute-Shader").
+ * x, residual, out: device fp32 [n_tokens][hidden]; out may equal residual (in-place
+ * residual update) but must not overlap x or ws. topk_idx (int32) and topk_w (fp32):
+ * device [n_tokens][top_k] or NULL. ws: device, >= fmoe_workspace_bytes(L, n_tokens). */
+fmoe_status fmoe_moe_layer(const fmoe_layer *L, int n_tokens, const float *x, const float *residual,
+                           float *out, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+                           void *stream);
+
+/* RMS scaling without a learned weight, two stages (sum of squares, then apply)
+ * ([P2] "Metal-Compute-Shader": RMS normalization, two-stage):
+ *   x_t = h_t / sqrt(sum_i h_t[i]^2 / hidden + eps). h, x: device fp32 [n_tokens][hidden];
+ * x may equal h. */
+fmoe_status fmoe_rms_scale(const float *h, float *x, int n_tokens, int hidden, float eps, void *stream);
+
+/* A stack of MoE layers with RMS scaling between them, all enqueued without a host
+ * synchronisation ([P2] "Verzoegerte GPU-Experten-Berechnung": the expert forward,
+ * combine and norm run on the GPU and feed the next layer directly):
+ *   h_0 = h0;  for l: x_l = rms_scale(h_l, eps); h_{l+1} = moe_layer(layers[l], x_l, residual = h_l)
+ * h0, h_out: device fp32 [n_tokens][hidden] (h_out may equal h0). h_all: device fp32
+ * [n_layers][n_tokens][hidden] receiving every h_{l+1}, or NULL. topk_idx / topk_w: device
+ * [n_layers][n_tokens][top_k], or NULL. Every layer must share hidden, inter, bits, group,
+ * top_k and n_experts with layers[0]. ws >= fmoe_stack_workspace_bytes(&layers[0], n_tokens). */
+fmoe_status fmoe_moe_stack(const fmoe_layer *layers, int n_layers, int n_tokens, const float *h0,
+                           float *h_out, float *h_all, int32_t *topk_idx, float *topk_w, float eps,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/* Human-readable text of a status (static storage). */
+const char *fmoe_status_string(fmoe_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int fmoe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FMOE_H_ */

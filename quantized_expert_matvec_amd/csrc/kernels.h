@@ -1,0 +1,54 @@
+// kernels.h -- host-side launchers of the HIP kernels (kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fmoe {
+
+// y[r] = sum_c W[r][c] x[c] for a packed matrix (row records at blob + r * row_bytes).
+hipError_t launch_qmatvec(int bits, const uint8_t *blob, int rows, int cols, const float *x, float *y,
+                          hipStream_t s);
+
+// h[r] = silu(gate_r . x) * (up_r . x) for one expert's interleaved gate/up region.
+hipError_t launch_expert_gateup(int bits, const uint8_t *gateup, int hidden, int inter, const float *x,
+                                float *h, hipStream_t s);
+
+// Everything one MoE layer needs for one token.
+struct LayerArgs {
+  const float *router;       // [E][H]
+  const float *shared_gate;  // [H] or null (no shared expert)
+  const uint8_t *bank;       // E expert blobs
+  const uint8_t *shared;     // one expert blob or null
+  int E, K, H, I, bits;
+  size_t expert_stride;      // bytes per expert blob
+  size_t gateup_bytes;       // offset of the down region inside an expert blob
+  const float *x;            // [H]
+  const float *residual;     // [H]
+  float *out;                // [H]
+  int32_t *topk_idx_out;     // [K] or null
+  float *topk_w_out;         // [K] or null
+  // workspace (device)
+  float *logits;             // [E]
+  float *sigma;              // [1]
+  int32_t *ws_idx;           // [K]
+  float *ws_w;               // [K]
+  float *h_shared;           // [I]
+  float *h_routed;           // [K][I]
+  float *d_shared;           // [H]
+};
+
+// Router + sigmoid gate + shared gate/up; routing + routed gate/up + shared down;
+// down + weighted combine + residual. Three launches, no host synchronisation.
+hipError_t launch_layer(const LayerArgs &a, hipStream_t s);
+
+// x_t = h_t / sqrt(mean(h_t^2) + eps) for B tokens of width H.
+hipError_t launch_rms(const float *h, float *x, int B, int H, float eps, hipStream_t s);
+
+// Device packer: record r of the matrix goes to blob + rec_offset + r * rec_stride.
+hipError_t launch_pack_matrix(int bits, int rows, int cols, const uint8_t *codes, const uint16_t *scale,
+                              const uint16_t *bias, uint8_t *blob, size_t rec_stride, size_t rec_offset,
+                              hipStream_t s);
+
+}  // namespace fmoe

@@ -1,0 +1,104 @@
+// layout.h -- sizes and offsets of the library's packed weight layout and of
+// its workspaces (host-side arithmetic shared by the packers and the launchers).
+//
+// A quantized matrix is a sequence of row records. A record holds cols/64
+// groups of 64 codes followed by one 32-bit word per group,
+// (bf16 scale << 16) | bf16 bias:
+//   4-bit: [group halves 0: 16 B each][group halves 1: 16 B each][words]  (36 B/group)
+//   2-bit: [groups: 16 B each][words]                                    (20 B/group)
+// so that the 64 lanes of a wavefront, one group each, read every 16-byte
+// piece of a row with one contiguous 128-bit load per lane.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fmoe {
+
+constexpr int kGroup = 64;
+constexpr int kWave = 64;
+constexpr int kBlock = 256;  // threads per block everywhere: 4 wavefronts
+constexpr int kMaxTopK = 8;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTokens = 64;
+
+inline bool bits_ok(int bits) { return bits == 2 || bits == 4; }
+inline bool cols_ok(int cols) {
+  return cols == 256 || cols == 512 || cols == 1024 || cols == 2048 || cols == 4096;
+}
+inline int ilog2(int v) {
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return l;
+}
+
+// bytes of one group inside a row record: its codes plus its scale/bias word
+inline size_t group_bytes(int bits) { return bits == 4 ? 36 : 20; }
+inline size_t code_bytes(int bits) { return bits == 4 ? 32 : 16; }
+inline size_t row_bytes(int bits, int cols) { return (size_t)(cols / kGroup) * group_bytes(bits); }
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline size_t qmat_bytes(int bits, int rows, int cols) {
+  return round_up((size_t)rows * row_bytes(bits, cols), 256);
+}
+// gate/up region of an expert: 2*inter interleaved records over hidden columns
+inline size_t gateup_bytes(int bits, int hidden, int inter) {
+  return round_up((size_t)2 * inter * row_bytes(bits, hidden), 256);
+}
+inline size_t down_bytes(int bits, int hidden, int inter) {
+  return round_up((size_t)hidden * row_bytes(bits, inter), 256);
+}
+inline size_t expert_bytes(int bits, int hidden, int inter) {
+  return gateup_bytes(bits, hidden, inter) + down_bytes(bits, hidden, inter);
+}
+
+// Workspace of one MoE layer for B tokens (all offsets 256-B aligned).
+struct LayerWs {
+  size_t logits;    // fp32 [B][E]
+  size_t sigma;     // fp32 [B]
+  size_t topk_idx;  // int32 [B][K]
+  size_t topk_w;    // fp32 [B][K]
+  size_t h_shared;  // fp32 [B][inter]
+  size_t h_routed;  // fp32 [B][K][inter]
+  size_t d_shared;  // fp32 [B][hidden]  sigma * shared-expert output
+  size_t total;
+};
+
+inline LayerWs layer_ws(int B, int E, int K, int hidden, int inter) {
+  LayerWs w{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = round_up(o + bytes, 256);
+    return at;
+  };
+  w.logits = take(sizeof(float) * (size_t)B * E);
+  w.sigma = take(sizeof(float) * (size_t)B);
+  w.topk_idx = take(sizeof(int32_t) * (size_t)B * K);
+  w.topk_w = take(sizeof(float) * (size_t)B * K);
+  w.h_shared = take(sizeof(float) * (size_t)B * inter);
+  w.h_routed = take(sizeof(float) * (size_t)B * K * inter);
+  w.d_shared = take(sizeof(float) * (size_t)B * hidden);
+  w.total = o;
+  return w;
+}
+
+// Workspace of a layer stack: x [B][H], two h buffers [B][H], then one layer workspace.
+struct StackWs {
+  size_t x, ha, hb, layer, total;
+  LayerWs lw;
+};
+
+inline StackWs stack_ws(int B, int E, int K, int hidden, int inter) {
+  StackWs s{};
+  size_t hb = round_up(sizeof(float) * (size_t)B * hidden, 256);
+  s.x = 0;
+  s.ha = hb;
+  s.hb = 2 * hb;
+  s.layer = 3 * hb;
+  s.lw = layer_ws(B, E, K, hidden, inter);
+  s.total = s.layer + s.lw.total;
+  return s;
+}
+
+}  // namespace fmoe
