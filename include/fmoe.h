@@ -186,6 +186,17 @@ fmoe_status fmoe_moe_layer(const fmoe_layer *L, int n_tokens, const float *x, co
                            float *out, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
                            void *stream);
 
+/* Diagnostic form of fmoe_moe_layer for per-kernel timing: enqueues only some of
+ * the layer's three kernels, in order -- bit 0: router, shared-expert gate and
+ * gate/up; bit 1: routing + routed gate/up + shared-expert down; bit 2: routed
+ * down + combine. phases == 7 is fmoe_moe_layer. A kernel reads what the
+ * previous ones left in ws, so partial calls are meaningful only after a full
+ * call with the same ws and inputs. FMOE_ERR_BATCH if phases is outside 1..7;
+ * otherwise the arguments and errors of fmoe_moe_layer. */
+fmoe_status fmoe_moe_layer_phases(const fmoe_layer *L, int n_tokens, const float *x, const float *residual,
+                                  float *out, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+                                  int phases, void *stream);
+
 /* RMS scaling without a learned weight, two stages (sum of squares, then apply)
  * ([P2] "Metal-Compute-Shader": RMS normalization, two-stage):
  *   x_t = h_t / sqrt(sum_i h_t[i]^2 / hidden + eps). h, x: device fp32 [n_tokens][hidden];

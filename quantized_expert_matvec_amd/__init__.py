@@ -78,6 +78,8 @@ _SIGS = {
                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "fmoe_moe_layer": (ctypes.c_int, [ctypes.POINTER(fmoe_layer), ctypes.c_int] + [ctypes.c_void_p] * 6 +
                        [ctypes.c_size_t, ctypes.c_void_p]),
+    "fmoe_moe_layer_phases": (ctypes.c_int, [ctypes.POINTER(fmoe_layer), ctypes.c_int] + [ctypes.c_void_p] * 6 +
+                              [ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]),
     "fmoe_rms_scale": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_float, ctypes.c_void_p]),
     "fmoe_moe_stack": (ctypes.c_int, [ctypes.POINTER(fmoe_layer), ctypes.c_int, ctypes.c_int] +
@@ -330,6 +332,17 @@ def fmoe_moe_layer(L: Layer, x: torch.Tensor, residual: torch.Tensor, out: Optio
     _ok(lib().fmoe_moe_layer(ctypes.byref(L.c()), n_tokens, _ptr(x), _ptr(residual), _ptr(out), _ptr(topk_idx),
                              _ptr(topk_w), _ptr(ws), nbytes, _stream(stream)), "fmoe_moe_layer")
     return out
+
+
+def fmoe_moe_layer_phases(L: Layer, x: torch.Tensor, residual: torch.Tensor, out: torch.Tensor, phases: int,
+                          ws, topk_idx: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None,
+                          stream=None, c_layer=None) -> None:
+    """Enqueue only some of the layer's three kernels (bit mask `phases`); for per-kernel timing."""
+    n_tokens = x.shape[0] if x.dim() == 2 else 1
+    cl = c_layer if c_layer is not None else L.c()
+    nbytes = ws.numel() * ws.element_size()
+    _ok(lib().fmoe_moe_layer_phases(ctypes.byref(cl), n_tokens, _ptr(x), _ptr(residual), _ptr(out), _ptr(topk_idx),
+                                    _ptr(topk_w), _ptr(ws), nbytes, phases, _stream(stream)), "fmoe_moe_layer_phases")
 
 
 def fmoe_rms_scale(h: torch.Tensor, x: Optional[torch.Tensor] = None, eps: float = 1e-6,

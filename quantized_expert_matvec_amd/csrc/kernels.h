@@ -25,6 +25,7 @@ struct LayerArgs {
   size_t expert_stride;      // bytes per expert blob
   size_t gateup_bytes;       // offset of the down region inside an expert blob
   const float *x;            // [H]
+  float rms_eps;             // >= 0: the layer input is rms_scale(x, rms_eps); < 0: x as given
   const float *residual;     // [H]
   float *out;                // [H]
   int32_t *topk_idx_out;     // [K] or null
@@ -37,11 +38,23 @@ struct LayerArgs {
   float *h_shared;           // [I]
   float *h_routed;           // [K][I]
   float *d_shared;           // [H]
+  // next layer of a stack (null when there is none): its router rows, gate
+  // vector and shared expert gate/up are prefetched into L2 while this layer ends
+  const float *next_router;
+  const float *next_gvec;
+  const uint8_t *next_shared;
+  // optional per-workgroup timestamps (device, 100 MHz clock) for profiling:
+  // [phase][workgroup][8]; null in normal use
+  uint64_t *trace;
+  // L2 prefetches to issue: bit 0 shared-expert down (phase 1), bit 1 routed
+  // down (phase 2), bit 2 the next layer's phase-1 weights (phase 3)
+  int prefetch_mask;
 };
 
 // Router + sigmoid gate + shared gate/up; routing + routed gate/up + shared down;
 // down + weighted combine + residual. Three launches, no host synchronisation.
-hipError_t launch_layer(const LayerArgs &a, hipStream_t s);
+// phases: bit p set = enqueue kernel p+1 (7 = the whole layer).
+hipError_t launch_layer(const LayerArgs &a, hipStream_t s, int phases = 7);
 
 // x_t = h_t / sqrt(mean(h_t^2) + eps) for B tokens of width H.
 hipError_t launch_rms(const float *h, float *x, int B, int H, float eps, hipStream_t s);

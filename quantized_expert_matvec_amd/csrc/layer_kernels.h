@@ -1,0 +1,1059 @@
+// layer_kernels.h -- templated HIP kernels of the MoE layer (one token) and their
+// host-side dispatch. Included by one translation unit per bit width
+// (kernels_q4.hip, kernels_q2.hip), which instantiate the *_b<BITS> entries.
+//
+// A layer is three launches:
+//   phase 1  router logits, sigmoid(g . x), shared expert gate/up + SwiGLU
+//   phase 2  top-K (re-derived by every wavefront from the logits), routed
+//            gate/up + SwiGLU, shared expert down (scaled by its gate)
+//   phase 3  routed down + weighted combine + residual + shared expert output
+// Each block has one role. Its wavefronts first issue all of their weight
+// loads (registers), then the block stages the input vector it needs in LDS
+// once (one coalesced read instead of one per wavefront; padded rows of 68
+// floats make the per-lane 128-bit slice reads conflict-free), and only then
+// does any arithmetic. The row count per wavefront is fixed at compile time so
+// the code is straight-line and the compiler cannot sink loads toward their uses.
+#pragma once
+
+#include "device.h"
+#include "kernels.h"
+
+namespace fmoe {
+namespace dev {
+
+constexpr int kXPad = 68;               // LDS floats per 64-value group (4 floats of padding)
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+__device__ __forceinline__ int wave_in_block() { return threadIdx.x >> 6; }
+__device__ __forceinline__ int lds_index(int c) { return (c >> 6) * kXPad + (c & 63); }
+
+// Stage n = 64*NG floats from global memory into padded LDS rows. With SUMSQ the
+// block's sum of squares of the vector is formed in a fixed order: each thread
+// over its float4s, DPP within the wavefront, then the wavefronts in order;
+// part[] receives one partial per wavefront. The caller synchronises.
+template <int NG, bool SUMSQ>
+__device__ __forceinline__ void stage_vec(const float *__restrict__ src, float *lds, float *part) {
+  constexpr int NF4 = NG * 16;
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < (NF4 + kBlock - 1) / kBlock; ++k) {
+    const int f = threadIdx.x + kBlock * k;
+    if (f < NF4) {
+      const float4 v = reinterpret_cast<const float4 *>(src)[f];
+      *reinterpret_cast<float4 *>(&lds[lds_index(4 * f)]) = v;
+      if constexpr (SUMSQ) ss += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
+    }
+  }
+  if constexpr (SUMSQ) {
+    ss = seg_reduce<kWave>(ss);
+    if (lane_id() == kWave - 1) part[wave_in_block()] = ss;
+  }
+}
+
+// Two-step staging, so that a wavefront can issue the vector's loads before its
+// weight loads (memory counters complete in order: waiting for the vector then
+// does not wait for the weights). N4 = float4s per thread.
+template <int N4>
+struct Staged {
+  float4 v[N4];
+};
+
+template <int N4>
+__device__ __forceinline__ void stage_load(const float *__restrict__ src, int nf4, Staged<N4> &st) {
+#pragma unroll
+  for (int k = 0; k < N4; ++k) {
+    const int f = threadIdx.x + kBlock * k;
+    if (f < nf4) st.v[k] = reinterpret_cast<const float4 *>(src)[f];
+  }
+}
+
+// Store into padded LDS rows; with SUMSQ, the wavefront's partial sum of squares
+// (same fixed order as stage_vec) goes to part[].
+template <int N4, bool SUMSQ>
+__device__ __forceinline__ void stage_store(const Staged<N4> &st, int nf4, float *lds, float *part) {
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < N4; ++k) {
+    const int f = threadIdx.x + kBlock * k;
+    if (f < nf4) {
+      const float4 v = st.v[k];
+      *reinterpret_cast<float4 *>(&lds[lds_index(4 * f)]) = v;
+      if constexpr (SUMSQ) ss += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
+    }
+  }
+  if constexpr (SUMSQ) {
+    ss = seg_reduce<kWave>(ss);
+    if (lane_id() == kWave - 1) part[wave_in_block()] = ss;
+  }
+}
+
+// RMS factor 1/sqrt(mean(x^2) + eps) from the wavefront partials (after the barrier).
+__device__ __forceinline__ float rms_inv(const float *part, int n, float eps) {
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < kWavesPerBlock; ++i) t += part[i];
+  return 1.f / sqrtf(t / (float)n + eps);
+}
+
+// Lane's slice x[64g .. 64g+63] from padded LDS, times `scale`.
+__device__ __forceinline__ void read_slice(const float *lds, int g, float scale, XSlice &xs) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float4 t = *reinterpret_cast<const float4 *>(&lds[g * kXPad + 4 * i]);
+    xs.v[4 * i] = t.x * scale;
+    xs.v[4 * i + 1] = t.y * scale;
+    xs.v[4 * i + 2] = t.z * scale;
+    xs.v[4 * i + 3] = t.w * scale;
+  }
+  xs.sum = tree_sum64(xs.v);
+}
+
+// ------------------------------------------------------------------ L2 prefetch
+//
+// Workgroup b of a launch runs on XCD b % 8, and L2 contents survive kernel
+// boundaries. A kernel whose own loads leave the memory system idle can
+// therefore fetch the next kernel's known weights into the L2 of the XCD whose
+// workgroups will read them: workgroup b prefetches for the next kernel's
+// workgroups c with c % 8 == b % 8. The prefetch uses load-to-LDS requests
+// (no register results; the LDS words written are a scratch area never read)
+// and is drained before the wavefront ends.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+constexpr int kDumpU4 = kBlock;  // 1 KB of LDS scratch per wavefront
+
+// [p, p + bytes), both multiples of 16, into this workgroup's L2.
+__device__ __forceinline__ void block_prefetch(const void *p, size_t bytes, uint4 *dump) {
+  lds_void_t *dst = (lds_void_t *)(dump + wave_in_block() * kWave);
+  const uint8_t *b = (const uint8_t *)p;
+  for (size_t off = (size_t)threadIdx.x * 16; off < bytes; off += (size_t)kBlock * 16)
+    __builtin_amdgcn_global_load_lds((glb_void_t *)(b + off), dst, 16, 0, 0);
+}
+
+// The part of [off, off + bytes) that lies inside a region of `total` bytes.
+__device__ __forceinline__ void block_prefetch_in(const uint8_t *base, size_t off, size_t bytes, size_t total,
+                                                  uint4 *dump) {
+  if (off >= total) return;
+  block_prefetch(base + off, bytes < total - off ? bytes : total - off, dump);
+}
+
+__device__ __forceinline__ void prefetch_drain() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Profiling hook: thread 0 of a workgroup records the device clock at a point.
+constexpr int kTraceSlots = 8;
+constexpr int kTraceBlocks = 4096;  // workgroups recorded per phase
+__device__ __forceinline__ void trace_mark(uint64_t *tr, int slot) {
+  if (tr && threadIdx.x == 0 && blockIdx.x < (unsigned)kTraceBlocks)
+    tr[(size_t)blockIdx.x * kTraceSlots + slot] = __builtin_amdgcn_s_memrealtime();
+}
+
+// ------------------------------------------------------------------ row work
+
+// Weight registers of ITERS row iterations of one wavefront (NG lanes per row).
+template <int BITS, int NG, int ITERS>
+struct RowLoads {
+  Chunk<BITS> c[ITERS];
+  uint32_t sb[ITERS];
+  // rows row0 + i*RPI + sub (clamped to rows-1) of a matrix with records of RB bytes
+  __device__ __forceinline__ void issue(const uint8_t *__restrict__ blob, int rows, int row0) {
+    constexpr int RPI = kWave / NG;
+    constexpr size_t RB = (size_t)NG * gbytes<BITS>();
+    const int lane = lane_id();
+    const int g = lane & (NG - 1), sub = lane / NG;
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+      const int row = min(row0 + i * RPI + sub, rows - 1);
+      load_group<BITS, NG>(blob + (size_t)row * RB, g, c[i], sb[i]);
+    }
+  }
+  // y[row] = alpha * row . x
+  __device__ __forceinline__ void finish(const XSlice &xs, float *__restrict__ y, int rows, int row0,
+                                         float alpha) const {
+    constexpr int RPI = kWave / NG;
+    const int lane = lane_id();
+    const int sub = lane / NG;
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+      const float p = seg_reduce<NG>(group_partial<BITS>(c[i], sb[i], xs));
+      const int row = row0 + i * RPI + sub;
+      if (seg_last<NG>(lane) && row < rows) y[row] = alpha * p;
+    }
+  }
+};
+
+// Row pairs of an interleaved gate/up region (records 2r and 2r+1).
+template <int BITS, int NG, int ITERS>
+struct PairLoads {
+  Chunk<BITS> cg[ITERS], cu[ITERS];
+  uint32_t sg[ITERS], su[ITERS];
+  __device__ __forceinline__ void issue(const uint8_t *__restrict__ gu, int pair0) {
+    constexpr int RPI = kWave / NG;
+    constexpr size_t RB = (size_t)NG * gbytes<BITS>();
+    const int lane = lane_id();
+    const int g = lane & (NG - 1), sub = lane / NG;
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+      const uint8_t *rec = gu + (size_t)(2 * (pair0 + i * RPI + sub)) * RB;
+      load_group<BITS, NG>(rec, g, cg[i], sg[i]);
+      load_group<BITS, NG>(rec + RB, g, cu[i], su[i]);
+    }
+  }
+  // h[r] = silu(gate_r . x) * (up_r . x)
+  __device__ __forceinline__ void finish(const XSlice &xs, float *__restrict__ h, int pair0) const {
+    constexpr int RPI = kWave / NG;
+    const int lane = lane_id();
+    const int sub = lane / NG;
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+      const float pg = seg_reduce<NG>(group_partial<BITS>(cg[i], sg[i], xs));
+      const float pu = seg_reduce<NG>(group_partial<BITS>(cu[i], su[i], xs));
+      if (seg_last<NG>(lane)) h[pair0 + i * RPI + sub] = silu(pg) * pu;
+    }
+  }
+};
+
+// Top-K of E logits held in LDS by one wavefront: K rounds of "largest remaining
+// value, lower index on a tie". Each lane keeps the best (value, index) of its
+// own remaining elements; a round takes the wavefront maximum of the values and
+// then the minimum index holding it (both by DPP), and only the winning lane
+// rescans its elements. Then the renormalised softmax weights of the chosen K,
+// w_j = exp(l_j - l_0) / sum (renormalising over the chosen K cancels the full
+// softmax denominator). Results are wavefront-uniform. NaN logits count as -inf.
+template <int VPL>
+__device__ __forceinline__ void wave_topk_lds_n(const float *lg, int E, int K, int *idx, float *w) {
+  const int lane = lane_id();
+  float v[VPL];
+#pragma unroll
+  for (int m = 0; m < VPL; ++m) {
+    const int e = lane + 64 * m;
+    const float t = e < E ? lg[e] : -INFINITY;
+    v[m] = t == t ? t : -INFINITY;
+  }
+  uint32_t taken = 0;  // bit m: element lane + 64m already chosen
+  // lane best among its available elements: largest value, smallest index on a
+  // tie; a lane with none left reports (-inf, INT_MAX)
+  auto lane_best = [&](float &bv, int &bi) {
+    bv = -INFINITY;
+    bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int m = VPL - 1; m >= 0; --m) {
+      const int e = lane + 64 * m;
+      const bool better = e < E && !((taken >> m) & 1u) && v[m] >= bv;  // descending m: smallest m wins ties
+      bv = better ? v[m] : bv;
+      bi = better ? e : bi;
+    }
+  };
+  float bv;
+  int bi;
+  lane_best(bv, bi);
+  float lv[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    idx[j] = 0;
+    lv[j] = 0.f;
+  }
+  for (int j = 0; j < K; ++j) {
+    float gm = bv;
+    gm = fmaxf(gm, dpp_f<0xB1, 0xF>(gm, -INFINITY));
+    gm = fmaxf(gm, dpp_f<0x4E, 0xF>(gm, -INFINITY));
+    gm = fmaxf(gm, dpp_f<0x141, 0xF>(gm, -INFINITY));
+    gm = fmaxf(gm, dpp_f<0x140, 0xF>(gm, -INFINITY));
+    gm = fmaxf(gm, dpp_f<0x142, 0xA>(gm, -INFINITY));
+    gm = fmaxf(gm, dpp_f<0x143, 0xC>(gm, -INFINITY));
+    const float gmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gm), 63));
+    int li = bv == gmax ? bi : 0x7FFFFFFF;
+    li = min(li, dpp_i<0xB1, 0xF>(li, 0x7FFFFFFF));
+    li = min(li, dpp_i<0x4E, 0xF>(li, 0x7FFFFFFF));
+    li = min(li, dpp_i<0x141, 0xF>(li, 0x7FFFFFFF));
+    li = min(li, dpp_i<0x140, 0xF>(li, 0x7FFFFFFF));
+    li = min(li, dpp_i<0x142, 0xA>(li, 0x7FFFFFFF));
+    li = min(li, dpp_i<0x143, 0xC>(li, 0x7FFFFFFF));
+    const int e = __builtin_amdgcn_readlane(li, 63);
+#pragma unroll
+    for (int q = 0; q < kMaxTopK; ++q)
+      if (q == j) {
+        idx[q] = e;
+        lv[q] = gmax;
+      }
+    if ((e & 63) == lane) {  // the winning lane marks the element taken and rescans
+      taken |= 1u << (e >> 6);
+      lane_best(bv, bi);
+    }
+  }
+  // weights: only the K chosen entries; one reciprocal of the sum
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    w[j] = 0.f;
+    if (j < K) {
+      w[j] = __expf(lv[j] - lv[0]);
+      sum += w[j];
+    }
+  }
+  const float inv = 1.f / sum;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) w[j] *= inv;
+}
+
+// Wavefront argmax under (value descending, index ascending) over one (v, e) pair
+// per lane; lanes with ok == false do not take part. Returns (value, index),
+// wavefront-uniform.
+__device__ __forceinline__ void wave_argmax(float v, int e, bool ok, float &gmax, int &gidx) {
+  float gm = ok ? v : -INFINITY;
+  gm = fmaxf(gm, dpp_f<0xB1, 0xF>(gm, -INFINITY));
+  gm = fmaxf(gm, dpp_f<0x4E, 0xF>(gm, -INFINITY));
+  gm = fmaxf(gm, dpp_f<0x141, 0xF>(gm, -INFINITY));
+  gm = fmaxf(gm, dpp_f<0x140, 0xF>(gm, -INFINITY));
+  gm = fmaxf(gm, dpp_f<0x142, 0xA>(gm, -INFINITY));
+  gm = fmaxf(gm, dpp_f<0x143, 0xC>(gm, -INFINITY));
+  gmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gm), 63));
+  int li = (ok && v == gmax) ? e : 0x7FFFFFFF;
+  li = min(li, dpp_i<0xB1, 0xF>(li, 0x7FFFFFFF));
+  li = min(li, dpp_i<0x4E, 0xF>(li, 0x7FFFFFFF));
+  li = min(li, dpp_i<0x141, 0xF>(li, 0x7FFFFFFF));
+  li = min(li, dpp_i<0x140, 0xF>(li, 0x7FFFFFFF));
+  li = min(li, dpp_i<0x142, 0xA>(li, 0x7FFFFFFF));
+  li = min(li, dpp_i<0x143, 0xC>(li, 0x7FFFFFFF));
+  gidx = __builtin_amdgcn_readlane(li, 63);
+}
+
+// Top-K of E logits held in LDS, by one wavefront, exactly under the order
+// (value descending, index ascending); element e sits in lane e % 64, slot e / 64.
+//  1. each lane finds its best element;
+//  2. K rounds pick the K lanes whose best elements rank highest -- every element
+//     of the top K lies in one of them (if an element's lane were not picked, the
+//     K picked lanes' best elements would all outrank it);
+//  3. those lanes copy their elements to LDS (`cand`, K*VPL floats), one
+//     candidate per lane is read back, and K rounds of argmax select the top K.
+// Then the renormalised softmax weights of the chosen K, w_j = exp(l_j - l_0) /
+// sum (renormalising over the chosen K cancels the full softmax denominator).
+// Results are wavefront-uniform. NaN logits count as -inf.
+template <int VPL>
+__device__ __forceinline__ void wave_topk_cand(const float *lg, int E, int K, int *idx, float *w, float *cand) {
+  const int lane = lane_id();
+  float v[VPL];
+#pragma unroll
+  for (int m = 0; m < VPL; ++m) {
+    const int e = lane + 64 * m;
+    const float t = e < E ? lg[e] : -INFINITY;
+    v[m] = t == t ? t : -INFINITY;
+  }
+  float bv = -INFINITY;
+  int bi = 0x7FFFFFFF;
+#pragma unroll
+  for (int m = VPL - 1; m >= 0; --m) {
+    const bool better = lane + 64 * m < E && v[m] >= bv;  // descending m: smallest index wins ties
+    bv = better ? v[m] : bv;
+    bi = better ? lane + 64 * m : bi;
+  }
+  // 2. the K lanes with the highest-ranked best elements
+  bool picked = false;
+  int lanes[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) lanes[j] = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j >= K) break;
+    float gmax;
+    int ge;
+    wave_argmax(bv, bi, !picked && bi != 0x7FFFFFFF, gmax, ge);
+    lanes[j] = ge & 63;
+    picked = picked || lane == lanes[j];
+  }
+  // 3. candidates through LDS: candidate t = element (lanes[t / VPL], slot t % VPL)
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j >= K) break;
+    if (lane == lanes[j]) {
+#pragma unroll
+      for (int m = 0; m < VPL; ++m) cand[j * VPL + m] = v[m];
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the copies are visible to this wavefront
+  float cv;
+  int ce;
+  bool ok;
+  {  // requires K * VPL <= 64: one candidate per lane
+    const int t = lane;
+    int src = lanes[0];
+#pragma unroll
+    for (int j = 1; j < kMaxTopK; ++j)
+      if (j == t / VPL) src = lanes[j];
+    const int e = src + 64 * (t % VPL);
+    ok = t < K * VPL && e < E;
+    cv = ok ? cand[t] : -INFINITY;
+    ce = ok ? e : 0x7FFFFFFF;
+  }
+  float lv[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    idx[j] = 0;
+    lv[j] = 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j >= K) break;
+    float gmax;
+    int ge;
+    wave_argmax(cv, ce, ok, gmax, ge);
+    idx[j] = ge;
+    lv[j] = gmax;
+    ok = ok && ce != ge;
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    w[j] = 0.f;
+    if (j < K) {
+      w[j] = __expf(lv[j] - lv[0]);
+      sum += w[j];
+    }
+  }
+  const float inv = 1.f / sum;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) w[j] *= inv;
+}
+
+// cand: LDS scratch of kMaxTopK * 8 floats for this wavefront.
+__device__ __forceinline__ void wave_topk_lds(const float *lg, int E, int K, int *idx, float *w, float *cand) {
+  if (E <= 512)
+    wave_topk_cand<8>(lg, E, K, idx, w, cand);
+  else if (K <= 4)
+    wave_topk_cand<16>(lg, E, K, idx, w, cand);
+  else
+    wave_topk_lds_n<16>(lg, E, K, idx, w);
+}
+
+// Block-wide top-K: one wavefront computes it from the logits in LDS and
+// publishes it through LDS (sidx, sw); contains one barrier; results uniform in
+// every thread. Workgroup b uses wavefront b % 4, so that the workgroups sharing
+// a CU do not all compute it on the same SIMD.
+__device__ __forceinline__ void block_topk(const float *lg, int E, int K, int *sidx, float *sw, float *cand,
+                                           int *idx, float *w) {
+  if (wave_in_block() == (int)(blockIdx.x % kWavesPerBlock)) {
+    // the rest of the workgroup waits on this wavefront: let it win the SIMD's
+    // issue arbitration against co-resident wavefronts of other workgroups
+    __builtin_amdgcn_s_setprio(3);
+    wave_topk_lds(lg, E, K, idx, w, cand);
+    __builtin_amdgcn_s_setprio(0);
+    const int lane = lane_id();
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (j == lane) {
+        sidx[j] = idx[j];
+        sw[j] = w[j];
+      }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    idx[j] = sidx[j];
+    w[j] = sw[j];
+  }
+}
+
+template <int N>
+__device__ __forceinline__ int pick(const int (&a)[N], int j) {
+  int r = a[0];
+#pragma unroll
+  for (int t = 1; t < N; ++t)
+    if (t == j) r = a[t];
+  return r;
+}
+template <int N>
+__device__ __forceinline__ float pick(const float (&a)[N], int j) {
+  float r = a[0];
+#pragma unroll
+  for (int t = 1; t < N; ++t)
+    if (t == j) r = a[t];
+  return r;
+}
+
+// ------------------------------------------------------------------ standalone kernels
+
+template <int BITS, int NG, int ITERS>
+__global__ __launch_bounds__(kBlock) void k_qmatvec(const uint8_t *__restrict__ blob, int rows,
+                                                     const float *__restrict__ x, float *__restrict__ y) {
+  __shared__ float xl[NG * kXPad];
+  constexpr int X4 = (NG * 16 + kBlock - 1) / kBlock;
+  const int row0 = wave_id() * ITERS * (kWave / NG);
+  Staged<X4> xst;
+  stage_load(x, NG * 16, xst);
+  RowLoads<BITS, NG, ITERS> L;
+  if (row0 < rows) L.issue(blob, rows, row0);
+  __builtin_amdgcn_sched_barrier(0);
+  stage_store<X4, false>(xst, NG * 16, xl, nullptr);
+  __syncthreads();
+  if (row0 >= rows) return;
+  XSlice xs;
+  read_slice(xl, lane_id() & (NG - 1), 1.f, xs);
+  L.finish(xs, y, rows, row0, 1.f);
+}
+
+template <int BITS, int NG, int ITERS>
+__global__ __launch_bounds__(kBlock) void k_expert_gateup(const uint8_t *__restrict__ gu, int inter,
+                                                           const float *__restrict__ x, float *__restrict__ h) {
+  __shared__ float xl[NG * kXPad];
+  constexpr int X4 = (NG * 16 + kBlock - 1) / kBlock;
+  const int pair0 = wave_id() * ITERS * (kWave / NG);
+  Staged<X4> xst;
+  stage_load(x, NG * 16, xst);
+  PairLoads<BITS, NG, ITERS> P;
+  if (pair0 < inter) P.issue(gu, pair0);
+  __builtin_amdgcn_sched_barrier(0);
+  stage_store<X4, false>(xst, NG * 16, xl, nullptr);
+  __syncthreads();
+  if (pair0 >= inter) return;
+  XSlice xs;
+  read_slice(xl, lane_id() & (NG - 1), 1.f, xs);
+  P.finish(xs, h, pair0);
+}
+
+// ------------------------------------------------------------------ layer kernels
+
+constexpr int kP1GateUpIters = 1;  // gate/up pair iterations per wavefront in phase 1
+constexpr int kP2GateUpIters = 2;  // routed gate/up
+constexpr int kP2DownIters = 4;    // shared down rows
+constexpr int kP3Iters = 4;        // down + combine
+
+struct Phase1Args {
+  const float *router;
+  const float *gvec;  // null: no shared expert
+  int E;
+  const float *x;
+  float rms_eps;  // >= 0: x is RMS-scaled first
+  float *logits;
+  float *sigma;
+  const uint8_t *shared_gu;  // null: no shared expert
+  int I;
+  float *h_shared;
+  int n_router_blocks;
+  // prefetch for phase 2's shared-down workgroups (null: none)
+  const uint8_t *pf_sdown;
+  size_t pf_sdown_bytes;  // bytes of down rows one phase-2 shared workgroup reads
+  size_t pf_sdown_total;  // bytes of the shared expert's down region
+  int pf_n2r, pf_n2s;     // phase 2: routed workgroups, shared-down workgroups
+  uint64_t *trace;
+};
+
+// Phase 1. Router blocks: one fp32 router row per wavefront (lane l covers
+// columns 4l + 256t + 0..3; row E is the shared expert's gate vector, giving
+// sigmoid(g . x)). Shared blocks: the shared expert's gate/up + SwiGLU.
+template <int BITS, int NGH>
+__global__ __launch_bounds__(kBlock) void k_phase1(const Phase1Args a) {
+  constexpr int NT = NGH / 4;  // hidden / 256
+  constexpr int H = NGH * kGroup;
+  constexpr int X4 = (NGH * 16 + kBlock - 1) / kBlock;
+  __shared__ float xl[NGH * kXPad];
+  __shared__ float part[kWavesPerBlock];
+  __shared__ uint4 dump[kDumpU4];
+  const int lane = lane_id();
+  const bool rms = a.rms_eps >= 0.f;
+  // phase 2's shared-down workgroup c = pf_n2r + s runs on XCD c % 8; s = b + k*grid keeps c % 8 == b % 8
+  // when pf_n2r and the grid are multiples of 8.
+  trace_mark(a.trace, 0);
+  auto prefetch = [&]() {
+    if (!a.pf_sdown) return;
+    for (int s2 = blockIdx.x; s2 < a.pf_n2s; s2 += gridDim.x)
+      block_prefetch_in(a.pf_sdown, (size_t)s2 * a.pf_sdown_bytes, a.pf_sdown_bytes, a.pf_sdown_total, dump);
+  };
+  if ((int)blockIdx.x < a.n_router_blocks) {
+    const int n_rows = a.E + (a.gvec ? 1 : 0);
+    const int row = blockIdx.x * kWavesPerBlock + wave_in_block();
+    const int rr = min(row, n_rows - 1);
+    const float *src = rr == a.E ? a.gvec : a.router + (size_t)rr * H;
+    Staged<X4> xst;
+    stage_load(a.x, NGH * 16, xst);
+    float4 w[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) w[t] = reinterpret_cast<const float4 *>(src)[lane + 64 * t];
+    __builtin_amdgcn_sched_barrier(0);
+    if (rms)
+      stage_store<X4, true>(xst, NGH * 16, xl, part);
+    else
+      stage_store<X4, false>(xst, NGH * 16, xl, part);
+    __syncthreads();
+    trace_mark(a.trace, 1);
+    prefetch();
+    const float inv = rms ? rms_inv(part, H, a.rms_eps) : 1.f;
+    float acc = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float4 xv = *reinterpret_cast<const float4 *>(&xl[lds_index(4 * lane + 256 * t)]);
+      acc = fmaf(w[t].x, xv.x * inv, acc);
+      acc = fmaf(w[t].y, xv.y * inv, acc);
+      acc = fmaf(w[t].z, xv.z * inv, acc);
+      acc = fmaf(w[t].w, xv.w * inv, acc);
+    }
+    const float d = seg_reduce<kWave>(acc);
+    trace_mark(a.trace, 2);
+    if (lane == kWave - 1 && row < n_rows) {
+      if (row == a.E)
+        *a.sigma = 1.f / (1.f + expf(-d));
+      else
+        a.logits[row] = d;
+    }
+  } else {
+    // shared expert gate/up
+    const int wv = (blockIdx.x - a.n_router_blocks) * kWavesPerBlock + wave_in_block();
+    const int pair0 = wv * kP1GateUpIters * (kWave / NGH);
+    Staged<X4> xst;
+    stage_load(a.x, NGH * 16, xst);
+    PairLoads<BITS, NGH, kP1GateUpIters> P;
+    if (pair0 < a.I) P.issue(a.shared_gu, pair0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (rms)
+      stage_store<X4, true>(xst, NGH * 16, xl, part);
+    else
+      stage_store<X4, false>(xst, NGH * 16, xl, part);
+    __syncthreads();
+    trace_mark(a.trace, 1);
+    prefetch();
+    if (pair0 < a.I) {
+      XSlice xs;
+      read_slice(xl, lane & (NGH - 1), rms ? rms_inv(part, H, a.rms_eps) : 1.f, xs);
+      P.finish(xs, a.h_shared, pair0);
+    }
+  }
+  trace_mark(a.trace, 3);
+  prefetch_drain();
+  trace_mark(a.trace, 4);
+}
+
+struct Phase2Args {
+  const float *logits;
+  int E, K;
+  const uint8_t *bank;
+  size_t stride;
+  const float *x;
+  float rms_eps;
+  int I;
+  float *h_routed;
+  int32_t *ws_idx;
+  float *ws_w;
+  int32_t *out_idx;
+  float *out_w;
+  int waves_per_slot;
+  int n_routed_blocks;
+  // shared expert's down projection (null: none)
+  const uint8_t *shared_down;
+  int H;
+  const float *h_shared;
+  const float *sigma;
+  float *d_shared;
+  // prefetch of the routed experts' down rows for phase 3 (pf_n3 = 0: none)
+  size_t gu_bytes;          // offset of the down region in an expert blob
+  size_t pf_down_bytes;     // bytes of down rows one phase-3 workgroup reads per expert
+  size_t pf_down_total;     // bytes of one expert's down region
+  int pf_n3;                // phase-3 workgroups
+  uint64_t *trace;
+};
+
+// Phase 2. Routed blocks stage the logits and x, every wavefront re-derives the
+// top-K, then runs gate/up + SwiGLU of its slot's expert. Shared blocks run the
+// shared expert's down projection, scaled by its sigmoid gate.
+template <int BITS, int NGH, int NGI>
+__global__ __launch_bounds__(kBlock) void k_phase2(const Phase2Args a) {
+  constexpr int H = NGH * kGroup;
+  constexpr int XL = NGH * kXPad > NGI * kXPad ? NGH * kXPad : NGI * kXPad;
+  __shared__ float xl[XL];
+  __shared__ float lg[kMaxExperts];
+  __shared__ float part[kWavesPerBlock];
+  __shared__ int sidx[kMaxTopK];
+  __shared__ float sw[kMaxTopK];
+  __shared__ float cand[kMaxTopK * 8];
+  __shared__ uint4 dump[kDumpU4];
+  const int lane = lane_id();
+  trace_mark(a.trace, 0);
+  if ((int)blockIdx.x < a.n_routed_blocks) {
+    const bool rms = a.rms_eps >= 0.f;
+    for (int i = threadIdx.x; i < a.E; i += kBlock) lg[i] = a.logits[i];
+    if (rms)
+      stage_vec<NGH, true>(a.x, xl, part);
+    else
+      stage_vec<NGH, false>(a.x, xl, part);
+    __syncthreads();
+    trace_mark(a.trace, 1);
+    int idx[kMaxTopK];
+    float w[kMaxTopK];
+    block_topk(lg, a.E, a.K, sidx, sw, cand, idx, w);
+    trace_mark(a.trace, 2);
+    const int wv = blockIdx.x * kWavesPerBlock + wave_in_block();
+    const int slot = min(wv / a.waves_per_slot, a.K - 1);
+    const int pair0 = (wv % a.waves_per_slot) * kP2GateUpIters * (kWave / NGH);
+    const bool active = wv < a.waves_per_slot * a.K;
+    PairLoads<BITS, NGH, kP2GateUpIters> P;
+    if (active) P.issue(a.bank + (size_t)pick(idx, slot) * a.stride, pair0);
+    if (a.pf_n3 > 0) {
+      // phase-3 workgroup c = b mod pf_n3 (same XCD when pf_n3 % 8 == 0); the
+      // routed workgroups that map to c split its K experts between them
+      const int c = blockIdx.x % a.pf_n3;
+      const int parts = (a.n_routed_blocks + a.pf_n3 - 1) / a.pf_n3;
+      const int part = blockIdx.x / a.pf_n3;
+      for (int k = part; k < a.K; k += parts)
+        block_prefetch_in(a.bank + (size_t)pick(idx, k) * a.stride + a.gu_bytes, (size_t)c * a.pf_down_bytes,
+                          a.pf_down_bytes, a.pf_down_total, dump);
+    }
+    if (wv == 0 && lane < a.K) {
+      const int sel = pick(idx, lane);
+      const float ws = pick(w, lane);
+      a.ws_idx[lane] = sel;
+      a.ws_w[lane] = ws;
+      if (a.out_idx) a.out_idx[lane] = sel;
+      if (a.out_w) a.out_w[lane] = ws;
+    }
+    if (active) {
+      XSlice xs;
+      read_slice(xl, lane & (NGH - 1), rms ? rms_inv(part, H, a.rms_eps) : 1.f, xs);
+      P.finish(xs, a.h_routed + (size_t)slot * a.I, pair0);
+    }
+    trace_mark(a.trace, 3);
+    prefetch_drain();
+    trace_mark(a.trace, 4);
+    return;
+  }
+  // shared expert down
+  const int wv = (blockIdx.x - a.n_routed_blocks) * kWavesPerBlock + wave_in_block();
+  const int row0 = wv * kP2DownIters * (kWave / NGI);
+  constexpr int I4 = (NGI * 16 + kBlock - 1) / kBlock;
+  Staged<I4> hst;
+  stage_load(a.h_shared, NGI * 16, hst);
+  RowLoads<BITS, NGI, kP2DownIters> R;
+  if (row0 < a.H) R.issue(a.shared_down, a.H, row0);
+  __builtin_amdgcn_sched_barrier(0);
+  stage_store<I4, false>(hst, NGI * 16, xl, nullptr);
+  __syncthreads();
+  if (row0 >= a.H) return;
+  XSlice xs;
+  read_slice(xl, lane & (NGI - 1), 1.f, xs);
+  R.finish(xs, a.d_shared, a.H, row0, *a.sigma);
+  trace_mark(a.trace, 3);
+  trace_mark(a.trace, 4);
+}
+
+struct Phase3Args {
+  const uint8_t *bank;
+  size_t stride, gu_bytes;
+  const int32_t *idx;
+  const float *w;
+  int K;
+  const float *h_routed;  // [K][I]
+  int I, H;
+  const float *d_shared;  // [H] or null
+  const float *residual;
+  float *out;
+  // prefetch of the next layer's phase-1 inputs (nrouter null: none)
+  const float *nrouter;
+  const float *ngvec;
+  const uint8_t *nshared_gu;
+  int nE, n1r, n1;          // next phase 1: experts, router workgroups, all workgroups
+  size_t n_row_bytes;       // bytes of one router row (hidden * 4)
+  size_t n_sh_bytes;        // bytes of gate/up pairs one phase-1 shared workgroup reads
+  size_t n_sh_total;        // bytes of the shared expert's gate/up region
+  uint64_t *trace;
+};
+
+// Phase 3: out_i = residual_i + sum_k w_k (down_k . h_k)_i + d_shared_i.
+// Lanes are (slot k, group j) pairs, so one cross-lane sum adds the K experts'
+// weighted partials of a row together; each lane keeps its slot's h slice.
+// KPAD = top_k rounded up to a power of two (slots beyond top_k stay idle). The
+// routed h vectors are staged in LDS when they fit (KPAD * inter <= 8192).
+template <int BITS, int NGI, int KPAD>
+__global__ __launch_bounds__(kBlock) void k_phase3(const Phase3Args a) {
+  constexpr int SLOTS = KPAD * NGI;
+  constexpr int SEG = SLOTS < kWave ? SLOTS : kWave;  // lanes per row
+  constexpr int SPL = SLOTS / SEG;                     // slots per lane
+  constexpr int RPI = kWave / SEG;
+  constexpr size_t RB = (size_t)NGI * gbytes<BITS>();
+  constexpr bool STAGE = KPAD * NGI <= 128;
+  __shared__ float hl[STAGE ? KPAD * NGI * kXPad : 1];
+  __shared__ uint4 dump[kDumpU4];
+  trace_mark(a.trace, 0);
+  const int lane = lane_id();
+  const int sub = lane / SEG;
+  const int row0 = wave_id() * kP3Iters * RPI;
+  const uint8_t *base[SPL];
+  float wk[SPL];
+  int grp[SPL], kk[SPL];
+  bool act[SPL];
+#pragma unroll
+  for (int m = 0; m < SPL; ++m) {
+    const int slot = (lane % SEG) + kWave * m;
+    const int k = slot / NGI;
+    grp[m] = slot % NGI;
+    act[m] = k < a.K && row0 < a.H;
+    kk[m] = k < a.K ? k : 0;
+    base[m] = a.bank + (size_t)a.idx[kk[m]] * a.stride + a.gu_bytes;
+    wk[m] = k < a.K ? a.w[kk[m]] : 0.f;
+  }
+  constexpr int H4 = STAGE ? (KPAD * NGI * 16 + kBlock - 1) / kBlock : 1;
+  Staged<H4> hst;
+  if constexpr (STAGE) stage_load(a.h_routed, a.K * a.I / 4, hst);
+  Chunk<BITS> c[kP3Iters][SPL];
+  uint32_t sb[kP3Iters][SPL];
+#pragma unroll
+  for (int i = 0; i < kP3Iters; ++i) {
+    const int row = min(row0 + i * RPI + sub, a.H - 1);
+#pragma unroll
+    for (int m = 0; m < SPL; ++m)
+      if (act[m]) load_group<BITS, NGI>(base[m] + (size_t)row * RB, grp[m], c[i][m], sb[i][m]);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // the h vectors were requested before the weights
+  if (a.nrouter) {
+    // next layer's phase-1 workgroups c = b + k*grid (same XCD when the grid is a multiple of 8)
+    for (int c = blockIdx.x; c < a.n1; c += gridDim.x) {
+      if (c < a.n1r) {
+        const int r0 = c * kWavesPerBlock;
+        const int r1 = min(r0 + kWavesPerBlock, a.nE);
+        if (r1 > r0) block_prefetch(a.nrouter + (size_t)r0 * (a.n_row_bytes / 4), (size_t)(r1 - r0) * a.n_row_bytes, dump);
+        if (a.ngvec && r0 + kWavesPerBlock > a.nE) block_prefetch(a.ngvec, a.n_row_bytes, dump);
+      } else if (a.nshared_gu) {
+        block_prefetch_in(a.nshared_gu, (size_t)(c - a.n1r) * a.n_sh_bytes, a.n_sh_bytes, a.n_sh_total, dump);
+      }
+    }
+  }
+  XSlice xs[SPL];
+  if constexpr (STAGE) {
+    // h_routed [K][I] -> LDS rows of 64 (slot k's group j is LDS row k*NGI + j)
+    stage_store<H4, false>(hst, a.K * a.I / 4, hl, nullptr);
+    __syncthreads();
+    trace_mark(a.trace, 1);
+    if (row0 >= a.H) {
+      prefetch_drain();
+      return;
+    }
+#pragma unroll
+    for (int m = 0; m < SPL; ++m) read_slice(hl, kk[m] * NGI + grp[m], 1.f, xs[m]);
+  } else {
+    if (row0 >= a.H) {
+      prefetch_drain();
+      return;
+    }
+#pragma unroll
+    for (int m = 0; m < SPL; ++m) load_xslice(a.h_routed + (size_t)kk[m] * a.I + kGroup * grp[m], xs[m]);
+  }
+#pragma unroll
+  for (int i = 0; i < kP3Iters; ++i) {
+    float p = 0.f;
+#pragma unroll
+    for (int m = 0; m < SPL; ++m)
+      if (act[m]) p = fmaf(wk[m], group_partial<BITS>(c[i][m], sb[i][m], xs[m]), p);
+    p = seg_reduce<SEG>(p);
+    const int row = row0 + i * RPI + sub;
+    if (seg_last<SEG>(lane) && row < a.H) {
+      float o = a.residual[row] + p;
+      if (a.d_shared) o += a.d_shared[row];
+      a.out[row] = o;
+    }
+  }
+  trace_mark(a.trace, 3);
+  prefetch_drain();
+  trace_mark(a.trace, 4);
+}
+
+// ------------------------------------------------------------------ host dispatch
+
+#define FMOE_NG_SWITCH(ng, FN, ...)          \
+  switch (ng) {                              \
+    case 4: return FN<4>(__VA_ARGS__);       \
+    case 8: return FN<8>(__VA_ARGS__);       \
+    case 16: return FN<16>(__VA_ARGS__);     \
+    case 32: return FN<32>(__VA_ARGS__);     \
+    case 64: return FN<64>(__VA_ARGS__);     \
+    default: return hipErrorInvalidValue;    \
+  }
+
+inline int blocks_for(long waves) { return (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock); }
+
+// Launch geometry of one layer's three kernels (shared by the launchers, which
+// also need each other's geometry for the XCD-aligned prefetch).
+template <int NGH, int NGI>
+struct LayerGeom {
+  static constexpr int RPIH = kWave / NGH, RPII = kWave / NGI;
+  int n1r, n1s, n2r, n2s, n3, wps, kpad;
+  size_t rbh, rbi;
+  __host__ LayerGeom(const LayerArgs &L, int bits) {
+    const bool sh = L.shared != nullptr;
+    rbh = (size_t)NGH * (bits == 4 ? 36 : 20);
+    rbi = (size_t)NGI * (bits == 4 ? 36 : 20);
+    n1r = blocks_for(L.E + (sh ? 1 : 0));
+    n1s = sh ? blocks_for((L.I / RPIH + kP1GateUpIters - 1) / kP1GateUpIters) : 0;
+    wps = (L.I / RPIH + kP2GateUpIters - 1) / kP2GateUpIters;
+    n2r = blocks_for((long)wps * L.K);
+    n2s = sh ? blocks_for((L.H / RPII + kP2DownIters - 1) / kP2DownIters) : 0;
+    kpad = 1;
+    while (kpad < L.K) kpad <<= 1;
+    const int slots = kpad * NGI;
+    const int seg = slots < kWave ? slots : kWave;
+    n3 = blocks_for(((long)L.H / (kWave / seg) + kP3Iters - 1) / kP3Iters);
+  }
+  size_t p1_sh_pair_bytes() const { return (size_t)kWavesPerBlock * kP1GateUpIters * RPIH * 2 * rbh; }
+  size_t p2_sdown_rows_bytes() const { return (size_t)kWavesPerBlock * kP2DownIters * RPII * rbi; }
+  size_t p3_rows_bytes() const {
+    const int slots = kpad * NGI;
+    const int seg = slots < kWave ? slots : kWave;
+    return (size_t)kWavesPerBlock * kP3Iters * (kWave / seg) * rbi;
+  }
+};
+
+template <int BITS>
+struct Dispatch {
+  template <int NG>
+  static hipError_t qmatvec(const uint8_t *blob, int rows, const float *x, float *y, hipStream_t s) {
+    constexpr int RPI = kWave / NG;
+    const long iters = (rows + RPI - 1) / RPI;
+    // Enough wavefronts to cover every SIMD several times over; more rows per
+    // wavefront only once there is work to spare.
+    if (iters >= 4L * 4096)
+      hipLaunchKernelGGL((k_qmatvec<BITS, NG, 4>), dim3(blocks_for((iters + 3) / 4)), dim3(kBlock), 0, s, blob, rows,
+                         x, y);
+    else if (iters >= 2L * 2048)
+      hipLaunchKernelGGL((k_qmatvec<BITS, NG, 2>), dim3(blocks_for((iters + 1) / 2)), dim3(kBlock), 0, s, blob, rows,
+                         x, y);
+    else
+      hipLaunchKernelGGL((k_qmatvec<BITS, NG, 1>), dim3(blocks_for(iters)), dim3(kBlock), 0, s, blob, rows, x, y);
+    return hipGetLastError();
+  }
+
+  template <int NG>
+  static hipError_t gateup(const uint8_t *gu, int inter, const float *x, float *h, hipStream_t s) {
+    constexpr int RPI = kWave / NG;
+    const long waves = inter / RPI;
+    hipLaunchKernelGGL((k_expert_gateup<BITS, NG, 1>), dim3(blocks_for(waves)), dim3(kBlock), 0, s, gu, inter, x, h);
+    return hipGetLastError();
+  }
+
+  template <int NGH, int NGI, int KPAD>
+  static hipError_t phase3(const LayerArgs &L, const LayerGeom<NGH, NGI> &G, hipStream_t s) {
+    Phase3Args p3{};
+    p3.bank = L.bank;
+    p3.stride = L.expert_stride;
+    p3.gu_bytes = L.gateup_bytes;
+    p3.idx = L.ws_idx;
+    p3.w = L.ws_w;
+    p3.K = L.K;
+    p3.h_routed = L.h_routed;
+    p3.I = L.I;
+    p3.H = L.H;
+    p3.d_shared = L.shared ? L.d_shared : nullptr;
+    p3.residual = L.residual;
+    p3.out = L.out;
+    p3.nrouter = (L.prefetch_mask & 4) ? L.next_router : nullptr;
+    p3.ngvec = L.next_router ? L.next_gvec : nullptr;
+    p3.nshared_gu = L.next_router ? L.next_shared : nullptr;
+    p3.nE = L.E;
+    p3.n1r = G.n1r;
+    p3.n1 = G.n1r + G.n1s;
+    p3.n_row_bytes = sizeof(float) * (size_t)L.H;
+    p3.n_sh_bytes = G.p1_sh_pair_bytes();
+    p3.n_sh_total = (size_t)2 * L.I * G.rbh;
+    p3.trace = L.trace ? L.trace + (size_t)2 * kTraceBlocks * kTraceSlots : nullptr;
+    hipLaunchKernelGGL((k_phase3<BITS, NGI, KPAD>), dim3(G.n3), dim3(kBlock), 0, s, p3);
+    return hipGetLastError();
+  }
+
+  template <int NGH, int NGI>
+  static hipError_t phase1(const LayerArgs &L, const LayerGeom<NGH, NGI> &G, hipStream_t s) {
+    const bool has_shared = L.shared != nullptr;
+    Phase1Args p1{};
+    p1.router = L.router;
+    p1.gvec = has_shared ? L.shared_gate : nullptr;
+    p1.E = L.E;
+    p1.x = L.x;
+    p1.rms_eps = L.rms_eps;
+    p1.logits = L.logits;
+    p1.sigma = L.sigma;
+    p1.shared_gu = has_shared ? L.shared : nullptr;
+    p1.I = L.I;
+    p1.h_shared = L.h_shared;
+    p1.n_router_blocks = G.n1r;
+    p1.pf_sdown = has_shared && (L.prefetch_mask & 1) ? L.shared + L.gateup_bytes : nullptr;
+    p1.pf_sdown_bytes = G.p2_sdown_rows_bytes();
+    p1.pf_sdown_total = (size_t)L.H * G.rbi;
+    p1.pf_n2r = G.n2r;
+    p1.pf_n2s = G.n2s;
+    p1.trace = L.trace;
+    hipLaunchKernelGGL((k_phase1<BITS, NGH>), dim3(G.n1r + G.n1s), dim3(kBlock), 0, s, p1);
+    return hipGetLastError();
+  }
+
+  template <int NGH, int NGI>
+  static hipError_t phase2(const LayerArgs &L, const LayerGeom<NGH, NGI> &G, hipStream_t s) {
+    const bool has_shared = L.shared != nullptr;
+    Phase2Args p2{};
+    p2.logits = L.logits;
+    p2.E = L.E;
+    p2.K = L.K;
+    p2.bank = L.bank;
+    p2.stride = L.expert_stride;
+    p2.x = L.x;
+    p2.rms_eps = L.rms_eps;
+    p2.I = L.I;
+    p2.h_routed = L.h_routed;
+    p2.ws_idx = L.ws_idx;
+    p2.ws_w = L.ws_w;
+    p2.out_idx = L.topk_idx_out;
+    p2.out_w = L.topk_w_out;
+    p2.waves_per_slot = G.wps;
+    p2.n_routed_blocks = G.n2r;
+    p2.shared_down = has_shared ? L.shared + L.gateup_bytes : nullptr;
+    p2.H = L.H;
+    p2.h_shared = L.h_shared;
+    p2.sigma = L.sigma;
+    p2.d_shared = L.d_shared;
+    p2.gu_bytes = L.gateup_bytes;
+    p2.pf_down_bytes = G.p3_rows_bytes();
+    p2.pf_down_total = (size_t)L.H * G.rbi;
+    p2.pf_n3 = (L.prefetch_mask & 2) ? G.n3 : 0;
+    p2.trace = L.trace ? L.trace + (size_t)kTraceBlocks * kTraceSlots : nullptr;
+    hipLaunchKernelGGL((k_phase2<BITS, NGH, NGI>), dim3(G.n2r + G.n2s), dim3(kBlock), 0, s, p2);
+    return hipGetLastError();
+  }
+
+  template <int NGH, int NGI>
+  static hipError_t phase3k(const LayerArgs &L, const LayerGeom<NGH, NGI> &G, hipStream_t s) {
+    if (L.K <= 1) return phase3<NGH, NGI, 1>(L, G, s);
+    if (L.K <= 2) return phase3<NGH, NGI, 2>(L, G, s);
+    if (L.K <= 4) return phase3<NGH, NGI, 4>(L, G, s);
+    return phase3<NGH, NGI, 8>(L, G, s);
+  }
+
+  template <int NGH, int NGI>
+  static hipError_t layer(const LayerArgs &L, hipStream_t s, int phases) {
+    const LayerGeom<NGH, NGI> G(L, BITS);
+    hipError_t err = hipSuccess;
+    if (phases & 1) err = phase1<NGH, NGI>(L, G, s);
+    if (err == hipSuccess && (phases & 2)) err = phase2<NGH, NGI>(L, G, s);
+    if (err == hipSuccess && (phases & 4)) err = phase3k<NGH, NGI>(L, G, s);
+    return err;
+  }
+
+  template <int NGH>
+  static hipError_t layer_h(const LayerArgs &L, hipStream_t s, int phases) {
+    switch (L.I / kGroup) {
+      case 4: return layer<NGH, 4>(L, s, phases);
+      case 8: return layer<NGH, 8>(L, s, phases);
+      case 16: return layer<NGH, 16>(L, s, phases);
+      case 32: return layer<NGH, 32>(L, s, phases);
+      case 64: return layer<NGH, 64>(L, s, phases);
+      default: return hipErrorInvalidValue;
+    }
+  }
+};
+
+template <int BITS>
+hipError_t qmatvec_b(const uint8_t *blob, int rows, int cols, const float *x, float *y, hipStream_t s) {
+  FMOE_NG_SWITCH(cols / kGroup, Dispatch<BITS>::template qmatvec, blob, rows, x, y, s)
+}
+
+template <int BITS>
+hipError_t gateup_b(const uint8_t *gu, int hidden, int inter, const float *x, float *h, hipStream_t s) {
+  FMOE_NG_SWITCH(hidden / kGroup, Dispatch<BITS>::template gateup, gu, inter, x, h, s)
+}
+
+template <int BITS>
+hipError_t layer_b(const LayerArgs &L, hipStream_t s, int phases) {
+  FMOE_NG_SWITCH(L.H / kGroup, Dispatch<BITS>::template layer_h, L, s, phases)
+}
+
+}  // namespace dev
+}  // namespace fmoe
