@@ -1,4 +1,4 @@
-"""Benchmark: µs per MoE decode layer (top-4 + shared expert, 4-bit, B=1) and weight GB/s.
+"""Benchmark: µs per MoE decode layer (top-4 + shared, 4-bit, B=1) and weight GB/s.
 
 Workload: a stack of MoE layers resident in HBM, each with 512 routed experts + 1
 shared expert (hidden 4096, inter 1024, group-64 4-bit codes with bf16 scale and
@@ -10,6 +10,15 @@ experts' gate/up + SwiGLU, down + weighted combine + residual + sigmoid-gated
 shared expert, RMS scaling. Inputs are synthetic and seeded (no trained weights
 exist here): codes ~ U{0..15}, scale ~ U(0.002, 0.02), bias = -8 scale (1 + U(-0.1, 0.1)),
 router and gate vector ~ N(0, 0.02), fresh hidden states ~ N(0, 1) per step.
+
+Besides the timed stack, the JSON line carries
+  roofline      the dominant kernel's algorithmic bytes per launch over its
+                average duration, timed with HIP events on its own stream;
+  cpu_baseline  the fp64 CPU oracle timed on one MoE layer of the same workload;
+  parity        layer 0 of the first step checked against that oracle.
+
+`--calibrate-copy` instead runs a plain 1 GiB device copy (for scaling the HBM
+byte counters of a profiler run) and prints its size.
 
 Prints one JSON line. With --gpus N > 1 it exits: this build runs on one GPU.
 """
@@ -25,6 +34,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+PHASE_NAMES = {1: "router + shared gate/up (k_phase1)", 2: "routing + routed gate/up + shared down (k_phase2)",
+               4: "routed down + combine (k_phase3)"}
 
 
 def log(*a):
@@ -45,9 +56,11 @@ def parse():
     p.add_argument("--topk", type=int, default=4)
     p.add_argument("--seed", type=int, default=42)
     p.add_argument("--no-graph", action="store_true")
+    p.add_argument("--kernel-reps", type=int, default=5, help="passes over the layers when timing one kernel")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--verify", type=int, default=1, help="tokens checked against the oracle after timing")
+    p.add_argument("--no-verify", action="store_true")
+    p.add_argument("--calibrate-copy", action="store_true")
     return p.parse_args()
 
 
@@ -70,12 +83,57 @@ class Filler:
         self.qem.fmoe_pack_expert_device(bits, H, I, self.codes, self.scale, self.bias, blob_out)
 
 
+def calibrate_copy():
+    """A plain device-to-device copy of known size, for the profiler's byte counters."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.int32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.bitwise_not(src, out=dst)   # one elementwise kernel: reads n bytes, writes n bytes
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "elementwise int32 bitwise_not, 1 GiB in, 1 GiB out",
+                      "bytes_read": n, "bytes_written": n}), flush=True)
+
+
+def phase_bytes(phase, d_routed, eb, gub, E, H, I, K, bits):
+    """Algorithmic bytes one launch of a layer kernel moves (B=1): the weights it must
+    stream once plus its activation reads and writes."""
+    down = eb - gub
+    if phase == 1:   # router rows + gate vector + shared gate/up; x in; logits, sigma, h_shared out
+        return E * H * 4 + H * 4 + gub + H * 4 + E * 4 + 4 + I * 4
+    if phase == 2:   # distinct routed gate/up + shared down; x, logits, h_shared in; h_routed, d_shared out
+        return d_routed * gub + down + H * 4 + E * 4 + I * 4 + K * I * 4 + H * 4
+    if phase == 4:   # distinct routed down; h_routed, d_shared, residual in; out (+ routing) out
+        return d_routed * down + K * I * 4 + H * 4 + H * 4 + H * 4
+    raise ValueError(phase)
+
+
+def cpu_baseline(a, synth, oracle, R0, g0, h0, budget_s):
+    """Time the fp64 oracle on MoE layer 0 for one token; also returns its output for parity."""
+    H, I, E, K, bits = a.hidden, a.inter, a.experts, a.topk, a.bits
+    x0 = oracle.rms_scale(h0)
+    idx, _, _ = oracle.route(oracle.router_logits(R0, x0), K)
+    experts = {int(e): synth.expert(a.seed, 0, int(e), bits, H, I) for e in idx}
+    shared = synth.expert(a.seed, 0, synth.SHARED_EXPERT, bits, H, I)
+    reps, t_total, res = 0, 0.0, None
+    while reps == 0 or t_total < budget_s:
+        t0 = time.perf_counter()
+        res = oracle.moe_layer(R0, g0, experts, shared, x0, h0, K)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    return t_total / reps, reps, t_total, res
+
+
 def main():
     a = parse()
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
                           "requested_gpus": a.gpus}))
         sys.exit(2)
+    if a.calibrate_copy:
+        calibrate_copy()
+        return
     import numpy as np
     import torch
 
@@ -85,6 +143,7 @@ def main():
     dev = torch.device("cuda:0")
     H, I, E, K, B, bits = a.hidden, a.inter, a.experts, a.topk, a.batch, a.bits
     eb = qem.fmoe_expert_bytes(bits, H, I)
+    gub = eb - H * (I // 64) * (bits * 8 + 4)
     layer_bytes = (E + 1) * eb + E * H * 4 + H * 4
     free, total = torch.cuda.mem_get_info()
     n_layers = min(a.layers, int((free - 8 * 2 ** 30) // layer_bytes))
@@ -111,7 +170,8 @@ def main():
     log(f"bench: fill done in {time.time() - t0:.1f} s")
 
     steps = a.warmup + a.steps
-    h0_all = torch.from_numpy(np.stack([synth.activations(a.seed, synth.T_H0, s, B, H) for s in range(steps)])).to(dev)
+    h0_host = np.stack([synth.activations(a.seed, synth.T_H0, s, B, H) for s in range(steps)])
+    h0_all = torch.from_numpy(h0_host).to(dev)
     c_layers = (qem.fmoe_layer * n_layers)(*[L.c() for L in layers])
     h_in = torch.empty((B, H), dtype=torch.float32, device=dev)
     h_out = torch.empty((B, H), dtype=torch.float32, device=dev)
@@ -144,12 +204,12 @@ def main():
         else:
             step_call()
 
+    log("bench: timing the stack")
     for s in range(a.warmup):
         run(s)
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    routed = []
     ev0.record()
     for s in range(a.warmup, steps):
         run(s)
@@ -170,8 +230,84 @@ def main():
     w_bytes_layer = (d_mean + 1) * eb + E * H * 4 + H * 4
     act_bytes_layer = 3 * B * H * 4
     weight_gbps = w_bytes_layer / (us_layer * 1e3)
+
+    # ---- per-kernel durations (HIP events on the launching stream), B=1 layers
+    roofline, kernels = None, {}
+    if B == 1:
+        log("bench: timing each layer kernel")
+        kstream = torch.cuda.Stream()
+        xs = torch.from_numpy(np.stack([synth.activations(a.seed, synth.T_X, l, 1, H)[0]
+                                        for l in range(n_layers)])).to(dev)
+        outs = torch.empty((n_layers, H), dtype=torch.float32, device=dev)
+        lws_bytes = qem.fmoe_workspace_bytes(layers[0], 1)
+        lws = torch.empty((n_layers, (lws_bytes + 255) // 256 * 256), dtype=torch.uint8, device=dev)
+        kidx = torch.empty((n_layers, K), dtype=torch.int32, device=dev)
+        with torch.cuda.stream(kstream):
+            for l in range(n_layers):   # full layers first: every kernel's inputs are then in place
+                qem.fmoe_moe_layer_phases(layers[l], xs[l:l + 1], xs[l:l + 1], outs[l:l + 1], 7, lws[l],
+                                          topk_idx=kidx[l:l + 1], stream=kstream, c_layer=c_layers[l])
+        kstream.synchronize()
+        kd = float(np.mean([len(set(r.tolist())) for r in kidx.cpu().numpy()]))
+        for ph in (1, 2, 4):
+            # n_layers launches of one kernel, captured once and replayed on kstream
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=kstream):
+                for l in range(n_layers):
+                    qem.fmoe_moe_layer_phases(layers[l], xs[l:l + 1], xs[l:l + 1], outs[l:l + 1], ph, lws[l],
+                                              c_layer=c_layers[l])
+            with torch.cuda.stream(kstream):
+                g.replay()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(kstream)
+                for _ in range(a.kernel_reps):
+                    g.replay()
+                e1.record(kstream)
+            kstream.synchronize()
+            del g
+            us = e0.elapsed_time(e1) * 1000.0 / (a.kernel_reps * n_layers)
+            nbytes = phase_bytes(ph, kd, eb, gub, E, H, I, K, bits)
+            kernels[PHASE_NAMES[ph]] = {"avg_us": round(us, 3), "algorithmic_bytes": int(nbytes),
+                                        "GBps": round(nbytes / (us * 1e3), 1)}
+        dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
+        kk = kernels[dom]
+        roofline = {"bound": "hbm", "achieved": kk["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(kk["GBps"] / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": dom,
+                    "avg_us": kk["avg_us"], "algorithmic_bytes_per_launch": kk["algorithmic_bytes"]}
+        del lws, outs, xs
+
+    # ---- parity of layer 0, step 0 against the oracle, and the oracle's CPU time
+    parity, cpu = None, None
+    need_oracle = B == 1 and (not a.no_verify or not a.no_cpu_baseline)
+    if need_oracle:
+        import oracle
+        R0 = synth.router(a.seed, 0, E, H)
+        g0 = synth.shared_gate(a.seed, 0, H)
+        h0 = h0_host[0][0].astype(np.float64)
+        budget = 0.0 if a.no_cpu_baseline else a.cpu_seconds
+        log(f"bench: oracle on layer 0 ({budget:.0f} s budget)")
+        t_layer, reps, t_total, (o_out, o_idx, o_w, _) = cpu_baseline(a, synth, oracle, R0, g0, h0, budget)
+        if not a.no_cpu_baseline:
+            cpu = {"value": round(t_layer * 1e6, 1), "unit": "us/layer", "cores": oracle.get_threads(),
+                   "kind": "oracle",
+                   "sample": f"fp64 oracle, one MoE layer (512-expert router, softmax top-{K}, {K} routed + shared "
+                             f"SwiGLU experts, q{bits}) for one token, run {reps}x in {t_total:.1f} s; "
+                             f"expert generation excluded"}
+        if not a.no_verify:
+            h_all = torch.empty((n_layers, 1, H), dtype=torch.float32, device=dev)
+            h_in.copy_(h0_all[0])
+            qem.fmoe_moe_stack(layers, h_in, h_out=h_out, h_all=h_all, topk_idx=idx, ws=ws, c_layers=c_layers)
+            torch.cuda.synchronize()
+            y = h_all[0, 0].cpu().numpy().astype(np.float64)
+            d = y - o_out
+            parity = {"layer": 0, "step": 0,
+                      "routing_exact": bool(list(idx[0, 0].cpu().numpy()) == list(o_idx)),
+                      "max_rel": float(np.max(np.abs(d)) / np.max(np.abs(o_out))),
+                      "l2_rel": float(np.linalg.norm(d) / np.linalg.norm(o_out))}
+            parity["pass"] = bool(parity["routing_exact"] and parity["max_rel"] <= 2e-3 and parity["l2_rel"] <= 1e-4)
+
     rec = {
-        "metric": "us per MoE layer (top-4 + shared, 4-bit, B=1) and weight GB/s vs HBM peak",
+        "metric": "µs per MoE layer (top-4 + shared, 4-bit, B=1) and weight GB/s vs HBM peak",
         "value": round(us_layer, 4),
         "unit": "us/layer",
         "n_gpus": 1,
@@ -181,16 +317,21 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u4 codes x fp32" if bits == 4 else "u2 codes x fp32",
+        "dtype": f"u{bits} codes, bf16 scale/bias, fp32 math",
         "data": "synthetic (seeded; random-init weights of the workload's shapes)",
-        "config": {"workload": f"moe_stack_q{bits}", "layers": n_layers, "batch": B, "experts": E,
-                   "top_k": K, "hidden": H, "inter": I, "group": 64, "graph": graph is not None},
+        "config": {"workload": f"moe_stack_q{bits}_B{B}", "layers": n_layers, "batch": B, "experts": E,
+                   "top_k": K, "hidden": H, "inter": I, "group": 64, "graph": graph is not None,
+                   "seed": a.seed},
         "weight_GBps": round(weight_gbps, 1),
         "frac_hbm_peak": round(weight_gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_layer": int(w_bytes_layer + act_bytes_layer),
         "distinct_routed_experts_per_layer": round(d_mean, 3),
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+        "parity": parity,
     }
-    print(json.dumps(rec), flush=True)
+    print(json.dumps(rec, ensure_ascii=False), flush=True)
 
 
 if __name__ == "__main__":

@@ -424,15 +424,18 @@ __device__ __forceinline__ void wave_topk_lds(const float *lg, int E, int K, int
 }
 
 // Block-wide top-K: one wavefront computes it from the logits in LDS and
-// publishes it through LDS (sidx, sw); contains one barrier; results uniform in
-// every thread. Workgroup b uses wavefront b % 4, so that the workgroups sharing
-// a CU do not all compute it on the same SIMD.
-__device__ __forceinline__ void block_topk(const float *lg, int E, int K, int *sidx, float *sw, float *cand,
-                                           int *idx, float *w) {
+// publishes it through LDS (sidx, sw); contains one barrier, after which every
+// thread reads the result from sidx / sw. (Results are not copied back into
+// per-thread arrays: indexing those by a runtime slot would put them in scratch
+// memory.) Workgroup b uses wavefront b % 4, so that the workgroups sharing a CU
+// do not all compute it on the same SIMD.
+__device__ __forceinline__ void block_topk(const float *lg, int E, int K, int *sidx, float *sw, float *cand) {
   if (wave_in_block() == (int)(blockIdx.x % kWavesPerBlock)) {
     // the rest of the workgroup waits on this wavefront: let it win the SIMD's
     // issue arbitration against co-resident wavefronts of other workgroups
     __builtin_amdgcn_s_setprio(3);
+    int idx[kMaxTopK];
+    float w[kMaxTopK];
     wave_topk_lds(lg, E, K, idx, w, cand);
     __builtin_amdgcn_s_setprio(0);
     const int lane = lane_id();
@@ -444,28 +447,6 @@ __device__ __forceinline__ void block_topk(const float *lg, int E, int K, int *s
       }
   }
   __syncthreads();
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    idx[j] = sidx[j];
-    w[j] = sw[j];
-  }
-}
-
-template <int N>
-__device__ __forceinline__ int pick(const int (&a)[N], int j) {
-  int r = a[0];
-#pragma unroll
-  for (int t = 1; t < N; ++t)
-    if (t == j) r = a[t];
-  return r;
-}
-template <int N>
-__device__ __forceinline__ float pick(const float (&a)[N], int j) {
-  float r = a[0];
-#pragma unroll
-  for (int t = 1; t < N; ++t)
-    if (t == j) r = a[t];
-  return r;
 }
 
 // ------------------------------------------------------------------ standalone kernels
@@ -673,16 +654,14 @@ __global__ __launch_bounds__(kBlock) void k_phase2(const Phase2Args a) {
       stage_vec<NGH, false>(a.x, xl, part);
     __syncthreads();
     trace_mark(a.trace, 1);
-    int idx[kMaxTopK];
-    float w[kMaxTopK];
-    block_topk(lg, a.E, a.K, sidx, sw, cand, idx, w);
+    block_topk(lg, a.E, a.K, sidx, sw, cand);
     trace_mark(a.trace, 2);
     const int wv = blockIdx.x * kWavesPerBlock + wave_in_block();
     const int slot = min(wv / a.waves_per_slot, a.K - 1);
     const int pair0 = (wv % a.waves_per_slot) * kP2GateUpIters * (kWave / NGH);
     const bool active = wv < a.waves_per_slot * a.K;
     PairLoads<BITS, NGH, kP2GateUpIters> P;
-    if (active) P.issue(a.bank + (size_t)pick(idx, slot) * a.stride, pair0);
+    if (active) P.issue(a.bank + (size_t)sidx[slot] * a.stride, pair0);
     if (a.pf_n3 > 0) {
       // phase-3 workgroup c = b mod pf_n3 (same XCD when pf_n3 % 8 == 0); the
       // routed workgroups that map to c split its K experts between them
@@ -690,12 +669,12 @@ __global__ __launch_bounds__(kBlock) void k_phase2(const Phase2Args a) {
       const int parts = (a.n_routed_blocks + a.pf_n3 - 1) / a.pf_n3;
       const int part = blockIdx.x / a.pf_n3;
       for (int k = part; k < a.K; k += parts)
-        block_prefetch_in(a.bank + (size_t)pick(idx, k) * a.stride + a.gu_bytes, (size_t)c * a.pf_down_bytes,
+        block_prefetch_in(a.bank + (size_t)sidx[k] * a.stride + a.gu_bytes, (size_t)c * a.pf_down_bytes,
                           a.pf_down_bytes, a.pf_down_total, dump);
     }
     if (wv == 0 && lane < a.K) {
-      const int sel = pick(idx, lane);
-      const float ws = pick(w, lane);
+      const int sel = sidx[lane];
+      const float ws = sw[lane];
       a.ws_idx[lane] = sel;
       a.ws_w[lane] = ws;
       if (a.out_idx) a.out_idx[lane] = sel;
