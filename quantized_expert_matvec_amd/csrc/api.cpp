@@ -69,11 +69,9 @@ fmoe_status matvec_common(const fmoe_qmat *W, const float *x, float *y, void *st
 
 // Enqueue one layer for n_tokens tokens (arguments already validated).
 // rms_eps >= 0: the layer input is rms_scale(x, rms_eps), computed inside the layer's kernels.
-// `next` is the layer whose kernels follow this one on the stream (null: none);
-// its first kernel's weights are prefetched into L2 while this layer finishes.
 fmoe_status layer_enqueue(const fmoe_layer *L, int B, const float *x, float rms_eps, const float *residual,
-                          float *out, int32_t *topk_idx, float *topk_w, uint8_t *ws, const fmoe_layer *next,
-                          hipStream_t s, int phases = 7) {
+                          float *out, int32_t *topk_idx, float *topk_w, uint8_t *ws, hipStream_t s,
+                          int phases = 7) {
   const LayerWs w = layer_ws(B, L->n_experts, L->top_k, L->hidden, L->inter);
   const int H = L->hidden, I = L->inter, E = L->n_experts, K = L->top_k;
   for (int t = 0; t < B; ++t) {
@@ -102,14 +100,6 @@ fmoe_status layer_enqueue(const fmoe_layer *L, int B, const float *x, float rms_
     a.h_shared = (float *)(ws + w.h_shared) + (size_t)t * I;
     a.h_routed = (float *)(ws + w.h_routed) + (size_t)t * K * I;
     a.d_shared = (float *)(ws + w.d_shared) + (size_t)t * H;
-    a.prefetch_mask = 0;  // cross-kernel L2 prefetch: measured no gain (streamed weights evict it)
-    // the next token of this layer reads the same router and shared expert
-    const fmoe_layer *nl = t + 1 < B ? L : next;
-    if (nl) {
-      a.next_router = nl->router;
-      a.next_gvec = nl->shared_gate;
-      a.next_shared = (const uint8_t *)nl->shared;
-    }
     if (launch_layer(a, s, phases) != hipSuccess) return FMOE_ERR_LAUNCH;
   }
   return FMOE_OK;
@@ -289,8 +279,8 @@ fmoe_status fmoe_moe_layer_phases(const fmoe_layer *L, int n_tokens, const float
       overlap(residual, ab, ws, need) || overlap(topk_idx, kb, ws, need) || overlap(topk_w, kb, ws, need) ||
       overlap(topk_idx, kb, out, ab) || overlap(topk_w, kb, out, ab) || overlap(topk_idx, kb, topk_w, kb))
     return FMOE_ERR_ALIAS;
-  return layer_enqueue(L, n_tokens, x, -1.f, residual, out, topk_idx, topk_w, (uint8_t *)ws, nullptr,
-                       as_stream(stream), phases);
+  return layer_enqueue(L, n_tokens, x, -1.f, residual, out, topk_idx, topk_w, (uint8_t *)ws, as_stream(stream),
+                       phases);
 }
 
 fmoe_status fmoe_rms_scale(const float *h, float *x, int n_tokens, int hidden, float eps, void *stream) {
@@ -344,8 +334,7 @@ fmoe_status fmoe_moe_stack(const fmoe_layer *layers, int n_layers, int n_tokens,
     else
       nxt = ping[l & 1];
     fmoe_status st = layer_enqueue(&layers[l], B, cur, eps, cur, nxt, topk_idx ? topk_idx + (size_t)l * B * K : nullptr,
-                                   topk_w ? topk_w + (size_t)l * B * K : nullptr, w + sw.layer,
-                                   l + 1 < n_layers ? &layers[l + 1] : nullptr, s);
+                                   topk_w ? topk_w + (size_t)l * B * K : nullptr, w + sw.layer, s);
     if (st != FMOE_OK) return st;
     cur = nxt;
   }

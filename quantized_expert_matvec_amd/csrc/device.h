@@ -219,71 +219,6 @@ __device__ __forceinline__ void rms_scale_slice(XSlice &xs, float eps) {
   xs.sum = tree_sum64(xs.v);
 }
 
-// One step of a wavefront argmax over (value, index): larger value wins, the lower
-// index on a tie. Rows outside ROWS keep their own pair.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ void argmax_step(float &v, int &i) {
-  const float ov = dpp_f<CTRL, ROWS>(v, -INFINITY);
-  const int oi = dpp_i<CTRL, ROWS>(i, 0x7FFFFFFF);
-  const bool take = ov > v || (ov == v && oi < i);
-  v = take ? ov : v;
-  i = take ? oi : i;
-}
-
-// Top-K of E logits, computed redundantly by a whole wavefront (no barrier):
-// K rounds of "largest remaining value, lower index on a tie", then the
-// renormalised softmax weights of the chosen K, w_j = exp(l_j - l_0) / sum.
-// (Renormalising over the chosen K cancels the full softmax denominator.)
-// Results are wavefront-uniform. NaN logits count as -inf.
-__device__ __forceinline__ void wave_topk(const float *__restrict__ logits, int E, int K, int *idx, float *w) {
-  const int lane = lane_id();
-  float v[16];
-#pragma unroll
-  for (int m = 0; m < 16; ++m) {
-    const int e = lane + 64 * m;
-    const float t = logits[min(e, E - 1)];
-    v[m] = (e < E && t == t) ? t : -INFINITY;
-  }
-  uint32_t taken = 0;
-  float lv[kMaxTopK];
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    idx[j] = 0;
-    lv[j] = 0.f;
-  }
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    if (j >= K) break;
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const int e = lane + 64 * m;
-      const bool ok = e < E && !((taken >> m) & 1u) && (v[m] > bv || (v[m] == bv && e < bi));
-      bv = ok ? v[m] : bv;
-      bi = ok ? e : bi;
-    }
-    argmax_step<0xB1, 0xF>(bv, bi);
-    argmax_step<0x4E, 0xF>(bv, bi);
-    argmax_step<0x141, 0xF>(bv, bi);
-    argmax_step<0x140, 0xF>(bv, bi);
-    argmax_step<0x142, 0xA>(bv, bi);
-    argmax_step<0x143, 0xC>(bv, bi);
-    bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 63));
-    bi = __builtin_amdgcn_readlane(bi, 63);
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    idx[j] = bi;
-    lv[j] = bv;
-  }
-  float sum = 0.f;
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    w[j] = j < K ? expf(lv[j] - lv[0]) : 0.f;
-    sum += w[j];
-  }
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) w[j] = w[j] / sum;
-}
 
 inline int blocks_for_waves(long waves) { return (int)((waves + (kBlock / kWave) - 1) / (kBlock / kWave)); }
 

@@ -38,17 +38,9 @@ struct LayerArgs {
   float *h_shared;           // [I]
   float *h_routed;           // [K][I]
   float *d_shared;           // [H]
-  // next layer of a stack (null when there is none): its router rows, gate
-  // vector and shared expert gate/up are prefetched into L2 while this layer ends
-  const float *next_router;
-  const float *next_gvec;
-  const uint8_t *next_shared;
   // optional per-workgroup timestamps (device, 100 MHz clock) for profiling:
   // [phase][workgroup][8]; null in normal use
   uint64_t *trace;
-  // L2 prefetches to issue: bit 0 shared-expert down (phase 1), bit 1 routed
-  // down (phase 2), bit 2 the next layer's phase-1 weights (phase 3)
-  int prefetch_mask;
 };
 
 // Router + sigmoid gate + shared gate/up; routing + routed gate/up + shared down;

@@ -108,36 +108,6 @@ __device__ __forceinline__ void read_slice(const float *lds, int g, float scale,
   xs.sum = tree_sum64(xs.v);
 }
 
-// ------------------------------------------------------------------ L2 prefetch
-//
-// Workgroup b of a launch runs on XCD b % 8, and L2 contents survive kernel
-// boundaries. A kernel whose own loads leave the memory system idle can
-// therefore fetch the next kernel's known weights into the L2 of the XCD whose
-// workgroups will read them: workgroup b prefetches for the next kernel's
-// workgroups c with c % 8 == b % 8. The prefetch uses load-to-LDS requests
-// (no register results; the LDS words written are a scratch area never read)
-// and is drained before the wavefront ends.
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
-constexpr int kDumpU4 = kBlock;  // 1 KB of LDS scratch per wavefront
-
-// [p, p + bytes), both multiples of 16, into this workgroup's L2.
-__device__ __forceinline__ void block_prefetch(const void *p, size_t bytes, uint4 *dump) {
-  lds_void_t *dst = (lds_void_t *)(dump + wave_in_block() * kWave);
-  const uint8_t *b = (const uint8_t *)p;
-  for (size_t off = (size_t)threadIdx.x * 16; off < bytes; off += (size_t)kBlock * 16)
-    __builtin_amdgcn_global_load_lds((glb_void_t *)(b + off), dst, 16, 0, 0);
-}
-
-// The part of [off, off + bytes) that lies inside a region of `total` bytes.
-__device__ __forceinline__ void block_prefetch_in(const uint8_t *base, size_t off, size_t bytes, size_t total,
-                                                  uint4 *dump) {
-  if (off >= total) return;
-  block_prefetch(base + off, bytes < total - off ? bytes : total - off, dump);
-}
-
-__device__ __forceinline__ void prefetch_drain() { __builtin_amdgcn_s_waitcnt(0); }
-
 // Profiling hook: thread 0 of a workgroup records the device clock at a point.
 constexpr int kTraceSlots = 8;
 constexpr int kTraceBlocks = 4096;  // workgroups recorded per phase
@@ -211,193 +181,68 @@ struct PairLoads {
   }
 };
 
-// Top-K of E logits held in LDS by one wavefront: K rounds of "largest remaining
-// value, lower index on a tie". Each lane keeps the best (value, index) of its
-// own remaining elements; a round takes the wavefront maximum of the values and
-// then the minimum index holding it (both by DPP), and only the winning lane
-// rescans its elements. Then the renormalised softmax weights of the chosen K,
-// w_j = exp(l_j - l_0) / sum (renormalising over the chosen K cancels the full
-// softmax denominator). Results are wavefront-uniform. NaN logits count as -inf.
-template <int VPL>
-__device__ __forceinline__ void wave_topk_lds_n(const float *lg, int E, int K, int *idx, float *w) {
-  const int lane = lane_id();
-  float v[VPL];
-#pragma unroll
-  for (int m = 0; m < VPL; ++m) {
-    const int e = lane + 64 * m;
-    const float t = e < E ? lg[e] : -INFINITY;
-    v[m] = t == t ? t : -INFINITY;
-  }
-  uint32_t taken = 0;  // bit m: element lane + 64m already chosen
-  // lane best among its available elements: largest value, smallest index on a
-  // tie; a lane with none left reports (-inf, INT_MAX)
-  auto lane_best = [&](float &bv, int &bi) {
-    bv = -INFINITY;
-    bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int m = VPL - 1; m >= 0; --m) {
-      const int e = lane + 64 * m;
-      const bool better = e < E && !((taken >> m) & 1u) && v[m] >= bv;  // descending m: smallest m wins ties
-      bv = better ? v[m] : bv;
-      bi = better ? e : bi;
-    }
-  };
-  float bv;
-  int bi;
-  lane_best(bv, bi);
-  float lv[kMaxTopK];
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    idx[j] = 0;
-    lv[j] = 0.f;
-  }
-  for (int j = 0; j < K; ++j) {
-    float gm = bv;
-    gm = fmaxf(gm, dpp_f<0xB1, 0xF>(gm, -INFINITY));
-    gm = fmaxf(gm, dpp_f<0x4E, 0xF>(gm, -INFINITY));
-    gm = fmaxf(gm, dpp_f<0x141, 0xF>(gm, -INFINITY));
-    gm = fmaxf(gm, dpp_f<0x140, 0xF>(gm, -INFINITY));
-    gm = fmaxf(gm, dpp_f<0x142, 0xA>(gm, -INFINITY));
-    gm = fmaxf(gm, dpp_f<0x143, 0xC>(gm, -INFINITY));
-    const float gmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gm), 63));
-    int li = bv == gmax ? bi : 0x7FFFFFFF;
-    li = min(li, dpp_i<0xB1, 0xF>(li, 0x7FFFFFFF));
-    li = min(li, dpp_i<0x4E, 0xF>(li, 0x7FFFFFFF));
-    li = min(li, dpp_i<0x141, 0xF>(li, 0x7FFFFFFF));
-    li = min(li, dpp_i<0x140, 0xF>(li, 0x7FFFFFFF));
-    li = min(li, dpp_i<0x142, 0xA>(li, 0x7FFFFFFF));
-    li = min(li, dpp_i<0x143, 0xC>(li, 0x7FFFFFFF));
-    const int e = __builtin_amdgcn_readlane(li, 63);
-#pragma unroll
-    for (int q = 0; q < kMaxTopK; ++q)
-      if (q == j) {
-        idx[q] = e;
-        lv[q] = gmax;
-      }
-    if ((e & 63) == lane) {  // the winning lane marks the element taken and rescans
-      taken |= 1u << (e >> 6);
-      lane_best(bv, bi);
-    }
-  }
-  // weights: only the K chosen entries; one reciprocal of the sum
-  float sum = 0.f;
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    w[j] = 0.f;
-    if (j < K) {
-      w[j] = __expf(lv[j] - lv[0]);
-      sum += w[j];
-    }
-  }
-  const float inv = 1.f / sum;
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) w[j] *= inv;
+// Order-preserving integer key of a float: a > b (as floats) <=> key(a) > key(b)
+// (as signed integers). key(-inf) = 0x807FFFFF; every key is above INT_MIN.
+__device__ __forceinline__ int order_key(float f) {
+  const int b = __float_as_int(f);
+  return b >= 0 ? b : b ^ 0x7FFFFFFF;
 }
-
-// Wavefront argmax under (value descending, index ascending) over one (v, e) pair
-// per lane; lanes with ok == false do not take part. Returns (value, index),
-// wavefront-uniform.
-__device__ __forceinline__ void wave_argmax(float v, int e, bool ok, float &gmax, int &gidx) {
-  float gm = ok ? v : -INFINITY;
-  gm = fmaxf(gm, dpp_f<0xB1, 0xF>(gm, -INFINITY));
-  gm = fmaxf(gm, dpp_f<0x4E, 0xF>(gm, -INFINITY));
-  gm = fmaxf(gm, dpp_f<0x141, 0xF>(gm, -INFINITY));
-  gm = fmaxf(gm, dpp_f<0x140, 0xF>(gm, -INFINITY));
-  gm = fmaxf(gm, dpp_f<0x142, 0xA>(gm, -INFINITY));
-  gm = fmaxf(gm, dpp_f<0x143, 0xC>(gm, -INFINITY));
-  gmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gm), 63));
-  int li = (ok && v == gmax) ? e : 0x7FFFFFFF;
-  li = min(li, dpp_i<0xB1, 0xF>(li, 0x7FFFFFFF));
-  li = min(li, dpp_i<0x4E, 0xF>(li, 0x7FFFFFFF));
-  li = min(li, dpp_i<0x141, 0xF>(li, 0x7FFFFFFF));
-  li = min(li, dpp_i<0x140, 0xF>(li, 0x7FFFFFFF));
-  li = min(li, dpp_i<0x142, 0xA>(li, 0x7FFFFFFF));
-  li = min(li, dpp_i<0x143, 0xC>(li, 0x7FFFFFFF));
-  gidx = __builtin_amdgcn_readlane(li, 63);
-}
+__device__ __forceinline__ float key_value(int k) { return __int_as_float(k >= 0 ? k : k ^ 0x7FFFFFFF); }
 
 // Top-K of E logits held in LDS, by one wavefront, exactly under the order
 // (value descending, index ascending); element e sits in lane e % 64, slot e / 64.
-//  1. each lane finds its best element;
-//  2. K rounds pick the K lanes whose best elements rank highest -- every element
-//     of the top K lies in one of them (if an element's lane were not picked, the
-//     K picked lanes' best elements would all outrank it);
-//  3. those lanes copy their elements to LDS (`cand`, K*VPL floats), one
-//     candidate per lane is read back, and K rounds of argmax select the top K.
-// Then the renormalised softmax weights of the chosen K, w_j = exp(l_j - l_0) /
-// sum (renormalising over the chosen K cancels the full softmax denominator).
-// Results are wavefront-uniform. NaN logits count as -inf.
+// Values are compared as order-preserving integer keys (NaN logits count as
+// -inf). K rounds of: per-lane maximum key, wavefront maximum (DPP), then the
+// lowest index holding it from one ballot per slot (index = lane + 64 * slot, so
+// the first slot with a hit and its lowest lane give the lowest index); the
+// chosen element's key becomes INT_MIN, below every real key, as are the padding
+// slots (e >= E). Then the renormalised softmax weights of the chosen K,
+// w_j = exp(l_j - l_0) / sum (renormalising over the chosen K cancels the full
+// softmax denominator). Results are wavefront-uniform.
 template <int VPL>
-__device__ __forceinline__ void wave_topk_cand(const float *lg, int E, int K, int *idx, float *w, float *cand) {
+__device__ __forceinline__ void wave_topk_ballot(const float *lg, int E, int K, int *idx, float *w) {
+  constexpr int kGone = (int)0x80000000;
   const int lane = lane_id();
-  float v[VPL];
+  int key[VPL];
 #pragma unroll
   for (int m = 0; m < VPL; ++m) {
     const int e = lane + 64 * m;
-    const float t = e < E ? lg[e] : -INFINITY;
-    v[m] = t == t ? t : -INFINITY;
-  }
-  float bv = -INFINITY;
-  int bi = 0x7FFFFFFF;
-#pragma unroll
-  for (int m = VPL - 1; m >= 0; --m) {
-    const bool better = lane + 64 * m < E && v[m] >= bv;  // descending m: smallest index wins ties
-    bv = better ? v[m] : bv;
-    bi = better ? lane + 64 * m : bi;
-  }
-  // 2. the K lanes with the highest-ranked best elements
-  bool picked = false;
-  int lanes[kMaxTopK];
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) lanes[j] = 0;
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    if (j >= K) break;
-    float gmax;
-    int ge;
-    wave_argmax(bv, bi, !picked && bi != 0x7FFFFFFF, gmax, ge);
-    lanes[j] = ge & 63;
-    picked = picked || lane == lanes[j];
-  }
-  // 3. candidates through LDS: candidate t = element (lanes[t / VPL], slot t % VPL)
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    if (j >= K) break;
-    if (lane == lanes[j]) {
-#pragma unroll
-      for (int m = 0; m < VPL; ++m) cand[j * VPL + m] = v[m];
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the copies are visible to this wavefront
-  float cv;
-  int ce;
-  bool ok;
-  {  // requires K * VPL <= 64: one candidate per lane
-    const int t = lane;
-    int src = lanes[0];
-#pragma unroll
-    for (int j = 1; j < kMaxTopK; ++j)
-      if (j == t / VPL) src = lanes[j];
-    const int e = src + 64 * (t % VPL);
-    ok = t < K * VPL && e < E;
-    cv = ok ? cand[t] : -INFINITY;
-    ce = ok ? e : 0x7FFFFFFF;
+    const float t = lg[min(e, E - 1)];
+    key[m] = e < E ? order_key(t == t ? t : -INFINITY) : kGone;
   }
   float lv[kMaxTopK];
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) {
     idx[j] = 0;
     lv[j] = 0.f;
-  }
+    if (j < K) {
+      int t[VPL];
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    if (j >= K) break;
-    float gmax;
-    int ge;
-    wave_argmax(cv, ce, ok, gmax, ge);
-    idx[j] = ge;
-    lv[j] = gmax;
-    ok = ok && ce != ge;
+      for (int m = 0; m < VPL; ++m) t[m] = key[m];
+#pragma unroll
+      for (int s = VPL / 2; s >= 1; s /= 2)
+#pragma unroll
+        for (int m = 0; m < s; ++m) t[m] = max(t[m], t[m + s]);
+      int g = t[0];
+      g = max(g, dpp_i<0xB1, 0xF>(g, kGone));
+      g = max(g, dpp_i<0x4E, 0xF>(g, kGone));
+      g = max(g, dpp_i<0x141, 0xF>(g, kGone));
+      g = max(g, dpp_i<0x140, 0xF>(g, kGone));
+      g = max(g, dpp_i<0x142, 0xA>(g, kGone));
+      g = max(g, dpp_i<0x143, 0xC>(g, kGone));
+      g = __builtin_amdgcn_readlane(g, 63);
+      unsigned long long hit[VPL];
+#pragma unroll
+      for (int m = 0; m < VPL; ++m) hit[m] = __ballot(key[m] == g);
+      int sel = 0;
+#pragma unroll
+      for (int m = VPL - 1; m >= 0; --m)
+        sel = hit[m] ? 64 * m + (__ffsll((long long)hit[m]) - 1) : sel;
+      idx[j] = sel;
+      lv[j] = key_value(g);
+#pragma unroll
+      for (int m = 0; m < VPL; ++m) key[m] = (lane + 64 * m == sel) ? kGone : key[m];
+    }
   }
   float sum = 0.f;
 #pragma unroll
@@ -413,14 +258,11 @@ __device__ __forceinline__ void wave_topk_cand(const float *lg, int E, int K, in
   for (int j = 0; j < kMaxTopK; ++j) w[j] *= inv;
 }
 
-// cand: LDS scratch of kMaxTopK * 8 floats for this wavefront.
-__device__ __forceinline__ void wave_topk_lds(const float *lg, int E, int K, int *idx, float *w, float *cand) {
+__device__ __forceinline__ void wave_topk_lds(const float *lg, int E, int K, int *idx, float *w) {
   if (E <= 512)
-    wave_topk_cand<8>(lg, E, K, idx, w, cand);
-  else if (K <= 4)
-    wave_topk_cand<16>(lg, E, K, idx, w, cand);
+    wave_topk_ballot<8>(lg, E, K, idx, w);
   else
-    wave_topk_lds_n<16>(lg, E, K, idx, w);
+    wave_topk_ballot<16>(lg, E, K, idx, w);
 }
 
 // Block-wide top-K: one wavefront computes it from the logits in LDS and
@@ -429,14 +271,14 @@ __device__ __forceinline__ void wave_topk_lds(const float *lg, int E, int K, int
 // per-thread arrays: indexing those by a runtime slot would put them in scratch
 // memory.) Workgroup b uses wavefront b % 4, so that the workgroups sharing a CU
 // do not all compute it on the same SIMD.
-__device__ __forceinline__ void block_topk(const float *lg, int E, int K, int *sidx, float *sw, float *cand) {
+__device__ __forceinline__ void block_topk(const float *lg, int E, int K, int *sidx, float *sw) {
   if (wave_in_block() == (int)(blockIdx.x % kWavesPerBlock)) {
     // the rest of the workgroup waits on this wavefront: let it win the SIMD's
     // issue arbitration against co-resident wavefronts of other workgroups
     __builtin_amdgcn_s_setprio(3);
     int idx[kMaxTopK];
     float w[kMaxTopK];
-    wave_topk_lds(lg, E, K, idx, w, cand);
+    wave_topk_lds(lg, E, K, idx, w);
     __builtin_amdgcn_s_setprio(0);
     const int lane = lane_id();
 #pragma unroll
@@ -508,11 +350,6 @@ struct Phase1Args {
   int I;
   float *h_shared;
   int n_router_blocks;
-  // prefetch for phase 2's shared-down workgroups (null: none)
-  const uint8_t *pf_sdown;
-  size_t pf_sdown_bytes;  // bytes of down rows one phase-2 shared workgroup reads
-  size_t pf_sdown_total;  // bytes of the shared expert's down region
-  int pf_n2r, pf_n2s;     // phase 2: routed workgroups, shared-down workgroups
   uint64_t *trace;
 };
 
@@ -526,17 +363,9 @@ __global__ __launch_bounds__(kBlock) void k_phase1(const Phase1Args a) {
   constexpr int X4 = (NGH * 16 + kBlock - 1) / kBlock;
   __shared__ float xl[NGH * kXPad];
   __shared__ float part[kWavesPerBlock];
-  __shared__ uint4 dump[kDumpU4];
   const int lane = lane_id();
   const bool rms = a.rms_eps >= 0.f;
-  // phase 2's shared-down workgroup c = pf_n2r + s runs on XCD c % 8; s = b + k*grid keeps c % 8 == b % 8
-  // when pf_n2r and the grid are multiples of 8.
   trace_mark(a.trace, 0);
-  auto prefetch = [&]() {
-    if (!a.pf_sdown) return;
-    for (int s2 = blockIdx.x; s2 < a.pf_n2s; s2 += gridDim.x)
-      block_prefetch_in(a.pf_sdown, (size_t)s2 * a.pf_sdown_bytes, a.pf_sdown_bytes, a.pf_sdown_total, dump);
-  };
   if ((int)blockIdx.x < a.n_router_blocks) {
     const int n_rows = a.E + (a.gvec ? 1 : 0);
     const int row = blockIdx.x * kWavesPerBlock + wave_in_block();
@@ -554,7 +383,6 @@ __global__ __launch_bounds__(kBlock) void k_phase1(const Phase1Args a) {
       stage_store<X4, false>(xst, NGH * 16, xl, part);
     __syncthreads();
     trace_mark(a.trace, 1);
-    prefetch();
     const float inv = rms ? rms_inv(part, H, a.rms_eps) : 1.f;
     float acc = 0.f;
 #pragma unroll
@@ -588,7 +416,6 @@ __global__ __launch_bounds__(kBlock) void k_phase1(const Phase1Args a) {
       stage_store<X4, false>(xst, NGH * 16, xl, part);
     __syncthreads();
     trace_mark(a.trace, 1);
-    prefetch();
     if (pair0 < a.I) {
       XSlice xs;
       read_slice(xl, lane & (NGH - 1), rms ? rms_inv(part, H, a.rms_eps) : 1.f, xs);
@@ -596,8 +423,6 @@ __global__ __launch_bounds__(kBlock) void k_phase1(const Phase1Args a) {
     }
   }
   trace_mark(a.trace, 3);
-  prefetch_drain();
-  trace_mark(a.trace, 4);
 }
 
 struct Phase2Args {
@@ -621,11 +446,6 @@ struct Phase2Args {
   const float *h_shared;
   const float *sigma;
   float *d_shared;
-  // prefetch of the routed experts' down rows for phase 3 (pf_n3 = 0: none)
-  size_t gu_bytes;          // offset of the down region in an expert blob
-  size_t pf_down_bytes;     // bytes of down rows one phase-3 workgroup reads per expert
-  size_t pf_down_total;     // bytes of one expert's down region
-  int pf_n3;                // phase-3 workgroups
   uint64_t *trace;
 };
 
@@ -641,8 +461,6 @@ __global__ __launch_bounds__(kBlock) void k_phase2(const Phase2Args a) {
   __shared__ float part[kWavesPerBlock];
   __shared__ int sidx[kMaxTopK];
   __shared__ float sw[kMaxTopK];
-  __shared__ float cand[kMaxTopK * 8];
-  __shared__ uint4 dump[kDumpU4];
   const int lane = lane_id();
   trace_mark(a.trace, 0);
   if ((int)blockIdx.x < a.n_routed_blocks) {
@@ -654,7 +472,7 @@ __global__ __launch_bounds__(kBlock) void k_phase2(const Phase2Args a) {
       stage_vec<NGH, false>(a.x, xl, part);
     __syncthreads();
     trace_mark(a.trace, 1);
-    block_topk(lg, a.E, a.K, sidx, sw, cand);
+    block_topk(lg, a.E, a.K, sidx, sw);
     trace_mark(a.trace, 2);
     const int wv = blockIdx.x * kWavesPerBlock + wave_in_block();
     const int slot = min(wv / a.waves_per_slot, a.K - 1);
@@ -662,16 +480,6 @@ __global__ __launch_bounds__(kBlock) void k_phase2(const Phase2Args a) {
     const bool active = wv < a.waves_per_slot * a.K;
     PairLoads<BITS, NGH, kP2GateUpIters> P;
     if (active) P.issue(a.bank + (size_t)sidx[slot] * a.stride, pair0);
-    if (a.pf_n3 > 0) {
-      // phase-3 workgroup c = b mod pf_n3 (same XCD when pf_n3 % 8 == 0); the
-      // routed workgroups that map to c split its K experts between them
-      const int c = blockIdx.x % a.pf_n3;
-      const int parts = (a.n_routed_blocks + a.pf_n3 - 1) / a.pf_n3;
-      const int part = blockIdx.x / a.pf_n3;
-      for (int k = part; k < a.K; k += parts)
-        block_prefetch_in(a.bank + (size_t)sidx[k] * a.stride + a.gu_bytes, (size_t)c * a.pf_down_bytes,
-                          a.pf_down_bytes, a.pf_down_total, dump);
-    }
     if (wv == 0 && lane < a.K) {
       const int sel = sidx[lane];
       const float ws = sw[lane];
@@ -686,14 +494,13 @@ __global__ __launch_bounds__(kBlock) void k_phase2(const Phase2Args a) {
       P.finish(xs, a.h_routed + (size_t)slot * a.I, pair0);
     }
     trace_mark(a.trace, 3);
-    prefetch_drain();
-    trace_mark(a.trace, 4);
     return;
   }
   // shared expert down
   const int wv = (blockIdx.x - a.n_routed_blocks) * kWavesPerBlock + wave_in_block();
   const int row0 = wv * kP2DownIters * (kWave / NGI);
   constexpr int I4 = (NGI * 16 + kBlock - 1) / kBlock;
+  const float sig = *a.sigma;  // requested before the weights, used after them
   Staged<I4> hst;
   stage_load(a.h_shared, NGI * 16, hst);
   RowLoads<BITS, NGI, kP2DownIters> R;
@@ -704,9 +511,8 @@ __global__ __launch_bounds__(kBlock) void k_phase2(const Phase2Args a) {
   if (row0 >= a.H) return;
   XSlice xs;
   read_slice(xl, lane & (NGI - 1), 1.f, xs);
-  R.finish(xs, a.d_shared, a.H, row0, *a.sigma);
+  R.finish(xs, a.d_shared, a.H, row0, sig);
   trace_mark(a.trace, 3);
-  trace_mark(a.trace, 4);
 }
 
 struct Phase3Args {
@@ -720,14 +526,6 @@ struct Phase3Args {
   const float *d_shared;  // [H] or null
   const float *residual;
   float *out;
-  // prefetch of the next layer's phase-1 inputs (nrouter null: none)
-  const float *nrouter;
-  const float *ngvec;
-  const uint8_t *nshared_gu;
-  int nE, n1r, n1;          // next phase 1: experts, router workgroups, all workgroups
-  size_t n_row_bytes;       // bytes of one router row (hidden * 4)
-  size_t n_sh_bytes;        // bytes of gate/up pairs one phase-1 shared workgroup reads
-  size_t n_sh_total;        // bytes of the shared expert's gate/up region
   uint64_t *trace;
 };
 
@@ -745,12 +543,14 @@ __global__ __launch_bounds__(kBlock) void k_phase3(const Phase3Args a) {
   constexpr size_t RB = (size_t)NGI * gbytes<BITS>();
   constexpr bool STAGE = KPAD * NGI <= 128;
   __shared__ float hl[STAGE ? KPAD * NGI * kXPad : 1];
-  __shared__ uint4 dump[kDumpU4];
   trace_mark(a.trace, 0);
   const int lane = lane_id();
   const int sub = lane / SEG;
   const int row0 = wave_id() * kP3Iters * RPI;
-  const uint8_t *base[SPL];
+  // requested first, all independent: the routing of each slot, the residual
+  // and sigma * shared-down values of this lane's rows (used only after the dot
+  // products), and the routed h vectors
+  int sel[SPL];
   float wk[SPL];
   int grp[SPL], kk[SPL];
   bool act[SPL];
@@ -761,12 +561,22 @@ __global__ __launch_bounds__(kBlock) void k_phase3(const Phase3Args a) {
     grp[m] = slot % NGI;
     act[m] = k < a.K && row0 < a.H;
     kk[m] = k < a.K ? k : 0;
-    base[m] = a.bank + (size_t)a.idx[kk[m]] * a.stride + a.gu_bytes;
+    sel[m] = a.idx[kk[m]];
     wk[m] = k < a.K ? a.w[kk[m]] : 0.f;
+  }
+  float res[kP3Iters], dsh[kP3Iters];
+#pragma unroll
+  for (int i = 0; i < kP3Iters; ++i) {
+    const int row = min(row0 + i * RPI + sub, a.H - 1);
+    res[i] = a.residual[row];
+    dsh[i] = a.d_shared ? a.d_shared[row] : 0.f;
   }
   constexpr int H4 = STAGE ? (KPAD * NGI * 16 + kBlock - 1) / kBlock : 1;
   Staged<H4> hst;
   if constexpr (STAGE) stage_load(a.h_routed, a.K * a.I / 4, hst);
+  const uint8_t *base[SPL];
+#pragma unroll
+  for (int m = 0; m < SPL; ++m) base[m] = a.bank + (size_t)sel[m] * a.stride + a.gu_bytes;
   Chunk<BITS> c[kP3Iters][SPL];
   uint32_t sb[kP3Iters][SPL];
 #pragma unroll
@@ -777,36 +587,17 @@ __global__ __launch_bounds__(kBlock) void k_phase3(const Phase3Args a) {
       if (act[m]) load_group<BITS, NGI>(base[m] + (size_t)row * RB, grp[m], c[i][m], sb[i][m]);
   }
   __builtin_amdgcn_sched_barrier(0);  // the h vectors were requested before the weights
-  if (a.nrouter) {
-    // next layer's phase-1 workgroups c = b + k*grid (same XCD when the grid is a multiple of 8)
-    for (int c = blockIdx.x; c < a.n1; c += gridDim.x) {
-      if (c < a.n1r) {
-        const int r0 = c * kWavesPerBlock;
-        const int r1 = min(r0 + kWavesPerBlock, a.nE);
-        if (r1 > r0) block_prefetch(a.nrouter + (size_t)r0 * (a.n_row_bytes / 4), (size_t)(r1 - r0) * a.n_row_bytes, dump);
-        if (a.ngvec && r0 + kWavesPerBlock > a.nE) block_prefetch(a.ngvec, a.n_row_bytes, dump);
-      } else if (a.nshared_gu) {
-        block_prefetch_in(a.nshared_gu, (size_t)(c - a.n1r) * a.n_sh_bytes, a.n_sh_bytes, a.n_sh_total, dump);
-      }
-    }
-  }
   XSlice xs[SPL];
   if constexpr (STAGE) {
     // h_routed [K][I] -> LDS rows of 64 (slot k's group j is LDS row k*NGI + j)
     stage_store<H4, false>(hst, a.K * a.I / 4, hl, nullptr);
     __syncthreads();
     trace_mark(a.trace, 1);
-    if (row0 >= a.H) {
-      prefetch_drain();
-      return;
-    }
+    if (row0 >= a.H) return;
 #pragma unroll
     for (int m = 0; m < SPL; ++m) read_slice(hl, kk[m] * NGI + grp[m], 1.f, xs[m]);
   } else {
-    if (row0 >= a.H) {
-      prefetch_drain();
-      return;
-    }
+    if (row0 >= a.H) return;
 #pragma unroll
     for (int m = 0; m < SPL; ++m) load_xslice(a.h_routed + (size_t)kk[m] * a.I + kGroup * grp[m], xs[m]);
   }
@@ -819,14 +610,12 @@ __global__ __launch_bounds__(kBlock) void k_phase3(const Phase3Args a) {
     p = seg_reduce<SEG>(p);
     const int row = row0 + i * RPI + sub;
     if (seg_last<SEG>(lane) && row < a.H) {
-      float o = a.residual[row] + p;
-      if (a.d_shared) o += a.d_shared[row];
+      float o = res[i] + p;
+      if (a.d_shared) o += dsh[i];
       a.out[row] = o;
     }
   }
   trace_mark(a.trace, 3);
-  prefetch_drain();
-  trace_mark(a.trace, 4);
 }
 
 // ------------------------------------------------------------------ host dispatch
@@ -843,8 +632,7 @@ __global__ __launch_bounds__(kBlock) void k_phase3(const Phase3Args a) {
 
 inline int blocks_for(long waves) { return (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock); }
 
-// Launch geometry of one layer's three kernels (shared by the launchers, which
-// also need each other's geometry for the XCD-aligned prefetch).
+// Launch geometry of one layer's three kernels.
 template <int NGH, int NGI>
 struct LayerGeom {
   static constexpr int RPIH = kWave / NGH, RPII = kWave / NGI;
@@ -864,13 +652,6 @@ struct LayerGeom {
     const int slots = kpad * NGI;
     const int seg = slots < kWave ? slots : kWave;
     n3 = blocks_for(((long)L.H / (kWave / seg) + kP3Iters - 1) / kP3Iters);
-  }
-  size_t p1_sh_pair_bytes() const { return (size_t)kWavesPerBlock * kP1GateUpIters * RPIH * 2 * rbh; }
-  size_t p2_sdown_rows_bytes() const { return (size_t)kWavesPerBlock * kP2DownIters * RPII * rbi; }
-  size_t p3_rows_bytes() const {
-    const int slots = kpad * NGI;
-    const int seg = slots < kWave ? slots : kWave;
-    return (size_t)kWavesPerBlock * kP3Iters * (kWave / seg) * rbi;
   }
 };
 
@@ -916,15 +697,6 @@ struct Dispatch {
     p3.d_shared = L.shared ? L.d_shared : nullptr;
     p3.residual = L.residual;
     p3.out = L.out;
-    p3.nrouter = (L.prefetch_mask & 4) ? L.next_router : nullptr;
-    p3.ngvec = L.next_router ? L.next_gvec : nullptr;
-    p3.nshared_gu = L.next_router ? L.next_shared : nullptr;
-    p3.nE = L.E;
-    p3.n1r = G.n1r;
-    p3.n1 = G.n1r + G.n1s;
-    p3.n_row_bytes = sizeof(float) * (size_t)L.H;
-    p3.n_sh_bytes = G.p1_sh_pair_bytes();
-    p3.n_sh_total = (size_t)2 * L.I * G.rbh;
     p3.trace = L.trace ? L.trace + (size_t)2 * kTraceBlocks * kTraceSlots : nullptr;
     hipLaunchKernelGGL((k_phase3<BITS, NGI, KPAD>), dim3(G.n3), dim3(kBlock), 0, s, p3);
     return hipGetLastError();
@@ -945,11 +717,6 @@ struct Dispatch {
     p1.I = L.I;
     p1.h_shared = L.h_shared;
     p1.n_router_blocks = G.n1r;
-    p1.pf_sdown = has_shared && (L.prefetch_mask & 1) ? L.shared + L.gateup_bytes : nullptr;
-    p1.pf_sdown_bytes = G.p2_sdown_rows_bytes();
-    p1.pf_sdown_total = (size_t)L.H * G.rbi;
-    p1.pf_n2r = G.n2r;
-    p1.pf_n2s = G.n2s;
     p1.trace = L.trace;
     hipLaunchKernelGGL((k_phase1<BITS, NGH>), dim3(G.n1r + G.n1s), dim3(kBlock), 0, s, p1);
     return hipGetLastError();
@@ -979,10 +746,6 @@ struct Dispatch {
     p2.h_shared = L.h_shared;
     p2.sigma = L.sigma;
     p2.d_shared = L.d_shared;
-    p2.gu_bytes = L.gateup_bytes;
-    p2.pf_down_bytes = G.p3_rows_bytes();
-    p2.pf_down_total = (size_t)L.H * G.rbi;
-    p2.pf_n3 = (L.prefetch_mask & 2) ? G.n3 : 0;
     p2.trace = L.trace ? L.trace + (size_t)kTraceBlocks * kTraceSlots : nullptr;
     hipLaunchKernelGGL((k_phase2<BITS, NGH, NGI>), dim3(G.n2r + G.n2s), dim3(kBlock), 0, s, p2);
     return hipGetLastError();
