@@ -181,15 +181,20 @@ fmoe_status fmoe_expert_ffn(const fmoe_expert *E, const float *x, float *out, vo
  * ([P2] "Pipeline-Leistung", "Technische Implementierung", "Metal-Compute-Shader").
  * x, residual, out: device fp32 [n_tokens][hidden]; out may equal residual (in-place
  * residual update) but must not overlap x or ws. topk_idx (int32) and topk_w (fp32):
- * device [n_tokens][top_k] or NULL. ws: device, >= fmoe_workspace_bytes(L, n_tokens). */
+ * device [n_tokens][top_k] or NULL. ws: device, >= fmoe_workspace_bytes(L, n_tokens).
+ * With n_tokens > 1 the tokens are grouped by expert: the router, the shared expert and
+ * each distinct chosen expert are read from HBM once per call and applied to every token
+ * that uses them (results equal the one-token definition above, per token). */
 fmoe_status fmoe_moe_layer(const fmoe_layer *L, int n_tokens, const float *x, const float *residual,
                            float *out, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
                            void *stream);
 
 /* Diagnostic form of fmoe_moe_layer for per-kernel timing: enqueues only some of
- * the layer's three kernels, in order -- bit 0: router, shared-expert gate and
- * gate/up; bit 1: routing + routed gate/up + shared-expert down; bit 2: routed
- * down + combine. phases == 7 is fmoe_moe_layer. A kernel reads what the
+ * the layer's kernels, in order. One token -- bit 0: router, shared-expert gate
+ * and gate/up; bit 1: routing + routed gate/up + shared-expert down; bit 2: routed
+ * down + combine. Several tokens -- bit 0: router and shared-expert gate/up; bit 1:
+ * routing and grouping, then routed gate/up + shared-expert down; bit 2: routed
+ * down, then combine. phases == 7 is fmoe_moe_layer. A kernel reads what the
  * previous ones left in ws, so partial calls are meaningful only after a full
  * call with the same ws and inputs. FMOE_ERR_BATCH if phases is outside 1..7;
  * otherwise the arguments and errors of fmoe_moe_layer. */

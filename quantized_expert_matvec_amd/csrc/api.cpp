@@ -67,13 +67,45 @@ fmoe_status matvec_common(const fmoe_qmat *W, const float *x, float *y, void *st
   return e == hipSuccess ? FMOE_OK : FMOE_ERR_LAUNCH;
 }
 
-// Enqueue one layer for n_tokens tokens (arguments already validated).
+// Enqueue one layer for n_tokens tokens (arguments already validated): the
+// one-token kernels for a single token, the grouped kernels for several.
 // rms_eps >= 0: the layer input is rms_scale(x, rms_eps), computed inside the layer's kernels.
 fmoe_status layer_enqueue(const fmoe_layer *L, int B, const float *x, float rms_eps, const float *residual,
                           float *out, int32_t *topk_idx, float *topk_w, uint8_t *ws, hipStream_t s,
                           int phases = 7) {
   const LayerWs w = layer_ws(B, L->n_experts, L->top_k, L->hidden, L->inter);
   const int H = L->hidden, I = L->inter, E = L->n_experts, K = L->top_k;
+  if (B > 1) {
+    GroupArgs g{};
+    g.router = L->router;
+    g.gvec = L->shared ? L->shared_gate : nullptr;
+    g.bank = (const uint8_t *)L->bank;
+    g.shared = (const uint8_t *)L->shared;
+    g.stride = expert_bytes(L->bits, H, I);
+    g.gu_bytes = gateup_bytes(L->bits, H, I);
+    g.E = E;
+    g.K = K;
+    g.H = H;
+    g.I = I;
+    g.B = B;
+    g.bits = L->bits;
+    g.x = x;
+    g.rms_eps = rms_eps;
+    g.residual = residual;
+    g.out = out;
+    g.out_idx = topk_idx;
+    g.out_w = topk_w;
+    g.logits = (float *)(ws + w.logits);
+    g.sigma = (float *)(ws + w.sigma);
+    g.idx = (int32_t *)(ws + w.topk_idx);
+    g.w = (float *)(ws + w.topk_w);
+    g.h_shared = (float *)(ws + w.h_shared);
+    g.h_routed = (float *)(ws + w.h_routed);
+    g.d_shared = (float *)(ws + w.d_shared);
+    g.partial = (float *)(ws + w.partial);
+    g.groups = (int32_t *)(ws + w.groups);
+    return launch_group(g, s, phases) == hipSuccess ? FMOE_OK : FMOE_ERR_LAUNCH;
+  }
   for (int t = 0; t < B; ++t) {
     LayerArgs a{};
     a.router = L->router;

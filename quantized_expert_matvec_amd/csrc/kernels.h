@@ -43,6 +43,39 @@ struct LayerArgs {
   uint64_t *trace;
 };
 
+// One MoE layer for B > 1 tokens grouped by expert (device pointers).
+struct GroupArgs {
+  const float *router;
+  const float *gvec;         // null: no shared expert
+  const uint8_t *bank;
+  const uint8_t *shared;     // null: no shared expert
+  size_t stride, gu_bytes;
+  int E, K, H, I, B, bits;
+  const float *x;
+  float rms_eps;             // >= 0: each token's x is RMS-scaled first
+  const float *residual;
+  float *out;
+  int32_t *out_idx;          // [B][K] or null
+  float *out_w;              // [B][K] or null
+  float *logits;             // [B][E]
+  float *sigma;              // [B]
+  int32_t *idx;              // [B][K]
+  float *w;                  // [B][K]
+  float *h_shared;           // [B][I]
+  float *h_routed;           // [B*K][I]
+  float *d_shared;           // [B][H]
+  float *partial;            // [B*K][H]
+  int32_t *groups;           // D, expert[S], offset[S+1], slot[S]
+  int n_router_blocks;       // g1
+  int n_g2_routed_blocks;    // g2: routed workgroups (grid-stride over work items)
+};
+
+// The grouped layer: five launches (router + shared gate/up; routing and grouping;
+// routed gate/up by distinct expert + shared down; routed down by distinct
+// expert; combine). phases: bit 0 the first, bit 1 the second and third, bit 2
+// the last two.
+hipError_t launch_group(const GroupArgs &a, hipStream_t s, int phases = 7);
+
 // Router + sigmoid gate + shared gate/up; routing + routed gate/up + shared down;
 // down + weighted combine + residual. Three launches, no host synchronisation.
 // phases: bit p set = enqueue kernel p+1 (7 = the whole layer).

@@ -20,6 +20,10 @@ extern template hipError_t gateup_b<4>(const uint8_t *, int, int, const float *,
 extern template hipError_t gateup_b<2>(const uint8_t *, int, int, const float *, float *, hipStream_t);
 extern template hipError_t layer_b<4>(const LayerArgs &, hipStream_t, int);
 extern template hipError_t layer_b<2>(const LayerArgs &, hipStream_t, int);
+template <int BITS>
+hipError_t group_b(const GroupArgs &, hipStream_t, int);
+extern template hipError_t group_b<4>(const GroupArgs &, hipStream_t, int);
+extern template hipError_t group_b<2>(const GroupArgs &, hipStream_t, int);
 
 namespace {
 
@@ -111,6 +115,10 @@ hipError_t launch_expert_gateup(int bits, const uint8_t *gu, int hidden, int int
 
 hipError_t launch_layer(const LayerArgs &a, hipStream_t s, int phases) {
   return a.bits == 4 ? dev::layer_b<4>(a, s, phases) : dev::layer_b<2>(a, s, phases);
+}
+
+hipError_t launch_group(const GroupArgs &a, hipStream_t s, int phases) {
+  return a.bits == 4 ? dev::group_b<4>(a, s, phases) : dev::group_b<2>(a, s, phases);
 }
 
 hipError_t launch_rms(const float *h, float *x, int B, int H, float eps, hipStream_t s) {

@@ -61,6 +61,10 @@ struct LayerWs {
   size_t h_shared;  // fp32 [B][inter]
   size_t h_routed;  // fp32 [B][K][inter]
   size_t d_shared;  // fp32 [B][hidden]  sigma * shared-expert output
+  // B > 1 only (tokens grouped by expert):
+  size_t partial;   // fp32 [B][K][hidden]  w * routed-expert output, per (token, slot)
+  size_t groups;    // int32 [1 + S + (S + 1) + S], S = B*K: number of distinct experts D,
+                    // their expert ids [S], offsets of their slot lists [S + 1], slot lists [S]
   size_t total;
 };
 
@@ -79,6 +83,9 @@ inline LayerWs layer_ws(int B, int E, int K, int hidden, int inter) {
   w.h_shared = take(sizeof(float) * (size_t)B * inter);
   w.h_routed = take(sizeof(float) * (size_t)B * K * inter);
   w.d_shared = take(sizeof(float) * (size_t)B * hidden);
+  const size_t S = (size_t)B * K;
+  w.partial = take(B > 1 ? sizeof(float) * S * hidden : 0);
+  w.groups = take(B > 1 ? sizeof(int32_t) * (3 * S + 2) : 0);
   w.total = o;
   return w;
 }

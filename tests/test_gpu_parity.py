@@ -175,6 +175,63 @@ def test_layer_full_size_vs_oracle(device, bits):
     torch.cuda.empty_cache()
 
 
+# --------------------------------------------------------------------------- grouped (B > 1)
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_grouped_layer_forced_collisions(device, bits):
+    """16 tokens in 4 groups of identical x (so every chosen expert serves several tokens and the
+    staging chunks of the grouped kernels loop), on 8 experts; each token against the oracle."""
+    hidden, inter, n_exp, k, B = 1024, 512, 8, 4, 16
+    L = host_layer(61, 0, bits, n_exp, k, hidden, inter, device)
+    OL = OracleLayer(61, 0, bits, n_exp, k, hidden, inter)
+    base = _x(61, 7, hidden, 4)
+    X = np.ascontiguousarray(base[np.arange(B) % 4])
+    RES = synth.activations(61, synth.T_RESIDUAL, 7, B, hidden)
+    assert _check_layer(device, OL, L, X, RES, f"collisions q{bits}") == 0
+
+
+def test_grouped_layer_max_slots(device):
+    """The largest batch (64 tokens) with top-8 of 16 experts: 512 slots, every expert shared by
+    many tokens; inter 4096 (the smallest staging chunk)."""
+    hidden, inter, n_exp, k, B = 256, 4096, 16, 8, 64
+    L = host_layer(62, 0, 4, n_exp, k, hidden, inter, device)
+    OL = OracleLayer(62, 0, 4, n_exp, k, hidden, inter)
+    X = _x(62, 3, hidden, B)
+    assert _check_layer(device, OL, L, X, X, "max slots") == 0
+
+
+def test_grouped_equals_one_token_routing(device):
+    """The grouped kernels route every token exactly as the one-token kernels do (same logits
+    arithmetic), and their outputs agree to the acceptance bar."""
+    hidden, inter, n_exp, k, B = 2048, 512, 64, 4, 6
+    L = host_layer(63, 0, 4, n_exp, k, hidden, inter, device)
+    X = _x(63, 0, hidden, B)
+    xd = to_dev(X, device)
+    ig = torch.empty((B, k), dtype=torch.int32, device=device)
+    og = qem.fmoe_moe_layer(L, xd, xd, topk_idx=ig)
+    singles, i1 = [], torch.empty((B, k), dtype=torch.int32, device=device)
+    for t in range(B):
+        singles.append(qem.fmoe_moe_layer(L, xd[t:t + 1], xd[t:t + 1], topk_idx=i1[t:t + 1]))
+    torch.cuda.synchronize()
+    assert torch.equal(ig, i1)
+    for t in range(B):
+        assert_close(og[t].cpu().numpy(), singles[t][0].cpu().numpy(), f"grouped vs single token {t}")
+
+
+def test_grouped_full_size_B16(device):
+    """The batched decode workload's layer: 16 tokens, 512 experts + shared, hidden 4096,
+    inter 1024, q4, generated and packed on the device; every token against the oracle."""
+    hidden, inter, n_exp, k, B = 4096, 1024, 512, 4, 16
+    print("grouped full size B=16", flush=True)
+    L = device_layer(synth.SEED, 1, 4, n_exp, k, hidden, inter, device)
+    OL = OracleLayer(synth.SEED, 1, 4, n_exp, k, hidden, inter)
+    X = _x(synth.SEED, 2016, hidden, B)
+    ties = _check_layer(device, OL, L, X, X, "full B=16")
+    print(f"  near-ties: {ties}", flush=True)
+    del L
+    torch.cuda.empty_cache()
+
+
 # --------------------------------------------------------------------------- RMS + stack
 
 def test_rms_scale_vs_oracle(device):
@@ -184,7 +241,7 @@ def test_rms_scale_vs_oracle(device):
         assert_close(x[t], oracle.rms_scale(h[t].astype(np.float64)), f"rms token {t}")
 
 
-@pytest.mark.parametrize("B", [1, 4])
+@pytest.mark.parametrize("B", [1, 4, 16])
 def test_stack_vs_oracle(device, B):
     """A 4-layer stack with RMS scaling between layers, every layer's output compared with the
     oracle's own chain (the oracle never sees a GPU value)."""
