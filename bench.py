@@ -34,8 +34,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-PHASE_NAMES = {1: "router + shared gate/up (k_phase1)", 2: "routing + routed gate/up + shared down (k_phase2)",
-               4: "routed down + combine (k_phase3)"}
+PHASE_NAMES = {1: "router + shared gate (k_phase1)", 2: "routing + routed and shared gate/up (k_phase2)",
+               4: "routed and shared down + combine (k_phase3)"}
 
 
 def log(*a):
@@ -100,12 +100,12 @@ def phase_bytes(phase, d_routed, eb, gub, E, H, I, K, bits):
     """Algorithmic bytes one launch of a layer kernel moves (B=1): the weights it must
     stream once plus its activation reads and writes."""
     down = eb - gub
-    if phase == 1:   # router rows + gate vector + shared gate/up; x in; logits, sigma, h_shared out
-        return E * H * 4 + H * 4 + gub + H * 4 + E * 4 + 4 + I * 4
-    if phase == 2:   # distinct routed gate/up + shared down; x, logits, h_shared in; h_routed, d_shared out
-        return d_routed * gub + down + H * 4 + E * 4 + I * 4 + K * I * 4 + H * 4
-    if phase == 4:   # distinct routed down; h_routed, d_shared, residual in; out (+ routing) out
-        return d_routed * down + K * I * 4 + H * 4 + H * 4 + H * 4
+    if phase == 1:   # router rows + gate vector; x in; logits, sigma out
+        return E * H * 4 + H * 4 + H * 4 + E * 4 + 4
+    if phase == 2:   # distinct routed gate/up + shared gate/up; x, logits in; h_routed, h_shared out
+        return d_routed * gub + gub + H * 4 + E * 4 + K * I * 4 + I * 4
+    if phase == 4:   # distinct routed down + shared down; h_routed, h_shared, residual, sigma in; out
+        return d_routed * down + down + K * I * 4 + I * 4 + H * 4 + 4 + H * 4
     raise ValueError(phase)
 
 

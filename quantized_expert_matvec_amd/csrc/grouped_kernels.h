@@ -28,6 +28,7 @@ template <int NGI>
 constexpr int hchunk() { return NGI >= 64 ? 2 : NGI >= 32 ? 4 : 8; }
 constexpr int kG2Iters = 2;    // gate/up pair iterations per wavefront per work item
 constexpr int kG3Iters = 4;    // down row iterations per wavefront per work item
+constexpr int kG2DownIters = 4;  // shared down row iterations per wavefront
 constexpr int kRouteThreads = 1024;
 constexpr int kMaxSlots = kMaxTokens * kMaxTopK;
 static_assert(kMaxSlots <= kRouteThreads, "one routing thread per slot");
@@ -237,8 +238,8 @@ __global__ __launch_bounds__(kBlock) void k_g2(const GroupArgs a) {
     return;
   }
   const int wv = (blockIdx.x - a.n_g2_routed_blocks) * kWavesPerBlock + wave_in_block();
-  const int row0 = wv * kP2DownIters * (kWave / NGI);
-  RowLoads<BITS, NGI, kP2DownIters> R;
+  const int row0 = wv * kG2DownIters * (kWave / NGI);
+  RowLoads<BITS, NGI, kG2DownIters> R;
   if (row0 < a.H) R.issue(a.shared + a.gu_bytes, a.H, row0);
   for (int t0 = 0; t0 < a.B; t0 += HC) {
     const int nt = min(HC, a.B - t0);
@@ -336,7 +337,7 @@ struct GroupDispatch {
     const int n1s = sh ? blocks_for(a.I / RPIH) : 0;
     const long items2 = (long)dmax * (a.I / (kWavesPerBlock * kG2Iters * RPIH));
     a.n_g2_routed_blocks = (int)(items2 < kG2Blocks ? items2 : kG2Blocks);
-    const int n2s = sh ? blocks_for((a.H / RPII + kP2DownIters - 1) / kP2DownIters) : 0;
+    const int n2s = sh ? blocks_for((a.H / RPII + kG2DownIters - 1) / kG2DownIters) : 0;
     const int rows3 = kWavesPerBlock * kG3Iters * RPII;
     const long items3 = (long)dmax * ((a.H + rows3 - 1) / rows3);
     const int n3 = (int)(items3 < kG3Blocks ? items3 : kG3Blocks);

@@ -58,12 +58,15 @@ struct Staged {
   float4 v[N4];
 };
 
+// The loads are unconditional (indices clamped to the vector), so that no branch
+// hides them from the compiler's memory-counter bookkeeping: waiting for them
+// then does not also wait for loads issued after them.
 template <int N4>
 __device__ __forceinline__ void stage_load(const float *__restrict__ src, int nf4, Staged<N4> &st) {
 #pragma unroll
   for (int k = 0; k < N4; ++k) {
-    const int f = threadIdx.x + kBlock * k;
-    if (f < nf4) st.v[k] = reinterpret_cast<const float4 *>(src)[f];
+    const int f = min((int)threadIdx.x + kBlock * k, nf4 - 1);
+    st.v[k] = reinterpret_cast<const float4 *>(src)[f];
   }
 }
 
@@ -270,7 +273,8 @@ __device__ __forceinline__ void wave_topk_lds(const float *lg, int E, int K, int
 // thread reads the result from sidx / sw. (Results are not copied back into
 // per-thread arrays: indexing those by a runtime slot would put them in scratch
 // memory.) Workgroup b uses wavefront b % 4, so that the workgroups sharing a CU
-// do not all compute it on the same SIMD.
+// do not all compute it on the same SIMD. (Measured: splitting the rounds over
+// the four wavefronts, with one barrier per round, is slower.)
 __device__ __forceinline__ void block_topk(const float *lg, int E, int K, int *sidx, float *sw) {
   if (wave_in_block() == (int)(blockIdx.x % kWavesPerBlock)) {
     // the rest of the workgroup waits on this wavefront: let it win the SIMD's
@@ -333,10 +337,8 @@ __global__ __launch_bounds__(kBlock) void k_expert_gateup(const uint8_t *__restr
 
 // ------------------------------------------------------------------ layer kernels
 
-constexpr int kP1GateUpIters = 1;  // gate/up pair iterations per wavefront in phase 1
-constexpr int kP2GateUpIters = 2;  // routed gate/up
-constexpr int kP2DownIters = 4;    // shared down rows
-constexpr int kP3Iters = 4;        // down + combine
+constexpr int kP2GateUpIters = 2;  // gate/up pair iterations per wavefront (routed and shared)
+constexpr int kP3Iters = 4;        // routed down row iterations per wavefront
 
 struct Phase1Args {
   const float *router;
@@ -346,17 +348,13 @@ struct Phase1Args {
   float rms_eps;  // >= 0: x is RMS-scaled first
   float *logits;
   float *sigma;
-  const uint8_t *shared_gu;  // null: no shared expert
-  int I;
-  float *h_shared;
-  int n_router_blocks;
   uint64_t *trace;
 };
 
-// Phase 1. Router blocks: one fp32 router row per wavefront (lane l covers
-// columns 4l + 256t + 0..3; row E is the shared expert's gate vector, giving
-// sigmoid(g . x)). Shared blocks: the shared expert's gate/up + SwiGLU.
-template <int BITS, int NGH>
+// Phase 1: the router. One fp32 router row per wavefront (lane l covers columns
+// 4l + 256t + 0..3); row E is the shared expert's gate vector, giving
+// sigmoid(g . x).
+template <int NGH>
 __global__ __launch_bounds__(kBlock) void k_phase1(const Phase1Args a) {
   constexpr int NT = NGH / 4;  // hidden / 256
   constexpr int H = NGH * kGroup;
@@ -366,61 +364,38 @@ __global__ __launch_bounds__(kBlock) void k_phase1(const Phase1Args a) {
   const int lane = lane_id();
   const bool rms = a.rms_eps >= 0.f;
   trace_mark(a.trace, 0);
-  if ((int)blockIdx.x < a.n_router_blocks) {
-    const int n_rows = a.E + (a.gvec ? 1 : 0);
-    const int row = blockIdx.x * kWavesPerBlock + wave_in_block();
-    const int rr = min(row, n_rows - 1);
-    const float *src = rr == a.E ? a.gvec : a.router + (size_t)rr * H;
-    Staged<X4> xst;
-    stage_load(a.x, NGH * 16, xst);
-    float4 w[NT];
+  const int n_rows = a.E + (a.gvec ? 1 : 0);
+  const int row = blockIdx.x * kWavesPerBlock + wave_in_block();
+  const int rr = min(row, n_rows - 1);
+  const float *src = rr == a.E ? a.gvec : a.router + (size_t)rr * H;
+  Staged<X4> xst;
+  stage_load(a.x, NGH * 16, xst);
+  float4 w[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) w[t] = reinterpret_cast<const float4 *>(src)[lane + 64 * t];
-    __builtin_amdgcn_sched_barrier(0);
-    if (rms)
-      stage_store<X4, true>(xst, NGH * 16, xl, part);
-    else
-      stage_store<X4, false>(xst, NGH * 16, xl, part);
-    __syncthreads();
-    trace_mark(a.trace, 1);
-    const float inv = rms ? rms_inv(part, H, a.rms_eps) : 1.f;
-    float acc = 0.f;
+  for (int t = 0; t < NT; ++t) w[t] = reinterpret_cast<const float4 *>(src)[lane + 64 * t];
+  __builtin_amdgcn_sched_barrier(0);
+  if (rms)
+    stage_store<X4, true>(xst, NGH * 16, xl, part);
+  else
+    stage_store<X4, false>(xst, NGH * 16, xl, part);
+  __syncthreads();
+  trace_mark(a.trace, 1);
+  const float inv = rms ? rms_inv(part, H, a.rms_eps) : 1.f;
+  float acc = 0.f;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const float4 xv = *reinterpret_cast<const float4 *>(&xl[lds_index(4 * lane + 256 * t)]);
-      acc = fmaf(w[t].x, xv.x * inv, acc);
-      acc = fmaf(w[t].y, xv.y * inv, acc);
-      acc = fmaf(w[t].z, xv.z * inv, acc);
-      acc = fmaf(w[t].w, xv.w * inv, acc);
-    }
-    const float d = seg_reduce<kWave>(acc);
-    trace_mark(a.trace, 2);
-    if (lane == kWave - 1 && row < n_rows) {
-      if (row == a.E)
-        *a.sigma = 1.f / (1.f + expf(-d));
-      else
-        a.logits[row] = d;
-    }
-  } else {
-    // shared expert gate/up
-    const int wv = (blockIdx.x - a.n_router_blocks) * kWavesPerBlock + wave_in_block();
-    const int pair0 = wv * kP1GateUpIters * (kWave / NGH);
-    Staged<X4> xst;
-    stage_load(a.x, NGH * 16, xst);
-    PairLoads<BITS, NGH, kP1GateUpIters> P;
-    if (pair0 < a.I) P.issue(a.shared_gu, pair0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (rms)
-      stage_store<X4, true>(xst, NGH * 16, xl, part);
+  for (int t = 0; t < NT; ++t) {
+    const float4 xv = *reinterpret_cast<const float4 *>(&xl[lds_index(4 * lane + 256 * t)]);
+    acc = fmaf(w[t].x, xv.x * inv, acc);
+    acc = fmaf(w[t].y, xv.y * inv, acc);
+    acc = fmaf(w[t].z, xv.z * inv, acc);
+    acc = fmaf(w[t].w, xv.w * inv, acc);
+  }
+  const float d = seg_reduce<kWave>(acc);
+  if (lane == kWave - 1 && row < n_rows) {
+    if (row == a.E)
+      *a.sigma = 1.f / (1.f + expf(-d));
     else
-      stage_store<X4, false>(xst, NGH * 16, xl, part);
-    __syncthreads();
-    trace_mark(a.trace, 1);
-    if (pair0 < a.I) {
-      XSlice xs;
-      read_slice(xl, lane & (NGH - 1), rms ? rms_inv(part, H, a.rms_eps) : 1.f, xs);
-      P.finish(xs, a.h_shared, pair0);
-    }
+      a.logits[row] = d;
   }
   trace_mark(a.trace, 3);
 }
@@ -440,31 +415,28 @@ struct Phase2Args {
   float *out_w;
   int waves_per_slot;
   int n_routed_blocks;
-  // shared expert's down projection (null: none)
-  const uint8_t *shared_down;
-  int H;
-  const float *h_shared;
-  const float *sigma;
-  float *d_shared;
+  const uint8_t *shared_gu;  // null: no shared expert
+  float *h_shared;
   uint64_t *trace;
 };
 
-// Phase 2. Routed blocks stage the logits and x, every wavefront re-derives the
-// top-K, then runs gate/up + SwiGLU of its slot's expert. Shared blocks run the
-// shared expert's down projection, scaled by its sigmoid gate.
-template <int BITS, int NGH, int NGI>
-__global__ __launch_bounds__(kBlock) void k_phase2(const Phase2Args a) {
+// Phase 2. Routed blocks stage the logits and x, derive the top-K (one wavefront
+// per block), then run gate/up + SwiGLU of their slot's expert. Shared blocks run
+// the shared expert's gate/up + SwiGLU: it does not depend on the routing, so its
+// weights stream while the routed blocks are still choosing.
+template <int BITS, int NGH>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void k_phase2(const Phase2Args a) {
   constexpr int H = NGH * kGroup;
-  constexpr int XL = NGH * kXPad > NGI * kXPad ? NGH * kXPad : NGI * kXPad;
-  __shared__ float xl[XL];
+  constexpr int RPIH = kWave / NGH;
+  __shared__ float xl[NGH * kXPad];
   __shared__ float lg[kMaxExperts];
   __shared__ float part[kWavesPerBlock];
   __shared__ int sidx[kMaxTopK];
   __shared__ float sw[kMaxTopK];
   const int lane = lane_id();
+  const bool rms = a.rms_eps >= 0.f;
   trace_mark(a.trace, 0);
   if ((int)blockIdx.x < a.n_routed_blocks) {
-    const bool rms = a.rms_eps >= 0.f;
     for (int i = threadIdx.x; i < a.E; i += kBlock) lg[i] = a.logits[i];
     if (rms)
       stage_vec<NGH, true>(a.x, xl, part);
@@ -476,7 +448,7 @@ __global__ __launch_bounds__(kBlock) void k_phase2(const Phase2Args a) {
     trace_mark(a.trace, 2);
     const int wv = blockIdx.x * kWavesPerBlock + wave_in_block();
     const int slot = min(wv / a.waves_per_slot, a.K - 1);
-    const int pair0 = (wv % a.waves_per_slot) * kP2GateUpIters * (kWave / NGH);
+    const int pair0 = (wv % a.waves_per_slot) * kP2GateUpIters * RPIH;
     const bool active = wv < a.waves_per_slot * a.K;
     PairLoads<BITS, NGH, kP2GateUpIters> P;
     if (active) P.issue(a.bank + (size_t)sidx[slot] * a.stride, pair0);
@@ -496,22 +468,22 @@ __global__ __launch_bounds__(kBlock) void k_phase2(const Phase2Args a) {
     trace_mark(a.trace, 3);
     return;
   }
-  // shared expert down
+  // shared expert gate/up
   const int wv = (blockIdx.x - a.n_routed_blocks) * kWavesPerBlock + wave_in_block();
-  const int row0 = wv * kP2DownIters * (kWave / NGI);
-  constexpr int I4 = (NGI * 16 + kBlock - 1) / kBlock;
-  const float sig = *a.sigma;  // requested before the weights, used after them
-  Staged<I4> hst;
-  stage_load(a.h_shared, NGI * 16, hst);
-  RowLoads<BITS, NGI, kP2DownIters> R;
-  if (row0 < a.H) R.issue(a.shared_down, a.H, row0);
-  __builtin_amdgcn_sched_barrier(0);
-  stage_store<I4, false>(hst, NGI * 16, xl, nullptr);
+  const int pair0 = wv * kP2GateUpIters * RPIH;
+  PairLoads<BITS, NGH, kP2GateUpIters> P;
+  if (pair0 < a.I) P.issue(a.shared_gu, pair0);
+  if (rms)
+    stage_vec<NGH, true>(a.x, xl, part);
+  else
+    stage_vec<NGH, false>(a.x, xl, part);
   __syncthreads();
-  if (row0 >= a.H) return;
-  XSlice xs;
-  read_slice(xl, lane & (NGI - 1), 1.f, xs);
-  R.finish(xs, a.d_shared, a.H, row0, sig);
+  trace_mark(a.trace, 1);
+  if (pair0 < a.I) {
+    XSlice xs;
+    read_slice(xl, lane & (NGH - 1), rms ? rms_inv(part, H, a.rms_eps) : 1.f, xs);
+    P.finish(xs, a.h_shared, pair0);
+  }
   trace_mark(a.trace, 3);
 }
 
@@ -521,35 +493,46 @@ struct Phase3Args {
   const int32_t *idx;
   const float *w;
   int K;
-  const float *h_routed;  // [K][I]
+  const float *h_routed;      // [K][I]
   int I, H;
-  const float *d_shared;  // [H] or null
+  const uint8_t *shared_down; // null: no shared expert
+  const float *h_shared;      // [I]
+  const float *sigma;
   const float *residual;
   float *out;
   uint64_t *trace;
 };
 
-// Phase 3: out_i = residual_i + sum_k w_k (down_k . h_k)_i + d_shared_i.
-// Lanes are (slot k, group j) pairs, so one cross-lane sum adds the K experts'
-// weighted partials of a row together; each lane keeps its slot's h slice.
-// KPAD = top_k rounded up to a power of two (slots beyond top_k stay idle). The
-// routed h vectors are staged in LDS when they fit (KPAD * inter <= 8192).
+// Phase 3: out_i = residual_i + sum_k w_k (down_k . h_k)_i + sigma (down_s . h_s)_i.
+// Routed: lanes are (slot k, group j) pairs, so one cross-lane sum adds the K
+// experts' weighted partials of a row together; each lane keeps its slot's h
+// slice. KPAD = top_k rounded up to a power of two (slots beyond top_k stay
+// idle). The routed h vectors are staged in LDS when they fit (KPAD * inter <=
+// 8192). Shared: the same wavefront's rows, NGI lanes per row; its weights do not
+// depend on the routing and are requested first. A wavefront passes its shared
+// results from the shared lanes to the combining lanes through LDS.
 template <int BITS, int NGI, int KPAD>
 __global__ __launch_bounds__(kBlock) void k_phase3(const Phase3Args a) {
   constexpr int SLOTS = KPAD * NGI;
   constexpr int SEG = SLOTS < kWave ? SLOTS : kWave;  // lanes per row
   constexpr int SPL = SLOTS / SEG;                     // slots per lane
   constexpr int RPI = kWave / SEG;
+  constexpr int RPW = kP3Iters * RPI;                  // rows per wavefront
+  constexpr int RPII = kWave / NGI;                    // shared-down rows per iteration
+  constexpr int SIT = (RPW + RPII - 1) / RPII;         // shared-down iterations
   constexpr size_t RB = (size_t)NGI * gbytes<BITS>();
   constexpr bool STAGE = KPAD * NGI <= 128;
   __shared__ float hl[STAGE ? KPAD * NGI * kXPad : 1];
+  __shared__ float hs[NGI * kXPad];
+  __shared__ float dsh[kWavesPerBlock * RPW];
   trace_mark(a.trace, 0);
   const int lane = lane_id();
   const int sub = lane / SEG;
-  const int row0 = wave_id() * kP3Iters * RPI;
-  // requested first, all independent: the routing of each slot, the residual
-  // and sigma * shared-down values of this lane's rows (used only after the dot
-  // products), and the routed h vectors
+  const int row0 = wave_id() * RPW;
+  const bool sh = a.shared_down != nullptr;
+  // requested first, all independent of each other: the routing of each slot, the
+  // residual of this lane's rows and sigma (used only after the dot products),
+  // the h vectors, and the shared expert's down rows
   int sel[SPL];
   float wk[SPL];
   int grp[SPL], kk[SPL];
@@ -564,16 +547,27 @@ __global__ __launch_bounds__(kBlock) void k_phase3(const Phase3Args a) {
     sel[m] = a.idx[kk[m]];
     wk[m] = k < a.K ? a.w[kk[m]] : 0.f;
   }
-  float res[kP3Iters], dsh[kP3Iters];
+  float res[kP3Iters];
 #pragma unroll
-  for (int i = 0; i < kP3Iters; ++i) {
-    const int row = min(row0 + i * RPI + sub, a.H - 1);
-    res[i] = a.residual[row];
-    dsh[i] = a.d_shared ? a.d_shared[row] : 0.f;
-  }
+  for (int i = 0; i < kP3Iters; ++i) res[i] = a.residual[min(row0 + i * RPI + sub, a.H - 1)];
+  const float sig = *a.sigma;  // (a workspace value; unused without a shared expert)
   constexpr int H4 = STAGE ? (KPAD * NGI * 16 + kBlock - 1) / kBlock : 1;
+  constexpr int S4 = (NGI * 16 + kBlock - 1) / kBlock;
   Staged<H4> hst;
   if constexpr (STAGE) stage_load(a.h_routed, a.K * a.I / 4, hst);
+  // without a shared expert these loads read the routed expert 0 instead (valid
+  // memory, results unused): unconditional loads keep the memory-counter waits exact
+  Staged<S4> sst;
+  stage_load(sh ? a.h_shared : a.h_routed, NGI * 16, sst);
+  const uint8_t *sdown = sh ? a.shared_down : a.bank + a.gu_bytes;
+  const int ssub = lane / NGI, sg = lane & (NGI - 1);
+  Chunk<BITS> cs[SIT];
+  uint32_t ss[SIT];
+#pragma unroll
+  for (int q = 0; q < SIT; ++q) {
+    const int row = min(row0 + q * RPII + ssub, a.H - 1);
+    load_group<BITS, NGI>(sdown + (size_t)row * RB, sg, cs[q], ss[q]);
+  }
   const uint8_t *base[SPL];
 #pragma unroll
   for (int m = 0; m < SPL; ++m) base[m] = a.bank + (size_t)sel[m] * a.stride + a.gu_bytes;
@@ -582,22 +576,31 @@ __global__ __launch_bounds__(kBlock) void k_phase3(const Phase3Args a) {
 #pragma unroll
   for (int i = 0; i < kP3Iters; ++i) {
     const int row = min(row0 + i * RPI + sub, a.H - 1);
+    // unconditional (inactive slots reload slot 0's rows, unused), as above
 #pragma unroll
-    for (int m = 0; m < SPL; ++m)
-      if (act[m]) load_group<BITS, NGI>(base[m] + (size_t)row * RB, grp[m], c[i][m], sb[i][m]);
+    for (int m = 0; m < SPL; ++m) load_group<BITS, NGI>(base[m] + (size_t)row * RB, grp[m], c[i][m], sb[i][m]);
   }
   __builtin_amdgcn_sched_barrier(0);  // the h vectors were requested before the weights
+  if constexpr (STAGE) stage_store<H4, false>(hst, a.K * a.I / 4, hl, nullptr);
+  stage_store<S4, false>(sst, NGI * 16, hs, nullptr);
+  __syncthreads();
+  trace_mark(a.trace, 1);
+  if (row0 >= a.H) return;
+  if (sh) {
+    XSlice xs;
+    read_slice(hs, sg, 1.f, xs);
+#pragma unroll
+    for (int q = 0; q < SIT; ++q) {
+      const float p = seg_reduce<NGI>(group_partial<BITS>(cs[q], ss[q], xs));
+      const int r = q * RPII + ssub;  // row within this wavefront's rows
+      if (seg_last<NGI>(lane) && r < RPW) dsh[wave_in_block() * RPW + r] = sig * p;
+    }
+  }
   XSlice xs[SPL];
   if constexpr (STAGE) {
-    // h_routed [K][I] -> LDS rows of 64 (slot k's group j is LDS row k*NGI + j)
-    stage_store<H4, false>(hst, a.K * a.I / 4, hl, nullptr);
-    __syncthreads();
-    trace_mark(a.trace, 1);
-    if (row0 >= a.H) return;
 #pragma unroll
     for (int m = 0; m < SPL; ++m) read_slice(hl, kk[m] * NGI + grp[m], 1.f, xs[m]);
   } else {
-    if (row0 >= a.H) return;
 #pragma unroll
     for (int m = 0; m < SPL; ++m) load_xslice(a.h_routed + (size_t)kk[m] * a.I + kGroup * grp[m], xs[m]);
   }
@@ -611,7 +614,7 @@ __global__ __launch_bounds__(kBlock) void k_phase3(const Phase3Args a) {
     const int row = row0 + i * RPI + sub;
     if (seg_last<SEG>(lane) && row < a.H) {
       float o = res[i] + p;
-      if (a.d_shared) o += dsh[i];
+      if (sh) o += dsh[wave_in_block() * RPW + i * RPI + sub];
       a.out[row] = o;
     }
   }
@@ -643,10 +646,10 @@ struct LayerGeom {
     rbh = (size_t)NGH * (bits == 4 ? 36 : 20);
     rbi = (size_t)NGI * (bits == 4 ? 36 : 20);
     n1r = blocks_for(L.E + (sh ? 1 : 0));
-    n1s = sh ? blocks_for((L.I / RPIH + kP1GateUpIters - 1) / kP1GateUpIters) : 0;
+    n1s = 0;
     wps = (L.I / RPIH + kP2GateUpIters - 1) / kP2GateUpIters;
     n2r = blocks_for((long)wps * L.K);
-    n2s = sh ? blocks_for((L.H / RPII + kP2DownIters - 1) / kP2DownIters) : 0;
+    n2s = sh ? blocks_for(wps) : 0;
     kpad = 1;
     while (kpad < L.K) kpad <<= 1;
     const int slots = kpad * NGI;
@@ -694,7 +697,9 @@ struct Dispatch {
     p3.h_routed = L.h_routed;
     p3.I = L.I;
     p3.H = L.H;
-    p3.d_shared = L.shared ? L.d_shared : nullptr;
+    p3.shared_down = L.shared ? L.shared + L.gateup_bytes : nullptr;
+    p3.h_shared = L.h_shared;
+    p3.sigma = L.sigma;
     p3.residual = L.residual;
     p3.out = L.out;
     p3.trace = L.trace ? L.trace + (size_t)2 * kTraceBlocks * kTraceSlots : nullptr;
@@ -713,12 +718,8 @@ struct Dispatch {
     p1.rms_eps = L.rms_eps;
     p1.logits = L.logits;
     p1.sigma = L.sigma;
-    p1.shared_gu = has_shared ? L.shared : nullptr;
-    p1.I = L.I;
-    p1.h_shared = L.h_shared;
-    p1.n_router_blocks = G.n1r;
     p1.trace = L.trace;
-    hipLaunchKernelGGL((k_phase1<BITS, NGH>), dim3(G.n1r + G.n1s), dim3(kBlock), 0, s, p1);
+    hipLaunchKernelGGL((k_phase1<NGH>), dim3(G.n1r), dim3(kBlock), 0, s, p1);
     return hipGetLastError();
   }
 
@@ -741,13 +742,10 @@ struct Dispatch {
     p2.out_w = L.topk_w_out;
     p2.waves_per_slot = G.wps;
     p2.n_routed_blocks = G.n2r;
-    p2.shared_down = has_shared ? L.shared + L.gateup_bytes : nullptr;
-    p2.H = L.H;
+    p2.shared_gu = has_shared ? L.shared : nullptr;
     p2.h_shared = L.h_shared;
-    p2.sigma = L.sigma;
-    p2.d_shared = L.d_shared;
     p2.trace = L.trace ? L.trace + (size_t)kTraceBlocks * kTraceSlots : nullptr;
-    hipLaunchKernelGGL((k_phase2<BITS, NGH, NGI>), dim3(G.n2r + G.n2s), dim3(kBlock), 0, s, p2);
+    hipLaunchKernelGGL((k_phase2<BITS, NGH>), dim3(G.n2r + G.n2s), dim3(kBlock), 0, s, p2);
     return hipGetLastError();
   }
 
