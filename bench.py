@@ -34,6 +34,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+KERNEL_SOURCES = ["layer_kernels.h", "device.h", "kernels.h", "layout.h", "kernels_q4.hip"]
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "moe_layer_q4_B1_hbm_counters.txt")
 PHASE_NAMES = {1: "router + shared gate (k_phase1)", 2: "routing + routed and shared gate/up (k_phase2)",
                4: "routed and shared down + combine (k_phase3)"}
 
@@ -107,6 +109,31 @@ def phase_bytes(phase, d_routed, eb, gub, E, H, I, K, bits):
     if phase == 4:   # distinct routed down + shared down; h_routed, h_shared, residual, sigma in; out
         return d_routed * down + down + K * I * 4 + I * 4 + H * 4 + 4 + H * 4
     raise ValueError(phase)
+
+
+def kernel_source_hash():
+    """sha256 over the sources of the one-token layer kernels (q4 instantiation)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "quantized_expert_matvec_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counter_traffic(tag):
+    """HBM bytes per launch of kernel `tag` from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, scaled by the copy calibration), or None when there is
+    none or the kernel sources changed since the counters were taken."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    h = kernel_source_hash()
+    with open(COUNTERS_FILE) as fh:
+        for line in fh:
+            f = line.split()
+            if len(f) == 8 and f[0] == "counters" and f[1] == tag and f[7] == h:
+                return int(f[3]) + int(f[5])
+    return None
 
 
 def cpu_baseline(a, synth, oracle, R0, g0, h0, budget_s):
@@ -271,9 +298,11 @@ def main():
                                         "GBps": round(nbytes / (us * 1e3), 1)}
         dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
         kk = kernels[dom]
+        tag = dom.split("(")[-1].rstrip(")")
+        traffic = counter_traffic(tag) if (bits == 4 and (H, I, E, K) == (4096, 1024, 512, 4)) else None
         roofline = {"bound": "hbm", "achieved": kk["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(kk["GBps"] / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": dom,
-                    "avg_us": kk["avg_us"], "algorithmic_bytes_per_launch": kk["algorithmic_bytes"]}
+                    "frac": round(kk["GBps"] / HBM_PEAK_GBPS, 4), "traffic": traffic, "traffic_unit": "bytes/launch",
+                    "kernel": dom, "avg_us": kk["avg_us"], "algorithmic_bytes_per_launch": kk["algorithmic_bytes"]}
         del lws, outs, xs
 
     # ---- parity of layer 0, step 0 against the oracle, and the oracle's CPU time
