@@ -444,7 +444,12 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       stage_vec<NGH, false>(a.x, xl, part);
     __syncthreads();
     trace_mark(a.trace, 1);
-    block_topk(lg, a.E, a.K, sidx, sw);
+    // a workgroup serves one slot (waves_per_slot is a multiple of 4) and needs
+    // only the first slot+1 winners: the rounds stop there, so the workgroups of
+    // the early slots start streaming before the last winner is known. The
+    // workgroup that publishes the routing is one of the last slot's (all K).
+    const int bslot = min((int)(blockIdx.x * kWavesPerBlock) / a.waves_per_slot, a.K - 1);
+    block_topk(lg, a.E, bslot + 1, sidx, sw);
     trace_mark(a.trace, 2);
     const int wv = blockIdx.x * kWavesPerBlock + wave_in_block();
     const int slot = min(wv / a.waves_per_slot, a.K - 1);
@@ -452,7 +457,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     const bool active = wv < a.waves_per_slot * a.K;
     PairLoads<BITS, NGH, kP2GateUpIters> P;
     if (active) P.issue(a.bank + (size_t)sidx[slot] * a.stride, pair0);
-    if (wv == 0 && lane < a.K) {
+    if (wv == (a.K - 1) * a.waves_per_slot && lane < a.K) {
       const int sel = sidx[lane];
       const float ws = sw[lane];
       a.ws_idx[lane] = sel;
