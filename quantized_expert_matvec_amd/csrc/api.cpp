@@ -99,8 +99,11 @@ fmoe_status layer_enqueue(const fmoe_layer *L, int B, const float *x, float rms_
     g.sigma = (float *)(ws + w.sigma);
     g.idx = (int32_t *)(ws + w.topk_idx);
     g.w = (float *)(ws + w.topk_w);
-    g.h_shared = (float *)(ws + w.h_shared);
-    g.h_routed = (float *)(ws + w.h_routed);
+    g.xq = (uint16_t *)(ws + w.xq);
+    g.xsum = (float *)(ws + w.xsum);
+    g.xinv = (float *)(ws + w.xinv);
+    g.hq = (uint16_t *)(ws + w.hq);
+    g.hsum = (float *)(ws + w.hsum);
     g.d_shared = (float *)(ws + w.d_shared);
     g.partial = (float *)(ws + w.partial);
     g.groups = (int32_t *)(ws + w.groups);

@@ -4,16 +4,34 @@
 // all the tokens that use it. Included by kernels_q4.hip / kernels_q2.hip after
 // layer_kernels.h, which instantiate group_b<BITS>.
 //
+// Several tokens against one weight row make a (skinny) dense contraction, so
+// the quantized experts run on the matrix cores: v_mfma_f32_16x16x32_bf16 with
+//   B operand = 16 weight rows x 32 columns of codes, each code c (BITS bits) as
+//               the exact bf16 value 1 + c / 2^BITS (c in the top mantissa bits,
+//               so the constant 1 stays small next to the code's part);
+//   A operand = 16 rows = 4 tokens x {hi, mid, lo, 0}, where hi = bf16(x),
+//               mid = bf16(x - hi), lo = bf16(x - hi - mid): three bf16 parts
+//               that add up to the fp32 x exactly (in the normal range);
+//   D (fp32)  = per (token part, weight row) the sum over 32 columns.
+// Two MFMAs cover a 64-column group; per (row, group) the epilogue applies the
+// affine dequantization in the group-factored form
+//   sum_j (c_j s + b) x_j = 2^BITS s * (sum_j (1 + c_j / 2^BITS) x'_j - sum_j x'_j) + b sum_j x_j
+// where x' = hi + mid + lo is the value the matrix cores saw: the constant is
+// taken off with the sum of x' itself, the bias with the fp32 group sum of x.
+// Both sums are formed when x (or h) is prepared.
+//
 // Five launches:
-//   g1  router logits and sigmoid(g . x) of every token, shared expert
-//       gate/up + SwiGLU of every token (weights in registers, the tokens'
-//       x vectors staged through LDS kTokChunk at a time)
+//   g1  router logits and sigmoid(g . x) of every token (fp32 rows, VALU, the
+//       tokens' x staged through LDS); other workgroups prepare each token's x
+//       for the matrix cores: RMS factor, per-group sums, bf16 parts
 //   g2r one workgroup: top-K of every token, then the distinct experts in
 //       order of first use and, for each, the ascending list of the slots
 //       (token t, choice k; slot = t*K + k) routed to it
-//   g2  routed gate/up + SwiGLU by (distinct expert, block of rows) for the
-//       expert's slots; the shared expert's down for every token
-//   g3  routed down by (distinct expert, block of rows): per slot, w * (D h)
+//   g2  gate/up + SwiGLU of (shared expert or distinct expert, one group of 64
+//       gate/up pairs = 128 rows, one 16-row tile per wavefront) for all the
+//       tokens / slots using it; writes h as bf16 parts plus its group sums
+//   g3  down of (shared expert or distinct expert, 128 rows): per token
+//       sigma * (D_s h) into d_shared, per slot w * (D h) into partial[slot]
 //   g4  out = residual + the K per-slot outputs in slot order + sigma * shared
 #pragma once
 
@@ -22,100 +40,405 @@
 namespace fmoe {
 namespace dev {
 
-constexpr int kTokChunk = 2;   // hidden-wide vectors staged in LDS at a time
-// inter-wide vectors staged in LDS at a time (NGI groups each): at most 128 groups
-template <int NGI>
-constexpr int hchunk() { return NGI >= 64 ? 2 : NGI >= 32 ? 4 : 8; }
-constexpr int kG2Iters = 2;    // gate/up pair iterations per wavefront per work item
-constexpr int kG3Iters = 4;    // down row iterations per wavefront per work item
-constexpr int kG2DownIters = 4;  // shared down row iterations per wavefront
 constexpr int kRouteThreads = 1024;
 constexpr int kMaxSlots = kMaxTokens * kMaxTopK;
 static_assert(kMaxSlots <= kRouteThreads, "one routing thread per slot");
+constexpr int kRouterTok = 8;  // tokens whose fp32 x the router stages in LDS at a time
+constexpr int kTokBlock = 16;  // tokens per pass over the weights
+constexpr int kTokPass = 4;    // tokens per MFMA row block (4 rows each: hi, mid, lo, 0)
+constexpr int kParts = 3;      // bf16 parts of an fp32 value
+constexpr int kGThreads = 512;  // workgroup of the matrix-core kernels: 8 wavefronts
+constexpr int kGWaves = kGThreads / kWave;
+constexpr int kWaveLds = 16 * (2 * 8 * 16 + 16) + 16 * 9 * 4;  // LDS bytes per wavefront for a weight chunk
+constexpr int kXBudget = 96 * 1024;                          // LDS bytes for staged x
+constexpr int kXLds = kXBudget + kParts * kTokBlock * 16;    // plus 16 B of padding per vector
+static_assert(kXBudget >= kParts * kTokBlock * 8 * 128, "x chunks of at least 8 groups");
 
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
-// Stage a hidden-wide (or inter-wide) vector through the generic helper of the
-// one-token kernels, with or without the sum of squares.
-template <int NG>
-__device__ __forceinline__ void stage_tok(const float *src, float *lds, float *part, bool sumsq) {
-  if (sumsq)
-    stage_vec<NG, true>(src, lds, part);
-  else
-    stage_vec<NG, false>(src, lds, part);
+// ------------------------------------------------------------------ bf16 and MFMA order
+
+// bf16 bits of a finite float, round to nearest even.
+__device__ __forceinline__ uint32_t bf16_bits(float v) {
+  const uint32_t b = __float_as_uint(v);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float bf16_float(uint32_t h) { return __uint_as_float(h << 16); }
+
+// v = bf16(p[0]) + bf16(p[1]) + bf16(p[2]) (exactly, for v in the normal range);
+// rep = that sum as a float.
+__device__ __forceinline__ void bf16_split3(float v, uint32_t (&p)[3], float &rep) {
+  p[0] = bf16_bits(v);
+  const float r1 = v - bf16_float(p[0]);
+  p[1] = bf16_bits(r1);
+  p[2] = bf16_bits(r1 - bf16_float(p[1]));
+  rep = bf16_float(p[0]) + (bf16_float(p[1]) + bf16_float(p[2]));
 }
 
-// g1: router rows (one fp32 row per wavefront; row E is the gate vector) or
-// shared-expert gate/up pairs, for every token.
+// The MFMA order of a group's 64 columns: MFMA m (0, 1) takes from k-block q
+// (0..3) the 8 consecutive columns starting at mfma_col(q, m), matching which
+// packed codes lane (row, q) holds (see MCodes).
+template <int BITS>
+__device__ __forceinline__ int mfma_col(int q, int m) {
+  return BITS == 4 ? 32 * (q >> 1) + 8 * (2 * (q & 1) + m) : 16 * q + 8 * m;
+}
+// Position (0..63) of column c of a group in MFMA order.
+template <int BITS>
+__device__ __forceinline__ int mfma_pos(int c) {
+  int q, m;
+  if constexpr (BITS == 4) {
+    const int w = (c >> 3) & 3;
+    q = 2 * (c >> 5) + (w >> 1);
+    m = w & 1;
+  } else {
+    q = c >> 4;
+    m = (c >> 3) & 1;
+  }
+  return (m * 4 + q) * 8 + (c & 7);
+}
+
+// One group of one weight row as held by lane (row, q): 16 codes for 4-bit (two
+// words, one per MFMA; bytes 8 (q & 1) .. + 7 of half q >> 1 of the group),
+// 16 codes for 2-bit (one word: word q of the group), and the (scale, bias) word.
+struct MCodes {
+  uint32_t c0, c1, sb;
+};
+
+// Four low bytes of bf16 values (0x80 | code in the top mantissa bits) in v ->
+// two dwords of bf16 pairs: the high byte 0x3F above each (value 1 + c / 2^BITS);
+// v_perm_b32 selects bytes 0..3 from v and 4..7 from the constant.
+__device__ __forceinline__ void bf16_pairs(uint32_t v, uint32_t &p0, uint32_t &p1) {
+  constexpr uint32_t K = 0x3F3F3F3Fu;
+  p0 = __builtin_amdgcn_perm(K, v, 0x04010400u);
+  p1 = __builtin_amdgcn_perm(K, v, 0x04030402u);
+}
+
+// The B operands of the group's two MFMAs (8 codes each, in column order).
+template <int BITS>
+__device__ __forceinline__ void mfma_codes(const MCodes &m, uint4 &u0, uint4 &u1) {
+  // each byte's code moved to bits 6..(7 - BITS) of its byte, with bit 7 set
+  // (the low bit of the bf16 exponent of 1.0)
+  constexpr uint32_t E = 0x80808080u;
+  if constexpr (BITS == 4) {
+    bf16_pairs(((m.c0 << 3) & 0x78787878u) | E, u0.x, u0.y);
+    bf16_pairs(((m.c0 >> 1) & 0x78787878u) | E, u0.z, u0.w);
+    bf16_pairs(((m.c1 << 3) & 0x78787878u) | E, u1.x, u1.y);
+    bf16_pairs(((m.c1 >> 1) & 0x78787878u) | E, u1.z, u1.w);
+  } else {
+    bf16_pairs(((m.c0 << 5) & 0x60606060u) | E, u0.x, u0.y);
+    bf16_pairs(((m.c0 << 3) & 0x60606060u) | E, u0.z, u0.w);
+    bf16_pairs(((m.c0 << 1) & 0x60606060u) | E, u1.x, u1.y);
+    bf16_pairs(((m.c0 >> 1) & 0x60606060u) | E, u1.z, u1.w);
+  }
+}
+
+// ------------------------------------------------------------------ matrix-core rows
+
+// Workgroup-cooperative (kGThreads threads): one 16-row tile per wavefront
+// (rows rec0 + r * RB, r = 0..15) against T <= kTokBlock vectors vec_of(u) of
+// a prepared source: part k (0..2) at xq_base + (3 vec + k) * NG * 64; per
+// group (sum x, sum x') at xs_base + 2 (vec * NG + g). The vectors are staged
+// in LDS (xl: kXLds bytes, xsl: kTokBlock * NG entries) in chunks of as many
+// groups as fit the budget: all of them for up to 4 tokens at NG = 64. On
+// return lane (n = lane % 16, qq = lane / 16) holds in y[p] row n for token
+// u = 4p + qq (meaningless for u >= T). Contains barriers: every thread of the
+// workgroup calls it with the same T.
+//
+// Weights stream in chunks of CG groups. A wavefront loads a chunk of its 16
+// rows with 16-byte loads over whole 16 CG-byte spans of each row (each load
+// instruction covers complete cache lines), keeps DEPTH chunks in flight, and
+// passes each chunk through its own LDS region (wl: kWaveLds bytes), from
+// which lane (n, q) reads the codes of k-block q of row n. The loop has no
+// branches around its loads, so every wait is exact; the empty asm statements
+// keep the optimiser from moving the loads (and the reads of their results)
+// away from where the pipeline needs them.
+template <int BITS, int NG>
+struct MfmaRows {
+  static constexpr int CG = NG < 8 ? NG : 8;          // groups per chunk
+  static constexpr int NC = NG / CG;                  // chunks per row
+  static constexpr int DEPTH = NC < 2 ? NC : 2;       // chunks in flight
+  static constexpr int HALVES = BITS == 4 ? 2 : 1;    // 16-byte code units per group
+  static constexpr int NI = 16 * HALVES * CG / kWave; // 16-byte code loads per lane per chunk
+  static constexpr int SBW = CG / 4;                  // scale/bias words per lane per chunk
+  static constexpr int RB = NG * gbytes<BITS>();      // bytes per row record
+  static constexpr int SBO = 16 * HALVES * NG;        // scale/bias words within a record
+  static constexpr int RS = 16 * HALVES * CG + 16;    // LDS bytes per row of codes (padded)
+  static constexpr int SBS = CG + 1;                  // LDS words per row of scale/bias (padded)
+  static_assert(16 * RS + 64 * SBS <= kWaveLds, "chunk fits the wavefront's LDS region");
+  static_assert(NC % DEPTH == 0, "whole rounds of chunks");
+
+  struct Chunk {
+    uint4 c[NI];
+    uint32_t s[SBW];
+  };
+
+  float y[kTokBlock / kTokPass];
+
+  template <typename VecOf>
+  __device__ __forceinline__ static void stage(const uint16_t *__restrict__ xq_base, const float *__restrict__ xs_base,
+                                               int T, VecOf vec_of, int g0, int gc, int vs, uint8_t *xl,
+                                               float2 *xsl) {
+    __syncthreads();  // earlier reads of xl / xsl are done
+    const int units = kParts * T * gc * 8;  // 16-byte units; vector v = 3u + k: token u, part k
+    for (int e = threadIdx.x; e < units; e += kGThreads) {
+      const int v = e / (gc * 8), r = e - v * (gc * 8);
+      const int gl = r >> 3, k16 = r & 7;
+      const int vu = v / kParts, vk = v - kParts * vu;
+      const uint16_t *src = xq_base + ((size_t)(kParts * vec_of(vu) + vk) * NG + g0 + gl) * 64 + 8 * k16;
+      *reinterpret_cast<uint4 *>(xl + v * vs + gl * 128 + k16 * 16) = *reinterpret_cast<const uint4 *>(src);
+    }
+    for (int e = threadIdx.x; e < T * gc; e += kGThreads) {
+      const int u = e / gc, gl = e - u * gc;
+      xsl[u * NG + gl] = reinterpret_cast<const float2 *>(xs_base)[(size_t)vec_of(u) * NG + g0 + gl];
+    }
+    __syncthreads();
+  }
+
+  template <int NP, bool WHOLE, typename VecOf>
+  __device__ __forceinline__ void loop(const uint8_t *__restrict__ rec0, const uint16_t *__restrict__ xq_base,
+                                       const float *__restrict__ xs_base, int T, VecOf vec_of, int gc, int vs,
+                                       uint8_t *xl, float2 *xsl, uint8_t *wl) {
+    const int lane = lane_id();
+    const int q = lane >> 4;  // k-block of the A / B operands; token of D
+    const int i = lane & 15;  // A row (4 token + part) / weight row of B and D
+    int aoff[NP], xoff[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int ua = min(kTokPass * p + (i >> 2), T - 1), ka = min(i & 3, kParts - 1);
+      aoff[p] = (kParts * ua + ka) * vs + q * 16;
+      xoff[p] = min(kTokPass * p + q, T - 1) * NG;
+    }
+    // this lane's share of a chunk: code unit u = 64 k + lane is (row, half, group)
+    // = (u / (HALVES CG), u / CG % HALVES, u % CG); scale/bias: row lane / 4, words
+    // SBW (lane % 4) .. + SBW - 1
+    int goff[NI], loff[NI];
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      const int u = kWave * k + lane;
+      const int j = u % CG, rh = u / CG;
+      const int r = rh / HALVES, h = rh % HALVES;
+      goff[k] = r * RB + 16 * (h * NG + j);
+      loff[k] = r * RS + 16 * (h * CG + j);
+    }
+    const int sr = lane >> 2, sp = lane & 3;
+    const int gsoff = sr * RB + SBO + 4 * SBW * sp;
+    const int lsoff = 16 * RS + 4 * (sr * SBS + SBW * sp);
+    // where lane (n = i, q) reads group j of the chunk in wl
+    const int rcode = BITS == 4 ? i * RS + 16 * (q >> 1) * CG + 8 * (q & 1) : i * RS + 4 * q;
+    const int rsb = 16 * RS + 4 * i * SBS;
+
+    auto load_chunk = [&](int c, Chunk &k) {
+#pragma unroll
+      for (int t = 0; t < NI; ++t) k.c[t] = *reinterpret_cast<const uint4 *>(rec0 + goff[t] + 16 * CG * c);
+      if constexpr (SBW == 2) {
+        const uint2 v = *reinterpret_cast<const uint2 *>(rec0 + gsoff + 4 * CG * c);
+        k.s[0] = v.x;
+        k.s[1] = v.y;
+      } else {
+        k.s[0] = *reinterpret_cast<const uint32_t *>(rec0 + gsoff + 4 * CG * c);
+      }
+    };
+    Chunk ring[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      load_chunk(d, ring[d]);
+      asm volatile("" ::: "memory");
+    }
+#pragma unroll 1
+    for (int cb = 0; cb < NC; cb += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        const int c = cb + d;
+        if (!WHOLE && c > 0 && ((c * CG) & (gc - 1)) == 0) stage(xq_base, xs_base, T, vec_of, c * CG, gc, vs, xl, xsl);
+        // chunk c arrives here; into this wavefront's LDS region (the reads of
+        // the previous chunk were issued before, and LDS keeps a wavefront's order)
+#pragma unroll
+        for (int t = 0; t < NI; ++t) {
+          asm volatile("" : "+v"(ring[d].c[t].x), "+v"(ring[d].c[t].y), "+v"(ring[d].c[t].z), "+v"(ring[d].c[t].w));
+          *reinterpret_cast<uint4 *>(wl + loff[t]) = ring[d].c[t];
+        }
+#pragma unroll
+        for (int t = 0; t < SBW; ++t) {
+          asm volatile("" : "+v"(ring[d].s[t]));
+          *reinterpret_cast<uint32_t *>(wl + lsoff + 4 * t) = ring[d].s[t];
+        }
+        // refill (a clamped chunk past the end)
+        load_chunk(min(c + DEPTH, NC - 1), ring[d]);
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int j = 0; j < CG; ++j) {
+          const int g = c * CG + j;
+          const int gl = WHOLE ? g : (g & (gc - 1));
+          MCodes m;
+          if constexpr (BITS == 4) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(wl + rcode + 16 * j);
+            m.c0 = v.x;
+            m.c1 = v.y;
+          } else {
+            m.c0 = *reinterpret_cast<const uint32_t *>(wl + rcode + 16 * j);
+            m.c1 = 0;
+          }
+          m.sb = *reinterpret_cast<const uint32_t *>(wl + rsb + 4 * j);
+          uint4 u0, u1;
+          mfma_codes<BITS>(m, u0, u1);
+          const float s = scale_of(m.sb) * (float)(1 << BITS);  // exact (power of two)
+          const float ns = -s;
+          const float bi = bias_of(m.sb);
+          const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, u0), b1 = __builtin_bit_cast(bf16x8_t, u1);
+#pragma unroll
+          for (int p = 0; p < NP; ++p) {
+            const uint8_t *src = xl + aoff[p] + gl * 128;
+            const bf16x8_t A0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(src));
+            const bf16x8_t A1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(src + 64));
+            const float2 X = xsl[xoff[p] + gl];
+            f32x4_t dd = {0.f, 0.f, 0.f, 0.f};
+            dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, b0, dd, 0, 0, 0);
+            dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, b1, dd, 0, 0, 0);
+            y[p] = fmaf(s, dd[0] + (dd[1] + dd[2]), fmaf(ns, X.y, fmaf(bi, X.x, y[p])));
+          }
+        }
+      }
+    }
+  }
+
+  // rec0: record of the wavefront's first row; wl: its LDS region
+  template <typename VecOf>
+  __device__ __forceinline__ void run(const uint8_t *__restrict__ rec0, const uint16_t *__restrict__ xq_base,
+                                      const float *__restrict__ xs_base, int T, VecOf vec_of, uint8_t *xl,
+                                      float2 *xsl, uint8_t *wl) {
+    int gc = NG;  // groups per staged chunk of x (a power of two, a multiple of CG)
+    while (gc > CG && kParts * T * gc * 128 > kXBudget) gc >>= 1;
+    const int vs = gc * 128 + 16;  // LDS bytes per staged vector
+#pragma unroll
+    for (int p = 0; p < kTokBlock / kTokPass; ++p) y[p] = 0.f;
+    stage(xq_base, xs_base, T, vec_of, 0, gc, vs, xl, xsl);
+    const int np = (T + kTokPass - 1) / kTokPass;
+    const bool whole = gc == NG;
+    if (np == 1) {
+      if (whole)
+        loop<1, true>(rec0, xq_base, xs_base, T, vec_of, gc, vs, xl, xsl, wl);
+      else
+        loop<1, false>(rec0, xq_base, xs_base, T, vec_of, gc, vs, xl, xsl, wl);
+    } else if (np == 2) {
+      if (whole)
+        loop<2, true>(rec0, xq_base, xs_base, T, vec_of, gc, vs, xl, xsl, wl);
+      else
+        loop<2, false>(rec0, xq_base, xs_base, T, vec_of, gc, vs, xl, xsl, wl);
+    } else if (np == 3) {
+      if (whole)
+        loop<3, true>(rec0, xq_base, xs_base, T, vec_of, gc, vs, xl, xsl, wl);
+      else
+        loop<3, false>(rec0, xq_base, xs_base, T, vec_of, gc, vs, xl, xsl, wl);
+    } else {
+      if (whole)
+        loop<4, true>(rec0, xq_base, xs_base, T, vec_of, gc, vs, xl, xsl, wl);
+      else
+        loop<4, false>(rec0, xq_base, xs_base, T, vec_of, gc, vs, xl, xsl, wl);
+    }
+  }
+};
+
+// ------------------------------------------------------------------ g1
+
+// g1: workgroups [0, n_router_blocks): router rows (one fp32 row per
+// wavefront; row E is the gate vector) for every token. Workgroups
+// n_router_blocks + t: token t's x for the matrix cores (RMS factor, per-group
+// sums of x, hi/lo bf16 parts in MFMA order).
 template <int BITS, int NGH>
 __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
   constexpr int NT = NGH / 4;
   constexpr int H = NGH * kGroup;
-  constexpr int RPIH = kWave / NGH;
-  constexpr int X4 = (NGH * 16 + kBlock - 1) / kBlock;
-  __shared__ float xl[kTokChunk][NGH * kXPad];
-  __shared__ float part[kTokChunk][kWavesPerBlock];
+  __shared__ float xl[kRouterTok][NGH * kXPad];
+  __shared__ float part[kRouterTok][kWavesPerBlock];
   const int lane = lane_id();
   const bool rms = a.rms_eps >= 0.f;
-  const bool router = (int)blockIdx.x < a.n_router_blocks;
+  if ((int)blockIdx.x >= a.n_router_blocks) {
+    // ---- input preparation of token t
+    const int t = blockIdx.x - a.n_router_blocks;
+    const float *xt = a.x + (size_t)t * H;
+    constexpr int UNITS = NGH * 8;  // 8 columns each, in MFMA order: unit = 8g + 4m + q
+    float ss = 0.f;
+    for (int u0 = 0; u0 < UNITS; u0 += kBlock) {
+      const int u = u0 + threadIdx.x;
+      const bool ok = u < UNITS;
+      const int uc = ok ? u : UNITS - 1;
+      const int g = uc >> 3, mq = uc & 7;
+      const int c = 64 * g + mfma_col<BITS>(mq & 3, mq >> 2);
+      const float4 v0 = *reinterpret_cast<const float4 *>(xt + c);
+      const float4 v1 = *reinterpret_cast<const float4 *>(xt + c + 4);
+      const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      uint32_t pt[8][3];
+      float sum = 0.f, rep = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float r;
+        bf16_split3(f[j], pt[j], r);
+        sum += f[j];
+        rep += r;
+        if (ok) ss = fmaf(f[j], f[j], ss);
+      }
+      // group sums: the group's 8 units are 8 consecutive threads
+      sum = seg_allreduce<8>(sum);
+      rep = seg_allreduce<8>(rep);
+      if (ok) {
+        uint16_t *dst = a.xq + ((size_t)(kParts * t) * NGH + g) * 64 + 8 * mq;
+#pragma unroll
+        for (int k = 0; k < kParts; ++k) {
+          const uint4 v4 = {pt[0][k] | pt[1][k] << 16, pt[2][k] | pt[3][k] << 16, pt[4][k] | pt[5][k] << 16,
+                            pt[6][k] | pt[7][k] << 16};
+          *reinterpret_cast<uint4 *>(dst + (size_t)k * NGH * 64) = v4;
+        }
+        if (mq == 0) reinterpret_cast<float2 *>(a.xsum)[(size_t)t * NGH + g] = make_float2(sum, rep);
+      }
+    }
+    ss = seg_reduce<kWave>(ss);
+    if (lane == kWave - 1) part[0][wave_in_block()] = ss;
+    __syncthreads();
+    if (threadIdx.x == 0) a.xinv[t] = rms ? rms_inv(part[0], H, a.rms_eps) : 1.f;
+    return;
+  }
+  // ---- router rows
   const int n_rows = a.E + (a.gvec ? 1 : 0);
   const int row = blockIdx.x * kWavesPerBlock + wave_in_block();
-  const int pair0 = ((blockIdx.x - a.n_router_blocks) * kWavesPerBlock + wave_in_block()) * RPIH;
-  // token 0's x is requested before the weights (memory counters complete in order)
-  Staged<X4> xst;
-  stage_load(a.x, NGH * 16, xst);
+  const int rr = min(row, n_rows - 1);
+  const float *src = rr == a.E ? a.gvec : a.router + (size_t)rr * H;
   float4 wr[NT];
-  PairLoads<BITS, NGH, 1> P;
-  if (router) {
-    const int rr = min(row, n_rows - 1);
-    const float *src = rr == a.E ? a.gvec : a.router + (size_t)rr * H;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) wr[t] = reinterpret_cast<const float4 *>(src)[lane + 64 * t];
-  } else if (pair0 < a.I) {
-    P.issue(a.shared, pair0);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  for (int t0 = 0; t0 < a.B; t0 += kTokChunk) {
-    const int nt = min(kTokChunk, a.B - t0);
+  for (int t = 0; t < NT; ++t) wr[t] = reinterpret_cast<const float4 *>(src)[lane + 64 * t];
+  for (int t0 = 0; t0 < a.B; t0 += kRouterTok) {
+    const int nt = min(kRouterTok, a.B - t0);
     if (t0 > 0) __syncthreads();  // the previous chunk's reads of xl are done
     for (int j = 0; j < nt; ++j) {
-      if (t0 + j == 0) {
-        if (rms)
-          stage_store<X4, true>(xst, NGH * 16, xl[0], part[0]);
-        else
-          stage_store<X4, false>(xst, NGH * 16, xl[0], part[0]);
-      } else {
-        stage_tok<NGH>(a.x + (size_t)(t0 + j) * H, xl[j], part[j], rms);
-      }
+      if (rms)
+        stage_vec<NGH, true>(a.x + (size_t)(t0 + j) * H, xl[j], part[j]);
+      else
+        stage_vec<NGH, false>(a.x + (size_t)(t0 + j) * H, xl[j], part[j]);
     }
     __syncthreads();
     for (int j = 0; j < nt; ++j) {
-      const int t = t0 + j;
       const float inv = rms ? rms_inv(part[j], H, a.rms_eps) : 1.f;
-      if (router) {
-        float acc = 0.f;
+      float acc = 0.f;
 #pragma unroll
-        for (int q = 0; q < NT; ++q) {
-          const float4 xv = *reinterpret_cast<const float4 *>(&xl[j][lds_index(4 * lane + 256 * q)]);
-          acc = fmaf(wr[q].x, xv.x * inv, acc);
-          acc = fmaf(wr[q].y, xv.y * inv, acc);
-          acc = fmaf(wr[q].z, xv.z * inv, acc);
-          acc = fmaf(wr[q].w, xv.w * inv, acc);
-        }
-        const float d = seg_reduce<kWave>(acc);
-        if (lane == kWave - 1 && row < n_rows) {
-          if (row == a.E)
-            a.sigma[t] = 1.f / (1.f + expf(-d));
-          else
-            a.logits[(size_t)t * a.E + row] = d;
-        }
-      } else if (pair0 < a.I) {
-        XSlice xs;
-        read_slice(xl[j], lane & (NGH - 1), inv, xs);
-        P.finish(xs, a.h_shared + (size_t)t * a.I, pair0);
+      for (int q = 0; q < NT; ++q) {
+        const float4 xv = *reinterpret_cast<const float4 *>(&xl[j][lds_index(4 * lane + 256 * q)]);
+        acc = fmaf(wr[q].x, xv.x * inv, acc);
+        acc = fmaf(wr[q].y, xv.y * inv, acc);
+        acc = fmaf(wr[q].z, xv.z * inv, acc);
+        acc = fmaf(wr[q].w, xv.w * inv, acc);
+      }
+      const float d = seg_reduce<kWave>(acc);
+      if (lane == kWave - 1 && row < n_rows) {
+        if (row == a.E)
+          a.sigma[t0 + j] = 1.f / (1.f + expf(-d));
+        else
+          a.logits[(size_t)(t0 + j) * a.E + row] = d;
       }
     }
   }
 }
+
+// ------------------------------------------------------------------ g2r
 
 // g2r: one workgroup of kRouteThreads. Top-K of each token (one wavefront per
 // token), then the grouping, deterministic whatever the thread timing:
@@ -196,100 +519,146 @@ __global__ __launch_bounds__(kRouteThreads) void k_g2r(const GroupArgs a) {
   if (s < S) G[1 + S + (S + 1) + off[r] + pos] = s;
 }
 
-// g2: routed gate/up by work item (distinct expert d, block of pair rows), and
-// the shared expert's down projection for every token (scaled by its sigma).
+// ------------------------------------------------------------------ g2, g3
+
+// Work of one owner: the shared expert (owner 0 when there is one; its tokens
+// 0..B-1) or distinct expert d (its slot list).
+struct GroupItem {
+  int expert;  // -1: the shared expert
+  int q0, n;   // slot-list range (routed) or tokens 0..B-1 (shared)
+};
+
+// false if the owner does not exist (past the D distinct experts)
+__device__ __forceinline__ bool group_item(const GroupArgs &a, int owner, GroupItem &it) {
+  const int S = a.B * a.K;
+  const bool sh = a.shared != nullptr;
+  if (sh && owner == 0) {
+    it.expert = -1;
+    it.q0 = 0;
+    it.n = a.B;
+    return true;
+  }
+  const int d = owner - (sh ? 1 : 0);
+  const int32_t *G = a.groups;
+  if (d >= G[0]) return false;
+  it.expert = G[1 + d];
+  it.q0 = G[1 + S + d];
+  it.n = G[1 + S + d + 1] - it.q0;
+  return true;
+}
+
+// g2: gate/up + SwiGLU of 128 interleaved rows (64 pairs = group gi of the
+// inter dimension) of one owner, for all its tokens / slots. Wavefront w holds
+// rows 16w .. 16w + 15. h vectors: slot s at index s, shared-expert token t at
+// index S + t.
 template <int BITS, int NGH, int NGI>
-__global__ __launch_bounds__(kBlock) void k_g2(const GroupArgs a) {
-  constexpr int H = NGH * kGroup;
-  constexpr int RPIH = kWave / NGH;
-  constexpr int HC = hchunk<NGI>();
-  constexpr int BUF = (kTokChunk * NGH > HC * NGI ? kTokChunk * NGH : HC * NGI) * kXPad;
-  __shared__ float buf[BUF];
-  __shared__ float part[kTokChunk][kWavesPerBlock];
-  const int lane = lane_id();
-  if ((int)blockIdx.x < a.n_g2_routed_blocks) {
-    const bool rms = a.rms_eps >= 0.f;
-    const int32_t *G = a.groups;
-    const int S = a.B * a.K;
-    const int D = G[0];
-    constexpr int kPairsPerItem = kWavesPerBlock * kG2Iters * RPIH;
-    const int per = a.I / kPairsPerItem;
-    for (int item = blockIdx.x; item < D * per; item += a.n_g2_routed_blocks) {
-      const int d = item / per;
-      const int pair0 = ((item - d * per) * kWavesPerBlock + wave_in_block()) * kG2Iters * RPIH;
-      const int e = G[1 + d];
-      const int q0 = G[1 + S + d], q1 = G[1 + S + d + 1];
-      const int32_t *slots = G + 1 + S + (S + 1);
-      PairLoads<BITS, NGH, kG2Iters> P;
-      P.issue(a.bank + (size_t)e * a.stride, pair0);
-      for (int c = q0; c < q1; c += kTokChunk) {
-        const int nt = min(kTokChunk, q1 - c);
-        __syncthreads();  // buf is free
-        for (int j = 0; j < nt; ++j)
-          stage_tok<NGH>(a.x + (size_t)(slots[c + j] / a.K) * H, buf + j * NGH * kXPad, part[j], rms);
-        __syncthreads();
-        for (int j = 0; j < nt; ++j) {
-          XSlice xs;
-          read_slice(buf + j * NGH * kXPad, lane & (NGH - 1), rms ? rms_inv(part[j], H, a.rms_eps) : 1.f, xs);
-          P.finish(xs, a.h_routed + (size_t)slots[c + j] * a.I, pair0);
-        }
+__global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
+  constexpr size_t RB = (size_t)NGH * gbytes<BITS>();
+  __shared__ __attribute__((aligned(16))) uint8_t xl[kXLds];
+  __shared__ float2 xsl[kTokBlock * NGH];
+  __shared__ float2 hpart[kGWaves][kTokBlock];
+  __shared__ __attribute__((aligned(16))) uint8_t wlds[kGWaves][kWaveLds];
+  GroupItem it;
+  const int owner = blockIdx.x / NGI, gi = blockIdx.x % NGI;
+  if (!group_item(a, owner, it)) return;  // uniform over the workgroup
+  const int S = a.B * a.K;
+  const int lane = lane_id(), wv = wave_in_block();
+  const int n = lane & 15, qq = lane >> 4;
+  const uint8_t *base = it.expert < 0 ? a.shared : a.bank + (size_t)it.expert * a.stride;
+  const uint8_t *rec0 = base + (size_t)(128 * gi + 16 * wv) * RB;
+  const int32_t *slots = a.groups + 1 + S + (S + 1);
+  for (int tb = 0; tb < it.n; tb += kTokBlock) {
+    const int T = min(kTokBlock, it.n - tb);
+    // the token whose x item token u takes, and the index of its h vector
+    auto xtok = [&](int u) { return it.expert < 0 ? tb + u : slots[it.q0 + tb + u] / a.K; };
+    auto hvec = [&](int u) { return it.expert < 0 ? S + tb + u : slots[it.q0 + tb + u]; };
+    MfmaRows<BITS, NGH> M;
+    M.run(rec0, a.xq, a.xsum, T, xtok, xl, xsl, wlds[wv]);
+    // h = silu(gate) * up: gate rows are even, up rows odd (adjacent lanes)
+    float hs[kTokBlock / kTokPass] = {}, hr[kTokBlock / kTokPass] = {};
+#pragma unroll
+    for (int p = 0; p < kTokBlock / kTokPass; ++p) {
+      const int u = kTokPass * p + qq;
+      const float inv = u < T ? a.xinv[xtok(u)] : 0.f;
+      const float yv = M.y[p] * inv;
+      const float up = dpp_f<0xB1, 0xF>(yv, 0.f);  // partner row (quad_perm [1,0,3,2])
+      if ((n & 1) == 0 && u < T) {
+        const float h = silu(yv) * up;
+        const int pl = 8 * wv + (n >> 1);  // pair within the group
+        uint16_t *dst = a.hq + (size_t)(kParts * hvec(u)) * a.I + 64 * gi + mfma_pos<BITS>(pl);
+        uint32_t pt[3];
+        float r;
+        bf16_split3(h, pt, r);
+#pragma unroll
+        for (int k = 0; k < kParts; ++k) dst[(size_t)k * a.I] = (uint16_t)pt[k];
+        hs[p] += h;
+        hr[p] += r;
       }
     }
-    return;
-  }
-  const int wv = (blockIdx.x - a.n_g2_routed_blocks) * kWavesPerBlock + wave_in_block();
-  const int row0 = wv * kG2DownIters * (kWave / NGI);
-  RowLoads<BITS, NGI, kG2DownIters> R;
-  if (row0 < a.H) R.issue(a.shared + a.gu_bytes, a.H, row0);
-  for (int t0 = 0; t0 < a.B; t0 += HC) {
-    const int nt = min(HC, a.B - t0);
-    if (t0 > 0) __syncthreads();
-    for (int j = 0; j < nt; ++j)
-      stage_vec<NGI, false>(a.h_shared + (size_t)(t0 + j) * a.I, buf + j * NGI * kXPad, nullptr);
+    // group sums of h: the even lanes of each 16-lane row (odd lanes hold 0), then
+    // the wavefronts in order
+#pragma unroll
+    for (int p = 0; p < kTokBlock / kTokPass; ++p) {
+      float r = hs[p], e = hr[p];
+      r += dpp_f<0xB1, 0xF>(r, 0.f);   // lanes n, n^1
+      e += dpp_f<0xB1, 0xF>(e, 0.f);
+      r += dpp_f<0x4E, 0xF>(r, 0.f);   // n, n^2
+      e += dpp_f<0x4E, 0xF>(e, 0.f);
+      r += dpp_f<0x141, 0xF>(r, 0.f);  // row_half_mirror: n, 7-n
+      e += dpp_f<0x141, 0xF>(e, 0.f);
+      r += dpp_f<0x140, 0xF>(r, 0.f);  // row_mirror: n, 15-n
+      e += dpp_f<0x140, 0xF>(e, 0.f);
+      const int u = kTokPass * p + qq;
+      if (n == 0 && u < T) hpart[wv][u] = make_float2(r, e);
+    }
     __syncthreads();
-    if (row0 < a.H) {
-      for (int j = 0; j < nt; ++j) {
-        XSlice xs;
-        read_slice(buf + j * NGI * kXPad, lane & (NGI - 1), 1.f, xs);
-        R.finish(xs, a.d_shared + (size_t)(t0 + j) * a.H, a.H, row0, a.sigma[t0 + j]);
+    if ((int)threadIdx.x < T) {
+      const int u = threadIdx.x;
+      float2 t = hpart[0][u];
+#pragma unroll
+      for (int v = 1; v < kGWaves; ++v) {
+        t.x += hpart[v][u].x;
+        t.y += hpart[v][u].y;
       }
+      reinterpret_cast<float2 *>(a.hsum)[(size_t)hvec(u) * NGI + gi] = t;
     }
   }
 }
 
-// g3: routed down by work item (distinct expert d, block of rows): for each of
-// the expert's slots s, partial[s][row] = w[s] * (down_row . h[s]).
+// g3: down of 128 rows (part rb) of one owner for all its tokens / slots:
+// shared: d_shared[t][row] = sigma[t] * row . h_shared[t]; routed:
+// partial[slot][row] = w[slot] * row . h[slot]. Wavefront w holds rows 16w .. +15.
 template <int BITS, int NGI>
-__global__ __launch_bounds__(kBlock) void k_g3(const GroupArgs a) {
-  constexpr int RPII = kWave / NGI;
-  constexpr int kRowsPerItem = kWavesPerBlock * kG3Iters * RPII;
-  constexpr int HC = hchunk<NGI>();
-  __shared__ float buf[HC * NGI * kXPad];
-  const int lane = lane_id();
-  const int32_t *G = a.groups;
+__global__ __launch_bounds__(kGThreads) void k_g3(const GroupArgs a) {
+  constexpr size_t RB = (size_t)NGI * gbytes<BITS>();
+  __shared__ __attribute__((aligned(16))) uint8_t xl[kXLds];
+  __shared__ float2 xsl[kTokBlock * NGI];
+  __shared__ __attribute__((aligned(16))) uint8_t wlds[kGWaves][kWaveLds];
+  const int per = a.H / 128;
+  GroupItem it;
+  const int owner = blockIdx.x / per, rb = blockIdx.x % per;
+  if (!group_item(a, owner, it)) return;
   const int S = a.B * a.K;
-  const int D = G[0];
-  const int per = (a.H + kRowsPerItem - 1) / kRowsPerItem;
-  const int32_t *slots = G + 1 + S + (S + 1);
-  for (int item = blockIdx.x; item < D * per; item += gridDim.x) {
-    const int d = item / per;
-    const int row0 = ((item - d * per) * kWavesPerBlock + wave_in_block()) * kG3Iters * RPII;
-    const int e = G[1 + d];
-    const int q0 = G[1 + S + d], q1 = G[1 + S + d + 1];
-    RowLoads<BITS, NGI, kG3Iters> R;
-    if (row0 < a.H) R.issue(a.bank + (size_t)e * a.stride + a.gu_bytes, a.H, row0);
-    for (int c = q0; c < q1; c += HC) {
-      const int nt = min(HC, q1 - c);
-      __syncthreads();
-      for (int j = 0; j < nt; ++j)
-        stage_vec<NGI, false>(a.h_routed + (size_t)slots[c + j] * a.I, buf + j * NGI * kXPad, nullptr);
-      __syncthreads();
-      if (row0 < a.H) {
-        for (int j = 0; j < nt; ++j) {
-          const int s = slots[c + j];
-          XSlice xs;
-          read_slice(buf + j * NGI * kXPad, lane & (NGI - 1), 1.f, xs);
-          R.finish(xs, a.partial + (size_t)s * a.H, a.H, row0, a.w[s]);
+  const int lane = lane_id(), wv = wave_in_block();
+  const int n = lane & 15, qq = lane >> 4;
+  const uint8_t *base = (it.expert < 0 ? a.shared : a.bank + (size_t)it.expert * a.stride) + a.gu_bytes;
+  const int row = 128 * rb + 16 * wv + n;
+  const uint8_t *rec0 = base + (size_t)(128 * rb + 16 * wv) * RB;
+  const int32_t *slots = a.groups + 1 + S + (S + 1);
+  for (int tb = 0; tb < it.n; tb += kTokBlock) {
+    const int T = min(kTokBlock, it.n - tb);
+    auto hvec = [&](int u) { return it.expert < 0 ? S + tb + u : slots[it.q0 + tb + u]; };
+    MfmaRows<BITS, NGI> M;
+    M.run(rec0, a.hq, a.hsum, T, hvec, xl, xsl, wlds[wv]);
+#pragma unroll
+    for (int p = 0; p < kTokBlock / kTokPass; ++p) {
+      const int u = kTokPass * p + qq;
+      if (u < T) {
+        if (it.expert < 0) {
+          a.d_shared[(size_t)(tb + u) * a.H + row] = a.sigma[tb + u] * M.y[p];
+        } else {
+          const int slot = slots[it.q0 + tb + u];
+          a.partial[(size_t)slot * a.H + row] = a.w[slot] * M.y[p];
         }
       }
     }
@@ -321,34 +690,23 @@ __global__ __launch_bounds__(kBlock) void k_g4(const GroupArgs a) {
   reinterpret_cast<float4 *>(a.out)[f] = o;
 }
 
-// Workgroup caps of the grid-stride kernels (a few per CU).
-constexpr int kG2Blocks = 512;
-constexpr int kG3Blocks = 512;
-
 template <int BITS>
 struct GroupDispatch {
   template <int NGH, int NGI>
   static hipError_t layer(GroupArgs a, hipStream_t s, int phases) {
-    constexpr int RPIH = kWave / NGH, RPII = kWave / NGI;
     const bool sh = a.shared != nullptr;
     const int S = a.B * a.K;
-    const int dmax = S < a.E ? S : a.E;
+    const int owners = (S < a.E ? S : a.E) + (sh ? 1 : 0);
     a.n_router_blocks = blocks_for(a.E + (sh ? 1 : 0));
-    const int n1s = sh ? blocks_for(a.I / RPIH) : 0;
-    const long items2 = (long)dmax * (a.I / (kWavesPerBlock * kG2Iters * RPIH));
-    a.n_g2_routed_blocks = (int)(items2 < kG2Blocks ? items2 : kG2Blocks);
-    const int n2s = sh ? blocks_for((a.H / RPII + kG2DownIters - 1) / kG2DownIters) : 0;
-    const int rows3 = kWavesPerBlock * kG3Iters * RPII;
-    const long items3 = (long)dmax * ((a.H + rows3 - 1) / rows3);
-    const int n3 = (int)(items3 < kG3Blocks ? items3 : kG3Blocks);
     const int n4 = (a.B * (a.H / 4) + kBlock - 1) / kBlock;
-    if (phases & 1) hipLaunchKernelGGL((k_g1<BITS, NGH>), dim3(a.n_router_blocks + n1s), dim3(kBlock), 0, s, a);
+    if (phases & 1)
+      hipLaunchKernelGGL((k_g1<BITS, NGH>), dim3(a.n_router_blocks + a.B), dim3(kBlock), 0, s, a);
     if (phases & 2) {
       hipLaunchKernelGGL(k_g2r<BITS>, dim3(1), dim3(kRouteThreads), 0, s, a);
-      hipLaunchKernelGGL((k_g2<BITS, NGH, NGI>), dim3(a.n_g2_routed_blocks + n2s), dim3(kBlock), 0, s, a);
+      hipLaunchKernelGGL((k_g2<BITS, NGH, NGI>), dim3(owners * NGI), dim3(kGThreads), 0, s, a);
     }
     if (phases & 4) {
-      hipLaunchKernelGGL((k_g3<BITS, NGI>), dim3(n3), dim3(kBlock), 0, s, a);
+      hipLaunchKernelGGL((k_g3<BITS, NGI>), dim3(owners * (a.H / 128)), dim3(kGThreads), 0, s, a);
       hipLaunchKernelGGL(k_g4<BITS>, dim3(n4), dim3(kBlock), 0, s, a);
     }
     return hipGetLastError();

@@ -57,23 +57,26 @@ struct GroupArgs {
   float *out;
   int32_t *out_idx;          // [B][K] or null
   float *out_w;              // [B][K] or null
+  // workspace
   float *logits;             // [B][E]
   float *sigma;              // [B]
   int32_t *idx;              // [B][K]
   float *w;                  // [B][K]
-  float *h_shared;           // [B][I]
-  float *h_routed;           // [B*K][I]
+  uint16_t *xq;              // [B][3][H]  x as three bf16 parts, matrix-core order
+  float *xsum;               // [B][H/64][2] per group: sum of x, sum of its parts
+  float *xinv;               // [B]        RMS factor of x (1 without RMS scaling)
+  uint16_t *hq;              // [S+B][3][I] h (routed slots, then shared tokens), as xq
+  float *hsum;               // [S+B][I/64][2]
   float *d_shared;           // [B][H]
-  float *partial;            // [B*K][H]
-  int32_t *groups;           // D, expert[S], offset[S+1], slot[S]
+  float *partial;            // [S][H]
+  int32_t *groups;           // D, expert[S], offset[S+1], slot[S]; S = B*K
   int n_router_blocks;       // g1
-  int n_g2_routed_blocks;    // g2: routed workgroups (grid-stride over work items)
 };
 
-// The grouped layer: five launches (router + shared gate/up; routing and grouping;
-// routed gate/up by distinct expert + shared down; routed down by distinct
-// expert; combine). phases: bit 0 the first, bit 1 the second and third, bit 2
-// the last two.
+// The grouped layer: five launches (router + input preparation; routing and
+// grouping; gate/up of the distinct experts and the shared expert; their down
+// projections; combine). phases: bit 0 the first, bit 1 the second and third,
+// bit 2 the last two.
 hipError_t launch_group(const GroupArgs &a, hipStream_t s, int phases = 7);
 
 // Router + sigmoid gate + shared gate/up; routing + routed gate/up + shared down;
