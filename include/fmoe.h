@@ -190,11 +190,12 @@ fmoe_status fmoe_moe_layer(const fmoe_layer *L, int n_tokens, const float *x, co
                            void *stream);
 
 /* Diagnostic form of fmoe_moe_layer for per-kernel timing: enqueues only some of
- * the layer's kernels, in order. One token -- bit 0: router, shared-expert gate
- * and gate/up; bit 1: routing + routed gate/up + shared-expert down; bit 2: routed
- * down + combine. Several tokens -- bit 0: router and shared-expert gate/up; bit 1:
- * routing and grouping, then routed gate/up + shared-expert down; bit 2: routed
- * down, then combine. phases == 7 is fmoe_moe_layer. A kernel reads what the
+ * the layer's kernels, in order. One token -- bit 0: router and the shared-expert
+ * gate sigma; bit 1: routing + routed and shared-expert gate/up; bit 2: routed and
+ * shared-expert down + combine. Several tokens -- bit 0: router and the input
+ * preparation; bit 1: routing and grouping with the routed and shared-expert
+ * gate/up; bit 2: routed and shared-expert down, then combine. phases == 7 is
+ * fmoe_moe_layer. A kernel reads what the
  * previous ones left in ws, so partial calls are meaningful only after a full
  * call with the same ws and inputs. FMOE_ERR_BATCH if phases is outside 1..7;
  * otherwise the arguments and errors of fmoe_moe_layer. */

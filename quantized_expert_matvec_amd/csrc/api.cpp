@@ -97,6 +97,7 @@ fmoe_status layer_enqueue(const fmoe_layer *L, int B, const float *x, float rms_
     g.out_w = topk_w;
     g.logits = (float *)(ws + w.logits);
     g.sigma = (float *)(ws + w.sigma);
+    g.gdot = (float *)(ws + w.gdot);
     g.idx = (int32_t *)(ws + w.topk_idx);
     g.w = (float *)(ws + w.topk_w);
     g.xq = (uint16_t *)(ws + w.xq);

@@ -7,52 +7,57 @@
 // Several tokens against one weight row make a (skinny) dense contraction, so
 // the quantized experts run on the matrix cores: v_mfma_f32_16x16x32_bf16 with
 //   B operand = 16 weight rows x 32 columns of codes, each code c (BITS bits) as
-//               the exact bf16 value 1 + c / 2^BITS (c in the top mantissa bits,
-//               so the constant 1 stays small next to the code's part);
+//               the exact bf16 value 2 + c / 2^(BITS-1): bit pattern 0x4000 with c
+//               in the top mantissa bits, which a shift, a mask and a byte
+//               permute produce (the constant stays small next to the code's part);
 //   A operand = 16 rows = 4 tokens x {hi, mid, lo, 0}, where hi = bf16(x),
 //               mid = bf16(x - hi), lo = bf16(x - hi - mid): three bf16 parts
 //               that add up to the fp32 x exactly (in the normal range);
 //   D (fp32)  = per (token part, weight row) the sum over 32 columns.
 // Two MFMAs cover a 64-column group; per (row, group) the epilogue applies the
 // affine dequantization in the group-factored form
-//   sum_j (c_j s + b) x_j = 2^BITS s * (sum_j (1 + c_j / 2^BITS) x'_j - sum_j x'_j) + b sum_j x_j
+//   sum_j (c_j s + b) x_j = 2^(BITS-1) s * sum_j (2 + c_j / 2^(BITS-1)) x'_j
+//                           - 2^BITS s * sum_j x'_j + b sum_j x_j
 // where x' = hi + mid + lo is the value the matrix cores saw: the constant is
 // taken off with the sum of x' itself, the bias with the fp32 group sum of x.
 // Both sums are formed when x (or h) is prepared.
 //
-// Five launches:
-//   g1  router logits and sigmoid(g . x) of every token (fp32 rows, VALU, the
-//       tokens' x staged through LDS); other workgroups prepare each token's x
-//       for the matrix cores: RMS factor, per-group sums, bf16 parts
-//   g2r one workgroup: top-K of every token, then the distinct experts in
-//       order of first use and, for each, the ascending list of the slots
-//       (token t, choice k; slot = t*K + k) routed to it
+// Four launches:
+//   g1  router rows . x of every token (fp32 rows held in registers, VALU, the
+//       tokens' x read from L2), unscaled; other workgroups prepare each token's
+//       x for the matrix cores: RMS factor, per-group sums, bf16 parts
 //   g2  gate/up + SwiGLU of (shared expert or distinct expert, one group of 64
 //       gate/up pairs = 128 rows, one 16-row tile per wavefront) for all the
-//       tokens / slots using it; writes h as bf16 parts plus its group sums
+//       tokens / slots using it; writes h as bf16 parts plus its group sums.
+//       The routed workgroups first derive the routing themselves (top-K of
+//       every token, the distinct experts in ascending id and, for each, the
+//       ascending list of the slots (token t, choice k; slot = t*K + k) routed to
+//       it); the shared expert's workgroups need none and stream at once
 //   g3  down of (shared expert or distinct expert, 128 rows): per token
 //       sigma * (D_s h) into d_shared, per slot w * (D h) into partial[slot]
 //   g4  out = residual + the K per-slot outputs in slot order + sigma * shared
 #pragma once
+
+#include <algorithm>
+#include <type_traits>
 
 #include "layer_kernels.h"
 
 namespace fmoe {
 namespace dev {
 
-constexpr int kRouteThreads = 1024;
 constexpr int kMaxSlots = kMaxTokens * kMaxTopK;
-static_assert(kMaxSlots <= kRouteThreads, "one routing thread per slot");
-constexpr int kRouterTok = 8;  // tokens whose fp32 x the router stages in LDS at a time
-constexpr int kTokBlock = 16;  // tokens per pass over the weights
-constexpr int kTokPass = 4;    // tokens per MFMA row block (4 rows each: hi, mid, lo, 0)
-constexpr int kParts = 3;      // bf16 parts of an fp32 value
+// Tokens per work item: one MFMA row block (4 rows each: hi, mid, lo, 0). An
+// expert used by more tokens (the shared expert, mostly) gives several items,
+// which run on different compute units and re-read its rows (from the caches).
+constexpr int kTokBlock = 4;
+constexpr int kParts = 3;       // bf16 parts of an fp32 value
 constexpr int kGThreads = 512;  // workgroup of the matrix-core kernels: 8 wavefronts
 constexpr int kGWaves = kGThreads / kWave;
+constexpr int kMaxNG = 64;      // groups per row (4096 columns)
 constexpr int kWaveLds = 16 * (2 * 8 * 16 + 16) + 16 * 9 * 4;  // LDS bytes per wavefront for a weight chunk
-constexpr int kXBudget = 96 * 1024;                          // LDS bytes for staged x
-constexpr int kXLds = kXBudget + kParts * kTokBlock * 16;    // plus 16 B of padding per vector
-static_assert(kXBudget >= kParts * kTokBlock * 8 * 128, "x chunks of at least 8 groups");
+// staged x of an item: kParts * kTokBlock vectors of kMaxNG groups, 16 B of padding each
+constexpr int kXLds = kParts * kTokBlock * (kMaxNG * 128 + 16);
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
@@ -105,11 +110,11 @@ struct MCodes {
   uint32_t c0, c1, sb;
 };
 
-// Four low bytes of bf16 values (0x80 | code in the top mantissa bits) in v ->
-// two dwords of bf16 pairs: the high byte 0x3F above each (value 1 + c / 2^BITS);
+// Four low bytes of bf16 values (code in the top mantissa bits) in v -> two
+// dwords of bf16 pairs: the high byte 0x40 above each (value 2 + c / 2^(BITS-1));
 // v_perm_b32 selects bytes 0..3 from v and 4..7 from the constant.
 __device__ __forceinline__ void bf16_pairs(uint32_t v, uint32_t &p0, uint32_t &p1) {
-  constexpr uint32_t K = 0x3F3F3F3Fu;
+  constexpr uint32_t K = 0x40404040u;
   p0 = __builtin_amdgcn_perm(K, v, 0x04010400u);
   p1 = __builtin_amdgcn_perm(K, v, 0x04030402u);
 }
@@ -117,47 +122,46 @@ __device__ __forceinline__ void bf16_pairs(uint32_t v, uint32_t &p0, uint32_t &p
 // The B operands of the group's two MFMAs (8 codes each, in column order).
 template <int BITS>
 __device__ __forceinline__ void mfma_codes(const MCodes &m, uint4 &u0, uint4 &u1) {
-  // each byte's code moved to bits 6..(7 - BITS) of its byte, with bit 7 set
-  // (the low bit of the bf16 exponent of 1.0)
-  constexpr uint32_t E = 0x80808080u;
+  // each byte's code moved to bits 6..(7 - BITS) of its byte (bit 7, the low
+  // bit of the bf16 exponent of 2.0, stays clear)
   if constexpr (BITS == 4) {
-    bf16_pairs(((m.c0 << 3) & 0x78787878u) | E, u0.x, u0.y);
-    bf16_pairs(((m.c0 >> 1) & 0x78787878u) | E, u0.z, u0.w);
-    bf16_pairs(((m.c1 << 3) & 0x78787878u) | E, u1.x, u1.y);
-    bf16_pairs(((m.c1 >> 1) & 0x78787878u) | E, u1.z, u1.w);
+    bf16_pairs((m.c0 << 3) & 0x78787878u, u0.x, u0.y);
+    bf16_pairs((m.c0 >> 1) & 0x78787878u, u0.z, u0.w);
+    bf16_pairs((m.c1 << 3) & 0x78787878u, u1.x, u1.y);
+    bf16_pairs((m.c1 >> 1) & 0x78787878u, u1.z, u1.w);
   } else {
-    bf16_pairs(((m.c0 << 5) & 0x60606060u) | E, u0.x, u0.y);
-    bf16_pairs(((m.c0 << 3) & 0x60606060u) | E, u0.z, u0.w);
-    bf16_pairs(((m.c0 << 1) & 0x60606060u) | E, u1.x, u1.y);
-    bf16_pairs(((m.c0 >> 1) & 0x60606060u) | E, u1.z, u1.w);
+    bf16_pairs((m.c0 << 5) & 0x60606060u, u0.x, u0.y);
+    bf16_pairs((m.c0 << 3) & 0x60606060u, u0.z, u0.w);
+    bf16_pairs((m.c0 << 1) & 0x60606060u, u1.x, u1.y);
+    bf16_pairs((m.c0 >> 1) & 0x60606060u, u1.z, u1.w);
   }
 }
 
 // ------------------------------------------------------------------ matrix-core rows
 
 // Workgroup-cooperative (kGThreads threads): one 16-row tile per wavefront
-// (rows rec0 + r * RB, r = 0..15) against T <= kTokBlock vectors vec_of(u) of
-// a prepared source: part k (0..2) at xq_base + (3 vec + k) * NG * 64; per
-// group (sum x, sum x') at xs_base + 2 (vec * NG + g). The vectors are staged
-// in LDS (xl: kXLds bytes, xsl: kTokBlock * NG entries) in chunks of as many
-// groups as fit the budget: all of them for up to 4 tokens at NG = 64. On
-// return lane (n = lane % 16, qq = lane / 16) holds in y[p] row n for token
-// u = 4p + qq (meaningless for u >= T). Contains barriers: every thread of the
-// workgroup calls it with the same T.
+// (rows rec0 + r * RB, r = 0..15) against T <= kTokBlock vectors tokv[u] of a
+// prepared source: part k (0..2) at xq_base + (3 vec + k) * NG * 64; per group
+// (sum x, sum x') at xs_base + 2 (vec * NG + g). The vectors are staged in LDS
+// (xl: kXLds + 16 bytes, xsl: kTokBlock * NG + 1 entries). On return lane
+// (n = lane % 16, u = lane / 16) holds in y row n for token u (meaningless for
+// u >= T). Contains barriers: every thread of the workgroup calls it with the
+// same T.
 //
 // Weights stream in chunks of CG groups. A wavefront loads a chunk of its 16
 // rows with 16-byte loads over whole 16 CG-byte spans of each row (each load
 // instruction covers complete cache lines), keeps DEPTH chunks in flight, and
 // passes each chunk through its own LDS region (wl: kWaveLds bytes), from
 // which lane (n, q) reads the codes of k-block q of row n. The loop has no
-// branches around its loads, so every wait is exact; the empty asm statements
-// keep the optimiser from moving the loads (and the reads of their results)
-// away from where the pipeline needs them.
+// branches around its loads (its last round, which requests nothing, is a
+// separate copy), so every wait is exact; the empty asm statements keep the
+// optimiser from moving the loads (and the reads of their results) away from
+// where the pipeline needs them.
 template <int BITS, int NG>
 struct MfmaRows {
   static constexpr int CG = NG < 8 ? NG : 8;          // groups per chunk
   static constexpr int NC = NG / CG;                  // chunks per row
-  static constexpr int DEPTH = NC < 2 ? NC : 2;       // chunks in flight
+  static constexpr int DEPTH = NC < 4 ? NC : 4;       // chunks in flight
   static constexpr int HALVES = BITS == 4 ? 2 : 1;    // 16-byte code units per group
   static constexpr int NI = 16 * HALVES * CG / kWave; // 16-byte code loads per lane per chunk
   static constexpr int SBW = CG / 4;                  // scale/bias words per lane per chunk
@@ -165,54 +169,29 @@ struct MfmaRows {
   static constexpr int SBO = 16 * HALVES * NG;        // scale/bias words within a record
   static constexpr int RS = 16 * HALVES * CG + 16;    // LDS bytes per row of codes (padded)
   static constexpr int SBS = CG + 1;                  // LDS words per row of scale/bias (padded)
+  static constexpr int VS = NG * 128 + 16;            // LDS bytes per staged vector (padded)
+  static_assert(NG <= kMaxNG, "row width");
   static_assert(16 * RS + 64 * SBS <= kWaveLds, "chunk fits the wavefront's LDS region");
   static_assert(NC % DEPTH == 0, "whole rounds of chunks");
+  static_assert(kTokBlock * NG <= kGThreads, "one group sum per thread");
 
   struct Chunk {
     uint4 c[NI];
     uint32_t s[SBW];
   };
 
-  float y[kTokBlock / kTokPass];
+  float y;
 
-  template <typename VecOf>
-  __device__ __forceinline__ static void stage(const uint16_t *__restrict__ xq_base, const float *__restrict__ xs_base,
-                                               int T, VecOf vec_of, int g0, int gc, int vs, uint8_t *xl,
-                                               float2 *xsl) {
-    __syncthreads();  // earlier reads of xl / xsl are done
-    const int units = kParts * T * gc * 8;  // 16-byte units; vector v = 3u + k: token u, part k
-    for (int e = threadIdx.x; e < units; e += kGThreads) {
-      const int v = e / (gc * 8), r = e - v * (gc * 8);
-      const int gl = r >> 3, k16 = r & 7;
-      const int vu = v / kParts, vk = v - kParts * vu;
-      const uint16_t *src = xq_base + ((size_t)(kParts * vec_of(vu) + vk) * NG + g0 + gl) * 64 + 8 * k16;
-      *reinterpret_cast<uint4 *>(xl + v * vs + gl * 128 + k16 * 16) = *reinterpret_cast<const uint4 *>(src);
-    }
-    for (int e = threadIdx.x; e < T * gc; e += kGThreads) {
-      const int u = e / gc, gl = e - u * gc;
-      xsl[u * NG + gl] = reinterpret_cast<const float2 *>(xs_base)[(size_t)vec_of(u) * NG + g0 + gl];
-    }
-    __syncthreads();
-  }
+  // this lane's share of a chunk: code unit u = 64 k + lane is (row, half, group)
+  // = (u / (HALVES CG), u / CG % HALVES, u % CG); scale/bias: row lane / 4, words
+  // SBW (lane % 4) .. + SBW - 1
+  int goff[NI], loff[NI], gsoff, lsoff;
+  // where lane (n, q) reads group j of the chunk in its LDS region
+  int rcode, rsb;
 
-  template <int NP, bool WHOLE, typename VecOf>
-  __device__ __forceinline__ void loop(const uint8_t *__restrict__ rec0, const uint16_t *__restrict__ xq_base,
-                                       const float *__restrict__ xs_base, int T, VecOf vec_of, int gc, int vs,
-                                       uint8_t *xl, float2 *xsl, uint8_t *wl) {
+  __device__ __forceinline__ void offsets() {
     const int lane = lane_id();
-    const int q = lane >> 4;  // k-block of the A / B operands; token of D
-    const int i = lane & 15;  // A row (4 token + part) / weight row of B and D
-    int aoff[NP], xoff[NP];
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const int ua = min(kTokPass * p + (i >> 2), T - 1), ka = min(i & 3, kParts - 1);
-      aoff[p] = (kParts * ua + ka) * vs + q * 16;
-      xoff[p] = min(kTokPass * p + q, T - 1) * NG;
-    }
-    // this lane's share of a chunk: code unit u = 64 k + lane is (row, half, group)
-    // = (u / (HALVES CG), u / CG % HALVES, u % CG); scale/bias: row lane / 4, words
-    // SBW (lane % 4) .. + SBW - 1
-    int goff[NI], loff[NI];
+    const int q = lane >> 4, i = lane & 15;
 #pragma unroll
     for (int k = 0; k < NI; ++k) {
       const int u = kWave * k + lane;
@@ -222,135 +201,170 @@ struct MfmaRows {
       loff[k] = r * RS + 16 * (h * CG + j);
     }
     const int sr = lane >> 2, sp = lane & 3;
-    const int gsoff = sr * RB + SBO + 4 * SBW * sp;
-    const int lsoff = 16 * RS + 4 * (sr * SBS + SBW * sp);
-    // where lane (n = i, q) reads group j of the chunk in wl
-    const int rcode = BITS == 4 ? i * RS + 16 * (q >> 1) * CG + 8 * (q & 1) : i * RS + 4 * q;
-    const int rsb = 16 * RS + 4 * i * SBS;
+    gsoff = sr * RB + SBO + 4 * SBW * sp;
+    lsoff = 16 * RS + 4 * (sr * SBS + SBW * sp);
+    rcode = BITS == 4 ? i * RS + 16 * (q >> 1) * CG + 8 * (q & 1) : i * RS + 4 * q;
+    rsb = 16 * RS + 4 * i * SBS;
+  }
 
-    auto load_chunk = [&](int c, Chunk &k) {
+  __device__ __forceinline__ void load_chunk(const uint8_t *__restrict__ rec0, int c, Chunk &k) const {
 #pragma unroll
-      for (int t = 0; t < NI; ++t) k.c[t] = *reinterpret_cast<const uint4 *>(rec0 + goff[t] + 16 * CG * c);
-      if constexpr (SBW == 2) {
-        const uint2 v = *reinterpret_cast<const uint2 *>(rec0 + gsoff + 4 * CG * c);
-        k.s[0] = v.x;
-        k.s[1] = v.y;
-      } else {
-        k.s[0] = *reinterpret_cast<const uint32_t *>(rec0 + gsoff + 4 * CG * c);
-      }
-    };
-    Chunk ring[DEPTH];
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      load_chunk(d, ring[d]);
-      asm volatile("" ::: "memory");
-    }
-#pragma unroll 1
-    for (int cb = 0; cb < NC; cb += DEPTH) {
-#pragma unroll
-      for (int d = 0; d < DEPTH; ++d) {
-        const int c = cb + d;
-        if (!WHOLE && c > 0 && ((c * CG) & (gc - 1)) == 0) stage(xq_base, xs_base, T, vec_of, c * CG, gc, vs, xl, xsl);
-        // chunk c arrives here; into this wavefront's LDS region (the reads of
-        // the previous chunk were issued before, and LDS keeps a wavefront's order)
-#pragma unroll
-        for (int t = 0; t < NI; ++t) {
-          asm volatile("" : "+v"(ring[d].c[t].x), "+v"(ring[d].c[t].y), "+v"(ring[d].c[t].z), "+v"(ring[d].c[t].w));
-          *reinterpret_cast<uint4 *>(wl + loff[t]) = ring[d].c[t];
-        }
-#pragma unroll
-        for (int t = 0; t < SBW; ++t) {
-          asm volatile("" : "+v"(ring[d].s[t]));
-          *reinterpret_cast<uint32_t *>(wl + lsoff + 4 * t) = ring[d].s[t];
-        }
-        // refill (a clamped chunk past the end)
-        load_chunk(min(c + DEPTH, NC - 1), ring[d]);
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int j = 0; j < CG; ++j) {
-          const int g = c * CG + j;
-          const int gl = WHOLE ? g : (g & (gc - 1));
-          MCodes m;
-          if constexpr (BITS == 4) {
-            const uint2 v = *reinterpret_cast<const uint2 *>(wl + rcode + 16 * j);
-            m.c0 = v.x;
-            m.c1 = v.y;
-          } else {
-            m.c0 = *reinterpret_cast<const uint32_t *>(wl + rcode + 16 * j);
-            m.c1 = 0;
-          }
-          m.sb = *reinterpret_cast<const uint32_t *>(wl + rsb + 4 * j);
-          uint4 u0, u1;
-          mfma_codes<BITS>(m, u0, u1);
-          const float s = scale_of(m.sb) * (float)(1 << BITS);  // exact (power of two)
-          const float ns = -s;
-          const float bi = bias_of(m.sb);
-          const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, u0), b1 = __builtin_bit_cast(bf16x8_t, u1);
-#pragma unroll
-          for (int p = 0; p < NP; ++p) {
-            const uint8_t *src = xl + aoff[p] + gl * 128;
-            const bf16x8_t A0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(src));
-            const bf16x8_t A1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(src + 64));
-            const float2 X = xsl[xoff[p] + gl];
-            f32x4_t dd = {0.f, 0.f, 0.f, 0.f};
-            dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, b0, dd, 0, 0, 0);
-            dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, b1, dd, 0, 0, 0);
-            y[p] = fmaf(s, dd[0] + (dd[1] + dd[2]), fmaf(ns, X.y, fmaf(bi, X.x, y[p])));
-          }
-        }
-      }
+    for (int t = 0; t < NI; ++t) k.c[t] = *reinterpret_cast<const uint4 *>(rec0 + goff[t] + 16 * CG * c);
+    if constexpr (SBW == 2) {
+      const uint2 v = *reinterpret_cast<const uint2 *>(rec0 + gsoff + 4 * CG * c);
+      k.s[0] = v.x;
+      k.s[1] = v.y;
+    } else {
+      k.s[0] = *reinterpret_cast<const uint32_t *>(rec0 + gsoff + 4 * CG * c);
     }
   }
 
-  // rec0: record of the wavefront's first row; wl: its LDS region
-  template <typename VecOf>
-  __device__ __forceinline__ void run(const uint8_t *__restrict__ rec0, const uint16_t *__restrict__ xq_base,
-                                      const float *__restrict__ xs_base, int T, VecOf vec_of, uint8_t *xl,
-                                      float2 *xsl, uint8_t *wl) {
-    int gc = NG;  // groups per staged chunk of x (a power of two, a multiple of CG)
-    while (gc > CG && kParts * T * gc * 128 > kXBudget) gc >>= 1;
-    const int vs = gc * 128 + 16;  // LDS bytes per staged vector
+  // one batch of staging loads: 16-byte units e0 + k kGThreads of the
+  // 3 T NG 8 (vector 3u + part, unit); past the end, a clamped unit whose store
+  // goes to the spare slot at kXLds
+  static constexpr int kBatch = 4;
+  __device__ __forceinline__ static void load_batch(const uint16_t *__restrict__ xq_base, const int *tokv, int units,
+                                                    int e0, uint4 (&xv)[kBatch], int (&xdst)[kBatch]) {
 #pragma unroll
-    for (int p = 0; p < kTokBlock / kTokPass; ++p) y[p] = 0.f;
-    stage(xq_base, xs_base, T, vec_of, 0, gc, vs, xl, xsl);
-    const int np = (T + kTokPass - 1) / kTokPass;
-    const bool whole = gc == NG;
-    if (np == 1) {
-      if (whole)
-        loop<1, true>(rec0, xq_base, xs_base, T, vec_of, gc, vs, xl, xsl, wl);
-      else
-        loop<1, false>(rec0, xq_base, xs_base, T, vec_of, gc, vs, xl, xsl, wl);
-    } else if (np == 2) {
-      if (whole)
-        loop<2, true>(rec0, xq_base, xs_base, T, vec_of, gc, vs, xl, xsl, wl);
-      else
-        loop<2, false>(rec0, xq_base, xs_base, T, vec_of, gc, vs, xl, xsl, wl);
-    } else if (np == 3) {
-      if (whole)
-        loop<3, true>(rec0, xq_base, xs_base, T, vec_of, gc, vs, xl, xsl, wl);
-      else
-        loop<3, false>(rec0, xq_base, xs_base, T, vec_of, gc, vs, xl, xsl, wl);
-    } else {
-      if (whole)
-        loop<4, true>(rec0, xq_base, xs_base, T, vec_of, gc, vs, xl, xsl, wl);
-      else
-        loop<4, false>(rec0, xq_base, xs_base, T, vec_of, gc, vs, xl, xsl, wl);
+    for (int k = 0; k < kBatch; ++k) {
+      const int ee = e0 + k * kGThreads;
+      const int e = min(ee, units - 1);
+      const int vv = e / (NG * 8), rr = e - vv * (NG * 8);
+      const int vu = vv / kParts, vk = vv - kParts * vu;
+      xv[k] = *reinterpret_cast<const uint4 *>(xq_base + ((size_t)(kParts * tokv[vu] + vk) * NG) * 64 + 8 * rr);
+      xdst[k] = ee < units ? vv * VS + 16 * rr : kXLds;
     }
+  }
+
+  // rec0: record of the wavefront's first row; wl: its LDS region; tokv: an
+  // LDS table of kTokBlock vector indices, which fill(u) (run by thread u < T
+  // first) writes; after() runs on every thread right after x is requested, to
+  // request what the caller's epilogue needs.
+  template <typename Fill, typename After>
+  __device__ __forceinline__ void run(const uint8_t *__restrict__ rec0, const uint16_t *__restrict__ xq_base,
+                                      const float *__restrict__ xs_base, int T, int *tokv, Fill fill, After after,
+                                      uint8_t *xl, float2 *xsl, uint8_t *wl) {
+    const int lane = lane_id();
+    const int q = lane >> 4;  // k-block of the A / B operands; token of D
+    const int i = lane & 15;  // A row (4 token + part) / weight row of B and D
+    y = 0.f;
+    offsets();
+    // per-token tables (tokv, ...) from values the caller requested earlier
+    if ((int)threadIdx.x < T) fill((int)threadIdx.x);
+    __syncthreads();  // tokv is written; earlier reads of xl / xsl are done
+    // Requests in the order they are needed: x (its group sums, then its parts:
+    // 3 T NG 8 16-byte units) and the caller's epilogue
+    // values; the first weight chunk; once x is in LDS (a wavefront issues in
+    // order, and a long queue of weight requests ahead of the staging stores
+    // would hold them up), the rest of the first DEPTH chunks. The parts move in
+    // batches (loads of a batch before its stores); stores are unconditional
+    // (lanes past the end write a spare slot: xl at kXLds, xsl at kTokBlock * NG),
+    // so that the optimiser keeps a batch's loads together.
+    const int units = kParts * T * NG * 8;
+    float2 sv;
+    int sdst;
+    {
+      const int e = min((int)threadIdx.x, T * NG - 1);
+      const int u = e / NG, gl = e - u * NG;
+      sv = reinterpret_cast<const float2 *>(xs_base)[(size_t)tokv[u] * NG + gl];
+      sdst = (int)threadIdx.x < T * NG ? u * NG + gl : kTokBlock * NG;
+    }
+    uint4 xv[kBatch];
+    int xdst[kBatch];
+    load_batch(xq_base, tokv, units, threadIdx.x, xv, xdst);
+    after();
+    Chunk ring[DEPTH];
+    load_chunk(rec0, 0, ring[0]);
+    asm volatile("" ::: "memory");
+    xsl[sdst] = sv;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) *reinterpret_cast<uint4 *>(xl + xdst[k]) = xv[k];
+    for (int e0 = threadIdx.x + kBatch * kGThreads; e0 < units; e0 += kBatch * kGThreads) {
+      load_batch(xq_base, tokv, units, e0, xv, xdst);
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) *reinterpret_cast<uint4 *>(xl + xdst[k]) = xv[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int d = 1; d < DEPTH; ++d) {
+      load_chunk(rec0, d, ring[d]);
+      asm volatile("" ::: "memory");  // the loop's issue order (each chunk's loads together)
+    }
+    // A row i: token min(i / 4, T - 1), part min(i % 4, 2) (rows past T and the
+    // fourth part feed D rows that are never read); X: token min(q, T - 1)
+    const int aoff = (kParts * min(i >> 2, T - 1) + min(i & 3, kParts - 1)) * VS + q * 16;
+    const int xoff = min(q, T - 1) * NG;
+    // chunk c from ring slot d; then (if REFILL) slot d requests chunk c + DEPTH
+    auto step = [&](auto refill, int c, Chunk &slot) {
+      // chunk c arrives here; into this wavefront's LDS region (the reads of
+      // the previous chunk were issued before, and LDS keeps a wavefront's order)
+#pragma unroll
+      for (int t = 0; t < NI; ++t) {
+        asm volatile("" : "+v"(slot.c[t].x), "+v"(slot.c[t].y), "+v"(slot.c[t].z), "+v"(slot.c[t].w));
+        *reinterpret_cast<uint4 *>(wl + loff[t]) = slot.c[t];
+      }
+#pragma unroll
+      for (int t = 0; t < SBW; ++t) {
+        asm volatile("" : "+v"(slot.s[t]));
+        *reinterpret_cast<uint32_t *>(wl + lsoff + 4 * t) = slot.s[t];
+      }
+      if constexpr (decltype(refill)::value) {
+        load_chunk(rec0, c + DEPTH, slot);
+        asm volatile("" ::: "memory");
+      }
+#pragma unroll 4
+      for (int j = 0; j < CG; ++j) {
+        const int g = c * CG + j;
+        MCodes m;
+        if constexpr (BITS == 4) {
+          const uint2 v = *reinterpret_cast<const uint2 *>(wl + rcode + 16 * j);
+          m.c0 = v.x;
+          m.c1 = v.y;
+        } else {
+          m.c0 = *reinterpret_cast<const uint32_t *>(wl + rcode + 16 * j);
+          m.c1 = 0;
+        }
+        m.sb = *reinterpret_cast<const uint32_t *>(wl + rsb + 4 * j);
+        uint4 u0, u1;
+        mfma_codes<BITS>(m, u0, u1);
+        const float sp = scale_of(m.sb) * (float)(1 << (BITS - 1));  // exact (powers of two)
+        const float ns = scale_of(m.sb) * -(float)(1 << BITS);
+        const float bi = bias_of(m.sb);
+        const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, u0), b1 = __builtin_bit_cast(bf16x8_t, u1);
+        const uint8_t *src = xl + aoff + g * 128;
+        const bf16x8_t A0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(src));
+        const bf16x8_t A1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(src + 64));
+        const float2 X = xsl[xoff + g];
+        f32x4_t dd = {0.f, 0.f, 0.f, 0.f};
+        dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, b0, dd, 0, 0, 0);
+        dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, b1, dd, 0, 0, 0);
+        y = fmaf(sp, dd[0] + (dd[1] + dd[2]), fmaf(ns, X.y, fmaf(bi, X.x, y)));
+      }
+    };
+    // every round but the last refills its slots; the last round requests
+    // nothing, so no loads are left in flight when the stream ends
+#pragma unroll 1
+    for (int cb = 0; cb < NC - DEPTH; cb += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) step(std::true_type{}, cb + d, ring[d]);
+    }
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) step(std::false_type{}, NC - DEPTH + d, ring[d]);
   }
 };
 
 // ------------------------------------------------------------------ g1
 
 // g1: workgroups [0, n_router_blocks): router rows (one fp32 row per
-// wavefront; row E is the gate vector) for every token. Workgroups
-// n_router_blocks + t: token t's x for the matrix cores (RMS factor, per-group
-// sums of x, hi/lo bf16 parts in MFMA order).
+// wavefront; row E is the gate vector) against every token's x, unscaled.
+// Workgroups n_router_blocks + t: token t's x for the matrix cores (RMS factor
+// xinv, per-group sums of x, three bf16 parts in MFMA order).
 template <int BITS, int NGH>
 __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
   constexpr int NT = NGH / 4;
   constexpr int H = NGH * kGroup;
-  __shared__ float xl[kRouterTok][NGH * kXPad];
-  __shared__ float part[kRouterTok][kWavesPerBlock];
+  __shared__ float part[1][kWavesPerBlock];
   const int lane = lane_id();
   const bool rms = a.rms_eps >= 0.f;
   if ((int)blockIdx.x >= a.n_router_blocks) {
@@ -398,7 +412,10 @@ __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
     if (threadIdx.x == 0) a.xinv[t] = rms ? rms_inv(part[0], H, a.rms_eps) : 1.f;
     return;
   }
-  // ---- router rows
+  // ---- router rows: one fp32 row per wavefront, held in registers; the tokens'
+  // x vectors are read straight from memory (they sit in L2), two tokens in
+  // flight. The dot products are written unscaled: the RMS factor of each token
+  // (xinv, from the preparation workgroups) is applied by the routing kernel.
   const int n_rows = a.E + (a.gvec ? 1 : 0);
   const int row = blockIdx.x * kWavesPerBlock + wave_in_block();
   const int rr = min(row, n_rows - 1);
@@ -406,200 +423,269 @@ __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
   float4 wr[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) wr[t] = reinterpret_cast<const float4 *>(src)[lane + 64 * t];
-  for (int t0 = 0; t0 < a.B; t0 += kRouterTok) {
-    const int nt = min(kRouterTok, a.B - t0);
-    if (t0 > 0) __syncthreads();  // the previous chunk's reads of xl are done
-    for (int j = 0; j < nt; ++j) {
-      if (rms)
-        stage_vec<NGH, true>(a.x + (size_t)(t0 + j) * H, xl[j], part[j]);
+  float4 xa[NT], xb[NT];
+  auto load_x = [&](int t, float4(&v)[NT]) {
+    const float4 *xt4 = reinterpret_cast<const float4 *>(a.x + (size_t)t * H);
+#pragma unroll
+    for (int q = 0; q < NT; ++q) v[q] = xt4[lane + 64 * q];
+  };
+  // the dot product of token t (its x in v) with the row; the loaded words of v
+  // are needed from here on, not before
+  auto emit = [&](int t, float4(&v)[NT]) {
+#pragma unroll
+    for (int q = 0; q < NT; ++q) asm volatile("" : "+v"(v[q].x), "+v"(v[q].y), "+v"(v[q].z), "+v"(v[q].w));
+    float acc = 0.f;
+#pragma unroll
+    for (int q = 0; q < NT; ++q) {
+      acc = fmaf(wr[q].x, v[q].x, acc);
+      acc = fmaf(wr[q].y, v[q].y, acc);
+      acc = fmaf(wr[q].z, v[q].z, acc);
+      acc = fmaf(wr[q].w, v[q].w, acc);
+    }
+    const float d = seg_reduce<kWave>(acc);
+    if (lane == kWave - 1 && row < n_rows) {
+      if (row == a.E)
+        a.gdot[t] = d;
       else
-        stage_vec<NGH, false>(a.x + (size_t)(t0 + j) * H, xl[j], part[j]);
+        a.logits[(size_t)t * a.E + row] = d;
     }
-    __syncthreads();
-    for (int j = 0; j < nt; ++j) {
-      const float inv = rms ? rms_inv(part[j], H, a.rms_eps) : 1.f;
-      float acc = 0.f;
-#pragma unroll
-      for (int q = 0; q < NT; ++q) {
-        const float4 xv = *reinterpret_cast<const float4 *>(&xl[j][lds_index(4 * lane + 256 * q)]);
-        acc = fmaf(wr[q].x, xv.x * inv, acc);
-        acc = fmaf(wr[q].y, xv.y * inv, acc);
-        acc = fmaf(wr[q].z, xv.z * inv, acc);
-        acc = fmaf(wr[q].w, xv.w * inv, acc);
-      }
-      const float d = seg_reduce<kWave>(acc);
-      if (lane == kWave - 1 && row < n_rows) {
-        if (row == a.E)
-          a.sigma[t0 + j] = 1.f / (1.f + expf(-d));
-        else
-          a.logits[(size_t)(t0 + j) * a.E + row] = d;
-      }
-    }
+  };
+  load_x(0, xa);
+  asm volatile("" ::: "memory");
+#pragma unroll 1
+  for (int t = 0; t < a.B; t += 2) {
+    // (past the end: token B - 1 again, which rewrites its own values)
+    load_x(min(t + 1, a.B - 1), xb);
+    asm volatile("" ::: "memory");
+    emit(t, xa);
+    load_x(min(t + 2, a.B - 1), xa);
+    asm volatile("" ::: "memory");
+    emit(min(t + 1, a.B - 1), xb);
   }
-}
-
-// ------------------------------------------------------------------ g2r
-
-// g2r: one workgroup of kRouteThreads. Top-K of each token (one wavefront per
-// token), then the grouping, deterministic whatever the thread timing:
-//  - first[e] = the lowest slot routed to expert e (an atomic minimum);
-//  - the slots with first[e] == slot lead their expert; the leaders, in slot
-//    order, number the distinct experts 0..D-1;
-//  - every slot's position in its expert's list = the number of lower slots
-//    routed to the same expert, so each list is in ascending slot order.
-template <int BITS>  // (instantiated per bit width, like the rest of the layer)
-__global__ __launch_bounds__(kRouteThreads) void k_g2r(const GroupArgs a) {
-  constexpr int NW = kRouteThreads / kWave;
-  __shared__ int first[kMaxExperts];
-  __shared__ int sidx[kMaxSlots];
-  __shared__ int rank_of[kMaxSlots];
-  __shared__ int cnt[kMaxSlots];
-  __shared__ int off[kMaxSlots + 1];
-  __shared__ int wsum[NW];
-  const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
-  const int S = a.B * a.K;
-  for (int t = wave; t < a.B; t += NW) {
-    int idx[kMaxTopK];
-    float w[kMaxTopK];
-    wave_topk_lds(a.logits + (size_t)t * a.E, a.E, a.K, idx, w);
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j)
-      if (j == lane && j < a.K) {
-        const int s = t * a.K + j;
-        a.idx[s] = idx[j];
-        a.w[s] = w[j];
-        if (a.out_idx) a.out_idx[s] = idx[j];
-        if (a.out_w) a.out_w[s] = w[j];
-        sidx[s] = idx[j];
-      }
-  }
-  for (int e = threadIdx.x; e < a.E; e += kRouteThreads) first[e] = 0x7FFFFFFF;
-  __syncthreads();
-  const int s = threadIdx.x;
-  if (s < S) atomicMin(&first[sidx[s]], s);
-  __syncthreads();
-  const bool lead = s < S && first[sidx[s]] == s;
-  const unsigned long long bl = __ballot(lead);
-  if (lane == 0) wsum[wave] = __popcll(bl);
-  __syncthreads();
-  int before = 0, D = 0;
-#pragma unroll
-  for (int v = 0; v < NW; ++v) {
-    before += v < wave ? wsum[v] : 0;
-    D += wsum[v];
-  }
-  const int rank = before + __popcll(bl & ((1ull << lane) - 1ull));
-  if (lead) {
-    rank_of[s] = rank;
-    cnt[rank] = 0;
-  }
-  __syncthreads();
-  int r = 0, pos = 0;
-  if (s < S) {
-    const int e = sidx[s];
-    r = rank_of[first[e]];
-    for (int q = first[e]; q < s; ++q) pos += sidx[q] == e;
-    atomicAdd(&cnt[r], 1);
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int o = 0;
-    for (int q = 0; q < D; ++q) {
-      off[q] = o;
-      o += cnt[q];
-    }
-    off[D] = o;
-  }
-  __syncthreads();
-  int32_t *G = a.groups;
-  if (threadIdx.x == 0) G[0] = D;
-  if (lead) G[1 + rank] = sidx[s];
-  if ((int)threadIdx.x <= D) G[1 + S + threadIdx.x] = off[threadIdx.x];
-  if (s < S) G[1 + S + (S + 1) + off[r] + pos] = s;
 }
 
 // ------------------------------------------------------------------ g2, g3
 
-// Work of one owner: the shared expert (owner 0 when there is one; its tokens
-// 0..B-1) or distinct expert d (its slot list).
+// The grouping table G (int32, in the workspace), written by the routing:
+//   G[0] = D, the number of distinct routed experts; G[1] = NB, the number of
+//   routed token blocks;
+//   G[2 .. 2 + S): the slot lists of the distinct experts, in ascending expert
+//   id, each in ascending slot order (slot = token * K + choice);
+//   G[2 + S + 3k ..]: token block k < NB = {expert, start of its slots in the
+//   lists, number of slots (1..kTokBlock)}; an expert's blocks are consecutive.
+__host__ __device__ constexpr int g_size(int S) { return 2 + 4 * S; }
+
+// One work item: up to kTokBlock tokens of one expert.
 struct GroupItem {
   int expert;  // -1: the shared expert
-  int q0, n;   // slot-list range (routed) or tokens 0..B-1 (shared)
+  int q0;      // routed: start of the slots in the lists; shared: first token
+  int n;       // slots / tokens (1..kTokBlock)
 };
 
-// false if the owner does not exist (past the D distinct experts)
-__device__ __forceinline__ bool group_item(const GroupArgs &a, int owner, GroupItem &it) {
+// ------------------------------------------------------------------ routing
+
+// LDS scratch of block_route (it lives in the x staging buffer, which is free
+// until staging starts).
+struct RouteLds {
+  unsigned long long mask[kGWaves][kMaxExperts];  // [v][e]: lanes of wavefront v routed to e
+  int sidx[kMaxSlots];                           // expert of each slot
+  int eoff[kMaxExperts];                         // list offset of each present expert
+  int wtot[kGWaves];
+};
+
+// Top-K of every token and the grouping of the S = B*K slots by expert, by one
+// workgroup of kGThreads threads, deterministic whatever the thread timing:
+//  - top-K of each token (wavefront t % 8) from its unscaled logits, weights with
+//    the token's RMS factor;
+//  - mask[v][e] = the lanes of wavefront v (slots 64v ..) routed to expert e (LDS
+//    atomic ORs: the result does not depend on their order); a slot's position in
+//    its expert's list = the set bits below it, in its own and earlier wavefronts:
+//    ascending slot order within each list;
+//  - the distinct experts in ascending id, with the offsets of their lists and of
+//    their token blocks, from one workgroup scan over the experts (two per thread).
+// On return slotl[0..S) holds the lists and blk[3k ..] the token blocks (LDS);
+// returns NB. The writer workgroup also stores the routing (idx, w, sigma, the
+// caller's outputs) and the table G.
+__device__ __forceinline__ int block_route(const GroupArgs &a, RouteLds &R, int *slotl, int *blk, bool writer) {
+  static_assert(kMaxSlots <= kGThreads, "one thread per slot");
+  static_assert(kMaxExperts <= 2 * kGThreads, "two experts per thread in the scan");
+  const int lane = lane_id();
+  const int wave = wave_in_block();
   const int S = a.B * a.K;
-  const bool sh = a.shared != nullptr;
-  if (sh && owner == 0) {
-    it.expert = -1;
-    it.q0 = 0;
-    it.n = a.B;
-    return true;
+  const int nwl = (S + kWave - 1) / kWave;  // wavefronts holding slots
+  for (int i = threadIdx.x; i < nwl * a.E; i += kGThreads) R.mask[i / a.E][i % a.E] = 0ull;
+  for (int t = wave; t < a.B; t += kGWaves) {
+    const float inv = a.xinv[t];
+    const float gd = a.gvec ? a.gdot[t] : 0.f;
+    int idx[kMaxTopK];
+    float w[kMaxTopK];
+    wave_topk_lds(a.logits + (size_t)t * a.E, a.E, a.K, idx, w, inv);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (j == lane && j < a.K) {
+        const int s = t * a.K + j;
+        R.sidx[s] = idx[j];
+        if (writer) {
+          a.idx[s] = idx[j];
+          a.w[s] = w[j];
+          if (a.out_idx) a.out_idx[s] = idx[j];
+          if (a.out_w) a.out_w[s] = w[j];
+        }
+      }
+    if (writer && lane == 0 && a.gvec) a.sigma[t] = 1.f / (1.f + expf(-gd * inv));
   }
-  const int d = owner - (sh ? 1 : 0);
-  const int32_t *G = a.groups;
-  if (d >= G[0]) return false;
-  it.expert = G[1 + d];
-  it.q0 = G[1 + S + d];
-  it.n = G[1 + S + d + 1] - it.q0;
-  return true;
+  __syncthreads();
+  const int s = threadIdx.x;
+  const bool live = s < S;
+  const int e = live ? R.sidx[s] : 0;
+  if (live) atomicOr(&R.mask[wave][e], 1ull << lane);
+  __syncthreads();
+  int pos = 0;
+  if (live) {
+    pos = __popcll(R.mask[wave][e] & ((1ull << lane) - 1ull));
+    for (int v = 0; v < wave; ++v) pos += __popcll(R.mask[v][e]);
+  }
+  // experts 2x and 2x + 1 of thread x: slot counts and token blocks, then an
+  // integer scan of (present experts | slots << 11 | token blocks << 21)
+  const int e0 = 2 * (int)threadIdx.x, e1 = e0 + 1;
+  int n0 = 0, n1 = 0;
+  for (int v = 0; v < nwl; ++v) {
+    n0 += e0 < a.E ? __popcll(R.mask[v][e0]) : 0;
+    n1 += e1 < a.E ? __popcll(R.mask[v][e1]) : 0;
+  }
+  const int p0 = n0 > 0, p1 = n1 > 0;
+  const int nb0 = (n0 + kTokBlock - 1) / kTokBlock, nb1 = (n1 + kTokBlock - 1) / kTokBlock;
+  const int mine = (p0 + p1) | (n0 + n1) << 11 | (nb0 + nb1) << 21;
+  int v = mine;
+  v += dpp_i<0x111, 0xF>(v, 0);  // row_shr:1
+  v += dpp_i<0x112, 0xF>(v, 0);  // row_shr:2
+  v += dpp_i<0x114, 0xF>(v, 0);  // row_shr:4
+  v += dpp_i<0x118, 0xF>(v, 0);  // row_shr:8
+  v += dpp_i<0x142, 0xA>(v, 0);  // row_bcast:15
+  v += dpp_i<0x143, 0xC>(v, 0);  // row_bcast:31
+  if (lane == kWave - 1) R.wtot[wave] = v;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kGWaves; ++w) {
+    base += w < wave ? R.wtot[w] : 0;
+    tot += R.wtot[w];
+  }
+  const int ex = base + v - mine;  // exclusive prefix of this thread
+  const int o0 = (ex >> 11) & 1023, b0 = ex >> 21;
+  const int D = tot & 2047, NB = tot >> 21;
+  if (p0) R.eoff[e0] = o0;
+  if (p1) R.eoff[e1] = o0 + n0;
+  // token blocks of the two experts
+  for (int k = 0; k < nb0; ++k) {
+    blk[3 * (b0 + k)] = e0;
+    blk[3 * (b0 + k) + 1] = o0 + kTokBlock * k;
+    blk[3 * (b0 + k) + 2] = min(kTokBlock, n0 - kTokBlock * k);
+  }
+  for (int k = 0; k < nb1; ++k) {
+    blk[3 * (b0 + nb0 + k)] = e1;
+    blk[3 * (b0 + nb0 + k) + 1] = o0 + n0 + kTokBlock * k;
+    blk[3 * (b0 + nb0 + k) + 2] = min(kTokBlock, n1 - kTokBlock * k);
+  }
+  __syncthreads();
+  if (live) slotl[R.eoff[e] + pos] = s;
+  __syncthreads();
+  if (writer) {
+    int32_t *G = a.groups;
+    if (threadIdx.x == 0) {
+      G[0] = D;
+      G[1] = NB;
+    }
+    if (live) G[2 + s] = slotl[s];
+    for (int k = threadIdx.x; k < 3 * NB; k += kGThreads) G[2 + S + k] = blk[k];
+  }
+  return NB;
 }
 
+// ------------------------------------------------------------------ g2, g3
+
 // g2: gate/up + SwiGLU of 128 interleaved rows (64 pairs = group gi of the
-// inter dimension) of one owner, for all its tokens / slots. Wavefront w holds
-// rows 16w .. 16w + 15. h vectors: slot s at index s, shared-expert token t at
-// index S + t.
+// inter dimension) of one item's expert, for the item's tokens / slots.
+// Wavefront w holds rows 16w .. 16w + 15. h vectors: slot s at index s,
+// shared-expert token t at index S + t.
 template <int BITS, int NGH, int NGI>
 __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
   constexpr size_t RB = (size_t)NGH * gbytes<BITS>();
-  __shared__ __attribute__((aligned(16))) uint8_t xl[kXLds];
-  __shared__ float2 xsl[kTokBlock * NGH];
+  __shared__ __attribute__((aligned(16))) uint8_t xl[kXLds + 16];
+  __shared__ float2 xsl[kTokBlock * NGH + 1];
   __shared__ float2 hpart[kGWaves][kTokBlock];
   __shared__ __attribute__((aligned(16))) uint8_t wlds[kGWaves][kWaveLds];
-  GroupItem it;
-  const int owner = blockIdx.x / NGI, gi = blockIdx.x % NGI;
-  if (!group_item(a, owner, it)) return;  // uniform over the workgroup
+  __shared__ int slotl[kMaxSlots], blk[3 * kMaxSlots];
+  __shared__ int tokv[kTokBlock], hvl[kTokBlock];
+  static_assert(sizeof(RouteLds) <= kXLds, "routing scratch fits the staging buffer");
+  const bool sh = a.shared != nullptr;
   const int S = a.B * a.K;
   const int lane = lane_id(), wv = wave_in_block();
   const int n = lane & 15, qq = lane >> 4;
-  const uint8_t *base = it.expert < 0 ? a.shared : a.bank + (size_t)it.expert * a.stride;
-  const uint8_t *rec0 = base + (size_t)(128 * gi + 16 * wv) * RB;
-  const int32_t *slots = a.groups + 1 + S + (S + 1);
-  for (int tb = 0; tb < it.n; tb += kTokBlock) {
-    const int T = min(kTokBlock, it.n - tb);
-    // the token whose x item token u takes, and the index of its h vector
-    auto xtok = [&](int u) { return it.expert < 0 ? tb + u : slots[it.q0 + tb + u] / a.K; };
-    auto hvec = [&](int u) { return it.expert < 0 ? S + tb + u : slots[it.q0 + tb + u]; };
+  // Work items: (token block, group gi of 64 gate/up pairs); first the shared
+  // expert's token blocks (if any), then the routed ones. Persistent workgroups
+  // take items in grid stride; a workgroup derives the routing (every one the
+  // same; the one that meets the first routed item first publishes it) when it
+  // meets its first routed item, so the shared expert's items stream at once.
+  const int sh_items = sh ? (a.B + kTokBlock - 1) / kTokBlock * NGI : 0;
+  const int max_items = sh_items + S * NGI;
+  const bool writer = (int)blockIdx.x == sh_items % (int)gridDim.x;
+  int NB = -1;  // routing not derived yet
+  for (int item = blockIdx.x; item < max_items; item += gridDim.x) {
+    GroupItem it;
+    int gi;
+    if (item < sh_items) {
+      gi = item % NGI;
+      it.expert = -1;
+      it.q0 = kTokBlock * (item / NGI);
+      it.n = min(kTokBlock, a.B - it.q0);
+    } else {
+      if (NB < 0) NB = block_route(a, *reinterpret_cast<RouteLds *>(xl), slotl, blk, writer);
+      const int kb = (item - sh_items) / NGI;
+      if (kb >= NB) break;  // (uniform) later items are past the last block
+      gi = (item - sh_items) % NGI;
+      // (uniform values: kept in scalar registers)
+      it.expert = __builtin_amdgcn_readfirstlane(blk[3 * kb]);
+      it.q0 = __builtin_amdgcn_readfirstlane(blk[3 * kb + 1]);
+      it.n = __builtin_amdgcn_readfirstlane(blk[3 * kb + 2]);
+    }
+    const int T = it.n;
+    const uint8_t *base = it.expert < 0 ? a.shared : a.bank + (size_t)it.expert * a.stride;
+    const uint8_t *rec0 = base + (size_t)(128 * gi + 16 * __builtin_amdgcn_readfirstlane(wv)) * RB;
+    // thread u < T: slot of item token u (unused for the shared expert, whose
+    // item tokens are tokens q0 + u)
+    const int sl = slotl[it.expert < 0 ? 0 : it.q0 + min((int)threadIdx.x, T - 1)];
+    // tables: the token whose x item token u takes, the index of its h vector
+    auto fill = [&](int u) {
+      tokv[u] = it.expert < 0 ? it.q0 + u : sl / a.K;
+      hvl[u] = it.expert < 0 ? S + it.q0 + u : sl;
+    };
+    float tinv;  // RMS factor of the token of this lane's D rows
+    auto after = [&]() { tinv = a.xinv[tokv[min(qq, T - 1)]]; };
     MfmaRows<BITS, NGH> M;
-    M.run(rec0, a.xq, a.xsum, T, xtok, xl, xsl, wlds[wv]);
+    M.run(rec0, a.xq, a.xsum, T, tokv, fill, after, xl, xsl, wlds[wv]);
     // h = silu(gate) * up: gate rows are even, up rows odd (adjacent lanes)
-    float hs[kTokBlock / kTokPass] = {}, hr[kTokBlock / kTokPass] = {};
-#pragma unroll
-    for (int p = 0; p < kTokBlock / kTokPass; ++p) {
-      const int u = kTokPass * p + qq;
-      const float inv = u < T ? a.xinv[xtok(u)] : 0.f;
-      const float yv = M.y[p] * inv;
+    float hs = 0.f, hr = 0.f;
+    {
+      const float yv = M.y * tinv;
       const float up = dpp_f<0xB1, 0xF>(yv, 0.f);  // partner row (quad_perm [1,0,3,2])
-      if ((n & 1) == 0 && u < T) {
+      if ((n & 1) == 0 && qq < T) {
         const float h = silu(yv) * up;
         const int pl = 8 * wv + (n >> 1);  // pair within the group
-        uint16_t *dst = a.hq + (size_t)(kParts * hvec(u)) * a.I + 64 * gi + mfma_pos<BITS>(pl);
+        uint16_t *dst = a.hq + (size_t)(kParts * hvl[qq]) * a.I + 64 * gi + mfma_pos<BITS>(pl);
         uint32_t pt[3];
         float r;
         bf16_split3(h, pt, r);
 #pragma unroll
         for (int k = 0; k < kParts; ++k) dst[(size_t)k * a.I] = (uint16_t)pt[k];
-        hs[p] += h;
-        hr[p] += r;
+        hs = h;
+        hr = r;
       }
     }
     // group sums of h: the even lanes of each 16-lane row (odd lanes hold 0), then
     // the wavefronts in order
-#pragma unroll
-    for (int p = 0; p < kTokBlock / kTokPass; ++p) {
-      float r = hs[p], e = hr[p];
+    {
+      float r = hs, e = hr;
       r += dpp_f<0xB1, 0xF>(r, 0.f);   // lanes n, n^1
       e += dpp_f<0xB1, 0xF>(e, 0.f);
       r += dpp_f<0x4E, 0xF>(r, 0.f);   // n, n^2
@@ -608,8 +694,7 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
       e += dpp_f<0x141, 0xF>(e, 0.f);
       r += dpp_f<0x140, 0xF>(r, 0.f);  // row_mirror: n, 15-n
       e += dpp_f<0x140, 0xF>(e, 0.f);
-      const int u = kTokPass * p + qq;
-      if (n == 0 && u < T) hpart[wv][u] = make_float2(r, e);
+      if (n == 0 && qq < T) hpart[wv][qq] = make_float2(r, e);
     }
     __syncthreads();
     if ((int)threadIdx.x < T) {
@@ -620,49 +705,63 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
         t.x += hpart[v][u].x;
         t.y += hpart[v][u].y;
       }
-      reinterpret_cast<float2 *>(a.hsum)[(size_t)hvec(u) * NGI + gi] = t;
+      reinterpret_cast<float2 *>(a.hsum)[(size_t)hvl[u] * NGI + gi] = t;
     }
   }
 }
 
-// g3: down of 128 rows (part rb) of one owner for all its tokens / slots:
-// shared: d_shared[t][row] = sigma[t] * row . h_shared[t]; routed:
-// partial[slot][row] = w[slot] * row . h[slot]. Wavefront w holds rows 16w .. +15.
+// g3: down of 128 rows (part rb) of one item's expert for the item's tokens /
+// slots: shared: d_shared[t][row] = sigma[t] * row . h_shared[t]; routed:
+// partial[slot][row] = w[slot] * row . h[slot]. Wavefront w holds rows
+// 16w .. 16w + 15. Workgroups: the shared expert's token blocks, then one per
+// possible routed token block (those past G[1] exit at once), each times the
+// H / 128 row parts.
 template <int BITS, int NGI>
 __global__ __launch_bounds__(kGThreads) void k_g3(const GroupArgs a) {
   constexpr size_t RB = (size_t)NGI * gbytes<BITS>();
-  __shared__ __attribute__((aligned(16))) uint8_t xl[kXLds];
-  __shared__ float2 xsl[kTokBlock * NGI];
+  __shared__ __attribute__((aligned(16))) uint8_t xl[kXLds + 16];
+  __shared__ float2 xsl[kTokBlock * NGI + 1];
   __shared__ __attribute__((aligned(16))) uint8_t wlds[kGWaves][kWaveLds];
+  __shared__ int tokv[kTokBlock], oidx[kTokBlock];
   const int per = a.H / 128;
-  GroupItem it;
-  const int owner = blockIdx.x / per, rb = blockIdx.x % per;
-  if (!group_item(a, owner, it)) return;
+  const bool sh = a.shared != nullptr;
   const int S = a.B * a.K;
+  const int shb = sh ? (a.B + kTokBlock - 1) / kTokBlock : 0;
+  const int ib = blockIdx.x / per, rb = blockIdx.x % per;
+  const int32_t *G = a.groups;
+  GroupItem it;
+  if (ib < shb) {
+    it.expert = -1;
+    it.q0 = kTokBlock * ib;
+    it.n = min(kTokBlock, a.B - it.q0);
+  } else {
+    const int kb = ib - shb;
+    // (requested together: one round trip)
+    const int nb = G[1];
+    it.expert = G[2 + S + 3 * kb];
+    it.q0 = G[2 + S + 3 * kb + 1];
+    it.n = G[2 + S + 3 * kb + 2];
+    if (kb >= nb) return;  // uniform over the workgroup
+  }
+  const int T = it.n;
   const int lane = lane_id(), wv = wave_in_block();
   const int n = lane & 15, qq = lane >> 4;
   const uint8_t *base = (it.expert < 0 ? a.shared : a.bank + (size_t)it.expert * a.stride) + a.gu_bytes;
   const int row = 128 * rb + 16 * wv + n;
   const uint8_t *rec0 = base + (size_t)(128 * rb + 16 * wv) * RB;
-  const int32_t *slots = a.groups + 1 + S + (S + 1);
-  for (int tb = 0; tb < it.n; tb += kTokBlock) {
-    const int T = min(kTokBlock, it.n - tb);
-    auto hvec = [&](int u) { return it.expert < 0 ? S + tb + u : slots[it.q0 + tb + u]; };
-    MfmaRows<BITS, NGI> M;
-    M.run(rec0, a.hq, a.hsum, T, hvec, xl, xsl, wlds[wv]);
-#pragma unroll
-    for (int p = 0; p < kTokBlock / kTokPass; ++p) {
-      const int u = kTokPass * p + qq;
-      if (u < T) {
-        if (it.expert < 0) {
-          a.d_shared[(size_t)(tb + u) * a.H + row] = a.sigma[tb + u] * M.y[p];
-        } else {
-          const int slot = slots[it.q0 + tb + u];
-          a.partial[(size_t)slot * a.H + row] = a.w[slot] * M.y[p];
-        }
-      }
-    }
-  }
+  float *const outp = it.expert < 0 ? a.d_shared : a.partial;
+  const float *const scl = it.expert < 0 ? a.sigma : a.w;
+  const int sl = G[2 + (it.expert < 0 ? 0 : it.q0 + min((int)threadIdx.x, T - 1))];
+  // tables: the h vector of item token u, and its output row (token or slot)
+  auto fill = [&](int u) {
+    tokv[u] = it.expert < 0 ? S + it.q0 + u : sl;
+    oidx[u] = it.expert < 0 ? it.q0 + u : sl;
+  };
+  float osc;  // sigma (shared) or routing weight of this lane's D rows
+  auto after = [&]() { osc = scl[oidx[min(qq, T - 1)]]; };
+  MfmaRows<BITS, NGI> M;
+  M.run(rec0, a.hq, a.hsum, T, tokv, fill, after, xl, xsl, wlds[wv]);
+  if (qq < T) outp[(size_t)oidx[qq] * a.H + row] = osc * M.y;
 }
 
 // g4: out[t] = residual[t] + sum_k partial[t*K + k] (k ascending) + d_shared[t]
@@ -672,16 +771,23 @@ __global__ __launch_bounds__(kBlock) void k_g4(const GroupArgs a) {
   const int h4 = a.H / 4;
   if (f >= a.B * h4) return;
   const int t = f / h4, i = f - t * h4;
+  // every load issued before the first add (clamped choices past K are not added)
+  float4 p[kMaxTopK];
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k)
+    p[k] = reinterpret_cast<const float4 *>(a.partial)[(size_t)(t * a.K + min(k, a.K - 1)) * h4 + i];
+  const float4 q = reinterpret_cast<const float4 *>(a.shared ? a.d_shared : a.residual)[f];
   float4 o = reinterpret_cast<const float4 *>(a.residual)[f];
-  for (int k = 0; k < a.K; ++k) {
-    const float4 p = reinterpret_cast<const float4 *>(a.partial)[(size_t)(t * a.K + k) * h4 + i];
-    o.x += p.x;
-    o.y += p.y;
-    o.z += p.z;
-    o.w += p.w;
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    if (k < a.K) {
+      o.x += p[k].x;
+      o.y += p[k].y;
+      o.z += p[k].z;
+      o.w += p[k].w;
+    }
   }
   if (a.shared) {
-    const float4 q = reinterpret_cast<const float4 *>(a.d_shared)[f];
     o.x += q.x;
     o.y += q.y;
     o.z += q.z;
@@ -690,23 +796,36 @@ __global__ __launch_bounds__(kBlock) void k_g4(const GroupArgs a) {
   reinterpret_cast<float4 *>(a.out)[f] = o;
 }
 
+// Compute units of the current device (cached per device): the persistent
+// gate/up kernel runs one workgroup per compute unit (its LDS admits one).
+inline int cu_count() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 template <int BITS>
 struct GroupDispatch {
   template <int NGH, int NGI>
   static hipError_t layer(GroupArgs a, hipStream_t s, int phases) {
     const bool sh = a.shared != nullptr;
     const int S = a.B * a.K;
-    const int owners = (S < a.E ? S : a.E) + (sh ? 1 : 0);
+    const int shb = sh ? (a.B + kTokBlock - 1) / kTokBlock : 0;  // shared token blocks
     a.n_router_blocks = blocks_for(a.E + (sh ? 1 : 0));
     const int n4 = (a.B * (a.H / 4) + kBlock - 1) / kBlock;
     if (phases & 1)
       hipLaunchKernelGGL((k_g1<BITS, NGH>), dim3(a.n_router_blocks + a.B), dim3(kBlock), 0, s, a);
-    if (phases & 2) {
-      hipLaunchKernelGGL(k_g2r<BITS>, dim3(1), dim3(kRouteThreads), 0, s, a);
-      hipLaunchKernelGGL((k_g2<BITS, NGH, NGI>), dim3(owners * NGI), dim3(kGThreads), 0, s, a);
-    }
+    if (phases & 2)
+      hipLaunchKernelGGL((k_g2<BITS, NGH, NGI>), dim3(std::min((shb + S) * NGI, cu_count())), dim3(kGThreads), 0,
+                         s, a);
     if (phases & 4) {
-      hipLaunchKernelGGL((k_g3<BITS, NGI>), dim3(owners * (a.H / 128)), dim3(kGThreads), 0, s, a);
+      hipLaunchKernelGGL((k_g3<BITS, NGI>), dim3((shb + S) * (a.H / 128)), dim3(kGThreads), 0, s, a);
       hipLaunchKernelGGL(k_g4<BITS>, dim3(n4), dim3(kBlock), 0, s, a);
     }
     return hipGetLastError();

@@ -58,8 +58,9 @@ struct GroupArgs {
   int32_t *out_idx;          // [B][K] or null
   float *out_w;              // [B][K] or null
   // workspace
-  float *logits;             // [B][E]
+  float *logits;             // [B][E]     router rows . x, before the RMS factor
   float *sigma;              // [B]
+  float *gdot;               // [B]        gate vector . x, before the RMS factor
   int32_t *idx;              // [B][K]
   float *w;                  // [B][K]
   uint16_t *xq;              // [B][3][H]  x as three bf16 parts, matrix-core order
@@ -69,14 +70,14 @@ struct GroupArgs {
   float *hsum;               // [S+B][I/64][2]
   float *d_shared;           // [B][H]
   float *partial;            // [S][H]
-  int32_t *groups;           // D, expert[S], offset[S+1], slot[S]; S = B*K
+  int32_t *groups;           // D, NB, slot lists[S], token blocks {expert, start, n}[S]; S = B*K
   int n_router_blocks;       // g1
 };
 
-// The grouped layer: five launches (router + input preparation; routing and
-// grouping; gate/up of the distinct experts and the shared expert; their down
-// projections; combine). phases: bit 0 the first, bit 1 the second and third,
-// bit 2 the last two.
+// The grouped layer: four launches (router + input preparation; routing,
+// grouping and the gate/up of the distinct experts and the shared expert; their
+// down projections; combine). phases: bit 0 the first, bit 1 the second, bit 2
+// the last two.
 hipError_t launch_group(const GroupArgs &a, hipStream_t s, int phases = 7);
 
 // Router + sigmoid gate + shared gate/up; routing + routed gate/up + shared down;

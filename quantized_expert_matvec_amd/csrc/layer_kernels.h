@@ -201,9 +201,12 @@ __device__ __forceinline__ float key_value(int k) { return __int_as_float(k >= 0
 // chosen element's key becomes INT_MIN, below every real key, as are the padding
 // slots (e >= E). Then the renormalised softmax weights of the chosen K,
 // w_j = exp(l_j - l_0) / sum (renormalising over the chosen K cancels the full
-// softmax denominator). Results are wavefront-uniform.
+// softmax denominator). The logits may be held unscaled: lscale > 0 is the
+// factor that turns them into the true logits (it does not change the order), so
+// w_j = exp((l_j - l_0) * lscale) / sum. Results are wavefront-uniform.
 template <int VPL>
-__device__ __forceinline__ void wave_topk_ballot(const float *lg, int E, int K, int *idx, float *w) {
+__device__ __forceinline__ void wave_topk_ballot(const float *lg, int E, int K, int *idx, float *w,
+                                                 float lscale = 1.f) {
   constexpr int kGone = (int)0x80000000;
   const int lane = lane_id();
   int key[VPL];
@@ -252,7 +255,7 @@ __device__ __forceinline__ void wave_topk_ballot(const float *lg, int E, int K, 
   for (int j = 0; j < kMaxTopK; ++j) {
     w[j] = 0.f;
     if (j < K) {
-      w[j] = __expf(lv[j] - lv[0]);
+      w[j] = __expf((lv[j] - lv[0]) * lscale);
       sum += w[j];
     }
   }
@@ -261,11 +264,12 @@ __device__ __forceinline__ void wave_topk_ballot(const float *lg, int E, int K, 
   for (int j = 0; j < kMaxTopK; ++j) w[j] *= inv;
 }
 
-__device__ __forceinline__ void wave_topk_lds(const float *lg, int E, int K, int *idx, float *w) {
+__device__ __forceinline__ void wave_topk_lds(const float *lg, int E, int K, int *idx, float *w,
+                                              float lscale = 1.f) {
   if (E <= 512)
-    wave_topk_ballot<8>(lg, E, K, idx, w);
+    wave_topk_ballot<8>(lg, E, K, idx, w, lscale);
   else
-    wave_topk_ballot<16>(lg, E, K, idx, w);
+    wave_topk_ballot<16>(lg, E, K, idx, w, lscale);
 }
 
 // Block-wide top-K: one wavefront computes it from the logits in LDS and

@@ -63,11 +63,13 @@ struct LayerWs {
   size_t d_shared;  // fp32 [B][hidden]  sigma * shared-expert output
   // B > 1 only (tokens grouped by expert):
   size_t partial;   // fp32 [B][K][hidden]  w * routed-expert output, per (token, slot)
-  size_t groups;    // int32 [1 + S + (S + 1) + S], S = B*K: number of distinct experts D,
-                    // their expert ids [S], offsets of their slot lists [S + 1], slot lists [S]
+  size_t groups;    // int32 [2 + 4 S], S = B*K: the number of distinct experts, the number of
+                    // token blocks, the slot lists grouped by expert [S], and per token block
+                    // {expert, start of its slots, number of slots} [3 S]
   size_t xq;        // bf16 [B][3][hidden]     the input as three bf16 parts
   size_t xsum;      // fp32 [B][hidden/64][2]  its per-group sums (of x, of hi + lo)
   size_t xinv;      // fp32 [B]                its RMS factor
+  size_t gdot;      // fp32 [B]                g . x before the RMS factor
   size_t hq;        // bf16 [S + B][3][inter]  the SwiGLU outputs as three bf16 parts
   size_t hsum;      // fp32 [S + B][inter/64][2] their per-group sums
   size_t total;
@@ -90,10 +92,11 @@ inline LayerWs layer_ws(int B, int E, int K, int hidden, int inter) {
   w.d_shared = take(sizeof(float) * (size_t)B * hidden);
   const size_t S = (size_t)B * K;
   w.partial = take(B > 1 ? sizeof(float) * S * hidden : 0);
-  w.groups = take(B > 1 ? sizeof(int32_t) * (3 * S + 2) : 0);
+  w.groups = take(B > 1 ? sizeof(int32_t) * (4 * S + 2) : 0);
   w.xq = take(B > 1 ? sizeof(uint16_t) * 3 * (size_t)B * hidden : 0);
   w.xsum = take(B > 1 ? 2 * sizeof(float) * (size_t)B * (hidden / 64) : 0);
   w.xinv = take(B > 1 ? sizeof(float) * (size_t)B : 0);
+  w.gdot = take(B > 1 ? sizeof(float) * (size_t)B : 0);
   w.hq = take(B > 1 ? sizeof(uint16_t) * 3 * (S + B) * inter : 0);
   w.hsum = take(B > 1 ? 2 * sizeof(float) * (S + B) * (inter / 64) : 0);
   w.total = o;
