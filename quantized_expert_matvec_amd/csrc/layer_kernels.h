@@ -264,12 +264,82 @@ __device__ __forceinline__ void wave_topk_ballot(const float *lg, int E, int K, 
   for (int j = 0; j < kMaxTopK; ++j) w[j] *= inv;
 }
 
+__device__ __forceinline__ int wave_max_i(int g) {
+  constexpr int kGone = (int)0x80000000;
+  g = max(g, dpp_i<0xB1, 0xF>(g, kGone));
+  g = max(g, dpp_i<0x4E, 0xF>(g, kGone));
+  g = max(g, dpp_i<0x141, 0xF>(g, kGone));
+  g = max(g, dpp_i<0x140, 0xF>(g, kGone));
+  g = max(g, dpp_i<0x142, 0xA>(g, kGone));
+  g = max(g, dpp_i<0x143, 0xC>(g, kGone));
+  return __builtin_amdgcn_readlane(g, 63);
+}
+
+// Fast path of the top-K, exact when it answers: lane l holds the VPL
+// consecutive elements VPL l .. VPL l + VPL - 1 (so a lower lane means a lower
+// index), and its maximum (first position among equal keys) and second key. K
+// rounds over the 64 lane maxima (wavefront maximum, lowest lane holding it)
+// give the K best lane maxima in order; they are the top K of all elements when
+// no second key reaches the K-th of them (a lane holding two of the top K, or a
+// tie, fails that test: then the caller runs the full rounds). Returns whether
+// it answered; w as wave_topk_ballot.
+template <int VPL>
+__device__ __forceinline__ bool wave_topk_fast(const float *lg, int E, int K, int *idx, float *w, float lscale) {
+  constexpr int kGone = (int)0x80000000;
+  const int lane = lane_id();
+  int key[VPL];
+#pragma unroll
+  for (int m = 0; m < VPL; ++m) {
+    const int e = VPL * lane + m;
+    const float t = lg[min(e, E - 1)];
+    key[m] = e < E ? order_key(t == t ? t : -INFINITY) : kGone;
+  }
+  int m1 = key[0], p1 = 0, m2 = kGone;
+#pragma unroll
+  for (int m = 1; m < VPL; ++m) {
+    const bool gt = key[m] > m1;
+    m2 = gt ? m1 : max(m2, key[m]);
+    p1 = gt ? m : p1;
+    m1 = gt ? key[m] : m1;
+  }
+  int a = m1, T = kGone;
+  float lv[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    idx[j] = 0;
+    lv[j] = 0.f;
+    if (j < K) {
+      const int g = wave_max_i(a);
+      const int L = __ffsll((long long)__ballot(a == g)) - 1;
+      idx[j] = VPL * L + __builtin_amdgcn_readlane(p1, L);
+      lv[j] = key_value(g);
+      a = lane == L ? kGone : a;
+      T = g;
+    }
+  }
+  if (wave_max_i(m2) >= T) return false;
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    w[j] = 0.f;
+    if (j < K) {
+      w[j] = __expf((lv[j] - lv[0]) * lscale);
+      sum += w[j];
+    }
+  }
+  const float inv = 1.f / sum;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) w[j] *= inv;
+  return true;
+}
+
 __device__ __forceinline__ void wave_topk_lds(const float *lg, int E, int K, int *idx, float *w,
                                               float lscale = 1.f) {
-  if (E <= 512)
-    wave_topk_ballot<8>(lg, E, K, idx, w, lscale);
-  else
+  if (E <= 512) {
+    if (!wave_topk_fast<8>(lg, E, K, idx, w, lscale)) wave_topk_ballot<8>(lg, E, K, idx, w, lscale);
+  } else {
     wave_topk_ballot<16>(lg, E, K, idx, w, lscale);
+  }
 }
 
 // Block-wide top-K: one wavefront computes it from the logits in LDS and
@@ -355,28 +425,39 @@ struct Phase1Args {
   uint64_t *trace;
 };
 
-// Phase 1: the router. One fp32 router row per wavefront (lane l covers columns
-// 4l + 256t + 0..3); row E is the shared expert's gate vector, giving
-// sigmoid(g . x).
+// Phase 1: the router. Each fp32 router row is split over kRouterSplit
+// wavefronts of a workgroup (half h: lane l covers columns 4l + 256t + 0..3 for
+// t in [h NT/2, (h+1) NT/2)), so that the 8 MB of rows spread over every compute
+// unit; the halves' sums are added in order. Row E is the shared expert's gate
+// vector, giving sigmoid(g . x).
+template <int NGH>
+constexpr int router_split() {
+  return NGH / 4 >= 2 ? 2 : 1;
+}
 template <int NGH>
 __global__ __launch_bounds__(kBlock) void k_phase1(const Phase1Args a) {
   constexpr int NT = NGH / 4;  // hidden / 256
   constexpr int H = NGH * kGroup;
   constexpr int X4 = (NGH * 16 + kBlock - 1) / kBlock;
+  constexpr int SPLIT = router_split<NGH>();
+  constexpr int NTW = NT / SPLIT;  // float4 per lane of this wavefront's part of the row
   __shared__ float xl[NGH * kXPad];
   __shared__ float part[kWavesPerBlock];
+  __shared__ float dpart[kWavesPerBlock];
   const int lane = lane_id();
   const bool rms = a.rms_eps >= 0.f;
   trace_mark(a.trace, 0);
   const int n_rows = a.E + (a.gvec ? 1 : 0);
-  const int row = blockIdx.x * kWavesPerBlock + wave_in_block();
+  const int wv = wave_in_block();
+  const int half = wv % SPLIT;
+  const int row = blockIdx.x * (kWavesPerBlock / SPLIT) + wv / SPLIT;
   const int rr = min(row, n_rows - 1);
-  const float *src = rr == a.E ? a.gvec : a.router + (size_t)rr * H;
+  const float *src = (rr == a.E ? a.gvec : a.router + (size_t)rr * H) + 256 * NTW * half;
   Staged<X4> xst;
   stage_load(a.x, NGH * 16, xst);
-  float4 w[NT];
+  float4 w[NTW];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) w[t] = reinterpret_cast<const float4 *>(src)[lane + 64 * t];
+  for (int t = 0; t < NTW; ++t) w[t] = reinterpret_cast<const float4 *>(src)[lane + 64 * t];
   __builtin_amdgcn_sched_barrier(0);
   if (rms)
     stage_store<X4, true>(xst, NGH * 16, xl, part);
@@ -387,15 +468,22 @@ __global__ __launch_bounds__(kBlock) void k_phase1(const Phase1Args a) {
   const float inv = rms ? rms_inv(part, H, a.rms_eps) : 1.f;
   float acc = 0.f;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const float4 xv = *reinterpret_cast<const float4 *>(&xl[lds_index(4 * lane + 256 * t)]);
+  for (int t = 0; t < NTW; ++t) {
+    const float4 xv = *reinterpret_cast<const float4 *>(&xl[lds_index(4 * lane + 256 * (t + NTW * half))]);
     acc = fmaf(w[t].x, xv.x * inv, acc);
     acc = fmaf(w[t].y, xv.y * inv, acc);
     acc = fmaf(w[t].z, xv.z * inv, acc);
     acc = fmaf(w[t].w, xv.w * inv, acc);
   }
-  const float d = seg_reduce<kWave>(acc);
-  if (lane == kWave - 1 && row < n_rows) {
+  float d = seg_reduce<kWave>(acc);
+  if constexpr (SPLIT > 1) {
+    if (lane == kWave - 1) dpart[wv] = d;
+    __syncthreads();
+    d = dpart[wv - half];
+#pragma unroll
+    for (int h = 1; h < SPLIT; ++h) d += dpart[wv - half + h];
+  }
+  if (lane == kWave - 1 && half == 0 && row < n_rows) {
     if (row == a.E)
       *a.sigma = 1.f / (1.f + expf(-d));
     else
@@ -654,7 +742,7 @@ struct LayerGeom {
     const bool sh = L.shared != nullptr;
     rbh = (size_t)NGH * (bits == 4 ? 36 : 20);
     rbi = (size_t)NGI * (bits == 4 ? 36 : 20);
-    n1r = blocks_for(L.E + (sh ? 1 : 0));
+    n1r = (L.E + (sh ? 1 : 0) + kWavesPerBlock / router_split<NGH>() - 1) / (kWavesPerBlock / router_split<NGH>());
     n1s = 0;
     wps = (L.I / RPIH + kP2GateUpIters - 1) / kP2GateUpIters;
     n2r = blocks_for((long)wps * L.K);
