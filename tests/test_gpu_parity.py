@@ -263,3 +263,45 @@ def test_stack_vs_oracle(device, B):
             assert list(gi[l, t]) == list(ri), (l, t)
             assert_close(ha[l, t], ref, f"stack B={B} token {t} layer {l}")
             h = ref
+
+
+# --------------------------------------------------------------------------- routing edge cases
+
+def _steered_router(seed, n_exp, hidden, x0, rows):
+    """The generated router with some rows replaced by c * u, u = x0 / (x0 . x0): for a
+    token near x0 the logit of such a row is about c, far above the random rows
+    (std 0.02 * sqrt(hidden)); rows given the same c are identical, an exact tie."""
+    R = synth.router(seed, 0, n_exp, hidden).copy()
+    u = x0.astype(np.float64) / float(np.dot(x0.astype(np.float64), x0.astype(np.float64)))
+    for e, c in rows.items():
+        R[e] = (c * u).astype(np.float32)
+    return R
+
+
+@pytest.mark.parametrize("case", ["same_lane_pair", "spread"])
+def test_routing_exact_ties_and_same_lane_pairs(device, case):
+    """Top-K edge cases, one-token and grouped paths, against the oracle exactly:
+    an exact tie of two identical router rows (lower index first, equal weights), and
+    (same_lane_pair) the two best experts among the same 8 consecutive logits, which
+    the lane-maxima fast path of the top-K cannot answer alone."""
+    hidden, inter, n_exp, bits = 1024, 512, 512, 4
+    if case == "same_lane_pair":
+        k, rows, want = 4, {5: 6.0, 6: 5.9, 100: 5.0, 300: 5.0}, [5, 6, 100, 300]
+    else:
+        k, rows, want = 3, {9: 6.0, 100: 5.0, 300: 5.0}, [9, 100, 300]
+    print(f"routing edge case {case}", flush=True)
+    x0 = _x(77, 0, hidden)[0]
+    noise = _x(77, 1, hidden, 3)
+    X = (x0[None, :] + 0.3 * noise).astype(np.float32)  # tokens near x0
+    R = _steered_router(77, n_exp, hidden, x0, rows)
+    L = device_layer(77, 0, bits, n_exp, k, hidden, inter, device)
+    L = qem.Layer(to_dev(R, device), L.shared_gate, L.bank, L.shared, n_exp, k, hidden, inter, bits)
+    OL = OracleLayer(77, 0, bits, n_exp, k, hidden, inter)
+    OL.R = R
+    for t in range(X.shape[0]):
+        _, ri, rw, _ = OL.forward(X[t], X[t])
+        assert list(ri) == want, (t, ri)
+    # one token at a time (one-token kernels), then all tokens grouped
+    for t in range(X.shape[0]):
+        assert _check_layer(device, OL, L, X[t:t + 1], X[t:t + 1], f"{case} token {t} alone") == 0
+    assert _check_layer(device, OL, L, X, X, f"{case} grouped") == 0
