@@ -56,8 +56,6 @@ constexpr int kGThreads = 512;  // workgroup of the matrix-core kernels: 8 wavef
 constexpr int kGWaves = kGThreads / kWave;
 constexpr int kMaxNG = 64;      // groups per row (4096 columns)
 constexpr int kWaveLds = 16 * (2 * 8 * 16 + 16) + 16 * 9 * 4;  // LDS bytes per wavefront for a weight chunk
-// staged x of an item: kParts * kTokBlock vectors of kMaxNG groups, 16 B of padding each
-constexpr int kXLds = kParts * kTokBlock * (kMaxNG * 128 + 16);
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
@@ -139,12 +137,13 @@ __device__ __forceinline__ void mfma_codes(const MCodes &m, uint4 &u0, uint4 &u1
 
 // ------------------------------------------------------------------ matrix-core rows
 
-// Workgroup-cooperative (kGThreads threads): one 16-row tile per wavefront
-// (rows rec0 + r * RB, r = 0..15) against T <= kTokBlock vectors tokv[u] of a
-// prepared source: part k (0..2) at xq_base + (3 vec + k) * NG * 64; per group
-// (sum x, sum x') at xs_base + 2 (vec * NG + g). The vectors are staged in LDS
-// (xl: kXLds + 16 bytes, xsl: kTokBlock * NG + 1 entries). On return lane
-// (n = lane % 16, u = lane / 16) holds in y row n for token u (meaningless for
+// Workgroup-cooperative (kGThreads threads): NTILE tiles of 16 rows per
+// wavefront (tile i: rows rec0 + i * tile_stride + r * RB, r = 0..15) against
+// T <= kTokBlock vectors tokv[u] of a prepared source: part k (0..2) at
+// xq_base + (3 vec + k) * NG * 64; per group (sum x, sum x') at
+// xs_base + 2 (vec * NG + g). The vectors are staged in LDS once (xl: XL + 16
+// bytes, xsl: kTokBlock * NG + 1 entries). As each tile ends, lane (n = lane %
+// 16, u = lane / 16) holds in y row n of the tile for token u (meaningless for
 // u >= T). Contains barriers: every thread of the workgroup calls it with the
 // same T.
 //
@@ -157,11 +156,12 @@ __device__ __forceinline__ void mfma_codes(const MCodes &m, uint4 &u0, uint4 &u1
 // separate copy), so every wait is exact; the empty asm statements keep the
 // optimiser from moving the loads (and the reads of their results) away from
 // where the pipeline needs them.
-template <int BITS, int NG>
+template <int BITS, int NG, int NTILE = 1>
 struct MfmaRows {
   static constexpr int CG = NG < 8 ? NG : 8;          // groups per chunk
   static constexpr int NC = NG / CG;                  // chunks per row
-  static constexpr int DEPTH = NC < 4 ? NC : 4;       // chunks in flight
+  static constexpr int NCT = NTILE * NC;              // chunks of the whole stream
+  static constexpr int DEPTH = NCT < 4 ? NCT : 4;     // chunks in flight
   static constexpr int HALVES = BITS == 4 ? 2 : 1;    // 16-byte code units per group
   static constexpr int NI = 16 * HALVES * CG / kWave; // 16-byte code loads per lane per chunk
   static constexpr int SBW = CG / 4;                  // scale/bias words per lane per chunk
@@ -170,9 +170,11 @@ struct MfmaRows {
   static constexpr int RS = 16 * HALVES * CG + 16;    // LDS bytes per row of codes (padded)
   static constexpr int SBS = CG + 1;                  // LDS words per row of scale/bias (padded)
   static constexpr int VS = NG * 128 + 16;            // LDS bytes per staged vector (padded)
+  static constexpr int XL = kParts * kTokBlock * VS;  // LDS bytes of staged x (a spare 16 B follow)
   static_assert(NG <= kMaxNG, "row width");
   static_assert(16 * RS + 64 * SBS <= kWaveLds, "chunk fits the wavefront's LDS region");
-  static_assert(NC % DEPTH == 0, "whole rounds of chunks");
+  static_assert(NCT % DEPTH == 0, "whole rounds of chunks");
+  static_assert((NC & (NC - 1)) == 0, "chunks per row: a power of two");
   static_assert(kTokBlock * NG <= kGThreads, "one group sum per thread");
 
   struct Chunk {
@@ -207,21 +209,26 @@ struct MfmaRows {
     rsb = 16 * RS + 4 * i * SBS;
   }
 
-  __device__ __forceinline__ void load_chunk(const uint8_t *__restrict__ rec0, int c, Chunk &k) const {
+  // chunk c of the stream: chunk c % NC of tile c / NC (tile rows tile_stride
+  // bytes after the previous tile's)
+  __device__ __forceinline__ void load_chunk(const uint8_t *__restrict__ rec0, size_t tile_stride, int c,
+                                             Chunk &k) const {
+    const uint8_t *r = rec0 + (size_t)(c / NC) * tile_stride;
+    const int cc = c % NC;
 #pragma unroll
-    for (int t = 0; t < NI; ++t) k.c[t] = *reinterpret_cast<const uint4 *>(rec0 + goff[t] + 16 * CG * c);
+    for (int t = 0; t < NI; ++t) k.c[t] = *reinterpret_cast<const uint4 *>(r + goff[t] + 16 * CG * cc);
     if constexpr (SBW == 2) {
-      const uint2 v = *reinterpret_cast<const uint2 *>(rec0 + gsoff + 4 * CG * c);
+      const uint2 v = *reinterpret_cast<const uint2 *>(r + gsoff + 4 * CG * cc);
       k.s[0] = v.x;
       k.s[1] = v.y;
     } else {
-      k.s[0] = *reinterpret_cast<const uint32_t *>(rec0 + gsoff + 4 * CG * c);
+      k.s[0] = *reinterpret_cast<const uint32_t *>(r + gsoff + 4 * CG * cc);
     }
   }
 
   // one batch of staging loads: 16-byte units e0 + k kGThreads of the
   // 3 T NG 8 (vector 3u + part, unit); past the end, a clamped unit whose store
-  // goes to the spare slot at kXLds
+  // goes to the spare slot at XL
   static constexpr int kBatch = 4;
   __device__ __forceinline__ static void load_batch(const uint16_t *__restrict__ xq_base, const int *tokv, int units,
                                                     int e0, uint4 (&xv)[kBatch], int (&xdst)[kBatch]) {
@@ -232,18 +239,21 @@ struct MfmaRows {
       const int vv = e / (NG * 8), rr = e - vv * (NG * 8);
       const int vu = vv / kParts, vk = vv - kParts * vu;
       xv[k] = *reinterpret_cast<const uint4 *>(xq_base + ((size_t)(kParts * tokv[vu] + vk) * NG) * 64 + 8 * rr);
-      xdst[k] = ee < units ? vv * VS + 16 * rr : kXLds;
+      xdst[k] = ee < units ? vv * VS + 16 * rr : XL;
     }
   }
 
-  // rec0: record of the wavefront's first row; wl: its LDS region; tokv: an
-  // LDS table of kTokBlock vector indices, which fill(u) (run by thread u < T
-  // first) writes; after() runs on every thread right after x is requested, to
-  // request what the caller's epilogue needs.
-  template <typename Fill, typename After>
-  __device__ __forceinline__ void run(const uint8_t *__restrict__ rec0, const uint16_t *__restrict__ xq_base,
-                                      const float *__restrict__ xs_base, int T, int *tokv, Fill fill, After after,
-                                      uint8_t *xl, float2 *xsl, uint8_t *wl) {
+  // rec0: record of the wavefront's first row of its first tile (the NTILE tiles
+  // of 16 rows lie tile_stride bytes apart); wl: its LDS region; tokv: an LDS
+  // table of kTokBlock vector indices, which fill(u) (run by thread u < T first)
+  // writes; after() runs on every thread right after x is requested, to request
+  // what the caller's epilogue needs; tile_done(tile) runs on every thread as
+  // each tile's stream ends, with its rows in y.
+  template <typename Fill, typename After, typename TileDone>
+  __device__ __forceinline__ void run(const uint8_t *__restrict__ rec0, size_t tile_stride,
+                                      const uint16_t *__restrict__ xq_base, const float *__restrict__ xs_base, int T,
+                                      int *tokv, Fill fill, After after, TileDone tile_done, uint8_t *xl,
+                                      float2 *xsl, uint8_t *wl) {
     const int lane = lane_id();
     const int q = lane >> 4;  // k-block of the A / B operands; token of D
     const int i = lane & 15;  // A row (4 token + part) / weight row of B and D
@@ -258,7 +268,7 @@ struct MfmaRows {
     // order, and a long queue of weight requests ahead of the staging stores
     // would hold them up), the rest of the first DEPTH chunks. The parts move in
     // batches (loads of a batch before its stores); stores are unconditional
-    // (lanes past the end write a spare slot: xl at kXLds, xsl at kTokBlock * NG),
+    // (lanes past the end write a spare slot: xl at XL, xsl at kTokBlock * NG),
     // so that the optimiser keeps a batch's loads together.
     const int units = kParts * T * NG * 8;
     float2 sv;
@@ -274,8 +284,13 @@ struct MfmaRows {
     load_batch(xq_base, tokv, units, threadIdx.x, xv, xdst);
     after();
     Chunk ring[DEPTH];
-    load_chunk(rec0, 0, ring[0]);
-    asm volatile("" ::: "memory");
+    // narrow rows stage little x: then the whole prologue goes out at once
+    constexpr int EARLY = NG <= 16 ? DEPTH : 1;
+#pragma unroll
+    for (int d = 0; d < EARLY; ++d) {
+      load_chunk(rec0, tile_stride, d, ring[d]);
+      asm volatile("" ::: "memory");
+    }
     xsl[sdst] = sv;
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) *reinterpret_cast<uint4 *>(xl + xdst[k]) = xv[k];
@@ -287,8 +302,8 @@ struct MfmaRows {
     }
     __syncthreads();
 #pragma unroll
-    for (int d = 1; d < DEPTH; ++d) {
-      load_chunk(rec0, d, ring[d]);
+    for (int d = EARLY; d < DEPTH; ++d) {
+      load_chunk(rec0, tile_stride, d, ring[d]);
       asm volatile("" ::: "memory");  // the loop's issue order (each chunk's loads together)
     }
     // A row i: token min(i / 4, T - 1), part min(i % 4, 2) (rows past T and the
@@ -310,12 +325,12 @@ struct MfmaRows {
         *reinterpret_cast<uint32_t *>(wl + lsoff + 4 * t) = slot.s[t];
       }
       if constexpr (decltype(refill)::value) {
-        load_chunk(rec0, c + DEPTH, slot);
+        load_chunk(rec0, tile_stride, c + DEPTH, slot);
         asm volatile("" ::: "memory");
       }
 #pragma unroll 4
       for (int j = 0; j < CG; ++j) {
-        const int g = c * CG + j;
+        const int g = (c % NC) * CG + j;
         MCodes m;
         if constexpr (BITS == 4) {
           const uint2 v = *reinterpret_cast<const uint2 *>(wl + rcode + 16 * j);
@@ -341,16 +356,20 @@ struct MfmaRows {
         dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, b1, dd, 0, 0, 0);
         y = fmaf(sp, dd[0] + (dd[1] + dd[2]), fmaf(ns, X.y, fmaf(bi, X.x, y)));
       }
+      if (c % NC == NC - 1) {  // (uniform) the tile's last chunk
+        tile_done(c / NC);
+        y = 0.f;
+      }
     };
     // every round but the last refills its slots; the last round requests
     // nothing, so no loads are left in flight when the stream ends
 #pragma unroll 1
-    for (int cb = 0; cb < NC - DEPTH; cb += DEPTH) {
+    for (int cb = 0; cb < NCT - DEPTH; cb += DEPTH) {
 #pragma unroll
       for (int d = 0; d < DEPTH; ++d) step(std::true_type{}, cb + d, ring[d]);
     }
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) step(std::false_type{}, NC - DEPTH + d, ring[d]);
+    for (int d = 0; d < DEPTH; ++d) step(std::false_type{}, NCT - DEPTH + d, ring[d]);
   }
 };
 
@@ -469,16 +488,17 @@ __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
 // The grouping table G (int32, in the workspace), written by the routing:
 //   G[0] = D, the number of distinct routed experts; G[1] = NB, the number of
 //   routed token blocks;
-//   G[2 .. 2 + S): the slot lists of the distinct experts, in ascending expert
-//   id, each in ascending slot order (slot = token * K + choice);
-//   G[2 + S + 3k ..]: token block k < NB = {expert, start of its slots in the
-//   lists, number of slots (1..kTokBlock)}; an expert's blocks are consecutive.
-__host__ __device__ constexpr int g_size(int S) { return 2 + 4 * S; }
+//   G[2 + kBlkInts k ..]: token block k < NB = {expert, number of slots n
+//   (1..kTokBlock), its slots (slot = token * K + choice)}. The distinct experts
+//   come in ascending id, their slots in ascending order, an expert's blocks
+//   consecutive. One record holds all a down-projection workgroup needs.
+constexpr int kBlkInts = 2 + kTokBlock;
+__host__ __device__ constexpr int g_size(int S) { return 2 + kBlkInts * S; }
 
 // One work item: up to kTokBlock tokens of one expert.
 struct GroupItem {
   int expert;  // -1: the shared expert
-  int q0;      // routed: start of the slots in the lists; shared: first token
+  int q0;      // routed: offset of its slots in the block table; shared: first token
   int n;       // slots / tokens (1..kTokBlock)
 };
 
@@ -503,9 +523,9 @@ struct RouteLds {
 //    ascending slot order within each list;
 //  - the distinct experts in ascending id, with the offsets of their lists and of
 //    their token blocks, from one workgroup scan over the experts (two per thread).
-// On return slotl[0..S) holds the lists and blk[3k ..] the token blocks (LDS);
-// returns NB. The writer workgroup also stores the routing (idx, w, sigma, the
-// caller's outputs) and the table G.
+// On return blk[kBlkInts k ..] holds the token blocks (LDS; slotl[0..S) the
+// lists, as scratch); returns NB. The writer workgroup also stores the routing
+// (idx, w, sigma, the caller's outputs) and the table G.
 __device__ __forceinline__ int block_route(const GroupArgs &a, RouteLds &R, int *slotl, int *blk, bool writer) {
   static_assert(kMaxSlots <= kGThreads, "one thread per slot");
   static_assert(kMaxExperts <= 2 * kGThreads, "two experts per thread in the scan");
@@ -576,19 +596,26 @@ __device__ __forceinline__ int block_route(const GroupArgs &a, RouteLds &R, int 
   const int D = tot & 2047, NB = tot >> 21;
   if (p0) R.eoff[e0] = o0;
   if (p1) R.eoff[e1] = o0 + n0;
-  // token blocks of the two experts
-  for (int k = 0; k < nb0; ++k) {
-    blk[3 * (b0 + k)] = e0;
-    blk[3 * (b0 + k) + 1] = o0 + kTokBlock * k;
-    blk[3 * (b0 + k) + 2] = min(kTokBlock, n0 - kTokBlock * k);
-  }
-  for (int k = 0; k < nb1; ++k) {
-    blk[3 * (b0 + nb0 + k)] = e1;
-    blk[3 * (b0 + nb0 + k) + 1] = o0 + n0 + kTokBlock * k;
-    blk[3 * (b0 + nb0 + k) + 2] = min(kTokBlock, n1 - kTokBlock * k);
-  }
   __syncthreads();
   if (live) slotl[R.eoff[e] + pos] = s;
+  __syncthreads();
+  // token blocks of the two experts, with their slots
+  for (int k = 0; k < nb0; ++k) {
+    const int n = min(kTokBlock, n0 - kTokBlock * k), q = o0 + kTokBlock * k;
+    int *r = blk + kBlkInts * (b0 + k);
+    r[0] = e0;
+    r[1] = n;
+#pragma unroll
+    for (int u = 0; u < kTokBlock; ++u) r[2 + u] = slotl[q + min(u, n - 1)];
+  }
+  for (int k = 0; k < nb1; ++k) {
+    const int n = min(kTokBlock, n1 - kTokBlock * k), q = o0 + n0 + kTokBlock * k;
+    int *r = blk + kBlkInts * (b0 + nb0 + k);
+    r[0] = e1;
+    r[1] = n;
+#pragma unroll
+    for (int u = 0; u < kTokBlock; ++u) r[2 + u] = slotl[q + min(u, n - 1)];
+  }
   __syncthreads();
   if (writer) {
     int32_t *G = a.groups;
@@ -596,8 +623,7 @@ __device__ __forceinline__ int block_route(const GroupArgs &a, RouteLds &R, int 
       G[0] = D;
       G[1] = NB;
     }
-    if (live) G[2 + s] = slotl[s];
-    for (int k = threadIdx.x; k < 3 * NB; k += kGThreads) G[2 + S + k] = blk[k];
+    for (int k = threadIdx.x; k < kBlkInts * NB; k += kGThreads) G[2 + k] = blk[k];
   }
   return NB;
 }
@@ -611,13 +637,16 @@ __device__ __forceinline__ int block_route(const GroupArgs &a, RouteLds &R, int 
 template <int BITS, int NGH, int NGI>
 __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
   constexpr size_t RB = (size_t)NGH * gbytes<BITS>();
-  __shared__ __attribute__((aligned(16))) uint8_t xl[kXLds + 16];
+  // staged x, and before it the routing scratch
+  constexpr size_t kXlBytes = MfmaRows<BITS, NGH>::XL + 16 > sizeof(RouteLds) ? MfmaRows<BITS, NGH>::XL + 16
+                                                                               : sizeof(RouteLds);
+  __shared__ __attribute__((aligned(16))) uint8_t xl[kXlBytes];
   __shared__ float2 xsl[kTokBlock * NGH + 1];
   __shared__ float2 hpart[kGWaves][kTokBlock];
   __shared__ __attribute__((aligned(16))) uint8_t wlds[kGWaves][kWaveLds];
-  __shared__ int slotl[kMaxSlots], blk[3 * kMaxSlots];
+  __shared__ int slotl[kMaxSlots], blk[kBlkInts * kMaxSlots];
   __shared__ int tokv[kTokBlock], hvl[kTokBlock];
-  static_assert(sizeof(RouteLds) <= kXLds, "routing scratch fits the staging buffer");
+  static_assert(sizeof(RouteLds) <= sizeof(xl), "routing scratch fits the staging buffer");
   const bool sh = a.shared != nullptr;
   const int S = a.B * a.K;
   const int lane = lane_id(), wv = wave_in_block();
@@ -645,16 +674,16 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
       if (kb >= NB) break;  // (uniform) later items are past the last block
       gi = (item - sh_items) % NGI;
       // (uniform values: kept in scalar registers)
-      it.expert = __builtin_amdgcn_readfirstlane(blk[3 * kb]);
-      it.q0 = __builtin_amdgcn_readfirstlane(blk[3 * kb + 1]);
-      it.n = __builtin_amdgcn_readfirstlane(blk[3 * kb + 2]);
+      it.expert = __builtin_amdgcn_readfirstlane(blk[kBlkInts * kb]);
+      it.n = __builtin_amdgcn_readfirstlane(blk[kBlkInts * kb + 1]);
+      it.q0 = kBlkInts * kb + 2;
     }
     const int T = it.n;
     const uint8_t *base = it.expert < 0 ? a.shared : a.bank + (size_t)it.expert * a.stride;
     const uint8_t *rec0 = base + (size_t)(128 * gi + 16 * __builtin_amdgcn_readfirstlane(wv)) * RB;
     // thread u < T: slot of item token u (unused for the shared expert, whose
     // item tokens are tokens q0 + u)
-    const int sl = slotl[it.expert < 0 ? 0 : it.q0 + min((int)threadIdx.x, T - 1)];
+    const int sl = blk[it.expert < 0 ? 0 : it.q0 + min((int)threadIdx.x, T - 1)];
     // tables: the token whose x item token u takes, the index of its h vector
     auto fill = [&](int u) {
       tokv[u] = it.expert < 0 ? it.q0 + u : sl / a.K;
@@ -662,12 +691,13 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
     };
     float tinv;  // RMS factor of the token of this lane's D rows
     auto after = [&]() { tinv = a.xinv[tokv[min(qq, T - 1)]]; };
+    float y = 0.f;
     MfmaRows<BITS, NGH> M;
-    M.run(rec0, a.xq, a.xsum, T, tokv, fill, after, xl, xsl, wlds[wv]);
+    M.run(rec0, 0, a.xq, a.xsum, T, tokv, fill, after, [&](int) { y = M.y; }, xl, xsl, wlds[wv]);
     // h = silu(gate) * up: gate rows are even, up rows odd (adjacent lanes)
     float hs = 0.f, hr = 0.f;
     {
-      const float yv = M.y * tinv;
+      const float yv = y * tinv;
       const float up = dpp_f<0xB1, 0xF>(yv, 0.f);  // partner row (quad_perm [1,0,3,2])
       if ((n & 1) == 0 && qq < T) {
         const float h = silu(yv) * up;
@@ -710,20 +740,21 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
   }
 }
 
-// g3: down of 128 rows (part rb) of one item's expert for the item's tokens /
-// slots: shared: d_shared[t][row] = sigma[t] * row . h_shared[t]; routed:
-// partial[slot][row] = w[slot] * row . h[slot]. Wavefront w holds rows
-// 16w .. 16w + 15. Workgroups: the shared expert's token blocks, then one per
-// possible routed token block (those past G[1] exit at once), each times the
-// H / 128 row parts.
+// g3: down of 256 rows (part rb: two tiles of 128, each wavefront 16 rows of
+// each) of one item's expert for the item's tokens / slots, from one staging of
+// h: shared: d_shared[t][row] = sigma[t] * row . h_shared[t]; routed:
+// partial[slot][row] = w[slot] * row . h[slot]. Workgroups: the shared
+// expert's token blocks, then one per possible routed token block (those past
+// G[1] exit at once), each times the H / 256 row parts.
+constexpr int kG3Tiles = 2;
 template <int BITS, int NGI>
 __global__ __launch_bounds__(kGThreads) void k_g3(const GroupArgs a) {
   constexpr size_t RB = (size_t)NGI * gbytes<BITS>();
-  __shared__ __attribute__((aligned(16))) uint8_t xl[kXLds + 16];
+  __shared__ __attribute__((aligned(16))) uint8_t xl[MfmaRows<BITS, NGI, kG3Tiles>::XL + 16];
   __shared__ float2 xsl[kTokBlock * NGI + 1];
   __shared__ __attribute__((aligned(16))) uint8_t wlds[kGWaves][kWaveLds];
   __shared__ int tokv[kTokBlock], oidx[kTokBlock];
-  const int per = a.H / 128;
+  const int per = a.H / (128 * kG3Tiles);
   const bool sh = a.shared != nullptr;
   const int S = a.B * a.K;
   const int shb = sh ? (a.B + kTokBlock - 1) / kTokBlock : 0;
@@ -736,22 +767,22 @@ __global__ __launch_bounds__(kGThreads) void k_g3(const GroupArgs a) {
     it.n = min(kTokBlock, a.B - it.q0);
   } else {
     const int kb = ib - shb;
-    // (requested together: one round trip)
+    // (requested together with the slots below: one round trip)
     const int nb = G[1];
-    it.expert = G[2 + S + 3 * kb];
-    it.q0 = G[2 + S + 3 * kb + 1];
-    it.n = G[2 + S + 3 * kb + 2];
+    it.expert = G[2 + kBlkInts * kb];
+    it.n = G[2 + kBlkInts * kb + 1];
+    it.q0 = 2 + kBlkInts * kb + 2;
     if (kb >= nb) return;  // uniform over the workgroup
   }
   const int T = it.n;
   const int lane = lane_id(), wv = wave_in_block();
   const int n = lane & 15, qq = lane >> 4;
   const uint8_t *base = (it.expert < 0 ? a.shared : a.bank + (size_t)it.expert * a.stride) + a.gu_bytes;
-  const int row = 128 * rb + 16 * wv + n;
-  const uint8_t *rec0 = base + (size_t)(128 * rb + 16 * wv) * RB;
+  const int row0 = 128 * kG3Tiles * rb + 16 * wv;  // this wavefront's first row of tile 0
+  const uint8_t *rec0 = base + (size_t)row0 * RB;
   float *const outp = it.expert < 0 ? a.d_shared : a.partial;
   const float *const scl = it.expert < 0 ? a.sigma : a.w;
-  const int sl = G[2 + (it.expert < 0 ? 0 : it.q0 + min((int)threadIdx.x, T - 1))];
+  const int sl = G[it.expert < 0 ? 0 : it.q0 + min((int)threadIdx.x, T - 1)];
   // tables: the h vector of item token u, and its output row (token or slot)
   auto fill = [&](int u) {
     tokv[u] = it.expert < 0 ? S + it.q0 + u : sl;
@@ -759,9 +790,11 @@ __global__ __launch_bounds__(kGThreads) void k_g3(const GroupArgs a) {
   };
   float osc;  // sigma (shared) or routing weight of this lane's D rows
   auto after = [&]() { osc = scl[oidx[min(qq, T - 1)]]; };
-  MfmaRows<BITS, NGI> M;
-  M.run(rec0, a.hq, a.hsum, T, tokv, fill, after, xl, xsl, wlds[wv]);
-  if (qq < T) outp[(size_t)oidx[qq] * a.H + row] = osc * M.y;
+  MfmaRows<BITS, NGI, kG3Tiles> M;
+  auto done = [&](int tile) {
+    if (qq < T) outp[(size_t)oidx[qq] * a.H + row0 + 128 * tile + n] = osc * M.y;
+  };
+  M.run(rec0, (size_t)128 * RB, a.hq, a.hsum, T, tokv, fill, after, done, xl, xsl, wlds[wv]);
 }
 
 // g4: out[t] = residual[t] + sum_k partial[t*K + k] (k ascending) + d_shared[t]
@@ -825,7 +858,8 @@ struct GroupDispatch {
       hipLaunchKernelGGL((k_g2<BITS, NGH, NGI>), dim3(std::min((shb + S) * NGI, cu_count())), dim3(kGThreads), 0,
                          s, a);
     if (phases & 4) {
-      hipLaunchKernelGGL((k_g3<BITS, NGI>), dim3((shb + S) * (a.H / 128)), dim3(kGThreads), 0, s, a);
+      hipLaunchKernelGGL((k_g3<BITS, NGI>), dim3((shb + S) * (a.H / (128 * kG3Tiles))), dim3(kGThreads), 0, s,
+                         a);
       hipLaunchKernelGGL(k_g4<BITS>, dim3(n4), dim3(kBlock), 0, s, a);
     }
     return hipGetLastError();

@@ -70,7 +70,7 @@ struct GroupArgs {
   float *hsum;               // [S+B][I/64][2]
   float *d_shared;           // [B][H]
   float *partial;            // [S][H]
-  int32_t *groups;           // D, NB, slot lists[S], token blocks {expert, start, n}[S]; S = B*K
+  int32_t *groups;           // D, NB, token blocks {expert, n, 4 slots}[S]; S = B*K
   int n_router_blocks;       // g1
 };
 

@@ -63,9 +63,8 @@ struct LayerWs {
   size_t d_shared;  // fp32 [B][hidden]  sigma * shared-expert output
   // B > 1 only (tokens grouped by expert):
   size_t partial;   // fp32 [B][K][hidden]  w * routed-expert output, per (token, slot)
-  size_t groups;    // int32 [2 + 4 S], S = B*K: the number of distinct experts, the number of
-                    // token blocks, the slot lists grouped by expert [S], and per token block
-                    // {expert, start of its slots, number of slots} [3 S]
+  size_t groups;    // int32 [2 + 6 S], S = B*K: the number of distinct experts, the number of
+                    // token blocks, and per token block {expert, number of slots, 4 slots} [6 S]
   size_t xq;        // bf16 [B][3][hidden]     the input as three bf16 parts
   size_t xsum;      // fp32 [B][hidden/64][2]  its per-group sums (of x, of hi + lo)
   size_t xinv;      // fp32 [B]                its RMS factor
@@ -92,7 +91,7 @@ inline LayerWs layer_ws(int B, int E, int K, int hidden, int inter) {
   w.d_shared = take(sizeof(float) * (size_t)B * hidden);
   const size_t S = (size_t)B * K;
   w.partial = take(B > 1 ? sizeof(float) * S * hidden : 0);
-  w.groups = take(B > 1 ? sizeof(int32_t) * (4 * S + 2) : 0);
+  w.groups = take(B > 1 ? sizeof(int32_t) * (6 * S + 2) : 0);
   w.xq = take(B > 1 ? sizeof(uint16_t) * 3 * (size_t)B * hidden : 0);
   w.xsum = take(B > 1 ? 2 * sizeof(float) * (size_t)B * (hidden / 64) : 0);
   w.xinv = take(B > 1 ? sizeof(float) * (size_t)B : 0);
