@@ -192,78 +192,25 @@ __device__ __forceinline__ int order_key(float f) {
 }
 __device__ __forceinline__ float key_value(int k) { return __int_as_float(k >= 0 ? k : k ^ 0x7FFFFFFF); }
 
-// Top-K of E logits held in LDS, by one wavefront, exactly under the order
-// (value descending, index ascending); element e sits in lane e % 64, slot e / 64.
-// Values are compared as order-preserving integer keys (NaN logits count as
-// -inf). K rounds of: per-lane maximum key, wavefront maximum (DPP), then the
-// lowest index holding it from one ballot per slot (index = lane + 64 * slot, so
-// the first slot with a hit and its lowest lane give the lowest index); the
-// chosen element's key becomes INT_MIN, below every real key, as are the padding
-// slots (e >= E). Then the renormalised softmax weights of the chosen K,
+// Top-K of E logits by one wavefront, exactly under the order (value
+// descending, index ascending). Values are compared as order-preserving integer
+// keys (NaN logits count as -inf); lane l holds the VPL consecutive elements
+// VPL l .. VPL l + VPL - 1, so a lower lane means a lower index, and padding
+// elements (e >= E) hold INT_MIN, below every real key.
+//
+// Fast path: each lane's maximum (first position among equal keys) and second
+// key; K rounds over the 64 lane maxima (wavefront maximum, lowest lane holding
+// it) give the K best lane maxima in order, and they are the top K of all
+// elements when no second key reaches the K-th of them. Otherwise (a lane holding
+// two of the top K, or a tie at the boundary) K full rounds run: each lane's
+// maximum over its remaining keys, the wavefront maximum, the lowest lane holding
+// it and that lane's first position holding it; the chosen key is retired.
+//
+// Then the renormalised softmax weights of the chosen K,
 // w_j = exp(l_j - l_0) / sum (renormalising over the chosen K cancels the full
 // softmax denominator). The logits may be held unscaled: lscale > 0 is the
 // factor that turns them into the true logits (it does not change the order), so
 // w_j = exp((l_j - l_0) * lscale) / sum. Results are wavefront-uniform.
-template <int VPL>
-__device__ __forceinline__ void wave_topk_ballot(const float *lg, int E, int K, int *idx, float *w,
-                                                 float lscale = 1.f) {
-  constexpr int kGone = (int)0x80000000;
-  const int lane = lane_id();
-  int key[VPL];
-#pragma unroll
-  for (int m = 0; m < VPL; ++m) {
-    const int e = lane + 64 * m;
-    const float t = lg[min(e, E - 1)];
-    key[m] = e < E ? order_key(t == t ? t : -INFINITY) : kGone;
-  }
-  float lv[kMaxTopK];
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    idx[j] = 0;
-    lv[j] = 0.f;
-    if (j < K) {
-      int t[VPL];
-#pragma unroll
-      for (int m = 0; m < VPL; ++m) t[m] = key[m];
-#pragma unroll
-      for (int s = VPL / 2; s >= 1; s /= 2)
-#pragma unroll
-        for (int m = 0; m < s; ++m) t[m] = max(t[m], t[m + s]);
-      int g = t[0];
-      g = max(g, dpp_i<0xB1, 0xF>(g, kGone));
-      g = max(g, dpp_i<0x4E, 0xF>(g, kGone));
-      g = max(g, dpp_i<0x141, 0xF>(g, kGone));
-      g = max(g, dpp_i<0x140, 0xF>(g, kGone));
-      g = max(g, dpp_i<0x142, 0xA>(g, kGone));
-      g = max(g, dpp_i<0x143, 0xC>(g, kGone));
-      g = __builtin_amdgcn_readlane(g, 63);
-      unsigned long long hit[VPL];
-#pragma unroll
-      for (int m = 0; m < VPL; ++m) hit[m] = __ballot(key[m] == g);
-      int sel = 0;
-#pragma unroll
-      for (int m = VPL - 1; m >= 0; --m)
-        sel = hit[m] ? 64 * m + (__ffsll((long long)hit[m]) - 1) : sel;
-      idx[j] = sel;
-      lv[j] = key_value(g);
-#pragma unroll
-      for (int m = 0; m < VPL; ++m) key[m] = (lane + 64 * m == sel) ? kGone : key[m];
-    }
-  }
-  float sum = 0.f;
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    w[j] = 0.f;
-    if (j < K) {
-      w[j] = __expf((lv[j] - lv[0]) * lscale);
-      sum += w[j];
-    }
-  }
-  const float inv = 1.f / sum;
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) w[j] *= inv;
-}
-
 __device__ __forceinline__ int wave_max_i(int g) {
   constexpr int kGone = (int)0x80000000;
   g = max(g, dpp_i<0xB1, 0xF>(g, kGone));
@@ -275,33 +222,27 @@ __device__ __forceinline__ int wave_max_i(int g) {
   return __builtin_amdgcn_readlane(g, 63);
 }
 
-// Fast path of the top-K, exact when it answers: lane l holds the VPL
-// consecutive elements VPL l .. VPL l + VPL - 1 (so a lower lane means a lower
-// index), and its maximum (first position among equal keys) and second key. K
-// rounds over the 64 lane maxima (wavefront maximum, lowest lane holding it)
-// give the K best lane maxima in order; they are the top K of all elements when
-// no second key reaches the K-th of them (a lane holding two of the top K, or a
-// tie, fails that test: then the caller runs the full rounds). Returns whether
-// it answered; w as wave_topk_ballot.
+// the lane's maximum key and its first position
 template <int VPL>
-__device__ __forceinline__ bool wave_topk_fast(const float *lg, int E, int K, int *idx, float *w, float lscale) {
-  constexpr int kGone = (int)0x80000000;
-  const int lane = lane_id();
-  int key[VPL];
-#pragma unroll
-  for (int m = 0; m < VPL; ++m) {
-    const int e = VPL * lane + m;
-    const float t = lg[min(e, E - 1)];
-    key[m] = e < E ? order_key(t == t ? t : -INFINITY) : kGone;
-  }
-  int m1 = key[0], p1 = 0, m2 = kGone;
+__device__ __forceinline__ void lane_max(const int (&key)[VPL], int &m1, int &p1) {
+  m1 = key[0];
+  p1 = 0;
 #pragma unroll
   for (int m = 1; m < VPL; ++m) {
     const bool gt = key[m] > m1;
-    m2 = gt ? m1 : max(m2, key[m]);
     p1 = gt ? m : p1;
     m1 = gt ? key[m] : m1;
   }
+}
+
+template <int VPL>
+__device__ __forceinline__ void wave_topk_keys(int (&key)[VPL], int K, int *idx, float *w, float lscale) {
+  constexpr int kGone = (int)0x80000000;
+  const int lane = lane_id();
+  int m1, p1, m2 = kGone;
+  lane_max<VPL>(key, m1, p1);
+#pragma unroll
+  for (int m = 0; m < VPL; ++m) m2 = m == p1 ? m2 : max(m2, key[m]);
   int a = m1, T = kGone;
   float lv[kMaxTopK];
 #pragma unroll
@@ -317,7 +258,22 @@ __device__ __forceinline__ bool wave_topk_fast(const float *lg, int E, int K, in
       T = g;
     }
   }
-  if (wave_max_i(m2) >= T) return false;
+  if (wave_max_i(m2) >= T) {
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j < K) {
+        int b, p;
+        lane_max<VPL>(key, b, p);
+        const int g = wave_max_i(b);
+        const int L = __ffsll((long long)__ballot(b == g)) - 1;
+        const int pl = __builtin_amdgcn_readlane(p, L);
+        idx[j] = VPL * L + pl;
+        lv[j] = key_value(g);
+#pragma unroll
+        for (int m = 0; m < VPL; ++m) key[m] = (lane == L && m == pl) ? kGone : key[m];
+      }
+    }
+  }
   float sum = 0.f;
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) {
@@ -330,15 +286,41 @@ __device__ __forceinline__ bool wave_topk_fast(const float *lg, int E, int K, in
   const float inv = 1.f / sum;
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) w[j] *= inv;
-  return true;
 }
 
+// lane l's VPL consecutive logits (clamped loads; the caller turns them into keys)
+template <int VPL>
+__device__ __forceinline__ void load_logits(const float *lg, int E, float (&v)[VPL]) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int m = 0; m < VPL; ++m) v[m] = lg[min(VPL * lane + m, E - 1)];
+}
+
+template <int VPL>
+__device__ __forceinline__ void logit_keys(const float (&v)[VPL], int E, int (&key)[VPL]) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int m = 0; m < VPL; ++m) {
+    const float t = v[m];
+    key[m] = VPL * lane + m < E ? order_key(t == t ? t : -INFINITY) : (int)0x80000000;
+  }
+}
+
+// top-K of E <= kMaxExperts logits in memory (LDS or global)
 __device__ __forceinline__ void wave_topk_lds(const float *lg, int E, int K, int *idx, float *w,
                                               float lscale = 1.f) {
   if (E <= 512) {
-    if (!wave_topk_fast<8>(lg, E, K, idx, w, lscale)) wave_topk_ballot<8>(lg, E, K, idx, w, lscale);
+    float v[8];
+    int key[8];
+    load_logits<8>(lg, E, v);
+    logit_keys<8>(v, E, key);
+    wave_topk_keys<8>(key, K, idx, w, lscale);
   } else {
-    wave_topk_ballot<16>(lg, E, K, idx, w, lscale);
+    float v[16];
+    int key[16];
+    load_logits<16>(lg, E, v);
+    logit_keys<16>(v, E, key);
+    wave_topk_keys<16>(key, K, idx, w, lscale);
   }
 }
 
@@ -520,6 +502,7 @@ template <int BITS, int NGH>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void k_phase2(const Phase2Args a) {
   constexpr int H = NGH * kGroup;
   constexpr int RPIH = kWave / NGH;
+  constexpr int X4 = (NGH * 16 + kBlock - 1) / kBlock;
   __shared__ float xl[NGH * kXPad];
   __shared__ float lg[kMaxExperts];
   __shared__ float part[kWavesPerBlock];
@@ -529,19 +512,52 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   const bool rms = a.rms_eps >= 0.f;
   trace_mark(a.trace, 0);
   if ((int)blockIdx.x < a.n_routed_blocks) {
-    for (int i = threadIdx.x; i < a.E; i += kBlock) lg[i] = a.logits[i];
-    if (rms)
-      stage_vec<NGH, true>(a.x, xl, part);
-    else
-      stage_vec<NGH, false>(a.x, xl, part);
-    __syncthreads();
-    trace_mark(a.trace, 1);
     // a workgroup serves one slot (waves_per_slot is a multiple of 4) and needs
     // only the first slot+1 winners: the rounds stop there, so the workgroups of
     // the early slots start streaming before the last winner is known. The
     // workgroup that publishes the routing is one of the last slot's (all K).
     const int bslot = min((int)(blockIdx.x * kWavesPerBlock) / a.waves_per_slot, a.K - 1);
-    block_topk(lg, a.E, bslot + 1, sidx, sw);
+    if (a.E <= 512) {
+      // Every wavefront requests the logits in the top-K's layout, then its share
+      // of x; one wavefront (b % 4, so that the workgroups sharing a CU use
+      // different SIMDs) waits for the logits only and derives the routing while
+      // x is still arriving, then stores its share of x like the others.
+      float lv[8];
+      load_logits<8>(a.logits, a.E, lv);
+      Staged<X4> xst;
+      stage_load(a.x, NGH * 16, xst);
+      if (wave_in_block() == (int)(blockIdx.x % kWavesPerBlock)) {
+        int key[8], idx[kMaxTopK];
+        float w[kMaxTopK];
+        logit_keys<8>(lv, a.E, key);
+        // the rest of the workgroup waits on this wavefront: let it win the
+        // SIMD's issue arbitration against co-resident wavefronts of other workgroups
+        __builtin_amdgcn_s_setprio(3);
+        wave_topk_keys<8>(key, bslot + 1, idx, w, 1.f);
+        __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j)
+          if (j == lane) {
+            sidx[j] = idx[j];
+            sw[j] = w[j];
+          }
+      }
+      if (rms)
+        stage_store<X4, true>(xst, NGH * 16, xl, part);
+      else
+        stage_store<X4, false>(xst, NGH * 16, xl, part);
+      __syncthreads();
+      trace_mark(a.trace, 1);
+    } else {
+      for (int i = threadIdx.x; i < a.E; i += kBlock) lg[i] = a.logits[i];
+      if (rms)
+        stage_vec<NGH, true>(a.x, xl, part);
+      else
+        stage_vec<NGH, false>(a.x, xl, part);
+      __syncthreads();
+      trace_mark(a.trace, 1);
+      block_topk(lg, a.E, bslot + 1, sidx, sw);
+    }
     trace_mark(a.trace, 2);
     const int wv = blockIdx.x * kWavesPerBlock + wave_in_block();
     const int slot = min(wv / a.waves_per_slot, a.K - 1);
