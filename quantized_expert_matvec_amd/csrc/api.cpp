@@ -136,6 +136,7 @@ fmoe_status layer_enqueue(const fmoe_layer *L, int B, const float *x, float rms_
     a.h_shared = (float *)(ws + w.h_shared) + (size_t)t * I;
     a.h_routed = (float *)(ws + w.h_routed) + (size_t)t * K * I;
     a.d_shared = (float *)(ws + w.d_shared) + (size_t)t * H;
+    a.xdig = (uint32_t *)(ws + w.xdig);
     if (launch_layer(a, s, phases) != hipSuccess) return FMOE_ERR_LAUNCH;
   }
   return FMOE_OK;

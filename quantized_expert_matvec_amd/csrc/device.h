@@ -154,6 +154,95 @@ __device__ __forceinline__ float group_partial(const Chunk<BITS> &c, uint32_t sb
   return fmaf(scale_of(sb), d, bias_of(sb) * xs.sum);
 }
 
+// ------------------------------------------------------------------ integer digits of x
+//
+// The one-token gate/up evaluates the same per-group identity with exact
+// integer dot products. A 64-column group of x is held as x_j = f * X_j, X_j an
+// integer with |X_j| <= 2^22 (the group's largest |x_j| scaled just below
+// 2^22), written with 6 signed base-16 digits d_p in [-8, 7], X = sum_p d_p 16^p.
+// A digit word holds digit p of the 8 columns whose codes share one 32-bit code
+// word, nibble n of the digit word for code nibble n, so that one
+// v_dot8_i32_i4 of a code word and a digit word adds the 8 products code * digit
+// exactly. 4-bit codes enter as c - 8 (the nibbles xor 8, two's complement), so
+//   sum_j c_j x_j = f * sum_p 16^p sum_j (c_j - 8) d_jp + 8 sum_j x_j;
+// 2-bit codes (0..3, non-negative as signed nibbles) enter as they are, after a
+// mask spreads each code word into two words of 4-bit fields. The only
+// roundings are those of X_j (at most 2^-22 of the group's largest |x_j|) and of
+// the final fp32 combination.
+constexpr int kDigits = 6;
+constexpr int kDigWords = 8 * kDigits;     // digit words of a group
+static_assert(kDigStride == kDigWords + 4, "per group: digit words, f, sum x, two spare words");
+
+// Column (within the group) of nibble n of code word k. 4-bit: word k holds
+// columns 8k .. 8k+7, byte b's low nibble column 8k+b, its high nibble 8k+4+b.
+// 2-bit: packed word u = k/2 holds columns 16u .. 16u+15, byte b's field q
+// column 16u+4q+b; the mask keeps fields 0 and 2 of every byte in nibbles
+// (k even), the mask after a shift by two fields 1 and 3 (k odd).
+template <int BITS>
+__device__ __forceinline__ int digit_column(int k, int n) {
+  if constexpr (BITS == 4) return 8 * k + (n >> 1) + 4 * (n & 1);
+  return 16 * (k >> 1) + 4 * (k & 1) + 8 * (n & 1) + (n >> 1);
+}
+
+struct XDig {
+  uint32_t d[kDigWords];  // digit word p of code word k at d[kDigits k + p]
+  float f;                // x_j = f * X_j
+  float sx;               // sum_j x_j
+};
+
+__device__ __forceinline__ void read_digits(const uint32_t *lds, int g, XDig &xd) {
+  const uint4 *src = reinterpret_cast<const uint4 *>(lds + g * kDigStride);
+#pragma unroll
+  for (int i = 0; i < kDigWords / 4; ++i) {
+    const uint4 t = src[i];
+    xd.d[4 * i] = t.x;
+    xd.d[4 * i + 1] = t.y;
+    xd.d[4 * i + 2] = t.z;
+    xd.d[4 * i + 3] = t.w;
+  }
+  const float2 fs = *reinterpret_cast<const float2 *>(lds + g * kDigStride + kDigWords);
+  xd.f = fs.x;
+  xd.sx = fs.y;
+}
+
+// sum_p 16^p acc_p (the low four digits exactly in 32-bit integers)
+__device__ __forceinline__ float digit_sum(const int (&acc)[kDigits]) {
+  const int lo = acc[0] + 16 * acc[1] + 256 * acc[2] + 4096 * acc[3];
+  const int hi = acc[4] + 16 * acc[5];
+  return fmaf((float)hi, 65536.f, (float)lo);
+}
+
+// scale * sum c x + bias * sum x over the lane's group, from the digit form of x
+template <int BITS>
+__device__ __forceinline__ float group_partial_dig(const Chunk<BITS> &c, uint32_t sb, const XDig &xd) {
+  int acc[kDigits];
+#pragma unroll
+  for (int p = 0; p < kDigits; ++p) acc[p] = 0;
+  if constexpr (BITS == 4) {
+    const uint32_t w[8] = {c.a.x, c.a.y, c.a.z, c.a.w, c.b.x, c.b.y, c.b.z, c.b.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int cs = (int)(w[k] ^ 0x88888888u);
+#pragma unroll
+      for (int p = 0; p < kDigits; ++p) acc[p] = __builtin_amdgcn_sdot8(cs, (int)xd.d[kDigits * k + p], acc[p], false);
+    }
+    const float s = scale_of(sb);
+    return fmaf(s * xd.f, digit_sum(acc), fmaf(8.f, s, bias_of(sb)) * xd.sx);
+  } else {
+    const uint32_t w[4] = {c.a.x, c.a.y, c.a.z, c.a.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int n0 = (int)(w[u] & 0x33333333u), n1 = (int)((w[u] >> 2) & 0x33333333u);
+#pragma unroll
+      for (int p = 0; p < kDigits; ++p) {
+        acc[p] = __builtin_amdgcn_sdot8(n0, (int)xd.d[kDigits * (2 * u) + p], acc[p], false);
+        acc[p] = __builtin_amdgcn_sdot8(n1, (int)xd.d[kDigits * (2 * u + 1) + p], acc[p], false);
+      }
+    }
+    return fmaf(scale_of(sb) * xd.f, digit_sum(acc), bias_of(sb) * xd.sx);
+  }
+}
+
 // ------------------------------------------------------------------ cross-lane
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }

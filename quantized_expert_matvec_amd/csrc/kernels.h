@@ -38,6 +38,7 @@ struct LayerArgs {
   float *h_shared;           // [I]
   float *h_routed;           // [K][I]
   float *d_shared;           // [H]
+  uint32_t *xdig;            // [H/64][kDigStride] x in digit form (router kernel -> gate/up kernel)
   // optional per-workgroup timestamps (device, 100 MHz clock) for profiling:
   // [phase][workgroup][8]; null in normal use
   uint64_t *trace;

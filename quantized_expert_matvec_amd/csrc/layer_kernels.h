@@ -61,23 +61,23 @@ struct Staged {
 // The loads are unconditional (indices clamped to the vector), so that no branch
 // hides them from the compiler's memory-counter bookkeeping: waiting for them
 // then does not also wait for loads issued after them.
-template <int N4>
+template <int N4, int BS = kBlock>
 __device__ __forceinline__ void stage_load(const float *__restrict__ src, int nf4, Staged<N4> &st) {
 #pragma unroll
   for (int k = 0; k < N4; ++k) {
-    const int f = min((int)threadIdx.x + kBlock * k, nf4 - 1);
+    const int f = min((int)threadIdx.x + BS * k, nf4 - 1);
     st.v[k] = reinterpret_cast<const float4 *>(src)[f];
   }
 }
 
 // Store into padded LDS rows; with SUMSQ, the wavefront's partial sum of squares
 // (same fixed order as stage_vec) goes to part[].
-template <int N4, bool SUMSQ>
+template <int N4, bool SUMSQ, int BS = kBlock>
 __device__ __forceinline__ void stage_store(const Staged<N4> &st, int nf4, float *lds, float *part) {
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < N4; ++k) {
-    const int f = threadIdx.x + kBlock * k;
+    const int f = threadIdx.x + BS * k;
     if (f < nf4) {
       const float4 v = st.v[k];
       *reinterpret_cast<float4 *>(&lds[lds_index(4 * f)]) = v;
@@ -87,6 +87,19 @@ __device__ __forceinline__ void stage_store(const Staged<N4> &st, int nf4, float
   if constexpr (SUMSQ) {
     ss = seg_reduce<kWave>(ss);
     if (lane_id() == kWave - 1) part[wave_in_block()] = ss;
+  }
+}
+
+// Store into unpadded LDS (a plain copy of nf4 16-byte units).
+template <int N4>
+__device__ __forceinline__ void stage_copy(const Staged<N4> &st, int nf4, uint32_t *lds) {
+#pragma unroll
+  for (int k = 0; k < N4; ++k) {
+    const int f = threadIdx.x + kBlock * k;
+    if (f < nf4) {
+      const float4 v = st.v[k];  // (through a local: a direct struct copy kept st in scratch memory)
+      reinterpret_cast<float4 *>(lds)[f] = v;
+    }
   }
 }
 
@@ -137,6 +150,7 @@ struct RowLoads {
       const int row = min(row0 + i * RPI + sub, rows - 1);
       load_group<BITS, NG>(blob + (size_t)row * RB, g, c[i], sb[i]);
     }
+    __builtin_amdgcn_sched_barrier(0);  // (as in PairLoads::issue)
   }
   // y[row] = alpha * row . x
   __device__ __forceinline__ void finish(const XSlice &xs, float *__restrict__ y, int rows, int row0,
@@ -169,6 +183,9 @@ struct PairLoads {
       load_group<BITS, NG>(rec, g, cg[i], sg[i]);
       load_group<BITS, NG>(rec + RB, g, cu[i], su[i]);
     }
+    // every load goes out before the first use of a loaded word (otherwise the
+    // scheduler can hoist that use between the loads, and its wait stalls the rest)
+    __builtin_amdgcn_sched_barrier(0);
   }
   // h[r] = silu(gate_r . x) * (up_r . x)
   __device__ __forceinline__ void finish(const XSlice &xs, float *__restrict__ h, int pair0) const {
@@ -179,6 +196,18 @@ struct PairLoads {
     for (int i = 0; i < ITERS; ++i) {
       const float pg = seg_reduce<NG>(group_partial<BITS>(cg[i], sg[i], xs));
       const float pu = seg_reduce<NG>(group_partial<BITS>(cu[i], su[i], xs));
+      if (seg_last<NG>(lane)) h[pair0 + i * RPI + sub] = silu(pg) * pu;
+    }
+  }
+  // the same from the digit form of x
+  __device__ __forceinline__ void finish_dig(const XDig &xd, float *__restrict__ h, int pair0) const {
+    constexpr int RPI = kWave / NG;
+    const int lane = lane_id();
+    const int sub = lane / NG;
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+      const float pg = seg_reduce<NG>(group_partial_dig<BITS>(cg[i], sg[i], xd));
+      const float pu = seg_reduce<NG>(group_partial_dig<BITS>(cu[i], su[i], xd));
       if (seg_last<NG>(lane)) h[pair0 + i * RPI + sub] = silu(pg) * pu;
     }
   }
@@ -395,17 +424,51 @@ __global__ __launch_bounds__(kBlock) void k_expert_gateup(const uint8_t *__restr
 
 constexpr int kP2GateUpIters = 2;  // gate/up pair iterations per wavefront (routed and shared)
 constexpr int kP3Iters = 4;        // routed down row iterations per wavefront
+constexpr int kP3Block = 256;      // threads per down + combine workgroup
+constexpr int kP3Waves = kP3Block / kWave;
 
 struct Phase1Args {
   const float *router;
   const float *gvec;  // null: no shared expert
   int E;
+  int bits;           // code width of the experts (digit word order)
   const float *x;
   float rms_eps;  // >= 0: x is RMS-scaled first
   float *logits;
   float *sigma;
+  uint32_t *xdig;     // [hidden/64][kDigStride] x in digit form
+  int n_router_blocks;
   uint64_t *trace;
 };
+
+// Group g of the layer input in digit form (lanes = the group's 64 columns), from
+// the staged raw vector and its RMS factor inv: X_j = round(h_j 2^k), with k such
+// that the group's largest |h_j| lies below 2^22; f = inv 2^-k, sum x = inv sum h.
+// A non-finite value in the group makes f and the sum NaN.
+template <int BITS>
+__device__ __forceinline__ void write_digits(const float *xl, int g, float inv, uint32_t *ybuf,
+                                             uint32_t *__restrict__ dst) {
+  const int lane = lane_id();
+  const float h = xl[lds_index(kGroup * g + lane)];
+  const float amax = __int_as_float(wave_max_i(__float_as_int(fabsf(h))));
+  int e;
+  frexpf(amax, &e);  // amax < 2^e (e = 0 for amax = 0)
+  const int k = 22 - e;
+  const int X = (int)rintf(ldexpf(h, k));
+  ybuf[lane] = (uint32_t)(X + 0x888888) ^ 0x888888u;  // nibble p = digit p + 8, then two's complement
+  const float sh = seg_allreduce<kWave>(h);
+  const bool finite = amax <= 3.402823466e38f;
+  if (lane < kDigWords) {
+    const int w = lane / kDigits, p = lane % kDigits;
+    uint32_t word = 0;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) word |= ((ybuf[digit_column<BITS>(w, n)] >> (4 * p)) & 15u) << (4 * n);
+    dst[g * kDigStride + lane] = word;
+  } else if (lane < kDigStride) {
+    const float v = lane == kDigWords ? ldexpf(inv, -k) : lane == kDigWords + 1 ? inv * sh : 0.f;
+    dst[g * kDigStride + lane] = __float_as_uint(finite || lane >= kDigWords + 2 ? v : __int_as_float(0x7FC00000));
+  }
+}
 
 // Phase 1: the router. Each fp32 router row is split over kRouterSplit
 // wavefronts of a workgroup (half h: lane l covers columns 4l + 256t + 0..3 for
@@ -426,11 +489,32 @@ __global__ __launch_bounds__(kBlock) void k_phase1(const Phase1Args a) {
   __shared__ float xl[NGH * kXPad];
   __shared__ float part[kWavesPerBlock];
   __shared__ float dpart[kWavesPerBlock];
+  __shared__ uint32_t ybuf[kWavesPerBlock][kWave];
   const int lane = lane_id();
   const bool rms = a.rms_eps >= 0.f;
   trace_mark(a.trace, 0);
-  const int n_rows = a.E + (a.gvec ? 1 : 0);
   const int wv = wave_in_block();
+  if ((int)blockIdx.x >= a.n_router_blocks) {
+    // the workgroups after the router's: x in digit form, one 64-column group per
+    // wavefront (beside the router rows, off their path)
+    Staged<X4> xst;
+    stage_load(a.x, NGH * 16, xst);
+    if (rms)
+      stage_store<X4, true>(xst, NGH * 16, xl, part);
+    else
+      stage_store<X4, false>(xst, NGH * 16, xl, part);
+    __syncthreads();
+    const float inv = rms ? rms_inv(part, H, a.rms_eps) : 1.f;
+    const int g = ((int)blockIdx.x - a.n_router_blocks) * kWavesPerBlock + wv;
+    if (g < NGH) {
+      if (a.bits == 4)
+        write_digits<4>(xl, g, inv, ybuf[wv], a.xdig);
+      else
+        write_digits<2>(xl, g, inv, ybuf[wv], a.xdig);
+    }
+    return;
+  }
+  const int n_rows = a.E + (a.gvec ? 1 : 0);
   const int half = wv % SPLIT;
   const int row = blockIdx.x * (kWavesPerBlock / SPLIT) + wv / SPLIT;
   const int rr = min(row, n_rows - 1);
@@ -479,8 +563,7 @@ struct Phase2Args {
   int E, K;
   const uint8_t *bank;
   size_t stride;
-  const float *x;
-  float rms_eps;
+  const uint32_t *xdig;  // x in digit form, [hidden/64][kDigStride]
   int I;
   float *h_routed;
   int32_t *ws_idx;
@@ -494,22 +577,23 @@ struct Phase2Args {
   uint64_t *trace;
 };
 
-// Phase 2. Routed blocks stage the logits and x, derive the top-K (one wavefront
-// per block), then run gate/up + SwiGLU of their slot's expert. Shared blocks run
-// the shared expert's gate/up + SwiGLU: it does not depend on the routing, so its
-// weights stream while the routed blocks are still choosing.
+// Phase 2. Routed blocks stage the logits and x (in digit form), derive the
+// top-K (one wavefront per block), then run gate/up + SwiGLU of their slot's
+// expert. Shared blocks run the shared expert's gate/up + SwiGLU: it does not
+// depend on the routing, so its weights stream while the routed blocks are still
+// choosing. x arrives in the digit form the router kernel wrote (RMS factor
+// included), so this kernel reads no raw x.
 template <int BITS, int NGH>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void k_phase2(const Phase2Args a) {
-  constexpr int H = NGH * kGroup;
   constexpr int RPIH = kWave / NGH;
-  constexpr int X4 = (NGH * 16 + kBlock - 1) / kBlock;
-  __shared__ float xl[NGH * kXPad];
+  constexpr int NF4 = NGH * kDigStride / 4;  // 16-byte units of the digit form
+  constexpr int D4 = (NF4 + kBlock - 1) / kBlock;
+  __shared__ uint32_t xdl[NGH * kDigStride];
   __shared__ float lg[kMaxExperts];
-  __shared__ float part[kWavesPerBlock];
   __shared__ int sidx[kMaxTopK];
   __shared__ float sw[kMaxTopK];
   const int lane = lane_id();
-  const bool rms = a.rms_eps >= 0.f;
+  const float *xsrc = reinterpret_cast<const float *>(a.xdig);
   trace_mark(a.trace, 0);
   if ((int)blockIdx.x < a.n_routed_blocks) {
     // a workgroup serves one slot (waves_per_slot is a multiple of 4) and needs
@@ -518,15 +602,18 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     // workgroup that publishes the routing is one of the last slot's (all K).
     const int bslot = min((int)(blockIdx.x * kWavesPerBlock) / a.waves_per_slot, a.K - 1);
     if (a.E <= 512) {
-      // Every wavefront requests the logits in the top-K's layout, then its share
-      // of x; one wavefront (b % 4, so that the workgroups sharing a CU use
-      // different SIMDs) waits for the logits only and derives the routing while
-      // x is still arriving, then stores its share of x like the others.
-      float lv[8];
-      load_logits<8>(a.logits, a.E, lv);
-      Staged<X4> xst;
-      stage_load(a.x, NGH * 16, xst);
+      // One wavefront (b % 4, so that the workgroups sharing a CU use different
+      // SIMDs) requests the logits in the top-K's layout before its share of x,
+      // waits for the logits only and derives the routing while x is still
+      // arriving; every wavefront then stores its share of x. (Each branch issues
+      // its own loads, in a fixed order, so that no wait joins the two.)
+      Staged<D4> xst;
       if (wave_in_block() == (int)(blockIdx.x % kWavesPerBlock)) {
+        float lv[8];
+        load_logits<8>(a.logits, a.E, lv);
+        __builtin_amdgcn_sched_barrier(0);
+        stage_load(xsrc, NF4, xst);
+        __builtin_amdgcn_sched_barrier(0);
         int key[8], idx[kMaxTopK];
         float w[kMaxTopK];
         logit_keys<8>(lv, a.E, key);
@@ -541,19 +628,17 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
             sidx[j] = idx[j];
             sw[j] = w[j];
           }
+      } else {
+        stage_load(xsrc, NF4, xst);
       }
-      if (rms)
-        stage_store<X4, true>(xst, NGH * 16, xl, part);
-      else
-        stage_store<X4, false>(xst, NGH * 16, xl, part);
+      stage_copy(xst, NF4, xdl);
       __syncthreads();
       trace_mark(a.trace, 1);
     } else {
       for (int i = threadIdx.x; i < a.E; i += kBlock) lg[i] = a.logits[i];
-      if (rms)
-        stage_vec<NGH, true>(a.x, xl, part);
-      else
-        stage_vec<NGH, false>(a.x, xl, part);
+      Staged<D4> xst;
+      stage_load(xsrc, NF4, xst);
+      stage_copy(xst, NF4, xdl);
       __syncthreads();
       trace_mark(a.trace, 1);
       block_topk(lg, a.E, bslot + 1, sidx, sw);
@@ -574,9 +659,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       if (a.out_w) a.out_w[lane] = ws;
     }
     if (active) {
-      XSlice xs;
-      read_slice(xl, lane & (NGH - 1), rms ? rms_inv(part, H, a.rms_eps) : 1.f, xs);
-      P.finish(xs, a.h_routed + (size_t)slot * a.I, pair0);
+      XDig xd;
+      read_digits(xdl, lane & (NGH - 1), xd);
+      P.finish_dig(xd, a.h_routed + (size_t)slot * a.I, pair0);
     }
     trace_mark(a.trace, 3);
     return;
@@ -586,16 +671,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   const int pair0 = wv * kP2GateUpIters * RPIH;
   PairLoads<BITS, NGH, kP2GateUpIters> P;
   if (pair0 < a.I) P.issue(a.shared_gu, pair0);
-  if (rms)
-    stage_vec<NGH, true>(a.x, xl, part);
-  else
-    stage_vec<NGH, false>(a.x, xl, part);
+  Staged<D4> xst;
+  stage_load(xsrc, NF4, xst);
+  stage_copy(xst, NF4, xdl);
   __syncthreads();
   trace_mark(a.trace, 1);
   if (pair0 < a.I) {
-    XSlice xs;
-    read_slice(xl, lane & (NGH - 1), rms ? rms_inv(part, H, a.rms_eps) : 1.f, xs);
-    P.finish(xs, a.h_shared, pair0);
+    XDig xd;
+    read_digits(xdl, lane & (NGH - 1), xd);
+    P.finish_dig(xd, a.h_shared, pair0);
   }
   trace_mark(a.trace, 3);
 }
@@ -625,7 +709,7 @@ struct Phase3Args {
 // depend on the routing and are requested first. A wavefront passes its shared
 // results from the shared lanes to the combining lanes through LDS.
 template <int BITS, int NGI, int KPAD>
-__global__ __launch_bounds__(kBlock) void k_phase3(const Phase3Args a) {
+__global__ __launch_bounds__(kP3Block) void k_phase3(const Phase3Args a) {
   constexpr int SLOTS = KPAD * NGI;
   constexpr int SEG = SLOTS < kWave ? SLOTS : kWave;  // lanes per row
   constexpr int SPL = SLOTS / SEG;                     // slots per lane
@@ -637,11 +721,11 @@ __global__ __launch_bounds__(kBlock) void k_phase3(const Phase3Args a) {
   constexpr bool STAGE = KPAD * NGI <= 128;
   __shared__ float hl[STAGE ? KPAD * NGI * kXPad : 1];
   __shared__ float hs[NGI * kXPad];
-  __shared__ float dsh[kWavesPerBlock * RPW];
+  __shared__ float dsh[kP3Waves * RPW];
   trace_mark(a.trace, 0);
   const int lane = lane_id();
   const int sub = lane / SEG;
-  const int row0 = wave_id() * RPW;
+  const int row0 = ((int)blockIdx.x * kP3Waves + wave_in_block()) * RPW;
   const bool sh = a.shared_down != nullptr;
   // requested first, all independent of each other: the routing of each slot, the
   // residual of this lane's rows and sigma (used only after the dot products),
@@ -664,14 +748,15 @@ __global__ __launch_bounds__(kBlock) void k_phase3(const Phase3Args a) {
 #pragma unroll
   for (int i = 0; i < kP3Iters; ++i) res[i] = a.residual[min(row0 + i * RPI + sub, a.H - 1)];
   const float sig = *a.sigma;  // (a workspace value; unused without a shared expert)
-  constexpr int H4 = STAGE ? (KPAD * NGI * 16 + kBlock - 1) / kBlock : 1;
-  constexpr int S4 = (NGI * 16 + kBlock - 1) / kBlock;
+  constexpr int H4 = STAGE ? (KPAD * NGI * 16 + kP3Block - 1) / kP3Block : 1;
+  constexpr int S4 = (NGI * 16 + kP3Block - 1) / kP3Block;
   Staged<H4> hst;
-  if constexpr (STAGE) stage_load(a.h_routed, a.K * a.I / 4, hst);
+  if constexpr (STAGE) stage_load<H4, kP3Block>(a.h_routed, a.K * a.I / 4, hst);
   // without a shared expert these loads read the routed expert 0 instead (valid
   // memory, results unused): unconditional loads keep the memory-counter waits exact
   Staged<S4> sst;
-  stage_load(sh ? a.h_shared : a.h_routed, NGI * 16, sst);
+  stage_load<S4, kP3Block>(sh ? a.h_shared : a.h_routed, NGI * 16, sst);
+  __builtin_amdgcn_sched_barrier(0);  // every h load goes out before any weight load
   const uint8_t *sdown = sh ? a.shared_down : a.bank + a.gu_bytes;
   const int ssub = lane / NGI, sg = lane & (NGI - 1);
   Chunk<BITS> cs[SIT];
@@ -681,9 +766,13 @@ __global__ __launch_bounds__(kBlock) void k_phase3(const Phase3Args a) {
     const int row = min(row0 + q * RPII + ssub, a.H - 1);
     load_group<BITS, NGI>(sdown + (size_t)row * RB, sg, cs[q], ss[q]);
   }
+  __builtin_amdgcn_sched_barrier(0);  // the shared rows go out before the routing is needed
   const uint8_t *base[SPL];
 #pragma unroll
-  for (int m = 0; m < SPL; ++m) base[m] = a.bank + (size_t)sel[m] * a.stride + a.gu_bytes;
+  for (int m = 0; m < SPL; ++m) {
+    asm volatile("" : "+v"(sel[m]));  // (keeps the address arithmetic, and its wait, here)
+    base[m] = a.bank + (size_t)sel[m] * a.stride + a.gu_bytes;
+  }
   Chunk<BITS> c[kP3Iters][SPL];
   uint32_t sb[kP3Iters][SPL];
 #pragma unroll
@@ -694,8 +783,8 @@ __global__ __launch_bounds__(kBlock) void k_phase3(const Phase3Args a) {
     for (int m = 0; m < SPL; ++m) load_group<BITS, NGI>(base[m] + (size_t)row * RB, grp[m], c[i][m], sb[i][m]);
   }
   __builtin_amdgcn_sched_barrier(0);  // the h vectors were requested before the weights
-  if constexpr (STAGE) stage_store<H4, false>(hst, a.K * a.I / 4, hl, nullptr);
-  stage_store<S4, false>(sst, NGI * 16, hs, nullptr);
+  if constexpr (STAGE) stage_store<H4, false, kP3Block>(hst, a.K * a.I / 4, hl, nullptr);
+  stage_store<S4, false, kP3Block>(sst, NGI * 16, hs, nullptr);
   __syncthreads();
   trace_mark(a.trace, 1);
   if (row0 >= a.H) return;
@@ -767,7 +856,8 @@ struct LayerGeom {
     while (kpad < L.K) kpad <<= 1;
     const int slots = kpad * NGI;
     const int seg = slots < kWave ? slots : kWave;
-    n3 = blocks_for(((long)L.H / (kWave / seg) + kP3Iters - 1) / kP3Iters);
+    const long w3 = ((long)L.H / (kWave / seg) + kP3Iters - 1) / kP3Iters;
+    n3 = (int)((w3 + kP3Waves - 1) / kP3Waves);
   }
 };
 
@@ -816,7 +906,7 @@ struct Dispatch {
     p3.residual = L.residual;
     p3.out = L.out;
     p3.trace = L.trace ? L.trace + (size_t)2 * kTraceBlocks * kTraceSlots : nullptr;
-    hipLaunchKernelGGL((k_phase3<BITS, NGI, KPAD>), dim3(G.n3), dim3(kBlock), 0, s, p3);
+    hipLaunchKernelGGL((k_phase3<BITS, NGI, KPAD>), dim3(G.n3), dim3(kP3Block), 0, s, p3);
     return hipGetLastError();
   }
 
@@ -827,12 +917,17 @@ struct Dispatch {
     p1.router = L.router;
     p1.gvec = has_shared ? L.shared_gate : nullptr;
     p1.E = L.E;
+    p1.bits = BITS;
     p1.x = L.x;
     p1.rms_eps = L.rms_eps;
     p1.logits = L.logits;
     p1.sigma = L.sigma;
+    p1.xdig = L.xdig;
+    p1.n_router_blocks = G.n1r;
     p1.trace = L.trace;
-    hipLaunchKernelGGL((k_phase1<NGH>), dim3(G.n1r), dim3(kBlock), 0, s, p1);
+    // after the router's workgroups, one per four 64-column groups of x (digit form)
+    hipLaunchKernelGGL((k_phase1<NGH>), dim3(G.n1r + (NGH + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0, s,
+                       p1);
     return hipGetLastError();
   }
 
@@ -845,8 +940,7 @@ struct Dispatch {
     p2.K = L.K;
     p2.bank = L.bank;
     p2.stride = L.expert_stride;
-    p2.x = L.x;
-    p2.rms_eps = L.rms_eps;
+    p2.xdig = L.xdig;
     p2.I = L.I;
     p2.h_routed = L.h_routed;
     p2.ws_idx = L.ws_idx;

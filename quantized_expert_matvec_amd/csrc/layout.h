@@ -21,6 +21,7 @@ constexpr int kBlock = 256;  // threads per block everywhere: 4 wavefronts
 constexpr int kMaxTopK = 8;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTokens = 64;
+constexpr int kDigStride = 52;  // u32 words per 64-column group of x in digit form
 
 inline bool bits_ok(int bits) { return bits == 2 || bits == 4; }
 inline bool cols_ok(int cols) {
@@ -61,6 +62,7 @@ struct LayerWs {
   size_t h_shared;  // fp32 [B][inter]
   size_t h_routed;  // fp32 [B][K][inter]
   size_t d_shared;  // fp32 [B][hidden]  sigma * shared-expert output
+  size_t xdig;      // B == 1: u32 [hidden/64][kDigStride] x as signed base-16 digits per group (+ factor, sum)
   // B > 1 only (tokens grouped by expert):
   size_t partial;   // fp32 [B][K][hidden]  w * routed-expert output, per (token, slot)
   size_t groups;    // int32 [2 + 6 S], S = B*K: the number of distinct experts, the number of
@@ -89,6 +91,7 @@ inline LayerWs layer_ws(int B, int E, int K, int hidden, int inter) {
   w.h_shared = take(sizeof(float) * (size_t)B * inter);
   w.h_routed = take(sizeof(float) * (size_t)B * K * inter);
   w.d_shared = take(sizeof(float) * (size_t)B * hidden);
+  w.xdig = take(B == 1 ? sizeof(uint32_t) * kDigStride * (size_t)(hidden / 64) : 0);
   const size_t S = (size_t)B * K;
   w.partial = take(B > 1 ? sizeof(float) * S * hidden : 0);
   w.groups = take(B > 1 ? sizeof(int32_t) * (6 * S + 2) : 0);
