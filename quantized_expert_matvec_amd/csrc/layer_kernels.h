@@ -470,11 +470,12 @@ __device__ __forceinline__ void write_digits(const float *xl, int g, float inv, 
   }
 }
 
-// Phase 1: the router. Each fp32 router row is split over kRouterSplit
+// Phase 1: the router. Each fp32 router row is split over router_split()
 // wavefronts of a workgroup (half h: lane l covers columns 4l + 256t + 0..3 for
 // t in [h NT/2, (h+1) NT/2)), so that the 8 MB of rows spread over every compute
-// unit; the halves' sums are added in order. Row E is the shared expert's gate
-// vector, giving sigmoid(g . x).
+// unit (512 rows: one workgroup per compute unit); the halves' sums are added in
+// order. The workgroups after the router's write x in digit form for the gate/up
+// kernel, and the last of them computes the shared expert's gate sigmoid(g . x).
 template <int NGH>
 constexpr int router_split() {
   return NGH / 4 >= 2 ? 2 : 1;
@@ -495,30 +496,58 @@ __global__ __launch_bounds__(kBlock) void k_phase1(const Phase1Args a) {
   trace_mark(a.trace, 0);
   const int wv = wave_in_block();
   if ((int)blockIdx.x >= a.n_router_blocks) {
-    // the workgroups after the router's: x in digit form, one 64-column group per
-    // wavefront (beside the router rows, off their path)
-    Staged<X4> xst;
+    // The workgroups after the router's: x in digit form, one 64-column group per
+    // wavefront, then one for the shared expert's gate sigma = sigmoid(g . x) --
+    // beside the router rows, off their path. (The gate vector's loads are
+    // unconditional, reading x where there is no gate.)
+    const int g = ((int)blockIdx.x - a.n_router_blocks) * kWavesPerBlock + wv;
+    const bool gate = a.gvec != nullptr && (int)blockIdx.x == a.n_router_blocks + (NGH + kWavesPerBlock - 1) / kWavesPerBlock;
+    Staged<X4> xst, gst;
     stage_load(a.x, NGH * 16, xst);
+    stage_load(a.gvec ? a.gvec : a.x, NGH * 16, gst);
     if (rms)
       stage_store<X4, true>(xst, NGH * 16, xl, part);
     else
       stage_store<X4, false>(xst, NGH * 16, xl, part);
     __syncthreads();
     const float inv = rms ? rms_inv(part, H, a.rms_eps) : 1.f;
-    const int g = ((int)blockIdx.x - a.n_router_blocks) * kWavesPerBlock + wv;
-    if (g < NGH) {
+    if (gate) {  // (uniform over the workgroup)
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < X4; ++k) {
+        const int f = threadIdx.x + kBlock * k;
+        if (f < NGH * 16) {
+          const float4 xv = *reinterpret_cast<const float4 *>(&xl[lds_index(4 * f)]);
+          const float4 gv = gst.v[k];
+          acc = fmaf(gv.x, xv.x, acc);
+          acc = fmaf(gv.y, xv.y, acc);
+          acc = fmaf(gv.z, xv.z, acc);
+          acc = fmaf(gv.w, xv.w, acc);
+        }
+      }
+      acc = seg_reduce<kWave>(acc);
+      if (lane == kWave - 1) dpart[wv] = acc;
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        float d = dpart[0];
+#pragma unroll
+        for (int i = 1; i < kWavesPerBlock; ++i) d += dpart[i];
+        *a.sigma = 1.f / (1.f + expf(-d * inv));
+      }
+    } else if (g < NGH) {
       if (a.bits == 4)
         write_digits<4>(xl, g, inv, ybuf[wv], a.xdig);
       else
         write_digits<2>(xl, g, inv, ybuf[wv], a.xdig);
     }
+    trace_mark(a.trace, 3);
     return;
   }
-  const int n_rows = a.E + (a.gvec ? 1 : 0);
+  const int n_rows = a.E;
   const int half = wv % SPLIT;
   const int row = blockIdx.x * (kWavesPerBlock / SPLIT) + wv / SPLIT;
   const int rr = min(row, n_rows - 1);
-  const float *src = (rr == a.E ? a.gvec : a.router + (size_t)rr * H) + 256 * NTW * half;
+  const float *src = a.router + (size_t)rr * H + 256 * NTW * half;
   Staged<X4> xst;
   stage_load(a.x, NGH * 16, xst);
   float4 w[NTW];
@@ -549,12 +578,7 @@ __global__ __launch_bounds__(kBlock) void k_phase1(const Phase1Args a) {
 #pragma unroll
     for (int h = 1; h < SPLIT; ++h) d += dpart[wv - half + h];
   }
-  if (lane == kWave - 1 && half == 0 && row < n_rows) {
-    if (row == a.E)
-      *a.sigma = 1.f / (1.f + expf(-d));
-    else
-      a.logits[row] = d;
-  }
+  if (lane == kWave - 1 && half == 0 && row < n_rows) a.logits[row] = d;
   trace_mark(a.trace, 3);
 }
 
@@ -847,7 +871,7 @@ struct LayerGeom {
     const bool sh = L.shared != nullptr;
     rbh = (size_t)NGH * (bits == 4 ? 36 : 20);
     rbi = (size_t)NGI * (bits == 4 ? 36 : 20);
-    n1r = (L.E + (sh ? 1 : 0) + kWavesPerBlock / router_split<NGH>() - 1) / (kWavesPerBlock / router_split<NGH>());
+    n1r = (L.E + kWavesPerBlock / router_split<NGH>() - 1) / (kWavesPerBlock / router_split<NGH>());
     n1s = 0;
     wps = (L.I / RPIH + kP2GateUpIters - 1) / kP2GateUpIters;
     n2r = blocks_for((long)wps * L.K);
@@ -925,9 +949,10 @@ struct Dispatch {
     p1.xdig = L.xdig;
     p1.n_router_blocks = G.n1r;
     p1.trace = L.trace;
-    // after the router's workgroups, one per four 64-column groups of x (digit form)
-    hipLaunchKernelGGL((k_phase1<NGH>), dim3(G.n1r + (NGH + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0, s,
-                       p1);
+    // after the router's workgroups: one per four 64-column groups of x (digit
+    // form), then one for the shared expert's gate
+    const int nd = (NGH + kWavesPerBlock - 1) / kWavesPerBlock + (has_shared ? 1 : 0);
+    hipLaunchKernelGGL((k_phase1<NGH>), dim3(G.n1r + nd), dim3(kBlock), 0, s, p1);
     return hipGetLastError();
   }
 
