@@ -693,10 +693,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   // shared expert gate/up
   const int wv = (blockIdx.x - a.n_routed_blocks) * kWavesPerBlock + wave_in_block();
   const int pair0 = wv * kP2GateUpIters * RPIH;
-  PairLoads<BITS, NGH, kP2GateUpIters> P;
-  if (pair0 < a.I) P.issue(a.shared_gu, pair0);
+  // x first (its loads complete before the weights', so the staging does not
+  // wait for them), then the weights
   Staged<D4> xst;
   stage_load(xsrc, NF4, xst);
+  __builtin_amdgcn_sched_barrier(0);
+  PairLoads<BITS, NGH, kP2GateUpIters> P;
+  if (pair0 < a.I) P.issue(a.shared_gu, pair0);
   stage_copy(xst, NF4, xdl);
   __syncthreads();
   trace_mark(a.trace, 1);
