@@ -102,10 +102,11 @@ def phase_bytes(phase, d_routed, eb, gub, E, H, I, K, bits):
     """Algorithmic bytes one launch of a layer kernel moves (B=1): the weights it must
     stream once plus its activation reads and writes."""
     down = eb - gub
-    if phase == 1:   # router rows + gate vector; x in; logits, sigma out
-        return E * H * 4 + H * 4 + H * 4 + E * 4 + 4
-    if phase == 2:   # distinct routed gate/up + shared gate/up; x, logits in; h_routed, h_shared out
-        return d_routed * gub + gub + H * 4 + E * 4 + K * I * 4 + I * 4
+    xd = (H // 64) * 52 * 4  # x in digit form: 52 words per 64-column group
+    if phase == 1:   # router rows + gate vector; x in; logits, sigma, x in digit form out
+        return E * H * 4 + H * 4 + H * 4 + E * 4 + 4 + xd
+    if phase == 2:   # distinct routed gate/up + shared gate/up; x (digit form), logits in; h_routed, h_shared out
+        return d_routed * gub + gub + xd + E * 4 + K * I * 4 + I * 4
     if phase == 4:   # distinct routed down + shared down; h_routed, h_shared, residual, sigma in; out
         return d_routed * down + down + K * I * 4 + I * 4 + H * 4 + 4 + H * 4
     raise ValueError(phase)
