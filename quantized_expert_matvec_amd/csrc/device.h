@@ -21,7 +21,8 @@
 // lanes (the high nibbles as 16*c, the 2-bit fields as 4^q*c), each such field
 // accumulates on its own, and the exact powers of two 1/16 and 4^-q are applied
 // once per group. Everything is fp32 with a fixed reduction order (bitwise
-// deterministic).
+// deterministic). The one-token gate/up takes sum_j c_j x_j on exact integer dot
+// products instead (the digit form of x, further below).
 #pragma once
 
 #include <hip/hip_runtime.h>
