@@ -33,6 +33,9 @@
  *    shared expert). The pages say nothing of renormalising or of ties; the
  *    reading taken is: order by probability descending, lower expert index
  *    first on an exact tie, and renormalise the K chosen probabilities to sum 1.
+ *    softmax being strictly increasing, that order is the order of the logits,
+ *    which is what is compared (fp64 probabilities far below the largest round
+ *    to 0 and would tie).
  *  - Combine: out = residual + sum_k w_k E_k(x) + sigmoid(g . x) E_shared(x)
  *    ([P2] "Metal-Compute-Shader": MoE combination + residual + sigmoid gate
  *    as one fused kernel). The gate is read as a scalar sigmoid of the dot
@@ -151,7 +154,13 @@ int orc_router(int n_experts, int hidden, const float *R, const double *x, doubl
 }
 
 /* p = softmax(logits); pick the k largest p (lower index first on exact ties),
- * in that order; w_j = p[idx_j] / sum of the k chosen p. prob (optional) gets p. */
+ * in that order; w_j = p[idx_j] / sum of the k chosen p. prob (optional) gets p.
+ * softmax is strictly increasing in each logit, so the k largest p are the k largest
+ * logits; they are ranked by the logits, because in fp64 every p more than ~745
+ * below the largest logit rounds to 0 and would tie with the rest. A NaN logit
+ * counts as -infinity (probability 0). */
+static double rank_key(double l) { return l == l ? l : -INFINITY; }
+
 int orc_route(int n, int k, const double *logits, int32_t *idx, double *w, double *prob) {
   if (n <= 0 || k < 1 || k > n) return -1;
   double *p = (double *)malloc(sizeof(double) * (size_t)n);
@@ -161,22 +170,22 @@ int orc_route(int n, int k, const double *logits, int32_t *idx, double *w, doubl
     free(taken);
     return -3;
   }
-  double m = logits[0];
+  double m = rank_key(logits[0]);
   for (int e = 1; e < n; ++e)
-    if (logits[e] > m) m = logits[e];
+    if (rank_key(logits[e]) > m) m = rank_key(logits[e]);
   double z = 0.0;
   for (int e = 0; e < n; ++e) {
-    p[e] = exp(logits[e] - m);
+    p[e] = exp(rank_key(logits[e]) - m);
     z = z + p[e];
   }
   for (int e = 0; e < n; ++e) p[e] = p[e] / z;
-  /* k passes of "largest remaining probability, smallest index on a tie" */
+  /* k passes of "largest remaining logit, smallest index on a tie" */
   double sum = 0.0;
   for (int j = 0; j < k; ++j) {
     int best = -1;
     for (int e = 0; e < n; ++e) {
       if (taken[e]) continue;
-      if (best < 0 || p[e] > p[best]) best = e;
+      if (best < 0 || rank_key(logits[e]) > rank_key(logits[best])) best = e;
     }
     taken[best] = 1;
     idx[j] = best;

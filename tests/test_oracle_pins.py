@@ -295,6 +295,32 @@ def test_s6_bruteforce_subset_maximises_mass():
         assert list(idx) == sorted(best, key=lambda e: (-p[e], e))
 
 
+def test_s6_extreme_spread_ranks_as_exact_softmax():
+    """Logits thousands apart: in fp64 every probability below the largest rounds to 0,
+    but the exact softmax still orders them as the logits (log-probabilities
+    l_i - logsumexp(l) are finite and strictly ordered like l). The top K and their order
+    follow the log-probabilities; the weights are the renormalised exact values (here 1
+    and underflowing zeros)."""
+    rng = np.random.default_rng(61)
+    for _ in range(20):
+        lg = rng.normal(0, 3e5, size=64)
+        idx, w, _ = oracle.route(lg, 4)
+        m = lg.max()
+        logp = lg - (m + np.log(np.exp(lg - m).sum()))
+        want = sorted(range(64), key=lambda e: (-logp[e], e))[:4]
+        assert list(idx) == want
+        t = logp[want]
+        assert np.array_equal(w, np.exp(t - t.max()) / np.exp(t - t.max()).sum())
+    idx, _, _ = oracle.route(np.array([0.0, -1000.0, -2000.0, -800.0, -3000.0]), 3)
+    assert list(idx) == [0, 3, 1]
+
+
+def test_s6_nan_logit_ranks_last():
+    idx, w, _ = oracle.route(np.array([np.nan, 0.5, 2.0, 1.0]), 3)
+    assert list(idx) == [2, 3, 1]
+    assert np.all(np.isfinite(w)) and abs(w.sum() - 1.0) < 1e-15
+
+
 # --------------------------------------------------------------------------- S7 SwiGLU
 
 def test_s7_silu_closed_forms():
