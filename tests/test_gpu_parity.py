@@ -175,6 +175,93 @@ def test_layer_full_size_vs_oracle(device, bits):
     torch.cuda.empty_cache()
 
 
+# --------------------------------------------------------------------------- one token (B = 1)
+
+def _one_token(device, OL, L, X, RES, what):
+    """Every token through the one-token kernels (one call per token) against the oracle."""
+    return sum(_check_layer(device, OL, L, X[t:t + 1], RES[t:t + 1], f"{what} token {t}") for t in range(X.shape[0]))
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("hidden,inter,k,n_exp", [(1024, 512, 4, 64), (256, 256, 1, 64), (512, 1024, 2, 32),
+                                                  (2048, 256, 3, 32), (4096, 256, 8, 16), (1024, 4096, 4, 8)])
+def test_one_token_layer_vs_oracle(device, bits, hidden, inter, k, n_exp):
+    """The one-token kernels (router + digit form of x, routing + gate/up, down + combine)
+    over the supported widths, every top_k class of the down kernel and both code widths."""
+    print(f"one token q{bits} hidden={hidden} inter={inter} k={k} experts={n_exp}", flush=True)
+    L = host_layer(41, 0, bits, n_exp, k, hidden, inter, device)
+    OL = OracleLayer(41, 0, bits, n_exp, k, hidden, inter)
+    X = _x(41, 200 + k, hidden, 2)
+    RES = synth.activations(41, synth.T_RESIDUAL, 200 + k, 2, hidden)
+    assert _one_token(device, OL, L, X, RES, f"one token q{bits}") == 0
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_one_token_full_size_vs_oracle(device, bits):
+    """The benchmarked configuration: one decode token through the one-token kernels, 512
+    experts + 1 shared, hidden 4096, inter 1024, top-4, generated and packed on the device."""
+    hidden, inter, n_exp, k = 4096, 1024, 512, 4
+    print(f"one token full size q{bits}", flush=True)
+    L = device_layer(synth.SEED, 2, bits, n_exp, k, hidden, inter, device)
+    OL = OracleLayer(synth.SEED, 2, bits, n_exp, k, hidden, inter)
+    X = _x(synth.SEED, 3000 + bits, hidden, 3)
+    RES = synth.activations(synth.SEED, synth.T_RESIDUAL, 3000 + bits, 3, hidden)
+    ties = _one_token(device, OL, L, X, RES, f"one token full q{bits}")
+    print(f"  near-ties: {ties}", flush=True)
+    del L
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("case", ["zero_group", "all_zero", "small", "large", "one_large_per_group", "integers"])
+def test_one_token_input_magnitudes(device, bits, case):
+    """Inputs that stress the digit form of x (per 64-column group: integers scaled below
+    2^22 from the group's largest magnitude): a group of zeros, x = 0 (every expert ties:
+    the lowest indices win), x scaled by 1e-6 and 1e6, one element 1e4 times the rest in
+    every group, and small integers (held exactly). The residual is 0, so the output is the
+    experts' contribution alone."""
+    hidden, inter, n_exp, k = 1024, 512, 32, 4
+    print(f"input magnitudes q{bits} {case}", flush=True)
+    L = host_layer(43, 0, bits, n_exp, k, hidden, inter, device)
+    OL = OracleLayer(43, 0, bits, n_exp, k, hidden, inter)
+    X = _x(43, 0, hidden, 2).astype(np.float64)
+    if case == "zero_group":
+        X[:, 64:128] = 0.0
+    elif case == "all_zero":
+        X[:] = 0.0
+    elif case == "small":
+        X *= 1e-6
+    elif case == "large":
+        X *= 1e6
+    elif case == "one_large_per_group":
+        X[:, ::64] *= 1e4
+    else:
+        X = np.round(X * 8.0)
+    X = X.astype(np.float32)
+    RES = np.zeros_like(X)
+    assert _one_token(device, OL, L, X, RES, f"magnitudes q{bits} {case}") == 0
+
+
+def test_stack_one_token_q2(device):
+    """A 4-layer 2-bit stack for one token, RMS scaling between layers, against the oracle's
+    own chain."""
+    hidden, inter, n_exp, k, n_layers, bits = 1024, 256, 32, 4, 4, 2
+    layers = [host_layer(51, l, bits, n_exp, k, hidden, inter, device) for l in range(n_layers)]
+    OLs = [OracleLayer(51, l, bits, n_exp, k, hidden, inter) for l in range(n_layers)]
+    h0 = synth.activations(51, synth.T_H0, 1, 1, hidden)
+    h_all = torch.empty((n_layers, 1, hidden), dtype=torch.float32, device=device)
+    idx = torch.empty((n_layers, 1, k), dtype=torch.int32, device=device)
+    qem.fmoe_moe_stack(layers, to_dev(h0, device), h_all=h_all, topk_idx=idx)
+    torch.cuda.synchronize()
+    ha, gi = h_all.cpu().numpy(), idx.cpu().numpy()
+    h = h0[0].astype(np.float64)
+    for l in range(n_layers):
+        ref, ri, rw, logits = OLs[l].forward(oracle.rms_scale(h), h)
+        assert list(gi[l, 0]) == list(ri), l
+        assert_close(ha[l, 0], ref, f"stack q2 layer {l}")
+        h = ref
+
+
 # --------------------------------------------------------------------------- grouped (B > 1)
 
 @pytest.mark.parametrize("bits", [4, 2])
