@@ -218,8 +218,8 @@ def test_one_token_input_magnitudes(device, bits, case):
     """Inputs that stress the digit form of x (per 64-column group: integers scaled below
     2^22 from the group's largest magnitude): a group of zeros, x = 0 (every expert ties:
     the lowest indices win), x scaled by 1e-6 and 1e6, one element 1e4 times the rest in
-    every group, and small integers (held exactly). The residual is 0, so the output is the
-    experts' contribution alone."""
+    every group, and small integers (held exactly); then the same tokens through the grouped
+    kernels. The residual is 0, so the output is the experts' contribution alone."""
     hidden, inter, n_exp, k = 1024, 512, 32, 4
     print(f"input magnitudes q{bits} {case}", flush=True)
     L = host_layer(43, 0, bits, n_exp, k, hidden, inter, device)
@@ -240,6 +240,8 @@ def test_one_token_input_magnitudes(device, bits, case):
     X = X.astype(np.float32)
     RES = np.zeros_like(X)
     assert _one_token(device, OL, L, X, RES, f"magnitudes q{bits} {case}") == 0
+    # the same tokens together (the grouped kernels: x as three bf16 parts)
+    assert _check_layer(device, OL, L, X, RES, f"magnitudes q{bits} {case} grouped") == 0
 
 
 def test_stack_one_token_q2(device):
