@@ -90,6 +90,34 @@ __device__ __forceinline__ void stage_store(const Staged<N4> &st, int nf4, float
   }
 }
 
+// Store into padded LDS rows, and each 64-value group's sum into gsum[]: a
+// thread's float4 sum ((x + y) + (z + w)), then DPP over the 16 consecutive
+// threads that hold the group (nf4 a multiple of 16, BS of 64).
+template <int N4, int BS>
+__device__ __forceinline__ void stage_store_gsum(const Staged<N4> &st, int nf4, float *lds, float *gsum) {
+#pragma unroll
+  for (int k = 0; k < N4; ++k) {
+    const int f = threadIdx.x + BS * k;
+    const float4 v = st.v[k];
+    if (f < nf4) *reinterpret_cast<float4 *>(&lds[lds_index(4 * f)]) = v;
+    const float t = seg_reduce<16>((v.x + v.y) + (v.z + v.w));
+    if (f < nf4 && seg_last<16>(lane_id())) gsum[f >> 4] = t;
+  }
+}
+
+// Lane's slice x[64g .. 64g+63] from padded LDS, with its sum given.
+__device__ __forceinline__ void read_slice_sum(const float *lds, int g, float sum, XSlice &xs) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float4 t = *reinterpret_cast<const float4 *>(&lds[g * kXPad + 4 * i]);
+    xs.v[4 * i] = t.x;
+    xs.v[4 * i + 1] = t.y;
+    xs.v[4 * i + 2] = t.z;
+    xs.v[4 * i + 3] = t.w;
+  }
+  xs.sum = sum;
+}
+
 // Store into unpadded LDS (a plain copy of nf4 16-byte units).
 template <int N4>
 __device__ __forceinline__ void stage_copy(const Staged<N4> &st, int nf4, uint32_t *lds) {
@@ -748,6 +776,8 @@ __global__ __launch_bounds__(kP3Block) void k_phase3(const Phase3Args a) {
   constexpr bool STAGE = KPAD * NGI <= 128;
   __shared__ float hl[STAGE ? KPAD * NGI * kXPad : 1];
   __shared__ float hs[NGI * kXPad];
+  __shared__ float hlsum[STAGE ? KPAD * NGI : 1];  // per-group sums of the staged h
+  __shared__ float hssum[NGI];
   __shared__ float dsh[kP3Waves * RPW];
   trace_mark(a.trace, 0);
   const int lane = lane_id();
@@ -785,7 +815,9 @@ __global__ __launch_bounds__(kP3Block) void k_phase3(const Phase3Args a) {
   stage_load<S4, kP3Block>(sh ? a.h_shared : a.h_routed, NGI * 16, sst);
   __builtin_amdgcn_sched_barrier(0);  // every h load goes out before any weight load
   const uint8_t *sdown = sh ? a.shared_down : a.bank + a.gu_bytes;
-  const int ssub = lane / NGI, sg = lane & (NGI - 1);
+  // shared rows: NGI lanes per row; with fewer rows per wavefront than a load
+  // covers, the spare lanes repeat this wavefront's rows (the same cache lines)
+  const int ssub = RPW < RPII ? (lane / NGI) % RPW : lane / NGI, sg = lane & (NGI - 1);
   Chunk<BITS> cs[SIT];
   uint32_t ss[SIT];
 #pragma unroll
@@ -810,14 +842,14 @@ __global__ __launch_bounds__(kP3Block) void k_phase3(const Phase3Args a) {
     for (int m = 0; m < SPL; ++m) load_group<BITS, NGI>(base[m] + (size_t)row * RB, grp[m], c[i][m], sb[i][m]);
   }
   __builtin_amdgcn_sched_barrier(0);  // the h vectors were requested before the weights
-  if constexpr (STAGE) stage_store<H4, false, kP3Block>(hst, a.K * a.I / 4, hl, nullptr);
-  stage_store<S4, false, kP3Block>(sst, NGI * 16, hs, nullptr);
+  if constexpr (STAGE) stage_store_gsum<H4, kP3Block>(hst, a.K * a.I / 4, hl, hlsum);
+  stage_store_gsum<S4, kP3Block>(sst, NGI * 16, hs, hssum);
   __syncthreads();
   trace_mark(a.trace, 1);
   if (row0 >= a.H) return;
   if (sh) {
     XSlice xs;
-    read_slice(hs, sg, 1.f, xs);
+    read_slice_sum(hs, sg, hssum[sg], xs);
 #pragma unroll
     for (int q = 0; q < SIT; ++q) {
       const float p = seg_reduce<NGI>(group_partial<BITS>(cs[q], ss[q], xs));
@@ -828,7 +860,7 @@ __global__ __launch_bounds__(kP3Block) void k_phase3(const Phase3Args a) {
   XSlice xs[SPL];
   if constexpr (STAGE) {
 #pragma unroll
-    for (int m = 0; m < SPL; ++m) read_slice(hl, kk[m] * NGI + grp[m], 1.f, xs[m]);
+    for (int m = 0; m < SPL; ++m) read_slice_sum(hl, kk[m] * NGI + grp[m], hlsum[kk[m] * NGI + grp[m]], xs[m]);
   } else {
 #pragma unroll
     for (int m = 0; m < SPL; ++m) load_xslice(a.h_routed + (size_t)kk[m] * a.I + kGroup * grp[m], xs[m]);
