@@ -375,23 +375,40 @@ struct MfmaRows {
 
 // ------------------------------------------------------------------ g1
 
-// g1: workgroups [0, n_router_blocks): router rows (one fp32 row per
-// wavefront; row E is the gate vector) against every token's x, unscaled.
-// Workgroups n_router_blocks + t: token t's x for the matrix cores (RMS factor
-// xinv, per-group sums of x, three bf16 parts in MFMA order).
+// g1: workgroups [0, n_router_blocks): router rows against every token's x,
+// unscaled (each row split over router_split() wavefronts, two rows per
+// workgroup, so that 512 rows take 256 compute units). Workgroups
+// n_router_blocks + t: token t's x for the matrix cores (RMS factor xinv,
+// per-group sums of x, three bf16 parts in MFMA order) and its gate dot product
+// g . x (unscaled).
+constexpr int kG1Chunk = 4;  // tokens whose x is staged in LDS at a time
+template <int NGH>
+__host__ __device__ constexpr int g1_rows_per_block() {
+  return kWavesPerBlock / router_split<NGH>();
+}
+
 template <int BITS, int NGH>
 __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
   constexpr int NT = NGH / 4;
   constexpr int H = NGH * kGroup;
-  __shared__ float part[1][kWavesPerBlock];
+  constexpr int SPLIT = router_split<NGH>();
+  constexpr int NTW = NT / SPLIT;                            // float4 per lane of a wavefront's part of a row
+  constexpr int RPB = g1_rows_per_block<NGH>();
+  constexpr int CF4 = kG1Chunk * H / 4;                      // float4 of a chunk of tokens
+  constexpr int C4 = (CF4 + kBlock - 1) / kBlock;
+  __shared__ float part[2][kWavesPerBlock];
+  __shared__ uint32_t xc[kG1Chunk * H];                      // a chunk of tokens' x (fp32 bits)
+  __shared__ float dp[kWavesPerBlock][kMaxTokens];           // per wavefront: its part of each token's dot
   const int lane = lane_id();
+  const int wv = wave_in_block();
   const bool rms = a.rms_eps >= 0.f;
   if ((int)blockIdx.x >= a.n_router_blocks) {
-    // ---- input preparation of token t
+    // ---- input preparation of token t, and its gate dot product
     const int t = blockIdx.x - a.n_router_blocks;
     const float *xt = a.x + (size_t)t * H;
+    const float *gv = a.gvec ? a.gvec : a.x;  // (read but unused without a shared expert)
     constexpr int UNITS = NGH * 8;  // 8 columns each, in MFMA order: unit = 8g + 4m + q
-    float ss = 0.f;
+    float ss = 0.f, gd = 0.f;
     for (int u0 = 0; u0 < UNITS; u0 += kBlock) {
       const int u = u0 + threadIdx.x;
       const bool ok = u < UNITS;
@@ -400,7 +417,10 @@ __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
       const int c = 64 * g + mfma_col<BITS>(mq & 3, mq >> 2);
       const float4 v0 = *reinterpret_cast<const float4 *>(xt + c);
       const float4 v1 = *reinterpret_cast<const float4 *>(xt + c + 4);
+      const float4 g0 = *reinterpret_cast<const float4 *>(gv + c);
+      const float4 g1 = *reinterpret_cast<const float4 *>(gv + c + 4);
       const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      const float gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
       uint32_t pt[8][3];
       float sum = 0.f, rep = 0.f;
 #pragma unroll
@@ -409,7 +429,10 @@ __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
         bf16_split3(f[j], pt[j], r);
         sum += f[j];
         rep += r;
-        if (ok) ss = fmaf(f[j], f[j], ss);
+        if (ok) {
+          ss = fmaf(f[j], f[j], ss);
+          gd = fmaf(gw[j], f[j], gd);
+        }
       }
       // group sums: the group's 8 units are 8 consecutive threads
       sum = seg_allreduce<8>(sum);
@@ -426,60 +449,71 @@ __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
       }
     }
     ss = seg_reduce<kWave>(ss);
-    if (lane == kWave - 1) part[0][wave_in_block()] = ss;
+    gd = seg_reduce<kWave>(gd);
+    if (lane == kWave - 1) {
+      part[0][wv] = ss;
+      part[1][wv] = gd;
+    }
     __syncthreads();
-    if (threadIdx.x == 0) a.xinv[t] = rms ? rms_inv(part[0], H, a.rms_eps) : 1.f;
+    if (threadIdx.x == 0) {
+      a.xinv[t] = rms ? rms_inv(part[0], H, a.rms_eps) : 1.f;
+      if (a.gvec) {
+        float d = part[1][0];
+#pragma unroll
+        for (int i = 1; i < kWavesPerBlock; ++i) d += part[1][i];
+        a.gdot[t] = d;
+      }
+    }
     return;
   }
-  // ---- router rows: one fp32 row per wavefront, held in registers; the tokens'
-  // x vectors are read straight from memory (they sit in L2), two tokens in
-  // flight. The dot products are written unscaled: the RMS factor of each token
-  // (xinv, from the preparation workgroups) is applied by the routing kernel.
-  const int n_rows = a.E + (a.gvec ? 1 : 0);
-  const int row = blockIdx.x * kWavesPerBlock + wave_in_block();
-  const int rr = min(row, n_rows - 1);
-  const float *src = rr == a.E ? a.gvec : a.router + (size_t)rr * H;
-  float4 wr[NT];
+  // ---- router rows: a wavefront holds its part of one fp32 row in registers;
+  // the tokens' x vectors pass through LDS kG1Chunk at a time (the next
+  // chunk's loads in flight while the current one is used). The dot products
+  // are written unscaled: the RMS factor of each token (xinv, from the
+  // preparation workgroups) is applied by the routing.
+  const int half = wv % SPLIT;
+  const int row = (int)blockIdx.x * RPB + wv / SPLIT;
+  const int rr = min(row, a.E - 1);
+  const float4 *src = reinterpret_cast<const float4 *>(a.router + (size_t)rr * H) + 64 * NTW * half;
+  float4 wr[NTW];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) wr[t] = reinterpret_cast<const float4 *>(src)[lane + 64 * t];
-  float4 xa[NT], xb[NT];
-  auto load_x = [&](int t, float4(&v)[NT]) {
-    const float4 *xt4 = reinterpret_cast<const float4 *>(a.x + (size_t)t * H);
-#pragma unroll
-    for (int q = 0; q < NT; ++q) v[q] = xt4[lane + 64 * q];
-  };
-  // the dot product of token t (its x in v) with the row; the loaded words of v
-  // are needed from here on, not before
-  auto emit = [&](int t, float4(&v)[NT]) {
-#pragma unroll
-    for (int q = 0; q < NT; ++q) asm volatile("" : "+v"(v[q].x), "+v"(v[q].y), "+v"(v[q].z), "+v"(v[q].w));
-    float acc = 0.f;
-#pragma unroll
-    for (int q = 0; q < NT; ++q) {
-      acc = fmaf(wr[q].x, v[q].x, acc);
-      acc = fmaf(wr[q].y, v[q].y, acc);
-      acc = fmaf(wr[q].z, v[q].z, acc);
-      acc = fmaf(wr[q].w, v[q].w, acc);
-    }
-    const float d = seg_reduce<kWave>(acc);
-    if (lane == kWave - 1 && row < n_rows) {
-      if (row == a.E)
-        a.gdot[t] = d;
-      else
-        a.logits[(size_t)t * a.E + row] = d;
-    }
-  };
-  load_x(0, xa);
-  asm volatile("" ::: "memory");
+  for (int q = 0; q < NTW; ++q) wr[q] = src[lane + 64 * q];
+  Staged<C4> nx;
+  stage_load(a.x, min(kG1Chunk, a.B) * (H / 4), nx);
 #pragma unroll 1
-  for (int t = 0; t < a.B; t += 2) {
-    // (past the end: token B - 1 again, which rewrites its own values)
-    load_x(min(t + 1, a.B - 1), xb);
+  for (int c = 0; c < a.B; c += kG1Chunk) {
+    __syncthreads();  // the previous chunk's reads are done
+    stage_copy(nx, CF4, xc);
+    __syncthreads();
+    // the next chunk (past the end: the last tokens again, unused)
+    const int cn = min(c + kG1Chunk, a.B - 1);
+    stage_load(a.x + (size_t)cn * H, min(kG1Chunk, a.B - cn) * (H / 4), nx);
     asm volatile("" ::: "memory");
-    emit(t, xa);
-    load_x(min(t + 2, a.B - 1), xa);
-    asm volatile("" ::: "memory");
-    emit(min(t + 1, a.B - 1), xb);
+#pragma unroll
+    for (int tt = 0; tt < kG1Chunk; ++tt) {
+      const float4 *xv4 = reinterpret_cast<const float4 *>(xc) + tt * (H / 4) + 64 * NTW * half;
+      float acc = 0.f;
+#pragma unroll
+      for (int q = 0; q < NTW; ++q) {
+        const float4 xv = xv4[lane + 64 * q];
+        acc = fmaf(wr[q].x, xv.x, acc);
+        acc = fmaf(wr[q].y, xv.y, acc);
+        acc = fmaf(wr[q].z, xv.z, acc);
+        acc = fmaf(wr[q].w, xv.w, acc);
+      }
+      const float d = seg_reduce<kWave>(acc);
+      if (lane == kWave - 1 && c + tt < a.B) dp[wv][c + tt] = d;
+    }
+  }
+  __syncthreads();
+  // the parts of each row, added in order
+  for (int i = threadIdx.x; i < RPB * a.B; i += kBlock) {
+    const int r = i / a.B, t = i - r * a.B;
+    float d = dp[SPLIT * r][t];
+#pragma unroll
+    for (int h = 1; h < SPLIT; ++h) d += dp[SPLIT * r + h][t];
+    const int rw = (int)blockIdx.x * RPB + r;
+    if (rw < a.E) a.logits[(size_t)t * a.E + rw] = d;
   }
 }
 
@@ -850,7 +884,7 @@ struct GroupDispatch {
     const bool sh = a.shared != nullptr;
     const int S = a.B * a.K;
     const int shb = sh ? (a.B + kTokBlock - 1) / kTokBlock : 0;  // shared token blocks
-    a.n_router_blocks = blocks_for(a.E + (sh ? 1 : 0));
+    a.n_router_blocks = (a.E + g1_rows_per_block<NGH>() - 1) / g1_rows_per_block<NGH>();
     const int n4 = (a.B * (a.H / 4) + kBlock - 1) / kBlock;
     if (phases & 1)
       hipLaunchKernelGGL((k_g1<BITS, NGH>), dim3(a.n_router_blocks + a.B), dim3(kBlock), 0, s, a);
