@@ -129,7 +129,7 @@ fmoe_status layer_enqueue(const fmoe_layer *L, int B, const float *x, float rms_
     a.out = out + (size_t)t * H;
     a.topk_idx_out = topk_idx ? topk_idx + (size_t)t * K : nullptr;
     a.topk_w_out = topk_w ? topk_w + (size_t)t * K : nullptr;
-    a.logits = (float *)(ws + w.logits) + (size_t)t * E;
+    a.logits = (float *)(ws + w.logits) + (size_t)t * logit_stride(E);
     a.sigma = (float *)(ws + w.sigma) + t;
     a.ws_idx = (int32_t *)(ws + w.topk_idx) + (size_t)t * K;
     a.ws_w = (float *)(ws + w.topk_w) + (size_t)t * K;

@@ -229,7 +229,9 @@ struct MfmaRows {
   // one batch of staging loads: 16-byte units e0 + k kGThreads of the
   // 3 T NG 8 (vector 3u + part, unit); past the end, a clamped unit whose store
   // goes to the spare slot at XL
-  static constexpr int kBatch = 4;
+  // (12 covers the 3 T NG 8 units of four tokens at NG = 64 in one batch: one
+  // memory round trip instead of three)
+  static constexpr int kBatch = NG >= 32 ? 12 : 4;
   __device__ __forceinline__ static void load_batch(const uint16_t *__restrict__ xq_base, const int *tokv, int units,
                                                     int e0, uint4 (&xv)[kBatch], int (&xdst)[kBatch]) {
 #pragma unroll
@@ -513,7 +515,7 @@ __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
 #pragma unroll
     for (int h = 1; h < SPLIT; ++h) d += dp[SPLIT * r + h][t];
     const int rw = (int)blockIdx.x * RPB + r;
-    if (rw < a.E) a.logits[(size_t)t * a.E + rw] = d;
+    if (rw < a.E) a.logits[(size_t)t * logit_stride(a.E) + rw] = d;
   }
 }
 
@@ -568,12 +570,8 @@ __device__ __forceinline__ int block_route(const GroupArgs &a, RouteLds &R, int 
   const int S = a.B * a.K;
   const int nwl = (S + kWave - 1) / kWave;  // wavefronts holding slots
   for (int i = threadIdx.x; i < nwl * a.E; i += kGThreads) R.mask[i / a.E][i % a.E] = 0ull;
-  for (int t = wave; t < a.B; t += kGWaves) {
-    const float inv = a.xinv[t];
-    const float gd = a.gvec ? a.gdot[t] : 0.f;
-    int idx[kMaxTopK];
-    float w[kMaxTopK];
-    wave_topk_lds(a.logits + (size_t)t * a.E, a.E, a.K, idx, w, inv);
+  // token t's routing from its top-K (idx, w): slot experts, and the writer's outputs
+  auto publish = [&](int t, const int *idx, const float *w, float inv, float gd) {
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j)
       if (j == lane && j < a.K) {
@@ -587,6 +585,37 @@ __device__ __forceinline__ int block_route(const GroupArgs &a, RouteLds &R, int 
         }
       }
     if (writer && lane == 0 && a.gvec) a.sigma[t] = 1.f / (1.f + expf(-gd * inv));
+  };
+  if (a.E <= 512) {
+    // wavefront v: tokens v, v + 8, ...; two tokens per pass, all their loads
+    // (logits in the top-K's layout, RMS factor, gate dot) requested together
+    for (int t0 = wave; t0 < a.B; t0 += 2 * kGWaves) {
+      const int t1 = min(t0 + kGWaves, a.B - 1);  // (past the end: a repeat, unused)
+      float v0[8], v1[8];
+      load_logits<8>(a.logits + (size_t)t0 * logit_stride(a.E), a.E, v0);
+      load_logits<8>(a.logits + (size_t)t1 * logit_stride(a.E), a.E, v1);
+      const float inv0 = a.xinv[t0], inv1 = a.xinv[t1];
+      const float gd0 = a.gvec ? a.gdot[t0] : 0.f, gd1 = a.gvec ? a.gdot[t1] : 0.f;
+      int key[8], idx[kMaxTopK];
+      float w[kMaxTopK];
+      logit_keys<8>(v0, a.E, key);
+      wave_topk_keys<8>(key, a.K, idx, w, inv0);
+      publish(t0, idx, w, inv0, gd0);
+      if (t0 + kGWaves < a.B) {
+        logit_keys<8>(v1, a.E, key);
+        wave_topk_keys<8>(key, a.K, idx, w, inv1);
+        publish(t1, idx, w, inv1, gd1);
+      }
+    }
+  } else {
+    for (int t = wave; t < a.B; t += kGWaves) {
+      const float inv = a.xinv[t];
+      const float gd = a.gvec ? a.gdot[t] : 0.f;
+      int idx[kMaxTopK];
+      float w[kMaxTopK];
+      wave_topk_lds(a.logits + (size_t)t * logit_stride(a.E), a.E, a.K, idx, w, inv);
+      publish(t, idx, w, inv, gd);
+    }
   }
   __syncthreads();
   const int s = threadIdx.x;

@@ -31,7 +31,7 @@ struct LayerArgs {
   int32_t *topk_idx_out;     // [K] or null
   float *topk_w_out;         // [K] or null
   // workspace (device)
-  float *logits;             // [E]
+  float *logits;             // [E] (16-byte aligned, padded to a multiple of 4)
   float *sigma;              // [1]
   int32_t *ws_idx;           // [K]
   float *ws_w;               // [K]
@@ -59,7 +59,7 @@ struct GroupArgs {
   int32_t *out_idx;          // [B][K] or null
   float *out_w;              // [B][K] or null
   // workspace
-  float *logits;             // [B][E]     router rows . x, before the RMS factor
+  float *logits;             // [B][logit_stride(E)] router rows . x, before the RMS factor
   float *sigma;              // [B]
   float *gdot;               // [B]        gate vector . x, before the RMS factor
   int32_t *idx;              // [B][K]

@@ -345,12 +345,23 @@ __device__ __forceinline__ void wave_topk_keys(int (&key)[VPL], int K, int *idx,
   for (int j = 0; j < kMaxTopK; ++j) w[j] *= inv;
 }
 
-// lane l's VPL consecutive logits (clamped loads; the caller turns them into keys)
+// lane l's VPL consecutive logits, with 16-byte loads (clamped to the row; lg
+// 16-byte aligned and readable up to E rounded up to 4; the caller turns the
+// values into keys, those past E into the lowest key): one load instruction of
+// the wavefront covers whole cache lines, where VPL-strided 4-byte loads would
+// touch VPL times as many lines per instruction.
 template <int VPL>
 __device__ __forceinline__ void load_logits(const float *lg, int E, float (&v)[VPL]) {
   const int lane = lane_id();
+  const float4 *l4 = reinterpret_cast<const float4 *>(lg);
 #pragma unroll
-  for (int m = 0; m < VPL; ++m) v[m] = lg[min(VPL * lane + m, E - 1)];
+  for (int q = 0; q < VPL / 4; ++q) {
+    const float4 t = l4[min(VPL / 4 * lane + q, (E + 3) / 4 - 1)];
+    v[4 * q] = t.x;
+    v[4 * q + 1] = t.y;
+    v[4 * q + 2] = t.z;
+    v[4 * q + 3] = t.w;
+  }
 }
 
 template <int VPL>
@@ -641,7 +652,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   constexpr int NF4 = NGH * kDigStride / 4;  // 16-byte units of the digit form
   constexpr int D4 = (NF4 + kBlock - 1) / kBlock;
   __shared__ uint32_t xdl[NGH * kDigStride];
-  __shared__ float lg[kMaxExperts];
+  __shared__ __align__(16) float lg[kMaxExperts];
   __shared__ int sidx[kMaxTopK];
   __shared__ float sw[kMaxTopK];
   const int lane = lane_id();

@@ -53,9 +53,13 @@ inline size_t expert_bytes(int bits, int hidden, int inter) {
   return gateup_bytes(bits, hidden, inter) + down_bytes(bits, hidden, inter);
 }
 
+// Logits of one token in the workspace: E floats, padded to a multiple of 4 (the
+// routing reads them with 16-byte loads).
+constexpr int logit_stride(int E) { return (E + 3) & ~3; }
+
 // Workspace of one MoE layer for B tokens (all offsets 256-B aligned).
 struct LayerWs {
-  size_t logits;    // fp32 [B][E]
+  size_t logits;    // fp32 [B][logit_stride(E)]
   size_t sigma;     // fp32 [B]
   size_t topk_idx;  // int32 [B][K]
   size_t topk_w;    // fp32 [B][K]
@@ -84,7 +88,7 @@ inline LayerWs layer_ws(int B, int E, int K, int hidden, int inter) {
     o = round_up(o + bytes, 256);
     return at;
   };
-  w.logits = take(sizeof(float) * (size_t)B * E);
+  w.logits = take(sizeof(float) * (size_t)B * logit_stride(E));
   w.sigma = take(sizeof(float) * (size_t)B);
   w.topk_idx = take(sizeof(int32_t) * (size_t)B * K);
   w.topk_w = take(sizeof(float) * (size_t)B * K);
