@@ -244,6 +244,22 @@ def test_one_token_input_magnitudes(device, bits, case):
     assert _check_layer(device, OL, L, X, RES, f"magnitudes q{bits} {case} grouped") == 0
 
 
+@pytest.mark.parametrize("n_exp,k", [(5, 4), (513, 4), (1024, 8)])
+def test_layer_expert_counts(device, n_exp, k):
+    """Expert counts around the routing's layouts: 5 (logit rows padded to a multiple of 4,
+    lanes past the end), 513 and 1024 (the most experts: 16 logits per lane, and the
+    one-token kernel's routing through LDS). One token at a time, then grouped."""
+    hidden, inter, bits = 256, 256, 4
+    print(f"expert count {n_exp} k={k}", flush=True)
+    L = device_layer(44, 0, bits, n_exp, k, hidden, inter, device)
+    OL = OracleLayer(44, 0, bits, n_exp, k, hidden, inter)
+    X = _x(44, n_exp, hidden, 3)
+    RES = synth.activations(44, synth.T_RESIDUAL, n_exp, 3, hidden)
+    ties = _one_token(device, OL, L, X, RES, f"experts {n_exp} one token")
+    ties += _check_layer(device, OL, L, X, RES, f"experts {n_exp} grouped")
+    assert ties == 0
+
+
 def test_stack_one_token_q2(device):
     """A 4-layer 2-bit stack for one token, RMS scaling between layers, against the oracle's
     own chain."""
