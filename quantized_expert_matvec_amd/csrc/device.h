@@ -294,22 +294,6 @@ __device__ __forceinline__ bool seg_last(int lane) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.f + expf(-z)); }
 
-// Optional RMS scaling of the lane's x slice: the lanes of a segment of NG lanes
-// hold the whole vector (hidden = 64 * NG values), so the segment's sum of
-// squares gives the scale: x = h / sqrt(sum h^2 / hidden + eps).
-template <int NG>
-__device__ __forceinline__ void rms_scale_slice(XSlice &xs, float eps) {
-  float sq[64];
-#pragma unroll
-  for (int i = 0; i < 64; ++i) sq[i] = xs.v[i] * xs.v[i];
-  const float ss = seg_allreduce<NG>(tree_sum64(sq));
-  const float inv = 1.f / sqrtf(ss / (float)(kGroup * NG) + eps);
-#pragma unroll
-  for (int i = 0; i < 64; ++i) xs.v[i] *= inv;
-  xs.sum = tree_sum64(xs.v);
-}
-
-
 inline int blocks_for_waves(long waves) { return (int)((waves + (kBlock / kWave) - 1) / (kBlock / kWave)); }
 
 }  // namespace dev

@@ -3,16 +3,19 @@
 // (kernels_q4.hip, kernels_q2.hip), which instantiate the *_b<BITS> entries.
 //
 // A layer is three launches:
-//   phase 1  router logits, sigmoid(g . x), shared expert gate/up + SwiGLU
-//   phase 2  top-K (re-derived by every wavefront from the logits), routed
-//            gate/up + SwiGLU, shared expert down (scaled by its gate)
-//   phase 3  routed down + weighted combine + residual + shared expert output
-// Each block has one role. Its wavefronts first issue all of their weight
-// loads (registers), then the block stages the input vector it needs in LDS
-// once (one coalesced read instead of one per wavefront; padded rows of 68
-// floats make the per-lane 128-bit slice reads conflict-free), and only then
-// does any arithmetic. The row count per wavefront is fixed at compile time so
-// the code is straight-line and the compiler cannot sink loads toward their uses.
+//   phase 1  router logits (RMS scaling of the incoming h fused), x in digit
+//            form for phase 2, sigmoid(g . x)
+//   phase 2  top-K (re-derived by one wavefront of every routed block from the
+//            logits), routed gate/up + SwiGLU; shared expert gate/up + SwiGLU in
+//            blocks of their own, which need no routing
+//   phase 3  routed and shared down + weighted combine + residual
+// Each block has one role. Loads go out in the order they are needed (what the
+// block must wait for first, then the weights), every group of loads before the
+// first use of any of them; a block stages the vector it needs in LDS once (one
+// coalesced read instead of one per wavefront; padded rows of 68 floats make the
+// per-lane 128-bit slice reads conflict-free). The row count per wavefront is
+// fixed at compile time so the code is straight-line and the compiler cannot
+// sink loads toward their uses.
 #pragma once
 
 #include "device.h"
@@ -26,29 +29,6 @@ constexpr int kWavesPerBlock = kBlock / kWave;
 
 __device__ __forceinline__ int wave_in_block() { return threadIdx.x >> 6; }
 __device__ __forceinline__ int lds_index(int c) { return (c >> 6) * kXPad + (c & 63); }
-
-// Stage n = 64*NG floats from global memory into padded LDS rows. With SUMSQ the
-// block's sum of squares of the vector is formed in a fixed order: each thread
-// over its float4s, DPP within the wavefront, then the wavefronts in order;
-// part[] receives one partial per wavefront. The caller synchronises.
-template <int NG, bool SUMSQ>
-__device__ __forceinline__ void stage_vec(const float *__restrict__ src, float *lds, float *part) {
-  constexpr int NF4 = NG * 16;
-  float ss = 0.f;
-#pragma unroll
-  for (int k = 0; k < (NF4 + kBlock - 1) / kBlock; ++k) {
-    const int f = threadIdx.x + kBlock * k;
-    if (f < NF4) {
-      const float4 v = reinterpret_cast<const float4 *>(src)[f];
-      *reinterpret_cast<float4 *>(&lds[lds_index(4 * f)]) = v;
-      if constexpr (SUMSQ) ss += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
-    }
-  }
-  if constexpr (SUMSQ) {
-    ss = seg_reduce<kWave>(ss);
-    if (lane_id() == kWave - 1) part[wave_in_block()] = ss;
-  }
-}
 
 // Two-step staging, so that a wavefront can issue the vector's loads before its
 // weight loads (memory counters complete in order: waiting for the vector then
@@ -70,8 +50,10 @@ __device__ __forceinline__ void stage_load(const float *__restrict__ src, int nf
   }
 }
 
-// Store into padded LDS rows; with SUMSQ, the wavefront's partial sum of squares
-// (same fixed order as stage_vec) goes to part[].
+// Store into padded LDS rows; with SUMSQ, the block's sum of squares of the
+// vector is formed in a fixed order (each thread over its float4s, DPP within the
+// wavefront): part[] receives one partial per wavefront, which rms_inv adds in
+// order after the caller's barrier.
 template <int N4, bool SUMSQ, int BS = kBlock>
 __device__ __forceinline__ void stage_store(const Staged<N4> &st, int nf4, float *lds, float *part) {
   float ss = 0.f;
