@@ -251,7 +251,7 @@ struct MfmaRows {
   // writes; after() runs on every thread right after x is requested, to request
   // what the caller's epilogue needs; tile_done(tile) runs on every thread as
   // each tile's stream ends, with its rows in y.
-  template <typename Fill, typename After, typename TileDone>
+  template <bool PRE, typename Fill, typename After, typename TileDone>
   __device__ __forceinline__ void run(const uint8_t *__restrict__ rec0, size_t tile_stride,
                                       const uint16_t *__restrict__ xq_base, const float *__restrict__ xs_base, int T,
                                       int *tokv, Fill fill, After after, TileDone tile_done, uint8_t *xl,
@@ -264,54 +264,69 @@ struct MfmaRows {
     // per-token tables (tokv, ...) from values the caller requested earlier
     if ((int)threadIdx.x < T) fill((int)threadIdx.x);
     __syncthreads();  // tokv is written; earlier reads of xl / xsl are done
-    // Requests in the order they are needed: x (its group sums, then its parts:
-    // 3 T NG 8 16-byte units) and the caller's epilogue
-    // values; the first weight chunk; once x is in LDS (a wavefront issues in
-    // order, and a long queue of weight requests ahead of the staging stores
-    // would hold them up), the rest of the first DEPTH chunks. The parts move in
-    // batches (loads of a batch before its stores); stores are unconditional
-    // (lanes past the end write a spare slot: xl at XL, xsl at kTokBlock * NG),
-    // so that the optimiser keeps a batch's loads together.
-    const int units = kParts * T * NG * 8;
-    float2 sv;
-    int sdst;
-    {
-      const int e = min((int)threadIdx.x, T * NG - 1);
-      const int u = e / NG, gl = e - u * NG;
-      sv = reinterpret_cast<const float2 *>(xs_base)[(size_t)tokv[u] * NG + gl];
-      sdst = (int)threadIdx.x < T * NG ? u * NG + gl : kTokBlock * NG;
-    }
-    uint4 xv[kBatch];
-    int xdst[kBatch];
-    load_batch(xq_base, tokv, units, threadIdx.x, xv, xdst);
-    after();
     Chunk ring[DEPTH];
-    // narrow rows stage little x: then the whole prologue goes out at once
-    constexpr int EARLY = NG <= 16 ? DEPTH : 1;
+    int aoff, xoff;
+    if constexpr (PRE) {
+      // x is staged already, every token of the batch in token order (vector
+      // 3 t + part, group sums at t NG): the whole prologue goes out at once, and
+      // an A row reads its token's vector
+      after();
 #pragma unroll
-    for (int d = 0; d < EARLY; ++d) {
-      load_chunk(rec0, tile_stride, d, ring[d]);
-      asm volatile("" ::: "memory");
-    }
-    xsl[sdst] = sv;
+      for (int d = 0; d < DEPTH; ++d) {
+        load_chunk(rec0, tile_stride, d, ring[d]);
+        asm volatile("" ::: "memory");
+      }
+      aoff = (kParts * tokv[min(i >> 2, T - 1)] + min(i & 3, kParts - 1)) * VS + q * 16;
+      xoff = tokv[min(q, T - 1)] * NG;
+    } else {
+      // Requests in the order they are needed: x (its group sums, then its parts:
+      // 3 T NG 8 16-byte units) and the caller's epilogue
+      // values; the first weight chunk; once x is in LDS (a wavefront issues in
+      // order, and a long queue of weight requests ahead of the staging stores
+      // would hold them up), the rest of the first DEPTH chunks. The parts move in
+      // batches (loads of a batch before its stores); stores are unconditional
+      // (lanes past the end write a spare slot: xl at XL, xsl at kTokBlock * NG),
+      // so that the optimiser keeps a batch's loads together.
+      const int units = kParts * T * NG * 8;
+      float2 sv;
+      int sdst;
+      {
+        const int e = min((int)threadIdx.x, T * NG - 1);
+        const int u = e / NG, gl = e - u * NG;
+        sv = reinterpret_cast<const float2 *>(xs_base)[(size_t)tokv[u] * NG + gl];
+        sdst = (int)threadIdx.x < T * NG ? u * NG + gl : kTokBlock * NG;
+      }
+      uint4 xv[kBatch];
+      int xdst[kBatch];
+      load_batch(xq_base, tokv, units, threadIdx.x, xv, xdst);
+      after();
+      // narrow rows stage little x: then the whole prologue goes out at once
+      constexpr int EARLY = NG <= 16 ? DEPTH : 1;
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) *reinterpret_cast<uint4 *>(xl + xdst[k]) = xv[k];
-    for (int e0 = threadIdx.x + kBatch * kGThreads; e0 < units; e0 += kBatch * kGThreads) {
-      load_batch(xq_base, tokv, units, e0, xv, xdst);
-      asm volatile("" ::: "memory");
+      for (int d = 0; d < EARLY; ++d) {
+        load_chunk(rec0, tile_stride, d, ring[d]);
+        asm volatile("" ::: "memory");
+      }
+      xsl[sdst] = sv;
 #pragma unroll
       for (int k = 0; k < kBatch; ++k) *reinterpret_cast<uint4 *>(xl + xdst[k]) = xv[k];
-    }
-    __syncthreads();
+      for (int e0 = threadIdx.x + kBatch * kGThreads; e0 < units; e0 += kBatch * kGThreads) {
+        load_batch(xq_base, tokv, units, e0, xv, xdst);
+        asm volatile("" ::: "memory");
 #pragma unroll
-    for (int d = EARLY; d < DEPTH; ++d) {
-      load_chunk(rec0, tile_stride, d, ring[d]);
-      asm volatile("" ::: "memory");  // the loop's issue order (each chunk's loads together)
+        for (int k = 0; k < kBatch; ++k) *reinterpret_cast<uint4 *>(xl + xdst[k]) = xv[k];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int d = EARLY; d < DEPTH; ++d) {
+        load_chunk(rec0, tile_stride, d, ring[d]);
+        asm volatile("" ::: "memory");  // the loop's issue order (each chunk's loads together)
+      }
+      // A row i: token min(i / 4, T - 1), part min(i % 4, 2) (rows past T and the
+      // fourth part feed D rows that are never read); X: token min(q, T - 1)
+      aoff = (kParts * min(i >> 2, T - 1) + min(i & 3, kParts - 1)) * VS + q * 16;
+      xoff = min(q, T - 1) * NG;
     }
-    // A row i: token min(i / 4, T - 1), part min(i % 4, 2) (rows past T and the
-    // fourth part feed D rows that are never read); X: token min(q, T - 1)
-    const int aoff = (kParts * min(i >> 2, T - 1) + min(i & 3, kParts - 1)) * VS + q * 16;
-    const int xoff = min(q, T - 1) * NG;
     // chunk c from ring slot d; then (if REFILL) slot d requests chunk c + DEPTH
     auto step = [&](auto refill, int c, Chunk &slot) {
       // chunk c arrives here; into this wavefront's LDS region (the reads of
@@ -542,12 +557,15 @@ struct GroupItem {
 
 // LDS scratch of block_route (it lives in the x staging buffer, which is free
 // until staging starts).
-struct RouteLds {
-  unsigned long long mask[kGWaves][kMaxExperts];  // [v][e]: lanes of wavefront v routed to e
-  int sidx[kMaxSlots];                           // expert of each slot
-  int eoff[kMaxExperts];                         // list offset of each present expert
+template <int NW>  // wavefronts holding slots (slots 64 v .. 64 v + 63)
+struct RouteLdsT {
+  unsigned long long mask[NW][kMaxExperts];  // [v][e]: lanes of wavefront v routed to e
+  int sidx[64 * NW];                         // expert of each slot
+  int eoff[kMaxExperts];                     // list offset of each present expert
   int wtot[kGWaves];
 };
+using RouteLds = RouteLdsT<kGWaves>;  // every batch (kMaxSlots slots)
+using RouteLds1 = RouteLdsT<1>;       // at most 64 slots
 
 // Top-K of every token and the grouping of the S = B*K slots by expert, by one
 // workgroup of kGThreads threads, deterministic whatever the thread timing:
@@ -562,7 +580,8 @@ struct RouteLds {
 // On return blk[kBlkInts k ..] holds the token blocks (LDS; slotl[0..S) the
 // lists, as scratch); returns NB. The writer workgroup also stores the routing
 // (idx, w, sigma, the caller's outputs) and the table G.
-__device__ __forceinline__ int block_route(const GroupArgs &a, RouteLds &R, int *slotl, int *blk, bool writer) {
+template <int NW>
+__device__ __forceinline__ int block_route(const GroupArgs &a, RouteLdsT<NW> &R, int *slotl, int *blk, bool writer) {
   static_assert(kMaxSlots <= kGThreads, "one thread per slot");
   static_assert(kMaxExperts <= 2 * kGThreads, "two experts per thread in the scan");
   const int lane = lane_id();
@@ -697,7 +716,7 @@ __device__ __forceinline__ int block_route(const GroupArgs &a, RouteLds &R, int 
 // inter dimension) of one item's expert, for the item's tokens / slots.
 // Wavefront w holds rows 16w .. 16w + 15. h vectors: slot s at index s,
 // shared-expert token t at index S + t.
-template <int BITS, int NGH, int NGI>
+template <int BITS, int NGH, int NGI, bool PRE>
 __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
   constexpr size_t RB = (size_t)NGH * gbytes<BITS>();
   // staged x, and before it the routing scratch
@@ -723,6 +742,37 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
   const int max_items = sh_items + S * NGI;
   const bool writer = (int)blockIdx.x == sh_items % (int)gridDim.x;
   int NB = -1;  // routing not derived yet
+  // A batch of at most kTokBlock tokens: every item's tokens are among them, so
+  // their x is staged once, now, by the wavefronts past the batch's tokens
+  // (wavefront t < B derives token t's top-K meanwhile), in token order; the
+  // routing scratch then lives in the wavefronts' chunk regions instead of xl.
+  using MR = MfmaRows<BITS, NGH>;
+  constexpr bool pre = PRE;  // (launched for batches of at most kTokBlock tokens)
+  static_assert(sizeof(RouteLds1) <= sizeof(wlds), "routing scratch of a small batch fits the chunk regions");
+  if (pre && wv >= a.B) {  // (B <= kTokBlock < kGWaves: at least four such wavefronts)
+    const int nst = (kGWaves - a.B) * kWave, st = (int)threadIdx.x - a.B * kWave;
+    const int units = kParts * a.B * NGH * 8;
+    constexpr int kB = 12;
+    for (int e0 = st; e0 < units; e0 += kB * nst) {
+      uint4 v[kB];
+      int dst[kB];
+#pragma unroll
+      for (int k = 0; k < kB; ++k) {
+        const int ee = e0 + k * nst;
+        const int e = min(ee, units - 1);
+        const int vv = e / (NGH * 8), rr = e - vv * (NGH * 8);
+        v[k] = *reinterpret_cast<const uint4 *>(a.xq + (size_t)vv * NGH * 64 + 8 * rr);
+        dst[k] = ee < units ? vv * MR::VS + 16 * rr : MR::XL;
+      }
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int k = 0; k < kB; ++k) {
+        const uint4 t = v[k];  // (through a local: a direct struct copy kept v in scratch memory)
+        *reinterpret_cast<uint4 *>(xl + dst[k]) = t;
+      }
+    }
+    for (int e = st; e < a.B * NGH; e += nst) xsl[e] = reinterpret_cast<const float2 *>(a.xsum)[e];
+  }
   for (int item = blockIdx.x; item < max_items; item += gridDim.x) {
     GroupItem it;
     int gi;
@@ -732,7 +782,12 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
       it.q0 = kTokBlock * (item / NGI);
       it.n = min(kTokBlock, a.B - it.q0);
     } else {
-      if (NB < 0) NB = block_route(a, *reinterpret_cast<RouteLds *>(xl), slotl, blk, writer);
+      if (NB < 0) {
+        if constexpr (PRE)
+          NB = block_route(a, *reinterpret_cast<RouteLds1 *>(&wlds[0][0]), slotl, blk, writer);
+        else
+          NB = block_route(a, *reinterpret_cast<RouteLds *>(xl), slotl, blk, writer);
+      }
       const int kb = (item - sh_items) / NGI;
       if (kb >= NB) break;  // (uniform) later items are past the last block
       gi = (item - sh_items) % NGI;
@@ -755,8 +810,8 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
     float tinv;  // RMS factor of the token of this lane's D rows
     auto after = [&]() { tinv = a.xinv[tokv[min(qq, T - 1)]]; };
     float y = 0.f;
-    MfmaRows<BITS, NGH> M;
-    M.run(rec0, 0, a.xq, a.xsum, T, tokv, fill, after, [&](int) { y = M.y; }, xl, xsl, wlds[wv]);
+    MR M;
+    M.template run<PRE>(rec0, 0, a.xq, a.xsum, T, tokv, fill, after, [&](int) { y = M.y; }, xl, xsl, wlds[wv]);
     // h = silu(gate) * up: gate rows are even, up rows odd (adjacent lanes)
     float hs = 0.f, hr = 0.f;
     {
@@ -857,7 +912,7 @@ __global__ __launch_bounds__(kGThreads) void k_g3(const GroupArgs a) {
   auto done = [&](int tile) {
     if (qq < T) outp[(size_t)oidx[qq] * a.H + row0 + 128 * tile + n] = osc * M.y;
   };
-  M.run(rec0, (size_t)128 * RB, a.hq, a.hsum, T, tokv, fill, after, done, xl, xsl, wlds[wv]);
+  M.template run<false>(rec0, (size_t)128 * RB, a.hq, a.hsum, T, tokv, fill, after, done, xl, xsl, wlds[wv]);
 }
 
 // g4: out[t] = residual[t] + sum_k partial[t*K + k] (k ascending) + d_shared[t]
@@ -917,9 +972,13 @@ struct GroupDispatch {
     const int n4 = (a.B * (a.H / 4) + kBlock - 1) / kBlock;
     if (phases & 1)
       hipLaunchKernelGGL((k_g1<BITS, NGH>), dim3(a.n_router_blocks + a.B), dim3(kBlock), 0, s, a);
-    if (phases & 2)
-      hipLaunchKernelGGL((k_g2<BITS, NGH, NGI>), dim3(std::min((shb + S) * NGI, cu_count())), dim3(kGThreads), 0,
-                         s, a);
+    if (phases & 2) {
+      const dim3 grid(std::min((shb + S) * NGI, cu_count()));
+      if (a.B <= kTokBlock)
+        hipLaunchKernelGGL((k_g2<BITS, NGH, NGI, true>), grid, dim3(kGThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((k_g2<BITS, NGH, NGI, false>), grid, dim3(kGThreads), 0, s, a);
+    }
     if (phases & 4) {
       hipLaunchKernelGGL((k_g3<BITS, NGI>), dim3((shb + S) * (a.H / (128 * kG3Tiles))), dim3(kGThreads), 0, s,
                          a);
