@@ -100,10 +100,10 @@ fmoe_status layer_enqueue(const fmoe_layer *L, int B, const float *x, float rms_
     g.gdot = (float *)(ws + w.gdot);
     g.idx = (int32_t *)(ws + w.topk_idx);
     g.w = (float *)(ws + w.topk_w);
-    g.xq = (uint16_t *)(ws + w.xq);
+    g.xq = (uint8_t *)(ws + w.xq);
     g.xsum = (float *)(ws + w.xsum);
     g.xinv = (float *)(ws + w.xinv);
-    g.hq = (uint16_t *)(ws + w.hq);
+    g.hq = (uint8_t *)(ws + w.hq);
     g.hsum = (float *)(ws + w.hsum);
     g.d_shared = (float *)(ws + w.d_shared);
     g.partial = (float *)(ws + w.partial);

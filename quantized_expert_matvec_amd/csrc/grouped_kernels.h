@@ -5,35 +5,36 @@
 // layer_kernels.h, which instantiate group_b<BITS>.
 //
 // Several tokens against one weight row make a (skinny) dense contraction, so
-// the quantized experts run on the matrix cores: v_mfma_f32_16x16x32_bf16 with
-//   B operand = 16 weight rows x 32 columns of codes, each code c (BITS bits) as
-//               the exact bf16 value 2 + c / 2^(BITS-1): bit pattern 0x4000 with c
-//               in the top mantissa bits, which a shift, a mask and a byte
-//               permute produce (the constant stays small next to the code's part);
-//   A operand = 16 rows = 4 tokens x {hi, mid, lo, 0}, where hi = bf16(x),
-//               mid = bf16(x - hi), lo = bf16(x - hi - mid): three bf16 parts
-//               that add up to the fp32 x exactly (in the normal range);
-//   D (fp32)  = per (token part, weight row) the sum over 32 columns.
-// Two MFMAs cover a 64-column group; per (row, group) the epilogue applies the
-// affine dequantization in the group-factored form
-//   sum_j (c_j s + b) x_j = 2^(BITS-1) s * sum_j (2 + c_j / 2^(BITS-1)) x'_j
-//                           - 2^BITS s * sum_j x'_j + b sum_j x_j
-// where x' = hi + mid + lo is the value the matrix cores saw: the constant is
-// taken off with the sum of x' itself, the bias with the fp32 group sum of x.
-// Both sums are formed when x (or h) is prepared.
+// the quantized experts run on the matrix cores, on exact integer products:
+// v_mfma_i32_16x16x64_i8 with
+//   B operand = 16 weight rows x 64 columns (one group) of codes, each code c
+//               (BITS bits) as the byte c: a mask (and a shift) of the packed
+//               code words puts 16 codes of a row in a lane, in column order;
+//   A operand = 16 rows = 4 tokens x {d0, d1, d2, 0}: a group of 64 values v_j
+//               (x, or h) is held as v_j = f X_j, X_j an integer with
+//               |X_j| <= 2^22 (the group's largest |v_j| scaled just below 2^22,
+//               f a power of two), written with three signed base-256 digits,
+//               X = d0 + 256 d1 + 65536 d2;
+//   D (int32) = per (token digit, weight row) the exact sum over the group.
+// Per (row, group) the epilogue applies the group-factored dequantization
+//   sum_j (c_j s + b) v_j = s f (D0 + 256 D1 + 65536 D2) + b sum_j v_j
+// with the fp32 group sum of v formed when v is prepared. The only roundings
+// are those of the X_j (at most 2^-22 of the group's largest magnitude) and of
+// the fp32 combination.
 //
 // Four launches:
 //   g1  router rows . x of every token (fp32 rows held in registers, VALU, the
-//       tokens' x read from L2), unscaled; other workgroups prepare each token's
-//       x for the matrix cores: RMS factor, per-group sums, bf16 parts
+//       tokens' x through LDS), unscaled; other workgroups prepare each token's
+//       x for the matrix cores: RMS factor, per group the digit planes, the
+//       factor f and the sum of x
 //   g2  gate/up + SwiGLU of (shared expert or distinct expert, one group of 64
 //       gate/up pairs = 128 rows, one 16-row tile per wavefront) for all the
-//       tokens / slots using it; writes h as bf16 parts plus its group sums.
-//       The routed workgroups first derive the routing themselves (top-K of
-//       every token, the distinct experts in ascending id and, for each, the
-//       ascending list of the slots (token t, choice k; slot = t*K + k) routed to
-//       it); the shared expert's workgroups need none and stream at once
-//   g3  down of (shared expert or distinct expert, 128 rows): per token
+//       tokens / slots using it; writes h (one whole group per item) in the same
+//       integer form. The routed workgroups first derive the routing themselves
+//       (top-K of every token, the distinct experts in ascending id and, for
+//       each, the ascending list of the slots (token t, choice k; slot = t*K + k)
+//       routed to it); the shared expert's workgroups need none and stream at once
+//   g3  down of (shared expert or distinct expert, 256 rows): per token
 //       sigma * (D_s h) into d_shared, per slot w * (D h) into partial[slot]
 //   g4  out = residual + the K per-slot outputs in slot order + sigma * shared
 #pragma once
@@ -51,96 +52,78 @@ constexpr int kMaxSlots = kMaxTokens * kMaxTopK;
 // expert used by more tokens (the shared expert, mostly) gives several items,
 // which run on different compute units and re-read its rows (from the caches).
 constexpr int kTokBlock = 4;
-constexpr int kParts = 3;       // bf16 parts of an fp32 value
+constexpr int kParts = 3;       // signed 8-bit digit planes of a value's integer form
 constexpr int kGThreads = 512;  // workgroup of the matrix-core kernels: 8 wavefronts
 constexpr int kGWaves = kGThreads / kWave;
 constexpr int kMaxNG = 64;      // groups per row (4096 columns)
 constexpr int kWaveLds = 16 * (2 * 8 * 16 + 16) + 16 * 9 * 4;  // LDS bytes per wavefront for a weight chunk
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) int i32x4_t;
 
-// ------------------------------------------------------------------ bf16 and MFMA order
+// ------------------------------------------------------------------ integer form
 
-// bf16 bits of a finite float, round to nearest even.
-__device__ __forceinline__ uint32_t bf16_bits(float v) {
-  const uint32_t b = __float_as_uint(v);
-  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+// The shift k of a group whose largest magnitude is amax (< 2^e): values are
+// scaled by 2^k = 2^(22 - e), so that every X_j = round(v_j 2^k) has |X_j| <= 2^22.
+__device__ __forceinline__ int group_shift(float amax) {
+  int e;
+  frexpf(amax, &e);  // (e = 0 for amax = 0)
+  return 22 - e;
 }
-__device__ __forceinline__ float bf16_float(uint32_t h) { return __uint_as_float(h << 16); }
-
-// v = bf16(p[0]) + bf16(p[1]) + bf16(p[2]) (exactly, for v in the normal range);
-// rep = that sum as a float.
-__device__ __forceinline__ void bf16_split3(float v, uint32_t (&p)[3], float &rep) {
-  p[0] = bf16_bits(v);
-  const float r1 = v - bf16_float(p[0]);
-  p[1] = bf16_bits(r1);
-  p[2] = bf16_bits(r1 - bf16_float(p[1]));
-  rep = bf16_float(p[0]) + (bf16_float(p[1]) + bf16_float(p[2]));
+// The three signed base-256 digits of X = round(v 2^k): byte p of the result is
+// d_p (two's complement); adding 128 to every digit first keeps the word positive.
+__device__ __forceinline__ uint32_t digits3(float v, int k) {
+  const int X = (int)rintf(ldexpf(v, k));
+  return (uint32_t)(X + 0x808080) ^ 0x808080u;
 }
-
-// The MFMA order of a group's 64 columns: MFMA m (0, 1) takes from k-block q
-// (0..3) the 8 consecutive columns starting at mfma_col(q, m), matching which
-// packed codes lane (row, q) holds (see MCodes).
-template <int BITS>
-__device__ __forceinline__ int mfma_col(int q, int m) {
-  return BITS == 4 ? 32 * (q >> 1) + 8 * (2 * (q & 1) + m) : 16 * q + 8 * m;
+// The group's factor f = 2^-k; NaN when the group holds a non-finite value.
+__device__ __forceinline__ float group_factor(float amax, int k) {
+  return amax <= 3.402823466e38f ? ldexpf(1.f, -k) : __int_as_float(0x7FC00000);
 }
-// Position (0..63) of column c of a group in MFMA order.
-template <int BITS>
-__device__ __forceinline__ int mfma_pos(int c) {
-  int q, m;
-  if constexpr (BITS == 4) {
-    const int w = (c >> 3) & 3;
-    q = 2 * (c >> 5) + (w >> 1);
-    m = w & 1;
-  } else {
-    q = c >> 4;
-    m = (c >> 3) & 1;
-  }
-  return (m * 4 + q) * 8 + (c & 7);
+// Largest magnitude over the 8 consecutive lanes of a segment, as float bits
+// (non-negative floats order as integers; NaN above infinity), in every lane.
+__device__ __forceinline__ int seg_max8_bits(float v) {
+  int m = __float_as_int(fabsf(v));
+  m = max(m, dpp_i<0xB1, 0xF>(m, 0));   // lanes i, i^1
+  m = max(m, dpp_i<0x4E, 0xF>(m, 0));   // i, i^2
+  m = max(m, dpp_i<0x141, 0xF>(m, 0));  // row_half_mirror: i, 7-i
+  return m;
 }
 
-// One group of one weight row as held by lane (row, q): 16 codes for 4-bit (two
-// words, one per MFMA; bytes 8 (q & 1) .. + 7 of half q >> 1 of the group),
-// 16 codes for 2-bit (one word: word q of the group), and the (scale, bias) word.
+// One group of one weight row as held by lane (row, q): the 16 codes of columns
+// 16q .. 16q + 15 (4-bit: words 2q and 2q + 1 of the group; 2-bit: word q), and
+// the (scale, bias) word.
 struct MCodes {
   uint32_t c0, c1, sb;
 };
 
-// Four low bytes of bf16 values (code in the top mantissa bits) in v -> two
-// dwords of bf16 pairs: the high byte 0x40 above each (value 2 + c / 2^(BITS-1));
-// v_perm_b32 selects bytes 0..3 from v and 4..7 from the constant.
-__device__ __forceinline__ void bf16_pairs(uint32_t v, uint32_t &p0, uint32_t &p1) {
-  constexpr uint32_t K = 0x40404040u;
-  p0 = __builtin_amdgcn_perm(K, v, 0x04010400u);
-  p1 = __builtin_amdgcn_perm(K, v, 0x04030402u);
-}
-
-// The B operands of the group's two MFMAs (8 codes each, in column order).
+// The lane's B operand for the group: its 16 codes as bytes, byte j the code of
+// column 16q + j. (A operand bytes j of lane (row, q) take the same columns:
+// the matrix cores pair A and B bytes of the same k-block and position.)
 template <int BITS>
-__device__ __forceinline__ void mfma_codes(const MCodes &m, uint4 &u0, uint4 &u1) {
-  // each byte's code moved to bits 6..(7 - BITS) of its byte (bit 7, the low
-  // bit of the bf16 exponent of 2.0, stays clear)
+__device__ __forceinline__ i32x4_t mfma_codes(const MCodes &m) {
+  i32x4_t b;
   if constexpr (BITS == 4) {
-    bf16_pairs((m.c0 << 3) & 0x78787878u, u0.x, u0.y);
-    bf16_pairs((m.c0 >> 1) & 0x78787878u, u0.z, u0.w);
-    bf16_pairs((m.c1 << 3) & 0x78787878u, u1.x, u1.y);
-    bf16_pairs((m.c1 >> 1) & 0x78787878u, u1.z, u1.w);
+    // word w: byte b's low nibble is column 8w + b, its high nibble 8w + 4 + b
+    b[0] = (int)(m.c0 & 0x0F0F0F0Fu);
+    b[1] = (int)((m.c0 >> 4) & 0x0F0F0F0Fu);
+    b[2] = (int)(m.c1 & 0x0F0F0F0Fu);
+    b[3] = (int)((m.c1 >> 4) & 0x0F0F0F0Fu);
   } else {
-    bf16_pairs((m.c0 << 5) & 0x60606060u, u0.x, u0.y);
-    bf16_pairs((m.c0 << 3) & 0x60606060u, u0.z, u0.w);
-    bf16_pairs((m.c0 << 1) & 0x60606060u, u1.x, u1.y);
-    bf16_pairs((m.c0 >> 1) & 0x60606060u, u1.z, u1.w);
+    // byte b's field f (bits 2f, 2f + 1) is column 16q + 4f + b
+    b[0] = (int)(m.c0 & 0x03030303u);
+    b[1] = (int)((m.c0 >> 2) & 0x03030303u);
+    b[2] = (int)((m.c0 >> 4) & 0x03030303u);
+    b[3] = (int)((m.c0 >> 6) & 0x03030303u);
   }
+  return b;
 }
 
 // ------------------------------------------------------------------ matrix-core rows
 
 // Workgroup-cooperative (kGThreads threads): NTILE tiles of 16 rows per
 // wavefront (tile i: rows rec0 + i * tile_stride + r * RB, r = 0..15) against
-// T <= kTokBlock vectors tokv[u] of a prepared source: part k (0..2) at
-// xq_base + (3 vec + k) * NG * 64; per group (sum x, sum x') at
+// T <= kTokBlock vectors tokv[u] of a prepared source: digit plane k (0..2) at
+// xq_base + (3 vec + k) * NG * 64 (bytes); per group (f, sum v) at
 // xs_base + 2 (vec * NG + g). The vectors are staged in LDS once (xl: XL + 16
 // bytes, xsl: kTokBlock * NG + 1 entries). As each tile ends, lane (n = lane %
 // 16, u = lane / 16) holds in y row n of the tile for token u (meaningless for
@@ -169,7 +152,7 @@ struct MfmaRows {
   static constexpr int SBO = 16 * HALVES * NG;        // scale/bias words within a record
   static constexpr int RS = 16 * HALVES * CG + 16;    // LDS bytes per row of codes (padded)
   static constexpr int SBS = CG + 1;                  // LDS words per row of scale/bias (padded)
-  static constexpr int VS = NG * 128 + 16;            // LDS bytes per staged vector (padded)
+  static constexpr int VS = NG * 64 + 16;             // LDS bytes per staged vector (padded)
   static constexpr int XL = kParts * kTokBlock * VS;  // LDS bytes of staged x (a spare 16 B follow)
   static_assert(NG <= kMaxNG, "row width");
   static_assert(16 * RS + 64 * SBS <= kWaveLds, "chunk fits the wavefront's LDS region");
@@ -227,20 +210,19 @@ struct MfmaRows {
   }
 
   // one batch of staging loads: 16-byte units e0 + k kGThreads of the
-  // 3 T NG 8 (vector 3u + part, unit); past the end, a clamped unit whose store
-  // goes to the spare slot at XL
-  // (12 covers the 3 T NG 8 units of four tokens at NG = 64 in one batch: one
-  // memory round trip instead of three)
-  static constexpr int kBatch = NG >= 32 ? 12 : 4;
-  __device__ __forceinline__ static void load_batch(const uint16_t *__restrict__ xq_base, const int *tokv, int units,
+  // 3 T NG 4 (vector 3u + plane, unit); past the end, a clamped unit whose store
+  // goes to the spare slot at XL. One batch covers four tokens: a single memory
+  // round trip.
+  static constexpr int kBatch = (kParts * kTokBlock * NG * 4 + kGThreads - 1) / kGThreads;
+  __device__ __forceinline__ static void load_batch(const uint8_t *__restrict__ xq_base, const int *tokv, int units,
                                                     int e0, uint4 (&xv)[kBatch], int (&xdst)[kBatch]) {
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const int ee = e0 + k * kGThreads;
       const int e = min(ee, units - 1);
-      const int vv = e / (NG * 8), rr = e - vv * (NG * 8);
+      const int vv = e / (NG * 4), rr = e - vv * (NG * 4);
       const int vu = vv / kParts, vk = vv - kParts * vu;
-      xv[k] = *reinterpret_cast<const uint4 *>(xq_base + ((size_t)(kParts * tokv[vu] + vk) * NG) * 64 + 8 * rr);
+      xv[k] = *reinterpret_cast<const uint4 *>(xq_base + ((size_t)(kParts * tokv[vu] + vk) * NG) * 64 + 16 * rr);
       xdst[k] = ee < units ? vv * VS + 16 * rr : XL;
     }
   }
@@ -253,7 +235,7 @@ struct MfmaRows {
   // each tile's stream ends, with its rows in y.
   template <bool PRE, typename Fill, typename After, typename TileDone>
   __device__ __forceinline__ void run(const uint8_t *__restrict__ rec0, size_t tile_stride,
-                                      const uint16_t *__restrict__ xq_base, const float *__restrict__ xs_base, int T,
+                                      const uint8_t *__restrict__ xq_base, const float *__restrict__ xs_base, int T,
                                       int *tokv, Fill fill, After after, TileDone tile_done, uint8_t *xl,
                                       float2 *xsl, uint8_t *wl) {
     const int lane = lane_id();
@@ -279,15 +261,15 @@ struct MfmaRows {
       aoff = (kParts * tokv[min(i >> 2, T - 1)] + min(i & 3, kParts - 1)) * VS + q * 16;
       xoff = tokv[min(q, T - 1)] * NG;
     } else {
-      // Requests in the order they are needed: x (its group sums, then its parts:
-      // 3 T NG 8 16-byte units) and the caller's epilogue
+      // Requests in the order they are needed: x (its group factors and sums,
+      // then its digit planes: 3 T NG 4 16-byte units) and the caller's epilogue
       // values; the first weight chunk; once x is in LDS (a wavefront issues in
       // order, and a long queue of weight requests ahead of the staging stores
       // would hold them up), the rest of the first DEPTH chunks. The parts move in
       // batches (loads of a batch before its stores); stores are unconditional
       // (lanes past the end write a spare slot: xl at XL, xsl at kTokBlock * NG),
       // so that the optimiser keeps a batch's loads together.
-      const int units = kParts * T * NG * 8;
+      const int units = kParts * T * NG * 4;
       float2 sv;
       int sdst;
       {
@@ -322,8 +304,9 @@ struct MfmaRows {
         load_chunk(rec0, tile_stride, d, ring[d]);
         asm volatile("" ::: "memory");  // the loop's issue order (each chunk's loads together)
       }
-      // A row i: token min(i / 4, T - 1), part min(i % 4, 2) (rows past T and the
-      // fourth part feed D rows that are never read); X: token min(q, T - 1)
+      // A row i: token min(i / 4, T - 1), digit plane min(i % 4, 2) (rows past T
+      // and the fourth row of a token feed D rows that are never read); X: token
+      // min(q, T - 1)
       aoff = (kParts * min(i >> 2, T - 1) + min(i & 3, kParts - 1)) * VS + q * 16;
       xoff = min(q, T - 1) * NG;
     }
@@ -358,20 +341,16 @@ struct MfmaRows {
           m.c1 = 0;
         }
         m.sb = *reinterpret_cast<const uint32_t *>(wl + rsb + 4 * j);
-        uint4 u0, u1;
-        mfma_codes<BITS>(m, u0, u1);
-        const float sp = scale_of(m.sb) * (float)(1 << (BITS - 1));  // exact (powers of two)
-        const float ns = scale_of(m.sb) * -(float)(1 << BITS);
-        const float bi = bias_of(m.sb);
-        const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, u0), b1 = __builtin_bit_cast(bf16x8_t, u1);
-        const uint8_t *src = xl + aoff + g * 128;
-        const bf16x8_t A0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(src));
-        const bf16x8_t A1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(src + 64));
-        const float2 X = xsl[xoff + g];
-        f32x4_t dd = {0.f, 0.f, 0.f, 0.f};
-        dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, b0, dd, 0, 0, 0);
-        dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, b1, dd, 0, 0, 0);
-        y = fmaf(sp, dd[0] + (dd[1] + dd[2]), fmaf(ns, X.y, fmaf(bi, X.x, y)));
+        const i32x4_t b = mfma_codes<BITS>(m);
+        const i32x4_t A = *reinterpret_cast<const i32x4_t *>(xl + aoff + g * 64);
+        i32x4_t dd = {0, 0, 0, 0};
+        dd = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, b, dd, 0, 0, 0);
+        // D rows 4q .. 4q + 2 of this lane: token q's three digit sums (exact);
+        // their value sum_j c_j X_j, the low two digits in 32-bit integers
+        const int lo = dd[0] + 256 * dd[1];
+        const float S = fmaf((float)dd[2], 65536.f, (float)lo);
+        const float2 F = xsl[xoff + g];  // (f, sum v) of token q's group
+        y = fmaf(scale_of(m.sb) * F.x, S, fmaf(bias_of(m.sb), F.y, y));
       }
       if (c % NC == NC - 1) {  // (uniform) the tile's last chunk
         tile_done(c / NC);
@@ -395,9 +374,9 @@ struct MfmaRows {
 // g1: workgroups [0, n_router_blocks): router rows against every token's x,
 // unscaled (each row split over router_split() wavefronts, two rows per
 // workgroup, so that 512 rows take 256 compute units). Workgroups
-// n_router_blocks + t: token t's x for the matrix cores (RMS factor xinv,
-// per-group sums of x, three bf16 parts in MFMA order) and its gate dot product
-// g . x (unscaled).
+// n_router_blocks + t: token t's x for the matrix cores (RMS factor xinv; per
+// group the three digit planes, the factor f and the sum of x) and its gate dot
+// product g . x (unscaled).
 constexpr int kG1Chunk = 4;  // tokens whose x is staged in LDS at a time
 template <int NGH>
 __host__ __device__ constexpr int g1_rows_per_block() {
@@ -424,45 +403,49 @@ __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
     const int t = blockIdx.x - a.n_router_blocks;
     const float *xt = a.x + (size_t)t * H;
     const float *gv = a.gvec ? a.gvec : a.x;  // (read but unused without a shared expert)
-    constexpr int UNITS = NGH * 8;  // 8 columns each, in MFMA order: unit = 8g + 4m + q
+    constexpr int UNITS = NGH * 8;  // 8 consecutive columns each: unit u = columns 8u .. 8u + 7
     float ss = 0.f, gd = 0.f;
     for (int u0 = 0; u0 < UNITS; u0 += kBlock) {
       const int u = u0 + threadIdx.x;
       const bool ok = u < UNITS;
       const int uc = ok ? u : UNITS - 1;
-      const int g = uc >> 3, mq = uc & 7;
-      const int c = 64 * g + mfma_col<BITS>(mq & 3, mq >> 2);
+      const int g = uc >> 3;
+      const int c = 8 * uc;
       const float4 v0 = *reinterpret_cast<const float4 *>(xt + c);
       const float4 v1 = *reinterpret_cast<const float4 *>(xt + c + 4);
       const float4 g0 = *reinterpret_cast<const float4 *>(gv + c);
       const float4 g1 = *reinterpret_cast<const float4 *>(gv + c + 4);
       const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
       const float gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-      uint32_t pt[8][3];
-      float sum = 0.f, rep = 0.f;
+      float sum = 0.f, amax = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        float r;
-        bf16_split3(f[j], pt[j], r);
         sum += f[j];
-        rep += r;
+        amax = __int_as_float(max(__float_as_int(amax), __float_as_int(fabsf(f[j]))));
         if (ok) {
           ss = fmaf(f[j], f[j], ss);
           gd = fmaf(gw[j], f[j], gd);
         }
       }
-      // group sums: the group's 8 units are 8 consecutive threads
+      // the group's 8 units are 8 consecutive threads
       sum = seg_allreduce<8>(sum);
-      rep = seg_allreduce<8>(rep);
-      if (ok) {
-        uint16_t *dst = a.xq + ((size_t)(kParts * t) * NGH + g) * 64 + 8 * mq;
+      const float gmax = __int_as_float(seg_max8_bits(amax));
+      const int k = group_shift(gmax);
+      uint32_t d[8];
 #pragma unroll
-        for (int k = 0; k < kParts; ++k) {
-          const uint4 v4 = {pt[0][k] | pt[1][k] << 16, pt[2][k] | pt[3][k] << 16, pt[4][k] | pt[5][k] << 16,
-                            pt[6][k] | pt[7][k] << 16};
-          *reinterpret_cast<uint4 *>(dst + (size_t)k * NGH * 64) = v4;
+      for (int j = 0; j < 8; ++j) d[j] = digits3(f[j], k);
+      if (ok) {
+        uint8_t *dst = a.xq + ((size_t)(kParts * t) * NGH + g) * 64 + 8 * (uc & 7);
+#pragma unroll
+        for (int p = 0; p < kParts; ++p) {
+          const int sh = 8 * p;
+          const uint2 w = {((d[0] >> sh) & 0xFFu) | ((d[1] >> sh) & 0xFFu) << 8 | ((d[2] >> sh) & 0xFFu) << 16 |
+                               ((d[3] >> sh) & 0xFFu) << 24,
+                           ((d[4] >> sh) & 0xFFu) | ((d[5] >> sh) & 0xFFu) << 8 | ((d[6] >> sh) & 0xFFu) << 16 |
+                               ((d[7] >> sh) & 0xFFu) << 24};
+          *reinterpret_cast<uint2 *>(dst + (size_t)p * NGH * 64) = w;
         }
-        if (mq == 0) reinterpret_cast<float2 *>(a.xsum)[(size_t)t * NGH + g] = make_float2(sum, rep);
+        if ((uc & 7) == 0) reinterpret_cast<float2 *>(a.xsum)[(size_t)t * NGH + g] = make_float2(group_factor(gmax, k), sum);
       }
     }
     ss = seg_reduce<kWave>(ss);
@@ -751,7 +734,7 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
   static_assert(sizeof(RouteLds1) <= sizeof(wlds), "routing scratch of a small batch fits the chunk regions");
   if (pre && wv >= a.B) {  // (B <= kTokBlock < kGWaves: at least four such wavefronts)
     const int nst = (kGWaves - a.B) * kWave, st = (int)threadIdx.x - a.B * kWave;
-    const int units = kParts * a.B * NGH * 8;
+    const int units = kParts * a.B * NGH * 4;
     constexpr int kB = 12;
     for (int e0 = st; e0 < units; e0 += kB * nst) {
       uint4 v[kB];
@@ -760,8 +743,8 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
       for (int k = 0; k < kB; ++k) {
         const int ee = e0 + k * nst;
         const int e = min(ee, units - 1);
-        const int vv = e / (NGH * 8), rr = e - vv * (NGH * 8);
-        v[k] = *reinterpret_cast<const uint4 *>(a.xq + (size_t)vv * NGH * 64 + 8 * rr);
+        const int vv = e / (NGH * 4), rr = e - vv * (NGH * 4);
+        v[k] = *reinterpret_cast<const uint4 *>(a.xq + (size_t)vv * NGH * 64 + 16 * rr);
         dst[k] = ee < units ? vv * MR::VS + 16 * rr : MR::XL;
       }
       asm volatile("" ::: "memory");
@@ -812,48 +795,56 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
     float y = 0.f;
     MR M;
     M.template run<PRE>(rec0, 0, a.xq, a.xsum, T, tokv, fill, after, [&](int) { y = M.y; }, xl, xsl, wlds[wv]);
-    // h = silu(gate) * up: gate rows are even, up rows odd (adjacent lanes)
-    float hs = 0.f, hr = 0.f;
+    // h = silu(gate) * up: gate rows are even, up rows odd (adjacent lanes); the
+    // item's 64 pairs are one whole group of h (pair 8 wv + n / 2)
+    float hv = 0.f;
     {
       const float yv = y * tinv;
       const float up = dpp_f<0xB1, 0xF>(yv, 0.f);  // partner row (quad_perm [1,0,3,2])
-      if ((n & 1) == 0 && qq < T) {
-        const float h = silu(yv) * up;
-        const int pl = 8 * wv + (n >> 1);  // pair within the group
-        uint16_t *dst = a.hq + (size_t)(kParts * hvl[qq]) * a.I + 64 * gi + mfma_pos<BITS>(pl);
-        uint32_t pt[3];
-        float r;
-        bf16_split3(h, pt, r);
-#pragma unroll
-        for (int k = 0; k < kParts; ++k) dst[(size_t)k * a.I] = (uint16_t)pt[k];
-        hs = h;
-        hr = r;
-      }
+      if ((n & 1) == 0 && qq < T) hv = silu(yv) * up;
     }
-    // group sums of h: the even lanes of each 16-lane row (odd lanes hold 0), then
-    // the wavefronts in order
+    // per token: the group's sum of h and largest magnitude, over the even lanes
+    // of each 16-lane row (odd lanes hold 0), then the wavefronts in order
     {
-      float r = hs, e = hr;
-      r += dpp_f<0xB1, 0xF>(r, 0.f);   // lanes n, n^1
-      e += dpp_f<0xB1, 0xF>(e, 0.f);
-      r += dpp_f<0x4E, 0xF>(r, 0.f);   // n, n^2
-      e += dpp_f<0x4E, 0xF>(e, 0.f);
+      float r = hv;
+      int m = __float_as_int(fabsf(hv));
+      r += dpp_f<0xB1, 0xF>(r, 0.f);  // lanes n, n^1
+      m = max(m, dpp_i<0xB1, 0xF>(m, 0));
+      r += dpp_f<0x4E, 0xF>(r, 0.f);  // n, n^2
+      m = max(m, dpp_i<0x4E, 0xF>(m, 0));
       r += dpp_f<0x141, 0xF>(r, 0.f);  // row_half_mirror: n, 7-n
-      e += dpp_f<0x141, 0xF>(e, 0.f);
+      m = max(m, dpp_i<0x141, 0xF>(m, 0));
       r += dpp_f<0x140, 0xF>(r, 0.f);  // row_mirror: n, 15-n
-      e += dpp_f<0x140, 0xF>(e, 0.f);
-      if (n == 0 && qq < T) hpart[wv][qq] = make_float2(r, e);
+      m = max(m, dpp_i<0x140, 0xF>(m, 0));
+      if (n == 0 && qq < T) hpart[wv][qq] = make_float2(r, __int_as_float(m));
     }
     __syncthreads();
+    // h of this lane in integer form (its token's group shift), and per token the
+    // group's factor and sum
+    {
+      const int u = min(qq, T - 1);
+      int mb = __float_as_int(hpart[0][u].y);
+#pragma unroll
+      for (int v = 1; v < kGWaves; ++v) mb = max(mb, __float_as_int(hpart[v][u].y));
+      const int k = group_shift(__int_as_float(mb));
+      if ((n & 1) == 0 && qq < T) {
+        const uint32_t d = digits3(hv, k);
+        uint8_t *dst = a.hq + (size_t)(kParts * hvl[qq]) * a.I + 64 * gi + 8 * wv + (n >> 1);
+#pragma unroll
+        for (int p = 0; p < kParts; ++p) dst[(size_t)p * a.I] = (uint8_t)(d >> (8 * p));
+      }
+    }
     if ((int)threadIdx.x < T) {
       const int u = threadIdx.x;
-      float2 t = hpart[0][u];
+      float sum = hpart[0][u].x;
+      int mb = __float_as_int(hpart[0][u].y);
 #pragma unroll
       for (int v = 1; v < kGWaves; ++v) {
-        t.x += hpart[v][u].x;
-        t.y += hpart[v][u].y;
+        sum += hpart[v][u].x;
+        mb = max(mb, __float_as_int(hpart[v][u].y));
       }
-      reinterpret_cast<float2 *>(a.hsum)[(size_t)hvl[u] * NGI + gi] = t;
+      const float amax = __int_as_float(mb);
+      reinterpret_cast<float2 *>(a.hsum)[(size_t)hvl[u] * NGI + gi] = make_float2(group_factor(amax, group_shift(amax)), sum);
     }
   }
 }

@@ -64,10 +64,10 @@ struct GroupArgs {
   float *gdot;               // [B]        gate vector . x, before the RMS factor
   int32_t *idx;              // [B][K]
   float *w;                  // [B][K]
-  uint16_t *xq;              // [B][3][H]  x as three bf16 parts, matrix-core order
-  float *xsum;               // [B][H/64][2] per group: sum of x, sum of its parts
+  uint8_t *xq;               // [B][3][H]  x in integer form: three signed 8-bit digit planes
+  float *xsum;               // [B][H/64][2] per group: the factor f, the sum of x
   float *xinv;               // [B]        RMS factor of x (1 without RMS scaling)
-  uint16_t *hq;              // [S+B][3][I] h (routed slots, then shared tokens), as xq
+  uint8_t *hq;               // [S+B][3][I] h (routed slots, then shared tokens), as xq
   float *hsum;               // [S+B][I/64][2]
   float *d_shared;           // [B][H]
   float *partial;            // [S][H]

@@ -71,12 +71,12 @@ struct LayerWs {
   size_t partial;   // fp32 [B][K][hidden]  w * routed-expert output, per (token, slot)
   size_t groups;    // int32 [2 + 6 S], S = B*K: the number of distinct experts, the number of
                     // token blocks, and per token block {expert, number of slots, 4 slots} [6 S]
-  size_t xq;        // bf16 [B][3][hidden]     the input as three bf16 parts
-  size_t xsum;      // fp32 [B][hidden/64][2]  its per-group sums (of x, of hi + lo)
+  size_t xq;        // int8 [B][3][hidden]     the input in integer form: three digit planes
+  size_t xsum;      // fp32 [B][hidden/64][2]  per group: its factor f and the sum of x
   size_t xinv;      // fp32 [B]                its RMS factor
   size_t gdot;      // fp32 [B]                g . x before the RMS factor
-  size_t hq;        // bf16 [S + B][3][inter]  the SwiGLU outputs as three bf16 parts
-  size_t hsum;      // fp32 [S + B][inter/64][2] their per-group sums
+  size_t hq;        // int8 [S + B][3][inter]  the SwiGLU outputs in the same form
+  size_t hsum;      // fp32 [S + B][inter/64][2] per group: factor f and sum
   size_t total;
 };
 
@@ -99,11 +99,11 @@ inline LayerWs layer_ws(int B, int E, int K, int hidden, int inter) {
   const size_t S = (size_t)B * K;
   w.partial = take(B > 1 ? sizeof(float) * S * hidden : 0);
   w.groups = take(B > 1 ? sizeof(int32_t) * (6 * S + 2) : 0);
-  w.xq = take(B > 1 ? sizeof(uint16_t) * 3 * (size_t)B * hidden : 0);
+  w.xq = take(B > 1 ? 3 * (size_t)B * hidden : 0);
   w.xsum = take(B > 1 ? 2 * sizeof(float) * (size_t)B * (hidden / 64) : 0);
   w.xinv = take(B > 1 ? sizeof(float) * (size_t)B : 0);
   w.gdot = take(B > 1 ? sizeof(float) * (size_t)B : 0);
-  w.hq = take(B > 1 ? sizeof(uint16_t) * 3 * (S + B) * inter : 0);
+  w.hq = take(B > 1 ? 3 * (S + B) * inter : 0);
   w.hsum = take(B > 1 ? 2 * sizeof(float) * (S + B) * (inter / 64) : 0);
   w.total = o;
   return w;
