@@ -63,6 +63,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-verify", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true")
+    p.add_argument("--timeline", action="store_true",
+                   help="print device-clock stamps of a few layers' kernels inside the graph-captured stack (B=1) "
+                        "instead of timing")
     return p.parse_args()
 
 
@@ -96,6 +99,67 @@ def calibrate_copy():
     torch.cuda.synchronize()
     print(json.dumps({"calibration": "elementwise int32 bitwise_not, 1 GiB in, 1 GiB out",
                       "bytes_read": n, "bytes_written": n}), flush=True)
+
+
+def timeline(torch, np, qem, layers, c_layers, h_in, h0_all, ws, n_layers):
+    """Per-workgroup device-clock stamps (100 MHz) of the three kernels of a few layers,
+    each inside the graph-captured stack, summarised per kernel: when the workgroups
+    start, have their inputs in LDS, know the routing, and end."""
+    tr = torch.zeros((3, qem.TRACE_BLOCKS, qem.TRACE_SLOTS), dtype=torch.int64, device=h_in.device)
+    h_out = torch.empty_like(h_in)
+    picks = sorted({n_layers // 4, n_layers // 2, (3 * n_layers) // 4})
+    names = ("k_phase1 (router, x digits, gate)", "k_phase2 (routing, gate/up)", "k_phase3 (down, combine)")
+    print("device-clock stamps of one layer's kernels inside the graph-captured stack (B=1); "
+          "µs from the first router workgroup's start; min / median / p90 / max over workgroups", flush=True)
+    for lt in picks:
+        def call():
+            qem.fmoe_moe_stack_trace(layers, h_in, tr, lt, h_out=h_out, ws=ws, c_layers=c_layers)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            call()
+        for s in range(3):
+            h_in.copy_(h0_all[s % h0_all.shape[0]])
+            g.replay()
+        torch.cuda.synchronize()
+        tr.zero_()
+        h_in.copy_(h0_all[3 % h0_all.shape[0]])
+        g.replay()
+        torch.cuda.synchronize()
+        del g
+        t = tr.cpu().numpy()
+        rec = [t[k][t[k, :, 0] > 0] for k in range(3)]
+        t0 = rec[0][:, 0].min()
+        us = lambda v: (v - t0) / 100.0
+        q = lambda v: "/".join(f"{x:5.2f}" for x in np.percentile(us(v), [0, 50, 90, 100]))
+        print(f"layer {lt}:", flush=True)
+        for k in range(3):
+            r = rec[k]
+            if k == 0:
+                groups = [("router", r[r[:, 1] > 0]), ("x digits, gate", r[r[:, 1] == 0])]
+            elif k == 1:
+                groups = [("routed", r[r[:, 2] > 0]), ("shared", r[r[:, 2] == 0])]
+            else:
+                groups = [("all", r)]
+            for gname, gr in groups:
+                if len(gr) == 0:
+                    continue
+                line = f"  {names[k]:34s} {gname:14s} {len(gr):4d} wg  start {q(gr[:, 0])}"
+                if (gr[:, 1] > 0).all():
+                    line += f"  inputs {q(gr[:, 1])}"
+                if (gr[:, 2] > 0).all():
+                    line += f"  routing {q(gr[:, 2])}"
+                line += f"  end {q(gr[:, 3])}"
+                print(line, flush=True)
+        gaps = [us(rec[k + 1][:, 0].min()) - us(rec[k][:, 3].max()) for k in range(2)]
+        print(f"  last end -> next kernel's first start: k_phase1 -> k_phase2 {gaps[0]:.2f}, "
+              f"k_phase2 -> k_phase3 {gaps[1]:.2f}; first start -> last end of the layer "
+              f"{us(rec[2][:, 3].max()):.2f}", flush=True)
 
 
 def phase_bytes(phase, d_routed, eb, gub, E, H, I, K, bits):
@@ -224,6 +288,12 @@ def main():
         with torch.cuda.graph(graph):
             step_call()
         torch.cuda.synchronize()
+
+    if a.timeline:
+        if B != 1:
+            raise SystemExit("--timeline needs --batch 1")
+        timeline(torch, np, qem, layers, c_layers, h_in, h0_all, ws, n_layers)
+        return
 
     def run(s):
         h_in.copy_(h0_all[s])

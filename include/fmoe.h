@@ -221,6 +221,25 @@ fmoe_status fmoe_moe_stack(const fmoe_layer *layers, int n_layers, int n_tokens,
                            float *h_out, float *h_all, int32_t *topk_idx, float *topk_w, float eps,
                            void *ws, size_t ws_bytes, void *stream);
 
+/* Diagnostic form of fmoe_moe_stack for one token (no h_all or routing outputs): the
+ * three kernels of layer trace_layer stamp the device clock (100 MHz, the same
+ * counter in every workgroup) into trace, a device uint64 array
+ * [3][FMOE_TRACE_BLOCKS][FMOE_TRACE_SLOTS] owned and zeroed by the caller. Entry
+ * [k][b][s]: kernel k (0 router and shared-expert gate, 1 routing + routed and
+ * shared-expert gate/up, 2 routed and shared-expert down + combine), workgroup b,
+ * stamp s: 0 start; 1 its inputs in LDS (x; for kernel 1's routed workgroups also
+ * the routing; for kernel 2 the routing and h); 2 (kernel 1, routed workgroups) the
+ * routing known; 3 end of its first wavefront. Stamps not taken stay 0; workgroups
+ * from FMOE_TRACE_BLOCKS on are not recorded. Results equal fmoe_moe_stack's.
+ * FMOE_ERR_NULL if trace is NULL, FMOE_ERR_BATCH unless n_tokens == 1 and
+ * 0 <= trace_layer < n_layers, FMOE_ERR_ALIAS if trace overlaps ws; otherwise the
+ * arguments and errors of fmoe_moe_stack. */
+#define FMOE_TRACE_BLOCKS 4096
+#define FMOE_TRACE_SLOTS 8
+fmoe_status fmoe_moe_stack_trace(const fmoe_layer *layers, int n_layers, int n_tokens, const float *h0,
+                                 float *h_out, float eps, void *ws, size_t ws_bytes, uint64_t *trace,
+                                 int trace_layer, void *stream);
+
 /* Human-readable text of a status (static storage). */
 const char *fmoe_status_string(fmoe_status s);
 

@@ -85,6 +85,9 @@ _SIGS = {
     "fmoe_moe_stack": (ctypes.c_int, [ctypes.POINTER(fmoe_layer), ctypes.c_int, ctypes.c_int] +
                        [ctypes.c_void_p] * 5 + [ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t,
                                                 ctypes.c_void_p]),
+    "fmoe_moe_stack_trace": (ctypes.c_int, [ctypes.POINTER(fmoe_layer), ctypes.c_int, ctypes.c_int] +
+                             [ctypes.c_void_p] * 2 + [ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t,
+                                                      ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]),
     "fmoe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fmoe_version": (ctypes.c_int, []),
 }
@@ -371,6 +374,30 @@ def fmoe_moe_stack(layers: Sequence[Layer], h0: torch.Tensor, h_out: Optional[to
     nbytes = ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else need
     _ok(lib().fmoe_moe_stack(arr, len(arr), n_tokens, _ptr(h0), _ptr(h_out), _ptr(h_all), _ptr(topk_idx),
                              _ptr(topk_w), eps, _ptr(ws), nbytes, _stream(stream)), "fmoe_moe_stack")
+    return h_out
+
+
+TRACE_BLOCKS, TRACE_SLOTS = 4096, 8  # FMOE_TRACE_BLOCKS, FMOE_TRACE_SLOTS
+
+
+def fmoe_moe_stack_trace(layers: Sequence[Layer], h0: torch.Tensor, trace: torch.Tensor, trace_layer: int,
+                         h_out: Optional[torch.Tensor] = None, eps: float = 1e-6, ws=None, stream=None,
+                         c_layers=None) -> torch.Tensor:
+    """fmoe_moe_stack for one token with device-clock stamps of layer `trace_layer`'s
+    kernels in `trace` (int64 [3, TRACE_BLOCKS, TRACE_SLOTS] on the device, zeroed by the caller)."""
+    _dev_f32(h0, "h0")
+    if trace.dtype != torch.int64 or trace.numel() < 3 * TRACE_BLOCKS * TRACE_SLOTS or not trace.is_cuda:
+        raise ValueError("trace: int64 device tensor of 3 * TRACE_BLOCKS * TRACE_SLOTS entries")
+    n_tokens = h0.shape[0]
+    if h_out is None:
+        h_out = torch.empty_like(h0)
+    arr = c_layers if c_layers is not None else (fmoe_layer * len(layers))(*[L.c() for L in layers])
+    need = int(lib().fmoe_stack_workspace_bytes(ctypes.byref(arr[0]), n_tokens))
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=h0.device)
+    nbytes = ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else need
+    _ok(lib().fmoe_moe_stack_trace(arr, len(arr), n_tokens, _ptr(h0), _ptr(h_out), eps, _ptr(ws), nbytes,
+                                   _ptr(trace), trace_layer, _stream(stream)), "fmoe_moe_stack_trace")
     return h_out
 
 

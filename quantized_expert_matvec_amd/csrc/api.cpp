@@ -70,9 +70,10 @@ fmoe_status matvec_common(const fmoe_qmat *W, const float *x, float *y, void *st
 // Enqueue one layer for n_tokens tokens (arguments already validated): the
 // one-token kernels for a single token, the grouped kernels for several.
 // rms_eps >= 0: the layer input is rms_scale(x, rms_eps), computed inside the layer's kernels.
+// trace: device-clock stamps of the one-token kernels (layout in fmoe.h), or null.
 fmoe_status layer_enqueue(const fmoe_layer *L, int B, const float *x, float rms_eps, const float *residual,
                           float *out, int32_t *topk_idx, float *topk_w, uint8_t *ws, hipStream_t s,
-                          int phases = 7) {
+                          int phases = 7, uint64_t *trace = nullptr) {
   const LayerWs w = layer_ws(B, L->n_experts, L->top_k, L->hidden, L->inter);
   const int H = L->hidden, I = L->inter, E = L->n_experts, K = L->top_k;
   if (B > 1) {
@@ -137,6 +138,7 @@ fmoe_status layer_enqueue(const fmoe_layer *L, int B, const float *x, float rms_
     a.h_routed = (float *)(ws + w.h_routed) + (size_t)t * K * I;
     a.d_shared = (float *)(ws + w.d_shared) + (size_t)t * H;
     a.xdig = (uint32_t *)(ws + w.xdig);
+    a.trace = trace;
     if (launch_layer(a, s, phases) != hipSuccess) return FMOE_ERR_LAUNCH;
   }
   return FMOE_OK;
@@ -330,9 +332,12 @@ fmoe_status fmoe_rms_scale(const float *h, float *x, int n_tokens, int hidden, f
   return launch_rms(h, x, n_tokens, hidden, eps, as_stream(stream)) == hipSuccess ? FMOE_OK : FMOE_ERR_LAUNCH;
 }
 
-fmoe_status fmoe_moe_stack(const fmoe_layer *layers, int n_layers, int n_tokens, const float *h0, float *h_out,
-                           float *h_all, int32_t *topk_idx, float *topk_w, float eps, void *ws, size_t ws_bytes,
-                           void *stream) {
+static_assert(FMOE_TRACE_BLOCKS == kTraceBlocks && FMOE_TRACE_SLOTS == kTraceSlots, "the kernels' stamp layout");
+
+// fmoe_moe_stack, with the stamps of layer trace_layer's kernels in trace (null: none)
+static fmoe_status stack_enqueue(const fmoe_layer *layers, int n_layers, int n_tokens, const float *h0,
+                                 float *h_out, float *h_all, int32_t *topk_idx, float *topk_w, float eps, void *ws,
+                                 size_t ws_bytes, void *stream, uint64_t *trace, int trace_layer) {
   if (!layers) return FMOE_ERR_NULL;
   if (n_layers < 1) return FMOE_ERR_BATCH;
   for (int l = 0; l < n_layers; ++l) {
@@ -371,12 +376,32 @@ fmoe_status fmoe_moe_stack(const fmoe_layer *layers, int n_layers, int n_tokens,
     else
       nxt = ping[l & 1];
     fmoe_status st = layer_enqueue(&layers[l], B, cur, eps, cur, nxt, topk_idx ? topk_idx + (size_t)l * B * K : nullptr,
-                                   topk_w ? topk_w + (size_t)l * B * K : nullptr, w + sw.layer, s);
+                                   topk_w ? topk_w + (size_t)l * B * K : nullptr, w + sw.layer, s, 7,
+                                   l == trace_layer ? trace : nullptr);
     if (st != FMOE_OK) return st;
     cur = nxt;
   }
   if (h_all && hipMemcpyAsync(h_out, cur, hb, hipMemcpyDeviceToDevice, s) != hipSuccess) return FMOE_ERR_LAUNCH;
   return FMOE_OK;
+}
+
+fmoe_status fmoe_moe_stack(const fmoe_layer *layers, int n_layers, int n_tokens, const float *h0, float *h_out,
+                           float *h_all, int32_t *topk_idx, float *topk_w, float eps, void *ws, size_t ws_bytes,
+                           void *stream) {
+  return stack_enqueue(layers, n_layers, n_tokens, h0, h_out, h_all, topk_idx, topk_w, eps, ws, ws_bytes, stream,
+                       nullptr, -1);
+}
+
+fmoe_status fmoe_moe_stack_trace(const fmoe_layer *layers, int n_layers, int n_tokens, const float *h0,
+                                 float *h_out, float eps, void *ws, size_t ws_bytes, uint64_t *trace,
+                                 int trace_layer, void *stream) {
+  if (!trace) return FMOE_ERR_NULL;
+  if (n_tokens != 1 || trace_layer < 0 || trace_layer >= n_layers) return FMOE_ERR_BATCH;
+  if ((uintptr_t)trace % 8) return FMOE_ERR_ALIGN;
+  if (ws && overlap(trace, sizeof(uint64_t) * 3 * FMOE_TRACE_BLOCKS * FMOE_TRACE_SLOTS, ws, ws_bytes))
+    return FMOE_ERR_ALIAS;
+  return stack_enqueue(layers, n_layers, n_tokens, h0, h_out, nullptr, nullptr, nullptr, eps, ws, ws_bytes, stream,
+                       trace, trace_layer);
 }
 
 const char *fmoe_status_string(fmoe_status s) {

@@ -371,12 +371,13 @@ struct MfmaRows {
 
 // ------------------------------------------------------------------ g1
 
-// g1: workgroups [0, n_router_blocks): router rows against every token's x,
-// unscaled (each row split over router_split() wavefronts, two rows per
-// workgroup, so that 512 rows take 256 compute units). Workgroups
-// n_router_blocks + t: token t's x for the matrix cores (RMS factor xinv; per
+// g1: workgroup t < B: token t's x for the matrix cores (RMS factor xinv; per
 // group the three digit planes, the factor f and the sum of x) and its gate dot
-// product g . x (unscaled).
+// product g . x (unscaled); dispatched first, so that their x requests do not
+// queue behind a router workgroup's rows on the same compute unit. Workgroups
+// B + b: router rows against every token's x, unscaled (each row split over
+// router_split() wavefronts, two rows per workgroup, so that 512 rows take 256
+// compute units).
 constexpr int kG1Chunk = 4;  // tokens whose x is staged in LDS at a time
 template <int NGH>
 __host__ __device__ constexpr int g1_rows_per_block() {
@@ -398,9 +399,9 @@ __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
   const int lane = lane_id();
   const int wv = wave_in_block();
   const bool rms = a.rms_eps >= 0.f;
-  if ((int)blockIdx.x >= a.n_router_blocks) {
+  if ((int)blockIdx.x < a.B) {
     // ---- input preparation of token t, and its gate dot product
-    const int t = blockIdx.x - a.n_router_blocks;
+    const int t = blockIdx.x;
     const float *xt = a.x + (size_t)t * H;
     const float *gv = a.gvec ? a.gvec : a.x;  // (read but unused without a shared expert)
     constexpr int UNITS = NGH * 8;  // 8 consecutive columns each: unit u = columns 8u .. 8u + 7
@@ -472,7 +473,8 @@ __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
   // are written unscaled: the RMS factor of each token (xinv, from the
   // preparation workgroups) is applied by the routing.
   const int half = wv % SPLIT;
-  const int row = (int)blockIdx.x * RPB + wv / SPLIT;
+  const int rblk = (int)blockIdx.x - a.B;  // router workgroup
+  const int row = rblk * RPB + wv / SPLIT;
   const int rr = min(row, a.E - 1);
   const float4 *src = reinterpret_cast<const float4 *>(a.router + (size_t)rr * H) + 64 * NTW * half;
   float4 wr[NTW];
@@ -512,7 +514,7 @@ __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
     float d = dp[SPLIT * r][t];
 #pragma unroll
     for (int h = 1; h < SPLIT; ++h) d += dp[SPLIT * r + h][t];
-    const int rw = (int)blockIdx.x * RPB + r;
+    const int rw = rblk * RPB + r;
     if (rw < a.E) a.logits[(size_t)t * logit_stride(a.E) + rw] = d;
   }
 }

@@ -40,9 +40,11 @@ struct LayerArgs {
   float *d_shared;           // [H]
   uint32_t *xdig;            // [H/64][kDigStride] x in digit form (router kernel -> gate/up kernel)
   // optional per-workgroup timestamps (device, 100 MHz clock) for profiling:
-  // [phase][workgroup][8]; null in normal use
+  // [phase][kTraceBlocks workgroups][kTraceSlots]; null in normal use
   uint64_t *trace;
 };
+constexpr int kTraceSlots = 8;
+constexpr int kTraceBlocks = 4096;  // workgroups recorded per phase
 
 // One MoE layer for B > 1 tokens grouped by expert (device pointers).
 struct GroupArgs {

@@ -135,8 +135,6 @@ __device__ __forceinline__ void read_slice(const float *lds, int g, float scale,
 }
 
 // Profiling hook: thread 0 of a workgroup records the device clock at a point.
-constexpr int kTraceSlots = 8;
-constexpr int kTraceBlocks = 4096;  // workgroups recorded per phase
 __device__ __forceinline__ void trace_mark(uint64_t *tr, int slot) {
   if (tr && threadIdx.x == 0 && blockIdx.x < (unsigned)kTraceBlocks)
     tr[(size_t)blockIdx.x * kTraceSlots + slot] = __builtin_amdgcn_s_memrealtime();
@@ -458,7 +456,7 @@ struct Phase1Args {
   float *logits;
   float *sigma;
   uint32_t *xdig;     // [hidden/64][kDigStride] x in digit form
-  int n_router_blocks;
+  int n_prep_blocks;  // workgroups before the router's: x in digit form, then the gate
   uint64_t *trace;
 };
 
@@ -495,7 +493,7 @@ __device__ __forceinline__ void write_digits(const float *xl, int g, float inv, 
 // wavefronts of a workgroup (half h: lane l covers columns 4l + 256t + 0..3 for
 // t in [h NT/2, (h+1) NT/2)), so that the 8 MB of rows spread over every compute
 // unit (512 rows: one workgroup per compute unit); the halves' sums are added in
-// order. The workgroups after the router's write x in digit form for the gate/up
+// order. The workgroups before the router's write x in digit form for the gate/up
 // kernel, and the last of them computes the shared expert's gate sigmoid(g . x).
 template <int NGH>
 constexpr int router_split() {
@@ -516,16 +514,18 @@ __global__ __launch_bounds__(kBlock) void k_phase1(const Phase1Args a) {
   const bool rms = a.rms_eps >= 0.f;
   trace_mark(a.trace, 0);
   const int wv = wave_in_block();
-  if ((int)blockIdx.x >= a.n_router_blocks) {
-    // The workgroups after the router's: x in digit form, one 64-column group per
+  if ((int)blockIdx.x < a.n_prep_blocks) {
+    // The workgroups before the router's: x in digit form, one 64-column group per
     // wavefront, then one for the shared expert's gate sigma = sigmoid(g . x) --
-    // beside the router rows, off their path. (The gate vector's loads are
-    // unconditional, reading x where there is no gate.)
-    const int g = ((int)blockIdx.x - a.n_router_blocks) * kWavesPerBlock + wv;
-    const bool gate = a.gvec != nullptr && (int)blockIdx.x == a.n_router_blocks + (NGH + kWavesPerBlock - 1) / kWavesPerBlock;
+    // beside the router rows, off their path. Dispatched first, so that their x
+    // requests do not queue behind a router workgroup's rows on the same compute
+    // unit. (The second vector's loads are unconditional: the gate vector in the
+    // gate's workgroup, x again in the others.)
+    const int g = (int)blockIdx.x * kWavesPerBlock + wv;
+    const bool gate = a.gvec != nullptr && (int)blockIdx.x == (NGH + kWavesPerBlock - 1) / kWavesPerBlock;
     Staged<X4> xst, gst;
     stage_load(a.x, NGH * 16, xst);
-    stage_load(a.gvec ? a.gvec : a.x, NGH * 16, gst);
+    stage_load(gate ? a.gvec : a.x, NGH * 16, gst);
     if (rms)
       stage_store<X4, true>(xst, NGH * 16, xl, part);
     else
@@ -566,7 +566,7 @@ __global__ __launch_bounds__(kBlock) void k_phase1(const Phase1Args a) {
   }
   const int n_rows = a.E;
   const int half = wv % SPLIT;
-  const int row = blockIdx.x * (kWavesPerBlock / SPLIT) + wv / SPLIT;
+  const int row = ((int)blockIdx.x - a.n_prep_blocks) * (kWavesPerBlock / SPLIT) + wv / SPLIT;
   const int rr = min(row, n_rows - 1);
   const float *src = a.router + (size_t)rr * H + 256 * NTW * half;
   Staged<X4> xst;
@@ -975,12 +975,11 @@ struct Dispatch {
     p1.logits = L.logits;
     p1.sigma = L.sigma;
     p1.xdig = L.xdig;
-    p1.n_router_blocks = G.n1r;
+    p1.n_prep_blocks = (NGH + kWavesPerBlock - 1) / kWavesPerBlock + (has_shared ? 1 : 0);
     p1.trace = L.trace;
-    // after the router's workgroups: one per four 64-column groups of x (digit
+    // before the router's workgroups: one per four 64-column groups of x (digit
     // form), then one for the shared expert's gate
-    const int nd = (NGH + kWavesPerBlock - 1) / kWavesPerBlock + (has_shared ? 1 : 0);
-    hipLaunchKernelGGL((k_phase1<NGH>), dim3(G.n1r + nd), dim3(kBlock), 0, s, p1);
+    hipLaunchKernelGGL((k_phase1<NGH>), dim3(G.n1r + p1.n_prep_blocks), dim3(kBlock), 0, s, p1);
     return hipGetLastError();
   }
 

@@ -222,6 +222,23 @@ def test_stack_validation():
     assert L.fmoe_moe_stack(arr, 2, 1, None, OUT, None, None, None, 1e-6, WSL, need, None) == 1
 
 
+def test_stack_trace_validation():
+    L0 = lay()
+    arr = (qem.fmoe_layer * 2)(L0, L0)
+    need = L.fmoe_stack_workspace_bytes(ctypes.byref(L0), 1)
+    TR = A + (9 << 30)
+    call = lambda n_tokens=1, trace=TR, layer=1, ws_bytes=need, h0=X: L.fmoe_moe_stack_trace(
+        arr, 2, n_tokens, h0, OUT, 1e-6, WSL, ws_bytes, trace, layer, None)
+    assert call(trace=None) == 1
+    assert call(n_tokens=2) == 6
+    assert call(layer=2) == 6 and call(layer=-1) == 6
+    assert call(trace=TR + 4) == 3
+    assert call(trace=WSL + 256) == 9
+    # the stack's own checks still apply
+    assert call(ws_bytes=need - 1) == 7
+    assert call(h0=None) == 1
+
+
 def test_rms_validation():
     assert L.fmoe_rms_scale(None, B, 1, 4096, 1e-6, None) == 1
     assert L.fmoe_rms_scale(A, B, 0, 4096, 1e-6, None) == 6

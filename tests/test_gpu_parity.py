@@ -280,6 +280,30 @@ def test_stack_one_token_q2(device):
         h = ref
 
 
+def test_stack_trace_equals_stack(device):
+    """The stamped form of the stack gives fmoe_moe_stack's output bit for bit; every recorded
+    workgroup's stamps are ordered, and each kernel of the traced layer starts after the
+    previous one's workgroups end (within 0.5 µs of clock skew)."""
+    hidden, inter, n_exp, k, n_layers, bits = 1024, 256, 32, 4, 3, 4
+    layers = [host_layer(52, l, bits, n_exp, k, hidden, inter, device) for l in range(n_layers)]
+    h0 = to_dev(synth.activations(52, synth.T_H0, 1, 1, hidden), device)
+    ref = qem.fmoe_moe_stack(layers, h0)
+    tr = torch.zeros((3, qem.TRACE_BLOCKS, qem.TRACE_SLOTS), dtype=torch.int64, device=device)
+    out = qem.fmoe_moe_stack_trace(layers, h0, tr, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    t = tr.cpu().numpy()
+    rec = [t[kk][t[kk, :, 0] > 0] for kk in range(3)]
+    for r in rec:
+        assert len(r) > 0
+        assert (r[:, 3] >= r[:, 0]).all()
+        has = r[:, 1] > 0
+        assert has.any() and ((r[has, 1] >= r[has, 0]) & (r[has, 3] >= r[has, 1])).all()
+    assert (rec[1][:, 2] > 0).any()  # routed workgroups of the gate/up kernel
+    for kk in range(2):
+        assert rec[kk + 1][:, 0].min() + 50 >= rec[kk][:, 3].max()
+
+
 # --------------------------------------------------------------------------- grouped (B > 1)
 
 @pytest.mark.parametrize("bits", [4, 2])
