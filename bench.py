@@ -162,6 +162,62 @@ def timeline(torch, np, qem, layers, c_layers, h_in, h0_all, ws, n_layers):
               f"{us(rec[2][:, 3].max()):.2f}", flush=True)
 
 
+def read_ceiling(torch, qem, dev):
+    """The HBM read rate this GPU reaches (the library's streaming-read kernel over a
+    4 GiB buffer, 12 passes in a graph), and the time per launch of an empty kernel in a
+    graph of 180 (the floor of a kernel boundary)."""
+    free = torch.cuda.mem_get_info()[0]
+    nb = min(4 << 30, (free - (1 << 30)) // (1 << 20) * (1 << 20))
+    buf = torch.empty(nb, dtype=torch.uint8, device=dev)
+    out = torch.zeros(1, dtype=torch.int32, device=dev)
+    res = []
+    for calls, src in ((4, buf), (180, None)):
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            qem.fmoe_read_xor(src, out)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for _ in range(calls):
+                qem.fmoe_read_xor(src, out)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        res.append(e0.elapsed_time(e1) * 1000.0 / (3 * calls))  # µs per launch
+        del g
+    del buf
+    return ({"GBps": round(nb / (res[0] * 1e3), 1), "bytes": int(nb),
+             "kernel": "fmoe_read_xor (16-byte non-temporal loads, 8 in flight per thread)"}, round(res[1], 3))
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def versions(torch):
+    v = {"torch": torch.__version__, "hip": torch.version.hip,
+         "gpu": torch.cuda.get_device_properties(0).gcnArchName}
+    for key, path in (("rocm", "/opt/rocm/.info/version"), ("amdgpu_driver", "/sys/module/amdgpu/version")):
+        try:
+            v[key] = open(path).read().strip()
+        except OSError:
+            v[key] = None
+    return v
+
+
 def phase_bytes(phase, d_routed, eb, gub, E, H, I, K, bits):
     """Algorithmic bytes one launch of a layer kernel moves (B=1): the weights it must
     stream once plus its activation reads and writes."""
@@ -306,16 +362,21 @@ def main():
     for s in range(a.warmup):
         run(s)
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for s in range(a.warmup, steps):
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+    evs[0].record()
+    for j, s in enumerate(range(a.warmup, steps)):
         run(s)
-    ev1.record()
+        evs[j + 1].record()
     torch.cuda.synchronize()
-    ms_total = ev0.elapsed_time(ev1)
+    ms_total = evs[0].elapsed_time(evs[-1])
     ms_step = ms_total / a.steps
     us_layer = ms_step * 1000.0 / n_layers
+    per_step = np.array([evs[j].elapsed_time(evs[j + 1]) for j in range(a.steps)]) * 1000.0 / n_layers
+    spread = [round(float(v), 3) for v in np.percentile(per_step, [10, 50, 90])]
+
+    # ---- the measured read ceiling and the empty-kernel gap inside a graph
+    log("bench: streaming-read ceiling and empty-kernel gap")
+    ceiling, gap = read_ceiling(torch, qem, dev)
 
     # algorithmic bytes: the distinct experts each layer-step touches (replayed untimed)
     distinct = []
@@ -388,7 +449,12 @@ def main():
         log(f"bench: oracle on layer 0 ({budget:.0f} s budget)")
         t_layer, reps, t_total, (o_out, o_idx, o_w, _) = cpu_baseline(a, synth, oracle, R0, g0, h0, budget)
         if not a.no_cpu_baseline:
-            cpu = {"value": round(t_layer * 1e6, 1), "unit": "us/layer", "cores": oracle.get_threads(),
+            n_threads = oracle.get_threads()
+            oracle.set_threads(1)
+            t1, reps1, t_total1, _ = cpu_baseline(a, synth, oracle, R0, g0, h0, budget / 2)
+            oracle.set_threads(n_threads)
+            cpu = {"value": round(t_layer * 1e6, 1), "unit": "us/layer", "cores": n_threads,
+                   "value_1core": round(t1 * 1e6, 1), "cpu_model": cpu_model(),
                    "kind": "oracle",
                    "sample": f"fp64 oracle, one MoE layer (512-expert router, softmax top-{K}, {K} routed + shared "
                              f"SwiGLU experts, q{bits}) for one token, run {reps}x in {t_total:.1f} s; "
@@ -405,6 +471,14 @@ def main():
                       "max_rel": float(np.max(np.abs(d)) / np.max(np.abs(o_out))),
                       "l2_rel": float(np.linalg.norm(d) / np.linalg.norm(o_out))}
             parity["pass"] = bool(parity["routing_exact"] and parity["max_rel"] <= 2e-3 and parity["l2_rel"] <= 1e-4)
+            # near-ties: gaps among the oracle's top K+1 logits below the fp32 rounding
+            # allowance 1e-5 * sum_i |R_ei x_i| of the two logits
+            x0 = oracle.rms_scale(h0)
+            lg = oracle.router_logits(R0, x0)
+            tau = 1e-5 * np.abs(R0.astype(np.float64) * x0[None, :]).sum(axis=1)
+            order = np.argsort(-lg, kind="stable")
+            parity["near_ties"] = int(sum(lg[order[j]] - lg[order[j + 1]] < max(tau[order[j]], tau[order[j + 1]])
+                                          for j in range(K)))
 
     rec = {
         "metric": "µs per MoE layer (top-4 + shared, 4-bit, B=1) and weight GB/s vs HBM peak",
@@ -422,14 +496,20 @@ def main():
         "config": {"workload": f"moe_stack_q{bits}_B{B}", "layers": n_layers, "batch": B, "experts": E,
                    "top_k": K, "hidden": H, "inter": I, "group": 64, "graph": graph is not None,
                    "seed": a.seed},
+        "us_per_layer_p10_p50_p90": spread,
+        "kernels_per_layer": 3 if B == 1 else 4,
         "weight_GBps": round(weight_gbps, 1),
         "frac_hbm_peak": round(weight_gbps / HBM_PEAK_GBPS, 4),
+        "read_ceiling_GBps": ceiling,
+        "frac_read_ceiling": round(weight_gbps / ceiling["GBps"], 4),
+        "empty_kernel_gap_us": gap,
         "algorithmic_bytes_per_layer": int(w_bytes_layer + act_bytes_layer),
         "distinct_routed_experts_per_layer": round(d_mean, 3),
         "roofline": roofline,
         "kernels": kernels,
         "cpu_baseline": cpu,
         "parity": parity,
+        "versions": versions(torch),
     }
     print(json.dumps(rec, ensure_ascii=False), flush=True)
 

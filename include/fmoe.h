@@ -240,6 +240,17 @@ fmoe_status fmoe_moe_stack_trace(const fmoe_layer *layers, int n_layers, int n_t
                                  float *h_out, float eps, void *ws, size_t ws_bytes, uint64_t *trace,
                                  int trace_layer, void *stream);
 
+/* Measurement aid, not a step of the method: the HBM read rate this GPU reaches, to
+ * report beside the nominal peak. Streams the bytes bytes of buf (device, 16-B
+ * aligned, bytes a multiple of 16) with 16-byte non-temporal loads, several in flight
+ * per thread, and folds the XOR of all its 32-bit words into *out (device uint32,
+ * 4-B aligned): *out ^= w_0 ^ w_1 ^ ... (atomically, so calls accumulate). bytes == 0
+ * launches one workgroup that reads nothing (an empty kernel, for timing launch gaps)
+ * and leaves *out unchanged. FMOE_ERR_NULL if out is NULL, or buf is NULL with
+ * bytes > 0; FMOE_ERR_ALIGN for a misaligned buf or out or bytes not a multiple of 16;
+ * FMOE_ERR_ALIAS if out lies inside the buffer. */
+fmoe_status fmoe_read_xor(const void *buf, size_t bytes, uint32_t *out, void *stream);
+
 /* Human-readable text of a status (static storage). */
 const char *fmoe_status_string(fmoe_status s);
 

@@ -88,6 +88,7 @@ _SIGS = {
     "fmoe_moe_stack_trace": (ctypes.c_int, [ctypes.POINTER(fmoe_layer), ctypes.c_int, ctypes.c_int] +
                              [ctypes.c_void_p] * 2 + [ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t,
                                                       ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]),
+    "fmoe_read_xor": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
     "fmoe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fmoe_version": (ctypes.c_int, []),
 }
@@ -399,6 +400,15 @@ def fmoe_moe_stack_trace(layers: Sequence[Layer], h0: torch.Tensor, trace: torch
     _ok(lib().fmoe_moe_stack_trace(arr, len(arr), n_tokens, _ptr(h0), _ptr(h_out), eps, _ptr(ws), nbytes,
                                    _ptr(trace), trace_layer, _stream(stream)), "fmoe_moe_stack_trace")
     return h_out
+
+
+def fmoe_read_xor(buf: Optional[torch.Tensor], out: torch.Tensor, nbytes: Optional[int] = None,
+                  stream=None) -> None:
+    """out (int32 [1] on the device) ^= XOR of the 32-bit words of the first nbytes
+    (default: all) bytes of buf; buf None or nbytes 0: an empty kernel."""
+    if nbytes is None:
+        nbytes = 0 if buf is None else buf.numel() * buf.element_size()
+    _ok(lib().fmoe_read_xor(_ptr(buf), nbytes, _ptr(out), _stream(stream)), "fmoe_read_xor")
 
 
 def fmoe_status_string(status: int) -> str:

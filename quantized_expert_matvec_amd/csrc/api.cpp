@@ -404,6 +404,13 @@ fmoe_status fmoe_moe_stack_trace(const fmoe_layer *layers, int n_layers, int n_t
                        trace, trace_layer);
 }
 
+fmoe_status fmoe_read_xor(const void *buf, size_t bytes, uint32_t *out, void *stream) {
+  if (!out || (bytes > 0 && !buf)) return FMOE_ERR_NULL;
+  if (bytes % 16 || (bytes > 0 && !al16(buf)) || (uintptr_t)out % 4) return FMOE_ERR_ALIGN;
+  if (bytes > 0 && overlap(out, sizeof(uint32_t), buf, bytes)) return FMOE_ERR_ALIAS;
+  return launch_read_xor(buf, bytes, out, as_stream(stream)) == hipSuccess ? FMOE_OK : FMOE_ERR_LAUNCH;
+}
+
 const char *fmoe_status_string(fmoe_status s) {
   switch (s) {
     case FMOE_OK: return "ok";

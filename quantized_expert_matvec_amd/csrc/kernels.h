@@ -90,6 +90,8 @@ hipError_t launch_layer(const LayerArgs &a, hipStream_t s, int phases = 7);
 
 // x_t = h_t / sqrt(mean(h_t^2) + eps) for B tokens of width H.
 hipError_t launch_rms(const float *h, float *x, int B, int H, float eps, hipStream_t s);
+// *out ^= XOR of the 32-bit words of buf (bytes a multiple of 16); bytes == 0: an empty kernel
+hipError_t launch_read_xor(const void *buf, size_t bytes, uint32_t *out, hipStream_t s);
 
 // Device packer: record r of the matrix goes to blob + rec_offset + r * rec_stride.
 hipError_t launch_pack_matrix(int bits, int rows, int cols, const uint8_t *codes, const uint16_t *scale,

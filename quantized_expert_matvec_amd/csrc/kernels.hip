@@ -45,6 +45,41 @@ __global__ __launch_bounds__(kBlock) void k_rms(const float *__restrict__ h, flo
   for (int i = threadIdx.x; i < H; i += kBlock) xt[i] = ht[i] / r;
 }
 
+// Streaming read: the XOR of every 32-bit word of n16 16-byte units, folded into
+// *out with one atomic per workgroup. Grid-stride over the units with
+// kReadUnroll independent non-temporal loads in flight per thread; an empty
+// buffer makes an empty kernel.
+constexpr int kReadUnroll = 8;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(kBlock) void k_read_xor(const u32x4 *__restrict__ p, size_t n16,
+                                                      uint32_t *__restrict__ out) {
+  __shared__ uint32_t part[kBlock / kWave];
+  const size_t stride = (size_t)gridDim.x * kBlock;
+  size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + (kReadUnroll - 1) * stride < n16; i += kReadUnroll * stride) {
+    u32x4 v[kReadUnroll];
+#pragma unroll
+    for (int k = 0; k < kReadUnroll; ++k) v[k] = __builtin_nontemporal_load(p + i + k * stride);
+#pragma unroll
+    for (int k = 0; k < kReadUnroll; ++k) acc ^= (v[k].x ^ v[k].y) ^ (v[k].z ^ v[k].w);
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 v = __builtin_nontemporal_load(p + i);
+    acc ^= (v.x ^ v.y) ^ (v.z ^ v.w);
+  }
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) acc ^= (uint32_t)__shfl_xor((int)acc, m);
+  if (lane_id() == 0) part[threadIdx.x / kWave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+#pragma unroll
+    for (int w = 0; w < kBlock / kWave; ++w) t ^= part[w];
+    if (t) atomicXor(out, t);
+  }
+}
+
 // Device packer: one thread per (row, group).
 template <int BITS>
 __global__ __launch_bounds__(kBlock) void k_pack(int rows, int ng, const uint8_t *__restrict__ codes,
@@ -111,6 +146,16 @@ hipError_t launch_qmatvec(int bits, const uint8_t *blob, int rows, int cols, con
 hipError_t launch_expert_gateup(int bits, const uint8_t *gu, int hidden, int inter, const float *x, float *h,
                                 hipStream_t s) {
   return bits == 4 ? dev::gateup_b<4>(gu, hidden, inter, x, h, s) : dev::gateup_b<2>(gu, hidden, inter, x, h, s);
+}
+
+hipError_t launch_read_xor(const void *buf, size_t bytes, uint32_t *out, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  const size_t per = (size_t)kBlock * dev::kReadUnroll;
+  const size_t want = (n16 + per - 1) / per;
+  const int grid = (int)(want < 1 ? 1 : want > 2048 ? 2048 : want);
+  hipLaunchKernelGGL(dev::k_read_xor, dim3(grid), dim3(kBlock), 0, s, reinterpret_cast<const dev::u32x4 *>(buf), n16,
+                     out);
+  return hipGetLastError();
 }
 
 hipError_t launch_layer(const LayerArgs &a, hipStream_t s, int phases) {

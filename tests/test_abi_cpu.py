@@ -239,6 +239,16 @@ def test_stack_trace_validation():
     assert call(h0=None) == 1
 
 
+def test_read_xor_validation():
+    OUTW = A + (10 << 30)
+    assert L.fmoe_read_xor(A, 64, None, None) == 1
+    assert L.fmoe_read_xor(None, 64, OUTW, None) == 1
+    assert L.fmoe_read_xor(A, 8, OUTW, None) == 3
+    assert L.fmoe_read_xor(A + 4, 64, OUTW, None) == 3
+    assert L.fmoe_read_xor(A, 64, OUTW + 2, None) == 3
+    assert L.fmoe_read_xor(A, 64, A + 32, None) == 9
+
+
 def test_rms_validation():
     assert L.fmoe_rms_scale(None, B, 1, 4096, 1e-6, None) == 1
     assert L.fmoe_rms_scale(A, B, 0, 4096, 1e-6, None) == 6

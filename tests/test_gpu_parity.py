@@ -304,6 +304,25 @@ def test_stack_trace_equals_stack(device):
         assert rec[kk + 1][:, 0].min() + 50 >= rec[kk][:, 3].max()
 
 
+def test_read_xor(device):
+    """The streaming-read measurement kernel: the XOR of a buffer's 32-bit words (several
+    grid-stride rounds and a ragged tail) equals numpy's; calls accumulate; an empty call
+    changes nothing."""
+    rng = np.random.default_rng(7)
+    words = rng.integers(0, 2 ** 32, size=4 * (2048 * 256 * 8 * 2 + 12345), dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(words.view(np.int32)).to(device)
+    out = torch.zeros(1, dtype=torch.int32, device=device)
+    qem.fmoe_read_xor(buf, out)
+    torch.cuda.synchronize()
+    want = int(np.bitwise_xor.reduce(words))
+    assert int(out.cpu().numpy().view(np.uint32)[0]) == want
+    qem.fmoe_read_xor(None, out)  # empty kernel
+    qem.fmoe_read_xor(buf, out, nbytes=16 * 1000)
+    torch.cuda.synchronize()
+    want ^= int(np.bitwise_xor.reduce(words[:4 * 1000]))
+    assert int(out.cpu().numpy().view(np.uint32)[0]) == want
+
+
 # --------------------------------------------------------------------------- grouped (B > 1)
 
 @pytest.mark.parametrize("bits", [4, 2])
