@@ -371,13 +371,12 @@ struct MfmaRows {
 
 // ------------------------------------------------------------------ g1
 
-// g1: workgroup t < B: token t's x for the matrix cores (RMS factor xinv; per
+// g1: workgroups [0, n_router_blocks): router rows against every token's x,
+// unscaled (each row split over router_split() wavefronts, two rows per
+// workgroup, so that 512 rows take 256 compute units). Workgroups
+// n_router_blocks + t: token t's x for the matrix cores (RMS factor xinv; per
 // group the three digit planes, the factor f and the sum of x) and its gate dot
-// product g . x (unscaled); dispatched first, so that their x requests do not
-// queue behind a router workgroup's rows on the same compute unit. Workgroups
-// B + b: router rows against every token's x, unscaled (each row split over
-// router_split() wavefronts, two rows per workgroup, so that 512 rows take 256
-// compute units).
+// product g . x (unscaled).
 constexpr int kG1Chunk = 4;  // tokens whose x is staged in LDS at a time
 template <int NGH>
 __host__ __device__ constexpr int g1_rows_per_block() {
@@ -399,9 +398,9 @@ __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
   const int lane = lane_id();
   const int wv = wave_in_block();
   const bool rms = a.rms_eps >= 0.f;
-  if ((int)blockIdx.x < a.B) {
+  if ((int)blockIdx.x >= a.n_router_blocks) {
     // ---- input preparation of token t, and its gate dot product
-    const int t = blockIdx.x;
+    const int t = blockIdx.x - a.n_router_blocks;
     const float *xt = a.x + (size_t)t * H;
     const float *gv = a.gvec ? a.gvec : a.x;  // (read but unused without a shared expert)
     constexpr int UNITS = NGH * 8;  // 8 consecutive columns each: unit u = columns 8u .. 8u + 7
@@ -473,8 +472,7 @@ __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
   // are written unscaled: the RMS factor of each token (xinv, from the
   // preparation workgroups) is applied by the routing.
   const int half = wv % SPLIT;
-  const int rblk = (int)blockIdx.x - a.B;  // router workgroup
-  const int row = rblk * RPB + wv / SPLIT;
+  const int row = (int)blockIdx.x * RPB + wv / SPLIT;
   const int rr = min(row, a.E - 1);
   const float4 *src = reinterpret_cast<const float4 *>(a.router + (size_t)rr * H) + 64 * NTW * half;
   float4 wr[NTW];
@@ -514,7 +512,7 @@ __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
     float d = dp[SPLIT * r][t];
 #pragma unroll
     for (int h = 1; h < SPLIT; ++h) d += dp[SPLIT * r + h][t];
-    const int rw = rblk * RPB + r;
+    const int rw = (int)blockIdx.x * RPB + r;
     if (rw < a.E) a.logits[(size_t)t * logit_stride(a.E) + rw] = d;
   }
 }
@@ -851,14 +849,15 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
   }
 }
 
-// g3: down of 256 rows (part rb: two tiles of 128, each wavefront 16 rows of
-// each) of one item's expert for the item's tokens / slots, from one staging of
-// h: shared: d_shared[t][row] = sigma[t] * row . h_shared[t]; routed:
+// g3: down of 128 TILES rows (part rb: TILES tiles of 128, each wavefront 16
+// rows of each) of one item's expert for the item's tokens / slots, from one
+// staging of h: shared: d_shared[t][row] = sigma[t] * row . h_shared[t]; routed:
 // partial[slot][row] = w[slot] * row . h[slot]. Workgroups: the shared
 // expert's token blocks, then one per possible routed token block (those past
-// G[1] exit at once), each times the H / 256 row parts.
-constexpr int kG3Tiles = 2;
-template <int BITS, int NGI>
+// G[1] exit at once), each times the H / (128 TILES) row parts. Two tiles per
+// staging halve the staging overhead when there are many token blocks; with
+// few, one tile per workgroup spreads the rows over more compute units.
+template <int BITS, int NGI, int kG3Tiles>
 __global__ __launch_bounds__(kGThreads) void k_g3(const GroupArgs a) {
   constexpr size_t RB = (size_t)NGI * gbytes<BITS>();
   __shared__ __attribute__((aligned(16))) uint8_t xl[MfmaRows<BITS, NGI, kG3Tiles>::XL + 16];
@@ -973,8 +972,10 @@ struct GroupDispatch {
         hipLaunchKernelGGL((k_g2<BITS, NGH, NGI, false>), grid, dim3(kGThreads), 0, s, a);
     }
     if (phases & 4) {
-      hipLaunchKernelGGL((k_g3<BITS, NGI>), dim3((shb + S) * (a.H / (128 * kG3Tiles))), dim3(kGThreads), 0, s,
-                         a);
+      if (a.B <= kTokBlock)
+        hipLaunchKernelGGL((k_g3<BITS, NGI, 1>), dim3((shb + S) * (a.H / 128)), dim3(kGThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((k_g3<BITS, NGI, 2>), dim3((shb + S) * (a.H / 256)), dim3(kGThreads), 0, s, a);
       hipLaunchKernelGGL(k_g4<BITS>, dim3(n4), dim3(kBlock), 0, s, a);
     }
     return hipGetLastError();
