@@ -168,6 +168,8 @@ def read_ceiling(torch, qem, dev):
     graph of 180 (the floor of a kernel boundary)."""
     free = torch.cuda.mem_get_info()[0]
     nb = min(4 << 30, (free - (1 << 30)) // (1 << 20) * (1 << 20))
+    if nb < (256 << 20):
+        return None, None  # no room for a buffer well beyond the caches
     buf = torch.empty(nb, dtype=torch.uint8, device=dev)
     out = torch.zeros(1, dtype=torch.int32, device=dev)
     res = []
@@ -501,7 +503,7 @@ def main():
         "weight_GBps": round(weight_gbps, 1),
         "frac_hbm_peak": round(weight_gbps / HBM_PEAK_GBPS, 4),
         "read_ceiling_GBps": ceiling,
-        "frac_read_ceiling": round(weight_gbps / ceiling["GBps"], 4),
+        "frac_read_ceiling": round(weight_gbps / ceiling["GBps"], 4) if ceiling else None,
         "empty_kernel_gap_us": gap,
         "algorithmic_bytes_per_layer": int(w_bytes_layer + act_bytes_layer),
         "distinct_routed_experts_per_layer": round(d_mean, 3),
