@@ -63,6 +63,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-verify", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true")
+    p.add_argument("--forms", action="store_true",
+                   help="time the standalone 1024 x 4096 matvec in each form of the per-weight dequant arithmetic "
+                        "(q4 and q2) instead of the stack")
     p.add_argument("--timeline", action="store_true",
                    help="print device-clock stamps of a few layers' kernels inside the graph-captured stack (B=1) "
                         "instead of timing")
@@ -160,6 +163,84 @@ def timeline(torch, np, qem, layers, c_layers, h_in, h0_all, ws, n_layers):
         print(f"  last end -> next kernel's first start: k_phase1 -> k_phase2 {gaps[0]:.2f}, "
               f"k_phase2 -> k_phase3 {gaps[1]:.2f}; first start -> last end of the layer "
               f"{us(rec[2][:, 3].max()):.2f}", flush=True)
+
+
+FORM_NAMES = {0: "naive (c*s+b)*x", 1: "recast fma(c, s*x, b*x)", 2: "group-factored s*sum(c*x)+b*sum(x)",
+              3: "table of c*s+b in LDS"}
+
+
+def forms(a):
+    """The standalone dequantized matvec W [rows][4096] (rows 1024, and 16384 where the
+    per-weight arithmetic weighs more than the launch) in each form of the per-weight
+    arithmetic (fmoe_qmatvec_form) and the library's own call, q4 and q2: a graph of one
+    launch per copy over enough independent copies of W and x (≥ 450 MB) that they
+    exceed the 256 MB Infinity Cache, replayed 5 times. Each form's output of copy 0 is compared with
+    the library call's (the tests check every form against the oracle)."""
+    import numpy as np
+    import torch
+
+    import synth
+    import quantized_expert_matvec_amd as qem
+    dev = torch.device("cuda:0")
+    cols = 4096
+    st = torch.cuda.current_stream().cuda_stream
+    recs = []
+    for rows, bits in ((1024, 4), (1024, 2), (16384, 4), (16384, 2)):
+        nb = qem.fmoe_qmat_bytes(bits, rows, cols)
+        stride = (nb + 255) // 256 * 256
+        copies = max(8, -(-(450 << 20) // stride))
+        bank = torch.empty(copies * stride, dtype=torch.uint8, device=dev)
+        codes = torch.empty(rows * cols, dtype=torch.uint8, device=dev)
+        scale = torch.empty(rows * cols // 64, dtype=torch.int16, device=dev)
+        bias = torch.empty(rows * cols // 64, dtype=torch.int16, device=dev)
+        for k in range(copies):
+            synth.dev_qmat(a.seed, synth.STANDALONE_LAYER, k, synth.T_MATRIX, bits, rows, cols, codes, scale, bias, st)
+            qem.fmoe_pack_qmat_device(bits, rows, cols, codes, scale, bias, bank[k * stride:(k + 1) * stride])
+        xs = torch.from_numpy(np.stack([synth.activations(a.seed, synth.T_X, k, 1, cols)[0]
+                                        for k in range(copies)])).to(dev)
+        ys = torch.empty((copies, rows), dtype=torch.float32, device=dev)
+        cq = [qem.QMat(bank[k * stride:(k + 1) * stride], rows, cols, bits).c() for k in range(copies)]
+        lib_fn = qem.lib().fmoe_q4_matvec if bits == 4 else qem.lib().fmoe_q2_matvec
+        variants = [(None, f"library call fmoe_q{bits}_matvec")] + [(f, FORM_NAMES[f]) for f in range(4)]
+        ref = None
+        for form, name in variants:
+            def call():
+                for k in range(copies):
+                    if form is None:
+                        lib_fn(cq[k], xs[k].data_ptr(), ys[k].data_ptr(), torch.cuda.current_stream().cuda_stream)
+                    else:
+                        qem.lib().fmoe_qmatvec_form(cq[k], xs[k].data_ptr(), ys[k].data_ptr(), form,
+                                                    torch.cuda.current_stream().cuda_stream)
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                call()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            y0 = ys[0].cpu().numpy().astype(np.float64)
+            if ref is None:
+                ref = y0
+            max_rel = float(np.max(np.abs(y0 - ref)) / np.max(np.abs(ref)))
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                call()
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(5):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1000.0 / (5 * copies)
+            algo = nb + cols * 4 + rows * 4
+            recs.append({"rows": rows, "cols": cols, "bits": bits, "form": form, "name": name,
+                         "us_per_matvec": round(us, 3),
+                         "GBps": round(algo / (us * 1e3), 1), "algorithmic_bytes": algo, "copies": copies,
+                         "max_rel_vs_library_call": max_rel})
+            print(json.dumps(recs[-1]), flush=True)
+            del g
+        del bank, xs, ys
 
 
 def read_ceiling(torch, qem, dev):
@@ -283,6 +364,9 @@ def main():
         sys.exit(2)
     if a.calibrate_copy:
         calibrate_copy()
+        return
+    if a.forms:
+        forms(a)
         return
     import numpy as np
     import torch

@@ -168,6 +168,20 @@ fmoe_status fmoe_q4_matvec(const fmoe_qmat *W, const float *x, float *y, void *s
  * FMOE_ERR_BITS unless W->bits == 2. */
 fmoe_status fmoe_q2_matvec(const fmoe_qmat *W, const float *x, float *y, void *stream);
 
+/* Comparison aid: y = W x for a matrix of either bit width (W->bits), with the
+ * per-weight arithmetic in one of four forms, c the code, s and b its group's scale
+ * and bias: form 0 naive, w = c*s + b then w*x accumulated; form 1 the recast
+ * fma(c, s*x, b*x) per weight ([P1] "2. Kernel de desquantizacion optimizado con
+ * FMA", [P2] "FMA-optimierter Dequant-Kernel"); form 2 group-factored,
+ * s * sum c*x + b * sum x per 64-column group (the form of fmoe_q4_matvec and every
+ * other call); form 3 a per-(row, group) table of c*s + b in LDS read per weight
+ * (the GPU dequant lookup table of [P1] "Lo que descartaron"). One row iteration per
+ * wavefront. Results agree with fmoe_q4_matvec / fmoe_q2_matvec up to fp32
+ * rounding (summation order and form differ). Arguments and errors as
+ * fmoe_q4_matvec, without the bit-width restriction; FMOE_ERR_SHAPE if form is
+ * outside 0..3. */
+fmoe_status fmoe_qmatvec_form(const fmoe_qmat *W, const float *x, float *y, int form, void *stream);
+
 /* One SwiGLU expert on one token: out = down( silu(gate x) * (up x) ), silu(z) = z/(1+e^-z)
  * ([P2] "Metal-Compute-Shader": fused SwiGLU activation). x: device fp32 [hidden];
  * out: device fp32 [hidden], must not overlap x; ws: device, >= fmoe_expert_workspace_bytes. */

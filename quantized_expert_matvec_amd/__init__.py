@@ -74,6 +74,8 @@ _SIGS = {
     "fmoe_pack_expert_device": (ctypes.c_int, [ctypes.c_int] * 4 + [ctypes.c_void_p] * 5),
     "fmoe_q4_matvec": (ctypes.c_int, [ctypes.POINTER(fmoe_qmat)] + [ctypes.c_void_p] * 3),
     "fmoe_q2_matvec": (ctypes.c_int, [ctypes.POINTER(fmoe_qmat)] + [ctypes.c_void_p] * 3),
+    "fmoe_qmatvec_form": (ctypes.c_int, [ctypes.POINTER(fmoe_qmat), ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_int, ctypes.c_void_p]),
     "fmoe_expert_ffn": (ctypes.c_int, [ctypes.POINTER(fmoe_expert), ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "fmoe_moe_layer": (ctypes.c_int, [ctypes.POINTER(fmoe_layer), ctypes.c_int] + [ctypes.c_void_p] * 6 +
@@ -303,6 +305,18 @@ def fmoe_q2_matvec(W: QMat, x: torch.Tensor, y: Optional[torch.Tensor] = None, s
     if y is None:
         y = torch.empty(W.rows, dtype=torch.float32, device=x.device)
     _ok(lib().fmoe_q2_matvec(ctypes.byref(W.c()), _ptr(x), _ptr(y), _stream(stream)), "fmoe_q2_matvec")
+    return y
+
+
+def fmoe_qmatvec_form(W: QMat, x: torch.Tensor, form: int, y: Optional[torch.Tensor] = None,
+                      stream=None, c_qmat=None) -> torch.Tensor:
+    """y = W x with the per-weight arithmetic in form 0 (naive), 1 (fma recast),
+    2 (group-factored) or 3 (table in LDS); either bit width."""
+    _dev_f32(x, "x")
+    if y is None:
+        y = torch.empty(W.rows, dtype=torch.float32, device=x.device)
+    cq = c_qmat if c_qmat is not None else W.c()
+    _ok(lib().fmoe_qmatvec_form(ctypes.byref(cq), _ptr(x), _ptr(y), form, _stream(stream)), "fmoe_qmatvec_form")
     return y
 
 

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include "../../include/fmoe.h"
+#include "forms.h"
 #include "kernels.h"
 #include "layout.h"
 #include "pack.h"
@@ -402,6 +403,18 @@ fmoe_status fmoe_moe_stack_trace(const fmoe_layer *layers, int n_layers, int n_t
     return FMOE_ERR_ALIAS;
   return stack_enqueue(layers, n_layers, n_tokens, h0, h_out, nullptr, nullptr, nullptr, eps, ws, ws_bytes, stream,
                        trace, trace_layer);
+}
+
+fmoe_status fmoe_qmatvec_form(const fmoe_qmat *W, const float *x, float *y, int form, void *stream) {
+  if (!W) return FMOE_ERR_NULL;
+  if (form < 0 || form >= kForms) return FMOE_ERR_SHAPE;
+  fmoe_status st = check_qmat(W, W->bits);
+  if (st != FMOE_OK) return st;
+  if (!x || !y) return FMOE_ERR_NULL;
+  if (!al16(x) || !al16(y)) return FMOE_ERR_ALIGN;
+  if (overlap(x, sizeof(float) * (size_t)W->cols, y, sizeof(float) * (size_t)W->rows)) return FMOE_ERR_ALIAS;
+  hipError_t e = launch_qmatvec_form(W->bits, form, (const uint8_t *)W->blob, W->rows, W->cols, x, y, as_stream(stream));
+  return e == hipSuccess ? FMOE_OK : FMOE_ERR_LAUNCH;
 }
 
 fmoe_status fmoe_read_xor(const void *buf, size_t bytes, uint32_t *out, void *stream) {

@@ -152,6 +152,13 @@ def qm(blob=A, rows=1024, cols=4096, bits=4, group=64):
     (lambda: L.fmoe_q4_matvec(qm(blob=A + 16), B, C, None), 3),
     (lambda: L.fmoe_q4_matvec(qm(), B + 4, C, None), 3),
     (lambda: L.fmoe_q4_matvec(qm(), B, B + 64, None), 9),
+    (lambda: L.fmoe_qmatvec_form(qm(), B, C, 4, None), 2),
+    (lambda: L.fmoe_qmatvec_form(qm(), B, C, -1, None), 2),
+    (lambda: L.fmoe_qmatvec_form(None, B, C, 0, None), 1),
+    (lambda: L.fmoe_qmatvec_form(qm(bits=3), B, C, 0, None), 4),
+    (lambda: L.fmoe_qmatvec_form(qm(cols=1000), B, C, 1, None), 2),
+    (lambda: L.fmoe_qmatvec_form(qm(), B + 4, C, 2, None), 3),
+    (lambda: L.fmoe_qmatvec_form(qm(bits=2), B, B + 64, 3, None), 9),
 ])
 def test_matvec_validation(call, status):
     assert call() == status

@@ -36,6 +36,21 @@ def test_matvec_vs_oracle(device, bits, rows, cols):
     assert_close(y.cpu().numpy(), oracle.qmatvec(q, x), f"q{bits} {rows}x{cols}")
 
 
+@pytest.mark.parametrize("form", [0, 1, 2, 3])
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("rows,cols", [(1024, 4096), (37, 512), (5, 256), (5000, 4096), (20000, 4096)])
+def test_matvec_forms_vs_oracle(device, form, bits, rows, cols):
+    """Each form of the per-weight arithmetic (naive, fma recast, group-factored, table)
+    against the oracle's dequantize-then-multiply, at one, two and four rows per
+    wavefront."""
+    q = synth.qmat(synth.SEED, synth.STANDALONE_LAYER, rows, synth.T_MATRIX, bits, rows, cols)
+    W = host_qmat(bits, q, device)
+    x = _x(synth.SEED, rows + cols, cols)[0]
+    y = qem.fmoe_qmatvec_form(W, to_dev(x, device), form)
+    torch.cuda.synchronize()
+    assert_close(y.cpu().numpy(), oracle.qmatvec(q, x), f"form {form} q{bits} {rows}x{cols}")
+
+
 @pytest.mark.parametrize("bits", [4, 2])
 def test_matvec_one_hot_extracts_columns_exactly(device, bits):
     """x = e_j: y = code[:, j]*scale + bias, exactly (fp32 holds it); checks the packed layout."""
