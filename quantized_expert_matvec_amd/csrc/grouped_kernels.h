@@ -227,17 +227,47 @@ struct MfmaRows {
     }
   }
 
+  // An item's staging data in registers: its vectors' group factors and sums
+  // (one float2 per thread) and its digit planes (one batch covers kTokBlock
+  // tokens), with their LDS destinations.
+  struct XAhead {
+    uint4 xv[kBatch];
+    int xdst[kBatch];
+    float2 sv;
+    int sdst;
+  };
+  static_assert(kBatch * kGThreads >= kParts * kTokBlock * NG * 4, "one batch stages an item");
+  // request the staging data of an item of T tokens whose vector indices are in tv
+  __device__ __forceinline__ static void stage_request(const uint8_t *__restrict__ xq_base,
+                                                       const float *__restrict__ xs_base, const int *tv, int T,
+                                                       XAhead &ah) {
+    const int e = min((int)threadIdx.x, T * NG - 1);
+    const int u = e / NG, gl = e - u * NG;
+    ah.sv = reinterpret_cast<const float2 *>(xs_base)[(size_t)tv[u] * NG + gl];
+    ah.sdst = (int)threadIdx.x < T * NG ? u * NG + gl : kTokBlock * NG;
+    load_batch(xq_base, tv, kParts * T * NG * 4, threadIdx.x, ah.xv, ah.xdst);
+  }
+
   // rec0: record of the wavefront's first row of its first tile (the NTILE tiles
   // of 16 rows lie tile_stride bytes apart); wl: its LDS region; tokv: an LDS
   // table of kTokBlock vector indices, which fill(u) (run by thread u < T first)
   // writes; after() runs on every thread right after x is requested, to request
   // what the caller's epilogue needs; tile_done(tile) runs on every thread as
   // each tile's stream ends, with its rows in y.
-  template <bool PRE, typename Fill, typename After, typename TileDone>
+  // AHEAD (a persistent caller, x staged per item): *have says that ah holds this
+  // item's staging data already; filln(u) (thread u < Tn) writes the next item's
+  // vector indices into tokn, and halfway through the last round of chunks (whose
+  // slots then hold no more requests) the next item's staging data is requested
+  // into ah -- unconditionally, this item's again when Tn == 0 (unused then) -- so
+  // that it arrives while this item's stream ends; *have = Tn > 0.
+  template <bool PRE, bool AHEAD = false, typename Fill, typename After, typename TileDone,
+            typename FillN = void (*)(int)>
   __device__ __forceinline__ void run(const uint8_t *__restrict__ rec0, size_t tile_stride,
                                       const uint8_t *__restrict__ xq_base, const float *__restrict__ xs_base, int T,
                                       int *tokv, Fill fill, After after, TileDone tile_done, uint8_t *xl,
-                                      float2 *xsl, uint8_t *wl) {
+                                      float2 *xsl, uint8_t *wl, XAhead *ah = nullptr, bool *have = nullptr,
+                                      int Tn = 0, int *tokn = nullptr, FillN filln = nullptr) {
+    static_assert(!(PRE && AHEAD), "a staged batch needs no staging ahead");
     const int lane = lane_id();
     const int q = lane >> 4;  // k-block of the A / B operands; token of D
     const int i = lane & 15;  // A row (4 token + part) / weight row of B and D
@@ -245,7 +275,10 @@ struct MfmaRows {
     offsets();
     // per-token tables (tokv, ...) from values the caller requested earlier
     if ((int)threadIdx.x < T) fill((int)threadIdx.x);
-    __syncthreads();  // tokv is written; earlier reads of xl / xsl are done
+    if constexpr (AHEAD) {
+      if ((int)threadIdx.x < Tn) filln((int)threadIdx.x);
+    }
+    __syncthreads();  // tokv (tokn) written; earlier reads of xl / xsl are done
     Chunk ring[DEPTH];
     int aoff, xoff;
     if constexpr (PRE) {
@@ -269,18 +302,9 @@ struct MfmaRows {
       // batches (loads of a batch before its stores); stores are unconditional
       // (lanes past the end write a spare slot: xl at XL, xsl at kTokBlock * NG),
       // so that the optimiser keeps a batch's loads together.
-      const int units = kParts * T * NG * 4;
-      float2 sv;
-      int sdst;
-      {
-        const int e = min((int)threadIdx.x, T * NG - 1);
-        const int u = e / NG, gl = e - u * NG;
-        sv = reinterpret_cast<const float2 *>(xs_base)[(size_t)tokv[u] * NG + gl];
-        sdst = (int)threadIdx.x < T * NG ? u * NG + gl : kTokBlock * NG;
-      }
-      uint4 xv[kBatch];
-      int xdst[kBatch];
-      load_batch(xq_base, tokv, units, threadIdx.x, xv, xdst);
+      XAhead own;
+      XAhead &st = AHEAD ? *ah : own;
+      if (!AHEAD || !*have) stage_request(xq_base, xs_base, tokv, T, st);  // (uniform)
       after();
       // narrow rows stage little x: then the whole prologue goes out at once
       constexpr int EARLY = NG <= 16 ? DEPTH : 1;
@@ -289,14 +313,14 @@ struct MfmaRows {
         load_chunk(rec0, tile_stride, d, ring[d]);
         asm volatile("" ::: "memory");
       }
-      xsl[sdst] = sv;
+      {
+        const float2 v = st.sv;  // (through locals: a direct struct copy kept st in scratch memory)
+        xsl[st.sdst] = v;
+      }
 #pragma unroll
-      for (int k = 0; k < kBatch; ++k) *reinterpret_cast<uint4 *>(xl + xdst[k]) = xv[k];
-      for (int e0 = threadIdx.x + kBatch * kGThreads; e0 < units; e0 += kBatch * kGThreads) {
-        load_batch(xq_base, tokv, units, e0, xv, xdst);
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int k = 0; k < kBatch; ++k) *reinterpret_cast<uint4 *>(xl + xdst[k]) = xv[k];
+      for (int k = 0; k < kBatch; ++k) {
+        const uint4 v = st.xv[k];
+        *reinterpret_cast<uint4 *>(xl + st.xdst[k]) = v;
       }
       __syncthreads();
 #pragma unroll
@@ -365,7 +389,16 @@ struct MfmaRows {
       for (int d = 0; d < DEPTH; ++d) step(std::true_type{}, cb + d, ring[d]);
     }
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) step(std::false_type{}, NCT - DEPTH + d, ring[d]);
+    for (int d = 0; d < DEPTH; ++d) {
+      step(std::false_type{}, NCT - DEPTH + d, ring[d]);
+      if constexpr (AHEAD) {
+        if (d == (DEPTH - 1) / 2) {
+          stage_request(xq_base, xs_base, Tn > 0 ? tokn : tokv, Tn > 0 ? Tn : T, *ah);
+          asm volatile("" ::: "memory");
+          *have = Tn > 0;
+        }
+      }
+    }
   }
 };
 
@@ -710,7 +743,7 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
   __shared__ float2 hpart[kGWaves][kTokBlock];
   __shared__ __attribute__((aligned(16))) uint8_t wlds[kGWaves][kWaveLds];
   __shared__ int slotl[kMaxSlots], blk[kBlkInts * kMaxSlots];
-  __shared__ int tokv[kTokBlock], hvl[kTokBlock];
+  __shared__ int tokv[kTokBlock], hvl[kTokBlock], tokn[kTokBlock];
   static_assert(sizeof(RouteLds) <= sizeof(xl), "routing scratch fits the staging buffer");
   const bool sh = a.shared != nullptr;
   const int S = a.B * a.K;
@@ -756,6 +789,11 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
     }
     for (int e = st; e < a.B * NGH; e += nst) xsl[e] = reinterpret_cast<const float2 *>(a.xsum)[e];
   }
+  // (items staged one by one) the next item's x is requested during this item's
+  // last chunks, when its tokens are known: any next shared item, a routed one
+  // once the routing is derived
+  typename MR::XAhead ahead;
+  bool have = false;
   for (int item = blockIdx.x; item < max_items; item += gridDim.x) {
     GroupItem it;
     int gi;
@@ -792,9 +830,29 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
     };
     float tinv;  // RMS factor of the token of this lane's D rows
     auto after = [&]() { tinv = a.xinv[tokv[min(qq, T - 1)]]; };
+    // the next item of this workgroup: its token count (0: not known yet, or none)
+    // and where its tokens come from
+    int Tn = 0, nq0 = 0;
+    bool nsh = false;
+    if constexpr (!PRE) {
+      const int nitem = item + (int)gridDim.x;
+      if (nitem < sh_items) {
+        nsh = true;
+        nq0 = kTokBlock * (nitem / NGI);
+        Tn = min(kTokBlock, a.B - nq0);
+      } else if (nitem < max_items && NB >= 0) {
+        const int kbn = (nitem - sh_items) / NGI;
+        if (kbn < NB) {
+          nq0 = kBlkInts * kbn + 2;
+          Tn = __builtin_amdgcn_readfirstlane(blk[kBlkInts * kbn + 1]);
+        }
+      }
+    }
+    auto filln = [&](int u) { tokn[u] = nsh ? nq0 + u : blk[nq0 + u] / a.K; };
     float y = 0.f;
     MR M;
-    M.template run<PRE>(rec0, 0, a.xq, a.xsum, T, tokv, fill, after, [&](int) { y = M.y; }, xl, xsl, wlds[wv]);
+    M.template run<PRE, !PRE>(rec0, 0, a.xq, a.xsum, T, tokv, fill, after, [&](int) { y = M.y; }, xl, xsl,
+                              wlds[wv], &ahead, &have, Tn, tokn, filln);
     // h = silu(gate) * up: gate rows are even, up rows odd (adjacent lanes); the
     // item's 64 pairs are one whole group of h (pair 8 wv + n / 2)
     float hv = 0.f;
