@@ -1,6 +1,10 @@
 // kernels_forms.hip -- the standalone dequantized matvec y = W x in four forms of
-// the per-weight arithmetic, to compare them on this GPU. With c_j the code of
-// column j of a 64-column group, s and b the group's scale and bias:
+// the per-weight arithmetic, to compare them on this GPU. Pages cited:
+//   [P1] "397B MoE en MacBook: Motor Flash-MoE a 4,4 t/s" (aibit.im)
+//   [P2] "Flash-MoE: Ausfuehren eines 397B-Parameter-Qwen-Modells auf dem MacBook
+//        Pro mit reinem C/Metal" (openclawradar.com)
+// With c_j the code of column j of a 64-column group, s and b the group's scale
+// and bias:
 //   0 naive:     w_j = c_j s + b, then acc += w_j x_j (two fused multiply-adds);
 //   1 recast:    acc += fma(c_j, s x_j, b x_j), the per-weight form of
 //                [P1] "2. Kernel de desquantización optimizado con FMA" and
