@@ -381,15 +381,18 @@ def test_grouped_equals_one_token_routing(device):
         assert_close(og[t].cpu().numpy(), singles[t][0].cpu().numpy(), f"grouped vs single token {t}")
 
 
-def test_grouped_full_size_B16(device):
-    """The batched decode workload's layer: 16 tokens, 512 experts + shared, hidden 4096,
-    inter 1024, q4, generated and packed on the device; every token against the oracle."""
-    hidden, inter, n_exp, k, B = 4096, 1024, 512, 4, 16
-    print("grouped full size B=16", flush=True)
+@pytest.mark.parametrize("B", [4, 16])
+def test_grouped_full_size(device, B):
+    """The batched decode workload's layer: 4 or 16 tokens (x staged once per workgroup and
+    one down tile per workgroup at 4; staged per item, ahead, and two tiles at 16), 512
+    experts + shared, hidden 4096, inter 1024, q4, generated and packed on the device;
+    every token against the oracle."""
+    hidden, inter, n_exp, k = 4096, 1024, 512, 4
+    print(f"grouped full size B={B}", flush=True)
     L = device_layer(synth.SEED, 1, 4, n_exp, k, hidden, inter, device)
     OL = OracleLayer(synth.SEED, 1, 4, n_exp, k, hidden, inter)
-    X = _x(synth.SEED, 2016, hidden, B)
-    ties = _check_layer(device, OL, L, X, X, "full B=16")
+    X = _x(synth.SEED, 2016 + B, hidden, B)
+    ties = _check_layer(device, OL, L, X, X, f"full B={B}")
     print(f"  near-ties: {ties}", flush=True)
     del L
     torch.cuda.empty_cache()
