@@ -381,18 +381,19 @@ def test_grouped_equals_one_token_routing(device):
         assert_close(og[t].cpu().numpy(), singles[t][0].cpu().numpy(), f"grouped vs single token {t}")
 
 
+@pytest.mark.parametrize("bits", [4, 2])
 @pytest.mark.parametrize("B", [4, 16])
-def test_grouped_full_size(device, B):
+def test_grouped_full_size(device, B, bits):
     """The batched decode workload's layer: 4 or 16 tokens (x staged once per workgroup and
     one down tile per workgroup at 4; staged per item, ahead, and two tiles at 16), 512
-    experts + shared, hidden 4096, inter 1024, q4, generated and packed on the device;
-    every token against the oracle."""
+    experts + shared, hidden 4096, inter 1024, q4 and q2, generated and packed on the
+    device; every token against the oracle."""
     hidden, inter, n_exp, k = 4096, 1024, 512, 4
-    print(f"grouped full size B={B}", flush=True)
-    L = device_layer(synth.SEED, 1, 4, n_exp, k, hidden, inter, device)
-    OL = OracleLayer(synth.SEED, 1, 4, n_exp, k, hidden, inter)
+    print(f"grouped full size B={B} q{bits}", flush=True)
+    L = device_layer(synth.SEED, 1, bits, n_exp, k, hidden, inter, device)
+    OL = OracleLayer(synth.SEED, 1, bits, n_exp, k, hidden, inter)
     X = _x(synth.SEED, 2016 + B, hidden, B)
-    ties = _check_layer(device, OL, L, X, X, f"full B={B}")
+    ties = _check_layer(device, OL, L, X, X, f"full B={B} q{bits}")
     print(f"  near-ties: {ties}", flush=True)
     del L
     torch.cuda.empty_cache()
