@@ -432,6 +432,32 @@ def test_stack_vs_oracle(device, B):
             h = ref
 
 
+@pytest.mark.parametrize("B", [1, 4])
+def test_stack_full_size(device, B):
+    """Two full-size q4 layers (512 experts + shared, hidden 4096, inter 1024, generated and
+    packed on the device) as a stack, RMS scaling folded into each layer's kernels, every
+    layer's output and routing against the oracle's own chain."""
+    hidden, inter, n_exp, k, n_layers = 4096, 1024, 512, 4, 2
+    print(f"stack full size B={B}", flush=True)
+    layers = [device_layer(synth.SEED, 10 + l, 4, n_exp, k, hidden, inter, device) for l in range(n_layers)]
+    OLs = [OracleLayer(synth.SEED, 10 + l, 4, n_exp, k, hidden, inter) for l in range(n_layers)]
+    h0 = synth.activations(synth.SEED, synth.T_H0, 100 + B, B, hidden)
+    h_all = torch.empty((n_layers, B, hidden), dtype=torch.float32, device=device)
+    idx = torch.empty((n_layers, B, k), dtype=torch.int32, device=device)
+    qem.fmoe_moe_stack(layers, to_dev(h0, device), h_all=h_all, topk_idx=idx)
+    torch.cuda.synchronize()
+    ha, gi = h_all.cpu().numpy(), idx.cpu().numpy()
+    for t in range(B):
+        h = h0[t].astype(np.float64)
+        for l in range(n_layers):
+            ref, ri, rw, logits = OLs[l].forward(oracle.rms_scale(h), h)
+            assert list(gi[l, t]) == list(ri), (l, t)
+            assert_close(ha[l, t], ref, f"full stack B={B} token {t} layer {l}")
+            h = ref
+    del layers
+    torch.cuda.empty_cache()
+
+
 # --------------------------------------------------------------------------- routing edge cases
 
 def _steered_router(seed, n_exp, hidden, x0, rows):
