@@ -199,7 +199,8 @@ def _one_token(device, OL, L, X, RES, what):
 
 @pytest.mark.parametrize("bits", [4, 2])
 @pytest.mark.parametrize("hidden,inter,k,n_exp", [(1024, 512, 4, 64), (256, 256, 1, 64), (512, 1024, 2, 32),
-                                                  (2048, 256, 3, 32), (4096, 256, 8, 16), (1024, 4096, 4, 8)])
+                                                  (2048, 256, 3, 32), (4096, 256, 8, 16), (1024, 4096, 4, 8),
+                                                  (1024, 4096, 8, 16)])
 def test_one_token_layer_vs_oracle(device, bits, hidden, inter, k, n_exp):
     """The one-token kernels (router + digit form of x, routing + gate/up, down + combine)
     over the supported widths, every top_k class of the down kernel and both code widths."""
