@@ -194,8 +194,10 @@ fmoe_status fmoe_expert_ffn(const fmoe_expert *E, const float *x, float *out, vo
  *   out_t = residual_t + sum_j w_j E_{T_j}(x_t) + sigmoid(shared_gate . x_t) E_shared(x_t)
  * ([P2] "Pipeline-Leistung", "Technische Implementierung", "Metal-Compute-Shader").
  * x, residual, out: device fp32 [n_tokens][hidden]; out may equal residual (in-place
- * residual update) but must not overlap x or ws. topk_idx (int32) and topk_w (fp32):
- * device [n_tokens][top_k] or NULL. ws: device, >= fmoe_workspace_bytes(L, n_tokens).
+ * residual update) but must not overlap it otherwise, nor overlap x or ws. topk_idx
+ * (int32) and topk_w (fp32): device [n_tokens][top_k] or NULL; neither may overlap the
+ * other, x, residual, out or ws. ws: device, >= fmoe_workspace_bytes(L, n_tokens).
+ * FMOE_ERR_ALIAS for any overlap named here.
  * With n_tokens > 1 the tokens are grouped by expert: the router, the shared expert and
  * each distinct chosen expert are read from HBM once per call and applied to every token
  * that uses them (results equal the one-token definition above, per token). */
@@ -229,7 +231,8 @@ fmoe_status fmoe_rms_scale(const float *h, float *x, int n_tokens, int hidden, f
  *   h_0 = h0;  for l: x_l = rms_scale(h_l, eps); h_{l+1} = moe_layer(layers[l], x_l, residual = h_l)
  * h0, h_out: device fp32 [n_tokens][hidden] (h_out may equal h0). h_all: device fp32
  * [n_layers][n_tokens][hidden] receiving every h_{l+1}, or NULL. topk_idx / topk_w: device
- * [n_layers][n_tokens][top_k], or NULL. Every layer must share hidden, inter, bits, group,
+ * [n_layers][n_tokens][top_k], or NULL. None of h0 (h_out), h_all, topk_idx, topk_w and ws
+ * may overlap another (FMOE_ERR_ALIAS), except h_out == h0. Every layer must share hidden, inter, bits, group,
  * top_k and n_experts with layers[0]. ws >= fmoe_stack_workspace_bytes(&layers[0], n_tokens). */
 fmoe_status fmoe_moe_stack(const fmoe_layer *layers, int n_layers, int n_tokens, const float *h0,
                            float *h_out, float *h_all, int32_t *topk_idx, float *topk_w, float eps,

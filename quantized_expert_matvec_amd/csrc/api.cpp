@@ -317,7 +317,9 @@ fmoe_status fmoe_moe_layer_phases(const fmoe_layer *L, int n_tokens, const float
   const size_t kb = sizeof(float) * (size_t)n_tokens * L->top_k;
   if (overlap(out, ab, x, ab) || overlap(out, ab, ws, need) || overlap(x, ab, ws, need) ||
       overlap(residual, ab, ws, need) || overlap(topk_idx, kb, ws, need) || overlap(topk_w, kb, ws, need) ||
-      overlap(topk_idx, kb, out, ab) || overlap(topk_w, kb, out, ab) || overlap(topk_idx, kb, topk_w, kb))
+      overlap(topk_idx, kb, out, ab) || overlap(topk_w, kb, out, ab) || overlap(topk_idx, kb, topk_w, kb) ||
+      (residual != out && overlap(residual, ab, out, ab)) || overlap(topk_idx, kb, residual, ab) ||
+      overlap(topk_w, kb, residual, ab) || overlap(topk_idx, kb, x, ab) || overlap(topk_w, kb, x, ab))
     return FMOE_ERR_ALIAS;
   return layer_enqueue(L, n_tokens, x, -1.f, residual, out, topk_idx, topk_w, (uint8_t *)ws, as_stream(stream),
                        phases);
@@ -360,7 +362,9 @@ static fmoe_status stack_enqueue(const fmoe_layer *layers, int n_layers, int n_t
   const size_t kb = sizeof(float) * (size_t)n_layers * B * K;
   if (overlap(h0, hb, ws, need) || overlap(h_out, hb, ws, need) || overlap(h_all, hb * n_layers, ws, need) ||
       overlap(h_all, hb * n_layers, h0, hb) || overlap(h_all, hb * n_layers, h_out, hb) ||
-      overlap(topk_idx, kb, ws, need) || overlap(topk_w, kb, ws, need) || overlap(topk_idx, kb, topk_w, kb))
+      overlap(topk_idx, kb, ws, need) || overlap(topk_w, kb, ws, need) || overlap(topk_idx, kb, topk_w, kb) ||
+      overlap(topk_idx, kb, h0, hb) || overlap(topk_idx, kb, h_out, hb) || overlap(topk_idx, kb, h_all, hb * n_layers) ||
+      overlap(topk_w, kb, h0, hb) || overlap(topk_w, kb, h_out, hb) || overlap(topk_w, kb, h_all, hb * n_layers))
     return FMOE_ERR_ALIAS;
   const StackWs sw = stack_ws(B, L0->n_experts, K, H, L0->inter);
   uint8_t *w = (uint8_t *)ws;

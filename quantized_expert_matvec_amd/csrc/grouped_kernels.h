@@ -876,6 +876,10 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
       m = max(m, dpp_i<0x140, 0xF>(m, 0));
       if (n == 0 && qq < T) hpart[wv][qq] = make_float2(r, __int_as_float(m));
     }
+    // the h vector indices this thread stores to, read before the barrier: after it,
+    // wavefront 0 may already be filling hvl with the next item's
+    const int hv_lane = hvl[min(qq, T - 1)];
+    const int hv_thr = hvl[min((int)threadIdx.x, T - 1)];
     __syncthreads();
     // h of this lane in integer form (its token's group shift), and per token the
     // group's factor and sum
@@ -887,7 +891,7 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
       const int k = group_shift(__int_as_float(mb));
       if ((n & 1) == 0 && qq < T) {
         const uint32_t d = digits3(hv, k);
-        uint8_t *dst = a.hq + (size_t)(kParts * hvl[qq]) * a.I + 64 * gi + 8 * wv + (n >> 1);
+        uint8_t *dst = a.hq + (size_t)(kParts * hv_lane) * a.I + 64 * gi + 8 * wv + (n >> 1);
 #pragma unroll
         for (int p = 0; p < kParts; ++p) dst[(size_t)p * a.I] = (uint8_t)(d >> (8 * p));
       }
@@ -902,7 +906,7 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
         mb = max(mb, __float_as_int(hpart[v][u].y));
       }
       const float amax = __int_as_float(mb);
-      reinterpret_cast<float2 *>(a.hsum)[(size_t)hvl[u] * NGI + gi] = make_float2(group_factor(amax, group_shift(amax)), sum);
+      reinterpret_cast<float2 *>(a.hsum)[(size_t)hv_thr * NGI + gi] = make_float2(group_factor(amax, group_shift(amax)), sum);
     }
   }
 }

@@ -217,6 +217,38 @@ def test_layer_validation():
     # NaN-free pointer checks pass through to a launch only when everything is valid; not exercised here
 
 
+def test_layer_alias_validation():
+    L0 = lay()
+    need = L.fmoe_workspace_bytes(ctypes.byref(L0), 2)
+    call = lambda x=X, r=RES, o=OUT, i=None, w=None: L.fmoe_moe_layer(
+        ctypes.byref(L0), 2, x, r, o, i, w, WSL, need, None)
+    IW = A + (11 << 30)
+    assert call(o=RES + 16) == 9                       # out partly overlaps the residual
+    assert call(r=OUT - 16) == 9
+    assert call(i=RES + 64) == 9                       # routing outputs inside the residual
+    assert call(w=RES + 64) == 9
+    assert call(i=X + 64) == 9                         # ... inside x
+    assert call(w=X) == 9
+    assert call(i=OUT + 64) == 9                       # ... inside out
+    assert call(i=IW, w=IW + 16) == 9                  # idx [2][4] and w overlap
+    assert call(i=WSL + 256) == 9                      # ... inside the workspace
+
+
+def test_stack_alias_validation():
+    L0 = lay()
+    arr = (qem.fmoe_layer * 2)(L0, L0)
+    need = L.fmoe_stack_workspace_bytes(ctypes.byref(L0), 1)
+    HA, IW = A + (11 << 30), A + (12 << 30)
+    call = lambda h0=X, ho=OUT, ha=None, i=None, w=None: L.fmoe_moe_stack(
+        arr, 2, 1, h0, ho, ha, i, w, 1e-6, WSL, need, None)
+    assert call(i=X + 64) == 9                         # routing outputs inside h0
+    assert call(w=OUT) == 9                            # ... inside h_out
+    assert call(ha=HA, i=HA + 4096 * 4) == 9           # ... inside h_all (second layer's rows)
+    assert call(ha=HA, w=HA) == 9
+    assert call(i=IW, w=IW + 16) == 9
+    assert call(ha=HA, h0=HA + 64) == 9                # h_all overlaps h0
+
+
 def test_stack_validation():
     L0 = lay()
     arr = (qem.fmoe_layer * 2)(L0, lay(inter=512))
@@ -261,3 +293,4 @@ def test_rms_validation():
     assert L.fmoe_rms_scale(A, B, 0, 4096, 1e-6, None) == 6
     assert L.fmoe_rms_scale(A, B, 1, 0, 1e-6, None) == 2
     assert L.fmoe_rms_scale(A, A + 64, 1, 4096, 1e-6, None) == 9
+
