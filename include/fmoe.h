@@ -24,8 +24,9 @@
  * blobs and workspaces must be 256-byte aligned.
  *
  * Ownership. The caller allocates and frees everything: blobs, activations and
- * workspaces. The library keeps no device state and never allocates or frees
- * device memory. Blobs are read-only during a call.
+ * workspaces. The library never allocates or frees device memory; its only
+ * device state is the static workspace of fmoe_moe_layer_noalloc. Blobs are
+ * read-only during a call.
  *
  * Asynchrony. A device entry point validates its arguments on the host, enqueues
  * its kernels on `stream` (a hipStream_t; NULL means the null stream) and
@@ -218,6 +219,21 @@ fmoe_status fmoe_moe_layer(const fmoe_layer *L, int n_tokens, const float *x, co
 fmoe_status fmoe_moe_layer_phases(const fmoe_layer *L, int n_tokens, const float *x, const float *residual,
                                   float *out, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
                                   int phases, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): fmoe_moe_layer with its
+ * workspace in a static device array that the library holds on every GPU it runs
+ * on, FMOE_NOALLOC_SCRATCH_BYTES (4 MiB) per GPU, kept until the process ends,
+ * instead of a caller's ws. The call allocates and frees nothing. Every call on one
+ * GPU shares that GPU's array, so calls that may overlap on one GPU (other streams,
+ * other threads) race and give undefined results; calls on one stream are ordered.
+ * FMOE_ERR_WORKSPACE if fmoe_workspace_bytes(L, n_tokens) exceeds the array (at
+ * hidden 4096, inter 1024, 512 experts and top_k 4: above 32 tokens);
+ * FMOE_ERR_LAUNCH if the array's device address cannot be looked up; otherwise the
+ * arguments, results and errors of fmoe_moe_layer. */
+#define FMOE_NOALLOC_SCRATCH_BYTES (4u << 20)
+fmoe_status fmoe_moe_layer_noalloc(const fmoe_layer *L, int n_tokens, const float *x, const float *residual,
+                                   float *out, int32_t *topk_idx, float *topk_w, void *stream);
 
 /* RMS scaling without a learned weight, two stages (sum of squares, then apply)
  * ([P2] "Metal-Compute-Shader": RMS normalization, two-stage):

@@ -82,6 +82,7 @@ _SIGS = {
                        [ctypes.c_size_t, ctypes.c_void_p]),
     "fmoe_moe_layer_phases": (ctypes.c_int, [ctypes.POINTER(fmoe_layer), ctypes.c_int] + [ctypes.c_void_p] * 6 +
                               [ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]),
+    "fmoe_moe_layer_noalloc": (ctypes.c_int, [ctypes.POINTER(fmoe_layer), ctypes.c_int] + [ctypes.c_void_p] * 6),
     "fmoe_rms_scale": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_float, ctypes.c_void_p]),
     "fmoe_moe_stack": (ctypes.c_int, [ctypes.POINTER(fmoe_layer), ctypes.c_int, ctypes.c_int] +
@@ -361,6 +362,23 @@ def fmoe_moe_layer_phases(L: Layer, x: torch.Tensor, residual: torch.Tensor, out
     nbytes = ws.numel() * ws.element_size()
     _ok(lib().fmoe_moe_layer_phases(ctypes.byref(cl), n_tokens, _ptr(x), _ptr(residual), _ptr(out), _ptr(topk_idx),
                                     _ptr(topk_w), _ptr(ws), nbytes, phases, _stream(stream)), "fmoe_moe_layer_phases")
+
+
+NOALLOC_SCRATCH_BYTES = 4 << 20  # FMOE_NOALLOC_SCRATCH_BYTES
+
+
+def fmoe_moe_layer_noalloc(L: Layer, x: torch.Tensor, residual: torch.Tensor, out: torch.Tensor,
+                           topk_idx: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """fmoe_moe_layer with the library's static per-GPU workspace: allocates nothing, so
+    `out` must be given. Calls that may overlap on one GPU race."""
+    _dev_f32(x, "x")
+    _dev_f32(residual, "residual")
+    _dev_f32(out, "out")
+    n_tokens = x.shape[0] if x.dim() == 2 else 1
+    _ok(lib().fmoe_moe_layer_noalloc(ctypes.byref(L.c()), n_tokens, _ptr(x), _ptr(residual), _ptr(out),
+                                     _ptr(topk_idx), _ptr(topk_w), _stream(stream)), "fmoe_moe_layer_noalloc")
+    return out
 
 
 def fmoe_rms_scale(h: torch.Tensor, x: Optional[torch.Tensor] = None, eps: float = 1e-6,

@@ -325,6 +325,20 @@ fmoe_status fmoe_moe_layer_phases(const fmoe_layer *L, int n_tokens, const float
                        phases);
 }
 
+fmoe_status fmoe_moe_layer_noalloc(const fmoe_layer *L, int n_tokens, const float *x, const float *residual,
+                                   float *out, int32_t *topk_idx, float *topk_w, void *stream) {
+  fmoe_status st = check_layer(L);
+  if (st != FMOE_OK) return st;
+  if (!x || !residual || !out) return FMOE_ERR_NULL;
+  if (n_tokens < 1 || n_tokens > kMaxTokens) return FMOE_ERR_BATCH;
+  const size_t need = fmoe_workspace_bytes(L, n_tokens);
+  if (need > kScratchBytes) return FMOE_ERR_WORKSPACE;
+  void *ws = nullptr;
+  if (scratch_device_ptr(&ws) != hipSuccess) return FMOE_ERR_LAUNCH;
+  // the full validation of fmoe_moe_layer, with the static workspace as ws
+  return fmoe_moe_layer_phases(L, n_tokens, x, residual, out, topk_idx, topk_w, ws, kScratchBytes, 7, stream);
+}
+
 fmoe_status fmoe_rms_scale(const float *h, float *x, int n_tokens, int hidden, float eps, void *stream) {
   if (!h || !x) return FMOE_ERR_NULL;
   if (n_tokens < 1 || n_tokens > kMaxTokens) return FMOE_ERR_BATCH;
@@ -335,6 +349,7 @@ fmoe_status fmoe_rms_scale(const float *h, float *x, int n_tokens, int hidden, f
   return launch_rms(h, x, n_tokens, hidden, eps, as_stream(stream)) == hipSuccess ? FMOE_OK : FMOE_ERR_LAUNCH;
 }
 
+static_assert(FMOE_NOALLOC_SCRATCH_BYTES == kScratchBytes, "the static workspace size");
 static_assert(FMOE_TRACE_BLOCKS == kTraceBlocks && FMOE_TRACE_SLOTS == kTraceSlots, "the kernels' stamp layout");
 
 // fmoe_moe_stack, with the stamps of layer trace_layer's kernels in trace (null: none)

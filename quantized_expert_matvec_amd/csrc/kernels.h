@@ -93,6 +93,10 @@ hipError_t launch_rms(const float *h, float *x, int B, int H, float eps, hipStre
 // *out ^= XOR of the 32-bit words of buf (bytes a multiple of 16); bytes == 0: an empty kernel
 hipError_t launch_read_xor(const void *buf, size_t bytes, uint32_t *out, hipStream_t s);
 
+// Device address of the current device's static workspace (kScratchBytes bytes,
+// scratch.hip), looked up once per device.
+hipError_t scratch_device_ptr(void **out);
+
 // Device packer: record r of the matrix goes to blob + rec_offset + r * rec_stride.
 hipError_t launch_pack_matrix(int bits, int rows, int cols, const uint8_t *codes, const uint16_t *scale,
                               const uint16_t *bias, uint8_t *blob, size_t rec_stride, size_t rec_offset,

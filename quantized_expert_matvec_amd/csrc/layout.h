@@ -22,6 +22,7 @@ constexpr int kMaxTopK = 8;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTokens = 64;
 constexpr int kDigStride = 52;  // u32 words per 64-column group of x in digit form
+constexpr size_t kScratchBytes = (size_t)4 << 20;  // static workspace of fmoe_moe_layer_noalloc (per GPU)
 
 inline bool bits_ok(int bits) { return bits == 2 || bits == 4; }
 inline bool cols_ok(int cols) {

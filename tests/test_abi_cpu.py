@@ -294,3 +294,16 @@ def test_rms_validation():
     assert L.fmoe_rms_scale(A, B, 1, 0, 1e-6, None) == 2
     assert L.fmoe_rms_scale(A, A + 64, 1, 4096, 1e-6, None) == 9
 
+
+def test_noalloc_validation():
+    """The static-workspace variant validates like fmoe_moe_layer and rejects batches whose
+    workspace exceeds its array before touching the device."""
+    L0 = lay()
+    call = lambda Lx=L0, n=1, x=X, r=RES, o=OUT: L.fmoe_moe_layer_noalloc(ctypes.byref(Lx), n, x, r, o, None, None,
+                                                                          None)
+    assert L.fmoe_workspace_bytes(ctypes.byref(L0), 64) > qem.NOALLOC_SCRATCH_BYTES
+    assert call(n=64) == 7
+    assert call(n=0) == 6
+    assert call(x=None) == 1
+    assert call(lay(top_k=9)) == 5
+    assert call(lay(hidden=3000)) == 2
