@@ -281,13 +281,29 @@ def read_ceiling(torch, qem, dev):
 
 
 def cpu_model():
+    """The host CPU as /proc/cpuinfo names it, with its family/model/stepping numbers."""
+    info = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = line.split(":", 1)
+                info.setdefault(k.strip(), v.strip())
     except OSError:
-        pass
-    return None
+        return None
+    name = info.get("model name")
+    if name is None:
+        return None
+    ids = ", ".join(f"{k} {info[k]}" for k in ("cpu family", "model", "stepping") if k in info)
+    return f"{name} ({ids})" if ids else name
+
+
+def host_threads():
+    """Hardware threads this process may run on (what std::thread::hardware_concurrency reports,
+    within the CPU set the process is allowed)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count()
 
 
 def versions(torch):
@@ -540,6 +556,7 @@ def main():
             t1, reps1, t_total1, _ = cpu_baseline(a, synth, oracle, R0, g0, h0, budget / 2)
             oracle.set_threads(n_threads)
             cpu = {"value": round(t_layer * 1e6, 1), "unit": "us/layer", "cores": n_threads,
+                   "host_threads": host_threads(),
                    "value_1core": round(t1 * 1e6, 1), "cpu_model": cpu_model(),
                    "kind": "oracle",
                    "sample": f"fp64 oracle, one MoE layer (512-expert router, softmax top-{K}, {K} routed + shared "
@@ -566,8 +583,16 @@ def main():
             parity["near_ties"] = int(sum(lg[order[j]] - lg[order[j + 1]] < max(tau[order[j]], tau[order[j + 1]])
                                           for j in range(K)))
 
+    # the layer's floor on this GPU: its weight bytes streamed at the measured read rate,
+    # plus one empty-kernel launch per kernel of the layer
+    floor = None
+    if ceiling and gap is not None:
+        n_k = 3 if B == 1 else 4
+        stream_us = w_bytes_layer / (ceiling["GBps"] * 1e3)
+        floor = {"stream_at_read_ceiling_us": round(stream_us, 3), "launch_gaps_us": round(n_k * gap, 3),
+                 "total_us": round(stream_us + n_k * gap, 3)}
     rec = {
-        "metric": "µs per MoE layer (top-4 + shared, 4-bit, B=1) and weight GB/s vs HBM peak",
+        "metric": f"µs per MoE layer (top-{K} + shared, {bits}-bit, B={B}) and weight GB/s vs HBM peak",
         "value": round(us_layer, 4),
         "unit": "us/layer",
         "n_gpus": 1,
@@ -577,13 +602,17 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": f"u{bits} codes, bf16 scale/bias, fp32 math",
+        "dtype": (f"u{bits} codes, bf16 scale/bias; gate/up as exact int4 dot products with x in per-64-group "
+                  f"block fixed point (2^-22 of the group max); router, down and combine fp32" if B == 1 else
+                  f"u{bits} codes, bf16 scale/bias; experts as exact int8 MFMA with x and h in per-64-group block "
+                  f"fixed point (2^-22 of the group max); router fp32"),
         "data": "synthetic (seeded; random-init weights of the workload's shapes)",
         "config": {"workload": f"moe_stack_q{bits}_B{B}", "layers": n_layers, "batch": B, "experts": E,
                    "top_k": K, "hidden": H, "inter": I, "group": 64, "graph": graph is not None,
                    "seed": a.seed},
         "us_per_layer_p10_p50_p90": spread,
         "kernels_per_layer": 3 if B == 1 else 4,
+        "floor_us": floor,
         "weight_GBps": round(weight_gbps, 1),
         "frac_hbm_peak": round(weight_gbps / HBM_PEAK_GBPS, 4),
         "read_ceiling_GBps": ceiling,

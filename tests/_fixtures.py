@@ -137,6 +137,24 @@ class OracleLayer:
         return out, idx, w, logits
 
 
+def forward_with_routing(OL, x, residual, idx):
+    """The oracle's layer for one token on a given routing: the oracle's softmax
+    probabilities of the chosen experts renormalised, the oracle's expert outputs,
+    shared gate and combine (out = residual + sum_k w_k E_k(x) + sigma E_shared(x)).
+    Used where a near-tie lets the GPU choose differently from the oracle."""
+    logits = oracle.router_logits(OL.R, x)
+    _, _, p = oracle.route(logits, OL.k)
+    idx = [int(e) for e in idx]
+    w = np.array([p[e] for e in idx], dtype=np.float64)
+    w = w / w.sum()
+    out = np.asarray(residual, dtype=np.float64).copy()
+    for wk, e in zip(w, idx):
+        out += wk * oracle.expert(OL.expert(e), x)[1]
+    if OL.shared:
+        out += oracle.shared_gate(OL.g, x) * oracle.expert(OL.expert(synth.SHARED_EXPERT), x)[1]
+    return out, w
+
+
 def near_tie(logits, R, x, k, idx_gpu):
     """True when the oracle's ranking of the top k+1 logits has a gap below the
     rounding allowance tau_e = 1e-5 * sum_i |R_ei x_i| and the GPU's choice is

@@ -452,3 +452,23 @@ def test_s10_bitwise_identical_across_thread_counts():
     finally:
         oracle.set_threads(before)
     assert np.array_equal(y1, y8)
+
+
+def test_forward_with_routing_reproduces_the_oracle_layer():
+    """The near-tie reference of the GPU tests (the oracle's layer on a given routing)
+    equals oracle.moe_layer when given the oracle's own routing, and moves by exactly one
+    expert's weighted output when one chosen expert is swapped."""
+    from tests._fixtures import OracleLayer, forward_with_routing
+    OL = OracleLayer(5, 0, 4, 16, 4, 256, 256)
+    x = synth.activations(5, synth.T_X, 3, 1, 256)[0].astype(np.float64)
+    res = synth.activations(5, synth.T_RESIDUAL, 3, 1, 256)[0].astype(np.float64)
+    ref, idx, w, _ = OL.forward(x, res)
+    got, gw = forward_with_routing(OL, x, res, idx)
+    assert np.allclose(got, ref, rtol=1e-13, atol=1e-13 * np.abs(ref).max())
+    assert np.allclose(gw, w, rtol=1e-14)
+    swapped = list(idx[:-1]) + [next(e for e in range(16) if e not in idx)]
+    got2, w2 = forward_with_routing(OL, x, res, swapped)
+    logits = oracle.router_logits(OL.R, x)
+    _, _, p = oracle.route(logits, 4)
+    assert np.allclose(w2, p[swapped] / p[swapped].sum(), rtol=1e-14)
+    assert not np.allclose(got2, ref)
