@@ -45,11 +45,14 @@
  * Re-entrancy. Calls are re-entrant; calls that may run concurrently need
  * distinct workspaces and outputs.
  *
- * Supported set. bits in {4, 2}; group == 64; every quantized matrix has cols
- * in {256, 512, 1024, 2048, 4096} (so hidden and inter are in that set) and
- * rows >= 1; 1 <= top_k <= FMOE_MAX_TOPK; 1 <= n_experts <= FMOE_MAX_EXPERTS;
- * 1 <= n_tokens <= FMOE_MAX_TOKENS. The tuned shape is hidden 4096, inter 1024,
- * 512 experts, top_k 4.
+ * Supported set. bits in {4, 2}; group == 64; every quantized matrix has cols a
+ * multiple of 256 from 256 to 4096 (so hidden and inter are such multiples: 768,
+ * 1536, 3072, ... as well as the powers of two) and rows >= 1; 1 <= top_k <=
+ * FMOE_MAX_TOPK; 1 <= n_experts <= FMOE_MAX_EXPERTS; 1 <= n_tokens <=
+ * FMOE_MAX_TOKENS. The tuned shape is hidden 4096, inter 1024, 512 experts, top_k 4.
+ * (A row's 64-column groups are spread one per lane over a wavefront, so 4096
+ * columns is the widest row; widths that are not powers of two leave some lanes
+ * of a row's segment idle.)
  *
  * ---------------------------------------------------------------- blob layout
  * A quantized matrix W [rows][cols] is stored as `rows` row records. A row

@@ -5,9 +5,10 @@
 // (two for 4-bit, one for 2-bit; consecutive lanes read consecutive 16-byte
 // pieces, so each load instruction of a wavefront covers a contiguous span) and
 // its (scale, bias) word, and keeps the matching 64 values of the input vector
-// in registers for every row it visits. A row of `cols` columns occupies
-// NG = cols/64 lanes; a wavefront covers 64/NG rows per iteration, and DPP
-// cross-lane adds over those lanes finish each row.
+// in registers for every row it visits. A row of `cols` columns has ng = cols/64
+// groups and occupies NGP lanes (ng rounded up to a power of two, pad_groups); a
+// wavefront covers 64/NGP rows per iteration, and DPP cross-lane adds over those
+// lanes finish each row.
 //
 // Arithmetic. The pages recast (code*scale + bias)*x as
 // fma(code, scale*x, bias*x) ("397B MoE en MacBook: Motor Flash-MoE a 4,4 t/s",
@@ -135,18 +136,26 @@ __device__ __forceinline__ float dot_codes(const Chunk<2> &c, const float *v) {
   return fmaf(a[3], 0.015625f, fmaf(a[2], 0.0625f, fmaf(a[1], 0.25f, a[0])));
 }
 
-// Loads of lane g's group from one row record (NG groups per row).
-template <int BITS, int NG>
-__device__ __forceinline__ void load_group(const uint8_t *__restrict__ rec, int g, Chunk<BITS> &c, uint32_t &sb) {
+// Loads of group g (g < ng) from one row record of ng groups.
+template <int BITS>
+__device__ __forceinline__ void load_group(const uint8_t *__restrict__ rec, int ng, int g, Chunk<BITS> &c,
+                                           uint32_t &sb) {
   if constexpr (BITS == 4) {
     c.a = *reinterpret_cast<const uint4 *>(rec + 16 * g);
-    c.b = *reinterpret_cast<const uint4 *>(rec + 16 * (NG + g));
-    sb = *reinterpret_cast<const uint32_t *>(rec + 32 * NG + 4 * g);
+    c.b = *reinterpret_cast<const uint4 *>(rec + 16 * (ng + g));
+    sb = *reinterpret_cast<const uint32_t *>(rec + 32 * ng + 4 * g);
   } else {
     c.a = *reinterpret_cast<const uint4 *>(rec + 16 * g);
-    sb = *reinterpret_cast<const uint32_t *>(rec + 16 * NG + 4 * g);
+    sb = *reinterpret_cast<const uint32_t *>(rec + 16 * ng + 4 * g);
   }
 }
+
+// Row widths. A row of ng groups (ng = cols / 64, any value 4 .. 64: cols a
+// multiple of 256 up to 4096) occupies a segment of NGP lanes, NGP the power of
+// two at or above ng; lane g < ng holds group g. The lanes past ng load group
+// ng - 1 again (the same bytes, no extra traffic) and see an input of zeros (the
+// staged vector is zero past ng groups), so they add exactly 0 to the row.
+__host__ __device__ constexpr int pad_groups(int ng) { return ng <= 4 ? 4 : ng <= 8 ? 8 : ng <= 16 ? 16 : ng <= 32 ? 32 : 64; }
 
 // scale * sum c x + bias * sum x over the lane's group
 template <int BITS>

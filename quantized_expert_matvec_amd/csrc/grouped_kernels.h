@@ -121,12 +121,13 @@ __device__ __forceinline__ i32x4_t mfma_codes(const MCodes &m) {
 // ------------------------------------------------------------------ matrix-core rows
 
 // Workgroup-cooperative (kGThreads threads): NTILE tiles of 16 rows per
-// wavefront (tile i: rows rec0 + i * tile_stride + r * RB, r = 0..15) against
-// T <= kTokBlock vectors tokv[u] of a prepared source: digit plane k (0..2) at
-// xq_base + (3 vec + k) * NG * 64 (bytes); per group (f, sum v) at
-// xs_base + 2 (vec * NG + g). The vectors are staged in LDS once (xl: XL + 16
-// bytes, xsl: kTokBlock * NG + 1 entries). As each tile ends, lane (n = lane %
-// 16, u = lane / 16) holds in y row n of the tile for token u (meaningless for
+// wavefront (tile i: rows rec0 + i * tile_stride + r * RB, r = 0..15; records of
+// ng groups, RB bytes) against T <= kTokBlock vectors tokv[u] of a prepared
+// source: digit plane k (0..2) at xq_base + (3 vec + k) * ng * 64 (bytes); per
+// group (f, sum v) at xs_base + 2 (vec * ng + g). The vectors are staged in LDS
+// once (xl: XL + 16 bytes, each vector NGP groups wide; xsl: kTokBlock * NGP + 1
+// entries, zero for the groups past ng). As each tile ends, lane (n = lane % 16,
+// u = lane / 16) holds in y row n of the tile for token u (meaningless for
 // u >= T). Contains barriers: every thread of the workgroup calls it with the
 // same T.
 //
@@ -138,27 +139,28 @@ __device__ __forceinline__ i32x4_t mfma_codes(const MCodes &m) {
 // branches around its loads (its last round, which requests nothing, is a
 // separate copy), so every wait is exact; the empty asm statements keep the
 // optimiser from moving the loads (and the reads of their results) away from
-// where the pipeline needs them.
-template <int BITS, int NG, int NTILE = 1>
+// where the pipeline needs them. A row of ng < NGP groups runs as NGP groups:
+// the groups past ng load group ng - 1 (and its neighbour's scale/bias) again,
+// and their factor f and sum are zero, so they add exactly 0. FULL: ng == NGP
+// (the group count is then a compile-time constant).
+template <int BITS, int NGP, int NTILE = 1, bool FULL = true>
 struct MfmaRows {
-  static constexpr int CG = NG < 8 ? NG : 8;          // groups per chunk
-  static constexpr int NC = NG / CG;                  // chunks per row
+  static constexpr int CG = NGP < 8 ? NGP : 8;        // groups per chunk
+  static constexpr int NC = NGP / CG;                 // chunks per row
   static constexpr int NCT = NTILE * NC;              // chunks of the whole stream
   static constexpr int DEPTH = NCT < 4 ? NCT : 4;     // chunks in flight
   static constexpr int HALVES = BITS == 4 ? 2 : 1;    // 16-byte code units per group
   static constexpr int NI = 16 * HALVES * CG / kWave; // 16-byte code loads per lane per chunk
   static constexpr int SBW = CG / 4;                  // scale/bias words per lane per chunk
-  static constexpr int RB = NG * gbytes<BITS>();      // bytes per row record
-  static constexpr int SBO = 16 * HALVES * NG;        // scale/bias words within a record
   static constexpr int RS = 16 * HALVES * CG + 16;    // LDS bytes per row of codes (padded)
   static constexpr int SBS = CG + 1;                  // LDS words per row of scale/bias (padded)
-  static constexpr int VS = NG * 64 + 16;             // LDS bytes per staged vector (padded)
+  static constexpr int VS = NGP * 64 + 16;            // LDS bytes per staged vector (padded)
   static constexpr int XL = kParts * kTokBlock * VS;  // LDS bytes of staged x (a spare 16 B follow)
-  static_assert(NG <= kMaxNG, "row width");
+  static_assert(NGP <= kMaxNG, "row width");
   static_assert(16 * RS + 64 * SBS <= kWaveLds, "chunk fits the wavefront's LDS region");
   static_assert(NCT % DEPTH == 0, "whole rounds of chunks");
   static_assert((NC & (NC - 1)) == 0, "chunks per row: a power of two");
-  static_assert(kTokBlock * NG <= kGThreads, "one group sum per thread");
+  static_assert(kTokBlock * NGP <= kGThreads, "one group sum per thread");
 
   struct Chunk {
     uint4 c[NI];
@@ -166,27 +168,31 @@ struct MfmaRows {
   };
 
   float y;
+  int ng;  // groups per row (<= NGP; a multiple of 4)
 
   // this lane's share of a chunk: code unit u = 64 k + lane is (row, half, group)
-  // = (u / (HALVES CG), u / CG % HALVES, u % CG); scale/bias: row lane / 4, words
-  // SBW (lane % 4) .. + SBW - 1
-  int goff[NI], loff[NI], gsoff, lsoff;
+  // = (u / (HALVES CG), u / CG % HALVES, u % CG), at goff + 16 (group); scale/bias:
+  // row lane / 4, groups SBW (lane % 4) .. + SBW - 1 of the chunk, at gsoff + 4 (group)
+  int goff[NI], loff[NI], gj, gsoff, gsg, lsoff;
   // where lane (n, q) reads group j of the chunk in its LDS region
   int rcode, rsb;
 
   __device__ __forceinline__ void offsets() {
     const int lane = lane_id();
     const int q = lane >> 4, i = lane & 15;
+    const int RB = ng * gbytes<BITS>();
 #pragma unroll
     for (int k = 0; k < NI; ++k) {
       const int u = kWave * k + lane;
       const int j = u % CG, rh = u / CG;
       const int r = rh / HALVES, h = rh % HALVES;
-      goff[k] = r * RB + 16 * (h * NG + j);
+      goff[k] = r * RB + 16 * h * ng;
       loff[k] = r * RS + 16 * (h * CG + j);
     }
+    gj = lane % CG;  // the group within the chunk, the same for every k (CG divides 64)
     const int sr = lane >> 2, sp = lane & 3;
-    gsoff = sr * RB + SBO + 4 * SBW * sp;
+    gsoff = sr * RB + 16 * HALVES * ng;
+    gsg = SBW * sp;
     lsoff = 16 * RS + 4 * (sr * SBS + SBW * sp);
     rcode = BITS == 4 ? i * RS + 16 * (q >> 1) * CG + 8 * (q & 1) : i * RS + 4 * q;
     rsb = 16 * RS + 4 * i * SBS;
@@ -197,55 +203,59 @@ struct MfmaRows {
   __device__ __forceinline__ void load_chunk(const uint8_t *__restrict__ rec0, size_t tile_stride, int c,
                                              Chunk &k) const {
     const uint8_t *r = rec0 + (size_t)(c / NC) * tile_stride;
-    const int cc = c % NC;
+    const int g0 = (c % NC) * CG;
 #pragma unroll
-    for (int t = 0; t < NI; ++t) k.c[t] = *reinterpret_cast<const uint4 *>(r + goff[t] + 16 * CG * cc);
+    for (int t = 0; t < NI; ++t)
+      k.c[t] = *reinterpret_cast<const uint4 *>(r + goff[t] + 16 * min(g0 + gj, ng - 1));
     if constexpr (SBW == 2) {
-      const uint2 v = *reinterpret_cast<const uint2 *>(r + gsoff + 4 * CG * cc);
+      // (ng is even: a pair past ng re-reads the last pair of the row)
+      const uint2 v = *reinterpret_cast<const uint2 *>(r + gsoff + 4 * min(g0 + gsg, ng - 2));
       k.s[0] = v.x;
       k.s[1] = v.y;
     } else {
-      k.s[0] = *reinterpret_cast<const uint32_t *>(r + gsoff + 4 * CG * cc);
+      k.s[0] = *reinterpret_cast<const uint32_t *>(r + gsoff + 4 * min(g0 + gsg, ng - 1));
     }
   }
 
   // one batch of staging loads: 16-byte units e0 + k kGThreads of the
-  // 3 T NG 4 (vector 3u + plane, unit); past the end, a clamped unit whose store
+  // 3 T ng 4 (vector 3u + plane, unit); past the end, a clamped unit whose store
   // goes to the spare slot at XL. One batch covers four tokens: a single memory
   // round trip.
-  static constexpr int kBatch = (kParts * kTokBlock * NG * 4 + kGThreads - 1) / kGThreads;
+  static constexpr int kBatch = (kParts * kTokBlock * NGP * 4 + kGThreads - 1) / kGThreads;
   __device__ __forceinline__ static void load_batch(const uint8_t *__restrict__ xq_base, const int *tokv, int units,
-                                                    int e0, uint4 (&xv)[kBatch], int (&xdst)[kBatch]) {
+                                                    int ng, int e0, uint4 (&xv)[kBatch], int (&xdst)[kBatch]) {
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const int ee = e0 + k * kGThreads;
       const int e = min(ee, units - 1);
-      const int vv = e / (NG * 4), rr = e - vv * (NG * 4);
+      const int vv = e / (ng * 4), rr = e - vv * (ng * 4);
       const int vu = vv / kParts, vk = vv - kParts * vu;
-      xv[k] = *reinterpret_cast<const uint4 *>(xq_base + ((size_t)(kParts * tokv[vu] + vk) * NG) * 64 + 16 * rr);
+      xv[k] = *reinterpret_cast<const uint4 *>(xq_base + ((size_t)(kParts * tokv[vu] + vk) * ng) * 64 + 16 * rr);
       xdst[k] = ee < units ? vv * VS + 16 * rr : XL;
     }
   }
 
   // An item's staging data in registers: its vectors' group factors and sums
-  // (one float2 per thread) and its digit planes (one batch covers kTokBlock
-  // tokens), with their LDS destinations.
+  // (one float2 per thread; zero for the groups past ng) and its digit planes
+  // (one batch covers kTokBlock tokens), with their LDS destinations.
   struct XAhead {
     uint4 xv[kBatch];
     int xdst[kBatch];
     float2 sv;
     int sdst;
+    bool szero;
   };
-  static_assert(kBatch * kGThreads >= kParts * kTokBlock * NG * 4, "one batch stages an item");
+  static_assert(kBatch * kGThreads >= kParts * kTokBlock * NGP * 4, "one batch stages an item");
   // request the staging data of an item of T tokens whose vector indices are in tv
   __device__ __forceinline__ static void stage_request(const uint8_t *__restrict__ xq_base,
                                                        const float *__restrict__ xs_base, const int *tv, int T,
-                                                       XAhead &ah) {
-    const int e = min((int)threadIdx.x, T * NG - 1);
-    const int u = e / NG, gl = e - u * NG;
-    ah.sv = reinterpret_cast<const float2 *>(xs_base)[(size_t)tv[u] * NG + gl];
-    ah.sdst = (int)threadIdx.x < T * NG ? u * NG + gl : kTokBlock * NG;
-    load_batch(xq_base, tv, kParts * T * NG * 4, threadIdx.x, ah.xv, ah.xdst);
+                                                       int ng, XAhead &ah) {
+    const int e = min((int)threadIdx.x, T * NGP - 1);
+    const int u = e / NGP, gl = e - u * NGP;
+    ah.sv = reinterpret_cast<const float2 *>(xs_base)[(size_t)tv[u] * ng + min(gl, ng - 1)];
+    ah.szero = gl >= ng;
+    ah.sdst = (int)threadIdx.x < T * NGP ? u * NGP + gl : kTokBlock * NGP;
+    load_batch(xq_base, tv, kParts * T * ng * 4, ng, threadIdx.x, ah.xv, ah.xdst);
   }
 
   // rec0: record of the wavefront's first row of its first tile (the NTILE tiles
@@ -262,7 +272,7 @@ struct MfmaRows {
   // that it arrives while this item's stream ends; *have = Tn > 0.
   template <bool PRE, bool AHEAD = false, typename Fill, typename After, typename TileDone,
             typename FillN = void (*)(int)>
-  __device__ __forceinline__ void run(const uint8_t *__restrict__ rec0, size_t tile_stride,
+  __device__ __forceinline__ void run(int ngroups, const uint8_t *__restrict__ rec0, size_t tile_stride,
                                       const uint8_t *__restrict__ xq_base, const float *__restrict__ xs_base, int T,
                                       int *tokv, Fill fill, After after, TileDone tile_done, uint8_t *xl,
                                       float2 *xsl, uint8_t *wl, XAhead *ah = nullptr, bool *have = nullptr,
@@ -272,6 +282,7 @@ struct MfmaRows {
     const int q = lane >> 4;  // k-block of the A / B operands; token of D
     const int i = lane & 15;  // A row (4 token + part) / weight row of B and D
     y = 0.f;
+    ng = FULL ? NGP : ngroups;
     offsets();
     // per-token tables (tokv, ...) from values the caller requested earlier
     if ((int)threadIdx.x < T) fill((int)threadIdx.x);
@@ -283,7 +294,7 @@ struct MfmaRows {
     int aoff, xoff;
     if constexpr (PRE) {
       // x is staged already, every token of the batch in token order (vector
-      // 3 t + part, group sums at t NG): the whole prologue goes out at once, and
+      // 3 t + part, group sums at t NGP): the whole prologue goes out at once, and
       // an A row reads its token's vector
       after();
 #pragma unroll
@@ -292,22 +303,22 @@ struct MfmaRows {
         asm volatile("" ::: "memory");
       }
       aoff = (kParts * tokv[min(i >> 2, T - 1)] + min(i & 3, kParts - 1)) * VS + q * 16;
-      xoff = tokv[min(q, T - 1)] * NG;
+      xoff = tokv[min(q, T - 1)] * NGP;
     } else {
       // Requests in the order they are needed: x (its group factors and sums,
-      // then its digit planes: 3 T NG 4 16-byte units) and the caller's epilogue
+      // then its digit planes: 3 T ng 4 16-byte units) and the caller's epilogue
       // values; the first weight chunk; once x is in LDS (a wavefront issues in
       // order, and a long queue of weight requests ahead of the staging stores
       // would hold them up), the rest of the first DEPTH chunks. The parts move in
       // batches (loads of a batch before its stores); stores are unconditional
-      // (lanes past the end write a spare slot: xl at XL, xsl at kTokBlock * NG),
+      // (lanes past the end write a spare slot: xl at XL, xsl at kTokBlock * NGP),
       // so that the optimiser keeps a batch's loads together.
       XAhead own;
       XAhead &st = AHEAD ? *ah : own;
-      if (!AHEAD || !*have) stage_request(xq_base, xs_base, tokv, T, st);  // (uniform)
+      if (!AHEAD || !*have) stage_request(xq_base, xs_base, tokv, T, ng, st);  // (uniform)
       after();
       // narrow rows stage little x: then the whole prologue goes out at once
-      constexpr int EARLY = NG <= 16 ? DEPTH : 1;
+      constexpr int EARLY = NGP <= 16 ? DEPTH : 1;
 #pragma unroll
       for (int d = 0; d < EARLY; ++d) {
         load_chunk(rec0, tile_stride, d, ring[d]);
@@ -315,7 +326,7 @@ struct MfmaRows {
       }
       {
         const float2 v = st.sv;  // (through locals: a direct struct copy kept st in scratch memory)
-        xsl[st.sdst] = v;
+        xsl[st.sdst] = st.szero ? make_float2(0.f, 0.f) : v;
       }
 #pragma unroll
       for (int k = 0; k < kBatch; ++k) {
@@ -332,7 +343,7 @@ struct MfmaRows {
       // and the fourth row of a token feed D rows that are never read); X: token
       // min(q, T - 1)
       aoff = (kParts * min(i >> 2, T - 1) + min(i & 3, kParts - 1)) * VS + q * 16;
-      xoff = min(q, T - 1) * NG;
+      xoff = min(q, T - 1) * NGP;
     }
     // chunk c from ring slot d; then (if REFILL) slot d requests chunk c + DEPTH
     auto step = [&](auto refill, int c, Chunk &slot) {
@@ -393,7 +404,7 @@ struct MfmaRows {
       step(std::false_type{}, NCT - DEPTH + d, ring[d]);
       if constexpr (AHEAD) {
         if (d == (DEPTH - 1) / 2) {
-          stage_request(xq_base, xs_base, Tn > 0 ? tokn : tokv, Tn > 0 ? Tn : T, *ah);
+          stage_request(xq_base, xs_base, Tn > 0 ? tokn : tokv, Tn > 0 ? Tn : T, ng, *ah);
           asm volatile("" ::: "memory");
           *have = Tn > 0;
         }
@@ -416,17 +427,16 @@ __host__ __device__ constexpr int g1_rows_per_block() {
   return kWavesPerBlock / router_split<NGH>();
 }
 
-template <int BITS, int NGH>
+template <int BITS, int NGHP>
 __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
-  constexpr int NT = NGH / 4;
-  constexpr int H = NGH * kGroup;
-  constexpr int SPLIT = router_split<NGH>();
-  constexpr int NTW = NT / SPLIT;                            // float4 per lane of a wavefront's part of a row
-  constexpr int RPB = g1_rows_per_block<NGH>();
-  constexpr int CF4 = kG1Chunk * H / 4;                      // float4 of a chunk of tokens
-  constexpr int C4 = (CF4 + kBlock - 1) / kBlock;
+  constexpr int SPLIT = router_split<NGHP>();
+  constexpr int NTW = NGHP / 4 / SPLIT;                      // float4 per lane of a wavefront's part of a row, at most
+  constexpr int RPB = g1_rows_per_block<NGHP>();
+  constexpr int C4 = (kG1Chunk * NGHP * 16 + kBlock - 1) / kBlock;
+  const int ng = a.H / kGroup, H = a.H, nt = ng / 4;
+  const int CF4 = kG1Chunk * H / 4;                          // float4 of a chunk of tokens
   __shared__ float part[2][kWavesPerBlock];
-  __shared__ uint32_t xc[kG1Chunk * H];                      // a chunk of tokens' x (fp32 bits)
+  __shared__ uint32_t xc[kG1Chunk * NGHP * kGroup];          // a chunk of tokens' x (fp32 bits)
   __shared__ float dp[kWavesPerBlock][kMaxTokens];           // per wavefront: its part of each token's dot
   const int lane = lane_id();
   const int wv = wave_in_block();
@@ -436,7 +446,7 @@ __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
     const int t = blockIdx.x - a.n_router_blocks;
     const float *xt = a.x + (size_t)t * H;
     const float *gv = a.gvec ? a.gvec : a.x;  // (read but unused without a shared expert)
-    constexpr int UNITS = NGH * 8;  // 8 consecutive columns each: unit u = columns 8u .. 8u + 7
+    const int UNITS = ng * 8;  // 8 consecutive columns each: unit u = columns 8u .. 8u + 7
     float ss = 0.f, gd = 0.f;
     for (int u0 = 0; u0 < UNITS; u0 += kBlock) {
       const int u = u0 + threadIdx.x;
@@ -468,7 +478,7 @@ __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) d[j] = digits3(f[j], k);
       if (ok) {
-        uint8_t *dst = a.xq + ((size_t)(kParts * t) * NGH + g) * 64 + 8 * (uc & 7);
+        uint8_t *dst = a.xq + ((size_t)(kParts * t) * ng + g) * 64 + 8 * (uc & 7);
 #pragma unroll
         for (int p = 0; p < kParts; ++p) {
           const int sh = 8 * p;
@@ -476,9 +486,9 @@ __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
                                ((d[3] >> sh) & 0xFFu) << 24,
                            ((d[4] >> sh) & 0xFFu) | ((d[5] >> sh) & 0xFFu) << 8 | ((d[6] >> sh) & 0xFFu) << 16 |
                                ((d[7] >> sh) & 0xFFu) << 24};
-          *reinterpret_cast<uint2 *>(dst + (size_t)p * NGH * 64) = w;
+          *reinterpret_cast<uint2 *>(dst + (size_t)p * ng * 64) = w;
         }
-        if ((uc & 7) == 0) reinterpret_cast<float2 *>(a.xsum)[(size_t)t * NGH + g] = make_float2(group_factor(gmax, k), sum);
+        if ((uc & 7) == 0) reinterpret_cast<float2 *>(a.xsum)[(size_t)t * ng + g] = make_float2(group_factor(gmax, k), sum);
       }
     }
     ss = seg_reduce<kWave>(ss);
@@ -507,10 +517,12 @@ __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
   const int half = wv % SPLIT;
   const int row = (int)blockIdx.x * RPB + wv / SPLIT;
   const int rr = min(row, a.E - 1);
-  const float4 *src = reinterpret_cast<const float4 *>(a.router + (size_t)rr * H) + 64 * NTW * half;
+  const int per = (nt + SPLIT - 1) / SPLIT;  // chunks of 256 columns per part
+  const int t0 = per * half, tn = min(per, nt - t0);  // this part's chunks (tn >= 1)
+  const float4 *src = reinterpret_cast<const float4 *>(a.router + (size_t)rr * H) + 64 * t0;
   float4 wr[NTW];
 #pragma unroll
-  for (int q = 0; q < NTW; ++q) wr[q] = src[lane + 64 * q];
+  for (int q = 0; q < NTW; ++q) wr[q] = src[lane + 64 * min(q, tn - 1)];
   Staged<C4> nx;
   stage_load(a.x, min(kG1Chunk, a.B) * (H / 4), nx);
 #pragma unroll 1
@@ -524,15 +536,17 @@ __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int tt = 0; tt < kG1Chunk; ++tt) {
-      const float4 *xv4 = reinterpret_cast<const float4 *>(xc) + tt * (H / 4) + 64 * NTW * half;
+      const float4 *xv4 = reinterpret_cast<const float4 *>(xc) + tt * (H / 4) + 64 * t0;
       float acc = 0.f;
 #pragma unroll
       for (int q = 0; q < NTW; ++q) {
-        const float4 xv = xv4[lane + 64 * q];
-        acc = fmaf(wr[q].x, xv.x, acc);
-        acc = fmaf(wr[q].y, xv.y, acc);
-        acc = fmaf(wr[q].z, xv.z, acc);
-        acc = fmaf(wr[q].w, xv.w, acc);
+        if (q < tn) {  // (uniform)
+          const float4 xv = xv4[lane + 64 * q];
+          acc = fmaf(wr[q].x, xv.x, acc);
+          acc = fmaf(wr[q].y, xv.y, acc);
+          acc = fmaf(wr[q].z, xv.z, acc);
+          acc = fmaf(wr[q].w, xv.w, acc);
+        }
       }
       const float d = seg_reduce<kWave>(acc);
       if (lane == kWave - 1 && c + tt < a.B) dp[wv][c + tt] = d;
@@ -732,9 +746,11 @@ __device__ __forceinline__ int block_route(const GroupArgs &a, RouteLdsT<NW> &R,
 // inter dimension) of one item's expert, for the item's tokens / slots.
 // Wavefront w holds rows 16w .. 16w + 15. h vectors: slot s at index s,
 // shared-expert token t at index S + t.
-template <int BITS, int NGH, int NGI, bool PRE>
+template <int BITS, int NGH, bool PRE, bool FULL>
 __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
-  constexpr size_t RB = (size_t)NGH * gbytes<BITS>();
+  // (NGH: the hidden groups ng rounded up to a power of two; FULL: ng == NGH)
+  const int ng = FULL ? NGH : a.H / kGroup, ngi = a.I / kGroup;
+  const size_t RB = (size_t)ng * gbytes<BITS>();
   // staged x, and before it the routing scratch
   constexpr size_t kXlBytes = MfmaRows<BITS, NGH>::XL + 16 > sizeof(RouteLds) ? MfmaRows<BITS, NGH>::XL + 16
                                                                                : sizeof(RouteLds);
@@ -754,20 +770,20 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
   // take items in grid stride; a workgroup derives the routing (every one the
   // same; the one that meets the first routed item first publishes it) when it
   // meets its first routed item, so the shared expert's items stream at once.
-  const int sh_items = sh ? (a.B + kTokBlock - 1) / kTokBlock * NGI : 0;
-  const int max_items = sh_items + S * NGI;
+  const int sh_items = sh ? (a.B + kTokBlock - 1) / kTokBlock * ngi : 0;
+  const int max_items = sh_items + S * ngi;
   const bool writer = (int)blockIdx.x == sh_items % (int)gridDim.x;
   int NB = -1;  // routing not derived yet
   // A batch of at most kTokBlock tokens: every item's tokens are among them, so
   // their x is staged once, now, by the wavefronts past the batch's tokens
   // (wavefront t < B derives token t's top-K meanwhile), in token order; the
   // routing scratch then lives in the wavefronts' chunk regions instead of xl.
-  using MR = MfmaRows<BITS, NGH>;
+  using MR = MfmaRows<BITS, NGH, 1, FULL>;
   constexpr bool pre = PRE;  // (launched for batches of at most kTokBlock tokens)
   static_assert(sizeof(RouteLds1) <= sizeof(wlds), "routing scratch of a small batch fits the chunk regions");
   if (pre && wv >= a.B) {  // (B <= kTokBlock < kGWaves: at least four such wavefronts)
     const int nst = (kGWaves - a.B) * kWave, st = (int)threadIdx.x - a.B * kWave;
-    const int units = kParts * a.B * NGH * 4;
+    const int units = kParts * a.B * ng * 4;
     constexpr int kB = 12;
     for (int e0 = st; e0 < units; e0 += kB * nst) {
       uint4 v[kB];
@@ -776,8 +792,8 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
       for (int k = 0; k < kB; ++k) {
         const int ee = e0 + k * nst;
         const int e = min(ee, units - 1);
-        const int vv = e / (NGH * 4), rr = e - vv * (NGH * 4);
-        v[k] = *reinterpret_cast<const uint4 *>(a.xq + (size_t)vv * NGH * 64 + 16 * rr);
+        const int vv = e / (ng * 4), rr = e - vv * (ng * 4);
+        v[k] = *reinterpret_cast<const uint4 *>(a.xq + (size_t)vv * ng * 64 + 16 * rr);
         dst[k] = ee < units ? vv * MR::VS + 16 * rr : MR::XL;
       }
       asm volatile("" ::: "memory");
@@ -787,7 +803,11 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
         *reinterpret_cast<uint4 *>(xl + dst[k]) = t;
       }
     }
-    for (int e = st; e < a.B * NGH; e += nst) xsl[e] = reinterpret_cast<const float2 *>(a.xsum)[e];
+    // group sums of token u at u NGH + g, zero for the groups past ng
+    for (int e = st; e < a.B * NGH; e += nst) {
+      const int u = e / NGH, g = e - u * NGH;
+      xsl[e] = g < ng ? reinterpret_cast<const float2 *>(a.xsum)[(size_t)u * ng + g] : make_float2(0.f, 0.f);
+    }
   }
   // (items staged one by one) the next item's x is requested during this item's
   // last chunks, when its tokens are known: any next shared item, a routed one
@@ -798,9 +818,9 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
     GroupItem it;
     int gi;
     if (item < sh_items) {
-      gi = item % NGI;
+      gi = item % ngi;
       it.expert = -1;
-      it.q0 = kTokBlock * (item / NGI);
+      it.q0 = kTokBlock * (item / ngi);
       it.n = min(kTokBlock, a.B - it.q0);
     } else {
       if (NB < 0) {
@@ -809,9 +829,9 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
         else
           NB = block_route(a, *reinterpret_cast<RouteLds *>(xl), slotl, blk, writer);
       }
-      const int kb = (item - sh_items) / NGI;
+      const int kb = (item - sh_items) / ngi;
       if (kb >= NB) break;  // (uniform) later items are past the last block
-      gi = (item - sh_items) % NGI;
+      gi = (item - sh_items) % ngi;
       // (uniform values: kept in scalar registers)
       it.expert = __builtin_amdgcn_readfirstlane(blk[kBlkInts * kb]);
       it.n = __builtin_amdgcn_readfirstlane(blk[kBlkInts * kb + 1]);
@@ -838,10 +858,10 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
       const int nitem = item + (int)gridDim.x;
       if (nitem < sh_items) {
         nsh = true;
-        nq0 = kTokBlock * (nitem / NGI);
+        nq0 = kTokBlock * (nitem / ngi);
         Tn = min(kTokBlock, a.B - nq0);
       } else if (nitem < max_items && NB >= 0) {
-        const int kbn = (nitem - sh_items) / NGI;
+        const int kbn = (nitem - sh_items) / ngi;
         if (kbn < NB) {
           nq0 = kBlkInts * kbn + 2;
           Tn = __builtin_amdgcn_readfirstlane(blk[kBlkInts * kbn + 1]);
@@ -851,7 +871,7 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
     auto filln = [&](int u) { tokn[u] = nsh ? nq0 + u : blk[nq0 + u] / a.K; };
     float y = 0.f;
     MR M;
-    M.template run<PRE, !PRE>(rec0, 0, a.xq, a.xsum, T, tokv, fill, after, [&](int) { y = M.y; }, xl, xsl,
+    M.template run<PRE, !PRE>(ng, rec0, 0, a.xq, a.xsum, T, tokv, fill, after, [&](int) { y = M.y; }, xl, xsl,
                               wlds[wv], &ahead, &have, Tn, tokn, filln);
     // h = silu(gate) * up: gate rows are even, up rows odd (adjacent lanes); the
     // item's 64 pairs are one whole group of h (pair 8 wv + n / 2)
@@ -906,7 +926,7 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
         mb = max(mb, __float_as_int(hpart[v][u].y));
       }
       const float amax = __int_as_float(mb);
-      reinterpret_cast<float2 *>(a.hsum)[(size_t)hv_thr * NGI + gi] = make_float2(group_factor(amax, group_shift(amax)), sum);
+      reinterpret_cast<float2 *>(a.hsum)[(size_t)hv_thr * ngi + gi] = make_float2(group_factor(amax, group_shift(amax)), sum);
     }
   }
 }
@@ -919,9 +939,11 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
 // G[1] exit at once), each times the H / (128 TILES) row parts. Two tiles per
 // staging halve the staging overhead when there are many token blocks; with
 // few, one tile per workgroup spreads the rows over more compute units.
-template <int BITS, int NGI, int kG3Tiles>
+template <int BITS, int NGI, int kG3Tiles, bool FULL>
 __global__ __launch_bounds__(kGThreads) void k_g3(const GroupArgs a) {
-  constexpr size_t RB = (size_t)NGI * gbytes<BITS>();
+  // (NGI: the inter groups ngi rounded up to a power of two; FULL: ngi == NGI)
+  const int ngi = FULL ? NGI : a.I / kGroup;
+  const size_t RB = (size_t)ngi * gbytes<BITS>();
   __shared__ __attribute__((aligned(16))) uint8_t xl[MfmaRows<BITS, NGI, kG3Tiles>::XL + 16];
   __shared__ float2 xsl[kTokBlock * NGI + 1];
   __shared__ __attribute__((aligned(16))) uint8_t wlds[kGWaves][kWaveLds];
@@ -962,11 +984,11 @@ __global__ __launch_bounds__(kGThreads) void k_g3(const GroupArgs a) {
   };
   float osc;  // sigma (shared) or routing weight of this lane's D rows
   auto after = [&]() { osc = scl[oidx[min(qq, T - 1)]]; };
-  MfmaRows<BITS, NGI, kG3Tiles> M;
+  MfmaRows<BITS, NGI, kG3Tiles, FULL> M;
   auto done = [&](int tile) {
     if (qq < T) outp[(size_t)oidx[qq] * a.H + row0 + 128 * tile + n] = osc * M.y;
   };
-  M.template run<false>(rec0, (size_t)128 * RB, a.hq, a.hsum, T, tokv, fill, after, done, xl, xsl, wlds[wv]);
+  M.template run<false>(ngi, rec0, (size_t)128 * RB, a.hq, a.hsum, T, tokv, fill, after, done, xl, xsl, wlds[wv]);
 }
 
 // g4: out[t] = residual[t] + sum_k partial[t*K + k] (k ascending) + d_shared[t]
@@ -1015,50 +1037,67 @@ inline int cu_count() {
   return cache[dev];
 }
 
+// Launches of the grouped layer; NGH and NGI are the hidden and inter group
+// counts rounded up to powers of two (the router and gate/up kernels depend on
+// the first, the down kernel on the second).
 template <int BITS>
 struct GroupDispatch {
-  template <int NGH, int NGI>
-  static hipError_t layer(GroupArgs a, hipStream_t s, int phases) {
+  template <int NGH>
+  static hipError_t front(GroupArgs a, hipStream_t s, int phases) {
     const bool sh = a.shared != nullptr;
     const int S = a.B * a.K;
     const int shb = sh ? (a.B + kTokBlock - 1) / kTokBlock : 0;  // shared token blocks
     a.n_router_blocks = (a.E + g1_rows_per_block<NGH>() - 1) / g1_rows_per_block<NGH>();
-    const int n4 = (a.B * (a.H / 4) + kBlock - 1) / kBlock;
     if (phases & 1)
       hipLaunchKernelGGL((k_g1<BITS, NGH>), dim3(a.n_router_blocks + a.B), dim3(kBlock), 0, s, a);
     if (phases & 2) {
-      const dim3 grid(std::min((shb + S) * NGI, cu_count()));
-      if (a.B <= kTokBlock)
-        hipLaunchKernelGGL((k_g2<BITS, NGH, NGI, true>), grid, dim3(kGThreads), 0, s, a);
+      const dim3 grid(std::min((shb + S) * (a.I / kGroup), cu_count()));
+      const bool full = a.H == NGH * kGroup;
+      if (a.B <= kTokBlock && full)
+        hipLaunchKernelGGL((k_g2<BITS, NGH, true, true>), grid, dim3(kGThreads), 0, s, a);
+      else if (a.B <= kTokBlock)
+        hipLaunchKernelGGL((k_g2<BITS, NGH, true, false>), grid, dim3(kGThreads), 0, s, a);
+      else if (full)
+        hipLaunchKernelGGL((k_g2<BITS, NGH, false, true>), grid, dim3(kGThreads), 0, s, a);
       else
-        hipLaunchKernelGGL((k_g2<BITS, NGH, NGI, false>), grid, dim3(kGThreads), 0, s, a);
-    }
-    if (phases & 4) {
-      if (a.B <= kTokBlock)
-        hipLaunchKernelGGL((k_g3<BITS, NGI, 1>), dim3((shb + S) * (a.H / 128)), dim3(kGThreads), 0, s, a);
-      else
-        hipLaunchKernelGGL((k_g3<BITS, NGI, 2>), dim3((shb + S) * (a.H / 256)), dim3(kGThreads), 0, s, a);
-      hipLaunchKernelGGL(k_g4<BITS>, dim3(n4), dim3(kBlock), 0, s, a);
+        hipLaunchKernelGGL((k_g2<BITS, NGH, false, false>), grid, dim3(kGThreads), 0, s, a);
     }
     return hipGetLastError();
   }
 
-  template <int NGH>
-  static hipError_t layer_h(const GroupArgs &a, hipStream_t s, int phases) {
-    switch (a.I / kGroup) {
-      case 4: return layer<NGH, 4>(a, s, phases);
-      case 8: return layer<NGH, 8>(a, s, phases);
-      case 16: return layer<NGH, 16>(a, s, phases);
-      case 32: return layer<NGH, 32>(a, s, phases);
-      case 64: return layer<NGH, 64>(a, s, phases);
-      default: return hipErrorInvalidValue;
+  template <int NGI>
+  static hipError_t back(const GroupArgs &a, hipStream_t s, int phases) {
+    const bool sh = a.shared != nullptr;
+    const int S = a.B * a.K;
+    const int shb = sh ? (a.B + kTokBlock - 1) / kTokBlock : 0;
+    const int n4 = (a.B * (a.H / 4) + kBlock - 1) / kBlock;
+    if (phases & 4) {
+      const bool full = a.I == NGI * kGroup;
+      const dim3 g1((shb + S) * (a.H / 128)), g2((shb + S) * (a.H / 256));
+      if (a.B <= kTokBlock && full)
+        hipLaunchKernelGGL((k_g3<BITS, NGI, 1, true>), g1, dim3(kGThreads), 0, s, a);
+      else if (a.B <= kTokBlock)
+        hipLaunchKernelGGL((k_g3<BITS, NGI, 1, false>), g1, dim3(kGThreads), 0, s, a);
+      else if (full)
+        hipLaunchKernelGGL((k_g3<BITS, NGI, 2, true>), g2, dim3(kGThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((k_g3<BITS, NGI, 2, false>), g2, dim3(kGThreads), 0, s, a);
+      hipLaunchKernelGGL(k_g4<BITS>, dim3(n4), dim3(kBlock), 0, s, a);
     }
+    return hipGetLastError();
   }
 };
 
 template <int BITS>
+hipError_t group_front(const GroupArgs &a, hipStream_t s, int phases) {
+  FMOE_NG_SWITCH(pad_groups(a.H / kGroup), GroupDispatch<BITS>::template front, a, s, phases)
+}
+
+template <int BITS>
 hipError_t group_b(const GroupArgs &a, hipStream_t s, int phases) {
-  FMOE_NG_SWITCH(a.H / kGroup, GroupDispatch<BITS>::template layer_h, a, s, phases)
+  const hipError_t e = group_front<BITS>(a, s, phases);
+  if (e != hipSuccess) return e;
+  FMOE_NG_SWITCH(pad_groups(a.I / kGroup), GroupDispatch<BITS>::template back, a, s, phases)
 }
 
 }  // namespace dev

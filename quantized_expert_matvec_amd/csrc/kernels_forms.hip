@@ -14,7 +14,8 @@
 //   3 table:     w_j = T[c_j] from a per-(row, group) table T[c] = c s + b that each
 //                lane writes to its own LDS row, then acc += w_j x_j: the GPU dequant
 //                lookup table that [P1] "Lo que descartaron" lists as slower.
-// One row per 64 / NG lanes, a lane per group, and 1, 2 or 4 row iterations per
+// One row per 64 / NGP lanes (NGP: the groups per row rounded up to a power of
+// two), a lane per group, and 1, 2 or 4 row iterations per
 // wavefront chosen by the matrix height, as in the library's matvec (form 2 is
 // that kernel); x staged once per workgroup.
 #include "forms.h"
@@ -70,65 +71,67 @@ __device__ __forceinline__ float partial_form(const Chunk<BITS> &c, uint32_t sb,
   }
 }
 
-template <int BITS, int NG, int ITERS, int FORM>
-__global__ __launch_bounds__(kBlock) void k_qmatvec_form(const uint8_t *__restrict__ blob, int rows,
+template <int BITS, int NGP, int ITERS, int FORM>
+__global__ __launch_bounds__(kBlock) void k_qmatvec_form(const uint8_t *__restrict__ blob, int ng, int rows,
                                                           const float *__restrict__ x, float *__restrict__ y) {
-  constexpr int RPI = kWave / NG;
-  __shared__ float xl[NG * kXPad];
+  constexpr int RPI = kWave / NGP;
+  __shared__ float xl[NGP * kXPad];
   __shared__ float lut[FORM == 3 ? kBlock * kLutStride : 1];
-  constexpr int X4 = (NG * 16 + kBlock - 1) / kBlock;
+  constexpr int X4 = (NGP * 16 + kBlock - 1) / kBlock;
   const int lane = lane_id();
   const int row0 = wave_id() * ITERS * RPI;
   Staged<X4> xst;
-  stage_load(x, NG * 16, xst);
-  RowLoads<BITS, NG, ITERS> L;
-  if (row0 < rows) L.issue(blob, rows, row0);
+  stage_load(x, ng * 16, xst);
+  RowLoads<BITS, NGP, ITERS> L;
+  if (row0 < rows) L.issue(blob, ng, rows, row0);
   __builtin_amdgcn_sched_barrier(0);
-  stage_store<X4, false>(xst, NG * 16, xl, nullptr);
+  stage_store<X4, false>(xst, ng * 16, xl, nullptr);
   __syncthreads();
   if (row0 >= rows) return;
   XSlice xs;
-  read_slice(xl, lane & (NG - 1), 1.f, xs);
+  read_slice(xl, min(lane & (NGP - 1), ng - 1), 1.f, xs);
 #pragma unroll
   for (int i = 0; i < ITERS; ++i) {
-    const float p = seg_reduce<NG>(
-        partial_form<BITS, FORM>(L.c[i], L.sb[i], xs, FORM == 3 ? lut + threadIdx.x * kLutStride : lut));
-    const int row = row0 + i * RPI + lane / NG;
-    if (seg_last<NG>(lane) && row < rows) y[row] = p;
+    const float p = seg_reduce<NGP>(
+        L.live ? partial_form<BITS, FORM>(L.c[i], L.sb[i], xs, FORM == 3 ? lut + threadIdx.x * kLutStride : lut)
+               : 0.f);
+    const int row = row0 + i * RPI + lane / NGP;
+    if (seg_last<NGP>(lane) && row < rows) y[row] = p;
   }
 }
 
-template <int BITS, int NG, int ITERS>
-hipError_t launch_it(int form, const uint8_t *blob, int rows, const float *x, float *y, hipStream_t s) {
-  const long iters = (rows + kWave / NG - 1) / (kWave / NG);
+template <int BITS, int NGP, int ITERS>
+hipError_t launch_it(int form, const uint8_t *blob, int ng, int rows, const float *x, float *y, hipStream_t s) {
+  const long iters = (rows + kWave / NGP - 1) / (kWave / NGP);
   const dim3 grid(blocks_for((iters + ITERS - 1) / ITERS));
   const dim3 block(kBlock);
   switch (form) {
-    case 0: hipLaunchKernelGGL((k_qmatvec_form<BITS, NG, ITERS, 0>), grid, block, 0, s, blob, rows, x, y); break;
-    case 1: hipLaunchKernelGGL((k_qmatvec_form<BITS, NG, ITERS, 1>), grid, block, 0, s, blob, rows, x, y); break;
-    case 2: hipLaunchKernelGGL((k_qmatvec_form<BITS, NG, ITERS, 2>), grid, block, 0, s, blob, rows, x, y); break;
-    default: hipLaunchKernelGGL((k_qmatvec_form<BITS, NG, ITERS, 3>), grid, block, 0, s, blob, rows, x, y); break;
+    case 0: hipLaunchKernelGGL((k_qmatvec_form<BITS, NGP, ITERS, 0>), grid, block, 0, s, blob, ng, rows, x, y); break;
+    case 1: hipLaunchKernelGGL((k_qmatvec_form<BITS, NGP, ITERS, 1>), grid, block, 0, s, blob, ng, rows, x, y); break;
+    case 2: hipLaunchKernelGGL((k_qmatvec_form<BITS, NGP, ITERS, 2>), grid, block, 0, s, blob, ng, rows, x, y); break;
+    default: hipLaunchKernelGGL((k_qmatvec_form<BITS, NGP, ITERS, 3>), grid, block, 0, s, blob, ng, rows, x, y); break;
   }
   return hipGetLastError();
 }
 
 // row iterations per wavefront as the library's matvec chooses them
-template <int BITS, int NG>
-hipError_t launch_ng(int form, const uint8_t *blob, int rows, const float *x, float *y, hipStream_t s) {
-  const long iters = (rows + kWave / NG - 1) / (kWave / NG);
-  if (iters >= 4L * 4096) return launch_it<BITS, NG, 4>(form, blob, rows, x, y, s);
-  if (iters >= 2L * 2048) return launch_it<BITS, NG, 2>(form, blob, rows, x, y, s);
-  return launch_it<BITS, NG, 1>(form, blob, rows, x, y, s);
+template <int BITS, int NGP>
+hipError_t launch_ng(int form, const uint8_t *blob, int ng, int rows, const float *x, float *y, hipStream_t s) {
+  const long iters = (rows + kWave / NGP - 1) / (kWave / NGP);
+  if (iters >= 4L * 4096) return launch_it<BITS, NGP, 4>(form, blob, ng, rows, x, y, s);
+  if (iters >= 2L * 2048) return launch_it<BITS, NGP, 2>(form, blob, ng, rows, x, y, s);
+  return launch_it<BITS, NGP, 1>(form, blob, ng, rows, x, y, s);
 }
 
 template <int BITS>
 hipError_t launch_bits(int form, const uint8_t *blob, int rows, int cols, const float *x, float *y, hipStream_t s) {
-  switch (cols / kGroup) {
-    case 4: return launch_ng<BITS, 4>(form, blob, rows, x, y, s);
-    case 8: return launch_ng<BITS, 8>(form, blob, rows, x, y, s);
-    case 16: return launch_ng<BITS, 16>(form, blob, rows, x, y, s);
-    case 32: return launch_ng<BITS, 32>(form, blob, rows, x, y, s);
-    case 64: return launch_ng<BITS, 64>(form, blob, rows, x, y, s);
+  const int ng = cols / kGroup;
+  switch (pad_groups(ng)) {
+    case 4: return launch_ng<BITS, 4>(form, blob, ng, rows, x, y, s);
+    case 8: return launch_ng<BITS, 8>(form, blob, ng, rows, x, y, s);
+    case 16: return launch_ng<BITS, 16>(form, blob, ng, rows, x, y, s);
+    case 32: return launch_ng<BITS, 32>(form, blob, ng, rows, x, y, s);
+    case 64: return launch_ng<BITS, 64>(form, blob, ng, rows, x, y, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -142,54 +142,60 @@ __device__ __forceinline__ void trace_mark(uint64_t *tr, int slot) {
 
 // ------------------------------------------------------------------ row work
 
-// Weight registers of ITERS row iterations of one wavefront (NG lanes per row).
-template <int BITS, int NG, int ITERS>
+// Weight registers of ITERS row iterations of one wavefront (a segment of NGP
+// lanes per row of ng groups, ng <= NGP; the lanes past ng add 0, see pad_groups).
+template <int BITS, int NGP, int ITERS>
 struct RowLoads {
   Chunk<BITS> c[ITERS];
   uint32_t sb[ITERS];
-  // rows row0 + i*RPI + sub (clamped to rows-1) of a matrix with records of RB bytes
-  __device__ __forceinline__ void issue(const uint8_t *__restrict__ blob, int rows, int row0) {
-    constexpr int RPI = kWave / NG;
-    constexpr size_t RB = (size_t)NG * gbytes<BITS>();
+  bool live;  // this lane's group exists
+  // rows row0 + i*RPI + sub (clamped to rows-1) of a matrix of ng-group records
+  __device__ __forceinline__ void issue(const uint8_t *__restrict__ blob, int ng, int rows, int row0) {
+    constexpr int RPI = kWave / NGP;
+    const size_t RB = (size_t)ng * gbytes<BITS>();
     const int lane = lane_id();
-    const int g = lane & (NG - 1), sub = lane / NG;
+    const int g = lane & (NGP - 1), sub = lane / NGP;
+    live = g < ng;
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) {
       const int row = min(row0 + i * RPI + sub, rows - 1);
-      load_group<BITS, NG>(blob + (size_t)row * RB, g, c[i], sb[i]);
+      load_group<BITS>(blob + (size_t)row * RB, ng, min(g, ng - 1), c[i], sb[i]);
     }
     __builtin_amdgcn_sched_barrier(0);  // (as in PairLoads::issue)
   }
   // y[row] = alpha * row . x
   __device__ __forceinline__ void finish(const XSlice &xs, float *__restrict__ y, int rows, int row0,
                                          float alpha) const {
-    constexpr int RPI = kWave / NG;
+    constexpr int RPI = kWave / NGP;
     const int lane = lane_id();
-    const int sub = lane / NG;
+    const int sub = lane / NGP;
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) {
-      const float p = seg_reduce<NG>(group_partial<BITS>(c[i], sb[i], xs));
+      const float p = seg_reduce<NGP>(live ? group_partial<BITS>(c[i], sb[i], xs) : 0.f);
       const int row = row0 + i * RPI + sub;
-      if (seg_last<NG>(lane) && row < rows) y[row] = alpha * p;
+      if (seg_last<NGP>(lane) && row < rows) y[row] = alpha * p;
     }
   }
 };
 
-// Row pairs of an interleaved gate/up region (records 2r and 2r+1).
-template <int BITS, int NG, int ITERS>
+// Row pairs of an interleaved gate/up region (records 2r and 2r+1), rows of ng groups.
+template <int BITS, int NGP, int ITERS>
 struct PairLoads {
   Chunk<BITS> cg[ITERS], cu[ITERS];
   uint32_t sg[ITERS], su[ITERS];
-  __device__ __forceinline__ void issue(const uint8_t *__restrict__ gu, int pair0) {
-    constexpr int RPI = kWave / NG;
-    constexpr size_t RB = (size_t)NG * gbytes<BITS>();
+  bool live;  // this lane's group exists
+  __device__ __forceinline__ void issue(const uint8_t *__restrict__ gu, int ng, int pair0) {
+    constexpr int RPI = kWave / NGP;
+    const size_t RB = (size_t)ng * gbytes<BITS>();
     const int lane = lane_id();
-    const int g = lane & (NG - 1), sub = lane / NG;
+    const int g = lane & (NGP - 1), sub = lane / NGP;
+    live = g < ng;
+    const int gl = min(g, ng - 1);
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) {
       const uint8_t *rec = gu + (size_t)(2 * (pair0 + i * RPI + sub)) * RB;
-      load_group<BITS, NG>(rec, g, cg[i], sg[i]);
-      load_group<BITS, NG>(rec + RB, g, cu[i], su[i]);
+      load_group<BITS>(rec, ng, gl, cg[i], sg[i]);
+      load_group<BITS>(rec + RB, ng, gl, cu[i], su[i]);
     }
     // every load goes out before the first use of a loaded word (otherwise the
     // scheduler can hoist that use between the loads, and its wait stalls the rest)
@@ -197,26 +203,26 @@ struct PairLoads {
   }
   // h[r] = silu(gate_r . x) * (up_r . x)
   __device__ __forceinline__ void finish(const XSlice &xs, float *__restrict__ h, int pair0) const {
-    constexpr int RPI = kWave / NG;
+    constexpr int RPI = kWave / NGP;
     const int lane = lane_id();
-    const int sub = lane / NG;
+    const int sub = lane / NGP;
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) {
-      const float pg = seg_reduce<NG>(group_partial<BITS>(cg[i], sg[i], xs));
-      const float pu = seg_reduce<NG>(group_partial<BITS>(cu[i], su[i], xs));
-      if (seg_last<NG>(lane)) h[pair0 + i * RPI + sub] = silu(pg) * pu;
+      const float pg = seg_reduce<NGP>(live ? group_partial<BITS>(cg[i], sg[i], xs) : 0.f);
+      const float pu = seg_reduce<NGP>(live ? group_partial<BITS>(cu[i], su[i], xs) : 0.f);
+      if (seg_last<NGP>(lane)) h[pair0 + i * RPI + sub] = silu(pg) * pu;
     }
   }
   // the same from the digit form of x
   __device__ __forceinline__ void finish_dig(const XDig &xd, float *__restrict__ h, int pair0) const {
-    constexpr int RPI = kWave / NG;
+    constexpr int RPI = kWave / NGP;
     const int lane = lane_id();
-    const int sub = lane / NG;
+    const int sub = lane / NGP;
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) {
-      const float pg = seg_reduce<NG>(group_partial_dig<BITS>(cg[i], sg[i], xd));
-      const float pu = seg_reduce<NG>(group_partial_dig<BITS>(cu[i], su[i], xd));
-      if (seg_last<NG>(lane)) h[pair0 + i * RPI + sub] = silu(pg) * pu;
+      const float pg = seg_reduce<NGP>(live ? group_partial_dig<BITS>(cg[i], sg[i], xd) : 0.f);
+      const float pu = seg_reduce<NGP>(live ? group_partial_dig<BITS>(cu[i], su[i], xd) : 0.f);
+      if (seg_last<NGP>(lane)) h[pair0 + i * RPI + sub] = silu(pg) * pu;
     }
   }
 };
@@ -401,48 +407,56 @@ __device__ __forceinline__ void block_topk(const float *lg, int E, int K, int *s
 
 // ------------------------------------------------------------------ standalone kernels
 
-template <int BITS, int NG, int ITERS>
-__global__ __launch_bounds__(kBlock) void k_qmatvec(const uint8_t *__restrict__ blob, int rows,
+template <int BITS, int NGP, int ITERS>
+__global__ __launch_bounds__(kBlock) void k_qmatvec(const uint8_t *__restrict__ blob, int ng, int rows,
                                                      const float *__restrict__ x, float *__restrict__ y) {
-  __shared__ float xl[NG * kXPad];
-  constexpr int X4 = (NG * 16 + kBlock - 1) / kBlock;
-  const int row0 = wave_id() * ITERS * (kWave / NG);
+  __shared__ float xl[NGP * kXPad];
+  constexpr int X4 = (NGP * 16 + kBlock - 1) / kBlock;
+  const int row0 = wave_id() * ITERS * (kWave / NGP);
   Staged<X4> xst;
-  stage_load(x, NG * 16, xst);
-  RowLoads<BITS, NG, ITERS> L;
-  if (row0 < rows) L.issue(blob, rows, row0);
+  stage_load(x, ng * 16, xst);
+  RowLoads<BITS, NGP, ITERS> L;
+  if (row0 < rows) L.issue(blob, ng, rows, row0);
   __builtin_amdgcn_sched_barrier(0);
-  stage_store<X4, false>(xst, NG * 16, xl, nullptr);
+  stage_store<X4, false>(xst, ng * 16, xl, nullptr);
   __syncthreads();
   if (row0 >= rows) return;
   XSlice xs;
-  read_slice(xl, lane_id() & (NG - 1), 1.f, xs);
+  read_slice(xl, min(lane_id() & (NGP - 1), ng - 1), 1.f, xs);
   L.finish(xs, y, rows, row0, 1.f);
 }
 
-template <int BITS, int NG, int ITERS>
-__global__ __launch_bounds__(kBlock) void k_expert_gateup(const uint8_t *__restrict__ gu, int inter,
+template <int BITS, int NGP, int ITERS>
+__global__ __launch_bounds__(kBlock) void k_expert_gateup(const uint8_t *__restrict__ gu, int ng, int inter,
                                                            const float *__restrict__ x, float *__restrict__ h) {
-  __shared__ float xl[NG * kXPad];
-  constexpr int X4 = (NG * 16 + kBlock - 1) / kBlock;
-  const int pair0 = wave_id() * ITERS * (kWave / NG);
+  __shared__ float xl[NGP * kXPad];
+  constexpr int X4 = (NGP * 16 + kBlock - 1) / kBlock;
+  const int pair0 = wave_id() * ITERS * (kWave / NGP);
   Staged<X4> xst;
-  stage_load(x, NG * 16, xst);
-  PairLoads<BITS, NG, ITERS> P;
-  if (pair0 < inter) P.issue(gu, pair0);
+  stage_load(x, ng * 16, xst);
+  PairLoads<BITS, NGP, ITERS> P;
+  if (pair0 < inter) P.issue(gu, ng, pair0);
   __builtin_amdgcn_sched_barrier(0);
-  stage_store<X4, false>(xst, NG * 16, xl, nullptr);
+  stage_store<X4, false>(xst, ng * 16, xl, nullptr);
   __syncthreads();
   if (pair0 >= inter) return;
   XSlice xs;
-  read_slice(xl, lane_id() & (NG - 1), 1.f, xs);
+  read_slice(xl, min(lane_id() & (NGP - 1), ng - 1), 1.f, xs);
   P.finish(xs, h, pair0);
 }
 
 // ------------------------------------------------------------------ layer kernels
 
-constexpr int kP2GateUpIters = 2;  // gate/up pair iterations per wavefront (routed and shared)
-constexpr int kP3Iters = 4;        // routed down row iterations per wavefront
+// gate/up pair iterations per wavefront (routed and shared) and routed down row
+// iterations per wavefront, by code width
+template <int BITS>
+constexpr int gateup_iters() {
+  return 2;
+}
+template <int BITS>
+constexpr int down_iters() {
+  return 4;
+}
 constexpr int kP3Block = 256;      // threads per down + combine workgroup
 constexpr int kP3Waves = kP3Block / kWave;
 
@@ -456,6 +470,7 @@ struct Phase1Args {
   float *logits;
   float *sigma;
   uint32_t *xdig;     // [hidden/64][kDigStride] x in digit form
+  int ng;             // hidden / 64
   int n_prep_blocks;  // workgroups before the router's: x in digit form, then the gate
   uint64_t *trace;
 };
@@ -490,26 +505,26 @@ __device__ __forceinline__ void write_digits(const float *xl, int g, float inv, 
 }
 
 // Phase 1: the router. Each fp32 router row is split over router_split()
-// wavefronts of a workgroup (half h: lane l covers columns 4l + 256t + 0..3 for
-// t in [h NT/2, (h+1) NT/2)), so that the 8 MB of rows spread over every compute
-// unit (512 rows: one workgroup per compute unit); the halves' sums are added in
-// order. The workgroups before the router's write x in digit form for the gate/up
-// kernel, and the last of them computes the shared expert's gate sigmoid(g . x).
-template <int NGH>
+// wavefronts of a workgroup (part h: lane l covers columns 4l + 256t + 0..3 for
+// the chunks t in [h c, (h+1) c), c = ceil(nt / SPLIT), nt = hidden / 256), so
+// that the 8 MB of rows spread over every compute unit (512 rows: one workgroup
+// per compute unit); the parts' sums are added in order. The workgroups before
+// the router's write x in digit form for the gate/up kernel, and the last of them
+// computes the shared expert's gate sigmoid(g . x).
+template <int NGHP>
 constexpr int router_split() {
-  return NGH / 4 >= 2 ? 2 : 1;
+  return NGHP / 4 >= 2 ? 2 : 1;
 }
-template <int NGH>
+template <int NGHP>
 __global__ __launch_bounds__(kBlock) void k_phase1(const Phase1Args a) {
-  constexpr int NT = NGH / 4;  // hidden / 256
-  constexpr int H = NGH * kGroup;
-  constexpr int X4 = (NGH * 16 + kBlock - 1) / kBlock;
-  constexpr int SPLIT = router_split<NGH>();
-  constexpr int NTW = NT / SPLIT;  // float4 per lane of this wavefront's part of the row
-  __shared__ float xl[NGH * kXPad];
+  constexpr int X4 = (NGHP * 16 + kBlock - 1) / kBlock;
+  constexpr int SPLIT = router_split<NGHP>();
+  constexpr int NTW = NGHP / 4 / SPLIT;  // float4 per lane of a wavefront's part of the row, at most
+  __shared__ float xl[NGHP * kXPad];
   __shared__ float part[kWavesPerBlock];
   __shared__ float dpart[kWavesPerBlock];
   __shared__ uint32_t ybuf[kWavesPerBlock][kWave];
+  const int ng = a.ng, H = ng * kGroup, nt = ng / 4;
   const int lane = lane_id();
   const bool rms = a.rms_eps >= 0.f;
   trace_mark(a.trace, 0);
@@ -522,14 +537,14 @@ __global__ __launch_bounds__(kBlock) void k_phase1(const Phase1Args a) {
     // unit. (The second vector's loads are unconditional: the gate vector in the
     // gate's workgroup, x again in the others.)
     const int g = (int)blockIdx.x * kWavesPerBlock + wv;
-    const bool gate = a.gvec != nullptr && (int)blockIdx.x == (NGH + kWavesPerBlock - 1) / kWavesPerBlock;
+    const bool gate = a.gvec != nullptr && (int)blockIdx.x == (ng + kWavesPerBlock - 1) / kWavesPerBlock;
     Staged<X4> xst, gst;
-    stage_load(a.x, NGH * 16, xst);
-    stage_load(gate ? a.gvec : a.x, NGH * 16, gst);
+    stage_load(a.x, ng * 16, xst);
+    stage_load(gate ? a.gvec : a.x, ng * 16, gst);
     if (rms)
-      stage_store<X4, true>(xst, NGH * 16, xl, part);
+      stage_store<X4, true>(xst, ng * 16, xl, part);
     else
-      stage_store<X4, false>(xst, NGH * 16, xl, part);
+      stage_store<X4, false>(xst, ng * 16, xl, part);
     __syncthreads();
     const float inv = rms ? rms_inv(part, H, a.rms_eps) : 1.f;
     if (gate) {  // (uniform over the workgroup)
@@ -537,7 +552,7 @@ __global__ __launch_bounds__(kBlock) void k_phase1(const Phase1Args a) {
 #pragma unroll
       for (int k = 0; k < X4; ++k) {
         const int f = threadIdx.x + kBlock * k;
-        if (f < NGH * 16) {
+        if (f < ng * 16) {
           const float4 xv = *reinterpret_cast<const float4 *>(&xl[lds_index(4 * f)]);
           const float4 gv = gst.v[k];
           acc = fmaf(gv.x, xv.x, acc);
@@ -555,7 +570,7 @@ __global__ __launch_bounds__(kBlock) void k_phase1(const Phase1Args a) {
         for (int i = 1; i < kWavesPerBlock; ++i) d += dpart[i];
         *a.sigma = 1.f / (1.f + expf(-d * inv));
       }
-    } else if (g < NGH) {
+    } else if (g < ng) {
       if (a.bits == 4)
         write_digits<4>(xl, g, inv, ybuf[wv], a.xdig);
       else
@@ -568,28 +583,32 @@ __global__ __launch_bounds__(kBlock) void k_phase1(const Phase1Args a) {
   const int half = wv % SPLIT;
   const int row = ((int)blockIdx.x - a.n_prep_blocks) * (kWavesPerBlock / SPLIT) + wv / SPLIT;
   const int rr = min(row, n_rows - 1);
-  const float *src = a.router + (size_t)rr * H + 256 * NTW * half;
+  const int per = (nt + SPLIT - 1) / SPLIT;  // chunks of 256 columns per part
+  const int t0 = per * half, tn = min(per, nt - t0);  // this part's chunks (tn >= 1)
+  const float4 *src = reinterpret_cast<const float4 *>(a.router + (size_t)rr * H);
   Staged<X4> xst;
-  stage_load(a.x, NGH * 16, xst);
+  stage_load(a.x, ng * 16, xst);
   float4 w[NTW];
 #pragma unroll
-  for (int t = 0; t < NTW; ++t) w[t] = reinterpret_cast<const float4 *>(src)[lane + 64 * t];
+  for (int t = 0; t < NTW; ++t) w[t] = src[lane + 64 * (t0 + min(t, tn - 1))];
   __builtin_amdgcn_sched_barrier(0);
   if (rms)
-    stage_store<X4, true>(xst, NGH * 16, xl, part);
+    stage_store<X4, true>(xst, ng * 16, xl, part);
   else
-    stage_store<X4, false>(xst, NGH * 16, xl, part);
+    stage_store<X4, false>(xst, ng * 16, xl, part);
   __syncthreads();
   trace_mark(a.trace, 1);
   const float inv = rms ? rms_inv(part, H, a.rms_eps) : 1.f;
   float acc = 0.f;
 #pragma unroll
   for (int t = 0; t < NTW; ++t) {
-    const float4 xv = *reinterpret_cast<const float4 *>(&xl[lds_index(4 * lane + 256 * (t + NTW * half))]);
-    acc = fmaf(w[t].x, xv.x * inv, acc);
-    acc = fmaf(w[t].y, xv.y * inv, acc);
-    acc = fmaf(w[t].z, xv.z * inv, acc);
-    acc = fmaf(w[t].w, xv.w * inv, acc);
+    if (t < tn) {  // (uniform)
+      const float4 xv = *reinterpret_cast<const float4 *>(&xl[lds_index(4 * lane + 256 * (t0 + t))]);
+      acc = fmaf(w[t].x, xv.x * inv, acc);
+      acc = fmaf(w[t].y, xv.y * inv, acc);
+      acc = fmaf(w[t].z, xv.z * inv, acc);
+      acc = fmaf(w[t].w, xv.w * inv, acc);
+    }
   }
   float d = seg_reduce<kWave>(acc);
   if constexpr (SPLIT > 1) {
@@ -609,6 +628,7 @@ struct Phase2Args {
   const uint8_t *bank;
   size_t stride;
   const uint32_t *xdig;  // x in digit form, [hidden/64][kDigStride]
+  int ng;                // hidden / 64
   int I;
   float *h_routed;
   int32_t *ws_idx;
@@ -628,12 +648,12 @@ struct Phase2Args {
 // depend on the routing, so its weights stream while the routed blocks are still
 // choosing. x arrives in the digit form the router kernel wrote (RMS factor
 // included), so this kernel reads no raw x.
-template <int BITS, int NGH>
+template <int BITS, int NGHP>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void k_phase2(const Phase2Args a) {
-  constexpr int RPIH = kWave / NGH;
-  constexpr int NF4 = NGH * kDigStride / 4;  // 16-byte units of the digit form
-  constexpr int D4 = (NF4 + kBlock - 1) / kBlock;
-  __shared__ uint32_t xdl[NGH * kDigStride];
+  constexpr int RPIH = kWave / NGHP;
+  constexpr int D4 = (NGHP * kDigStride / 4 + kBlock - 1) / kBlock;
+  const int NF4 = a.ng * kDigStride / 4;  // 16-byte units of the digit form
+  __shared__ uint32_t xdl[NGHP * kDigStride];
   __shared__ __align__(16) float lg[kMaxExperts];
   __shared__ int sidx[kMaxTopK];
   __shared__ float sw[kMaxTopK];
@@ -691,10 +711,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     trace_mark(a.trace, 2);
     const int wv = blockIdx.x * kWavesPerBlock + wave_in_block();
     const int slot = min(wv / a.waves_per_slot, a.K - 1);
-    const int pair0 = (wv % a.waves_per_slot) * kP2GateUpIters * RPIH;
+    const int pair0 = (wv % a.waves_per_slot) * gateup_iters<BITS>() * RPIH;
     const bool active = wv < a.waves_per_slot * a.K;
-    PairLoads<BITS, NGH, kP2GateUpIters> P;
-    if (active) P.issue(a.bank + (size_t)sidx[slot] * a.stride, pair0);
+    PairLoads<BITS, NGHP, gateup_iters<BITS>()> P;
+    if (active) P.issue(a.bank + (size_t)sidx[slot] * a.stride, a.ng, pair0);
     if (wv == (a.K - 1) * a.waves_per_slot && lane < a.K) {
       const int sel = sidx[lane];
       const float ws = sw[lane];
@@ -705,7 +725,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     }
     if (active) {
       XDig xd;
-      read_digits(xdl, lane & (NGH - 1), xd);
+      read_digits(xdl, min(lane & (NGHP - 1), a.ng - 1), xd);
       P.finish_dig(xd, a.h_routed + (size_t)slot * a.I, pair0);
     }
     trace_mark(a.trace, 3);
@@ -713,20 +733,20 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   }
   // shared expert gate/up
   const int wv = (blockIdx.x - a.n_routed_blocks) * kWavesPerBlock + wave_in_block();
-  const int pair0 = wv * kP2GateUpIters * RPIH;
+  const int pair0 = wv * gateup_iters<BITS>() * RPIH;
   // x first (its loads complete before the weights', so the staging does not
   // wait for them), then the weights
   Staged<D4> xst;
   stage_load(xsrc, NF4, xst);
   __builtin_amdgcn_sched_barrier(0);
-  PairLoads<BITS, NGH, kP2GateUpIters> P;
-  if (pair0 < a.I) P.issue(a.shared_gu, pair0);
+  PairLoads<BITS, NGHP, gateup_iters<BITS>()> P;
+  if (pair0 < a.I) P.issue(a.shared_gu, a.ng, pair0);
   stage_copy(xst, NF4, xdl);
   __syncthreads();
   trace_mark(a.trace, 1);
   if (pair0 < a.I) {
     XDig xd;
-    read_digits(xdl, lane & (NGH - 1), xd);
+    read_digits(xdl, min(lane & (NGHP - 1), a.ng - 1), xd);
     P.finish_dig(xd, a.h_shared, pair0);
   }
   trace_mark(a.trace, 3);
@@ -751,26 +771,30 @@ struct Phase3Args {
 // Phase 3: out_i = residual_i + sum_k w_k (down_k . h_k)_i + sigma (down_s . h_s)_i.
 // Routed: lanes are (slot k, group j) pairs, so one cross-lane sum adds the K
 // experts' weighted partials of a row together; each lane keeps its slot's h
-// slice. KPAD = top_k rounded up to a power of two (slots beyond top_k stay
-// idle). The routed h vectors are staged in LDS when they fit (KPAD * inter <=
-// 8192). Shared: the same wavefront's rows, NGI lanes per row; its weights do not
-// depend on the routing and are requested first. A wavefront passes its shared
-// results from the shared lanes to the combining lanes through LDS.
-template <int BITS, int NGI, int KPAD>
+// slice. KPAD = top_k rounded up to a power of two, NGIP = the inter groups ngi
+// rounded up to a power of two (lanes of slots past top_k or groups past ngi stay
+// idle). The routed h vectors are staged in LDS when they fit (KPAD * NGIP <=
+// 128), group j of slot k in row k ngi + j. Shared: the same wavefront's rows,
+// NGIP lanes per row; its weights do not depend on the routing and are requested
+// first. A wavefront passes its shared results from the shared lanes to the
+// combining lanes through LDS.
+template <int BITS, int NGIP, int KPAD>
 __global__ __launch_bounds__(kP3Block) void k_phase3(const Phase3Args a) {
-  constexpr int SLOTS = KPAD * NGI;
+  constexpr int kP3Iters = down_iters<BITS>();
+  constexpr int SLOTS = KPAD * NGIP;
   constexpr int SEG = SLOTS < kWave ? SLOTS : kWave;  // lanes per row
   constexpr int SPL = SLOTS / SEG;                     // slots per lane
   constexpr int RPI = kWave / SEG;
   constexpr int RPW = kP3Iters * RPI;                  // rows per wavefront
-  constexpr int RPII = kWave / NGI;                    // shared-down rows per iteration
+  constexpr int RPII = kWave / NGIP;                   // shared-down rows per iteration
   constexpr int SIT = (RPW + RPII - 1) / RPII;         // shared-down iterations
-  constexpr size_t RB = (size_t)NGI * gbytes<BITS>();
-  constexpr bool STAGE = KPAD * NGI <= 128;
-  __shared__ float hl[STAGE ? KPAD * NGI * kXPad : 1];
-  __shared__ float hs[NGI * kXPad];
-  __shared__ float hlsum[STAGE ? KPAD * NGI : 1];  // per-group sums of the staged h
-  __shared__ float hssum[NGI];
+  constexpr bool STAGE = KPAD * NGIP <= 128;
+  const int ngi = a.I / kGroup;
+  const size_t RB = (size_t)ngi * gbytes<BITS>();
+  __shared__ float hl[STAGE ? KPAD * NGIP * kXPad : 1];
+  __shared__ float hs[NGIP * kXPad];
+  __shared__ float hlsum[STAGE ? KPAD * NGIP : 1];  // per-group sums of the staged h
+  __shared__ float hssum[NGIP];
   __shared__ float dsh[kP3Waves * RPW];
   trace_mark(a.trace, 0);
   const int lane = lane_id();
@@ -787,9 +811,9 @@ __global__ __launch_bounds__(kP3Block) void k_phase3(const Phase3Args a) {
 #pragma unroll
   for (int m = 0; m < SPL; ++m) {
     const int slot = (lane % SEG) + kWave * m;
-    const int k = slot / NGI;
-    grp[m] = slot % NGI;
-    act[m] = k < a.K && row0 < a.H;
+    const int k = slot / NGIP;
+    grp[m] = min(slot % NGIP, ngi - 1);
+    act[m] = k < a.K && slot % NGIP < ngi && row0 < a.H;
     kk[m] = k < a.K ? k : 0;
     sel[m] = a.idx[kk[m]];
     wk[m] = k < a.K ? a.w[kk[m]] : 0.f;
@@ -798,25 +822,27 @@ __global__ __launch_bounds__(kP3Block) void k_phase3(const Phase3Args a) {
 #pragma unroll
   for (int i = 0; i < kP3Iters; ++i) res[i] = a.residual[min(row0 + i * RPI + sub, a.H - 1)];
   const float sig = *a.sigma;  // (a workspace value; unused without a shared expert)
-  constexpr int H4 = STAGE ? (KPAD * NGI * 16 + kP3Block - 1) / kP3Block : 1;
-  constexpr int S4 = (NGI * 16 + kP3Block - 1) / kP3Block;
+  constexpr int H4 = STAGE ? (KPAD * NGIP * 16 + kP3Block - 1) / kP3Block : 1;
+  constexpr int S4 = (NGIP * 16 + kP3Block - 1) / kP3Block;
   Staged<H4> hst;
   if constexpr (STAGE) stage_load<H4, kP3Block>(a.h_routed, a.K * a.I / 4, hst);
   // without a shared expert these loads read the routed expert 0 instead (valid
   // memory, results unused): unconditional loads keep the memory-counter waits exact
   Staged<S4> sst;
-  stage_load<S4, kP3Block>(sh ? a.h_shared : a.h_routed, NGI * 16, sst);
+  stage_load<S4, kP3Block>(sh ? a.h_shared : a.h_routed, ngi * 16, sst);
   __builtin_amdgcn_sched_barrier(0);  // every h load goes out before any weight load
   const uint8_t *sdown = sh ? a.shared_down : a.bank + a.gu_bytes;
-  // shared rows: NGI lanes per row; with fewer rows per wavefront than a load
+  // shared rows: NGIP lanes per row; with fewer rows per wavefront than a load
   // covers, the spare lanes repeat this wavefront's rows (the same cache lines)
-  const int ssub = RPW < RPII ? (lane / NGI) % RPW : lane / NGI, sg = lane & (NGI - 1);
+  const int ssub = RPW < RPII ? (lane / NGIP) % RPW : lane / NGIP;
+  const int sg = min(lane & (NGIP - 1), ngi - 1);
+  const bool slive = (lane & (NGIP - 1)) < ngi;
   Chunk<BITS> cs[SIT];
   uint32_t ss[SIT];
 #pragma unroll
   for (int q = 0; q < SIT; ++q) {
     const int row = min(row0 + q * RPII + ssub, a.H - 1);
-    load_group<BITS, NGI>(sdown + (size_t)row * RB, sg, cs[q], ss[q]);
+    load_group<BITS>(sdown + (size_t)row * RB, ngi, sg, cs[q], ss[q]);
   }
   __builtin_amdgcn_sched_barrier(0);  // the shared rows go out before the routing is needed
   const uint8_t *base[SPL];
@@ -832,11 +858,11 @@ __global__ __launch_bounds__(kP3Block) void k_phase3(const Phase3Args a) {
     const int row = min(row0 + i * RPI + sub, a.H - 1);
     // unconditional (inactive slots reload slot 0's rows, unused), as above
 #pragma unroll
-    for (int m = 0; m < SPL; ++m) load_group<BITS, NGI>(base[m] + (size_t)row * RB, grp[m], c[i][m], sb[i][m]);
+    for (int m = 0; m < SPL; ++m) load_group<BITS>(base[m] + (size_t)row * RB, ngi, grp[m], c[i][m], sb[i][m]);
   }
   __builtin_amdgcn_sched_barrier(0);  // the h vectors were requested before the weights
   if constexpr (STAGE) stage_store_gsum<H4, kP3Block>(hst, a.K * a.I / 4, hl, hlsum);
-  stage_store_gsum<S4, kP3Block>(sst, NGI * 16, hs, hssum);
+  stage_store_gsum<S4, kP3Block>(sst, ngi * 16, hs, hssum);
   __syncthreads();
   trace_mark(a.trace, 1);
   if (row0 >= a.H) return;
@@ -845,15 +871,15 @@ __global__ __launch_bounds__(kP3Block) void k_phase3(const Phase3Args a) {
     read_slice_sum(hs, sg, hssum[sg], xs);
 #pragma unroll
     for (int q = 0; q < SIT; ++q) {
-      const float p = seg_reduce<NGI>(group_partial<BITS>(cs[q], ss[q], xs));
+      const float p = seg_reduce<NGIP>(slive ? group_partial<BITS>(cs[q], ss[q], xs) : 0.f);
       const int r = q * RPII + ssub;  // row within this wavefront's rows
-      if (seg_last<NGI>(lane) && r < RPW) dsh[wave_in_block() * RPW + r] = sig * p;
+      if (seg_last<NGIP>(lane) && r < RPW) dsh[wave_in_block() * RPW + r] = sig * p;
     }
   }
   XSlice xs[SPL];
   if constexpr (STAGE) {
 #pragma unroll
-    for (int m = 0; m < SPL; ++m) read_slice_sum(hl, kk[m] * NGI + grp[m], hlsum[kk[m] * NGI + grp[m]], xs[m]);
+    for (int m = 0; m < SPL; ++m) read_slice_sum(hl, kk[m] * ngi + grp[m], hlsum[kk[m] * ngi + grp[m]], xs[m]);
   } else {
 #pragma unroll
     for (int m = 0; m < SPL; ++m) load_xslice(a.h_routed + (size_t)kk[m] * a.I + kGroup * grp[m], xs[m]);
@@ -889,59 +915,59 @@ __global__ __launch_bounds__(kP3Block) void k_phase3(const Phase3Args a) {
 
 inline int blocks_for(long waves) { return (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock); }
 
-// Launch geometry of one layer's three kernels.
-template <int NGH, int NGI>
+// Launch geometry of one layer's three kernels (NGH, NGI: the hidden and inter
+// group counts rounded up to powers of two).
+template <int BITS, int NGH, int NGI>
 struct LayerGeom {
-  static constexpr int RPIH = kWave / NGH, RPII = kWave / NGI;
-  int n1r, n1s, n2r, n2s, n3, wps, kpad;
-  size_t rbh, rbi;
+  static constexpr int RPIH = kWave / NGH;
+  int n1r, n2r, n2s, n3, wps, kpad;
   __host__ LayerGeom(const LayerArgs &L, int bits) {
     const bool sh = L.shared != nullptr;
-    rbh = (size_t)NGH * (bits == 4 ? 36 : 20);
-    rbi = (size_t)NGI * (bits == 4 ? 36 : 20);
     n1r = (L.E + kWavesPerBlock / router_split<NGH>() - 1) / (kWavesPerBlock / router_split<NGH>());
-    n1s = 0;
-    wps = (L.I / RPIH + kP2GateUpIters - 1) / kP2GateUpIters;
+    constexpr int GI = gateup_iters<BITS>(), DI = down_iters<BITS>();
+    wps = (L.I / RPIH + GI - 1) / GI;
     n2r = blocks_for((long)wps * L.K);
     n2s = sh ? blocks_for(wps) : 0;
     kpad = 1;
     while (kpad < L.K) kpad <<= 1;
     const int slots = kpad * NGI;
     const int seg = slots < kWave ? slots : kWave;
-    const long w3 = ((long)L.H / (kWave / seg) + kP3Iters - 1) / kP3Iters;
+    const long w3 = ((long)L.H / (kWave / seg) + DI - 1) / DI;
     n3 = (int)((w3 + kP3Waves - 1) / kP3Waves);
   }
 };
 
 template <int BITS>
 struct Dispatch {
-  template <int NG>
-  static hipError_t qmatvec(const uint8_t *blob, int rows, const float *x, float *y, hipStream_t s) {
-    constexpr int RPI = kWave / NG;
+  template <int NGP>
+  static hipError_t qmatvec(const uint8_t *blob, int ng, int rows, const float *x, float *y, hipStream_t s) {
+    constexpr int RPI = kWave / NGP;
     const long iters = (rows + RPI - 1) / RPI;
     // Enough wavefronts to cover every SIMD several times over; more rows per
     // wavefront only once there is work to spare.
     if (iters >= 4L * 4096)
-      hipLaunchKernelGGL((k_qmatvec<BITS, NG, 4>), dim3(blocks_for((iters + 3) / 4)), dim3(kBlock), 0, s, blob, rows,
-                         x, y);
+      hipLaunchKernelGGL((k_qmatvec<BITS, NGP, 4>), dim3(blocks_for((iters + 3) / 4)), dim3(kBlock), 0, s, blob, ng,
+                         rows, x, y);
     else if (iters >= 2L * 2048)
-      hipLaunchKernelGGL((k_qmatvec<BITS, NG, 2>), dim3(blocks_for((iters + 1) / 2)), dim3(kBlock), 0, s, blob, rows,
-                         x, y);
+      hipLaunchKernelGGL((k_qmatvec<BITS, NGP, 2>), dim3(blocks_for((iters + 1) / 2)), dim3(kBlock), 0, s, blob, ng,
+                         rows, x, y);
     else
-      hipLaunchKernelGGL((k_qmatvec<BITS, NG, 1>), dim3(blocks_for(iters)), dim3(kBlock), 0, s, blob, rows, x, y);
+      hipLaunchKernelGGL((k_qmatvec<BITS, NGP, 1>), dim3(blocks_for(iters)), dim3(kBlock), 0, s, blob, ng, rows, x,
+                         y);
     return hipGetLastError();
   }
 
-  template <int NG>
-  static hipError_t gateup(const uint8_t *gu, int inter, const float *x, float *h, hipStream_t s) {
-    constexpr int RPI = kWave / NG;
+  template <int NGP>
+  static hipError_t gateup(const uint8_t *gu, int ng, int inter, const float *x, float *h, hipStream_t s) {
+    constexpr int RPI = kWave / NGP;
     const long waves = inter / RPI;
-    hipLaunchKernelGGL((k_expert_gateup<BITS, NG, 1>), dim3(blocks_for(waves)), dim3(kBlock), 0, s, gu, inter, x, h);
+    hipLaunchKernelGGL((k_expert_gateup<BITS, NGP, 1>), dim3(blocks_for(waves)), dim3(kBlock), 0, s, gu, ng, inter, x,
+                       h);
     return hipGetLastError();
   }
 
   template <int NGH, int NGI, int KPAD>
-  static hipError_t phase3(const LayerArgs &L, const LayerGeom<NGH, NGI> &G, hipStream_t s) {
+  static hipError_t phase3(const LayerArgs &L, const LayerGeom<BITS, NGH, NGI> &G, hipStream_t s) {
     Phase3Args p3{};
     p3.bank = L.bank;
     p3.stride = L.expert_stride;
@@ -963,7 +989,7 @@ struct Dispatch {
   }
 
   template <int NGH, int NGI>
-  static hipError_t phase1(const LayerArgs &L, const LayerGeom<NGH, NGI> &G, hipStream_t s) {
+  static hipError_t phase1(const LayerArgs &L, const LayerGeom<BITS, NGH, NGI> &G, hipStream_t s) {
     const bool has_shared = L.shared != nullptr;
     Phase1Args p1{};
     p1.router = L.router;
@@ -975,7 +1001,8 @@ struct Dispatch {
     p1.logits = L.logits;
     p1.sigma = L.sigma;
     p1.xdig = L.xdig;
-    p1.n_prep_blocks = (NGH + kWavesPerBlock - 1) / kWavesPerBlock + (has_shared ? 1 : 0);
+    p1.ng = L.H / kGroup;
+    p1.n_prep_blocks = (p1.ng + kWavesPerBlock - 1) / kWavesPerBlock + (has_shared ? 1 : 0);
     p1.trace = L.trace;
     // before the router's workgroups: one per four 64-column groups of x (digit
     // form), then one for the shared expert's gate
@@ -984,7 +1011,7 @@ struct Dispatch {
   }
 
   template <int NGH, int NGI>
-  static hipError_t phase2(const LayerArgs &L, const LayerGeom<NGH, NGI> &G, hipStream_t s) {
+  static hipError_t phase2(const LayerArgs &L, const LayerGeom<BITS, NGH, NGI> &G, hipStream_t s) {
     const bool has_shared = L.shared != nullptr;
     Phase2Args p2{};
     p2.logits = L.logits;
@@ -993,6 +1020,7 @@ struct Dispatch {
     p2.bank = L.bank;
     p2.stride = L.expert_stride;
     p2.xdig = L.xdig;
+    p2.ng = L.H / kGroup;
     p2.I = L.I;
     p2.h_routed = L.h_routed;
     p2.ws_idx = L.ws_idx;
@@ -1009,7 +1037,7 @@ struct Dispatch {
   }
 
   template <int NGH, int NGI>
-  static hipError_t phase3k(const LayerArgs &L, const LayerGeom<NGH, NGI> &G, hipStream_t s) {
+  static hipError_t phase3k(const LayerArgs &L, const LayerGeom<BITS, NGH, NGI> &G, hipStream_t s) {
     if (L.K <= 1) return phase3<NGH, NGI, 1>(L, G, s);
     if (L.K <= 2) return phase3<NGH, NGI, 2>(L, G, s);
     if (L.K <= 4) return phase3<NGH, NGI, 4>(L, G, s);
@@ -1018,7 +1046,7 @@ struct Dispatch {
 
   template <int NGH, int NGI>
   static hipError_t layer(const LayerArgs &L, hipStream_t s, int phases) {
-    const LayerGeom<NGH, NGI> G(L, BITS);
+    const LayerGeom<BITS, NGH, NGI> G(L, BITS);
     hipError_t err = hipSuccess;
     if (phases & 1) err = phase1<NGH, NGI>(L, G, s);
     if (err == hipSuccess && (phases & 2)) err = phase2<NGH, NGI>(L, G, s);
@@ -1028,7 +1056,7 @@ struct Dispatch {
 
   template <int NGH>
   static hipError_t layer_h(const LayerArgs &L, hipStream_t s, int phases) {
-    switch (L.I / kGroup) {
+    switch (pad_groups(L.I / kGroup)) {
       case 4: return layer<NGH, 4>(L, s, phases);
       case 8: return layer<NGH, 8>(L, s, phases);
       case 16: return layer<NGH, 16>(L, s, phases);
@@ -1041,17 +1069,17 @@ struct Dispatch {
 
 template <int BITS>
 hipError_t qmatvec_b(const uint8_t *blob, int rows, int cols, const float *x, float *y, hipStream_t s) {
-  FMOE_NG_SWITCH(cols / kGroup, Dispatch<BITS>::template qmatvec, blob, rows, x, y, s)
+  FMOE_NG_SWITCH(pad_groups(cols / kGroup), Dispatch<BITS>::template qmatvec, blob, cols / kGroup, rows, x, y, s)
 }
 
 template <int BITS>
 hipError_t gateup_b(const uint8_t *gu, int hidden, int inter, const float *x, float *h, hipStream_t s) {
-  FMOE_NG_SWITCH(hidden / kGroup, Dispatch<BITS>::template gateup, gu, inter, x, h, s)
+  FMOE_NG_SWITCH(pad_groups(hidden / kGroup), Dispatch<BITS>::template gateup, gu, hidden / kGroup, inter, x, h, s)
 }
 
 template <int BITS>
 hipError_t layer_b(const LayerArgs &L, hipStream_t s, int phases) {
-  FMOE_NG_SWITCH(L.H / kGroup, Dispatch<BITS>::template layer_h, L, s, phases)
+  FMOE_NG_SWITCH(pad_groups(L.H / kGroup), Dispatch<BITS>::template layer_h, L, s, phases)
 }
 
 }  // namespace dev

@@ -25,9 +25,9 @@ constexpr int kDigStride = 52;  // u32 words per 64-column group of x in digit f
 constexpr size_t kScratchBytes = (size_t)4 << 20;  // static workspace of fmoe_moe_layer_noalloc (per GPU)
 
 inline bool bits_ok(int bits) { return bits == 2 || bits == 4; }
-inline bool cols_ok(int cols) {
-  return cols == 256 || cols == 512 || cols == 1024 || cols == 2048 || cols == 4096;
-}
+// Columns of a quantized matrix: a multiple of 256 (four 64-column groups) up to
+// 4096, so that a row's groups fit one wavefront (one group per lane).
+inline bool cols_ok(int cols) { return cols >= 256 && cols <= 4096 && cols % 256 == 0; }
 inline int ilog2(int v) {
   int l = 0;
   while ((1 << l) < v) ++l;

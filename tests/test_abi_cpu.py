@@ -48,9 +48,24 @@ def test_sizes_match_page_facts():
     assert qem.fmoe_expert_bytes(2, 4096, 1024) == 3 * (1024 * 4096 // 4 + 1024 * 64 * 4)
 
 
-@pytest.mark.parametrize("args", [(3, 4096, 1024), (4, 4096, 768), (4, 100, 1024), (4, 8192, 1024)])
+@pytest.mark.parametrize("args", [(3, 4096, 1024), (4, 4096, 640), (4, 100, 1024), (4, 8192, 1024), (4, 4352, 1024),
+                                  (2, 4096, 128), (4, 0, 1024)])
 def test_unsupported_sizes_are_zero(args):
     assert qem.fmoe_expert_bytes(*args) == 0
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("hidden,inter", [(4096, 768), (3072, 1024), (3072, 768), (1280, 2816), (256, 3840),
+                                          (4096, 4096)])
+def test_multiples_of_256_are_supported(bits, hidden, inter):
+    """hidden and inter may be any multiple of 256 from 256 to 4096: an expert is the
+    sum of its three matrices' row records (36 or 20 bytes per 64-column group), each
+    region padded to 256 bytes."""
+    gb = 36 if bits == 4 else 20
+    up = lambda v: (v + 255) // 256 * 256
+    want = up(2 * inter * (hidden // 64) * gb) + up(hidden * (inter // 64) * gb)
+    assert qem.fmoe_expert_bytes(bits, hidden, inter) == want
+    assert qem.fmoe_qmat_bytes(bits, 7, hidden) == up(7 * (hidden // 64) * gb)
 
 
 def test_unsupported_group_is_zero():
@@ -59,7 +74,8 @@ def test_unsupported_group_is_zero():
 
 
 @pytest.mark.parametrize("bits", [4, 2])
-@pytest.mark.parametrize("rows,cols", [(1, 256), (37, 512), (1024, 4096), (4096, 1024), (5, 2048)])
+@pytest.mark.parametrize("rows,cols", [(1, 256), (37, 512), (1024, 4096), (4096, 1024), (5, 2048), (3, 768),
+                                       (9, 3072), (2, 1280), (4, 3840)])
 def test_pack_unpack_round_trip(bits, rows, cols):
     q = synth.qmat(3, 0, rows, synth.T_MATRIX, bits, rows, cols)
     blob = qem.fmoe_pack_qmat(bits, q.codes, q.scale, q.bias)
@@ -93,10 +109,11 @@ def _layout_reference(bits, codes, scale, bias):
 
 @pytest.mark.parametrize("bits", [4, 2])
 def test_packed_layout_is_the_documented_one(bits):
-    q = synth.qmat(9, 1, 2, synth.T_UP, bits, 6, 512)
-    blob = qem.fmoe_pack_qmat(bits, q.codes, q.scale, q.bias)
-    ref = _layout_reference(bits, q.codes, q.scale, q.bias)
-    assert np.array_equal(blob[:ref.size], ref)
+    for cols in (512, 768, 1280):
+        q = synth.qmat(9, 1, cols, synth.T_UP, bits, 6, cols)
+        blob = qem.fmoe_pack_qmat(bits, q.codes, q.scale, q.bias)
+        ref = _layout_reference(bits, q.codes, q.scale, q.bias)
+        assert np.array_equal(blob[:ref.size], ref), cols
 
 
 @pytest.mark.parametrize("bits", [4, 2])
@@ -146,6 +163,7 @@ def qm(blob=A, rows=1024, cols=4096, bits=4, group=64):
     (lambda: L.fmoe_q4_matvec(qm(bits=2), B, C, None), 4),
     (lambda: L.fmoe_q2_matvec(qm(bits=4), B, C, None), 4),
     (lambda: L.fmoe_q4_matvec(qm(cols=1000), B, C, None), 2),
+    (lambda: L.fmoe_q4_matvec(qm(cols=640), B, C, None), 2),
     (lambda: L.fmoe_q4_matvec(qm(cols=8192), B, C, None), 2),
     (lambda: L.fmoe_q4_matvec(qm(rows=0), B, C, None), 2),
     (lambda: L.fmoe_q4_matvec(qm(group=32), B, C, None), 2),
