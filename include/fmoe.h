@@ -82,8 +82,8 @@ extern "C" {
 #endif
 
 #define FMOE_GROUP 64
-#define FMOE_MAX_TOPK 8
-#define FMOE_MAX_TOKENS 64
+#define FMOE_MAX_TOPK 16
+#define FMOE_MAX_TOKENS 256
 #define FMOE_MAX_EXPERTS 1024
 
 typedef enum fmoe_status {
@@ -237,6 +237,59 @@ fmoe_status fmoe_moe_layer_phases(const fmoe_layer *L, int n_tokens, const float
 #define FMOE_NOALLOC_SCRATCH_BYTES (4u << 20)
 fmoe_status fmoe_moe_layer_noalloc(const fmoe_layer *L, int n_tokens, const float *x, const float *residual,
                                    float *out, int32_t *topk_idx, float *topk_w, void *stream);
+
+/* ------------------------------------------------------------------ host-memory expert tier
+ * The pages stream the routed experts from SSD and let the operating system's
+ * page cache keep the recently used ones in memory ([P1] "1. Streaming de
+ * expertos desde SSD + 'Confia en el SO'", [P2] "SSD-Experten-Streaming"). Here
+ * the slow tier is host memory: a layer's routed expert bank lives in host memory
+ * (fmoe_layer.bank is then a HOST pointer, best pinned: hipHostMalloc or a pinned
+ * torch tensor, so that the copies are DMA transfers), and an HBM cache of n_slots
+ * expert blobs holds the most recently used (layer, expert) pairs. The router,
+ * the shared-expert gate vector and the shared expert stay in device memory.
+ *
+ * fmoe_cache_device_bytes: bytes of the caller's device buffer for a cache of
+ * n_slots blobs of experts with this shape and up to n_experts experts per layer
+ * (the slots and a table of blob addresses); 0 if unsupported.
+ * fmoe_cache_create: the cache over that buffer (256-B aligned, device_bytes at
+ * least the above). The library allocates the host bookkeeping here and, at the
+ * first tiered call, two small pinned host buffers (the routing read-back and the
+ * address table), all released by fmoe_cache_destroy; no device memory.
+ * FMOE_ERR_WORKSPACE if n_slots < 1 or the buffer is too small, FMOE_ERR_ROUTING for
+ * n_experts outside 1..FMOE_MAX_EXPERTS; a tiered call returns FMOE_ERR_LAUNCH if
+ * the pinned host buffers cannot be allocated.
+ * fmoe_cache_plan: the cache's policy step alone (host only, no device work): for
+ * n distinct experts of layer `layer`, slot_out[i] is the slot that holds expert
+ * experts[i] after the call and miss_out[i] 1 when it had to be (re)filled. A hit
+ * refreshes the slot; a miss takes the first empty slot, else the least recently
+ * used slot that the call does not need (ties: the lower slot). FMOE_ERR_ROUTING
+ * for an expert outside 0..n_experts-1 or a repeated one, FMOE_ERR_WORKSPACE if n
+ * exceeds the slots (nothing changes then).
+ * fmoe_moe_layer_tiered: fmoe_moe_layer with L->bank in host memory, any n_tokens
+ * (the tokens grouped by expert, as fmoe_moe_layer does for several): the router
+ * and top-K run on the GPU; the call then synchronises `stream` once to read the
+ * routing, plans the batch's distinct experts (ascending id) through the cache,
+ * copies the missing blobs from host memory into their slots (on `stream`), and
+ * enqueues the experts and the combine, which read the blobs from their slots.
+ * Results equal fmoe_moe_layer's. ws >= fmoe_tiered_workspace_bytes(L, n_tokens);
+ * the batch's distinct experts must fit the slots (FMOE_ERR_WORKSPACE, found after
+ * the routing: the routing outputs are then written, nothing else). Calls on one
+ * cache must be serialised on one stream. Otherwise the arguments and errors of
+ * fmoe_moe_layer; FMOE_ERR_SHAPE if L does not match the cache's shape. */
+typedef struct fmoe_cache fmoe_cache;
+size_t fmoe_cache_device_bytes(int bits, int hidden, int inter, int group, int n_experts, int n_slots);
+fmoe_status fmoe_cache_create(int bits, int hidden, int inter, int group, int n_experts, int n_slots,
+                              void *device_buf, size_t device_bytes, fmoe_cache **out);
+void fmoe_cache_destroy(fmoe_cache *c);
+/* Counters since creation: expert lookups, hits, misses, bytes copied from host memory. */
+fmoe_status fmoe_cache_get_stats(const fmoe_cache *c, int64_t *lookups, int64_t *hits, int64_t *misses,
+                                 int64_t *bytes_copied);
+fmoe_status fmoe_cache_plan(fmoe_cache *c, int layer, const int32_t *experts, int n, int32_t *slot_out,
+                            int32_t *miss_out);
+size_t fmoe_tiered_workspace_bytes(const fmoe_layer *L, int n_tokens);
+fmoe_status fmoe_moe_layer_tiered(fmoe_cache *c, int layer, const fmoe_layer *L, int n_tokens, const float *x,
+                                  const float *residual, float *out, int32_t *topk_idx, float *topk_w, void *ws,
+                                  size_t ws_bytes, void *stream);
 
 /* RMS scaling without a learned weight, two stages (sum of squares, then apply)
  * ([P2] "Metal-Compute-Shader": RMS normalization, two-stage):

@@ -23,8 +23,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfmoe.so")
 
 GROUP = 64
-MAX_TOPK = 8
-MAX_TOKENS = 64
+MAX_TOPK = 16
+MAX_TOKENS = 256
 MAX_EXPERTS = 1024
 
 STATUS = {
@@ -83,6 +83,16 @@ _SIGS = {
     "fmoe_moe_layer_phases": (ctypes.c_int, [ctypes.POINTER(fmoe_layer), ctypes.c_int] + [ctypes.c_void_p] * 6 +
                               [ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]),
     "fmoe_moe_layer_noalloc": (ctypes.c_int, [ctypes.POINTER(fmoe_layer), ctypes.c_int] + [ctypes.c_void_p] * 6),
+    "fmoe_cache_device_bytes": (ctypes.c_size_t, [ctypes.c_int] * 6),
+    "fmoe_cache_create": (ctypes.c_int, [ctypes.c_int] * 6 + [ctypes.c_void_p, ctypes.c_size_t,
+                                                              ctypes.POINTER(ctypes.c_void_p)]),
+    "fmoe_cache_destroy": (None, [ctypes.c_void_p]),
+    "fmoe_cache_get_stats": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.POINTER(ctypes.c_int64)] * 4),
+    "fmoe_cache_plan": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_void_p]),
+    "fmoe_tiered_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(fmoe_layer), ctypes.c_int]),
+    "fmoe_moe_layer_tiered": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(fmoe_layer), ctypes.c_int] +
+                              [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p]),
     "fmoe_rms_scale": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_float, ctypes.c_void_p]),
     "fmoe_moe_stack": (ctypes.c_int, [ctypes.POINTER(fmoe_layer), ctypes.c_int, ctypes.c_int] +
@@ -378,6 +388,96 @@ def fmoe_moe_layer_noalloc(L: Layer, x: torch.Tensor, residual: torch.Tensor, ou
     n_tokens = x.shape[0] if x.dim() == 2 else 1
     _ok(lib().fmoe_moe_layer_noalloc(ctypes.byref(L.c()), n_tokens, _ptr(x), _ptr(residual), _ptr(out),
                                      _ptr(topk_idx), _ptr(topk_w), _stream(stream)), "fmoe_moe_layer_noalloc")
+    return out
+
+
+# ----------------------------------------------------------------------------- host-memory expert tier
+
+def fmoe_cache_device_bytes(bits: int, hidden: int, inter: int, n_experts: int, n_slots: int,
+                            group: int = GROUP) -> int:
+    return int(lib().fmoe_cache_device_bytes(bits, hidden, inter, group, n_experts, n_slots))
+
+
+def fmoe_cache_create(bits: int, hidden: int, inter: int, n_experts: int, n_slots: int, device_buf,
+                      group: int = GROUP) -> ctypes.c_void_p:
+    nbytes = device_buf.numel() * device_buf.element_size() if isinstance(device_buf, torch.Tensor) else 0
+    h = ctypes.c_void_p()
+    _ok(lib().fmoe_cache_create(bits, hidden, inter, group, n_experts, n_slots, _ptr(device_buf), nbytes,
+                                ctypes.byref(h)), "fmoe_cache_create")
+    return h
+
+
+def fmoe_cache_destroy(handle) -> None:
+    lib().fmoe_cache_destroy(handle)
+
+
+def fmoe_cache_get_stats(handle) -> dict:
+    v = [ctypes.c_int64() for _ in range(4)]
+    _ok(lib().fmoe_cache_get_stats(handle, *[ctypes.byref(x) for x in v]), "fmoe_cache_get_stats")
+    return dict(zip(("lookups", "hits", "misses", "bytes_copied"), (x.value for x in v)))
+
+
+def fmoe_cache_plan(handle, layer: int, experts):
+    """The cache's policy step alone (host only): returns (slots, misses) for the
+    distinct experts of one call."""
+    e = np.ascontiguousarray(experts, dtype=np.int32)
+    slots = np.empty(e.size, np.int32)
+    miss = np.empty(e.size, np.int32)
+    _ok(lib().fmoe_cache_plan(handle, layer, e.ctypes.data, e.size, slots.ctypes.data, miss.ctypes.data),
+        "fmoe_cache_plan")
+    return slots, miss
+
+
+class ExpertCache:
+    """An HBM cache of n_slots expert blobs for the host-memory expert tier (device
+    buffer allocated here with torch; the library owns only host bookkeeping)."""
+
+    def __init__(self, bits: int, hidden: int, inter: int, n_experts: int, n_slots: int, device="cuda"):
+        nb = fmoe_cache_device_bytes(bits, hidden, inter, n_experts, n_slots)
+        if nb == 0:
+            raise FmoeError(2, "fmoe_cache_device_bytes")
+        self.buf = torch.empty(nb, dtype=torch.uint8, device=device)
+        self.handle = fmoe_cache_create(bits, hidden, inter, n_experts, n_slots, self.buf)
+
+    def stats(self) -> dict:
+        return fmoe_cache_get_stats(self.handle)
+
+    def plan(self, layer: int, experts):
+        return fmoe_cache_plan(self.handle, layer, experts)
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            fmoe_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def fmoe_tiered_workspace_bytes(L: Layer, n_tokens: int) -> int:
+    return int(lib().fmoe_tiered_workspace_bytes(ctypes.byref(L.c()), n_tokens))
+
+
+def fmoe_moe_layer_tiered(cache: ExpertCache, layer: int, L: Layer, x: torch.Tensor, residual: torch.Tensor,
+                          out: Optional[torch.Tensor] = None, topk_idx: Optional[torch.Tensor] = None,
+                          topk_w: Optional[torch.Tensor] = None, ws=None, stream=None) -> torch.Tensor:
+    """One MoE layer whose routed expert bank (L.bank) is in host memory (a pinned CPU
+    tensor): the chosen experts go through the HBM cache. Synchronises the stream once."""
+    _dev_f32(x, "x")
+    _dev_f32(residual, "residual")
+    n_tokens = x.shape[0] if x.dim() == 2 else 1
+    if out is None:
+        out = torch.empty_like(residual)
+    need = fmoe_tiered_workspace_bytes(L, n_tokens)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    nbytes = ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else need
+    _ok(lib().fmoe_moe_layer_tiered(cache.handle, layer, ctypes.byref(L.c()), n_tokens, _ptr(x), _ptr(residual),
+                                    _ptr(out), _ptr(topk_idx), _ptr(topk_w), _ptr(ws), nbytes, _stream(stream)),
+        "fmoe_moe_layer_tiered")
     return out
 
 

@@ -5,7 +5,12 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+#include <new>
+#include <vector>
+
 #include "../../include/fmoe.h"
+#include "expert_cache.h"
 #include "forms.h"
 #include "kernels.h"
 #include "layout.h"
@@ -68,6 +73,47 @@ fmoe_status matvec_common(const fmoe_qmat *W, const float *x, float *y, void *st
   return e == hipSuccess ? FMOE_OK : FMOE_ERR_LAUNCH;
 }
 
+// The arguments of the grouped kernels for one layer (workspace carved as layer_ws(grouped)).
+GroupArgs group_args(const fmoe_layer *L, int B, const float *x, float rms_eps, const float *residual, float *out,
+                     int32_t *topk_idx, float *topk_w, uint8_t *ws) {
+  const LayerWs w = layer_ws(B, L->n_experts, L->top_k, L->hidden, L->inter, true);
+  const int H = L->hidden, I = L->inter, E = L->n_experts, K = L->top_k;
+  GroupArgs g{};
+  g.router = L->router;
+  g.gvec = L->shared ? L->shared_gate : nullptr;
+  g.bank = (const uint8_t *)L->bank;
+  g.shared = (const uint8_t *)L->shared;
+  g.stride = expert_bytes(L->bits, H, I);
+  g.gu_bytes = gateup_bytes(L->bits, H, I);
+  g.E = E;
+  g.K = K;
+  g.H = H;
+  g.I = I;
+  g.B = B;
+  g.bits = L->bits;
+  g.x = x;
+  g.rms_eps = rms_eps;
+  g.residual = residual;
+  g.out = out;
+  g.out_idx = topk_idx;
+  g.out_w = topk_w;
+  g.logits = (float *)(ws + w.logits);
+  g.sigma = (float *)(ws + w.sigma);
+  g.gdot = (float *)(ws + w.gdot);
+  g.idx = (int32_t *)(ws + w.topk_idx);
+  g.w = (float *)(ws + w.topk_w);
+  g.xq = (uint8_t *)(ws + w.xq);
+  g.xsum = (float *)(ws + w.xsum);
+  g.xinv = (float *)(ws + w.xinv);
+  g.hq = (uint8_t *)(ws + w.hq);
+  g.hsum = (float *)(ws + w.hsum);
+  g.d_shared = (float *)(ws + w.d_shared);
+  g.partial = (float *)(ws + w.partial);
+  g.groups = (int32_t *)(ws + w.groups);
+  g.expert_ptr = nullptr;
+  return g;
+}
+
 // Enqueue one layer for n_tokens tokens (arguments already validated): the
 // one-token kernels for a single token, the grouped kernels for several.
 // rms_eps >= 0: the layer input is rms_scale(x, rms_eps), computed inside the layer's kernels.
@@ -75,41 +121,10 @@ fmoe_status matvec_common(const fmoe_qmat *W, const float *x, float *y, void *st
 fmoe_status layer_enqueue(const fmoe_layer *L, int B, const float *x, float rms_eps, const float *residual,
                           float *out, int32_t *topk_idx, float *topk_w, uint8_t *ws, hipStream_t s,
                           int phases = 7, uint64_t *trace = nullptr) {
-  const LayerWs w = layer_ws(B, L->n_experts, L->top_k, L->hidden, L->inter);
+  const LayerWs w = layer_ws(B, L->n_experts, L->top_k, L->hidden, L->inter, B > 1);
   const int H = L->hidden, I = L->inter, E = L->n_experts, K = L->top_k;
   if (B > 1) {
-    GroupArgs g{};
-    g.router = L->router;
-    g.gvec = L->shared ? L->shared_gate : nullptr;
-    g.bank = (const uint8_t *)L->bank;
-    g.shared = (const uint8_t *)L->shared;
-    g.stride = expert_bytes(L->bits, H, I);
-    g.gu_bytes = gateup_bytes(L->bits, H, I);
-    g.E = E;
-    g.K = K;
-    g.H = H;
-    g.I = I;
-    g.B = B;
-    g.bits = L->bits;
-    g.x = x;
-    g.rms_eps = rms_eps;
-    g.residual = residual;
-    g.out = out;
-    g.out_idx = topk_idx;
-    g.out_w = topk_w;
-    g.logits = (float *)(ws + w.logits);
-    g.sigma = (float *)(ws + w.sigma);
-    g.gdot = (float *)(ws + w.gdot);
-    g.idx = (int32_t *)(ws + w.topk_idx);
-    g.w = (float *)(ws + w.topk_w);
-    g.xq = (uint8_t *)(ws + w.xq);
-    g.xsum = (float *)(ws + w.xsum);
-    g.xinv = (float *)(ws + w.xinv);
-    g.hq = (uint8_t *)(ws + w.hq);
-    g.hsum = (float *)(ws + w.hsum);
-    g.d_shared = (float *)(ws + w.d_shared);
-    g.partial = (float *)(ws + w.partial);
-    g.groups = (int32_t *)(ws + w.groups);
+    const GroupArgs g = group_args(L, B, x, rms_eps, residual, out, topk_idx, topk_w, ws);
     return launch_group(g, s, phases) == hipSuccess ? FMOE_OK : FMOE_ERR_LAUNCH;
   }
   for (int t = 0; t < B; ++t) {
@@ -169,7 +184,7 @@ size_t fmoe_workspace_bytes(const fmoe_layer *L, int n_tokens) {
   if (n_tokens < 1 || n_tokens > kMaxTokens || L->top_k < 1 || L->top_k > kMaxTopK || L->n_experts < 1 ||
       L->n_experts > kMaxExperts)
     return 0;
-  return layer_ws(n_tokens, L->n_experts, L->top_k, L->hidden, L->inter).total;
+  return layer_ws(n_tokens, L->n_experts, L->top_k, L->hidden, L->inter, n_tokens > 1).total;
 }
 
 size_t fmoe_stack_workspace_bytes(const fmoe_layer *L, int n_tokens) {
@@ -337,6 +352,175 @@ fmoe_status fmoe_moe_layer_noalloc(const fmoe_layer *L, int n_tokens, const floa
   if (scratch_device_ptr(&ws) != hipSuccess) return FMOE_ERR_LAUNCH;
   // the full validation of fmoe_moe_layer, with the static workspace as ws
   return fmoe_moe_layer_phases(L, n_tokens, x, residual, out, topk_idx, topk_w, ws, kScratchBytes, 7, stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ host-memory expert tier
+
+// The cache: n_slots expert blobs and a table of expert blob addresses in the
+// caller's device buffer; the slot bookkeeping, and pinned host staging for the
+// routing read-back and the address table, on the host.
+struct fmoe_cache {
+  int bits, hidden, inter, n_experts, n_slots;
+  size_t stride;                 // bytes per expert blob
+  uint8_t *slots;                // device: n_slots blobs
+  const uint8_t **table;         // device: [n_experts] blob addresses
+  const uint8_t **table_host;    // pinned host mirror of table
+  int32_t *idx_host;             // pinned host: routing read-back [kMaxTokens * kMaxTopK]
+  fmoe::ExpertCache lru;
+  int64_t lookups = 0, bytes = 0;
+  fmoe_cache(int n) : lru(n) {}
+};
+
+namespace {
+size_t cache_table_offset(int bits, int hidden, int inter, int n_slots) {
+  return round_up((size_t)n_slots * expert_bytes(bits, hidden, inter), 256);
+}
+}  // namespace
+
+extern "C" {
+
+size_t fmoe_cache_device_bytes(int bits, int hidden, int inter, int group, int n_experts, int n_slots) {
+  if (check_expert_shape(bits, hidden, inter, group) != FMOE_OK || n_slots < 1 || n_experts < 1 ||
+      n_experts > kMaxExperts)
+    return 0;
+  return cache_table_offset(bits, hidden, inter, n_slots) + round_up(sizeof(void *) * (size_t)n_experts, 256);
+}
+
+fmoe_status fmoe_cache_create(int bits, int hidden, int inter, int group, int n_experts, int n_slots,
+                              void *device_buf, size_t device_bytes, fmoe_cache **out) {
+  if (!out || !device_buf) return FMOE_ERR_NULL;
+  *out = nullptr;
+  fmoe_status st = check_expert_shape(bits, hidden, inter, group);
+  if (st != FMOE_OK) return st;
+  if (n_experts < 1 || n_experts > kMaxExperts) return FMOE_ERR_ROUTING;
+  if (n_slots < 1) return FMOE_ERR_WORKSPACE;
+  if (!al256(device_buf)) return FMOE_ERR_ALIGN;
+  if (device_bytes < fmoe_cache_device_bytes(bits, hidden, inter, group, n_experts, n_slots))
+    return FMOE_ERR_WORKSPACE;
+  fmoe_cache *c = new (std::nothrow) fmoe_cache(n_slots);
+  if (!c) return FMOE_ERR_WORKSPACE;
+  c->bits = bits;
+  c->hidden = hidden;
+  c->inter = inter;
+  c->n_experts = n_experts;
+  c->n_slots = n_slots;
+  c->stride = expert_bytes(bits, hidden, inter);
+  c->slots = (uint8_t *)device_buf;
+  c->table = (const uint8_t **)((uint8_t *)device_buf + cache_table_offset(bits, hidden, inter, n_slots));
+  c->table_host = nullptr;  // (pinned host buffers: allocated by the first tiered call)
+  c->idx_host = nullptr;
+  *out = c;
+  return FMOE_OK;
+}
+
+void fmoe_cache_destroy(fmoe_cache *c) {
+  if (!c) return;
+  if (c->table_host) (void)hipHostFree((void *)c->table_host);
+  if (c->idx_host) (void)hipHostFree(c->idx_host);
+  delete c;
+}
+
+fmoe_status fmoe_cache_get_stats(const fmoe_cache *c, int64_t *lookups, int64_t *hits, int64_t *misses,
+                                 int64_t *bytes_copied) {
+  if (!c) return FMOE_ERR_NULL;
+  if (lookups) *lookups = c->lookups;
+  if (hits) *hits = c->lru.hits();
+  if (misses) *misses = c->lru.misses();
+  if (bytes_copied) *bytes_copied = c->bytes;
+  return FMOE_OK;
+}
+
+fmoe_status fmoe_cache_plan(fmoe_cache *c, int layer, const int32_t *experts, int n, int32_t *slot_out,
+                            int32_t *miss_out) {
+  if (!c || !experts || !slot_out || !miss_out) return FMOE_ERR_NULL;
+  if (layer < 0 || n < 1) return FMOE_ERR_BATCH;
+  std::vector<int32_t> sorted(experts, experts + n);
+  std::sort(sorted.begin(), sorted.end());
+  for (int i = 0; i < n; ++i)
+    if (sorted[i] < 0 || sorted[i] >= c->n_experts || (i > 0 && sorted[i] == sorted[i - 1])) return FMOE_ERR_ROUTING;
+  if (n > c->n_slots) return FMOE_ERR_WORKSPACE;
+  c->lookups += n;
+  return c->lru.plan(layer, experts, n, slot_out, miss_out) ? FMOE_OK : FMOE_ERR_WORKSPACE;
+}
+
+size_t fmoe_tiered_workspace_bytes(const fmoe_layer *L, int n_tokens) {
+  if (fmoe_workspace_bytes(L, n_tokens) == 0) return 0;
+  return layer_ws(n_tokens, L->n_experts, L->top_k, L->hidden, L->inter, true).total;
+}
+
+fmoe_status fmoe_moe_layer_tiered(fmoe_cache *c, int layer, const fmoe_layer *L, int n_tokens, const float *x,
+                                  const float *residual, float *out, int32_t *topk_idx, float *topk_w, void *ws,
+                                  size_t ws_bytes, void *stream) {
+  if (!c) return FMOE_ERR_NULL;
+  fmoe_status st = check_layer(L);
+  if (st != FMOE_OK) return st;
+  if (L->bits != c->bits || L->hidden != c->hidden || L->inter != c->inter || L->n_experts > c->n_experts)
+    return FMOE_ERR_SHAPE;
+  if (!x || !residual || !out) return FMOE_ERR_NULL;
+  if (layer < 0 || n_tokens < 1 || n_tokens > kMaxTokens) return FMOE_ERR_BATCH;
+  if (!al16(x) || !al16(residual) || !al16(out) || (topk_idx && !al16(topk_idx)) || (topk_w && !al16(topk_w)))
+    return FMOE_ERR_ALIGN;
+  const size_t need = fmoe_tiered_workspace_bytes(L, n_tokens);
+  if (!ws || ws_bytes < need) return FMOE_ERR_WORKSPACE;
+  if (!al256(ws)) return FMOE_ERR_ALIGN;
+  const size_t ab = sizeof(float) * (size_t)n_tokens * L->hidden;
+  const size_t kb = sizeof(float) * (size_t)n_tokens * L->top_k;
+  if (overlap(out, ab, x, ab) || overlap(out, ab, ws, need) || overlap(x, ab, ws, need) ||
+      overlap(residual, ab, ws, need) || overlap(topk_idx, kb, ws, need) || overlap(topk_w, kb, ws, need) ||
+      overlap(topk_idx, kb, out, ab) || overlap(topk_w, kb, out, ab) || overlap(topk_idx, kb, topk_w, kb) ||
+      (residual != out && overlap(residual, ab, out, ab)) || overlap(topk_idx, kb, residual, ab) ||
+      overlap(topk_w, kb, residual, ab) || overlap(topk_idx, kb, x, ab) || overlap(topk_w, kb, x, ab))
+    return FMOE_ERR_ALIAS;
+  if (!c->table_host) {
+    if (hipHostMalloc((void **)&c->table_host, sizeof(void *) * (size_t)c->n_experts, hipHostMallocDefault) !=
+        hipSuccess) {
+      c->table_host = nullptr;
+      return FMOE_ERR_LAUNCH;
+    }
+    for (int e = 0; e < c->n_experts; ++e) c->table_host[e] = nullptr;
+  }
+  if (!c->idx_host &&
+      hipHostMalloc((void **)&c->idx_host, sizeof(int32_t) * kMaxTokens * kMaxTopK, hipHostMallocDefault) !=
+          hipSuccess) {
+    c->idx_host = nullptr;
+    return FMOE_ERR_LAUNCH;
+  }
+  hipStream_t s = as_stream(stream);
+  GroupArgs g = group_args(L, n_tokens, x, -1.f, residual, out, topk_idx, topk_w, (uint8_t *)ws);
+  g.expert_ptr = c->table;
+  // 1. the routing on the GPU, read back (the one host synchronisation of the call)
+  if (launch_group_route(g, s) != hipSuccess) return FMOE_ERR_LAUNCH;
+  const int S = n_tokens * L->top_k;
+  if (hipMemcpyAsync(c->idx_host, g.idx, sizeof(int32_t) * S, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return FMOE_ERR_LAUNCH;
+  // 2. the distinct experts, in ascending id; their slots; the missing blobs copied in
+  std::vector<int32_t> ex(c->idx_host, c->idx_host + S);
+  std::sort(ex.begin(), ex.end());
+  ex.erase(std::unique(ex.begin(), ex.end()), ex.end());
+  const int n = (int)ex.size();
+  if (n > c->n_slots) return FMOE_ERR_WORKSPACE;  // (checked before anything is copied)
+  std::vector<int32_t> slot(n), miss(n);
+  c->lookups += n;
+  if (!c->lru.plan(layer, ex.data(), n, slot.data(), miss.data())) return FMOE_ERR_WORKSPACE;
+  const uint8_t *host_bank = (const uint8_t *)L->bank;
+  for (int i = 0; i < n; ++i) {
+    uint8_t *dst = c->slots + (size_t)slot[i] * c->stride;
+    c->table_host[ex[i]] = dst;
+    if (miss[i]) {
+      if (hipMemcpyAsync(dst, host_bank + (size_t)ex[i] * c->stride, c->stride, hipMemcpyHostToDevice, s) !=
+          hipSuccess)
+        return FMOE_ERR_LAUNCH;
+      c->bytes += (int64_t)c->stride;
+    }
+  }
+  if (hipMemcpyAsync((void *)c->table, (const void *)c->table_host, sizeof(void *) * (size_t)L->n_experts,
+                     hipMemcpyHostToDevice, s) != hipSuccess)
+    return FMOE_ERR_LAUNCH;
+  // 3. the experts from their slots, and the combine
+  return launch_group_experts(g, s) == hipSuccess ? FMOE_OK : FMOE_ERR_LAUNCH;
 }
 
 fmoe_status fmoe_rms_scale(const float *h, float *x, int n_tokens, int hidden, float eps, void *stream) {

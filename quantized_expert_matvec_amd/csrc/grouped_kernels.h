@@ -47,7 +47,12 @@
 namespace fmoe {
 namespace dev {
 
-constexpr int kMaxSlots = kMaxTokens * kMaxTopK;
+// Slots (token, choice) that the gate/up kernel's own routing handles (one thread
+// per slot): batches with more, with more than kRouteTokens tokens or with
+// top_k > 8 are routed by the routing kernels before it (k_topk, k_group) and read
+// the grouping table.
+constexpr int kRouteSlots = 512;
+constexpr int kRouteTokens = 64;
 // Tokens per work item: one MFMA row block (4 rows each: hi, mid, lo, 0). An
 // expert used by more tokens (the shared expert, mostly) gives several items,
 // which run on different compute units and re-read its rows (from the caches).
@@ -594,7 +599,7 @@ struct RouteLdsT {
   int eoff[kMaxExperts];                     // list offset of each present expert
   int wtot[kGWaves];
 };
-using RouteLds = RouteLdsT<kGWaves>;  // every batch (kMaxSlots slots)
+using RouteLds = RouteLdsT<kGWaves>;  // every routed-in-kernel batch (kRouteSlots slots)
 using RouteLds1 = RouteLdsT<1>;       // at most 64 slots
 
 // Top-K of every token and the grouping of the S = B*K slots by expert, by one
@@ -612,7 +617,7 @@ using RouteLds1 = RouteLdsT<1>;       // at most 64 slots
 // (idx, w, sigma, the caller's outputs) and the table G.
 template <int NW>
 __device__ __forceinline__ int block_route(const GroupArgs &a, RouteLdsT<NW> &R, int *slotl, int *blk, bool writer) {
-  static_assert(kMaxSlots <= kGThreads, "one thread per slot");
+  static_assert(kRouteSlots <= kGThreads, "one thread per slot");
   static_assert(kMaxExperts <= 2 * kGThreads, "two experts per thread in the scan");
   const int lane = lane_id();
   const int wave = wave_in_block();
@@ -621,18 +626,19 @@ __device__ __forceinline__ int block_route(const GroupArgs &a, RouteLdsT<NW> &R,
   for (int i = threadIdx.x; i < nwl * a.E; i += kGThreads) R.mask[i / a.E][i % a.E] = 0ull;
   // token t's routing from its top-K (idx, w): slot experts, and the writer's outputs
   auto publish = [&](int t, const int *idx, const float *w, float inv, float gd) {
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j)
-      if (j == lane && j < a.K) {
-        const int s = t * a.K + j;
-        R.sidx[s] = idx[j];
-        if (writer) {
-          a.idx[s] = idx[j];
-          a.w[s] = w[j];
-          if (a.out_idx) a.out_idx[s] = idx[j];
-          if (a.out_w) a.out_w[s] = w[j];
-        }
+    auto one = [&](int j) {
+      const int s = t * a.K + j;
+      R.sidx[s] = idx[j];
+      if (writer) {
+        a.idx[s] = idx[j];
+        a.w[s] = w[j];
+        if (a.out_idx) a.out_idx[s] = idx[j];
+        if (a.out_w) a.out_w[s] = w[j];
       }
+    };
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j == lane && j < a.K) one(j);
     if (writer && lane == 0 && a.gvec) a.sigma[t] = 1.f / (1.f + expf(-gd * inv));
   };
   if (a.E <= 512) {
@@ -645,14 +651,14 @@ __device__ __forceinline__ int block_route(const GroupArgs &a, RouteLdsT<NW> &R,
       load_logits<8>(a.logits + (size_t)t1 * logit_stride(a.E), a.E, v1);
       const float inv0 = a.xinv[t0], inv1 = a.xinv[t1];
       const float gd0 = a.gvec ? a.gdot[t0] : 0.f, gd1 = a.gvec ? a.gdot[t1] : 0.f;
-      int key[8], idx[kMaxTopK];
-      float w[kMaxTopK];
+      int key[8], idx[8];
+      float w[8];
       logit_keys<8>(v0, a.E, key);
-      wave_topk_keys<8>(key, a.K, idx, w, inv0);
+      wave_topk_keys<8, 8>(key, a.K, idx, w, inv0);
       publish(t0, idx, w, inv0, gd0);
       if (t0 + kGWaves < a.B) {
         logit_keys<8>(v1, a.E, key);
-        wave_topk_keys<8>(key, a.K, idx, w, inv1);
+        wave_topk_keys<8, 8>(key, a.K, idx, w, inv1);
         publish(t1, idx, w, inv1, gd1);
       }
     }
@@ -660,9 +666,9 @@ __device__ __forceinline__ int block_route(const GroupArgs &a, RouteLdsT<NW> &R,
     for (int t = wave; t < a.B; t += kGWaves) {
       const float inv = a.xinv[t];
       const float gd = a.gvec ? a.gdot[t] : 0.f;
-      int idx[kMaxTopK];
-      float w[kMaxTopK];
-      wave_topk_lds(a.logits + (size_t)t * logit_stride(a.E), a.E, a.K, idx, w, inv);
+      int idx[8];
+      float w[8];
+      wave_topk_lds<8>(a.logits + (size_t)t * logit_stride(a.E), a.E, a.K, idx, w, inv);
       publish(t, idx, w, inv, gd);
     }
   }
@@ -742,11 +748,173 @@ __device__ __forceinline__ int block_route(const GroupArgs &a, RouteLdsT<NW> &R,
 
 // ------------------------------------------------------------------ g2, g3
 
+// ------------------------------------------------------------------ routing kernels (large batches)
+
+// k_topk: the routing of every token, one wavefront per token: the top-K of its
+// unscaled logits with the weights taken after its RMS factor (as block_route),
+// into idx / w (and the caller's outputs), and its shared-expert gate sigma.
+// KM: 8 for top_k <= 8, else kMaxTopK.
+template <int BITS, int KM>
+__global__ __launch_bounds__(kGThreads) void k_topk(const GroupArgs a) {
+  const int t = (int)blockIdx.x * kGWaves + wave_in_block();
+  if (t >= a.B) return;  // (uniform over the wavefront)
+  const int lane = lane_id();
+  const float inv = a.xinv[t];
+  const float gd = a.gvec ? a.gdot[t] : 0.f;
+  int idx[KM];
+  float w[KM];
+  if (a.E <= 512) {
+    float v[8];
+    int key[8];
+    load_logits<8>(a.logits + (size_t)t * logit_stride(a.E), a.E, v);
+    logit_keys<8>(v, a.E, key);
+    wave_topk_keys<8, KM>(key, a.K, idx, w, inv);
+  } else {
+    wave_topk_lds<KM>(a.logits + (size_t)t * logit_stride(a.E), a.E, a.K, idx, w, inv);
+  }
+  // lane j < K stores choice j (selected from the unrolled arrays, then one store each)
+  int mi = 0;
+  float mw = 0.f;
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    mi = j == lane ? idx[j] : mi;
+    mw = j == lane ? w[j] : mw;
+  }
+  if (lane < a.K) {
+    const int s = t * a.K + lane;
+    a.idx[s] = mi;
+    a.w[s] = mw;
+    if (a.out_idx) a.out_idx[s] = mi;
+    if (a.out_w) a.out_w[s] = mw;
+  }
+  if (lane == 0 && a.gvec) a.sigma[t] = 1.f / (1.f + expf(-gd * inv));
+}
+
+// k_group: one workgroup groups the S = B K slots by expert into the table G
+// (layout above): per expert its slots in ascending order, the experts in
+// ascending id, each expert's list cut into token blocks of up to kTokBlock.
+// Deterministic whatever the thread timing: the counts come from LDS atomic adds
+// (their order does not matter), and a slot's place in its expert's list is the
+// number of lower slots with the same expert, taken 512 slots at a time from
+// per-wavefront 64-bit masks (as in block_route), plus the expert's running
+// count over the earlier rounds.
+struct GroupLds {
+  unsigned long long mask[kGWaves][kMaxExperts];
+  int cnt[kMaxExperts], eoff[kMaxExperts], boff[kMaxExperts], run[kMaxExperts];
+  int slotl[kMaxTokens * kMaxTopK];
+  int wtot[kGWaves];
+};
+template <int BITS>
+__global__ __launch_bounds__(kGThreads) void k_group(const GroupArgs a) {
+  static_assert(kMaxExperts <= 2 * kGThreads, "two experts per thread in the scan");
+  __shared__ GroupLds R;
+  const int lane = lane_id(), wave = wave_in_block();
+  const int S = a.B * a.K, E = a.E;
+  for (int e = threadIdx.x; e < E; e += kGThreads) {
+    R.cnt[e] = 0;
+    R.run[e] = 0;
+  }
+  __syncthreads();
+  for (int s = threadIdx.x; s < S; s += kGThreads) atomicAdd(&R.cnt[a.idx[s]], 1);
+  __syncthreads();
+  // experts 2x and 2x + 1 of thread x: slot counts and token blocks, then integer
+  // scans of two words, (present experts | slots << 11) and token blocks
+  const int e0 = 2 * (int)threadIdx.x, e1 = e0 + 1;
+  const int n0 = e0 < E ? R.cnt[e0] : 0, n1 = e1 < E ? R.cnt[e1] : 0;
+  const int nb0 = (n0 + kTokBlock - 1) / kTokBlock, nb1 = (n1 + kTokBlock - 1) / kTokBlock;
+  int v1 = (n0 > 0) + (n1 > 0) + ((n0 + n1) << 11);  // present experts (< 2048), slots (<= 4096)
+  int v2 = nb0 + nb1;                                // token blocks
+  const int m1 = v1, m2 = v2;
+  v1 += dpp_i<0x111, 0xF>(v1, 0);
+  v2 += dpp_i<0x111, 0xF>(v2, 0);
+  v1 += dpp_i<0x112, 0xF>(v1, 0);
+  v2 += dpp_i<0x112, 0xF>(v2, 0);
+  v1 += dpp_i<0x114, 0xF>(v1, 0);
+  v2 += dpp_i<0x114, 0xF>(v2, 0);
+  v1 += dpp_i<0x118, 0xF>(v1, 0);
+  v2 += dpp_i<0x118, 0xF>(v2, 0);
+  v1 += dpp_i<0x142, 0xA>(v1, 0);
+  v2 += dpp_i<0x142, 0xA>(v2, 0);
+  v1 += dpp_i<0x143, 0xC>(v1, 0);
+  v2 += dpp_i<0x143, 0xC>(v2, 0);
+  __shared__ int wtot2[kGWaves];
+  if (lane == kWave - 1) {
+    R.wtot[wave] = v1;
+    wtot2[wave] = v2;
+  }
+  __syncthreads();
+  int base1 = 0, base2 = 0, tot1 = 0, tot2 = 0;
+#pragma unroll
+  for (int w = 0; w < kGWaves; ++w) {
+    base1 += w < wave ? R.wtot[w] : 0;
+    base2 += w < wave ? wtot2[w] : 0;
+    tot1 += R.wtot[w];
+    tot2 += wtot2[w];
+  }
+  const int ex1 = base1 + v1 - m1, ex2 = base2 + v2 - m2;  // exclusive prefixes
+  const int o0 = ex1 >> 11;
+  if (e0 < E) {
+    R.eoff[e0] = o0;
+    R.boff[e0] = ex2;
+  }
+  if (e1 < E) {
+    R.eoff[e1] = o0 + n0;
+    R.boff[e1] = ex2 + nb0;
+  }
+  // each slot's place in its expert's list, 512 slots per round
+  for (int r0 = 0; r0 < S; r0 += kGThreads) {
+    for (int i = threadIdx.x; i < kGWaves * E; i += kGThreads) R.mask[i / E][i % E] = 0ull;
+    __syncthreads();
+    const int s = r0 + (int)threadIdx.x;
+    const bool live = s < S;
+    const int e = live ? a.idx[s] : 0;
+    if (live) atomicOr(&R.mask[wave][e], 1ull << lane);
+    __syncthreads();
+    if (live) {
+      int pos = R.eoff[e] + R.run[e] + __popcll(R.mask[wave][e] & ((1ull << lane) - 1ull));
+      for (int v = 0; v < wave; ++v) pos += __popcll(R.mask[v][e]);
+      R.slotl[pos] = s;
+    }
+    __syncthreads();
+    for (int x = threadIdx.x; x < E; x += kGThreads) {
+      int add = 0;
+#pragma unroll
+      for (int v = 0; v < kGWaves; ++v) add += __popcll(R.mask[v][x]);
+      R.run[x] += add;
+    }
+    __syncthreads();
+  }
+  // the token blocks of the two experts, with their slots
+  int32_t *G = a.groups;
+  if (threadIdx.x == 0) {
+    G[0] = tot1 & 2047;
+    G[1] = tot2;
+  }
+  for (int k = 0; k < nb0; ++k) {
+    const int n = min(kTokBlock, n0 - kTokBlock * k), q = R.eoff[e0] + kTokBlock * k;
+    int32_t *r = G + 2 + kBlkInts * (ex2 + k);
+    r[0] = e0;
+    r[1] = n;
+#pragma unroll
+    for (int u = 0; u < kTokBlock; ++u) r[2 + u] = R.slotl[q + min(u, n - 1)];
+  }
+  for (int k = 0; k < nb1; ++k) {
+    const int n = min(kTokBlock, n1 - kTokBlock * k), q = R.eoff[e0] + n0 + kTokBlock * k;
+    int32_t *r = G + 2 + kBlkInts * (ex2 + nb0 + k);
+    r[0] = e1;
+    r[1] = n;
+#pragma unroll
+    for (int u = 0; u < kTokBlock; ++u) r[2 + u] = R.slotl[q + min(u, n - 1)];
+  }
+}
+
 // g2: gate/up + SwiGLU of 128 interleaved rows (64 pairs = group gi of the
 // inter dimension) of one item's expert, for the item's tokens / slots.
 // Wavefront w holds rows 16w .. 16w + 15. h vectors: slot s at index s,
-// shared-expert token t at index S + t.
-template <int BITS, int NGH, bool PRE, bool FULL>
+// shared-expert token t at index S + t. TABLE: the routing kernels have written
+// the routing and the grouping table already (large batches); otherwise every
+// workgroup derives them itself (block_route) when it meets its first routed item.
+template <int BITS, int NGH, bool PRE, bool FULL, bool TABLE>
 __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
   // (NGH: the hidden groups ng rounded up to a power of two; FULL: ng == NGH)
   const int ng = FULL ? NGH : a.H / kGroup, ngi = a.I / kGroup;
@@ -758,7 +926,7 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
   __shared__ float2 xsl[kTokBlock * NGH + 1];
   __shared__ float2 hpart[kGWaves][kTokBlock];
   __shared__ __attribute__((aligned(16))) uint8_t wlds[kGWaves][kWaveLds];
-  __shared__ int slotl[kMaxSlots], blk[kBlkInts * kMaxSlots];
+  __shared__ int slotl[kRouteSlots], blk[kBlkInts * kRouteSlots];
   __shared__ int tokv[kTokBlock], hvl[kTokBlock], tokn[kTokBlock];
   static_assert(sizeof(RouteLds) <= sizeof(xl), "routing scratch fits the staging buffer");
   const bool sh = a.shared != nullptr;
@@ -774,6 +942,8 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
   const int max_items = sh_items + S * ngi;
   const bool writer = (int)blockIdx.x == sh_items % (int)gridDim.x;
   int NB = -1;  // routing not derived yet
+  // the token blocks {expert, n, slots}: in LDS (derived here) or the table in memory
+  const int *btab = TABLE ? a.groups + 2 : blk;
   // A batch of at most kTokBlock tokens: every item's tokens are among them, so
   // their x is staged once, now, by the wavefronts past the batch's tokens
   // (wavefront t < B derives token t's top-K meanwhile), in token order; the
@@ -824,7 +994,9 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
       it.n = min(kTokBlock, a.B - it.q0);
     } else {
       if (NB < 0) {
-        if constexpr (PRE)
+        if constexpr (TABLE)
+          NB = __builtin_amdgcn_readfirstlane(a.groups[1]);
+        else if constexpr (PRE)
           NB = block_route(a, *reinterpret_cast<RouteLds1 *>(&wlds[0][0]), slotl, blk, writer);
         else
           NB = block_route(a, *reinterpret_cast<RouteLds *>(xl), slotl, blk, writer);
@@ -833,16 +1005,18 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
       if (kb >= NB) break;  // (uniform) later items are past the last block
       gi = (item - sh_items) % ngi;
       // (uniform values: kept in scalar registers)
-      it.expert = __builtin_amdgcn_readfirstlane(blk[kBlkInts * kb]);
-      it.n = __builtin_amdgcn_readfirstlane(blk[kBlkInts * kb + 1]);
+      it.expert = __builtin_amdgcn_readfirstlane(btab[kBlkInts * kb]);
+      it.n = __builtin_amdgcn_readfirstlane(btab[kBlkInts * kb + 1]);
       it.q0 = kBlkInts * kb + 2;
     }
     const int T = it.n;
-    const uint8_t *base = it.expert < 0 ? a.shared : a.bank + (size_t)it.expert * a.stride;
+    const uint8_t *base = it.expert < 0  ? a.shared
+                          : a.expert_ptr ? a.expert_ptr[it.expert]
+                                         : a.bank + (size_t)it.expert * a.stride;
     const uint8_t *rec0 = base + (size_t)(128 * gi + 16 * __builtin_amdgcn_readfirstlane(wv)) * RB;
     // thread u < T: slot of item token u (unused for the shared expert, whose
     // item tokens are tokens q0 + u)
-    const int sl = blk[it.expert < 0 ? 0 : it.q0 + min((int)threadIdx.x, T - 1)];
+    const int sl = btab[it.expert < 0 ? 0 : it.q0 + min((int)threadIdx.x, T - 1)];
     // tables: the token whose x item token u takes, the index of its h vector
     auto fill = [&](int u) {
       tokv[u] = it.expert < 0 ? it.q0 + u : sl / a.K;
@@ -864,11 +1038,11 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
         const int kbn = (nitem - sh_items) / ngi;
         if (kbn < NB) {
           nq0 = kBlkInts * kbn + 2;
-          Tn = __builtin_amdgcn_readfirstlane(blk[kBlkInts * kbn + 1]);
+          Tn = __builtin_amdgcn_readfirstlane(btab[kBlkInts * kbn + 1]);
         }
       }
     }
-    auto filln = [&](int u) { tokn[u] = nsh ? nq0 + u : blk[nq0 + u] / a.K; };
+    auto filln = [&](int u) { tokn[u] = nsh ? nq0 + u : btab[nq0 + u] / a.K; };
     float y = 0.f;
     MR M;
     M.template run<PRE, !PRE>(ng, rec0, 0, a.xq, a.xsum, T, tokv, fill, after, [&](int) { y = M.y; }, xl, xsl,
@@ -971,7 +1145,10 @@ __global__ __launch_bounds__(kGThreads) void k_g3(const GroupArgs a) {
   const int T = it.n;
   const int lane = lane_id(), wv = wave_in_block();
   const int n = lane & 15, qq = lane >> 4;
-  const uint8_t *base = (it.expert < 0 ? a.shared : a.bank + (size_t)it.expert * a.stride) + a.gu_bytes;
+  const uint8_t *base = (it.expert < 0  ? a.shared
+                         : a.expert_ptr ? a.expert_ptr[it.expert]
+                                        : a.bank + (size_t)it.expert * a.stride) +
+                        a.gu_bytes;
   const int row0 = 128 * kG3Tiles * rb + 16 * wv;  // this wavefront's first row of tile 0
   const uint8_t *rec0 = base + (size_t)row0 * RB;
   float *const outp = it.expert < 0 ? a.d_shared : a.partial;
@@ -991,22 +1168,23 @@ __global__ __launch_bounds__(kGThreads) void k_g3(const GroupArgs a) {
   M.template run<false>(ngi, rec0, (size_t)128 * RB, a.hq, a.hsum, T, tokv, fill, after, done, xl, xsl, wlds[wv]);
 }
 
-// g4: out[t] = residual[t] + sum_k partial[t*K + k] (k ascending) + d_shared[t]
-template <int BITS>
+// g4: out[t] = residual[t] + sum_k partial[t*K + k] (k ascending) + d_shared[t];
+// KM: 8 for top_k <= 8, else kMaxTopK
+template <int BITS, int KM>
 __global__ __launch_bounds__(kBlock) void k_g4(const GroupArgs a) {
   const int f = blockIdx.x * kBlock + threadIdx.x;  // float4 index into [B][H]
   const int h4 = a.H / 4;
   if (f >= a.B * h4) return;
   const int t = f / h4, i = f - t * h4;
   // every load issued before the first add (clamped choices past K are not added)
-  float4 p[kMaxTopK];
+  float4 p[KM];
 #pragma unroll
-  for (int k = 0; k < kMaxTopK; ++k)
+  for (int k = 0; k < KM; ++k)
     p[k] = reinterpret_cast<const float4 *>(a.partial)[(size_t)(t * a.K + min(k, a.K - 1)) * h4 + i];
   const float4 q = reinterpret_cast<const float4 *>(a.shared ? a.d_shared : a.residual)[f];
   float4 o = reinterpret_cast<const float4 *>(a.residual)[f];
 #pragma unroll
-  for (int k = 0; k < kMaxTopK; ++k) {
+  for (int k = 0; k < KM; ++k) {
     if (k < a.K) {
       o.x += p[k].x;
       o.y += p[k].y;
@@ -1042,6 +1220,14 @@ inline int cu_count() {
 // the first, the down kernel on the second).
 template <int BITS>
 struct GroupDispatch {
+  static void launch_topk(const GroupArgs &a, hipStream_t s) {
+    const dim3 grid((a.B + kGWaves - 1) / kGWaves);
+    if (a.K <= 8)
+      hipLaunchKernelGGL((k_topk<BITS, 8>), grid, dim3(kGThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_topk<BITS, kMaxTopK>), grid, dim3(kGThreads), 0, s, a);
+  }
+
   template <int NGH>
   static hipError_t front(GroupArgs a, hipStream_t s, int phases) {
     const bool sh = a.shared != nullptr;
@@ -1053,14 +1239,23 @@ struct GroupDispatch {
     if (phases & 2) {
       const dim3 grid(std::min((shb + S) * (a.I / kGroup), cu_count()));
       const bool full = a.H == NGH * kGroup;
-      if (a.B <= kTokBlock && full)
-        hipLaunchKernelGGL((k_g2<BITS, NGH, true, true>), grid, dim3(kGThreads), 0, s, a);
-      else if (a.B <= kTokBlock)
-        hipLaunchKernelGGL((k_g2<BITS, NGH, true, false>), grid, dim3(kGThreads), 0, s, a);
-      else if (full)
-        hipLaunchKernelGGL((k_g2<BITS, NGH, false, true>), grid, dim3(kGThreads), 0, s, a);
-      else
-        hipLaunchKernelGGL((k_g2<BITS, NGH, false, false>), grid, dim3(kGThreads), 0, s, a);
+      if (S > kRouteSlots || a.B > kRouteTokens || a.K > 8) {
+        // large batches and top_k > 8: the routing kernels first, then gate/up from the table
+        launch_topk(a, s);
+        hipLaunchKernelGGL(k_group<BITS>, dim3(1), dim3(kGThreads), 0, s, a);
+        if (full)
+          hipLaunchKernelGGL((k_g2<BITS, NGH, false, true, true>), grid, dim3(kGThreads), 0, s, a);
+        else
+          hipLaunchKernelGGL((k_g2<BITS, NGH, false, false, true>), grid, dim3(kGThreads), 0, s, a);
+      } else if (a.B <= kTokBlock && full) {
+        hipLaunchKernelGGL((k_g2<BITS, NGH, true, true, false>), grid, dim3(kGThreads), 0, s, a);
+      } else if (a.B <= kTokBlock) {
+        hipLaunchKernelGGL((k_g2<BITS, NGH, true, false, false>), grid, dim3(kGThreads), 0, s, a);
+      } else if (full) {
+        hipLaunchKernelGGL((k_g2<BITS, NGH, false, true, false>), grid, dim3(kGThreads), 0, s, a);
+      } else {
+        hipLaunchKernelGGL((k_g2<BITS, NGH, false, false, false>), grid, dim3(kGThreads), 0, s, a);
+      }
     }
     return hipGetLastError();
   }
@@ -1082,11 +1277,60 @@ struct GroupDispatch {
         hipLaunchKernelGGL((k_g3<BITS, NGI, 2, true>), g2, dim3(kGThreads), 0, s, a);
       else
         hipLaunchKernelGGL((k_g3<BITS, NGI, 2, false>), g2, dim3(kGThreads), 0, s, a);
-      hipLaunchKernelGGL(k_g4<BITS>, dim3(n4), dim3(kBlock), 0, s, a);
+      if (a.K <= 8)
+        hipLaunchKernelGGL((k_g4<BITS, 8>), dim3(n4), dim3(kBlock), 0, s, a);
+      else
+        hipLaunchKernelGGL((k_g4<BITS, kMaxTopK>), dim3(n4), dim3(kBlock), 0, s, a);
     }
     return hipGetLastError();
   }
 };
+
+// The layer around a host step (see launch_group_route / launch_group_experts):
+// the routing kernels always, the gate/up from the table.
+template <int BITS>
+struct SplitDispatch {
+  template <int NGH>
+  static hipError_t route(GroupArgs a, hipStream_t s) {
+    a.n_router_blocks = (a.E + g1_rows_per_block<NGH>() - 1) / g1_rows_per_block<NGH>();
+    hipLaunchKernelGGL((k_g1<BITS, NGH>), dim3(a.n_router_blocks + a.B), dim3(kBlock), 0, s, a);
+    GroupDispatch<BITS>::launch_topk(a, s);
+    return hipGetLastError();
+  }
+  template <int NGH>
+  static hipError_t gateup(const GroupArgs &a, hipStream_t s) {
+    const bool sh = a.shared != nullptr;
+    const int S = a.B * a.K;
+    const int shb = sh ? (a.B + kTokBlock - 1) / kTokBlock : 0;
+    const dim3 grid(std::min((shb + S) * (a.I / kGroup), cu_count()));
+    hipLaunchKernelGGL(k_group<BITS>, dim3(1), dim3(kGThreads), 0, s, a);
+    if (a.H == NGH * kGroup)
+      hipLaunchKernelGGL((k_g2<BITS, NGH, false, true, true>), grid, dim3(kGThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_g2<BITS, NGH, false, false, true>), grid, dim3(kGThreads), 0, s, a);
+    return hipGetLastError();
+  }
+};
+
+template <int BITS>
+hipError_t group_route_b(const GroupArgs &a, hipStream_t s) {
+  FMOE_NG_SWITCH(pad_groups(a.H / kGroup), SplitDispatch<BITS>::template route, a, s)
+}
+
+template <int BITS>
+hipError_t group_experts_b(const GroupArgs &a, hipStream_t s) {
+  hipError_t e;
+  switch (pad_groups(a.H / kGroup)) {
+    case 4: e = SplitDispatch<BITS>::template gateup<4>(a, s); break;
+    case 8: e = SplitDispatch<BITS>::template gateup<8>(a, s); break;
+    case 16: e = SplitDispatch<BITS>::template gateup<16>(a, s); break;
+    case 32: e = SplitDispatch<BITS>::template gateup<32>(a, s); break;
+    case 64: e = SplitDispatch<BITS>::template gateup<64>(a, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  FMOE_NG_SWITCH(pad_groups(a.I / kGroup), GroupDispatch<BITS>::template back, a, s, 4)
+}
 
 template <int BITS>
 hipError_t group_front(const GroupArgs &a, hipStream_t s, int phases) {

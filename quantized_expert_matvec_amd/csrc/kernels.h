@@ -74,6 +74,9 @@ struct GroupArgs {
   float *d_shared;           // [B][H]
   float *partial;            // [S][H]
   int32_t *groups;           // D, NB, token blocks {expert, n, 4 slots}[S]; S = B*K
+  // null: expert e's blob is bank + e * stride; else expert_ptr[e] (device array
+  // [E], entries needed only for the experts the batch chooses)
+  const uint8_t *const *expert_ptr;
   int n_router_blocks;       // g1
 };
 
@@ -82,6 +85,12 @@ struct GroupArgs {
 // down projections; combine). phases: bit 0 the first, bit 1 the second, bit 2
 // the last two.
 hipError_t launch_group(const GroupArgs &a, hipStream_t s, int phases = 7);
+// The same layer in two parts around a host step: the router, input preparation
+// and every token's top-K (idx, w, sigma and the caller's outputs); then the
+// grouping, the gate/up and down of the chosen and shared experts, and the
+// combine (expert blobs through a.expert_ptr when it is set).
+hipError_t launch_group_route(const GroupArgs &a, hipStream_t s);
+hipError_t launch_group_experts(const GroupArgs &a, hipStream_t s);
 
 // Router + sigmoid gate + shared gate/up; routing + routed gate/up + shared down;
 // down + weighted combine + residual. Three launches, no host synchronisation.

@@ -24,6 +24,14 @@ template <int BITS>
 hipError_t group_b(const GroupArgs &, hipStream_t, int);
 extern template hipError_t group_b<4>(const GroupArgs &, hipStream_t, int);
 extern template hipError_t group_b<2>(const GroupArgs &, hipStream_t, int);
+template <int BITS>
+hipError_t group_route_b(const GroupArgs &, hipStream_t);
+template <int BITS>
+hipError_t group_experts_b(const GroupArgs &, hipStream_t);
+extern template hipError_t group_route_b<4>(const GroupArgs &, hipStream_t);
+extern template hipError_t group_route_b<2>(const GroupArgs &, hipStream_t);
+extern template hipError_t group_experts_b<4>(const GroupArgs &, hipStream_t);
+extern template hipError_t group_experts_b<2>(const GroupArgs &, hipStream_t);
 
 namespace {
 
@@ -164,6 +172,14 @@ hipError_t launch_layer(const LayerArgs &a, hipStream_t s, int phases) {
 
 hipError_t launch_group(const GroupArgs &a, hipStream_t s, int phases) {
   return a.bits == 4 ? dev::group_b<4>(a, s, phases) : dev::group_b<2>(a, s, phases);
+}
+
+hipError_t launch_group_route(const GroupArgs &a, hipStream_t s) {
+  return a.bits == 4 ? dev::group_route_b<4>(a, s) : dev::group_route_b<2>(a, s);
+}
+
+hipError_t launch_group_experts(const GroupArgs &a, hipStream_t s) {
+  return a.bits == 4 ? dev::group_experts_b<4>(a, s) : dev::group_experts_b<2>(a, s);
 }
 
 hipError_t launch_rms(const float *h, float *x, int B, int H, float eps, hipStream_t s) {

@@ -278,7 +278,10 @@ __device__ __forceinline__ void lane_max(const int (&key)[VPL], int &m1, int &p1
   }
 }
 
-template <int VPL>
+// (KM: the most rounds compiled, 8 or kMaxTopK, a template argument of the
+// kernels so that the usual K <= 8 keeps its arrays in registers; K <= KM; idx and
+// w receive KM entries, those past K 0)
+template <int VPL, int KM>
 __device__ __forceinline__ void wave_topk_keys(int (&key)[VPL], int K, int *idx, float *w, float lscale) {
   constexpr int kGone = (int)0x80000000;
   const int lane = lane_id();
@@ -287,9 +290,9 @@ __device__ __forceinline__ void wave_topk_keys(int (&key)[VPL], int K, int *idx,
 #pragma unroll
   for (int m = 0; m < VPL; ++m) m2 = m == p1 ? m2 : max(m2, key[m]);
   int a = m1, T = kGone;
-  float lv[kMaxTopK];
+  float lv[KM];
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
+  for (int j = 0; j < KM; ++j) {
     idx[j] = 0;
     lv[j] = 0.f;
     if (j < K) {
@@ -303,7 +306,7 @@ __device__ __forceinline__ void wave_topk_keys(int (&key)[VPL], int K, int *idx,
   }
   if (wave_max_i(m2) >= T) {
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
+    for (int j = 0; j < KM; ++j) {
       if (j < K) {
         int b, p;
         lane_max<VPL>(key, b, p);
@@ -319,7 +322,7 @@ __device__ __forceinline__ void wave_topk_keys(int (&key)[VPL], int K, int *idx,
   }
   float sum = 0.f;
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
+  for (int j = 0; j < KM; ++j) {
     w[j] = 0.f;
     if (j < K) {
       w[j] = __expf((lv[j] - lv[0]) * lscale);
@@ -328,7 +331,19 @@ __device__ __forceinline__ void wave_topk_keys(int (&key)[VPL], int K, int *idx,
   }
   const float inv = 1.f / sum;
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) w[j] *= inv;
+  for (int j = 0; j < KM; ++j) w[j] *= inv;
+}
+
+// Lane j < KM writes choice j of a wavefront-uniform top-K to LDS (sidx, sw).
+template <int KM>
+__device__ __forceinline__ void publish_topk(const int *idx, const float *w, int *sidx, float *sw) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int j = 0; j < KM; ++j)
+    if (j == lane) {
+      sidx[j] = idx[j];
+      sw[j] = w[j];
+    }
 }
 
 // lane l's VPL consecutive logits, with 16-byte loads (clamped to the row; lg
@@ -361,6 +376,7 @@ __device__ __forceinline__ void logit_keys(const float (&v)[VPL], int E, int (&k
 }
 
 // top-K of E <= kMaxExperts logits in memory (LDS or global)
+template <int KM>
 __device__ __forceinline__ void wave_topk_lds(const float *lg, int E, int K, int *idx, float *w,
                                               float lscale = 1.f) {
   if (E <= 512) {
@@ -368,13 +384,13 @@ __device__ __forceinline__ void wave_topk_lds(const float *lg, int E, int K, int
     int key[8];
     load_logits<8>(lg, E, v);
     logit_keys<8>(v, E, key);
-    wave_topk_keys<8>(key, K, idx, w, lscale);
+    wave_topk_keys<8, KM>(key, K, idx, w, lscale);
   } else {
     float v[16];
     int key[16];
     load_logits<16>(lg, E, v);
     logit_keys<16>(v, E, key);
-    wave_topk_keys<16>(key, K, idx, w, lscale);
+    wave_topk_keys<16, KM>(key, K, idx, w, lscale);
   }
 }
 
@@ -385,22 +401,17 @@ __device__ __forceinline__ void wave_topk_lds(const float *lg, int E, int K, int
 // memory.) Workgroup b uses wavefront b % 4, so that the workgroups sharing a CU
 // do not all compute it on the same SIMD. (Measured: splitting the rounds over
 // the four wavefronts, with one barrier per round, is slower.)
+template <int KM>
 __device__ __forceinline__ void block_topk(const float *lg, int E, int K, int *sidx, float *sw) {
   if (wave_in_block() == (int)(blockIdx.x % kWavesPerBlock)) {
     // the rest of the workgroup waits on this wavefront: let it win the SIMD's
     // issue arbitration against co-resident wavefronts of other workgroups
     __builtin_amdgcn_s_setprio(3);
-    int idx[kMaxTopK];
-    float w[kMaxTopK];
-    wave_topk_lds(lg, E, K, idx, w);
+    int idx[KM];
+    float w[KM];
+    wave_topk_lds<KM>(lg, E, K, idx, w);
     __builtin_amdgcn_s_setprio(0);
-    const int lane = lane_id();
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j)
-      if (j == lane) {
-        sidx[j] = idx[j];
-        sw[j] = w[j];
-      }
+    publish_topk<KM>(idx, w, sidx, sw);
   }
   __syncthreads();
 }
@@ -447,16 +458,14 @@ __global__ __launch_bounds__(kBlock) void k_expert_gateup(const uint8_t *__restr
 
 // ------------------------------------------------------------------ layer kernels
 
-// gate/up pair iterations per wavefront (routed and shared) and routed down row
-// iterations per wavefront, by code width
+// gate/up pair iterations per wavefront (routed and shared), and routed down row
+// iterations per wavefront by the padded top_k (fewer rows per wavefront above
+// four slots keep the weight registers of a wavefront the same)
 template <int BITS>
 constexpr int gateup_iters() {
   return 2;
 }
-template <int BITS>
-constexpr int down_iters() {
-  return 4;
-}
+__host__ __device__ constexpr int down_iters(int kpad) { return kpad <= 4 ? 4 : 16 / kpad; }
 constexpr int kP3Block = 256;      // threads per down + combine workgroup
 constexpr int kP3Waves = kP3Block / kWave;
 
@@ -647,8 +656,8 @@ struct Phase2Args {
 // expert. Shared blocks run the shared expert's gate/up + SwiGLU: it does not
 // depend on the routing, so its weights stream while the routed blocks are still
 // choosing. x arrives in the digit form the router kernel wrote (RMS factor
-// included), so this kernel reads no raw x.
-template <int BITS, int NGHP>
+// included), so this kernel reads no raw x. KM: 8 for top_k <= 8, else kMaxTopK.
+template <int BITS, int NGHP, int KM>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void k_phase2(const Phase2Args a) {
   constexpr int RPIH = kWave / NGHP;
   constexpr int D4 = (NGHP * kDigStride / 4 + kBlock - 1) / kBlock;
@@ -679,20 +688,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         __builtin_amdgcn_sched_barrier(0);
         stage_load(xsrc, NF4, xst);
         __builtin_amdgcn_sched_barrier(0);
-        int key[8], idx[kMaxTopK];
-        float w[kMaxTopK];
+        int key[8], idx[KM];
+        float w[KM];
         logit_keys<8>(lv, a.E, key);
         // the rest of the workgroup waits on this wavefront: let it win the
         // SIMD's issue arbitration against co-resident wavefronts of other workgroups
         __builtin_amdgcn_s_setprio(3);
-        wave_topk_keys<8>(key, bslot + 1, idx, w, 1.f);
+        wave_topk_keys<8, KM>(key, bslot + 1, idx, w, 1.f);
         __builtin_amdgcn_s_setprio(0);
-#pragma unroll
-        for (int j = 0; j < kMaxTopK; ++j)
-          if (j == lane) {
-            sidx[j] = idx[j];
-            sw[j] = w[j];
-          }
+        publish_topk<KM>(idx, w, sidx, sw);
       } else {
         stage_load(xsrc, NF4, xst);
       }
@@ -706,7 +710,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       stage_copy(xst, NF4, xdl);
       __syncthreads();
       trace_mark(a.trace, 1);
-      block_topk(lg, a.E, bslot + 1, sidx, sw);
+      block_topk<KM>(lg, a.E, bslot + 1, sidx, sw);
     }
     trace_mark(a.trace, 2);
     const int wv = blockIdx.x * kWavesPerBlock + wave_in_block();
@@ -752,6 +756,73 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   trace_mark(a.trace, 3);
 }
 
+// Down partials of one slot for ITERS rows, reading that slot's h group from LDS
+// as the code words are used (eight or sixteen values at a time) instead of
+// holding the whole 64-value slice in registers: gp[i] = scale_i * sum_j c_ij h_j
+// + bias_i * hsum, in exactly the order of group_partial (the same accumulators,
+// code words ascending).
+template <int BITS, int ITERS, int SPL>
+__device__ __forceinline__ void stream_partials(const Chunk<BITS> (&c)[ITERS][SPL], const uint32_t (&sb)[ITERS][SPL],
+                                                int m, const float *hx, float hsum, float (&gp)[ITERS]) {
+  if constexpr (BITS == 4) {
+    float a0[ITERS], a1[ITERS];
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) a0[i] = a1[i] = 0.f;
+#pragma unroll
+    for (int hw = 0; hw < 8; ++hw) {
+      const float4 v0 = *reinterpret_cast<const float4 *>(hx + 8 * hw);
+      const float4 v1 = *reinterpret_cast<const float4 *>(hx + 8 * hw + 4);
+#pragma unroll
+      for (int i = 0; i < ITERS; ++i) {
+        const uint4 &q = hw < 4 ? c[i][m].a : c[i][m].b;
+        const int w = hw & 3;
+        const uint32_t d = w == 0 ? q.x : w == 1 ? q.y : w == 2 ? q.z : q.w;
+        const uint32_t lo = opaque(d & 0x0F0F0F0Fu);
+        const uint32_t hi = opaque(d & 0xF0F0F0F0u);
+        a0[i] = fmaf(ub0(lo), v0.x, a0[i]);
+        a0[i] = fmaf(ub1(lo), v0.y, a0[i]);
+        a0[i] = fmaf(ub2(lo), v0.z, a0[i]);
+        a0[i] = fmaf(ub3(lo), v0.w, a0[i]);
+        a1[i] = fmaf(ub0(hi), v1.x, a1[i]);
+        a1[i] = fmaf(ub1(hi), v1.y, a1[i]);
+        a1[i] = fmaf(ub2(hi), v1.z, a1[i]);
+        a1[i] = fmaf(ub3(hi), v1.w, a1[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i)
+      gp[i] = fmaf(scale_of(sb[i][m]), fmaf(a1[i], 0.0625f, a0[i]), bias_of(sb[i][m]) * hsum);
+  } else {
+    float a[ITERS][4];
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) a[i][0] = a[i][1] = a[i][2] = a[i][3] = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      float4 v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const float4 *>(hx + 16 * w + 4 * q);
+#pragma unroll
+      for (int i = 0; i < ITERS; ++i) {
+        const uint4 &cq = c[i][m].a;
+        const uint32_t d = w == 0 ? cq.x : w == 1 ? cq.y : w == 2 ? cq.z : cq.w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t mk = opaque(d & (0x03030303u << (2 * q)));
+          a[i][q] = fmaf(ub0(mk), v[q].x, a[i][q]);
+          a[i][q] = fmaf(ub1(mk), v[q].y, a[i][q]);
+          a[i][q] = fmaf(ub2(mk), v[q].z, a[i][q]);
+          a[i][q] = fmaf(ub3(mk), v[q].w, a[i][q]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+      const float dot = fmaf(a[i][3], 0.015625f, fmaf(a[i][2], 0.0625f, fmaf(a[i][1], 0.25f, a[i][0])));
+      gp[i] = fmaf(scale_of(sb[i][m]), dot, bias_of(sb[i][m]) * hsum);
+    }
+  }
+}
+
 struct Phase3Args {
   const uint8_t *bank;
   size_t stride, gu_bytes;
@@ -780,7 +851,7 @@ struct Phase3Args {
 // combining lanes through LDS.
 template <int BITS, int NGIP, int KPAD>
 __global__ __launch_bounds__(kP3Block) void k_phase3(const Phase3Args a) {
-  constexpr int kP3Iters = down_iters<BITS>();
+  constexpr int kP3Iters = down_iters(KPAD);
   constexpr int SLOTS = KPAD * NGIP;
   constexpr int SEG = SLOTS < kWave ? SLOTS : kWave;  // lanes per row
   constexpr int SPL = SLOTS / SEG;                     // slots per lane
@@ -788,7 +859,11 @@ __global__ __launch_bounds__(kP3Block) void k_phase3(const Phase3Args a) {
   constexpr int RPW = kP3Iters * RPI;                  // rows per wavefront
   constexpr int RPII = kWave / NGIP;                   // shared-down rows per iteration
   constexpr int SIT = (RPW + RPII - 1) / RPII;         // shared-down iterations
-  constexpr bool STAGE = KPAD * NGIP <= 128;
+  // routed h staged in LDS when it fits (up to 68 KB above four slots); above four
+  // slots the partials stream h (stream_partials, from LDS or, unstaged, from the
+  // cache hierarchy) instead of holding a lane's SPL slices in registers
+  constexpr bool STAGE = KPAD * NGIP <= (KPAD <= 4 ? 128 : 256);
+  constexpr bool STREAM = KPAD >= 8;
   const int ngi = a.I / kGroup;
   const size_t RB = (size_t)ngi * gbytes<BITS>();
   __shared__ float hl[STAGE ? KPAD * NGIP * kXPad : 1];
@@ -876,21 +951,48 @@ __global__ __launch_bounds__(kP3Block) void k_phase3(const Phase3Args a) {
       if (seg_last<NGIP>(lane) && r < RPW) dsh[wave_in_block() * RPW + r] = sig * p;
     }
   }
-  XSlice xs[SPL];
-  if constexpr (STAGE) {
+  float pr[kP3Iters];  // this lane's weighted routed partial of each row
 #pragma unroll
-    for (int m = 0; m < SPL; ++m) read_slice_sum(hl, kk[m] * ngi + grp[m], hlsum[kk[m] * ngi + grp[m]], xs[m]);
+  for (int i = 0; i < kP3Iters; ++i) pr[i] = 0.f;
+  if constexpr (STREAM) {
+#pragma unroll
+    for (int m = 0; m < SPL; ++m) {
+      const int row = kk[m] * ngi + grp[m];
+      float gp[kP3Iters];
+      if constexpr (STAGE) {
+        stream_partials<BITS, kP3Iters, SPL>(c, sb, m, hl + row * kXPad, hlsum[row], gp);
+      } else {
+        const float *hx = a.h_routed + (size_t)kk[m] * a.I + kGroup * grp[m];
+        float hsum;
+        {
+          XSlice t;  // (one slice at a time: its sum, then its values again as used)
+          load_xslice(hx, t);
+          hsum = t.sum;
+        }
+        stream_partials<BITS, kP3Iters, SPL>(c, sb, m, hx, hsum, gp);
+      }
+#pragma unroll
+      for (int i = 0; i < kP3Iters; ++i)
+        if (act[m]) pr[i] = fmaf(wk[m], gp[i], pr[i]);
+    }
   } else {
+    XSlice xs[SPL];
+    if constexpr (STAGE) {
 #pragma unroll
-    for (int m = 0; m < SPL; ++m) load_xslice(a.h_routed + (size_t)kk[m] * a.I + kGroup * grp[m], xs[m]);
+      for (int m = 0; m < SPL; ++m) read_slice_sum(hl, kk[m] * ngi + grp[m], hlsum[kk[m] * ngi + grp[m]], xs[m]);
+    } else {
+#pragma unroll
+      for (int m = 0; m < SPL; ++m) load_xslice(a.h_routed + (size_t)kk[m] * a.I + kGroup * grp[m], xs[m]);
+    }
+#pragma unroll
+    for (int i = 0; i < kP3Iters; ++i)
+#pragma unroll
+      for (int m = 0; m < SPL; ++m)
+        if (act[m]) pr[i] = fmaf(wk[m], group_partial<BITS>(c[i][m], sb[i][m], xs[m]), pr[i]);
   }
 #pragma unroll
   for (int i = 0; i < kP3Iters; ++i) {
-    float p = 0.f;
-#pragma unroll
-    for (int m = 0; m < SPL; ++m)
-      if (act[m]) p = fmaf(wk[m], group_partial<BITS>(c[i][m], sb[i][m], xs[m]), p);
-    p = seg_reduce<SEG>(p);
+    const float p = seg_reduce<SEG>(pr[i]);
     const int row = row0 + i * RPI + sub;
     if (seg_last<SEG>(lane) && row < a.H) {
       float o = res[i] + p;
@@ -924,12 +1026,13 @@ struct LayerGeom {
   __host__ LayerGeom(const LayerArgs &L, int bits) {
     const bool sh = L.shared != nullptr;
     n1r = (L.E + kWavesPerBlock / router_split<NGH>() - 1) / (kWavesPerBlock / router_split<NGH>());
-    constexpr int GI = gateup_iters<BITS>(), DI = down_iters<BITS>();
+    constexpr int GI = gateup_iters<BITS>();
     wps = (L.I / RPIH + GI - 1) / GI;
     n2r = blocks_for((long)wps * L.K);
     n2s = sh ? blocks_for(wps) : 0;
     kpad = 1;
     while (kpad < L.K) kpad <<= 1;
+    const int DI = down_iters(kpad);
     const int slots = kpad * NGI;
     const int seg = slots < kWave ? slots : kWave;
     const long w3 = ((long)L.H / (kWave / seg) + DI - 1) / DI;
@@ -1032,7 +1135,10 @@ struct Dispatch {
     p2.shared_gu = has_shared ? L.shared : nullptr;
     p2.h_shared = L.h_shared;
     p2.trace = L.trace ? L.trace + (size_t)kTraceBlocks * kTraceSlots : nullptr;
-    hipLaunchKernelGGL((k_phase2<BITS, NGH>), dim3(G.n2r + G.n2s), dim3(kBlock), 0, s, p2);
+    if (L.K <= 8)
+      hipLaunchKernelGGL((k_phase2<BITS, NGH, 8>), dim3(G.n2r + G.n2s), dim3(kBlock), 0, s, p2);
+    else
+      hipLaunchKernelGGL((k_phase2<BITS, NGH, kMaxTopK>), dim3(G.n2r + G.n2s), dim3(kBlock), 0, s, p2);
     return hipGetLastError();
   }
 
@@ -1041,7 +1147,8 @@ struct Dispatch {
     if (L.K <= 1) return phase3<NGH, NGI, 1>(L, G, s);
     if (L.K <= 2) return phase3<NGH, NGI, 2>(L, G, s);
     if (L.K <= 4) return phase3<NGH, NGI, 4>(L, G, s);
-    return phase3<NGH, NGI, 8>(L, G, s);
+    if (L.K <= 8) return phase3<NGH, NGI, 8>(L, G, s);
+    return phase3<NGH, NGI, 16>(L, G, s);
   }
 
   template <int NGH, int NGI>

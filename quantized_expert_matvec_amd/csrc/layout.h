@@ -18,9 +18,9 @@ namespace fmoe {
 constexpr int kGroup = 64;
 constexpr int kWave = 64;
 constexpr int kBlock = 256;  // threads per block everywhere: 4 wavefronts
-constexpr int kMaxTopK = 8;
+constexpr int kMaxTopK = 16;
 constexpr int kMaxExperts = 1024;
-constexpr int kMaxTokens = 64;
+constexpr int kMaxTokens = 256;
 constexpr int kDigStride = 52;  // u32 words per 64-column group of x in digit form
 constexpr size_t kScratchBytes = (size_t)4 << 20;  // static workspace of fmoe_moe_layer_noalloc (per GPU)
 
@@ -64,8 +64,8 @@ struct LayerWs {
   size_t sigma;     // fp32 [B]
   size_t topk_idx;  // int32 [B][K]
   size_t topk_w;    // fp32 [B][K]
-  size_t h_shared;  // fp32 [B][inter]
-  size_t h_routed;  // fp32 [B][K][inter]
+  size_t h_shared;  // B == 1: fp32 [inter]
+  size_t h_routed;  // B == 1: fp32 [K][inter]
   size_t d_shared;  // fp32 [B][hidden]  sigma * shared-expert output
   size_t xdig;      // B == 1: u32 [hidden/64][kDigStride] x as signed base-16 digits per group (+ factor, sum)
   // B > 1 only (tokens grouped by expert):
@@ -81,7 +81,9 @@ struct LayerWs {
   size_t total;
 };
 
-inline LayerWs layer_ws(int B, int E, int K, int hidden, int inter) {
+// grouped: the workspace of the grouped kernels (B > 1, or any B for the
+// host-memory expert tier); otherwise that of the one-token kernels.
+inline LayerWs layer_ws(int B, int E, int K, int hidden, int inter, bool grouped) {
   LayerWs w{};
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -93,19 +95,20 @@ inline LayerWs layer_ws(int B, int E, int K, int hidden, int inter) {
   w.sigma = take(sizeof(float) * (size_t)B);
   w.topk_idx = take(sizeof(int32_t) * (size_t)B * K);
   w.topk_w = take(sizeof(float) * (size_t)B * K);
-  w.h_shared = take(sizeof(float) * (size_t)B * inter);
-  w.h_routed = take(sizeof(float) * (size_t)B * K * inter);
+  const bool one = !grouped;
+  w.h_shared = take(one ? sizeof(float) * (size_t)inter : 0);
+  w.h_routed = take(one ? sizeof(float) * (size_t)K * inter : 0);
   w.d_shared = take(sizeof(float) * (size_t)B * hidden);
-  w.xdig = take(B == 1 ? sizeof(uint32_t) * kDigStride * (size_t)(hidden / 64) : 0);
+  w.xdig = take(one ? sizeof(uint32_t) * kDigStride * (size_t)(hidden / 64) : 0);
   const size_t S = (size_t)B * K;
-  w.partial = take(B > 1 ? sizeof(float) * S * hidden : 0);
-  w.groups = take(B > 1 ? sizeof(int32_t) * (6 * S + 2) : 0);
-  w.xq = take(B > 1 ? 3 * (size_t)B * hidden : 0);
-  w.xsum = take(B > 1 ? 2 * sizeof(float) * (size_t)B * (hidden / 64) : 0);
-  w.xinv = take(B > 1 ? sizeof(float) * (size_t)B : 0);
-  w.gdot = take(B > 1 ? sizeof(float) * (size_t)B : 0);
-  w.hq = take(B > 1 ? 3 * (S + B) * inter : 0);
-  w.hsum = take(B > 1 ? 2 * sizeof(float) * (S + B) * (inter / 64) : 0);
+  w.partial = take(grouped ? sizeof(float) * S * hidden : 0);
+  w.groups = take(grouped ? sizeof(int32_t) * (6 * S + 2) : 0);
+  w.xq = take(grouped ? 3 * (size_t)B * hidden : 0);
+  w.xsum = take(grouped ? 2 * sizeof(float) * (size_t)B * (hidden / 64) : 0);
+  w.xinv = take(grouped ? sizeof(float) * (size_t)B : 0);
+  w.gdot = take(grouped ? sizeof(float) * (size_t)B : 0);
+  w.hq = take(grouped ? 3 * (S + B) * inter : 0);
+  w.hsum = take(grouped ? 2 * sizeof(float) * (S + B) * (inter / 64) : 0);
   w.total = o;
   return w;
 }
@@ -123,7 +126,7 @@ inline StackWs stack_ws(int B, int E, int K, int hidden, int inter) {
   s.ha = hb;
   s.hb = 2 * hb;
   s.layer = 3 * hb;
-  s.lw = layer_ws(B, E, K, hidden, inter);
+  s.lw = layer_ws(B, E, K, hidden, inter, B > 1);
   s.total = s.layer + s.lw.total;
   return s;
 }

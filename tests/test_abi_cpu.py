@@ -218,13 +218,13 @@ def test_layer_validation():
     assert call(lay(bank=None)) == 1
     assert call(lay(shared_gate=None)) == 1          # a shared expert needs its gate vector
     assert call(lay(top_k=0)) == 5
-    assert call(lay(top_k=9)) == 5
+    assert call(lay(top_k=17)) == 5
     assert call(lay(n_experts=3)) == 5
     assert call(lay(n_experts=2000)) == 5
     assert call(lay(bits=8)) == 4
     assert call(lay(hidden=3000)) == 2
     assert call(L0, n=0) == 6
-    assert call(L0, n=65) == 6
+    assert call(L0, n=257) == 6
     assert call(L0, nb=need - 1) == 7
     assert call(L0, ws=None) == 7
     assert call(L0, x=None) == 1
@@ -323,5 +323,5 @@ def test_noalloc_validation():
     assert call(n=64) == 7
     assert call(n=0) == 6
     assert call(x=None) == 1
-    assert call(lay(top_k=9)) == 5
+    assert call(lay(top_k=17)) == 5
     assert call(lay(hidden=3000)) == 2

@@ -435,7 +435,7 @@ def test_stack_vs_oracle(device, B):
             h = ref
 
 
-@pytest.mark.parametrize("B", [1, 4])
+@pytest.mark.parametrize("B", [1, 4, 16])
 def test_stack_full_size(device, B):
     """Two full-size q4 layers (512 experts + shared, hidden 4096, inter 1024, generated and
     packed on the device) as a stack, RMS scaling folded into each layer's kernels, every
@@ -453,8 +453,12 @@ def test_stack_full_size(device, B):
     for t in range(B):
         h = h0[t].astype(np.float64)
         for l in range(n_layers):
-            ref, ri, rw, logits = OLs[l].forward(oracle.rms_scale(h), h)
-            assert list(gi[l, t]) == list(ri), (l, t)
+            x = oracle.rms_scale(h)
+            ref, ri, rw, logits = OLs[l].forward(x, h)
+            if list(gi[l, t]) != list(ri):
+                # a near-tie: checked against the oracle's layer on the GPU's routing
+                assert near_tie(logits, OLs[l].R, x, k, gi[l, t]), (l, t, gi[l, t], ri)
+                ref, _ = forward_with_routing(OLs[l], x, h, gi[l, t])
             assert_close(ha[l, t], ref, f"full stack B={B} token {t} layer {l}")
             h = ref
     del layers
