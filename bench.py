@@ -66,6 +66,11 @@ def parse():
     p.add_argument("--forms", action="store_true",
                    help="time the standalone 1024 x 4096 matvec in each form of the per-weight dequant arithmetic "
                         "(q4 and q2) instead of the stack")
+    p.add_argument("--tier-slots", type=str, default=None,
+                   help="time the host-memory expert tier instead of the resident stack: comma-separated HBM cache "
+                        "sizes in expert slots ('pages' = the pages' page-cache share of the bank, 35 of 209 GB); "
+                        "one JSON line each, plus one for a repeated token (every expert a hit)")
+    p.add_argument("--tier-layers", type=int, default=8, help="layers whose routed banks sit in pinned host memory")
     p.add_argument("--timeline", action="store_true",
                    help="print device-clock stamps of a few layers' kernels inside the graph-captured stack (B=1) "
                         "instead of timing")
@@ -89,6 +94,131 @@ class Filler:
         for j, (tid, r, c) in enumerate([(s.T_GATE, I, H), (s.T_UP, I, H), (s.T_DOWN, H, I)]):
             s.dev_qmat(seed, layer, expert_id, tid, bits, r, c, self.codes[j], self.scale[j], self.bias[j], st)
         self.qem.fmoe_pack_expert_device(bits, H, I, self.codes, self.scale, self.bias, blob_out)
+
+
+def tier(a):
+    """The host-memory expert tier: the routed banks of --tier-layers layers in pinned host
+    memory, an HBM cache of expert slots shared by the layers. A step runs the layers in
+    order (RMS scaling, then the tiered layer call: routing on the GPU, one read-back,
+    copies of the misses, the experts from their slots). Fresh synthetic tokens every
+    step (uniform routing: the hit rate is about the cache's share of the bank); the last
+    line repeats one token (every expert a hit after the first step), the call's floor."""
+    import numpy as np
+    import psutil
+    import torch
+
+    import synth
+    import quantized_expert_matvec_amd as qem
+
+    dev = torch.device("cuda:0")
+    H, I, E, K, B, bits = a.hidden, a.inter, a.experts, a.topk, a.batch, a.bits
+    eb = qem.fmoe_expert_bytes(bits, H, I)
+    bank_bytes = E * eb
+    avail = psutil.virtual_memory().available
+    n_layers = max(1, min(a.tier_layers, int(0.4 * avail // bank_bytes)))
+    if n_layers < a.tier_layers:
+        log(f"bench: tier with {n_layers} layers ({avail / 2**30:.0f} GiB host memory available)")
+    log(f"bench: filling {n_layers} host banks x {bank_bytes / 1e9:.2f} GB (pinned)")
+    t0 = time.time()
+    filler = Filler(torch, synth, qem, H, I, dev)
+    stage = torch.empty(bank_bytes, dtype=torch.uint8, device=dev)
+    layers, keep = [], []
+    for l in range(n_layers):
+        for e in range(E):
+            filler.expert(a.seed, l, e, bits, stage[e * eb:(e + 1) * eb])
+        host = torch.empty(bank_bytes, dtype=torch.uint8, pin_memory=True)
+        host.copy_(stage)
+        sh = torch.empty(eb, dtype=torch.uint8, device=dev)
+        filler.expert(a.seed, l, synth.SHARED_EXPERT, bits, sh)
+        R = torch.from_numpy(synth.router(a.seed, l, E, H)).to(dev)
+        g = torch.from_numpy(synth.shared_gate(a.seed, l, H)).to(dev)
+        keep.append((host, sh, R, g))
+        layers.append(qem.Layer(R, g, host, sh, E, K, H, I, bits))
+    torch.cuda.synchronize()
+    del stage, filler
+    log(f"bench: fill done in {time.time() - t0:.1f} s")
+
+    # host-to-device rate of one expert blob at a time (the tier's unit of transfer)
+    probe = torch.empty(4 * eb, dtype=torch.uint8, device=dev)
+    src = keep[0][0]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for rep_ in range(2):
+        e0.record()
+        for r in range(16):
+            for j in range(4):
+                probe[j * eb:(j + 1) * eb].copy_(src[((4 * r + j) * 37 % E) * eb:][:eb], non_blocking=True)
+        e1.record()
+        torch.cuda.synchronize()
+    h2d_gbps = 64 * eb / (e0.elapsed_time(e1) * 1e6)
+    del probe
+
+    h = torch.empty((B, H), dtype=torch.float32, device=dev)
+    h2 = torch.empty_like(h)
+    x = torch.empty_like(h)
+    ws = torch.empty(qem.fmoe_tiered_workspace_bytes(layers[0], B), dtype=torch.uint8, device=dev)
+
+    def tokens(i):
+        return torch.from_numpy(synth.activations(a.seed, synth.T_H0, i, B, H)).to(dev)
+
+    def step(cache, h0):
+        nonlocal h, h2
+        h.copy_(h0)
+        for l in range(n_layers):
+            qem.fmoe_rms_scale(h, x)
+            qem.fmoe_moe_layer_tiered(cache, l, layers[l], x, h, out=h2, ws=ws)
+            h, h2 = h2, h
+        torch.cuda.synchronize()
+
+    total_slots = n_layers * E
+    sizes = []
+    for t in a.tier_slots.split(","):
+        t = t.strip()
+        sizes.append(max(K * B, round(total_slots * 35 / 209)) if t == "pages" else int(t))
+    for n_slots, repeat in [(n, False) for n in sizes] + [(max(sizes), True)]:
+        buf_bytes = qem.fmoe_cache_device_bytes(bits, H, I, E, n_slots)
+        cache = qem.ExpertCache(bits, H, I, E, n_slots, dev)
+        warm = a.warmup + (1 if repeat else int(np.ceil(2 * n_slots / (K * B * n_layers))))
+        log(f"bench: tier {n_slots} slots{' (repeated token)' if repeat else ''}: {warm} warm-up steps")
+        tok = 0
+        for s in range(warm):
+            step(cache, tokens(0 if repeat else tok))
+            tok += 1
+        st0 = cache.stats()
+        times = []
+        for s in range(a.steps):
+            h0 = tokens(0 if repeat else tok)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            step(cache, h0)
+            times.append(time.perf_counter() - t1)
+            tok += 1
+        st1 = cache.stats()
+        hits, misses = st1["hits"] - st0["hits"], st1["misses"] - st0["misses"]
+        copied = st1["bytes_copied"] - st0["bytes_copied"]
+        per_layer = np.array(times) * 1e6 / n_layers
+        us_layer = float(np.sum(times) * 1e6 / (a.steps * n_layers))
+        rec = {
+            "metric": f"µs per MoE layer, routed experts in host memory behind an HBM cache "
+                      f"(top-{K} + shared, {bits}-bit, B={B})",
+            "value": round(us_layer, 2), "unit": "us/layer", "higher_is_better": False,
+            "steps": a.steps, "warmup": warm,
+            "config": {"workload": f"moe_stack_q{bits}_B{B}_host_tier", "layers": n_layers, "batch": B,
+                       "experts": E, "top_k": K, "hidden": H, "inter": I, "group": 64,
+                       "cache_slots": n_slots, "cache_share_of_bank": round(n_slots / total_slots, 4),
+                       "cache_GB": round(buf_bytes / 1e9, 2), "host_bank_GB": round(n_layers * bank_bytes / 1e9, 2),
+                       "tokens": "one token repeated" if repeat else "fresh synthetic tokens each step"},
+            "us_per_layer_p10_p50_p90": [round(float(v), 1) for v in np.percentile(per_layer, [10, 50, 90])],
+            "hit_rate": round(hits / max(1, hits + misses), 4),
+            "distinct_experts_per_layer": round((hits + misses) / (a.steps * n_layers), 3),
+            "misses_per_layer": round(misses / (a.steps * n_layers), 3),
+            "copied_MB_per_layer": round(copied / (a.steps * n_layers) / 1e6, 2),
+            "h2d_GBps_one_expert_copies": round(h2d_gbps, 1),
+            "data": "synthetic (seeded; random-init weights of the workload's shapes)",
+        }
+        print(json.dumps(rec, ensure_ascii=False), flush=True)
+        cache.close()
+        del cache
+        torch.cuda.empty_cache()
 
 
 def calibrate_copy():
@@ -384,6 +514,9 @@ def main():
     if a.forms:
         forms(a)
         return
+    if a.tier_slots:
+        tier(a)
+        return
     import numpy as np
     import torch
 
@@ -502,13 +635,14 @@ def main():
         outs = torch.empty((n_layers, H), dtype=torch.float32, device=dev)
         lws_bytes = qem.fmoe_workspace_bytes(layers[0], 1)
         lws = torch.empty((n_layers, (lws_bytes + 255) // 256 * 256), dtype=torch.uint8, device=dev)
-        kidx = torch.empty((n_layers, K), dtype=torch.int32, device=dev)
+        kp = (K + 3) // 4 * 4  # (rows 16-byte aligned)
+        kidx = torch.empty((n_layers, kp), dtype=torch.int32, device=dev)
         with torch.cuda.stream(kstream):
             for l in range(n_layers):   # full layers first: every kernel's inputs are then in place
                 qem.fmoe_moe_layer_phases(layers[l], xs[l:l + 1], xs[l:l + 1], outs[l:l + 1], 7, lws[l],
-                                          topk_idx=kidx[l:l + 1], stream=kstream, c_layer=c_layers[l])
+                                          topk_idx=kidx[l:l + 1, :K], stream=kstream, c_layer=c_layers[l])
         kstream.synchronize()
-        kd = float(np.mean([len(set(r.tolist())) for r in kidx.cpu().numpy()]))
+        kd = float(np.mean([len(set(r[:K].tolist())) for r in kidx.cpu().numpy()]))
         for ph in (1, 2, 4):
             # n_layers launches of one kernel, captured once and replayed on kstream
             g = torch.cuda.CUDAGraph()

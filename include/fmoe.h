@@ -264,14 +264,18 @@ fmoe_status fmoe_moe_layer_noalloc(const fmoe_layer *L, int n_tokens, const floa
  * refreshes the slot; a miss takes the first empty slot, else the least recently
  * used slot that the call does not need (ties: the lower slot). FMOE_ERR_ROUTING
  * for an expert outside 0..n_experts-1 or a repeated one, FMOE_ERR_WORKSPACE if n
- * exceeds the slots (nothing changes then).
+ * exceeds the slots (nothing changes then). It updates the bookkeeping as a tiered
+ * call does but copies nothing, so a later tiered call would take the planned
+ * experts as resident: it is for inspecting the policy on a cache that no tiered
+ * call uses.
  * fmoe_moe_layer_tiered: fmoe_moe_layer with L->bank in host memory, any n_tokens
  * (the tokens grouped by expert, as fmoe_moe_layer does for several): the router
  * and top-K run on the GPU; the call then synchronises `stream` once to read the
  * routing, plans the batch's distinct experts (ascending id) through the cache,
  * copies the missing blobs from host memory into their slots (on `stream`), and
  * enqueues the experts and the combine, which read the blobs from their slots.
- * Results equal fmoe_moe_layer's. ws >= fmoe_tiered_workspace_bytes(L, n_tokens);
+ * Results equal fmoe_moe_layer's for several tokens (one token takes the same
+ * grouped kernels here, so it matches fmoe_moe_layer up to rounding). ws >= fmoe_tiered_workspace_bytes(L, n_tokens);
  * the batch's distinct experts must fit the slots (FMOE_ERR_WORKSPACE, found after
  * the routing: the routing outputs are then written, nothing else). Calls on one
  * cache must be serialised on one stream. Otherwise the arguments and errors of
