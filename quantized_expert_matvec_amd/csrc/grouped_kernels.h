@@ -48,9 +48,8 @@ namespace fmoe {
 namespace dev {
 
 // Slots (token, choice) that the gate/up kernel's own routing handles (one thread
-// per slot): batches with more, with more than kRouteTokens tokens or with
-// top_k > 8 are routed by the routing kernels before it (k_topk, k_group) and read
-// the grouping table.
+// per slot): batches with more, or with more than kRouteTokens tokens, are routed
+// by the routing kernels before it (k_topk, k_group) and read the grouping table.
 constexpr int kRouteSlots = 512;
 constexpr int kRouteTokens = 64;
 // Tokens per work item: one MFMA row block (4 rows each: hi, mid, lo, 0). An
@@ -432,6 +431,162 @@ __host__ __device__ constexpr int g1_rows_per_block() {
   return kWavesPerBlock / router_split<NGH>();
 }
 
+// From kRouterTileMin tokens the router runs on the matrix cores instead
+// (router_tile below): every workgroup of the row-held form reads every token's
+// x. Measured per layer (60-layer q4 stack): equal at 32 tokens, 11 us less at
+// 48, 20 at 64, 58 at 128; at 24 tokens the row-held form is 2 us faster.
+constexpr int kRouterTileMin = 32;
+constexpr int kRt = 16;  // experts and tokens per router tile
+__host__ __device__ inline bool router_tiled(int B) { return B >= kRouterTileMin; }
+__host__ __device__ inline int router_tiles(int E, int B) { return ((E + kRt - 1) / kRt) * ((B + kRt - 1) / kRt); }
+
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+// One tile of the router on the matrix cores: logits[t][e] = R_e . x_t (fp32,
+// unscaled) for 16 experts x 16 tokens, with v_mfma_f32_16x16x4_f32 (fp32
+// products, fp32 sums). Lane l holds A[l % 16][k] and B[k][l % 16] for k = l / 16:
+// with two float4 loads per operand the lane covers columns c + 8 (l / 16) .. + 7
+// of its expert's row and of its token, and eight MFMAs take them in turn (the
+// same column order on both sides). The four wavefronts take a quarter of the
+// columns each; their partial tiles are added in LDS in wavefront order, so the
+// result does not depend on timing. Tiles that share experts run on one XCD
+// (the dispatcher places workgroup b on XCD b % 8; with a multiple of 8 expert
+// tiles, expert tile r goes to XCD r % 8), so each XCD's L2 serves the router rows
+// to all token tiles after one read. part: 4 x 256 floats of LDS.
+__device__ __forceinline__ void router_tile(const GroupArgs &a, float (*part)[kRt * kRt]) {
+  const int lane = lane_id(), wv = wave_in_block();
+  const int n_rt = (a.E + kRt - 1) / kRt, n_tt = (a.B + kRt - 1) / kRt;
+  const int b = blockIdx.x;
+  int rt, tt;
+  if (n_rt % 8 == 0) {
+    const int x = b % 8, s = b / 8;
+    rt = x + 8 * (s / n_tt);
+    tt = s % n_tt;
+  } else {
+    rt = b / n_tt;
+    tt = b % n_tt;
+  }
+  const int H = a.H;
+  const int e0 = rt * kRt, t0 = tt * kRt;
+  const int cw = wv * (H / kWavesPerBlock) + 8 * (lane >> 4);  // this lane's first column
+  const float4 *rp = reinterpret_cast<const float4 *>(a.router + (size_t)min(e0 + (lane & 15), a.E - 1) * H + cw);
+  const float4 *xp = reinterpret_cast<const float4 *>(a.x + (size_t)min(t0 + (lane & 15), a.B - 1) * H + cw);
+  const int steps = H / kWavesPerBlock / 32;  // 32 columns per step (H a multiple of 256: even, >= 2)
+  constexpr int U = 8;                        // steps in flight (128 KB per workgroup)
+  float4 ra[U][2], xa[U][2];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int nx = min(u, steps - 1);
+    ra[u][0] = rp[8 * nx];
+    ra[u][1] = rp[8 * nx + 1];
+    xa[u][0] = xp[8 * nx];
+    xa[u][1] = xp[8 * nx + 1];
+  }
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int st = 0; st < steps; st += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (st + u >= steps) break;  // (uniform; steps is even, U a power of two)
+      const float4 r0 = ra[u][0], r1 = ra[u][1], x0 = xa[u][0], x1 = xa[u][1];
+      const int nx = min(st + U + u, steps - 1);  // (past the end: the last step again, unused)
+      ra[u][0] = rp[8 * nx];
+      ra[u][1] = rp[8 * nx + 1];
+      xa[u][0] = xp[8 * nx];
+      xa[u][1] = xp[8 * nx + 1];
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r0.x, x0.x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r0.y, x0.y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r0.z, x0.z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r0.w, x0.w, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r1.x, x1.x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r1.y, x1.y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r1.z, x1.z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r1.w, x1.w, acc, 0, 0, 0);
+    }
+  }
+  // lane l holds D[4 (l / 16) + j][l % 16]: expert e0 + 4 (l / 16) + j, token t0 + l % 16
+#pragma unroll
+  for (int j = 0; j < 4; ++j) part[wv][64 * j + lane] = acc[j];
+  __syncthreads();
+  const int o = threadIdx.x;  // (kBlock = 256 = the tile's outputs)
+  const float d = ((part[0][o] + part[1][o]) + part[2][o]) + part[3][o];
+  const int l = o & 63, j = o >> 6;
+  const int e = e0 + 4 * (l >> 4) + j, t = t0 + (l & 15);
+  if (e < a.E && t < a.B) a.logits[(size_t)t * logit_stride(a.E) + e] = d;
+}
+
+// Input preparation of token t for the matrix cores (RMS factor xinv; per group
+// the three digit planes, the factor f and the sum of x) and its gate dot
+// product g . x (unscaled), by one workgroup. part: 2 x kWavesPerBlock floats of LDS.
+__device__ __forceinline__ void g1_prep(const GroupArgs &a, int t, float (*part)[kWavesPerBlock]) {
+  const int lane = lane_id();
+  const int wv = wave_in_block();
+  const int ng = a.H / kGroup, H = a.H;
+  const bool rms = a.rms_eps >= 0.f;
+  const float *xt = a.x + (size_t)t * H;
+  const float *gv = a.gvec ? a.gvec : a.x;  // (read but unused without a shared expert)
+  const int UNITS = ng * 8;  // 8 consecutive columns each: unit u = columns 8u .. 8u + 7
+  float ss = 0.f, gd = 0.f;
+  for (int u0 = 0; u0 < UNITS; u0 += kBlock) {
+    const int u = u0 + threadIdx.x;
+    const bool ok = u < UNITS;
+    const int uc = ok ? u : UNITS - 1;
+    const int g = uc >> 3;
+    const int c = 8 * uc;
+    const float4 v0 = *reinterpret_cast<const float4 *>(xt + c);
+    const float4 v1 = *reinterpret_cast<const float4 *>(xt + c + 4);
+    const float4 g0 = *reinterpret_cast<const float4 *>(gv + c);
+    const float4 g1 = *reinterpret_cast<const float4 *>(gv + c + 4);
+    const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    const float gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    float sum = 0.f, amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      sum += f[j];
+      amax = __int_as_float(max(__float_as_int(amax), __float_as_int(fabsf(f[j]))));
+      if (ok) {
+        ss = fmaf(f[j], f[j], ss);
+        gd = fmaf(gw[j], f[j], gd);
+      }
+    }
+    // the group's 8 units are 8 consecutive threads
+    sum = seg_allreduce<8>(sum);
+    const float gmax = __int_as_float(seg_max8_bits(amax));
+    const int k = group_shift(gmax);
+    uint32_t d[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) d[j] = digits3(f[j], k);
+    if (ok) {
+      uint8_t *dst = a.xq + ((size_t)(kParts * t) * ng + g) * 64 + 8 * (uc & 7);
+#pragma unroll
+      for (int p = 0; p < kParts; ++p) {
+        const int sh = 8 * p;
+        const uint2 w = {((d[0] >> sh) & 0xFFu) | ((d[1] >> sh) & 0xFFu) << 8 | ((d[2] >> sh) & 0xFFu) << 16 |
+                             ((d[3] >> sh) & 0xFFu) << 24,
+                         ((d[4] >> sh) & 0xFFu) | ((d[5] >> sh) & 0xFFu) << 8 | ((d[6] >> sh) & 0xFFu) << 16 |
+                             ((d[7] >> sh) & 0xFFu) << 24};
+        *reinterpret_cast<uint2 *>(dst + (size_t)p * ng * 64) = w;
+      }
+      if ((uc & 7) == 0) reinterpret_cast<float2 *>(a.xsum)[(size_t)t * ng + g] = make_float2(group_factor(gmax, k), sum);
+    }
+  }
+  ss = seg_reduce<kWave>(ss);
+  gd = seg_reduce<kWave>(gd);
+  if (lane == kWave - 1) {
+    part[0][wv] = ss;
+    part[1][wv] = gd;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    a.xinv[t] = rms ? rms_inv(part[0], H, a.rms_eps) : 1.f;
+    if (a.gvec) {
+      float d = part[1][0];
+#pragma unroll
+      for (int i = 1; i < kWavesPerBlock; ++i) d += part[1][i];
+      a.gdot[t] = d;
+    }
+  }
+}
+
 template <int BITS, int NGHP>
 __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
   constexpr int SPLIT = router_split<NGHP>();
@@ -445,73 +600,8 @@ __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
   __shared__ float dp[kWavesPerBlock][kMaxTokens];           // per wavefront: its part of each token's dot
   const int lane = lane_id();
   const int wv = wave_in_block();
-  const bool rms = a.rms_eps >= 0.f;
   if ((int)blockIdx.x >= a.n_router_blocks) {
-    // ---- input preparation of token t, and its gate dot product
-    const int t = blockIdx.x - a.n_router_blocks;
-    const float *xt = a.x + (size_t)t * H;
-    const float *gv = a.gvec ? a.gvec : a.x;  // (read but unused without a shared expert)
-    const int UNITS = ng * 8;  // 8 consecutive columns each: unit u = columns 8u .. 8u + 7
-    float ss = 0.f, gd = 0.f;
-    for (int u0 = 0; u0 < UNITS; u0 += kBlock) {
-      const int u = u0 + threadIdx.x;
-      const bool ok = u < UNITS;
-      const int uc = ok ? u : UNITS - 1;
-      const int g = uc >> 3;
-      const int c = 8 * uc;
-      const float4 v0 = *reinterpret_cast<const float4 *>(xt + c);
-      const float4 v1 = *reinterpret_cast<const float4 *>(xt + c + 4);
-      const float4 g0 = *reinterpret_cast<const float4 *>(gv + c);
-      const float4 g1 = *reinterpret_cast<const float4 *>(gv + c + 4);
-      const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-      const float gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-      float sum = 0.f, amax = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        sum += f[j];
-        amax = __int_as_float(max(__float_as_int(amax), __float_as_int(fabsf(f[j]))));
-        if (ok) {
-          ss = fmaf(f[j], f[j], ss);
-          gd = fmaf(gw[j], f[j], gd);
-        }
-      }
-      // the group's 8 units are 8 consecutive threads
-      sum = seg_allreduce<8>(sum);
-      const float gmax = __int_as_float(seg_max8_bits(amax));
-      const int k = group_shift(gmax);
-      uint32_t d[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) d[j] = digits3(f[j], k);
-      if (ok) {
-        uint8_t *dst = a.xq + ((size_t)(kParts * t) * ng + g) * 64 + 8 * (uc & 7);
-#pragma unroll
-        for (int p = 0; p < kParts; ++p) {
-          const int sh = 8 * p;
-          const uint2 w = {((d[0] >> sh) & 0xFFu) | ((d[1] >> sh) & 0xFFu) << 8 | ((d[2] >> sh) & 0xFFu) << 16 |
-                               ((d[3] >> sh) & 0xFFu) << 24,
-                           ((d[4] >> sh) & 0xFFu) | ((d[5] >> sh) & 0xFFu) << 8 | ((d[6] >> sh) & 0xFFu) << 16 |
-                               ((d[7] >> sh) & 0xFFu) << 24};
-          *reinterpret_cast<uint2 *>(dst + (size_t)p * ng * 64) = w;
-        }
-        if ((uc & 7) == 0) reinterpret_cast<float2 *>(a.xsum)[(size_t)t * ng + g] = make_float2(group_factor(gmax, k), sum);
-      }
-    }
-    ss = seg_reduce<kWave>(ss);
-    gd = seg_reduce<kWave>(gd);
-    if (lane == kWave - 1) {
-      part[0][wv] = ss;
-      part[1][wv] = gd;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      a.xinv[t] = rms ? rms_inv(part[0], H, a.rms_eps) : 1.f;
-      if (a.gvec) {
-        float d = part[1][0];
-#pragma unroll
-        for (int i = 1; i < kWavesPerBlock; ++i) d += part[1][i];
-        a.gdot[t] = d;
-      }
-    }
+    g1_prep(a, blockIdx.x - a.n_router_blocks, part);
     return;
   }
   // ---- router rows: a wavefront holds its part of one fp32 row in registers;
@@ -569,6 +659,21 @@ __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
   }
 }
 
+// g1, for batches of kRouterTileMin tokens or more: workgroups [0,
+// n_router_blocks) compute the router in 16 x 16 tiles on the matrix cores
+// (router_tile), workgroups n_router_blocks + t prepare token t (g1_prep).
+template <int BITS>
+__global__ __launch_bounds__(kBlock) void k_g1t(const GroupArgs a) {
+  static_assert(kBlock == kRt * kRt && kWavesPerBlock == 4, "one output per thread, four column quarters");
+  __shared__ float part[2][kWavesPerBlock];
+  __shared__ float tile[kWavesPerBlock][kRt * kRt];
+  if ((int)blockIdx.x >= a.n_router_blocks) {
+    g1_prep(a, blockIdx.x - a.n_router_blocks, part);
+    return;
+  }
+  router_tile(a, tile);
+}
+
 // ------------------------------------------------------------------ g2, g3
 
 // The grouping table G (int32, in the workspace), written by the routing:
@@ -598,6 +703,7 @@ struct RouteLdsT {
   int sidx[64 * NW];                         // expert of each slot
   int eoff[kMaxExperts];                     // list offset of each present expert
   int wtot[kGWaves];
+  TopkLds tk[kGWaves];                       // each wavefront's top-K scratch
 };
 using RouteLds = RouteLdsT<kGWaves>;  // every routed-in-kernel batch (kRouteSlots slots)
 using RouteLds1 = RouteLdsT<1>;       // at most 64 slots
@@ -624,23 +730,22 @@ __device__ __forceinline__ int block_route(const GroupArgs &a, RouteLdsT<NW> &R,
   const int S = a.B * a.K;
   const int nwl = (S + kWave - 1) / kWave;  // wavefronts holding slots
   for (int i = threadIdx.x; i < nwl * a.E; i += kGThreads) R.mask[i / a.E][i % a.E] = 0ull;
-  // token t's routing from its top-K (idx, w): slot experts, and the writer's outputs
-  auto publish = [&](int t, const int *idx, const float *w, float inv, float gd) {
-    auto one = [&](int j) {
-      const int s = t * a.K + j;
-      R.sidx[s] = idx[j];
+  // token t's routing from its top-K (lane j < K: choice j): slot experts, and
+  // the writer's outputs
+  auto publish = [&](int t, int mi, float mw, float inv, float gd) {
+    if (lane < a.K) {
+      const int s = t * a.K + lane;
+      R.sidx[s] = mi;
       if (writer) {
-        a.idx[s] = idx[j];
-        a.w[s] = w[j];
-        if (a.out_idx) a.out_idx[s] = idx[j];
-        if (a.out_w) a.out_w[s] = w[j];
+        a.idx[s] = mi;
+        a.w[s] = mw;
+        if (a.out_idx) a.out_idx[s] = mi;
+        if (a.out_w) a.out_w[s] = mw;
       }
-    };
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j == lane && j < a.K) one(j);
+    }
     if (writer && lane == 0 && a.gvec) a.sigma[t] = 1.f / (1.f + expf(-gd * inv));
   };
+  TopkLds &tk = R.tk[wave];
   if (a.E <= 512) {
     // wavefront v: tokens v, v + 8, ...; two tokens per pass, all their loads
     // (logits in the top-K's layout, RMS factor, gate dot) requested together
@@ -651,25 +756,25 @@ __device__ __forceinline__ int block_route(const GroupArgs &a, RouteLdsT<NW> &R,
       load_logits<8>(a.logits + (size_t)t1 * logit_stride(a.E), a.E, v1);
       const float inv0 = a.xinv[t0], inv1 = a.xinv[t1];
       const float gd0 = a.gvec ? a.gdot[t0] : 0.f, gd1 = a.gvec ? a.gdot[t1] : 0.f;
-      int key[8], idx[8];
-      float w[8];
+      int key[8], mi;
+      float mw;
       logit_keys<8>(v0, a.E, key);
-      wave_topk_keys<8, 8>(key, a.K, idx, w, inv0);
-      publish(t0, idx, w, inv0, gd0);
+      wave_topk<8>(key, a.K, inv0, tk, mi, mw);
+      publish(t0, mi, mw, inv0, gd0);
       if (t0 + kGWaves < a.B) {
         logit_keys<8>(v1, a.E, key);
-        wave_topk_keys<8, 8>(key, a.K, idx, w, inv1);
-        publish(t1, idx, w, inv1, gd1);
+        wave_topk<8>(key, a.K, inv1, tk, mi, mw);
+        publish(t1, mi, mw, inv1, gd1);
       }
     }
   } else {
     for (int t = wave; t < a.B; t += kGWaves) {
       const float inv = a.xinv[t];
       const float gd = a.gvec ? a.gdot[t] : 0.f;
-      int idx[8];
-      float w[8];
-      wave_topk_lds<8>(a.logits + (size_t)t * logit_stride(a.E), a.E, a.K, idx, w, inv);
-      publish(t, idx, w, inv, gd);
+      int mi;
+      float mw;
+      wave_topk_lds(a.logits + (size_t)t * logit_stride(a.E), a.E, a.K, inv, tk, mi, mw);
+      publish(t, mi, mw, inv, gd);
     }
   }
   __syncthreads();
@@ -746,41 +851,23 @@ __device__ __forceinline__ int block_route(const GroupArgs &a, RouteLdsT<NW> &R,
   return NB;
 }
 
-// ------------------------------------------------------------------ g2, g3
-
 // ------------------------------------------------------------------ routing kernels (large batches)
 
 // k_topk: the routing of every token, one wavefront per token: the top-K of its
 // unscaled logits with the weights taken after its RMS factor (as block_route),
 // into idx / w (and the caller's outputs), and its shared-expert gate sigma.
-// KM: 8 for top_k <= 8, else kMaxTopK.
-template <int BITS, int KM>
+template <int BITS>
 __global__ __launch_bounds__(kGThreads) void k_topk(const GroupArgs a) {
+  __shared__ TopkLds tks[kGWaves];
   const int t = (int)blockIdx.x * kGWaves + wave_in_block();
   if (t >= a.B) return;  // (uniform over the wavefront)
   const int lane = lane_id();
   const float inv = a.xinv[t];
   const float gd = a.gvec ? a.gdot[t] : 0.f;
-  int idx[KM];
-  float w[KM];
-  if (a.E <= 512) {
-    float v[8];
-    int key[8];
-    load_logits<8>(a.logits + (size_t)t * logit_stride(a.E), a.E, v);
-    logit_keys<8>(v, a.E, key);
-    wave_topk_keys<8, KM>(key, a.K, idx, w, inv);
-  } else {
-    wave_topk_lds<KM>(a.logits + (size_t)t * logit_stride(a.E), a.E, a.K, idx, w, inv);
-  }
-  // lane j < K stores choice j (selected from the unrolled arrays, then one store each)
-  int mi = 0;
-  float mw = 0.f;
-#pragma unroll
-  for (int j = 0; j < KM; ++j) {
-    mi = j == lane ? idx[j] : mi;
-    mw = j == lane ? w[j] : mw;
-  }
-  if (lane < a.K) {
+  int mi;
+  float mw;
+  wave_topk_lds(a.logits + (size_t)t * logit_stride(a.E), a.E, a.K, inv, tks[wave_in_block()], mi, mw);
+  if (lane < a.K) {  // lane j stores choice j
     const int s = t * a.K + lane;
     a.idx[s] = mi;
     a.w[s] = mw;
@@ -1220,12 +1307,21 @@ inline int cu_count() {
 // the first, the down kernel on the second).
 template <int BITS>
 struct GroupDispatch {
+  // router + token preparation (sets a.n_router_blocks)
+  template <int NGH>
+  static void launch_g1(GroupArgs &a, hipStream_t s) {
+    if (router_tiled(a.B)) {
+      a.n_router_blocks = router_tiles(a.E, a.B);
+      hipLaunchKernelGGL(k_g1t<BITS>, dim3(a.n_router_blocks + a.B), dim3(kBlock), 0, s, a);
+    } else {
+      a.n_router_blocks = (a.E + g1_rows_per_block<NGH>() - 1) / g1_rows_per_block<NGH>();
+      hipLaunchKernelGGL((k_g1<BITS, NGH>), dim3(a.n_router_blocks + a.B), dim3(kBlock), 0, s, a);
+    }
+  }
+
   static void launch_topk(const GroupArgs &a, hipStream_t s) {
     const dim3 grid((a.B + kGWaves - 1) / kGWaves);
-    if (a.K <= 8)
-      hipLaunchKernelGGL((k_topk<BITS, 8>), grid, dim3(kGThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((k_topk<BITS, kMaxTopK>), grid, dim3(kGThreads), 0, s, a);
+    hipLaunchKernelGGL(k_topk<BITS>, grid, dim3(kGThreads), 0, s, a);
   }
 
   template <int NGH>
@@ -1233,14 +1329,12 @@ struct GroupDispatch {
     const bool sh = a.shared != nullptr;
     const int S = a.B * a.K;
     const int shb = sh ? (a.B + kTokBlock - 1) / kTokBlock : 0;  // shared token blocks
-    a.n_router_blocks = (a.E + g1_rows_per_block<NGH>() - 1) / g1_rows_per_block<NGH>();
-    if (phases & 1)
-      hipLaunchKernelGGL((k_g1<BITS, NGH>), dim3(a.n_router_blocks + a.B), dim3(kBlock), 0, s, a);
+    if (phases & 1) launch_g1<NGH>(a, s);
     if (phases & 2) {
       const dim3 grid(std::min((shb + S) * (a.I / kGroup), cu_count()));
       const bool full = a.H == NGH * kGroup;
-      if (S > kRouteSlots || a.B > kRouteTokens || a.K > 8) {
-        // large batches and top_k > 8: the routing kernels first, then gate/up from the table
+      if (S > kRouteSlots || a.B > kRouteTokens) {
+        // large batches: the routing kernels first, then gate/up from the table
         launch_topk(a, s);
         hipLaunchKernelGGL(k_group<BITS>, dim3(1), dim3(kGThreads), 0, s, a);
         if (full)
@@ -1292,8 +1386,7 @@ template <int BITS>
 struct SplitDispatch {
   template <int NGH>
   static hipError_t route(GroupArgs a, hipStream_t s) {
-    a.n_router_blocks = (a.E + g1_rows_per_block<NGH>() - 1) / g1_rows_per_block<NGH>();
-    hipLaunchKernelGGL((k_g1<BITS, NGH>), dim3(a.n_router_blocks + a.B), dim3(kBlock), 0, s, a);
+    GroupDispatch<BITS>::template launch_g1<NGH>(a, s);
     GroupDispatch<BITS>::launch_topk(a, s);
     return hipGetLastError();
   }

@@ -240,20 +240,6 @@ __device__ __forceinline__ float key_value(int k) { return __int_as_float(k >= 0
 // keys (NaN logits count as -inf); lane l holds the VPL consecutive elements
 // VPL l .. VPL l + VPL - 1, so a lower lane means a lower index, and padding
 // elements (e >= E) hold INT_MIN, below every real key.
-//
-// Fast path: each lane's maximum (first position among equal keys) and second
-// key; K rounds over the 64 lane maxima (wavefront maximum, lowest lane holding
-// it) give the K best lane maxima in order, and they are the top K of all
-// elements when no second key reaches the K-th of them. Otherwise (a lane holding
-// two of the top K, or a tie at the boundary) K full rounds run: each lane's
-// maximum over its remaining keys, the wavefront maximum, the lowest lane holding
-// it and that lane's first position holding it; the chosen key is retired.
-//
-// Then the renormalised softmax weights of the chosen K,
-// w_j = exp(l_j - l_0) / sum (renormalising over the chosen K cancels the full
-// softmax denominator). The logits may be held unscaled: lscale > 0 is the
-// factor that turns them into the true logits (it does not change the order), so
-// w_j = exp((l_j - l_0) * lscale) / sum. Results are wavefront-uniform.
 __device__ __forceinline__ int wave_max_i(int g) {
   constexpr int kGone = (int)0x80000000;
   g = max(g, dpp_i<0xB1, 0xF>(g, kGone));
@@ -262,6 +248,17 @@ __device__ __forceinline__ int wave_max_i(int g) {
   g = max(g, dpp_i<0x140, 0xF>(g, kGone));
   g = max(g, dpp_i<0x142, 0xA>(g, kGone));
   g = max(g, dpp_i<0x143, 0xC>(g, kGone));
+  return __builtin_amdgcn_readlane(g, 63);
+}
+
+__device__ __forceinline__ int wave_min_i(int g) {
+  constexpr int kTop = 0x7FFFFFFF;
+  g = min(g, dpp_i<0xB1, 0xF>(g, kTop));
+  g = min(g, dpp_i<0x4E, 0xF>(g, kTop));
+  g = min(g, dpp_i<0x141, 0xF>(g, kTop));
+  g = min(g, dpp_i<0x140, 0xF>(g, kTop));
+  g = min(g, dpp_i<0x142, 0xA>(g, kTop));
+  g = min(g, dpp_i<0x143, 0xC>(g, kTop));
   return __builtin_amdgcn_readlane(g, 63);
 }
 
@@ -278,72 +275,134 @@ __device__ __forceinline__ void lane_max(const int (&key)[VPL], int &m1, int &p1
   }
 }
 
-// (KM: the most rounds compiled, 8 or kMaxTopK, a template argument of the
-// kernels so that the usual K <= 8 keeps its arrays in registers; K <= KM; idx and
-// w receive KM entries, those past K 0)
-template <int VPL, int KM>
-__device__ __forceinline__ void wave_topk_keys(int (&key)[VPL], int K, int *idx, float *w, float lscale) {
+// Orders one wavefront's LDS writes before its later LDS reads of what other
+// lanes wrote (without it the compiler may forward a lane's own stored value).
+__device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); }
+
+// LDS scratch of one wavefront's top-K.
+struct TopkLds {
+  int m[kWave];        // each lane's maximum key; later the candidates' keys
+  int ci[kWave];       // the candidates' indices
+  int widx[kMaxTopK];  // the K choices in order: index, key
+  int wkey[kMaxTopK];
+};
+
+// Exact rank of candidate i among the first C in S (keys S.m, indices S.ci).
+__device__ __forceinline__ int candidate_rank(const TopkLds &S, int C, int ck, int cx) {
+  int r = 0;
+  for (int j = 0; j < C; ++j) {
+    const int k = S.m[j];
+    r += (k > ck || (k == ck && S.ci[j] < cx)) ? 1 : 0;
+  }
+  return r;
+}
+
+// The top K (1 <= K <= kMaxTopK) at a cost that does not grow with K:
+//  1. each lane's maximum key m1 (first position p1 among equal keys) and its
+//     second key m2;
+//  2. each lane ranks its maximum among the 64 by the number of greater lane
+//     maxima (broadcast LDS reads, four lanes a read);
+//  3. the lanes ranked below K write their element to that rank's slot; when
+//     exactly K of them did, each finds its own write there (no two share a rank:
+//     no tie among them) and no lane's second key reaches the K-th of them, those
+//     K lane maxima are the top K, in rank order;
+//  4. otherwise the candidates are every key at or above T, the least lane
+//     maximum ranked below K: at least K lane maxima reach T, so the top K are
+//     among them. At most 64 candidates are ranked exactly among themselves (value
+//     descending, index ascending); beyond that (many equal keys) K rounds take
+//     the wavefront maximum, lowest index first, one at a time.
+// Then lane j < K holds choice j: my_idx, and its renormalised softmax weight
+// my_w = exp((l_j - l_0) lscale) / sum_{i<K} exp((l_i - l_0) lscale) (renormalising
+// over the chosen K cancels the full softmax denominator), the sum taken in
+// choice order by every lane; lanes j >= K get 0 and 0. The logits may be held
+// unscaled: lscale > 0 is the factor that turns them into the true logits (it
+// does not change the order). key may be modified.
+template <int VPL>
+__device__ __forceinline__ void wave_topk(int (&key)[VPL], int K, float lscale, TopkLds &S, int &my_idx,
+                                          float &my_w) {
   constexpr int kGone = (int)0x80000000;
   const int lane = lane_id();
   int m1, p1, m2 = kGone;
   lane_max<VPL>(key, m1, p1);
 #pragma unroll
   for (int m = 0; m < VPL; ++m) m2 = m == p1 ? m2 : max(m2, key[m]);
-  int a = m1, T = kGone;
-  float lv[KM];
+  S.m[lane] = m1;
+  wave_lds_fence();
+  int r = 0;
 #pragma unroll
-  for (int j = 0; j < KM; ++j) {
-    idx[j] = 0;
-    lv[j] = 0.f;
-    if (j < K) {
-      const int g = wave_max_i(a);
-      const int L = __ffsll((long long)__ballot(a == g)) - 1;
-      idx[j] = VPL * L + __builtin_amdgcn_readlane(p1, L);
-      lv[j] = key_value(g);
-      a = lane == L ? kGone : a;
-      T = g;
-    }
+  for (int j = 0; j < kWave / 4; ++j) {
+    const int4 q = reinterpret_cast<const int4 *>(S.m)[j];
+    r += (q.x > m1 ? 1 : 0) + (q.y > m1 ? 1 : 0) + (q.z > m1 ? 1 : 0) + (q.w > m1 ? 1 : 0);
   }
-  if (wave_max_i(m2) >= T) {
+  const bool win = r < K;
+  const int me = VPL * lane + p1;
+  if (win) {
+    S.widx[r] = me;
+    S.wkey[r] = m1;
+  }
+  wave_lds_fence();
+  const bool clash = win && S.widx[r] != me;
+  bool fast = __popcll(__ballot(win)) == K && __ballot(clash) == 0ull;
+  if (fast) fast = __ballot(m2 >= S.wkey[K - 1]) == 0ull;
+  if (!fast) {
+    // T: the least lane maximum ranked below K
+    const int t = wave_min_i(win ? m1 : 0x7FFFFFFF);
+    int c = 0;
 #pragma unroll
-    for (int j = 0; j < KM; ++j) {
-      if (j < K) {
+    for (int m = 0; m < VPL; ++m) c += key[m] >= t ? 1 : 0;
+    int off = 0, C = 0;
+#pragma unroll
+    for (int b = 0; b < 5; ++b) {  // (c <= VPL <= 16)
+      const unsigned long long bm = __ballot((c >> b) & 1);
+      off += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u)) << b;
+      C += __popcll(bm) << b;
+    }
+    if (C <= kWave) {
+#pragma unroll
+      for (int m = 0; m < VPL; ++m) {
+        if (key[m] >= t) {
+          S.m[off] = key[m];
+          S.ci[off] = VPL * lane + m;
+          ++off;
+        }
+      }
+      wave_lds_fence();
+      if (lane < C) {
+        const int ck = S.m[lane], cx = S.ci[lane];
+        const int rk = candidate_rank(S, C, ck, cx);
+        if (rk < K) {
+          S.widx[rk] = cx;
+          S.wkey[rk] = ck;
+        }
+      }
+    } else {
+      for (int j = 0; j < K; ++j) {
         int b, p;
         lane_max<VPL>(key, b, p);
         const int g = wave_max_i(b);
         const int L = __ffsll((long long)__ballot(b == g)) - 1;
         const int pl = __builtin_amdgcn_readlane(p, L);
-        idx[j] = VPL * L + pl;
-        lv[j] = key_value(g);
+        if (lane == 0) {
+          S.widx[j] = VPL * L + pl;
+          S.wkey[j] = g;
+        }
 #pragma unroll
         for (int m = 0; m < VPL; ++m) key[m] = (lane == L && m == pl) ? kGone : key[m];
       }
     }
   }
+  wave_lds_fence();
+  // weights, the sum in choice order
+  const float l0 = key_value(S.wkey[0]);
   float sum = 0.f;
-#pragma unroll
-  for (int j = 0; j < KM; ++j) {
-    w[j] = 0.f;
-    if (j < K) {
-      w[j] = __expf((lv[j] - lv[0]) * lscale);
-      sum += w[j];
-    }
-  }
+  for (int j = 0; j < K; ++j) sum += __expf((key_value(S.wkey[j]) - l0) * lscale);
   const float inv = 1.f / sum;
-#pragma unroll
-  for (int j = 0; j < KM; ++j) w[j] *= inv;
-}
-
-// Lane j < KM writes choice j of a wavefront-uniform top-K to LDS (sidx, sw).
-template <int KM>
-__device__ __forceinline__ void publish_topk(const int *idx, const float *w, int *sidx, float *sw) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int j = 0; j < KM; ++j)
-    if (j == lane) {
-      sidx[j] = idx[j];
-      sw[j] = w[j];
-    }
+  my_idx = 0;
+  my_w = 0.f;
+  if (lane < K) {
+    my_idx = S.widx[lane];
+    my_w = __expf((key_value(S.wkey[lane]) - l0) * lscale) * inv;
+  }
 }
 
 // lane l's VPL consecutive logits, with 16-byte loads (clamped to the row; lg
@@ -375,43 +434,42 @@ __device__ __forceinline__ void logit_keys(const float (&v)[VPL], int E, int (&k
   }
 }
 
-// top-K of E <= kMaxExperts logits in memory (LDS or global)
-template <int KM>
-__device__ __forceinline__ void wave_topk_lds(const float *lg, int E, int K, int *idx, float *w,
-                                              float lscale = 1.f) {
+// top-K of E <= kMaxExperts logits in memory (LDS or global); see wave_topk
+__device__ __forceinline__ void wave_topk_lds(const float *lg, int E, int K, float lscale, TopkLds &S, int &my_idx,
+                                              float &my_w) {
   if (E <= 512) {
     float v[8];
     int key[8];
     load_logits<8>(lg, E, v);
     logit_keys<8>(v, E, key);
-    wave_topk_keys<8, KM>(key, K, idx, w, lscale);
+    wave_topk<8>(key, K, lscale, S, my_idx, my_w);
   } else {
     float v[16];
     int key[16];
     load_logits<16>(lg, E, v);
     logit_keys<16>(v, E, key);
-    wave_topk_keys<16, KM>(key, K, idx, w, lscale);
+    wave_topk<16>(key, K, lscale, S, my_idx, my_w);
   }
 }
 
 // Block-wide top-K: one wavefront computes it from the logits in LDS and
-// publishes it through LDS (sidx, sw); contains one barrier, after which every
-// thread reads the result from sidx / sw. (Results are not copied back into
-// per-thread arrays: indexing those by a runtime slot would put them in scratch
-// memory.) Workgroup b uses wavefront b % 4, so that the workgroups sharing a CU
-// do not all compute it on the same SIMD. (Measured: splitting the rounds over
-// the four wavefronts, with one barrier per round, is slower.)
-template <int KM>
-__device__ __forceinline__ void block_topk(const float *lg, int E, int K, int *sidx, float *sw) {
+// publishes it through LDS (sidx, sw: lane j writes choice j); contains one
+// barrier, after which every thread reads the result from sidx / sw. Workgroup b
+// uses wavefront b % 4, so that the workgroups sharing a CU do not all compute it
+// on the same SIMD.
+__device__ __forceinline__ void block_topk(const float *lg, int E, int K, TopkLds &S, int *sidx, float *sw) {
   if (wave_in_block() == (int)(blockIdx.x % kWavesPerBlock)) {
     // the rest of the workgroup waits on this wavefront: let it win the SIMD's
     // issue arbitration against co-resident wavefronts of other workgroups
     __builtin_amdgcn_s_setprio(3);
-    int idx[KM];
-    float w[KM];
-    wave_topk_lds<KM>(lg, E, K, idx, w);
+    int mi;
+    float mw;
+    wave_topk_lds(lg, E, K, 1.f, S, mi, mw);
     __builtin_amdgcn_s_setprio(0);
-    publish_topk<KM>(idx, w, sidx, sw);
+    if (lane_id() < K) {
+      sidx[lane_id()] = mi;
+      sw[lane_id()] = mw;
+    }
   }
   __syncthreads();
 }
@@ -458,14 +516,15 @@ __global__ __launch_bounds__(kBlock) void k_expert_gateup(const uint8_t *__restr
 
 // ------------------------------------------------------------------ layer kernels
 
-// gate/up pair iterations per wavefront (routed and shared), and routed down row
-// iterations per wavefront by the padded top_k (fewer rows per wavefront above
-// four slots keep the weight registers of a wavefront the same)
-template <int BITS>
-constexpr int gateup_iters() {
-  return 2;
-}
-__host__ __device__ constexpr int down_iters(int kpad) { return kpad <= 4 ? 4 : 16 / kpad; }
+// gate/up pair iterations per wavefront (routed and shared): four above four
+// slots, which halves the routed workgroups so that they are all resident at once
+// (3 per compute unit; at top-10, 1,280 workgroups with two pairs each ran in two
+// rounds); and routed down row iterations per wavefront by the padded top_k: two
+// above four slots (measured,
+// top-10 layer: 12.8 us for the down kernel against 14.9 with one row per
+// wavefront, whose workgroups each stage all of h for a quarter of the rows)
+__host__ __device__ constexpr int gateup_iters(int K) { return K <= 4 ? 2 : 4; }
+__host__ __device__ constexpr int down_iters(int kpad) { return kpad <= 4 ? 4 : 2; }
 constexpr int kP3Block = 256;      // threads per down + combine workgroup
 constexpr int kP3Waves = kP3Block / kWave;
 
@@ -656,8 +715,9 @@ struct Phase2Args {
 // expert. Shared blocks run the shared expert's gate/up + SwiGLU: it does not
 // depend on the routing, so its weights stream while the routed blocks are still
 // choosing. x arrives in the digit form the router kernel wrote (RMS factor
-// included), so this kernel reads no raw x. KM: 8 for top_k <= 8, else kMaxTopK.
-template <int BITS, int NGHP, int KM>
+// included), so this kernel reads no raw x. GI: gate/up pair iterations per
+// wavefront (gateup_iters(top_k)).
+template <int BITS, int NGHP, int GI>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void k_phase2(const Phase2Args a) {
   constexpr int RPIH = kWave / NGHP;
   constexpr int D4 = (NGHP * kDigStride / 4 + kBlock - 1) / kBlock;
@@ -666,6 +726,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   __shared__ __align__(16) float lg[kMaxExperts];
   __shared__ int sidx[kMaxTopK];
   __shared__ float sw[kMaxTopK];
+  __shared__ TopkLds tks;
   const int lane = lane_id();
   const float *xsrc = reinterpret_cast<const float *>(a.xdig);
   trace_mark(a.trace, 0);
@@ -688,15 +749,19 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         __builtin_amdgcn_sched_barrier(0);
         stage_load(xsrc, NF4, xst);
         __builtin_amdgcn_sched_barrier(0);
-        int key[8], idx[KM];
-        float w[KM];
+        int key[8];
         logit_keys<8>(lv, a.E, key);
         // the rest of the workgroup waits on this wavefront: let it win the
         // SIMD's issue arbitration against co-resident wavefronts of other workgroups
         __builtin_amdgcn_s_setprio(3);
-        wave_topk_keys<8, KM>(key, bslot + 1, idx, w, 1.f);
+        int mi;
+        float mw;
+        wave_topk<8>(key, bslot + 1, 1.f, tks, mi, mw);
         __builtin_amdgcn_s_setprio(0);
-        publish_topk<KM>(idx, w, sidx, sw);
+        if (lane <= bslot) {
+          sidx[lane] = mi;
+          sw[lane] = mw;
+        }
       } else {
         stage_load(xsrc, NF4, xst);
       }
@@ -710,14 +775,14 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       stage_copy(xst, NF4, xdl);
       __syncthreads();
       trace_mark(a.trace, 1);
-      block_topk<KM>(lg, a.E, bslot + 1, sidx, sw);
+      block_topk(lg, a.E, bslot + 1, tks, sidx, sw);
     }
     trace_mark(a.trace, 2);
     const int wv = blockIdx.x * kWavesPerBlock + wave_in_block();
     const int slot = min(wv / a.waves_per_slot, a.K - 1);
-    const int pair0 = (wv % a.waves_per_slot) * gateup_iters<BITS>() * RPIH;
+    const int pair0 = (wv % a.waves_per_slot) * GI * RPIH;
     const bool active = wv < a.waves_per_slot * a.K;
-    PairLoads<BITS, NGHP, gateup_iters<BITS>()> P;
+    PairLoads<BITS, NGHP, GI> P;
     if (active) P.issue(a.bank + (size_t)sidx[slot] * a.stride, a.ng, pair0);
     if (wv == (a.K - 1) * a.waves_per_slot && lane < a.K) {
       const int sel = sidx[lane];
@@ -737,13 +802,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   }
   // shared expert gate/up
   const int wv = (blockIdx.x - a.n_routed_blocks) * kWavesPerBlock + wave_in_block();
-  const int pair0 = wv * gateup_iters<BITS>() * RPIH;
+  const int pair0 = wv * GI * RPIH;
   // x first (its loads complete before the weights', so the staging does not
   // wait for them), then the weights
   Staged<D4> xst;
   stage_load(xsrc, NF4, xst);
   __builtin_amdgcn_sched_barrier(0);
-  PairLoads<BITS, NGHP, gateup_iters<BITS>()> P;
+  PairLoads<BITS, NGHP, GI> P;
   if (pair0 < a.I) P.issue(a.shared_gu, a.ng, pair0);
   stage_copy(xst, NF4, xdl);
   __syncthreads();
@@ -1026,7 +1091,7 @@ struct LayerGeom {
   __host__ LayerGeom(const LayerArgs &L, int bits) {
     const bool sh = L.shared != nullptr;
     n1r = (L.E + kWavesPerBlock / router_split<NGH>() - 1) / (kWavesPerBlock / router_split<NGH>());
-    constexpr int GI = gateup_iters<BITS>();
+    const int GI = gateup_iters(L.K);
     wps = (L.I / RPIH + GI - 1) / GI;
     n2r = blocks_for((long)wps * L.K);
     n2s = sh ? blocks_for(wps) : 0;
@@ -1135,10 +1200,12 @@ struct Dispatch {
     p2.shared_gu = has_shared ? L.shared : nullptr;
     p2.h_shared = L.h_shared;
     p2.trace = L.trace ? L.trace + (size_t)kTraceBlocks * kTraceSlots : nullptr;
-    if (L.K <= 8)
-      hipLaunchKernelGGL((k_phase2<BITS, NGH, 8>), dim3(G.n2r + G.n2s), dim3(kBlock), 0, s, p2);
+    static_assert(gateup_iters(4) == 2 && gateup_iters(5) == 4, "the builds below");
+    const dim3 grid(G.n2r + G.n2s);
+    if (L.K <= 4)
+      hipLaunchKernelGGL((k_phase2<BITS, NGH, 2>), grid, dim3(kBlock), 0, s, p2);
     else
-      hipLaunchKernelGGL((k_phase2<BITS, NGH, kMaxTopK>), dim3(G.n2r + G.n2s), dim3(kBlock), 0, s, p2);
+      hipLaunchKernelGGL((k_phase2<BITS, NGH, 4>), grid, dim3(kBlock), 0, s, p2);
     return hipGetLastError();
   }
 

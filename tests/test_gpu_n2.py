@@ -139,3 +139,33 @@ def test_large_batch_stack(device):
             l2 = np.linalg.norm(ha[l, t] - ref) / np.linalg.norm(ref)
             assert mx <= 2e-3 and l2 <= 1e-4, (l, t, mx, l2)
             h = ref
+
+
+@pytest.mark.parametrize("n_exp,B,hidden,inter,k", [(40, 33, 768, 256, 4), (13, 35, 1280, 256, 3),
+                                                    (64, 48, 2304, 512, 8), (24, 47, 256, 768, 2)])
+def test_router_tiles_ragged(device, n_exp, B, hidden, inter, k):
+    """From 32 tokens the router runs as 16 x 16 tiles on the matrix cores: expert and
+    token counts that are not multiples of 16 (clamped tile edges), expert tile counts
+    that are not multiples of 8 (the plain tile order), and several widths."""
+    print(f"router tiles E={n_exp} B={B} hidden={hidden}", flush=True)
+    L = host_layer(75, 0, 4, n_exp, k, hidden, inter, device)
+    OL = OracleLayer(75, 0, 4, n_exp, k, hidden, inter)
+    X = _x(75, B + n_exp, hidden, B)
+    RES = synth.activations(75, synth.T_RESIDUAL, B, B, hidden)
+    _check(device, OL, L, X, RES, f"router tiles E={n_exp} B={B}")
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_router_tiles_full_size(device, bits):
+    """32 and 40 tokens at the workload's size (512 experts: 32 expert tiles, placed by
+    XCD), every token against the oracle."""
+    hidden, inter, n_exp, k = 4096, 1024, 512, 4
+    L = device_layer(synth.SEED, 31, bits, n_exp, k, hidden, inter, device)
+    OL = OracleLayer(synth.SEED, 31, bits, n_exp, k, hidden, inter)
+    for B in (32, 40):
+        print(f"router tiles full size q{bits} B={B}", flush=True)
+        X = _x(synth.SEED, 9500 + B, hidden, B)
+        RES = synth.activations(synth.SEED, synth.T_RESIDUAL, 9500 + B, B, hidden)
+        _check(device, OL, L, X, RES, f"router tiles full size q{bits} B={B}")
+    del L
+    torch.cuda.empty_cache()
