@@ -38,6 +38,12 @@ KERNEL_SOURCES = ["layer_kernels.h", "device.h", "kernels.h", "layout.h", "kerne
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "moe_layer_q4_B1_hbm_counters.txt")
 PHASE_NAMES = {1: "router + shared gate (k_phase1)", 2: "routing + routed and shared gate/up (k_phase2)",
                4: "routed and shared down + combine (k_phase3)"}
+# the grouped layer's launches per phase (B > 1): the router and token preparation;
+# the gate/up of the distinct experts (above 64 tokens after the routing kernels);
+# the down projections and the combine
+GROUP_PHASE_NAMES = {1: "router + token preparation (k_g1 / k_g1t)",
+                     2: "gate/up of the distinct routed and shared experts (k_g2; k_topk + k_group above 64 tokens)",
+                     4: "down projections + combine (k_g3 + k_g4)"}
 
 
 def log(*a):
@@ -447,6 +453,25 @@ def versions(torch):
     return v
 
 
+def kernels_per_layer(B, K):
+    """Launches of one layer: 3 for one token; grouped, 4, or 6 with the routing kernels
+    (more than 64 tokens or 512 (token, choice) slots)."""
+    if B == 1:
+        return 3
+    return 6 if (B > 64 or B * K > 512) else 4
+
+
+def group_phase_bytes(phase, d_routed, eb, gub, E, H, I, K, B):
+    """Algorithmic bytes of one grouped phase: every weight row once, plus activations."""
+    if phase == 1:   # router + gate vector; x in; logits, x in integer form out
+        return E * H * 4 + H * 4 + B * H * 4 + B * E * 4 + 3 * B * H
+    if phase == 2:   # distinct routed + shared gate/up halves; logits, x (integer form) in
+        return (d_routed + 1) * gub + B * E * 4 + 3 * B * H
+    if phase == 4:   # distinct routed + shared down halves; partials, residual, shared output, out
+        return (d_routed + 1) * (eb - gub) + B * (K + 2) * H * 4
+    raise ValueError(phase)
+
+
 def phase_bytes(phase, d_routed, eb, gub, E, H, I, K, bits):
     """Algorithmic bytes one launch of a layer kernel moves (B=1): the weights it must
     stream once plus its activation reads and writes."""
@@ -625,31 +650,31 @@ def main():
     act_bytes_layer = 3 * B * H * 4
     weight_gbps = w_bytes_layer / (us_layer * 1e3)
 
-    # ---- per-kernel durations (HIP events on the launching stream), B=1 layers
+    # ---- per-kernel (B=1) or per-phase (grouped) durations, HIP events on the launching stream
     roofline, kernels = None, {}
-    if B == 1:
+    if True:
         log("bench: timing each layer kernel")
         kstream = torch.cuda.Stream()
-        xs = torch.from_numpy(np.stack([synth.activations(a.seed, synth.T_X, l, 1, H)[0]
+        xs = torch.from_numpy(np.stack([synth.activations(a.seed, synth.T_X, l, B, H)
                                         for l in range(n_layers)])).to(dev)
-        outs = torch.empty((n_layers, H), dtype=torch.float32, device=dev)
-        lws_bytes = qem.fmoe_workspace_bytes(layers[0], 1)
+        outs = torch.empty((n_layers, B, H), dtype=torch.float32, device=dev)
+        lws_bytes = qem.fmoe_workspace_bytes(layers[0], B)
         lws = torch.empty((n_layers, (lws_bytes + 255) // 256 * 256), dtype=torch.uint8, device=dev)
-        kp = (K + 3) // 4 * 4  # (rows 16-byte aligned)
+        kp = (B * K + 3) // 4 * 4  # (rows 16-byte aligned)
         kidx = torch.empty((n_layers, kp), dtype=torch.int32, device=dev)
         with torch.cuda.stream(kstream):
             for l in range(n_layers):   # full layers first: every kernel's inputs are then in place
-                qem.fmoe_moe_layer_phases(layers[l], xs[l:l + 1], xs[l:l + 1], outs[l:l + 1], 7, lws[l],
-                                          topk_idx=kidx[l:l + 1, :K], stream=kstream, c_layer=c_layers[l])
+                qem.fmoe_moe_layer_phases(layers[l], xs[l], xs[l], outs[l], 7, lws[l],
+                                          topk_idx=kidx[l, :B * K], stream=kstream, c_layer=c_layers[l])
         kstream.synchronize()
-        kd = float(np.mean([len(set(r[:K].tolist())) for r in kidx.cpu().numpy()]))
+        kd = float(np.mean([len(set(r[:B * K].tolist())) for r in kidx.cpu().numpy()]))
+        names = PHASE_NAMES if B == 1 else GROUP_PHASE_NAMES
         for ph in (1, 2, 4):
-            # n_layers launches of one kernel, captured once and replayed on kstream
+            # n_layers launches of one phase, captured once and replayed on kstream
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=kstream):
                 for l in range(n_layers):
-                    qem.fmoe_moe_layer_phases(layers[l], xs[l:l + 1], xs[l:l + 1], outs[l:l + 1], ph, lws[l],
-                                              c_layer=c_layers[l])
+                    qem.fmoe_moe_layer_phases(layers[l], xs[l], xs[l], outs[l], ph, lws[l], c_layer=c_layers[l])
             with torch.cuda.stream(kstream):
                 g.replay()
                 e0 = torch.cuda.Event(enable_timing=True)
@@ -661,13 +686,15 @@ def main():
             kstream.synchronize()
             del g
             us = e0.elapsed_time(e1) * 1000.0 / (a.kernel_reps * n_layers)
-            nbytes = phase_bytes(ph, kd, eb, gub, E, H, I, K, bits)
-            kernels[PHASE_NAMES[ph]] = {"avg_us": round(us, 3), "algorithmic_bytes": int(nbytes),
-                                        "GBps": round(nbytes / (us * 1e3), 1)}
+            nbytes = (phase_bytes(ph, kd, eb, gub, E, H, I, K, bits) if B == 1
+                      else group_phase_bytes(ph, kd, eb, gub, E, H, I, K, B))
+            kernels[names[ph]] = {"avg_us": round(us, 3), "algorithmic_bytes": int(nbytes),
+                                  "GBps": round(nbytes / (us * 1e3), 1)}
         dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
         kk = kernels[dom]
         tag = dom.split("(")[-1].rstrip(")")
-        traffic = counter_traffic(tag) if (bits == 4 and (H, I, E, K) == (4096, 1024, 512, 4)) else None
+        traffic = (counter_traffic(tag) if (B == 1 and bits == 4 and (H, I, E, K) == (4096, 1024, 512, 4))
+                   else None)
         roofline = {"bound": "hbm", "achieved": kk["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(kk["GBps"] / HBM_PEAK_GBPS, 4), "traffic": traffic, "traffic_unit": "bytes/launch",
                     "kernel": dom, "avg_us": kk["avg_us"], "algorithmic_bytes_per_launch": kk["algorithmic_bytes"]}
@@ -721,7 +748,7 @@ def main():
     # plus one empty-kernel launch per kernel of the layer
     floor = None
     if ceiling and gap is not None:
-        n_k = 3 if B == 1 else 4
+        n_k = kernels_per_layer(B, K)
         stream_us = w_bytes_layer / (ceiling["GBps"] * 1e3)
         floor = {"stream_at_read_ceiling_us": round(stream_us, 3), "launch_gaps_us": round(n_k * gap, 3),
                  "total_us": round(stream_us + n_k * gap, 3)}
@@ -745,7 +772,7 @@ def main():
                    "top_k": K, "hidden": H, "inter": I, "group": 64, "graph": graph is not None,
                    "seed": a.seed},
         "us_per_layer_p10_p50_p90": spread,
-        "kernels_per_layer": 3 if B == 1 else 4,
+        "kernels_per_layer": kernels_per_layer(B, K),
         "floor_us": floor,
         "weight_GBps": round(weight_gbps, 1),
         "frac_hbm_peak": round(weight_gbps / HBM_PEAK_GBPS, 4),

@@ -98,6 +98,7 @@ GroupArgs group_args(const fmoe_layer *L, int B, const float *x, float rms_eps, 
   g.out_idx = topk_idx;
   g.out_w = topk_w;
   g.logits = (float *)(ws + w.logits);
+  g.logit_parts = router_parts(E, B, H);
   g.sigma = (float *)(ws + w.sigma);
   g.gdot = (float *)(ws + w.gdot);
   g.idx = (int32_t *)(ws + w.topk_idx);

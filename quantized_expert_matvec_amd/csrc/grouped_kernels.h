@@ -432,46 +432,43 @@ __host__ __device__ constexpr int g1_rows_per_block() {
 }
 
 // From kRouterTileMin tokens the router runs on the matrix cores instead
-// (router_tile below): every workgroup of the row-held form reads every token's
-// x. Measured per layer (60-layer q4 stack): equal at 32 tokens, 11 us less at
-// 48, 20 at 64, 58 at 128; at 24 tokens the row-held form is 2 us faster.
-constexpr int kRouterTileMin = 32;
-constexpr int kRt = 16;  // experts and tokens per router tile
-__host__ __device__ inline bool router_tiled(int B) { return B >= kRouterTileMin; }
-__host__ __device__ inline int router_tiles(int E, int B) { return ((E + kRt - 1) / kRt) * ((B + kRt - 1) / kRt); }
+// (router_tile below): every workgroup of the row-held form reads every token's x.
 
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
-// One tile of the router on the matrix cores: logits[t][e] = R_e . x_t (fp32,
-// unscaled) for 16 experts x 16 tokens, with v_mfma_f32_16x16x4_f32 (fp32
-// products, fp32 sums). Lane l holds A[l % 16][k] and B[k][l % 16] for k = l / 16:
-// with two float4 loads per operand the lane covers columns c + 8 (l / 16) .. + 7
-// of its expert's row and of its token, and eight MFMAs take them in turn (the
-// same column order on both sides). The four wavefronts take a quarter of the
-// columns each; their partial tiles are added in LDS in wavefront order, so the
-// result does not depend on timing. Tiles that share experts run on one XCD
-// (the dispatcher places workgroup b on XCD b % 8; with a multiple of 8 expert
-// tiles, expert tile r goes to XCD r % 8), so each XCD's L2 serves the router rows
-// to all token tiles after one read. part: 4 x 256 floats of LDS.
+// One part of one tile of the router on the matrix cores: for 16 experts x 16
+// tokens, the dot products R_e . x_t over the part's columns (fp32, unscaled),
+// with v_mfma_f32_16x16x4_f32 (fp32 products, fp32 sums), into logit slab p.
+// Lane l holds A[l % 16][k] and B[k][l % 16] for k = l / 16: with two float4
+// loads per operand the lane covers columns c + 8 (l / 16) .. + 7 of its expert's
+// row and of its token, and eight MFMAs take them in turn (the same column order
+// on both sides). The four wavefronts take a quarter of the part's columns each;
+// their partial tiles are added in LDS in wavefront order, so the result does not
+// depend on timing. Workgroups that share router rows (same expert tile and part)
+// run on one XCD (the dispatcher places workgroup b on XCD b % 8; with a multiple
+// of 8 such units, unit u goes to XCD u % 8), so each XCD's L2 serves those rows to
+// all token tiles after one read. part: 4 x 256 floats of LDS.
 __device__ __forceinline__ void router_tile(const GroupArgs &a, float (*part)[kRt * kRt]) {
   const int lane = lane_id(), wv = wave_in_block();
-  const int n_rt = (a.E + kRt - 1) / kRt, n_tt = (a.B + kRt - 1) / kRt;
+  const int P = a.logit_parts;
+  const int n_units = ((a.E + kRt - 1) / kRt) * P, n_tt = (a.B + kRt - 1) / kRt;
   const int b = blockIdx.x;
-  int rt, tt;
-  if (n_rt % 8 == 0) {
+  int un, tt;  // unit = (expert tile, part), token tile
+  if (n_units % 8 == 0) {
     const int x = b % 8, s = b / 8;
-    rt = x + 8 * (s / n_tt);
+    un = x + 8 * (s / n_tt);
     tt = s % n_tt;
   } else {
-    rt = b / n_tt;
+    un = b / n_tt;
     tt = b % n_tt;
   }
-  const int H = a.H;
+  const int rt = un / P, pt = un % P;
+  const int H = a.H, HP = H / P;  // the part's columns
   const int e0 = rt * kRt, t0 = tt * kRt;
-  const int cw = wv * (H / kWavesPerBlock) + 8 * (lane >> 4);  // this lane's first column
+  const int cw = pt * HP + wv * (HP / kWavesPerBlock) + 8 * (lane >> 4);  // this lane's first column
   const float4 *rp = reinterpret_cast<const float4 *>(a.router + (size_t)min(e0 + (lane & 15), a.E - 1) * H + cw);
   const float4 *xp = reinterpret_cast<const float4 *>(a.x + (size_t)min(t0 + (lane & 15), a.B - 1) * H + cw);
-  const int steps = H / kWavesPerBlock / 32;  // 32 columns per step (H a multiple of 256: even, >= 2)
+  const int steps = HP / kWavesPerBlock / 32;  // 32 columns per step (router_parts keeps it whole, >= 1)
   constexpr int U = 8;                        // steps in flight (128 KB per workgroup)
   float4 ra[U][2], xa[U][2];
 #pragma unroll
@@ -486,7 +483,7 @@ __device__ __forceinline__ void router_tile(const GroupArgs &a, float (*part)[kR
   for (int st = 0; st < steps; st += U) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (st + u >= steps) break;  // (uniform; steps is even, U a power of two)
+      if (st + u >= steps) break;  // (uniform)
       const float4 r0 = ra[u][0], r1 = ra[u][1], x0 = xa[u][0], x1 = xa[u][1];
       const int nx = min(st + U + u, steps - 1);  // (past the end: the last step again, unused)
       ra[u][0] = rp[8 * nx];
@@ -511,7 +508,7 @@ __device__ __forceinline__ void router_tile(const GroupArgs &a, float (*part)[kR
   const float d = ((part[0][o] + part[1][o]) + part[2][o]) + part[3][o];
   const int l = o & 63, j = o >> 6;
   const int e = e0 + 4 * (l >> 4) + j, t = t0 + (l & 15);
-  if (e < a.E && t < a.B) a.logits[(size_t)t * logit_stride(a.E) + e] = d;
+  if (e < a.E && t < a.B) a.logits[((size_t)pt * a.B + t) * logit_stride(a.E) + e] = d;
 }
 
 // Input preparation of token t for the matrix cores (RMS factor xinv; per group
@@ -660,8 +657,8 @@ __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
 }
 
 // g1, for batches of kRouterTileMin tokens or more: workgroups [0,
-// n_router_blocks) compute the router in 16 x 16 tiles on the matrix cores
-// (router_tile), workgroups n_router_blocks + t prepare token t (g1_prep).
+// n_router_blocks) compute the router in parts of 16 x 16 tiles on the matrix
+// cores (router_tile), workgroups n_router_blocks + t prepare token t (g1_prep).
 template <int BITS>
 __global__ __launch_bounds__(kBlock) void k_g1t(const GroupArgs a) {
   static_assert(kBlock == kRt * kRt && kWavesPerBlock == 4, "one output per thread, four column quarters");
@@ -752,8 +749,9 @@ __device__ __forceinline__ int block_route(const GroupArgs &a, RouteLdsT<NW> &R,
     for (int t0 = wave; t0 < a.B; t0 += 2 * kGWaves) {
       const int t1 = min(t0 + kGWaves, a.B - 1);  // (past the end: a repeat, unused)
       float v0[8], v1[8];
-      load_logits<8>(a.logits + (size_t)t0 * logit_stride(a.E), a.E, v0);
-      load_logits<8>(a.logits + (size_t)t1 * logit_stride(a.E), a.E, v1);
+      const size_t ps = (size_t)a.B * logit_stride(a.E);  // (slab stride)
+      load_logits<8>(a.logits + (size_t)t0 * logit_stride(a.E), a.E, v0, a.logit_parts, ps);
+      load_logits<8>(a.logits + (size_t)t1 * logit_stride(a.E), a.E, v1, a.logit_parts, ps);
       const float inv0 = a.xinv[t0], inv1 = a.xinv[t1];
       const float gd0 = a.gvec ? a.gdot[t0] : 0.f, gd1 = a.gvec ? a.gdot[t1] : 0.f;
       int key[8], mi;
@@ -773,7 +771,8 @@ __device__ __forceinline__ int block_route(const GroupArgs &a, RouteLdsT<NW> &R,
       const float gd = a.gvec ? a.gdot[t] : 0.f;
       int mi;
       float mw;
-      wave_topk_lds(a.logits + (size_t)t * logit_stride(a.E), a.E, a.K, inv, tk, mi, mw);
+      wave_topk_lds(a.logits + (size_t)t * logit_stride(a.E), a.E, a.K, inv, tk, mi, mw, a.logit_parts,
+                    (size_t)a.B * logit_stride(a.E));
       publish(t, mi, mw, inv, gd);
     }
   }
@@ -866,7 +865,8 @@ __global__ __launch_bounds__(kGThreads) void k_topk(const GroupArgs a) {
   const float gd = a.gvec ? a.gdot[t] : 0.f;
   int mi;
   float mw;
-  wave_topk_lds(a.logits + (size_t)t * logit_stride(a.E), a.E, a.K, inv, tks[wave_in_block()], mi, mw);
+  wave_topk_lds(a.logits + (size_t)t * logit_stride(a.E), a.E, a.K, inv, tks[wave_in_block()], mi, mw,
+                a.logit_parts, (size_t)a.B * logit_stride(a.E));
   if (lane < a.K) {  // lane j stores choice j
     const int s = t * a.K + lane;
     a.idx[s] = mi;
@@ -1311,7 +1311,7 @@ struct GroupDispatch {
   template <int NGH>
   static void launch_g1(GroupArgs &a, hipStream_t s) {
     if (router_tiled(a.B)) {
-      a.n_router_blocks = router_tiles(a.E, a.B);
+      a.n_router_blocks = router_tiles(a.E, a.B) * a.logit_parts;
       hipLaunchKernelGGL(k_g1t<BITS>, dim3(a.n_router_blocks + a.B), dim3(kBlock), 0, s, a);
     } else {
       a.n_router_blocks = (a.E + g1_rows_per_block<NGH>() - 1) / g1_rows_per_block<NGH>();

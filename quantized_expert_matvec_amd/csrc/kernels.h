@@ -61,7 +61,8 @@ struct GroupArgs {
   int32_t *out_idx;          // [B][K] or null
   float *out_w;              // [B][K] or null
   // workspace
-  float *logits;             // [B][logit_stride(E)] router rows . x, before the RMS factor
+  float *logits;             // [logit_parts][B][logit_stride(E)] router rows . x, before the RMS factor
+  int logit_parts;           // slabs to add (router_parts)
   float *sigma;              // [B]
   float *gdot;               // [B]        gate vector . x, before the RMS factor
   int32_t *idx;              // [B][K]

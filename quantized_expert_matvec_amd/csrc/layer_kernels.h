@@ -411,12 +411,31 @@ __device__ __forceinline__ void wave_topk(int (&key)[VPL], int K, float lscale, 
 // the wavefront covers whole cache lines, where VPL-strided 4-byte loads would
 // touch VPL times as many lines per instruction.
 template <int VPL>
-__device__ __forceinline__ void load_logits(const float *lg, int E, float (&v)[VPL]) {
+__device__ __forceinline__ void load_logits(const float *lg, int E, float (&v)[VPL], int parts = 1,
+                                            size_t pstride = 0) {
   const int lane = lane_id();
   const float4 *l4 = reinterpret_cast<const float4 *>(lg);
 #pragma unroll
   for (int q = 0; q < VPL / 4; ++q) {
-    const float4 t = l4[min(VPL / 4 * lane + q, (E + 3) / 4 - 1)];
+    const int i = min(VPL / 4 * lane + q, (E + 3) / 4 - 1);
+    float4 t = l4[i];
+    if (parts > 1) {
+      // slabs of a split router, all requested at once (past the last: the last
+      // again, not added), then added in slab order (every reader the same)
+      float4 u[kRouterMaxParts - 1];
+#pragma unroll
+      for (int p = 1; p < kRouterMaxParts; ++p)
+        u[p - 1] = reinterpret_cast<const float4 *>(lg + min(p, parts - 1) * pstride)[i];
+#pragma unroll
+      for (int p = 1; p < kRouterMaxParts; ++p) {
+        if (p < parts) {
+          t.x += u[p - 1].x;
+          t.y += u[p - 1].y;
+          t.z += u[p - 1].z;
+          t.w += u[p - 1].w;
+        }
+      }
+    }
     v[4 * q] = t.x;
     v[4 * q + 1] = t.y;
     v[4 * q + 2] = t.z;
@@ -436,17 +455,17 @@ __device__ __forceinline__ void logit_keys(const float (&v)[VPL], int E, int (&k
 
 // top-K of E <= kMaxExperts logits in memory (LDS or global); see wave_topk
 __device__ __forceinline__ void wave_topk_lds(const float *lg, int E, int K, float lscale, TopkLds &S, int &my_idx,
-                                              float &my_w) {
+                                              float &my_w, int parts = 1, size_t pstride = 0) {
   if (E <= 512) {
     float v[8];
     int key[8];
-    load_logits<8>(lg, E, v);
+    load_logits<8>(lg, E, v, parts, pstride);
     logit_keys<8>(v, E, key);
     wave_topk<8>(key, K, lscale, S, my_idx, my_w);
   } else {
     float v[16];
     int key[16];
-    load_logits<16>(lg, E, v);
+    load_logits<16>(lg, E, v, parts, pstride);
     logit_keys<16>(v, E, key);
     wave_topk<16>(key, K, lscale, S, my_idx, my_w);
   }
