@@ -297,7 +297,7 @@ __device__ __forceinline__ int candidate_rank(const TopkLds &S, int C, int ck, i
   return r;
 }
 
-// The top K (1 <= K <= kMaxTopK) at a cost that does not grow with K:
+// The general top K (1 <= K <= kMaxTopK) at a cost that does not grow with K:
 //  1. each lane's maximum key m1 (first position p1 among equal keys) and its
 //     second key m2;
 //  2. each lane ranks its maximum among the 64 by the number of greater lane
@@ -311,15 +311,9 @@ __device__ __forceinline__ int candidate_rank(const TopkLds &S, int C, int ck, i
 //     among them. At most 64 candidates are ranked exactly among themselves (value
 //     descending, index ascending); beyond that (many equal keys) K rounds take
 //     the wavefront maximum, lowest index first, one at a time.
-// Then lane j < K holds choice j: my_idx, and its renormalised softmax weight
-// my_w = exp((l_j - l_0) lscale) / sum_{i<K} exp((l_i - l_0) lscale) (renormalising
-// over the chosen K cancels the full softmax denominator), the sum taken in
-// choice order by every lane; lanes j >= K get 0 and 0. The logits may be held
-// unscaled: lscale > 0 is the factor that turns them into the true logits (it
-// does not change the order). key may be modified.
+// Slot j of S.widx / S.wkey receives choice j. key may be modified.
 template <int VPL>
-__device__ __forceinline__ void wave_topk(int (&key)[VPL], int K, float lscale, TopkLds &S, int &my_idx,
-                                          float &my_w) {
+__device__ __forceinline__ void topk_rank(int (&key)[VPL], int K, TopkLds &S) {
   constexpr int kGone = (int)0x80000000;
   const int lane = lane_id();
   int m1, p1, m2 = kGone;
@@ -391,6 +385,62 @@ __device__ __forceinline__ void wave_topk(int (&key)[VPL], int K, float lscale, 
       }
     }
   }
+}
+
+// Small K (at most kRoundsTopK): K rounds of the wavefront maximum over the lane
+// maxima, each taking every lane that equals it, need no exchange through LDS and
+// cost about one cross-lane reduction a round (on gfx950 ~110 cycles, which is why
+// it stops at small K). The picks are the top K exactly when no round matched two
+// lanes (no tie among lane maxima) and no lane holds a second key at or above the
+// last pick (then no element below a lane maximum can belong to the top K, nor tie
+// with the last pick); otherwise returns false and writes nothing. On success,
+// slot j of S.widx / S.wkey holds pick j (the lane of a pick writes it).
+constexpr int kRoundsTopK = 4;
+template <int VPL>
+__device__ __forceinline__ bool topk_rounds(const int (&key)[VPL], int K, TopkLds &S) {
+  constexpr int kGone = (int)0x80000000;
+  const int lane = lane_id();
+  int m1 = key[0];
+#pragma unroll
+  for (int m = 1; m < VPL; ++m) m1 = max(m1, key[m]);
+  int v = m1, myr = -1, last = kGone;
+  unsigned long long multi = 0ull;
+  for (int j = 0; j < K; ++j) {
+    const int g = wave_max_i(v);
+    const bool hit = v == g;
+    const unsigned long long bm = __ballot(hit);
+    multi |= bm & (bm - 1ull);  // (nonzero when more than one lane matched)
+    myr = hit ? j : myr;
+    v = hit ? kGone : v;
+    last = g;
+  }
+  int c = 0;
+#pragma unroll
+  for (int m = 0; m < VPL; ++m) c += key[m] >= last ? 1 : 0;
+  if (multi != 0ull || __ballot(c > 1) != 0ull) return false;
+  if (myr >= 0) {
+    int p = VPL - 1;  // the maximum's (only) position
+#pragma unroll
+    for (int m = VPL - 2; m >= 0; --m) p = key[m] == m1 ? m : p;
+    S.widx[myr] = VPL * lane + p;
+    S.wkey[myr] = m1;
+  }
+  return true;
+}
+
+// The top K (1 <= K <= kMaxTopK) of the wavefront's keys, exactly under the order
+// (value descending, index ascending): topk_rounds for small K, else (or when it
+// cannot decide) topk_rank. Then lane j < K holds choice j: my_idx, and its
+// renormalised softmax weight my_w = exp((l_j - l_0) lscale) / sum_{i<K}
+// exp((l_i - l_0) lscale) (renormalising over the chosen K cancels the full softmax
+// denominator), the sum taken in choice order by every lane; lanes j >= K get 0 and
+// 0. The logits may be held unscaled: lscale > 0 is the factor that turns them into
+// the true logits (it does not change the order). key may be modified.
+template <int VPL>
+__device__ __forceinline__ void wave_topk(int (&key)[VPL], int K, float lscale, TopkLds &S, int &my_idx,
+                                          float &my_w) {
+  const int lane = lane_id();
+  if (!(K <= kRoundsTopK && topk_rounds<VPL>(key, K, S))) topk_rank<VPL>(key, K, S);  // (uniform)
   wave_lds_fence();
   // weights, the sum in choice order
   const float l0 = key_value(S.wkey[0]);
@@ -755,6 +805,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     // the early slots start streaming before the last winner is known. The
     // workgroup that publishes the routing is one of the last slot's (all K).
     const int bslot = min((int)(blockIdx.x * kWavesPerBlock) / a.waves_per_slot, a.K - 1);
+    const int wv = blockIdx.x * kWavesPerBlock + wave_in_block();
+    const int slot = min(wv / a.waves_per_slot, a.K - 1);
+    const int pair0 = (wv % a.waves_per_slot) * GI * RPIH;
+    const bool active = wv < a.waves_per_slot * a.K;
+    PairLoads<BITS, NGHP, GI> P;
     if (a.E <= 512) {
       // One wavefront (b % 4, so that the workgroups sharing a CU use different
       // SIMDs) requests the logits in the top-K's layout before its share of x,
@@ -784,6 +839,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       } else {
         stage_load(xsrc, NF4, xst);
       }
+      // the routing is published before x is staged: the weight requests go out as
+      // soon as the top-K is known, and the staging then waits for x only (its
+      // loads went out first)
+      __syncthreads();
+      trace_mark(a.trace, 2);
+      // unconditional, so that the staging's wait counts the x loads only (every
+      // routed wavefront is active: waves_per_slot * K is a whole number of
+      // workgroups, and each wavefront's pairs lie inside its expert)
+      P.issue(a.bank + (size_t)sidx[slot] * a.stride, a.ng, pair0);
       stage_copy(xst, NF4, xdl);
       __syncthreads();
       trace_mark(a.trace, 1);
@@ -795,14 +859,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       __syncthreads();
       trace_mark(a.trace, 1);
       block_topk(lg, a.E, bslot + 1, tks, sidx, sw);
+      trace_mark(a.trace, 2);
+      if (active) P.issue(a.bank + (size_t)sidx[slot] * a.stride, a.ng, pair0);
     }
-    trace_mark(a.trace, 2);
-    const int wv = blockIdx.x * kWavesPerBlock + wave_in_block();
-    const int slot = min(wv / a.waves_per_slot, a.K - 1);
-    const int pair0 = (wv % a.waves_per_slot) * GI * RPIH;
-    const bool active = wv < a.waves_per_slot * a.K;
-    PairLoads<BITS, NGHP, GI> P;
-    if (active) P.issue(a.bank + (size_t)sidx[slot] * a.stride, a.ng, pair0);
     if (wv == (a.K - 1) * a.waves_per_slot && lane < a.K) {
       const int sel = sidx[lane];
       const float ws = sw[lane];
