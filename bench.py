@@ -78,7 +78,7 @@ def parse():
                         "one JSON line each, plus one for a repeated token (every expert a hit)")
     p.add_argument("--tier-layers", type=int, default=8, help="layers whose routed banks sit in pinned host memory")
     p.add_argument("--timeline", action="store_true",
-                   help="print device-clock stamps of a few layers' kernels inside the graph-captured stack (B=1) "
+                   help="print device-clock stamps of a few layers' kernels inside the graph-captured stack "
                         "instead of timing")
     return p.parse_args()
 
@@ -241,14 +241,16 @@ def calibrate_copy():
 
 
 def timeline(torch, np, qem, layers, c_layers, h_in, h0_all, ws, n_layers):
-    """Per-workgroup device-clock stamps (100 MHz) of the three kernels of a few layers,
+    """Per-workgroup device-clock stamps (100 MHz) of the kernels of a few layers,
     each inside the graph-captured stack, summarised per kernel: when the workgroups
-    start, have their inputs in LDS, know the routing, and end."""
+    start, have their inputs in LDS, know the routing, and end (one token), or finish
+    their work items (the grouped layer's persistent gate/up kernel)."""
+    B = h_in.shape[0]
     tr = torch.zeros((3, qem.TRACE_BLOCKS, qem.TRACE_SLOTS), dtype=torch.int64, device=h_in.device)
     h_out = torch.empty_like(h_in)
     picks = sorted({n_layers // 4, n_layers // 2, (3 * n_layers) // 4})
     names = ("k_phase1 (router, x digits, gate)", "k_phase2 (routing, gate/up)", "k_phase3 (down, combine)")
-    print("device-clock stamps of one layer's kernels inside the graph-captured stack (B=1); "
+    print(f"device-clock stamps of one layer's kernels inside the graph-captured stack (B={B}); "
           "µs from the first router workgroup's start; min / median / p90 / max over workgroups", flush=True)
     for lt in picks:
         def call():
@@ -277,6 +279,9 @@ def timeline(torch, np, qem, layers, c_layers, h_in, h0_all, ws, n_layers):
         us = lambda v: (v - t0) / 100.0
         q = lambda v: "/".join(f"{x:5.2f}" for x in np.percentile(us(v), [0, 50, 90, 100]))
         print(f"layer {lt}:", flush=True)
+        if B > 1:
+            timeline_grouped(np, rec, us, q)
+            continue
         for k in range(3):
             r = rec[k]
             if k == 0:
@@ -299,6 +304,40 @@ def timeline(torch, np, qem, layers, c_layers, h_in, h0_all, ws, n_layers):
         print(f"  last end -> next kernel's first start: k_phase1 -> k_phase2 {gaps[0]:.2f}, "
               f"k_phase2 -> k_phase3 {gaps[1]:.2f}; first start -> last end of the layer "
               f"{us(rec[2][:, 3].max()):.2f}", flush=True)
+
+
+def timeline_grouped(np, rec, us, q):
+    """Summary of the grouped layer's stamps: router + token preparation; the persistent
+    gate/up workgroups (start, routing derived, each item's end, end; items per workgroup
+    and the time per item); the down workgroups."""
+    names = ("router + token preparation", "gate/up (persistent)", "down")
+    r = rec[0]
+    print(f"  {names[0]:28s} {len(r):4d} wg  start {q(r[:, 0])}  end {q(r[:, 3])}", flush=True)
+    r = rec[1]
+    line = f"  {names[1]:28s} {len(r):4d} wg  start {q(r[:, 0])}"
+    routed = r[r[:, 1] > 0]
+    if len(routed):
+        line += f"  routing {q(routed[:, 1])}"
+    line += f"  first item end {q(r[r[:, 2] > 0][:, 2])}  end {q(r[:, 7])}"
+    print(line, flush=True)
+    items = (r[:, 2:7] > 0).sum(axis=1)
+    hist = {int(k): int(v) for k, v in zip(*np.unique(items, return_counts=True))}
+    durs = []
+    for row in r:
+        prev = row[1] if row[1] > 0 and row[1] < row[2] else row[0]
+        for i in range(5):
+            if row[2 + i] > 0:
+                durs.append((row[2 + i] - prev) / 100.0)
+                prev = row[2 + i]
+    d = np.array(durs)
+    print(f"  {'':28s} items per workgroup {hist} (5 = five or more); time per item "
+          f"{'/'.join(f'{x:5.2f}' for x in np.percentile(d, [0, 50, 90, 100]))} µs", flush=True)
+    r = rec[2]
+    print(f"  {names[2]:28s} {len(r):4d} wg  start {q(r[:, 0])}  end {q(r[:, 3])}", flush=True)
+    gaps = [us(rec[k + 1][:, 0].min()) - us(rec[k][:, 3 if k == 0 else 7].max()) for k in range(2)]
+    print(f"  last end -> next kernel's first start: router -> gate/up {gaps[0]:.2f} (routing kernels "
+          f"between them above 64 tokens), gate/up -> down {gaps[1]:.2f}; first start -> last down end "
+          f"{us(rec[2][:, 3].max()):.2f} (the combine follows)", flush=True)
 
 
 FORM_NAMES = {0: "naive (c*s+b)*x", 1: "recast fma(c, s*x, b*x)", 2: "group-factored s*sum(c*x)+b*sum(x)",
@@ -606,8 +645,6 @@ def main():
         torch.cuda.synchronize()
 
     if a.timeline:
-        if B != 1:
-            raise SystemExit("--timeline needs --batch 1")
         timeline(torch, np, qem, layers, c_layers, h_in, h0_all, ws, n_layers)
         return
 

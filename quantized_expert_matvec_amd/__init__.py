@@ -516,7 +516,7 @@ TRACE_BLOCKS, TRACE_SLOTS = 4096, 8  # FMOE_TRACE_BLOCKS, FMOE_TRACE_SLOTS
 def fmoe_moe_stack_trace(layers: Sequence[Layer], h0: torch.Tensor, trace: torch.Tensor, trace_layer: int,
                          h_out: Optional[torch.Tensor] = None, eps: float = 1e-6, ws=None, stream=None,
                          c_layers=None) -> torch.Tensor:
-    """fmoe_moe_stack for one token with device-clock stamps of layer `trace_layer`'s
+    """fmoe_moe_stack with device-clock stamps of layer `trace_layer`'s
     kernels in `trace` (int64 [3, TRACE_BLOCKS, TRACE_SLOTS] on the device, zeroed by the caller)."""
     _dev_f32(h0, "h0")
     if trace.dtype != torch.int64 or trace.numel() < 3 * TRACE_BLOCKS * TRACE_SLOTS or not trace.is_cuda:

@@ -118,14 +118,15 @@ GroupArgs group_args(const fmoe_layer *L, int B, const float *x, float rms_eps, 
 // Enqueue one layer for n_tokens tokens (arguments already validated): the
 // one-token kernels for a single token, the grouped kernels for several.
 // rms_eps >= 0: the layer input is rms_scale(x, rms_eps), computed inside the layer's kernels.
-// trace: device-clock stamps of the one-token kernels (layout in fmoe.h), or null.
+// trace: device-clock stamps of the layer's kernels (layout in fmoe.h), or null.
 fmoe_status layer_enqueue(const fmoe_layer *L, int B, const float *x, float rms_eps, const float *residual,
                           float *out, int32_t *topk_idx, float *topk_w, uint8_t *ws, hipStream_t s,
                           int phases = 7, uint64_t *trace = nullptr) {
   const LayerWs w = layer_ws(B, L->n_experts, L->top_k, L->hidden, L->inter, B > 1);
   const int H = L->hidden, I = L->inter, E = L->n_experts, K = L->top_k;
   if (B > 1) {
-    const GroupArgs g = group_args(L, B, x, rms_eps, residual, out, topk_idx, topk_w, ws);
+    GroupArgs g = group_args(L, B, x, rms_eps, residual, out, topk_idx, topk_w, ws);
+    g.trace = trace;
     return launch_group(g, s, phases) == hipSuccess ? FMOE_OK : FMOE_ERR_LAUNCH;
   }
   for (int t = 0; t < B; ++t) {
@@ -601,7 +602,7 @@ fmoe_status fmoe_moe_stack_trace(const fmoe_layer *layers, int n_layers, int n_t
                                  float *h_out, float eps, void *ws, size_t ws_bytes, uint64_t *trace,
                                  int trace_layer, void *stream) {
   if (!trace) return FMOE_ERR_NULL;
-  if (n_tokens != 1 || trace_layer < 0 || trace_layer >= n_layers) return FMOE_ERR_BATCH;
+  if (trace_layer < 0 || trace_layer >= n_layers) return FMOE_ERR_BATCH;
   if ((uintptr_t)trace % 8) return FMOE_ERR_ALIGN;
   if (ws && overlap(trace, sizeof(uint64_t) * 3 * FMOE_TRACE_BLOCKS * FMOE_TRACE_SLOTS, ws, ws_bytes))
     return FMOE_ERR_ALIAS;

@@ -64,6 +64,12 @@ constexpr int kWaveLds = 16 * (2 * 8 * 16 + 16) + 16 * 9 * 4;  // LDS bytes per 
 
 typedef __attribute__((ext_vector_type(4))) int i32x4_t;
 
+// Profiling hook: thread 0 of the workgroup stamps the device clock into stamp
+// slot of kernel k's rows of the trace (null in normal use).
+__device__ __forceinline__ void gtrace(const GroupArgs &a, int k, int slot) {
+  trace_mark(a.trace ? a.trace + (size_t)k * kTraceBlocks * kTraceSlots : nullptr, slot);
+}
+
 // ------------------------------------------------------------------ integer form
 
 // The shift k of a group whose largest magnitude is amax (< 2^e): values are
@@ -597,8 +603,10 @@ __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
   __shared__ float dp[kWavesPerBlock][kMaxTokens];           // per wavefront: its part of each token's dot
   const int lane = lane_id();
   const int wv = wave_in_block();
+  gtrace(a, 0, 0);
   if ((int)blockIdx.x >= a.n_router_blocks) {
     g1_prep(a, blockIdx.x - a.n_router_blocks, part);
+    gtrace(a, 0, 3);
     return;
   }
   // ---- router rows: a wavefront holds its part of one fp32 row in registers;
@@ -654,6 +662,7 @@ __global__ __launch_bounds__(kBlock) void k_g1(const GroupArgs a) {
     const int rw = (int)blockIdx.x * RPB + r;
     if (rw < a.E) a.logits[(size_t)t * logit_stride(a.E) + rw] = d;
   }
+  gtrace(a, 0, 3);
 }
 
 // g1, for batches of kRouterTileMin tokens or more: workgroups [0,
@@ -664,11 +673,12 @@ __global__ __launch_bounds__(kBlock) void k_g1t(const GroupArgs a) {
   static_assert(kBlock == kRt * kRt && kWavesPerBlock == 4, "one output per thread, four column quarters");
   __shared__ float part[2][kWavesPerBlock];
   __shared__ float tile[kWavesPerBlock][kRt * kRt];
-  if ((int)blockIdx.x >= a.n_router_blocks) {
+  gtrace(a, 0, 0);
+  if ((int)blockIdx.x >= a.n_router_blocks)
     g1_prep(a, blockIdx.x - a.n_router_blocks, part);
-    return;
-  }
-  router_tile(a, tile);
+  else
+    router_tile(a, tile);
+  gtrace(a, 0, 3);
 }
 
 // ------------------------------------------------------------------ g2, g3
@@ -1025,6 +1035,7 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
   // take items in grid stride; a workgroup derives the routing (every one the
   // same; the one that meets the first routed item first publishes it) when it
   // meets its first routed item, so the shared expert's items stream at once.
+  gtrace(a, 1, 0);
   const int sh_items = sh ? (a.B + kTokBlock - 1) / kTokBlock * ngi : 0;
   const int max_items = sh_items + S * ngi;
   const bool writer = (int)blockIdx.x == sh_items % (int)gridDim.x;
@@ -1071,6 +1082,7 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
   // once the routing is derived
   typename MR::XAhead ahead;
   bool have = false;
+  int done = 0;  // items finished (for the trace)
   for (int item = blockIdx.x; item < max_items; item += gridDim.x) {
     GroupItem it;
     int gi;
@@ -1087,6 +1099,7 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
           NB = block_route(a, *reinterpret_cast<RouteLds1 *>(&wlds[0][0]), slotl, blk, writer);
         else
           NB = block_route(a, *reinterpret_cast<RouteLds *>(xl), slotl, blk, writer);
+        gtrace(a, 1, 1);
       }
       const int kb = (item - sh_items) / ngi;
       if (kb >= NB) break;  // (uniform) later items are past the last block
@@ -1189,7 +1202,10 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
       const float amax = __int_as_float(mb);
       reinterpret_cast<float2 *>(a.hsum)[(size_t)hv_thr * ngi + gi] = make_float2(group_factor(amax, group_shift(amax)), sum);
     }
+    if (done < 5) gtrace(a, 1, 2 + done);
+    ++done;
   }
+  gtrace(a, 1, 7);
 }
 
 // g3: down of 128 TILES rows (part rb: TILES tiles of 128, each wavefront 16
@@ -1229,6 +1245,7 @@ __global__ __launch_bounds__(kGThreads) void k_g3(const GroupArgs a) {
     it.q0 = 2 + kBlkInts * kb + 2;
     if (kb >= nb) return;  // uniform over the workgroup
   }
+  gtrace(a, 2, 0);
   const int T = it.n;
   const int lane = lane_id(), wv = wave_in_block();
   const int n = lane & 15, qq = lane >> 4;
@@ -1253,6 +1270,7 @@ __global__ __launch_bounds__(kGThreads) void k_g3(const GroupArgs a) {
     if (qq < T) outp[(size_t)oidx[qq] * a.H + row0 + 128 * tile + n] = osc * M.y;
   };
   M.template run<false>(ngi, rec0, (size_t)128 * RB, a.hq, a.hsum, T, tokv, fill, after, done, xl, xsl, wlds[wv]);
+  gtrace(a, 2, 3);
 }
 
 // g4: out[t] = residual[t] + sum_k partial[t*K + k] (k ascending) + d_shared[t];

@@ -79,6 +79,9 @@ struct GroupArgs {
   // [E], entries needed only for the experts the batch chooses)
   const uint8_t *const *expert_ptr;
   int n_router_blocks;       // g1
+  // optional per-workgroup timestamps (device, 100 MHz clock) for profiling, as
+  // LayerArgs::trace: [0] router + token preparation, [1] gate/up, [2] down; null in normal use
+  uint64_t *trace;
 };
 
 // The grouped layer: four launches (router + input preparation; routing,

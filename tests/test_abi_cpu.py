@@ -287,7 +287,7 @@ def test_stack_trace_validation():
     call = lambda n_tokens=1, trace=TR, layer=1, ws_bytes=need, h0=X: L.fmoe_moe_stack_trace(
         arr, 2, n_tokens, h0, OUT, 1e-6, WSL, ws_bytes, trace, layer, None)
     assert call(trace=None) == 1
-    assert call(n_tokens=2) == 6
+    assert call(n_tokens=0) == 6 and call(n_tokens=257) == 6
     assert call(layer=2) == 6 and call(layer=-1) == 6
     assert call(trace=TR + 4) == 3
     assert call(trace=WSL + 256) == 9

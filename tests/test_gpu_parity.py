@@ -322,6 +322,32 @@ def test_stack_trace_equals_stack(device):
         assert rec[kk + 1][:, 0].min() + 50 >= rec[kk][:, 3].max()
 
 
+@pytest.mark.parametrize("B", [4, 16])
+def test_stack_trace_grouped_equals_stack(device, B):
+    """The stamped form of the grouped stack gives fmoe_moe_stack's output bit for bit;
+    every persistent gate/up workgroup's item ends are ordered and lie between its start
+    and end, and the down kernel starts after the gate/up kernel's workgroups end."""
+    hidden, inter, n_exp, k, n_layers, bits = 1024, 256, 32, 4, 3, 4
+    layers = [host_layer(53, l, bits, n_exp, k, hidden, inter, device) for l in range(n_layers)]
+    h0 = to_dev(synth.activations(53, synth.T_H0, 2, B, hidden), device)
+    ref = qem.fmoe_moe_stack(layers, h0)
+    tr = torch.zeros((3, qem.TRACE_BLOCKS, qem.TRACE_SLOTS), dtype=torch.int64, device=device)
+    out = qem.fmoe_moe_stack_trace(layers, h0, tr, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    t = tr.cpu().numpy()
+    rec = [t[kk][t[kk, :, 0] > 0] for kk in range(3)]
+    for kk in (0, 2):
+        assert len(rec[kk]) > 0 and (rec[kk][:, 3] >= rec[kk][:, 0]).all()
+    g2 = rec[1]
+    assert len(g2) > 0 and (g2[:, 7] >= g2[:, 0]).all()
+    for row in g2:
+        ends = [v for v in row[2:7] if v > 0]
+        assert ends == sorted(ends) and all(row[0] <= v <= row[7] for v in ends)
+    assert (g2[:, 1] > 0).any()  # workgroups that derived the routing
+    assert rec[2][:, 0].min() + 50 >= g2[:, 7].max()
+
+
 def test_read_xor(device):
     """The streaming-read measurement kernel: the XOR of a buffer's 32-bit words (several
     grid-stride rounds and a ragged tail) equals numpy's; calls accumulate; an empty call
