@@ -39,10 +39,10 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "moe_layer_q4_B1_hbm_counters.txt
 PHASE_NAMES = {1: "router + shared gate (k_phase1)", 2: "routing + routed and shared gate/up (k_phase2)",
                4: "routed and shared down + combine (k_phase3)"}
 # the grouped layer's launches per phase (B > 1): the router and token preparation;
-# the gate/up of the distinct experts (above 64 tokens after the routing kernels);
+# the gate/up of the distinct experts (above 8 tokens after the routing kernels);
 # the down projections and the combine
 GROUP_PHASE_NAMES = {1: "router + token preparation (k_g1 / k_g1t)",
-                     2: "gate/up of the distinct routed and shared experts (k_g2; k_topk + k_group above 64 tokens)",
+                     2: "gate/up of the distinct routed and shared experts (k_g2; k_topk + k_group above 8 tokens)",
                      4: "down projections + combine (k_g3 + k_g4)"}
 
 
@@ -336,7 +336,7 @@ def timeline_grouped(np, rec, us, q):
     print(f"  {names[2]:28s} {len(r):4d} wg  start {q(r[:, 0])}  end {q(r[:, 3])}", flush=True)
     gaps = [us(rec[k + 1][:, 0].min()) - us(rec[k][:, 3 if k == 0 else 7].max()) for k in range(2)]
     print(f"  last end -> next kernel's first start: router -> gate/up {gaps[0]:.2f} (routing kernels "
-          f"between them above 64 tokens), gate/up -> down {gaps[1]:.2f}; first start -> last down end "
+          f"between them above 8 tokens), gate/up -> down {gaps[1]:.2f}; first start -> last down end "
           f"{us(rec[2][:, 3].max()):.2f} (the combine follows)", flush=True)
 
 
@@ -494,10 +494,10 @@ def versions(torch):
 
 def kernels_per_layer(B, K):
     """Launches of one layer: 3 for one token; grouped, 4, or 6 with the routing kernels
-    (more than 64 tokens or 512 (token, choice) slots)."""
+    (more than 8 tokens or 512 (token, choice) slots)."""
     if B == 1:
         return 3
-    return 6 if (B > 64 or B * K > 512) else 4
+    return 6 if (B > 8 or B * K > 512) else 4
 
 
 def group_phase_bytes(phase, d_routed, eb, gub, E, H, I, K, B):

@@ -50,8 +50,14 @@ namespace dev {
 // Slots (token, choice) that the gate/up kernel's own routing handles (one thread
 // per slot): batches with more, or with more than kRouteTokens tokens, are routed
 // by the routing kernels before it (k_topk, k_group) and read the grouping table.
+// Every gate/up workgroup that routes for itself reads all the batch's logits
+// (B x the router's slabs x 2 KB): from 16 tokens that traffic, and the top-Ks
+// of two tokens per wavefront, cost more than the two extra launches (same-build
+// layer times on the 60-layer q4 stack, in-kernel against routing kernels: 8
+// tokens 69.5 / 70.9 us, 16 tokens 100.2 / 95.6, 32 tokens 156.3 / 144.6, 64
+// tokens 261.5 / 232.8).
 constexpr int kRouteSlots = 512;
-constexpr int kRouteTokens = 64;
+constexpr int kRouteTokens = 8;
 // Tokens per work item: one MFMA row block (4 rows each: hi, mid, lo, 0). An
 // expert used by more tokens (the shared expert, mostly) gives several items,
 // which run on different compute units and re-read its rows (from the caches).

@@ -78,7 +78,7 @@ def test_topk10_full_size(device, bits):
 
 @pytest.mark.parametrize("B,k", [(65, 4), (128, 4), (256, 4), (64, 10), (200, 16)])
 def test_large_batch_small_layer(device, B, k):
-    """Batches past the gate/up kernel's own routing (more than 64 tokens or 512 slots):
+    """Batches past the gate/up kernel's own routing (more than 8 tokens or 512 slots):
     the routing kernels' top-K and grouping, then the grouped kernels, every token."""
     hidden, inter, n_exp, bits = 1024, 512, 64, 4
     print(f"large batch B={B} k={k}", flush=True)

@@ -369,27 +369,38 @@ def test_read_xor(device):
 
 # --------------------------------------------------------------------------- grouped (B > 1)
 
-@pytest.mark.parametrize("bits", [4, 2])
-def test_grouped_layer_forced_collisions(device, bits):
-    """16 tokens in 4 groups of identical x (so every chosen expert serves several tokens and the
-    staging chunks of the grouped kernels loop), on 8 experts; each token against the oracle."""
-    hidden, inter, n_exp, k, B = 1024, 512, 8, 4, 16
+@pytest.mark.parametrize("bits,B", [(4, 16), (2, 16), (4, 8)])
+def test_grouped_layer_forced_collisions(device, bits, B):
+    """B tokens in 4 groups of identical x (so every chosen expert serves several tokens and the
+    staging chunks of the grouped kernels loop), on 8 experts; each token against the oracle
+    (8 tokens: routed inside the gate/up kernel; 16: by the routing kernels)."""
+    hidden, inter, n_exp, k = 1024, 512, 8, 4
     L = host_layer(61, 0, bits, n_exp, k, hidden, inter, device)
     OL = OracleLayer(61, 0, bits, n_exp, k, hidden, inter)
     base = _x(61, 7, hidden, 4)
     X = np.ascontiguousarray(base[np.arange(B) % 4])
     RES = synth.activations(61, synth.T_RESIDUAL, 7, B, hidden)
-    assert _check_layer(device, OL, L, X, RES, f"collisions q{bits}") == 0
+    assert _check_layer(device, OL, L, X, RES, f"collisions q{bits} B={B}") == 0
 
 
 def test_grouped_layer_max_slots(device):
-    """The largest batch (64 tokens) with top-8 of 16 experts: 512 slots, every expert shared by
-    many tokens; inter 4096 (the smallest staging chunk)."""
+    """64 tokens with top-8 of 16 experts: 512 slots, every expert shared by many tokens;
+    inter 4096 (the smallest staging chunk)."""
     hidden, inter, n_exp, k, B = 256, 4096, 16, 8, 64
     L = host_layer(62, 0, 4, n_exp, k, hidden, inter, device)
     OL = OracleLayer(62, 0, 4, n_exp, k, hidden, inter)
     X = _x(62, 3, hidden, B)
     assert _check_layer(device, OL, L, X, X, "max slots") == 0
+
+
+def test_grouped_layer_in_kernel_routing_max(device):
+    """The largest batch the gate/up kernel routes for itself: 8 tokens with top-16 of 32
+    experts (128 slots, each expert chosen by several tokens), every token against the oracle."""
+    hidden, inter, n_exp, k, B = 1024, 256, 32, 16, 8
+    L = host_layer(64, 0, 4, n_exp, k, hidden, inter, device)
+    OL = OracleLayer(64, 0, 4, n_exp, k, hidden, inter)
+    X = _x(64, 5, hidden, B)
+    assert _check_layer(device, OL, L, X, X, "in-kernel routing, 128 slots") == 0
 
 
 def test_grouped_equals_one_token_routing(device):
