@@ -164,7 +164,12 @@ struct MfmaRows {
   static constexpr int CG = NGP < 8 ? NGP : 8;        // groups per chunk
   static constexpr int NC = NGP / CG;                 // chunks per row
   static constexpr int NCT = NTILE * NC;              // chunks of the whole stream
-  static constexpr int DEPTH = NCT < 4 ? NCT : 4;     // chunks in flight
+  // chunks in flight per wavefront: one (the next chunk is requested as the
+  // current one is taken). A chunk is 16 rows x CG groups in 128-byte pieces of 16
+  // records; with more of them outstanding the stream got slower, not faster
+  // (60-layer q4 stack, per layer: 4 tokens 47.1 / 44.7 / 43.9 us with 4 / 2 / 1
+  // chunks in flight, 16 tokens 95.9 / 91.2 / 88.9 us; 8 chunks 50.0 / 100.6 us)
+  static constexpr int DEPTH = 1;
   static constexpr int HALVES = BITS == 4 ? 2 : 1;    // 16-byte code units per group
   static constexpr int NI = 16 * HALVES * CG / kWave; // 16-byte code loads per lane per chunk
   static constexpr int SBW = CG / 4;                  // scale/bias words per lane per chunk
