@@ -494,10 +494,10 @@ def versions(torch):
 
 def kernels_per_layer(B, K):
     """Launches of one layer: 3 for one token; grouped, 4, or 6 with the routing kernels
-    (more than 8 tokens or 512 (token, choice) slots)."""
+    (more than 8 tokens)."""
     if B == 1:
         return 3
-    return 6 if (B > 8 or B * K > 512) else 4
+    return 6 if B > 8 else 4
 
 
 def group_phase_bytes(phase, d_routed, eb, gub, E, H, I, K, B):

@@ -56,8 +56,8 @@ namespace dev {
 // layer times on the 60-layer q4 stack, in-kernel against routing kernels: 8
 // tokens 69.5 / 70.9 us, 16 tokens 100.2 / 95.6, 32 tokens 156.3 / 144.6, 64
 // tokens 261.5 / 232.8).
-constexpr int kRouteSlots = 512;
 constexpr int kRouteTokens = 8;
+constexpr int kRouteSlots = kRouteTokens * kMaxTopK;  // 128: every batch of at most kRouteTokens tokens
 // Tokens per work item: one MFMA row block (4 rows each: hi, mid, lo, 0). An
 // expert used by more tokens (the shared expert, mostly) gives several items,
 // which run on different compute units and re-read its rows (from the caches).
@@ -66,7 +66,10 @@ constexpr int kParts = 3;       // signed 8-bit digit planes of a value's intege
 constexpr int kGThreads = 512;  // workgroup of the matrix-core kernels: 8 wavefronts
 constexpr int kGWaves = kGThreads / kWave;
 constexpr int kMaxNG = 64;      // groups per row (4096 columns)
-constexpr int kWaveLds = 16 * (2 * 8 * 16 + 16) + 16 * 9 * 4;  // LDS bytes per wavefront for a weight chunk
+// groups per weight chunk (16 rows x 8 groups; 16 groups a chunk measured slower:
+// 4 tokens 46.4 against 42.7 us per layer, 16 tokens 95.2 against 89.0)
+constexpr int kChunkGroups = 8;
+constexpr int kWaveLds = 16 * (2 * kChunkGroups * 16 + 16) + 16 * (kChunkGroups + 1) * 4;  // LDS bytes per wavefront for a weight chunk
 
 typedef __attribute__((ext_vector_type(4))) int i32x4_t;
 
@@ -161,7 +164,7 @@ __device__ __forceinline__ i32x4_t mfma_codes(const MCodes &m) {
 // (the group count is then a compile-time constant).
 template <int BITS, int NGP, int NTILE = 1, bool FULL = true>
 struct MfmaRows {
-  static constexpr int CG = NGP < 8 ? NGP : 8;        // groups per chunk
+  static constexpr int CG = NGP < kChunkGroups ? NGP : kChunkGroups;        // groups per chunk
   static constexpr int NC = NGP / CG;                 // chunks per row
   static constexpr int NCT = NTILE * NC;              // chunks of the whole stream
   // chunks in flight per wavefront: one (the next chunk is requested as the
@@ -723,7 +726,7 @@ struct RouteLdsT {
   int wtot[kGWaves];
   TopkLds tk[kGWaves];                       // each wavefront's top-K scratch
 };
-using RouteLds = RouteLdsT<kGWaves>;  // every routed-in-kernel batch (kRouteSlots slots)
+using RouteLds = RouteLdsT<kRouteSlots / kWave>;  // every routed-in-kernel batch (kRouteSlots slots)
 using RouteLds1 = RouteLdsT<1>;       // at most 64 slots
 
 // Top-K of every token and the grouping of the S = B*K slots by expert, by one
