@@ -70,8 +70,8 @@ def parse():
     p.add_argument("--no-verify", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true")
     p.add_argument("--forms", action="store_true",
-                   help="time the standalone 1024 x 4096 matvec in each form of the per-weight dequant arithmetic "
-                        "(q4 and q2) instead of the stack")
+                   help="time the standalone matvec (1024 and 16384 x 4096) and the whole 4096/1024 SwiGLU "
+                        "expert in each form of the per-weight dequant arithmetic (q4 and q2) instead of the stack")
     p.add_argument("--tier-slots", type=str, default=None,
                    help="time the host-memory expert tier instead of the resident stack: comma-separated HBM cache "
                         "sizes in expert slots ('pages' = the pages' page-cache share of the bank, 35 of 209 GB); "
@@ -347,10 +347,12 @@ FORM_NAMES = {0: "naive (c*s+b)*x", 1: "recast fma(c, s*x, b*x)", 2: "group-fact
 def forms(a):
     """The standalone dequantized matvec W [rows][4096] (rows 1024, and 16384 where the
     per-weight arithmetic weighs more than the launch) in each form of the per-weight
-    arithmetic (fmoe_qmatvec_form) and the library's own call, q4 and q2: a graph of one
-    launch per copy over enough independent copies of W and x (≥ 450 MB) that they
-    exceed the 256 MB Infinity Cache, replayed 5 times. Each form's output of copy 0 is compared with
-    the library call's (the tests check every form against the oracle)."""
+    arithmetic (fmoe_qmatvec_form) and the library's own call, q4 and q2; then the whole
+    SwiGLU expert (hidden 4096, inter 1024: fmoe_expert_ffn against fmoe_expert_ffn_form
+    in each form). Each is a graph of one call per copy over enough independent copies of
+    the weights and x (≥ 450 MB) that they exceed the 256 MB Infinity Cache, replayed 5
+    times. Each form's output of copy 0 is compared with the library call's (the tests
+    check every form against the oracle)."""
     import numpy as np
     import torch
 
@@ -416,6 +418,63 @@ def forms(a):
             print(json.dumps(recs[-1]), flush=True)
             del g
         del bank, xs, ys
+    # the whole SwiGLU expert (hidden 4096, inter 1024) in each form: the library's
+    # fmoe_expert_ffn and fmoe_expert_ffn_form(0..3), a graph of one call per copy
+    H, I = cols, 1024
+    filler = Filler(torch, synth, qem, H, I, dev)
+    for bits in (4, 2):
+        eb = qem.fmoe_expert_bytes(bits, H, I)
+        copies = max(8, -(-(450 << 20) // eb))
+        bank = torch.empty(copies * eb, dtype=torch.uint8, device=dev)
+        for k in range(copies):
+            filler.expert(a.seed, synth.STANDALONE_LAYER, k, bits, bank[k * eb:(k + 1) * eb])
+        xs = torch.from_numpy(np.stack([synth.activations(a.seed, synth.T_X, k, 1, H)[0]
+                                        for k in range(copies)])).to(dev)
+        ys = torch.empty((copies, H), dtype=torch.float32, device=dev)
+        Es = [qem.Expert(bank[k * eb:(k + 1) * eb], H, I, bits) for k in range(copies)]
+        ce = [E.c() for E in Es]
+        need = qem.fmoe_expert_workspace_bytes(Es[0])
+        ws = torch.empty((copies, (need + 255) // 256 * 256), dtype=torch.uint8, device=dev)
+        ref = None
+        for form, name in [(None, "library call fmoe_expert_ffn")] + [(f, FORM_NAMES[f]) for f in range(4)]:
+            def call():
+                stn = torch.cuda.current_stream().cuda_stream
+                for k in range(copies):
+                    if form is None:
+                        qem.lib().fmoe_expert_ffn(ce[k], xs[k].data_ptr(), ys[k].data_ptr(), ws[k].data_ptr(),
+                                                  ws.shape[1], stn)
+                    else:
+                        qem.lib().fmoe_expert_ffn_form(ce[k], xs[k].data_ptr(), ys[k].data_ptr(), ws[k].data_ptr(),
+                                                       ws.shape[1], form, stn)
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                call()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            y0 = ys[0].cpu().numpy().astype(np.float64)
+            if ref is None:
+                ref = y0
+            max_rel = float(np.max(np.abs(y0 - ref)) / np.max(np.abs(ref)))
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                call()
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(5):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1000.0 / (5 * copies)
+            algo = eb + 2 * H * 4 + I * 4 * 2
+            recs.append({"expert": f"{H}/{I}", "bits": bits, "form": form, "name": name,
+                         "us_per_expert": round(us, 3), "GBps": round(algo / (us * 1e3), 1),
+                         "algorithmic_bytes": algo, "copies": copies, "max_rel_vs_library_call": max_rel})
+            print(json.dumps(recs[-1]), flush=True)
+            del g
+        del bank, xs, ys, ws
 
 
 def read_ceiling(torch, qem, dev):

@@ -192,6 +192,14 @@ fmoe_status fmoe_qmatvec_form(const fmoe_qmat *W, const float *x, float *y, int 
 fmoe_status fmoe_expert_ffn(const fmoe_expert *E, const float *x, float *out, void *ws, size_t ws_bytes,
                             void *stream);
 
+/* Comparison aid: fmoe_expert_ffn with the per-weight arithmetic of every projection in
+ * form `form` (0 naive, 1 fma recast, 2 group-factored, 3 table in LDS; as
+ * fmoe_qmatvec_form): the fused gate/up + SwiGLU kernel, then the down projection as
+ * fmoe_qmatvec_form does it. Results agree with fmoe_expert_ffn up to fp32 rounding.
+ * Arguments and errors as fmoe_expert_ffn; FMOE_ERR_SHAPE if form is outside 0..3. */
+fmoe_status fmoe_expert_ffn_form(const fmoe_expert *E, const float *x, float *out, void *ws, size_t ws_bytes,
+                                 int form, void *stream);
+
 /* One MoE layer for n_tokens independent tokens t:
  *   logits = router x_t; p = softmax(logits); T = the top_k experts by p (descending,
  *   lower index first on a tie); w_j = p[T_j] / sum_{i in T} p[i];

@@ -78,6 +78,8 @@ _SIGS = {
                                          ctypes.c_int, ctypes.c_void_p]),
     "fmoe_expert_ffn": (ctypes.c_int, [ctypes.POINTER(fmoe_expert), ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "fmoe_expert_ffn_form": (ctypes.c_int, [ctypes.POINTER(fmoe_expert), ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]),
     "fmoe_moe_layer": (ctypes.c_int, [ctypes.POINTER(fmoe_layer), ctypes.c_int] + [ctypes.c_void_p] * 6 +
                        [ctypes.c_size_t, ctypes.c_void_p]),
     "fmoe_moe_layer_phases": (ctypes.c_int, [ctypes.POINTER(fmoe_layer), ctypes.c_int] + [ctypes.c_void_p] * 6 +
@@ -342,6 +344,23 @@ def fmoe_expert_ffn(E: Expert, x: torch.Tensor, out: Optional[torch.Tensor] = No
     nbytes = ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else need
     _ok(lib().fmoe_expert_ffn(ctypes.byref(E.c()), _ptr(x), _ptr(out), _ptr(ws), nbytes, _stream(stream)),
         "fmoe_expert_ffn")
+    return out
+
+
+def fmoe_expert_ffn_form(E: Expert, x: torch.Tensor, form: int, out: Optional[torch.Tensor] = None, ws=None,
+                         stream=None, c_expert=None) -> torch.Tensor:
+    """fmoe_expert_ffn with the per-weight arithmetic of every projection in form 0 (naive),
+    1 (fma recast), 2 (group-factored) or 3 (table in LDS)."""
+    _dev_f32(x, "x")
+    if out is None:
+        out = torch.empty(E.hidden, dtype=torch.float32, device=x.device)
+    need = fmoe_expert_workspace_bytes(E)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    nbytes = ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else need
+    ce = c_expert if c_expert is not None else E.c()
+    _ok(lib().fmoe_expert_ffn_form(ctypes.byref(ce), _ptr(x), _ptr(out), _ptr(ws), nbytes, form, _stream(stream)),
+        "fmoe_expert_ffn_form")
     return out
 
 

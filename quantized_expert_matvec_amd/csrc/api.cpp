@@ -312,6 +312,29 @@ fmoe_status fmoe_expert_ffn(const fmoe_expert *E, const float *x, float *out, vo
   return FMOE_OK;
 }
 
+fmoe_status fmoe_expert_ffn_form(const fmoe_expert *E, const float *x, float *out, void *ws, size_t ws_bytes, int form,
+                                 void *stream) {
+  if (!E || !E->blob || !x || !out) return FMOE_ERR_NULL;
+  if (form < 0 || form >= kForms) return FMOE_ERR_SHAPE;
+  fmoe_status st = check_expert_shape(E->bits, E->hidden, E->inter, E->group);
+  if (st != FMOE_OK) return st;
+  if (!al256(E->blob) || !al16(x) || !al16(out)) return FMOE_ERR_ALIGN;
+  const size_t need = fmoe_expert_workspace_bytes(E);
+  if (!ws || ws_bytes < need) return FMOE_ERR_WORKSPACE;
+  if (!al256(ws)) return FMOE_ERR_ALIGN;
+  const size_t xb = sizeof(float) * (size_t)E->hidden;
+  if (overlap(x, xb, out, xb) || overlap(out, xb, ws, need) || overlap(x, xb, ws, need)) return FMOE_ERR_ALIAS;
+  const uint8_t *blob = (const uint8_t *)E->blob;
+  hipStream_t s = as_stream(stream);
+  float *h = (float *)ws;
+  if (launch_expert_gateup_form(E->bits, form, blob, E->hidden, E->inter, x, h, s) != hipSuccess)
+    return FMOE_ERR_LAUNCH;
+  if (launch_qmatvec_form(E->bits, form, blob + gateup_bytes(E->bits, E->hidden, E->inter), E->hidden, E->inter, h, out,
+                          s) != hipSuccess)
+    return FMOE_ERR_LAUNCH;
+  return FMOE_OK;
+}
+
 fmoe_status fmoe_moe_layer(const fmoe_layer *L, int n_tokens, const float *x, const float *residual, float *out,
                            int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes, void *stream) {
   return fmoe_moe_layer_phases(L, n_tokens, x, residual, out, topk_idx, topk_w, ws, ws_bytes, 7, stream);

@@ -1,5 +1,5 @@
-// forms.h -- launcher of the standalone dequantized matvec in four forms of the
-// per-weight arithmetic (kernels_forms.hip).
+// forms.h -- launchers of the standalone dequantized matvec and of an expert's fused
+// gate/up + SwiGLU in four forms of the per-weight arithmetic (kernels_forms.hip).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -10,5 +10,9 @@ namespace fmoe {
 constexpr int kForms = 4;
 hipError_t launch_qmatvec_form(int bits, int form, const uint8_t *blob, int rows, int cols, const float *x, float *y,
                                hipStream_t s);
+// h[r] = silu(gate_r . x) * (up_r . x) for one expert's interleaved gate/up region, in
+// the same four forms
+hipError_t launch_expert_gateup_form(int bits, int form, const uint8_t *gu, int hidden, int inter, const float *x,
+                                     float *h, hipStream_t s);
 
 }  // namespace fmoe

@@ -17,7 +17,9 @@
 // One row per 64 / NGP lanes (NGP: the groups per row rounded up to a power of
 // two), a lane per group, and 1, 2 or 4 row iterations per
 // wavefront chosen by the matrix height, as in the library's matvec (form 2 is
-// that kernel); x staged once per workgroup.
+// that kernel); x staged once per workgroup. The expert's fused gate/up + SwiGLU
+// kernel comes in the same four forms, so that a whole expert (gate/up, then the
+// down projection as a matvec) can run in each.
 #include "forms.h"
 #include "layer_kernels.h"
 
@@ -100,6 +102,60 @@ __global__ __launch_bounds__(kBlock) void k_qmatvec_form(const uint8_t *__restri
   }
 }
 
+// The expert's fused gate/up + SwiGLU (h[r] = silu(gate_r . x) * (up_r . x)) with the
+// per-weight arithmetic in form FORM: the library's gate/up kernel for one expert with
+// its partial sums replaced (form 2 is that kernel's arithmetic).
+template <int BITS, int NGP, int FORM>
+__global__ __launch_bounds__(kBlock) void k_expert_gateup_form(const uint8_t *__restrict__ gu, int ng, int inter,
+                                                                const float *__restrict__ x, float *__restrict__ h) {
+  constexpr int RPI = kWave / NGP;
+  __shared__ float xl[NGP * kXPad];
+  __shared__ float lut[FORM == 3 ? kBlock * kLutStride : 1];
+  constexpr int X4 = (NGP * 16 + kBlock - 1) / kBlock;
+  const int lane = lane_id();
+  const int pair0 = wave_id() * RPI;
+  Staged<X4> xst;
+  stage_load(x, ng * 16, xst);
+  PairLoads<BITS, NGP, 1> P;
+  if (pair0 < inter) P.issue(gu, ng, pair0);
+  __builtin_amdgcn_sched_barrier(0);
+  stage_store<X4, false>(xst, ng * 16, xl, nullptr);
+  __syncthreads();
+  if (pair0 >= inter) return;
+  XSlice xs;
+  read_slice(xl, min(lane & (NGP - 1), ng - 1), 1.f, xs);
+  float *tab = FORM == 3 ? lut + threadIdx.x * kLutStride : lut;
+  const float pg = seg_reduce<NGP>(P.live ? partial_form<BITS, FORM>(P.cg[0], P.sg[0], xs, tab) : 0.f);
+  const float pu = seg_reduce<NGP>(P.live ? partial_form<BITS, FORM>(P.cu[0], P.su[0], xs, tab) : 0.f);
+  if (seg_last<NGP>(lane)) h[pair0 + lane / NGP] = silu(pg) * pu;
+}
+
+template <int BITS, int NGP>
+hipError_t launch_gateup(int form, const uint8_t *gu, int ng, int inter, const float *x, float *h, hipStream_t s) {
+  const dim3 grid(blocks_for(inter / (kWave / NGP))), block(kBlock);
+  switch (form) {
+    case 0: hipLaunchKernelGGL((k_expert_gateup_form<BITS, NGP, 0>), grid, block, 0, s, gu, ng, inter, x, h); break;
+    case 1: hipLaunchKernelGGL((k_expert_gateup_form<BITS, NGP, 1>), grid, block, 0, s, gu, ng, inter, x, h); break;
+    case 2: hipLaunchKernelGGL((k_expert_gateup_form<BITS, NGP, 2>), grid, block, 0, s, gu, ng, inter, x, h); break;
+    default: hipLaunchKernelGGL((k_expert_gateup_form<BITS, NGP, 3>), grid, block, 0, s, gu, ng, inter, x, h); break;
+  }
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_gateup_bits(int form, const uint8_t *gu, int hidden, int inter, const float *x, float *h,
+                              hipStream_t s) {
+  const int ng = hidden / kGroup;
+  switch (pad_groups(ng)) {
+    case 4: return launch_gateup<BITS, 4>(form, gu, ng, inter, x, h, s);
+    case 8: return launch_gateup<BITS, 8>(form, gu, ng, inter, x, h, s);
+    case 16: return launch_gateup<BITS, 16>(form, gu, ng, inter, x, h, s);
+    case 32: return launch_gateup<BITS, 32>(form, gu, ng, inter, x, h, s);
+    case 64: return launch_gateup<BITS, 64>(form, gu, ng, inter, x, h, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int BITS, int NGP, int ITERS>
 hipError_t launch_it(int form, const uint8_t *blob, int ng, int rows, const float *x, float *y, hipStream_t s) {
   const long iters = (rows + kWave / NGP - 1) / (kWave / NGP);
@@ -143,6 +199,12 @@ hipError_t launch_qmatvec_form(int bits, int form, const uint8_t *blob, int rows
                                hipStream_t s) {
   return bits == 4 ? dev::launch_bits<4>(form, blob, rows, cols, x, y, s)
                    : dev::launch_bits<2>(form, blob, rows, cols, x, y, s);
+}
+
+hipError_t launch_expert_gateup_form(int bits, int form, const uint8_t *gu, int hidden, int inter, const float *x,
+                                     float *h, hipStream_t s) {
+  return bits == 4 ? dev::launch_gateup_bits<4>(form, gu, hidden, inter, x, h, s)
+                   : dev::launch_gateup_bits<2>(form, gu, hidden, inter, x, h, s);
 }
 
 }  // namespace fmoe

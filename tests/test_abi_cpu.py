@@ -198,6 +198,18 @@ def test_expert_validation():
     assert L.fmoe_expert_ffn(ex(), B, C, WS + 16, need, None) == 3
 
 
+def test_expert_form_validation():
+    need = L.fmoe_expert_workspace_bytes(ex())
+    call = lambda form=0, e=None, x=B, out=C, ws=WS, nb=need: L.fmoe_expert_ffn_form(e or ex(), x, out, ws, nb, form, None)
+    assert call(form=-1) == 2 and call(form=4) == 2
+    assert call(x=None) == 1 and call(out=None) == 1
+    assert call(nb=need - 1) == 7 and call(ws=None) == 7
+    assert call(e=ex(bits=3)) == 4
+    assert call(e=ex(inter=100)) == 2
+    assert call(out=B) == 9
+    assert call(ws=WS + 16) == 3
+
+
 def lay(**kw):
     d = dict(router=A, shared_gate=B, bank=C, shared=WS + (1 << 29), n_experts=512, top_k=4, hidden=4096,
              inter=1024, bits=4, group=64)

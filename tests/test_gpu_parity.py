@@ -108,6 +108,21 @@ def test_expert_ffn_vs_oracle(device, bits, hidden, inter):
     assert_close(out.cpu().numpy(), ref, f"expert q{bits} {hidden}/{inter}")
 
 
+@pytest.mark.parametrize("form", [0, 1, 2, 3])
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("hidden,inter", [(4096, 1024), (512, 256)])
+def test_expert_ffn_forms_vs_oracle(device, form, bits, hidden, inter):
+    """The whole expert with the per-weight arithmetic in each form (naive, fma recast,
+    group-factored, table) against the oracle's dequantize-then-multiply expert."""
+    e = synth.expert(synth.SEED, synth.STANDALONE_LAYER, hidden + inter + 1, bits, hidden, inter)
+    E = host_expert(bits, e, device)
+    x = _x(synth.SEED, 8, hidden)[0]
+    out = qem.fmoe_expert_ffn_form(E, to_dev(x, device), form)
+    torch.cuda.synchronize()
+    _, ref = oracle.expert(e, x)
+    assert_close(out.cpu().numpy(), ref, f"expert form {form} q{bits} {hidden}/{inter}")
+
+
 # --------------------------------------------------------------------------- layer
 
 def _check_layer(device, OL, L, X, RES, what, in_place=False):
