@@ -349,10 +349,11 @@ def forms(a):
     per-weight arithmetic weighs more than the launch) in each form of the per-weight
     arithmetic (fmoe_qmatvec_form) and the library's own call, q4 and q2; then the whole
     SwiGLU expert (hidden 4096, inter 1024: fmoe_expert_ffn against fmoe_expert_ffn_form
-    in each form). Each is a graph of one call per copy over enough independent copies of
-    the weights and x (≥ 450 MB) that they exceed the 256 MB Infinity Cache, replayed 5
-    times. Each form's output of copy 0 is compared with the library call's (the tests
-    check every form against the oracle)."""
+    in each form); then the one-token MoE layer (fmoe_moe_layer against
+    fmoe_moe_layer_form). Each is a graph of one call per copy (per layer) over enough
+    independent copies of the weights and x that they exceed the 256 MB Infinity Cache.
+    Each form's output of copy 0 is compared with the library call's (the tests check
+    every form against the oracle)."""
     import numpy as np
     import torch
 
@@ -475,6 +476,68 @@ def forms(a):
             print(json.dumps(recs[-1]), flush=True)
             del g
         del bank, xs, ys, ws
+    # the one-token MoE layer (512 experts + shared, hidden 4096, inter 1024, top-4) with
+    # every expert projection in each form: fmoe_moe_layer against fmoe_moe_layer_form,
+    # a graph of one call per layer over 8 layers (350 MB of chosen weights at q4)
+    E, K, NL = 512, 4, 8
+    for bits in (4, 2):
+        eb = qem.fmoe_expert_bytes(bits, H, I)
+        keep, layers = [], []
+        for l in range(NL):
+            bank = torch.empty((E + 1) * eb, dtype=torch.uint8, device=dev)
+            for e in range(E):
+                filler.expert(a.seed, 200 + l, e, bits, bank[e * eb:(e + 1) * eb])
+            filler.expert(a.seed, 200 + l, synth.SHARED_EXPERT, bits, bank[E * eb:])
+            R = torch.from_numpy(synth.router(a.seed, 200 + l, E, H)).to(dev)
+            gv = torch.from_numpy(synth.shared_gate(a.seed, 200 + l, H)).to(dev)
+            keep.append((bank, R, gv))
+            layers.append(qem.Layer(R, gv, bank[:E * eb], bank[E * eb:], E, K, H, I, bits))
+        cl = [L.c() for L in layers]
+        x = torch.from_numpy(synth.activations(a.seed, synth.T_X, 77, 1, H)).to(dev)
+        res = torch.from_numpy(synth.activations(a.seed, synth.T_RESIDUAL, 77, 1, H)).to(dev)
+        outs = torch.empty((NL, 1, H), dtype=torch.float32, device=dev)
+        need = qem.fmoe_workspace_bytes(layers[0], 1)
+        ws = torch.empty((NL, (need + 255) // 256 * 256), dtype=torch.uint8, device=dev)
+        ref = None
+        for form, name in [(None, "library call fmoe_moe_layer")] + [(f, FORM_NAMES[f]) for f in range(4)]:
+            def call():
+                stn = torch.cuda.current_stream().cuda_stream
+                for l in range(NL):
+                    if form is None:
+                        qem.lib().fmoe_moe_layer(cl[l], 1, x.data_ptr(), res.data_ptr(), outs[l].data_ptr(), None,
+                                                 None, ws[l].data_ptr(), ws.shape[1], stn)
+                    else:
+                        qem.lib().fmoe_moe_layer_form(cl[l], x.data_ptr(), res.data_ptr(), outs[l].data_ptr(), None,
+                                                      None, ws[l].data_ptr(), ws.shape[1], form, stn)
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                call()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            y0 = (outs[0] - res).cpu().numpy().astype(np.float64)
+            if ref is None:
+                ref = y0
+            max_rel = float(np.max(np.abs(y0 - ref)) / np.max(np.abs(ref)))
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                call()
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1000.0 / (10 * NL)
+            algo = (K + 1) * eb + E * H * 4 + H * 4
+            recs.append({"layer": f"{E}+1 experts, {H}/{I}, top-{K}", "bits": bits, "form": form, "name": name,
+                         "us_per_layer": round(us, 3), "GBps": round(algo / (us * 1e3), 1),
+                         "algorithmic_bytes": algo, "layers": NL, "max_rel_vs_library_call": max_rel})
+            print(json.dumps(recs[-1]), flush=True)
+            del g
+        del keep, layers, outs, ws
 
 
 def read_ceiling(torch, qem, dev):

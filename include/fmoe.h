@@ -217,6 +217,19 @@ fmoe_status fmoe_moe_layer(const fmoe_layer *L, int n_tokens, const float *x, co
                            float *out, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
                            void *stream);
 
+/* Comparison aid: fmoe_moe_layer for one token with the per-weight arithmetic of every
+ * expert projection (the routed and shared experts' gate/up and down) in dequant form
+ * `form` (0 naive, 1 fma recast, 2 group-factored, 3 table in LDS; as fmoe_qmatvec_form).
+ * The router, top-K and combine are fmoe_moe_layer's; the gate/up kernel takes x in fp32
+ * instead of the digit form its library build uses ([P1] "2. Kernel de desquantizacion
+ * optimizado con FMA", [P1] "Lo que descartaron"). Results agree with fmoe_moe_layer up
+ * to fp32 rounding. Arguments and errors as fmoe_moe_layer with n_tokens = 1;
+ * FMOE_ERR_SHAPE if form is outside 0..3 or the layer is not hidden 4096, inter 1024 with
+ * at most 512 experts; FMOE_ERR_ROUTING unless top_k == 4. */
+fmoe_status fmoe_moe_layer_form(const fmoe_layer *L, const float *x, const float *residual, float *out,
+                                int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes, int form,
+                                void *stream);
+
 /* Diagnostic form of fmoe_moe_layer for per-kernel timing: enqueues only some of
  * the layer's kernels, in order. One token -- bit 0: router and the shared-expert
  * gate sigma; bit 1: routing + routed and shared-expert gate/up; bit 2: routed and

@@ -80,6 +80,8 @@ _SIGS = {
                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "fmoe_expert_ffn_form": (ctypes.c_int, [ctypes.POINTER(fmoe_expert), ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]),
+    "fmoe_moe_layer_form": (ctypes.c_int, [ctypes.POINTER(fmoe_layer)] + [ctypes.c_void_p] * 6 +
+                            [ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]),
     "fmoe_moe_layer": (ctypes.c_int, [ctypes.POINTER(fmoe_layer), ctypes.c_int] + [ctypes.c_void_p] * 6 +
                        [ctypes.c_size_t, ctypes.c_void_p]),
     "fmoe_moe_layer_phases": (ctypes.c_int, [ctypes.POINTER(fmoe_layer), ctypes.c_int] + [ctypes.c_void_p] * 6 +
@@ -379,6 +381,26 @@ def fmoe_moe_layer(L: Layer, x: torch.Tensor, residual: torch.Tensor, out: Optio
     nbytes = ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else need
     _ok(lib().fmoe_moe_layer(ctypes.byref(L.c()), n_tokens, _ptr(x), _ptr(residual), _ptr(out), _ptr(topk_idx),
                              _ptr(topk_w), _ptr(ws), nbytes, _stream(stream)), "fmoe_moe_layer")
+    return out
+
+
+def fmoe_moe_layer_form(L: Layer, x: torch.Tensor, residual: torch.Tensor, form: int,
+                        out: Optional[torch.Tensor] = None, topk_idx: Optional[torch.Tensor] = None,
+                        topk_w: Optional[torch.Tensor] = None, ws=None, stream=None, c_layer=None) -> torch.Tensor:
+    """fmoe_moe_layer for one token (x, residual: [hidden] or [1, hidden]) with the expert
+    projections' per-weight arithmetic in form 0 (naive), 1 (fma recast), 2 (group-factored)
+    or 3 (table in LDS)."""
+    _dev_f32(x, "x")
+    _dev_f32(residual, "residual")
+    if out is None:
+        out = torch.empty_like(residual)
+    need = fmoe_workspace_bytes(L, 1)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    nbytes = ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else need
+    cl = c_layer if c_layer is not None else L.c()
+    _ok(lib().fmoe_moe_layer_form(ctypes.byref(cl), _ptr(x), _ptr(residual), _ptr(out), _ptr(topk_idx),
+                                  _ptr(topk_w), _ptr(ws), nbytes, form, _stream(stream)), "fmoe_moe_layer_form")
     return out
 
 

@@ -119,9 +119,11 @@ GroupArgs group_args(const fmoe_layer *L, int B, const float *x, float rms_eps, 
 // one-token kernels for a single token, the grouped kernels for several.
 // rms_eps >= 0: the layer input is rms_scale(x, rms_eps), computed inside the layer's kernels.
 // trace: device-clock stamps of the layer's kernels (layout in fmoe.h), or null.
+// form >= 0 (one token): the dequant-form build of the layer kernels (launch_layer_form),
+// with x in fp32 in the workspace's d_shared region, which the one-token kernels leave unused.
 fmoe_status layer_enqueue(const fmoe_layer *L, int B, const float *x, float rms_eps, const float *residual,
                           float *out, int32_t *topk_idx, float *topk_w, uint8_t *ws, hipStream_t s,
-                          int phases = 7, uint64_t *trace = nullptr) {
+                          int phases = 7, uint64_t *trace = nullptr, int form = -1) {
   const LayerWs w = layer_ws(B, L->n_experts, L->top_k, L->hidden, L->inter, B > 1);
   const int H = L->hidden, I = L->inter, E = L->n_experts, K = L->top_k;
   if (B > 1) {
@@ -157,6 +159,11 @@ fmoe_status layer_enqueue(const fmoe_layer *L, int B, const float *x, float rms_
     a.d_shared = (float *)(ws + w.d_shared) + (size_t)t * H;
     a.xdig = (uint32_t *)(ws + w.xdig);
     a.trace = trace;
+    if (form >= 0) {
+      a.xs = (float *)(ws + w.d_shared) + (size_t)t * H;
+      if (launch_layer_form(a, form, s) != hipSuccess) return FMOE_ERR_LAUNCH;
+      continue;
+    }
     if (launch_layer(a, s, phases) != hipSuccess) return FMOE_ERR_LAUNCH;
   }
   return FMOE_OK;
@@ -340,10 +347,9 @@ fmoe_status fmoe_moe_layer(const fmoe_layer *L, int n_tokens, const float *x, co
   return fmoe_moe_layer_phases(L, n_tokens, x, residual, out, topk_idx, topk_w, ws, ws_bytes, 7, stream);
 }
 
-fmoe_status fmoe_moe_layer_phases(const fmoe_layer *L, int n_tokens, const float *x, const float *residual,
-                                  float *out, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
-                                  int phases, void *stream) {
-  if (phases < 1 || phases > 7) return FMOE_ERR_BATCH;
+// the checks of fmoe_moe_layer (status FMOE_OK: the call may be enqueued)
+static fmoe_status check_layer_call(const fmoe_layer *L, int n_tokens, const float *x, const float *residual,
+                                    float *out, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes) {
   fmoe_status st = check_layer(L);
   if (st != FMOE_OK) return st;
   if (!x || !residual || !out) return FMOE_ERR_NULL;
@@ -361,8 +367,28 @@ fmoe_status fmoe_moe_layer_phases(const fmoe_layer *L, int n_tokens, const float
       (residual != out && overlap(residual, ab, out, ab)) || overlap(topk_idx, kb, residual, ab) ||
       overlap(topk_w, kb, residual, ab) || overlap(topk_idx, kb, x, ab) || overlap(topk_w, kb, x, ab))
     return FMOE_ERR_ALIAS;
+  return FMOE_OK;
+}
+
+fmoe_status fmoe_moe_layer_phases(const fmoe_layer *L, int n_tokens, const float *x, const float *residual,
+                                  float *out, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+                                  int phases, void *stream) {
+  if (phases < 1 || phases > 7) return FMOE_ERR_BATCH;
+  const fmoe_status st = check_layer_call(L, n_tokens, x, residual, out, topk_idx, topk_w, ws, ws_bytes);
+  if (st != FMOE_OK) return st;
   return layer_enqueue(L, n_tokens, x, -1.f, residual, out, topk_idx, topk_w, (uint8_t *)ws, as_stream(stream),
                        phases);
+}
+
+fmoe_status fmoe_moe_layer_form(const fmoe_layer *L, const float *x, const float *residual, float *out,
+                                int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes, int form, void *stream) {
+  if (form < 0 || form >= kForms) return FMOE_ERR_SHAPE;
+  const fmoe_status st = check_layer_call(L, 1, x, residual, out, topk_idx, topk_w, ws, ws_bytes);
+  if (st != FMOE_OK) return st;
+  if (L->hidden != 4096 || L->inter != 1024 || L->n_experts > 512) return FMOE_ERR_SHAPE;
+  if (L->top_k != 4) return FMOE_ERR_ROUTING;
+  return layer_enqueue(L, 1, x, -1.f, residual, out, topk_idx, topk_w, (uint8_t *)ws, as_stream(stream), 7, nullptr,
+                       form);
 }
 
 fmoe_status fmoe_moe_layer_noalloc(const fmoe_layer *L, int n_tokens, const float *x, const float *residual,

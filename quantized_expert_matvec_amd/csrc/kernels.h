@@ -39,6 +39,7 @@ struct LayerArgs {
   float *h_routed;           // [K][I]
   float *d_shared;           // [H]
   uint32_t *xdig;            // [H/64][kDigStride] x in digit form (router kernel -> gate/up kernel)
+  float *xs;                 // null, or [H]: x in fp32 as well (the dequant-form builds of the gate/up kernel)
   // optional per-workgroup timestamps (device, 100 MHz clock) for profiling:
   // [phase][kTraceBlocks workgroups][kTraceSlots]; null in normal use
   uint64_t *trace;
@@ -100,6 +101,10 @@ hipError_t launch_group_experts(const GroupArgs &a, hipStream_t s);
 // down + weighted combine + residual. Three launches, no host synchronisation.
 // phases: bit p set = enqueue kernel p+1 (7 = the whole layer).
 hipError_t launch_layer(const LayerArgs &a, hipStream_t s, int phases = 7);
+// The same layer (one token, hidden 4096, inter 1024, top_k <= 4, n_experts <= 512) with
+// the per-weight arithmetic of its gate/up and down projections in dequant form `form`
+// (forms.h); a.xs must hold H floats of workspace.
+hipError_t launch_layer_form(const LayerArgs &a, int form, hipStream_t s);
 
 // x_t = h_t / sqrt(mean(h_t^2) + eps) for B tokens of width H.
 hipError_t launch_rms(const float *h, float *x, int B, int H, float eps, hipStream_t s);

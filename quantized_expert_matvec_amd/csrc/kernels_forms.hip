@@ -21,57 +21,12 @@
 // kernel comes in the same four forms, so that a whole expert (gate/up, then the
 // down projection as a matvec) can run in each.
 #include "forms.h"
+#include "kernels.h"
 #include "layer_kernels.h"
 
 namespace fmoe {
 namespace dev {
 namespace {
-
-constexpr int kLutStride = 17;  // LDS floats per lane's table (16 entries, padded)
-
-// code of column j of the lane's group, as stored: 4-bit -- word j / 8 of the
-// group's eight words, low nibble of byte j % 4 for j % 8 < 4, else its high
-// nibble; 2-bit -- word j / 16, field (j / 4) % 4 of byte j % 4.
-template <int BITS>
-__device__ __forceinline__ uint32_t code_of(const Chunk<BITS> &c, int j);
-template <>
-__device__ __forceinline__ uint32_t code_of<4>(const Chunk<4> &c, int j) {
-  const uint32_t w[8] = {c.a.x, c.a.y, c.a.z, c.a.w, c.b.x, c.b.y, c.b.z, c.b.w};
-  const int hw = j / 8, r = j % 8;
-  return (w[hw] >> (8 * (r % 4) + 4 * (r / 4))) & 15u;
-}
-template <>
-__device__ __forceinline__ uint32_t code_of<2>(const Chunk<2> &c, int j) {
-  const uint32_t w[4] = {c.a.x, c.a.y, c.a.z, c.a.w};
-  const int wd = j / 16, q = (j / 4) % 4, b = j % 4;
-  return (w[wd] >> (8 * b + 2 * q)) & 3u;
-}
-
-template <int BITS, int FORM>
-__device__ __forceinline__ float partial_form(const Chunk<BITS> &c, uint32_t sb, const XSlice &xs, float *lut) {
-  const float s = scale_of(sb), b = bias_of(sb);
-  if constexpr (FORM == 2) {
-    return group_partial<BITS>(c, sb, xs);
-  } else if constexpr (FORM == 3) {
-#pragma unroll
-    for (int k = 0; k < (1 << BITS); ++k) lut[k] = fmaf((float)k, s, b);
-    float acc = 0.f;
-#pragma unroll
-    for (int j = 0; j < kGroup; ++j) acc = fmaf(lut[code_of<BITS>(c, j)], xs.v[j], acc);
-    return acc;
-  } else {
-    float acc = 0.f;
-#pragma unroll
-    for (int j = 0; j < kGroup; ++j) {
-      const float cj = (float)code_of<BITS>(c, j);
-      if constexpr (FORM == 0)
-        acc = fmaf(fmaf(cj, s, b), xs.v[j], acc);
-      else
-        acc += fmaf(cj, s * xs.v[j], b * xs.v[j]);
-    }
-    return acc;
-  }
-}
 
 template <int BITS, int NGP, int ITERS, int FORM>
 __global__ __launch_bounds__(kBlock) void k_qmatvec_form(const uint8_t *__restrict__ blob, int ng, int rows,
@@ -192,8 +147,36 @@ hipError_t launch_bits(int form, const uint8_t *blob, int rows, int cols, const 
   }
 }
 
+// The one-token layer at hidden 4096, inter 1024, top-4 with the gate/up and down
+// arithmetic in form FORM (the router kernel as in the library, writing x in fp32 too).
+template <int BITS, int FORM>
+hipError_t layer_form_it(const LayerArgs &L, hipStream_t s) {
+  using D = Dispatch<BITS>;
+  const LayerGeom<BITS, 64, 16> G(L, BITS);
+  hipError_t e = D::template phase1<64, 16>(L, G, s);
+  if (e == hipSuccess) e = D::template phase2<64, 16, FORM>(L, G, s);
+  if (e == hipSuccess) e = D::template phase3<64, 16, 4, FORM>(L, G, s);
+  return e;
+}
+
+template <int BITS>
+hipError_t layer_form_bits(const LayerArgs &L, int form, hipStream_t s) {
+  switch (form) {
+    case 0: return layer_form_it<BITS, 0>(L, s);
+    case 1: return layer_form_it<BITS, 1>(L, s);
+    case 2: return layer_form_it<BITS, 2>(L, s);
+    default: return layer_form_it<BITS, 3>(L, s);
+  }
+}
+
 }  // namespace
 }  // namespace dev
+
+hipError_t launch_layer_form(const LayerArgs &a, int form, hipStream_t s) {
+  if (a.H != 4096 || a.I != 1024 || a.K != 4 || a.E > 512 || !a.xs || form < 0 || form >= kForms)
+    return hipErrorInvalidValue;
+  return a.bits == 4 ? dev::layer_form_bits<4>(a, form, s) : dev::layer_form_bits<2>(a, form, s);
+}
 
 hipError_t launch_qmatvec_form(int bits, int form, const uint8_t *blob, int rows, int cols, const float *x, float *y,
                                hipStream_t s) {

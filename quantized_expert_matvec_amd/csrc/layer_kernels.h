@@ -140,6 +140,68 @@ __device__ __forceinline__ void trace_mark(uint64_t *tr, int slot) {
     tr[(size_t)blockIdx.x * kTraceSlots + slot] = __builtin_amdgcn_s_memrealtime();
 }
 
+// ------------------------------------------------------------------ dequant forms
+
+// The per-weight arithmetic of a group's partial sum in one of four forms, for the
+// comparison entry points (fmoe_qmatvec_form, fmoe_expert_ffn_form,
+// fmoe_moe_layer_form). Pages cited: [P1] "397B MoE en MacBook: Motor Flash-MoE a
+// 4,4 t/s" (aibit.im); [P2] "Flash-MoE: Ausfuehren eines 397B-Parameter-Qwen-Modells
+// auf dem MacBook Pro mit reinem C/Metal" (openclawradar.com). With c_j the code of
+// column j of a 64-column group, s and b the group's scale and bias:
+//   0 naive:     w_j = c_j s + b, then acc += w_j x_j (two fused multiply-adds);
+//   1 recast:    acc += fma(c_j, s x_j, b x_j), the per-weight form of
+//                [P1] "2. Kernel de desquantización optimizado con FMA" and
+//                [P2] "FMA-optimierter Dequant-Kernel" (s x_j and b x_j formed per weight);
+//   2 factored:  s * sum_j c_j x_j + b * sum_j x_j (group_partial, the library's form);
+//   3 table:     w_j = T[c_j] from a per-(row, group) table T[c] = c s + b that each
+//                lane writes to its own LDS row (kLutStride floats), then acc += w_j x_j:
+//                the GPU dequant lookup table that [P1] "Lo que descartaron" lists as slower.
+constexpr int kLutStride = 17;  // LDS floats per lane's table (16 entries, padded)
+
+// code of column j of the lane's group, as stored: 4-bit -- word j / 8 of the
+// group's eight words, low nibble of byte j % 4 for j % 8 < 4, else its high
+// nibble; 2-bit -- word j / 16, field (j / 4) % 4 of byte j % 4.
+template <int BITS>
+__device__ __forceinline__ uint32_t code_of(const Chunk<BITS> &c, int j);
+template <>
+__device__ __forceinline__ uint32_t code_of<4>(const Chunk<4> &c, int j) {
+  const uint32_t w[8] = {c.a.x, c.a.y, c.a.z, c.a.w, c.b.x, c.b.y, c.b.z, c.b.w};
+  const int hw = j / 8, r = j % 8;
+  return (w[hw] >> (8 * (r % 4) + 4 * (r / 4))) & 15u;
+}
+template <>
+__device__ __forceinline__ uint32_t code_of<2>(const Chunk<2> &c, int j) {
+  const uint32_t w[4] = {c.a.x, c.a.y, c.a.z, c.a.w};
+  const int wd = j / 16, q = (j / 4) % 4, b = j % 4;
+  return (w[wd] >> (8 * b + 2 * q)) & 3u;
+}
+
+template <int BITS, int FORM>
+__device__ __forceinline__ float partial_form(const Chunk<BITS> &c, uint32_t sb, const XSlice &xs, float *lut) {
+  const float s = scale_of(sb), b = bias_of(sb);
+  if constexpr (FORM == 2) {
+    return group_partial<BITS>(c, sb, xs);
+  } else if constexpr (FORM == 3) {
+#pragma unroll
+    for (int k = 0; k < (1 << BITS); ++k) lut[k] = fmaf((float)k, s, b);
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) acc = fmaf(lut[code_of<BITS>(c, j)], xs.v[j], acc);
+    return acc;
+  } else {
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      const float cj = (float)code_of<BITS>(c, j);
+      if constexpr (FORM == 0)
+        acc = fmaf(fmaf(cj, s, b), xs.v[j], acc);
+      else
+        acc += fmaf(cj, s * xs.v[j], b * xs.v[j]);
+    }
+    return acc;
+  }
+}
+
 // ------------------------------------------------------------------ row work
 
 // Weight registers of ITERS row iterations of one wavefront (a segment of NGP
@@ -210,6 +272,19 @@ struct PairLoads {
     for (int i = 0; i < ITERS; ++i) {
       const float pg = seg_reduce<NGP>(live ? group_partial<BITS>(cg[i], sg[i], xs) : 0.f);
       const float pu = seg_reduce<NGP>(live ? group_partial<BITS>(cu[i], su[i], xs) : 0.f);
+      if (seg_last<NGP>(lane)) h[pair0 + i * RPI + sub] = silu(pg) * pu;
+    }
+  }
+  // the same with the per-weight arithmetic in form FORM (tab: this lane's LDS table row)
+  template <int FORM>
+  __device__ __forceinline__ void finish_form(const XSlice &xs, float *__restrict__ h, int pair0, float *tab) const {
+    constexpr int RPI = kWave / NGP;
+    const int lane = lane_id();
+    const int sub = lane / NGP;
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+      const float pg = seg_reduce<NGP>(live ? partial_form<BITS, FORM>(cg[i], sg[i], xs, tab) : 0.f);
+      const float pu = seg_reduce<NGP>(live ? partial_form<BITS, FORM>(cu[i], su[i], xs, tab) : 0.f);
       if (seg_last<NGP>(lane)) h[pair0 + i * RPI + sub] = silu(pg) * pu;
     }
   }
@@ -609,6 +684,7 @@ struct Phase1Args {
   uint32_t *xdig;     // [hidden/64][kDigStride] x in digit form
   int ng;             // hidden / 64
   int n_prep_blocks;  // workgroups before the router's: x in digit form, then the gate
+  float *xs;          // null, or [hidden]: x (RMS-scaled) in fp32 too, for the form variants of phase 2
   uint64_t *trace;
 };
 
@@ -712,6 +788,7 @@ __global__ __launch_bounds__(kBlock) void k_phase1(const Phase1Args a) {
         write_digits<4>(xl, g, inv, ybuf[wv], a.xdig);
       else
         write_digits<2>(xl, g, inv, ybuf[wv], a.xdig);
+      if (a.xs) a.xs[kGroup * g + lane] = xl[lds_index(kGroup * g + lane)] * inv;
     }
     trace_mark(a.trace, 3);
     return;
@@ -776,6 +853,7 @@ struct Phase2Args {
   int n_routed_blocks;
   const uint8_t *shared_gu;  // null: no shared expert
   float *h_shared;
+  const float *xs;           // the form variants (FORM >= 0): x in fp32 [hidden] instead of xdig
   uint64_t *trace;
 };
 
@@ -785,19 +863,42 @@ struct Phase2Args {
 // depend on the routing, so its weights stream while the routed blocks are still
 // choosing. x arrives in the digit form the router kernel wrote (RMS factor
 // included), so this kernel reads no raw x. GI: gate/up pair iterations per
-// wavefront (gateup_iters(top_k)).
-template <int BITS, int NGHP, int GI>
+// wavefront (gateup_iters(top_k)). FORM >= 0 (comparison builds): x in fp32
+// (a.xs) and the per-weight arithmetic of partial_form<FORM> instead of the digit
+// form's integer dot products.
+template <int BITS, int NGHP, int GI, int FORM = -1>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void k_phase2(const Phase2Args a) {
   constexpr int RPIH = kWave / NGHP;
-  constexpr int D4 = (NGHP * kDigStride / 4 + kBlock - 1) / kBlock;
-  const int NF4 = a.ng * kDigStride / 4;  // 16-byte units of the digit form
-  __shared__ uint32_t xdl[NGHP * kDigStride];
+  constexpr bool DIG = FORM < 0;
+  constexpr int D4 = DIG ? (NGHP * kDigStride / 4 + kBlock - 1) / kBlock : (NGHP * 16 + kBlock - 1) / kBlock;
+  const int NF4 = DIG ? a.ng * kDigStride / 4 : a.ng * 16;  // 16-byte units of x's staged form
+  __shared__ uint32_t xdl[DIG ? NGHP * kDigStride : 1];
+  __shared__ float xfl[DIG ? 1 : NGHP * kXPad];
+  __shared__ float lut[FORM == 3 ? kBlock * kLutStride : 1];
   __shared__ __align__(16) float lg[kMaxExperts];
   __shared__ int sidx[kMaxTopK];
   __shared__ float sw[kMaxTopK];
   __shared__ TopkLds tks;
   const int lane = lane_id();
-  const float *xsrc = reinterpret_cast<const float *>(a.xdig);
+  const float *xsrc = DIG ? reinterpret_cast<const float *>(a.xdig) : a.xs;
+  auto x_store = [&](const Staged<D4> &st) {
+    if constexpr (DIG)
+      stage_copy(st, NF4, xdl);
+    else
+      stage_store<D4, false>(st, NF4, xfl, nullptr);
+  };
+  auto finish = [&](const PairLoads<BITS, NGHP, GI> &P, float *h, int pair0) {
+    const int g = min(lane & (NGHP - 1), a.ng - 1);
+    if constexpr (DIG) {
+      XDig xd;
+      read_digits(xdl, g, xd);
+      P.finish_dig(xd, h, pair0);
+    } else {
+      XSlice xs;
+      read_slice(xfl, g, 1.f, xs);
+      P.template finish_form<DIG ? 0 : FORM>(xs, h, pair0, FORM == 3 ? lut + threadIdx.x * kLutStride : lut);
+    }
+  };
   trace_mark(a.trace, 0);
   if ((int)blockIdx.x < a.n_routed_blocks) {
     // a workgroup serves one slot (waves_per_slot is a multiple of 4) and needs
@@ -848,14 +949,14 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       // routed wavefront is active: waves_per_slot * K is a whole number of
       // workgroups, and each wavefront's pairs lie inside its expert)
       P.issue(a.bank + (size_t)sidx[slot] * a.stride, a.ng, pair0);
-      stage_copy(xst, NF4, xdl);
+      x_store(xst);
       __syncthreads();
       trace_mark(a.trace, 1);
     } else {
       for (int i = threadIdx.x; i < a.E; i += kBlock) lg[i] = a.logits[i];
       Staged<D4> xst;
       stage_load(xsrc, NF4, xst);
-      stage_copy(xst, NF4, xdl);
+      x_store(xst);
       __syncthreads();
       trace_mark(a.trace, 1);
       block_topk(lg, a.E, bslot + 1, tks, sidx, sw);
@@ -870,11 +971,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       if (a.out_idx) a.out_idx[lane] = sel;
       if (a.out_w) a.out_w[lane] = ws;
     }
-    if (active) {
-      XDig xd;
-      read_digits(xdl, min(lane & (NGHP - 1), a.ng - 1), xd);
-      P.finish_dig(xd, a.h_routed + (size_t)slot * a.I, pair0);
-    }
+    if (active) finish(P, a.h_routed + (size_t)slot * a.I, pair0);
     trace_mark(a.trace, 3);
     return;
   }
@@ -888,14 +985,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   __builtin_amdgcn_sched_barrier(0);
   PairLoads<BITS, NGHP, GI> P;
   if (pair0 < a.I) P.issue(a.shared_gu, a.ng, pair0);
-  stage_copy(xst, NF4, xdl);
+  x_store(xst);
   __syncthreads();
   trace_mark(a.trace, 1);
-  if (pair0 < a.I) {
-    XDig xd;
-    read_digits(xdl, min(lane & (NGHP - 1), a.ng - 1), xd);
-    P.finish_dig(xd, a.h_shared, pair0);
-  }
+  if (pair0 < a.I) finish(P, a.h_shared, pair0);
   trace_mark(a.trace, 3);
 }
 
@@ -992,7 +1085,9 @@ struct Phase3Args {
 // NGIP lanes per row; its weights do not depend on the routing and are requested
 // first. A wavefront passes its shared results from the shared lanes to the
 // combining lanes through LDS.
-template <int BITS, int NGIP, int KPAD>
+// FORM >= 0 (comparison builds, at most four slots): the per-weight arithmetic of
+// partial_form<FORM> instead of group_partial.
+template <int BITS, int NGIP, int KPAD, int FORM = -1>
 __global__ __launch_bounds__(kP3Block) void k_phase3(const Phase3Args a) {
   constexpr int kP3Iters = down_iters(KPAD);
   constexpr int SLOTS = KPAD * NGIP;
@@ -1007,6 +1102,7 @@ __global__ __launch_bounds__(kP3Block) void k_phase3(const Phase3Args a) {
   // cache hierarchy) instead of holding a lane's SPL slices in registers
   constexpr bool STAGE = KPAD * NGIP <= (KPAD <= 4 ? 128 : 256);
   constexpr bool STREAM = KPAD >= 8;
+  static_assert(FORM < 0 || !STREAM, "the form builds take at most four slots");
   const int ngi = a.I / kGroup;
   const size_t RB = (size_t)ngi * gbytes<BITS>();
   __shared__ float hl[STAGE ? KPAD * NGIP * kXPad : 1];
@@ -1014,6 +1110,14 @@ __global__ __launch_bounds__(kP3Block) void k_phase3(const Phase3Args a) {
   __shared__ float hlsum[STAGE ? KPAD * NGIP : 1];  // per-group sums of the staged h
   __shared__ float hssum[NGIP];
   __shared__ float dsh[kP3Waves * RPW];
+  __shared__ float lut[FORM == 3 ? kP3Block * kLutStride : 1];
+  // a group's partial sum in this build's form
+  auto gpart = [&](const Chunk<BITS> &c, uint32_t sb, const XSlice &xs) {
+    if constexpr (FORM < 0)
+      return group_partial<BITS>(c, sb, xs);
+    else
+      return partial_form<BITS, FORM>(c, sb, xs, FORM == 3 ? lut + threadIdx.x * kLutStride : lut);
+  };
   trace_mark(a.trace, 0);
   const int lane = lane_id();
   const int sub = lane / SEG;
@@ -1089,7 +1193,7 @@ __global__ __launch_bounds__(kP3Block) void k_phase3(const Phase3Args a) {
     read_slice_sum(hs, sg, hssum[sg], xs);
 #pragma unroll
     for (int q = 0; q < SIT; ++q) {
-      const float p = seg_reduce<NGIP>(slive ? group_partial<BITS>(cs[q], ss[q], xs) : 0.f);
+      const float p = seg_reduce<NGIP>(slive ? gpart(cs[q], ss[q], xs) : 0.f);
       const int r = q * RPII + ssub;  // row within this wavefront's rows
       if (seg_last<NGIP>(lane) && r < RPW) dsh[wave_in_block() * RPW + r] = sig * p;
     }
@@ -1131,7 +1235,7 @@ __global__ __launch_bounds__(kP3Block) void k_phase3(const Phase3Args a) {
     for (int i = 0; i < kP3Iters; ++i)
 #pragma unroll
       for (int m = 0; m < SPL; ++m)
-        if (act[m]) pr[i] = fmaf(wk[m], group_partial<BITS>(c[i][m], sb[i][m], xs[m]), pr[i]);
+        if (act[m]) pr[i] = fmaf(wk[m], gpart(c[i][m], sb[i][m], xs[m]), pr[i]);
   }
 #pragma unroll
   for (int i = 0; i < kP3Iters; ++i) {
@@ -1212,7 +1316,7 @@ struct Dispatch {
     return hipGetLastError();
   }
 
-  template <int NGH, int NGI, int KPAD>
+  template <int NGH, int NGI, int KPAD, int FORM = -1>
   static hipError_t phase3(const LayerArgs &L, const LayerGeom<BITS, NGH, NGI> &G, hipStream_t s) {
     Phase3Args p3{};
     p3.bank = L.bank;
@@ -1230,7 +1334,7 @@ struct Dispatch {
     p3.residual = L.residual;
     p3.out = L.out;
     p3.trace = L.trace ? L.trace + (size_t)2 * kTraceBlocks * kTraceSlots : nullptr;
-    hipLaunchKernelGGL((k_phase3<BITS, NGI, KPAD>), dim3(G.n3), dim3(kP3Block), 0, s, p3);
+    hipLaunchKernelGGL((k_phase3<BITS, NGI, KPAD, FORM>), dim3(G.n3), dim3(kP3Block), 0, s, p3);
     return hipGetLastError();
   }
 
@@ -1249,6 +1353,7 @@ struct Dispatch {
     p1.xdig = L.xdig;
     p1.ng = L.H / kGroup;
     p1.n_prep_blocks = (p1.ng + kWavesPerBlock - 1) / kWavesPerBlock + (has_shared ? 1 : 0);
+    p1.xs = L.xs;
     p1.trace = L.trace;
     // before the router's workgroups: one per four 64-column groups of x (digit
     // form), then one for the shared expert's gate
@@ -1256,7 +1361,7 @@ struct Dispatch {
     return hipGetLastError();
   }
 
-  template <int NGH, int NGI>
+  template <int NGH, int NGI, int FORM = -1>
   static hipError_t phase2(const LayerArgs &L, const LayerGeom<BITS, NGH, NGI> &G, hipStream_t s) {
     const bool has_shared = L.shared != nullptr;
     Phase2Args p2{};
@@ -1277,13 +1382,16 @@ struct Dispatch {
     p2.n_routed_blocks = G.n2r;
     p2.shared_gu = has_shared ? L.shared : nullptr;
     p2.h_shared = L.h_shared;
+    p2.xs = L.xs;
     p2.trace = L.trace ? L.trace + (size_t)kTraceBlocks * kTraceSlots : nullptr;
     static_assert(gateup_iters(4) == 2 && gateup_iters(5) == 4, "the builds below");
     const dim3 grid(G.n2r + G.n2s);
     if (L.K <= 4)
-      hipLaunchKernelGGL((k_phase2<BITS, NGH, 2>), grid, dim3(kBlock), 0, s, p2);
-    else
+      hipLaunchKernelGGL((k_phase2<BITS, NGH, 2, FORM>), grid, dim3(kBlock), 0, s, p2);
+    else if constexpr (FORM < 0)
       hipLaunchKernelGGL((k_phase2<BITS, NGH, 4>), grid, dim3(kBlock), 0, s, p2);
+    else
+      return hipErrorInvalidValue;  // (the form builds take at most four slots)
     return hipGetLastError();
   }
 

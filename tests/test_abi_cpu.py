@@ -247,6 +247,23 @@ def test_layer_validation():
     # NaN-free pointer checks pass through to a launch only when everything is valid; not exercised here
 
 
+def test_layer_form_validation():
+    L0 = lay()
+    need = L.fmoe_workspace_bytes(ctypes.byref(L0), 1)
+    call = lambda Lx=L0, form=0, x=X, r=RES, o=OUT, ws=WSL, nb=need: L.fmoe_moe_layer_form(
+        ctypes.byref(Lx), x, r, o, None, None, ws, nb, form, None)
+    assert call(form=-1) == 2 and call(form=4) == 2
+    assert call(lay(hidden=2048)) == 2                 # the form builds take hidden 4096, inter 1024
+    assert call(lay(inter=512)) == 2
+    L1000 = lay(n_experts=1000)
+    assert call(L1000, nb=L.fmoe_workspace_bytes(ctypes.byref(L1000), 1)) == 2
+    assert call(lay(top_k=2)) == 5
+    assert call(lay(router=None)) == 1                 # fmoe_moe_layer's own checks
+    assert call(nb=need - 1) == 7
+    assert call(o=X) == 9
+    assert call(x=X + 8) == 3
+
+
 def test_layer_alias_validation():
     L0 = lay()
     need = L.fmoe_workspace_bytes(ctypes.byref(L0), 2)

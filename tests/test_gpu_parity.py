@@ -125,13 +125,16 @@ def test_expert_ffn_forms_vs_oracle(device, form, bits, hidden, inter):
 
 # --------------------------------------------------------------------------- layer
 
-def _check_layer(device, OL, L, X, RES, what, in_place=False):
+def _check_layer(device, OL, L, X, RES, what, in_place=False, form=None):
     xd = to_dev(X, device)
     rd = to_dev(RES, device)
     B = X.shape[0]
     idx = torch.full((B, OL.k), -1, dtype=torch.int32, device=device)
     w = torch.zeros((B, OL.k), dtype=torch.float32, device=device)
-    if in_place:
+    if form is not None:
+        assert B == 1
+        out = qem.fmoe_moe_layer_form(L, xd, rd, form, topk_idx=idx, topk_w=w)
+    elif in_place:
         out = qem.fmoe_moe_layer(L, xd, rd, out=rd, topk_idx=idx, topk_w=w)
         assert out.data_ptr() == rd.data_ptr()
     else:
@@ -227,6 +230,27 @@ def test_one_token_layer_vs_oracle(device, bits, hidden, inter, k, n_exp):
     X = _x(41, 200 + k, hidden, 2)
     RES = synth.activations(41, synth.T_RESIDUAL, 200 + k, 2, hidden)
     assert _one_token(device, OL, L, X, RES, f"one token q{bits}") == 0
+
+
+_FORM_LAYERS = {}
+
+
+@pytest.mark.parametrize("form", [0, 1, 2, 3])
+@pytest.mark.parametrize("bits", [4, 2])
+def test_layer_forms_vs_oracle(device, form, bits):
+    """The one-token layer with the expert projections' per-weight arithmetic in each form
+    (naive, fma recast, group-factored, table; fmoe_moe_layer_form) against the oracle:
+    16 experts + shared, hidden 4096, inter 1024, top-4, two tokens."""
+    hidden, inter, n_exp, k = 4096, 1024, 16, 4
+    if bits not in _FORM_LAYERS:
+        _FORM_LAYERS[bits] = (host_layer(45, 0, bits, n_exp, k, hidden, inter, device),
+                              OracleLayer(45, 0, bits, n_exp, k, hidden, inter))
+    L, OL = _FORM_LAYERS[bits]
+    X = _x(45, 300 + bits, hidden, 2)
+    RES = synth.activations(45, synth.T_RESIDUAL, 300 + bits, 2, hidden)
+    ties = sum(_check_layer(device, OL, L, X[t:t + 1], RES[t:t + 1], f"layer form {form} q{bits} token {t}", form=form)
+               for t in range(2))
+    assert ties == 0
 
 
 @pytest.mark.parametrize("bits", [4, 2])
