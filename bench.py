@@ -577,6 +577,51 @@ def read_ceiling(torch, qem, dev):
              "kernel": "fmoe_read_xor (16-byte non-temporal loads, 8 in flight per thread)"}, round(res[1], 3))
 
 
+def burst_floor(torch, qem, dev, sizes, rounds=60):
+    """How long plain streaming kernels with the given byte counts take back to back: the
+    library's streaming-read kernel (every thread's loads requested at once: one burst per
+    launch) on `rounds` rounds of distinct buffers, one launch per size per round, in a
+    graph replayed 3 times. Returns µs per round and, per size, µs per launch alone."""
+    sizes = [(n + 15) // 16 * 16 for n in sizes]
+    need = rounds * sum(sizes)
+    if torch.cuda.mem_get_info()[0] < need + (1 << 30):
+        return None
+    buf = torch.empty(need, dtype=torch.uint8, device=dev)
+    out = torch.zeros(1, dtype=torch.int32, device=dev)
+    offs = [sum(sizes[:i]) for i in range(len(sizes))]
+
+    def timed(which):
+        def call():
+            for r in range(rounds):
+                base = r * sum(sizes)
+                for i in which:
+                    qem.fmoe_read_xor(buf[base + offs[i]:base + offs[i] + sizes[i]], out)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            call()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        del g
+        return e0.elapsed_time(e1) * 1000.0 / (3 * rounds)
+
+    chain = timed(list(range(len(sizes))))
+    alone = [timed([i]) for i in range(len(sizes))]
+    del buf
+    return round(chain, 3), [round(t, 3) for t in alone]
+
+
 def cpu_model():
     """The host CPU as /proc/cpuinfo names it, with its family/model/stepping numbers."""
     info = {}
@@ -859,6 +904,18 @@ def main():
                     "kernel": dom, "avg_us": kk["avg_us"], "algorithmic_bytes_per_launch": kk["algorithmic_bytes"]}
         del lws, outs, xs
 
+    # ---- one token: how long three plain streaming kernels with the layer kernels' bytes take
+    chain_floor = None
+    if B == 1 and kernels:
+        log("bench: streaming bursts with the layer kernels' bytes")
+        names1 = list(kernels)
+        bf = burst_floor(torch, qem, dev, [kernels[n]["algorithmic_bytes"] for n in names1])
+        if bf is not None:
+            chain_floor = {"three_bursts_us_per_layer": bf[0],
+                           "burst_alone_us": {n: t for n, t in zip(names1, bf[1])},
+                           "kernel": "fmoe_read_xor (each thread's loads requested at once: one burst per launch)",
+                           "layer_us": round(us_layer, 3)}
+
     # ---- parity of layer 0, step 0 against the oracle, and the oracle's CPU time
     parity, cpu = None, None
     need_oracle = B == 1 and (not a.no_verify or not a.no_cpu_baseline)
@@ -933,6 +990,7 @@ def main():
         "us_per_layer_p10_p50_p90": spread,
         "kernels_per_layer": kernels_per_layer(B, K),
         "floor_us": floor,
+        "chain_floor": chain_floor,
         "weight_GBps": round(weight_gbps, 1),
         "frac_hbm_peak": round(weight_gbps / HBM_PEAK_GBPS, 4),
         "read_ceiling_GBps": ceiling,

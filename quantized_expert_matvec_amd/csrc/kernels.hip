@@ -65,16 +65,19 @@ __global__ __launch_bounds__(kBlock) void k_read_xor(const u32x4 *__restrict__ p
   const size_t stride = (size_t)gridDim.x * kBlock;
   size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x;
   uint32_t acc = 0;
-  for (; i + (kReadUnroll - 1) * stride < n16; i += kReadUnroll * stride) {
+  // rounds of kReadUnroll loads, all requested before any is used; in the last round
+  // the loads past the end re-read the last unit (not folded in), so that a buffer that
+  // takes one round per thread is one burst whatever its size
+  for (; i < n16; i += kReadUnroll * stride) {
     u32x4 v[kReadUnroll];
 #pragma unroll
-    for (int k = 0; k < kReadUnroll; ++k) v[k] = __builtin_nontemporal_load(p + i + k * stride);
+    for (int k = 0; k < kReadUnroll; ++k) {
+      const size_t j = i + k * stride;
+      v[k] = __builtin_nontemporal_load(p + (j < n16 ? j : n16 - 1));
+    }
 #pragma unroll
-    for (int k = 0; k < kReadUnroll; ++k) acc ^= (v[k].x ^ v[k].y) ^ (v[k].z ^ v[k].w);
-  }
-  for (; i < n16; i += stride) {
-    const u32x4 v = __builtin_nontemporal_load(p + i);
-    acc ^= (v.x ^ v.y) ^ (v.z ^ v.w);
+    for (int k = 0; k < kReadUnroll; ++k)
+      if (i + k * stride < n16) acc ^= (v[k].x ^ v[k].y) ^ (v[k].z ^ v[k].w);
   }
 #pragma unroll
   for (int m = 1; m < kWave; m <<= 1) acc ^= (uint32_t)__shfl_xor((int)acc, m);
