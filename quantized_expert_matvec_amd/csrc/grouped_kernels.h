@@ -727,36 +727,21 @@ struct RouteLdsT {
   TopkLds tk[kGWaves];                       // each wavefront's top-K scratch
 };
 using RouteLds = RouteLdsT<kRouteSlots / kWave>;  // every routed-in-kernel batch (kRouteSlots slots)
-using RouteLds1 = RouteLdsT<1>;       // at most 64 slots
 
-// Top-K of every token and the grouping of the S = B*K slots by expert, by one
-// workgroup of kGThreads threads, deterministic whatever the thread timing:
-//  - top-K of each token (wavefront t % 8) from its unscaled logits, weights with
-//    the token's RMS factor;
-//  - mask[v][e] = the lanes of wavefront v (slots 64v ..) routed to expert e (LDS
-//    atomic ORs: the result does not depend on their order); a slot's position in
-//    its expert's list = the set bits below it, in its own and earlier wavefronts:
-//    ascending slot order within each list;
-//  - the distinct experts in ascending id, with the offsets of their lists and of
-//    their token blocks, from one workgroup scan over the experts (two per thread).
-// On return blk[kBlkInts k ..] holds the token blocks (LDS; slotl[0..S) the
-// lists, as scratch); returns NB. The writer workgroup also stores the routing
-// (idx, w, sigma, the caller's outputs) and the table G.
-template <int NW>
-__device__ __forceinline__ int block_route(const GroupArgs &a, RouteLdsT<NW> &R, int *slotl, int *blk, bool writer) {
-  static_assert(kRouteSlots <= kGThreads, "one thread per slot");
-  static_assert(kMaxExperts <= 2 * kGThreads, "two experts per thread in the scan");
+// The top-K of every token of the batch (wavefront t % 8 takes token t, two
+// tokens per pass, all their loads requested together), from its unscaled logits
+// with the weights taken after its RMS factor: sidx[t K + j] = choice j of token t
+// (LDS). The writer workgroup also stores the routing (idx, w, sigma, the
+// caller's outputs). No barrier: the caller synchronises before reading sidx.
+__device__ __forceinline__ void route_topk(const GroupArgs &a, int *sidx, TopkLds (&tks)[kGWaves], bool writer) {
   const int lane = lane_id();
   const int wave = wave_in_block();
-  const int S = a.B * a.K;
-  const int nwl = (S + kWave - 1) / kWave;  // wavefronts holding slots
-  for (int i = threadIdx.x; i < nwl * a.E; i += kGThreads) R.mask[i / a.E][i % a.E] = 0ull;
   // token t's routing from its top-K (lane j < K: choice j): slot experts, and
   // the writer's outputs
   auto publish = [&](int t, int mi, float mw, float inv, float gd) {
     if (lane < a.K) {
       const int s = t * a.K + lane;
-      R.sidx[s] = mi;
+      sidx[s] = mi;
       if (writer) {
         a.idx[s] = mi;
         a.w[s] = mw;
@@ -766,7 +751,7 @@ __device__ __forceinline__ int block_route(const GroupArgs &a, RouteLdsT<NW> &R,
     }
     if (writer && lane == 0 && a.gvec) a.sigma[t] = 1.f / (1.f + expf(-gd * inv));
   };
-  TopkLds &tk = R.tk[wave];
+  TopkLds &tk = tks[wave];
   if (a.E <= 512) {
     // wavefront v: tokens v, v + 8, ...; two tokens per pass, all their loads
     // (logits in the top-K's layout, RMS factor, gate dot) requested together
@@ -800,6 +785,30 @@ __device__ __forceinline__ int block_route(const GroupArgs &a, RouteLdsT<NW> &R,
       publish(t, mi, mw, inv, gd);
     }
   }
+}
+
+// Top-K of every token and the grouping of the S = B*K slots by expert, by one
+// workgroup of kGThreads threads, deterministic whatever the thread timing:
+//  - top-K of each token (route_topk);
+//  - mask[v][e] = the lanes of wavefront v (slots 64v ..) routed to expert e (LDS
+//    atomic ORs: the result does not depend on their order); a slot's position in
+//    its expert's list = the set bits below it, in its own and earlier wavefronts:
+//    ascending slot order within each list;
+//  - the distinct experts in ascending id, with the offsets of their lists and of
+//    their token blocks, from one workgroup scan over the experts (two per thread).
+// On return blk[kBlkInts k ..] holds the token blocks (LDS; slotl[0..S) the
+// lists, as scratch); returns NB. The writer workgroup also stores the routing
+// (idx, w, sigma, the caller's outputs) and the table G.
+template <int NW>
+__device__ __forceinline__ int block_route(const GroupArgs &a, RouteLdsT<NW> &R, int *slotl, int *blk, bool writer) {
+  static_assert(kRouteSlots <= kGThreads, "one thread per slot");
+  static_assert(kMaxExperts <= 2 * kGThreads, "two experts per thread in the scan");
+  const int lane = lane_id();
+  const int wave = wave_in_block();
+  const int S = a.B * a.K;
+  const int nwl = (S + kWave - 1) / kWave;  // wavefronts holding slots
+  for (int i = threadIdx.x; i < nwl * a.E; i += kGThreads) R.mask[i / a.E][i % a.E] = 0ull;
+  route_topk(a, R.sidx, R.tk, writer);
   __syncthreads();
   const int s = threadIdx.x;
   const bool live = s < S;
@@ -872,6 +881,89 @@ __device__ __forceinline__ int block_route(const GroupArgs &a, RouteLdsT<NW> &R,
     for (int k = threadIdx.x; k < kBlkInts * NB; k += kGThreads) G[2 + k] = blk[k];
   }
   return NB;
+}
+
+// LDS scratch of route_small.
+struct __attribute__((aligned(16))) RouteSmallLds {
+  int sidx[kWave];  // expert of each slot (16-byte aligned: read four at a time)
+  int sorted[kWave];  // the slots in (expert, slot) order
+  int info[kWave];  // per sorted position: its slot's list index k | expert << 8 | slots in its block << 24
+  int nb;
+  TopkLds tk[kGWaves];
+};
+
+// The routing of a batch of S <= 64 slots, with the same result as block_route
+// (the table G and blk: the distinct experts in ascending id, each expert's slots
+// in ascending order cut into token blocks of up to kTokBlock, the blocks in that
+// order), with one wavefront doing the grouping instead of a scan over every
+// expert: after the top-Ks, lane s of wavefront 0 holds slot s and counts, over
+// all slots, those of a lower expert, those of its own and those of its own below
+// it (its index k in its expert's list); its rank under the key (expert, slot) is
+// the first count plus k, and it opens a token block when k is a multiple of
+// kTokBlock. The slots are placed in rank order in LDS, and each
+// block-opening position writes its block, numbered by the block-opening
+// positions below it. Returns NB.
+__device__ __forceinline__ int route_small(const GroupArgs &a, RouteSmallLds &R, int *blk, bool writer) {
+  static_assert(kTokBlock * kMaxTopK <= kWave, "every batch of at most kTokBlock tokens: one slot per lane");
+  const int lane = lane_id();
+  const int S = a.B * a.K;
+  route_topk(a, R.sidx, R.tk, writer);
+  __syncthreads();
+  if (wave_in_block() == 0) {
+    const bool live = lane < S;
+    const int e = live ? R.sidx[lane] : kMaxExperts;
+    // every lane reads the slots' experts four at a time (the same LDS words for
+    // all lanes: broadcasts); slots past S read as kMaxExperts, above every expert
+    int lower = 0, same = 0, k = 0;
+    for (int j0 = 0; j0 < S; j0 += 4) {  // (uniform)
+      const int4 q = *reinterpret_cast<const int4 *>(R.sidx + j0);
+      const int ej[4] = {q.x, j0 + 1 < S ? q.y : kMaxExperts, j0 + 2 < S ? q.z : kMaxExperts,
+                         j0 + 3 < S ? q.w : kMaxExperts};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        lower += ej[u] < e ? 1 : 0;
+        same += ej[u] == e ? 1 : 0;
+        k += ej[u] == e && j0 + u < lane ? 1 : 0;  // index of the slot in its expert's list
+      }
+    }
+    const int rank = lower + k;  // position of the slot under the key (expert, slot)
+    const unsigned long long first = __ballot(live && k == 0);  // one slot per distinct expert
+    if (live) {
+      const bool opens = k % kTokBlock == 0;
+      R.sorted[rank] = lane;
+      R.info[rank] = opens ? (k | e << 8 | min(kTokBlock, same - k) << 24) : -1;
+    }
+    wave_lds_fence();
+    // lane p: sorted position p
+    const int inf = lane < S ? R.info[lane] : -1;
+    const bool opens = inf >= 0;
+    const unsigned long long bm = __ballot(opens);
+    const int nb = __popcll(bm);
+    if (opens) {
+      const int b = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
+      const int n = inf >> 24, ex = (inf >> 8) & 0xFFFF;
+      int rec[kBlkInts];
+      rec[0] = ex;
+      rec[1] = n;
+#pragma unroll
+      for (int u = 0; u < kTokBlock; ++u) rec[2 + u] = R.sorted[lane + min(u, n - 1)];
+#pragma unroll
+      for (int i = 0; i < kBlkInts; ++i) blk[kBlkInts * b + i] = rec[i];
+      if (writer) {
+#pragma unroll
+        for (int i = 0; i < kBlkInts; ++i) a.groups[2 + kBlkInts * b + i] = rec[i];
+      }
+    }
+    if (lane == 0) {
+      R.nb = nb;
+      if (writer) {
+        a.groups[0] = __popcll(first);
+        a.groups[1] = nb;
+      }
+    }
+  }
+  __syncthreads();
+  return R.nb;
 }
 
 // ------------------------------------------------------------------ routing kernels (large batches)
@@ -1024,7 +1116,8 @@ __global__ __launch_bounds__(kGThreads) void k_group(const GroupArgs a) {
 // Wavefront w holds rows 16w .. 16w + 15. h vectors: slot s at index s,
 // shared-expert token t at index S + t. TABLE: the routing kernels have written
 // the routing and the grouping table already (large batches); otherwise every
-// workgroup derives them itself (block_route) when it meets its first routed item.
+// workgroup derives them itself when it meets its first routed item (route_small
+// for batches of at most kTokBlock tokens, block_route for the others).
 template <int BITS, int NGH, bool PRE, bool FULL, bool TABLE>
 __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
   // (NGH: the hidden groups ng rounded up to a power of two; FULL: ng == NGH)
@@ -1062,7 +1155,7 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
   // routing scratch then lives in the wavefronts' chunk regions instead of xl.
   using MR = MfmaRows<BITS, NGH, 1, FULL>;
   constexpr bool pre = PRE;  // (launched for batches of at most kTokBlock tokens)
-  static_assert(sizeof(RouteLds1) <= sizeof(wlds), "routing scratch of a small batch fits the chunk regions");
+  static_assert(sizeof(RouteSmallLds) <= sizeof(wlds), "routing scratch of a small batch fits the chunk regions");
   if (pre && wv >= a.B) {  // (B <= kTokBlock < kGWaves: at least four such wavefronts)
     const int nst = (kGWaves - a.B) * kWave, st = (int)threadIdx.x - a.B * kWave;
     const int units = kParts * a.B * ng * 4;
@@ -1110,7 +1203,7 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
         if constexpr (TABLE)
           NB = __builtin_amdgcn_readfirstlane(a.groups[1]);
         else if constexpr (PRE)
-          NB = block_route(a, *reinterpret_cast<RouteLds1 *>(&wlds[0][0]), slotl, blk, writer);
+          NB = route_small(a, *reinterpret_cast<RouteSmallLds *>(&wlds[0][0]), blk, writer);
         else
           NB = block_route(a, *reinterpret_cast<RouteLds *>(xl), slotl, blk, writer);
         gtrace(a, 1, 1);
