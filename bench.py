@@ -64,7 +64,9 @@ def parse():
     p.add_argument("--topk", type=int, default=4)
     p.add_argument("--seed", type=int, default=42)
     p.add_argument("--no-graph", action="store_true")
-    p.add_argument("--kernel-reps", type=int, default=5, help="passes over the layers when timing one kernel")
+    p.add_argument("--kernel-reps", type=int, default=5,
+                   help="passes over the layers when timing one kernel (0: no per-kernel timing, so that a "
+                        "counter run sees only the stack's own dispatches)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-verify", action="store_true")
@@ -856,7 +858,7 @@ def main():
 
     # ---- per-kernel (B=1) or per-phase (grouped) durations, HIP events on the launching stream
     roofline, kernels = None, {}
-    if True:
+    if a.kernel_reps > 0:
         log("bench: timing each layer kernel")
         kstream = torch.cuda.Stream()
         xs = torch.from_numpy(np.stack([synth.activations(a.seed, synth.T_X, l, B, H)
