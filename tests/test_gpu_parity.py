@@ -3,6 +3,8 @@ seeded inputs. Bar: routing indices identical (near-ties of the oracle's logits
 excepted, and then the GPU's choice must be consistent with them), routing
 weights within 1e-5 relative, outputs within max-relative 2e-3 and per-token
 L2-relative 1e-4; byte work (packing, generation) bit-exact."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -422,6 +424,20 @@ def test_grouped_layer_forced_collisions(device, bits, B):
     assert _check_layer(device, OL, L, X, RES, f"collisions q{bits} B={B}") == 0
 
 
+@pytest.mark.parametrize("B,k,n_exp", [(4, 16, 32), (3, 4, 8), (2, 8, 8), (4, 1, 4)])
+def test_grouped_small_batch_routing(device, B, k, n_exp):
+    """Batches of at most four tokens, grouped by one wavefront inside the gate/up kernel: up
+    to 64 slots (4 tokens x top-16), tokens in pairs of identical x so that chosen experts
+    serve two to four slots; every token against the oracle."""
+    hidden, inter = 1024, 256
+    L = host_layer(65, 0, 4, n_exp, k, hidden, inter, device)
+    OL = OracleLayer(65, 0, 4, n_exp, k, hidden, inter)
+    base = _x(65, 11, hidden, 2)
+    X = np.ascontiguousarray(base[np.arange(B) % 2])
+    RES = synth.activations(65, synth.T_RESIDUAL, 11, B, hidden)
+    assert _check_layer(device, OL, L, X, RES, f"small batch B={B} top-{k} of {n_exp}") == 0
+
+
 def test_grouped_layer_max_slots(device):
     """64 tokens with top-8 of 16 experts: 512 slots, every expert shared by many tokens;
     inter 4096 (the smallest staging chunk)."""
@@ -509,6 +525,50 @@ def test_stack_vs_oracle(device, B):
             assert list(gi[l, t]) == list(ri), (l, t)
             assert_close(ha[l, t], ref, f"stack B={B} token {t} layer {l}")
             h = ref
+
+
+@pytest.mark.parametrize("B", [1, 4, 16])
+def test_stack_graph_replays_equal_eager(device, B):
+    """The stack captured once in a HIP graph (as the benchmark times it) and replayed on three
+    inputs in turn, with eager stack calls and synchronisations between the replays: every
+    replay's output and routing equal, bit for bit, those of an eager call on the same input."""
+    hidden, inter, n_exp, k, n_layers = 1024, 256, 32, 4, 3
+    print(f"stack graph replays B={B}", flush=True)
+    layers = [host_layer(70, l, 4, n_exp, k, hidden, inter, device) for l in range(n_layers)]
+    inputs = [to_dev(synth.activations(70, synth.T_H0, 300 + 17 * r + B, B, hidden), device) for r in range(3)]
+    refs, ref_idx = [], []
+    for x in inputs:
+        idx = torch.empty((n_layers, B, k), dtype=torch.int32, device=device)
+        refs.append(qem.fmoe_moe_stack(layers, x, topk_idx=idx))
+        ref_idx.append(idx)
+    torch.cuda.synchronize()
+    h_in = torch.empty_like(inputs[0])
+    h_out = torch.empty_like(inputs[0])
+    g_idx = torch.empty((n_layers, B, k), dtype=torch.int32, device=device)
+    need = int(qem.lib().fmoe_stack_workspace_bytes(ctypes.byref(layers[0].c()), B))
+    ws = torch.empty(need, dtype=torch.uint8, device=device)
+    h_in.copy_(inputs[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        qem.fmoe_moe_stack(layers, h_in, h_out=h_out, topk_idx=g_idx, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        qem.fmoe_moe_stack(layers, h_in, h_out=h_out, topk_idx=g_idx, ws=ws)
+    for r in (1, 0, 2, 1):
+        h_out.fill_(float("nan"))
+        g_idx.fill_(-1)
+        h_in.copy_(inputs[r])
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(h_out, refs[r]), (B, r)
+        assert torch.equal(g_idx, ref_idx[r]), (B, r)
+        other = qem.fmoe_moe_stack(layers, inputs[(r + 1) % 3])  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(other, refs[(r + 1) % 3])
+    del g
 
 
 @pytest.mark.parametrize("B", [1, 4, 16])
