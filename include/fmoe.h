@@ -271,7 +271,8 @@ fmoe_status fmoe_moe_layer_noalloc(const fmoe_layer *L, int n_tokens, const floa
  *
  * fmoe_cache_device_bytes: bytes of the caller's device buffer for a cache of
  * n_slots blobs of experts with this shape and up to n_experts experts per layer
- * (the slots and a table of blob addresses); 0 if unsupported.
+ * (the slots, a table of blob addresses and the state of the policy when it runs on
+ * the GPU: 16 bytes per slot and 8 KB); 0 if unsupported.
  * fmoe_cache_create: the cache over that buffer (256-B aligned, device_bytes at
  * least the above). The library allocates the host bookkeeping here and, at the
  * first tiered call, two small pinned host buffers (the routing read-back and the
@@ -315,6 +316,27 @@ size_t fmoe_tiered_workspace_bytes(const fmoe_layer *L, int n_tokens);
 fmoe_status fmoe_moe_layer_tiered(fmoe_cache *c, int layer, const fmoe_layer *L, int n_tokens, const float *x,
                                   const float *residual, float *out, int32_t *topk_idx, float *topk_w, void *ws,
                                   size_t ws_bytes, void *stream);
+/* fmoe_moe_layer_tiered_device: the same layer and the same policy, run on the GPU,
+ * with no host synchronisation (it can be captured in a graph). After the router and
+ * top-K, one kernel plans the call's distinct experts (ascending id) through the
+ * cache's state, which lives in the cache's device buffer, writes the chosen
+ * experts' slot addresses and the list of misses; a second kernel copies each
+ * missing blob from L->bank, read directly over the bus (L->bank must be pinned host
+ * memory the device can address: hipHostMalloc or a pinned torch tensor); then the
+ * experts and the combine, as fmoe_moe_layer_tiered. For the same sequence of calls
+ * the slots, counters and results equal the host policy's. A cache is driven by one
+ * policy: FMOE_ERR_SHAPE if fmoe_cache_plan or fmoe_moe_layer_tiered used it before
+ * (and they return FMOE_ERR_SHAPE on a cache this call used). The first such call on
+ * a cache initialises its device state (every slot empty) on `stream` and must not be
+ * captured (FMOE_ERR_WORKSPACE if `stream` is capturing then); later calls may be.
+ * fmoe_cache_get_stats on such a cache synchronises the device and reads the counters
+ * back (call it outside graph capture). FMOE_ERR_WORKSPACE if n_slots exceeds 65536 or is below
+ * min(n_tokens * top_k, n_experts) (every call's experts must fit; checked on the host,
+ * before anything is enqueued); FMOE_ERR_LAUNCH if L->bank is not device-addressable
+ * host memory. Otherwise the arguments and errors of fmoe_moe_layer_tiered. */
+fmoe_status fmoe_moe_layer_tiered_device(fmoe_cache *c, int layer, const fmoe_layer *L, int n_tokens,
+                                         const float *x, const float *residual, float *out, int32_t *topk_idx,
+                                         float *topk_w, void *ws, size_t ws_bytes, void *stream);
 
 /* RMS scaling without a learned weight, two stages (sum of squares, then apply)
  * ([P2] "Metal-Compute-Shader": RMS normalization, two-stage):

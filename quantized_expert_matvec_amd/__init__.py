@@ -97,6 +97,9 @@ _SIGS = {
     "fmoe_tiered_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(fmoe_layer), ctypes.c_int]),
     "fmoe_moe_layer_tiered": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(fmoe_layer), ctypes.c_int] +
                               [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "fmoe_moe_layer_tiered_device": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(fmoe_layer),
+                                                    ctypes.c_int] + [ctypes.c_void_p] * 6 +
+                                     [ctypes.c_size_t, ctypes.c_void_p]),
     "fmoe_rms_scale": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_float, ctypes.c_void_p]),
     "fmoe_moe_stack": (ctypes.c_int, [ctypes.POINTER(fmoe_layer), ctypes.c_int, ctypes.c_int] +
@@ -519,6 +522,27 @@ def fmoe_moe_layer_tiered(cache: ExpertCache, layer: int, L: Layer, x: torch.Ten
     _ok(lib().fmoe_moe_layer_tiered(cache.handle, layer, ctypes.byref(L.c()), n_tokens, _ptr(x), _ptr(residual),
                                     _ptr(out), _ptr(topk_idx), _ptr(topk_w), _ptr(ws), nbytes, _stream(stream)),
         "fmoe_moe_layer_tiered")
+    return out
+
+
+def fmoe_moe_layer_tiered_device(cache: ExpertCache, layer: int, L: Layer, x: torch.Tensor, residual: torch.Tensor,
+                                 out: Optional[torch.Tensor] = None, topk_idx: Optional[torch.Tensor] = None,
+                                 topk_w: Optional[torch.Tensor] = None, ws=None, stream=None) -> torch.Tensor:
+    """fmoe_moe_layer_tiered with the cache's policy and the copies on the GPU: no host
+    synchronisation (L.bank: a pinned CPU tensor)."""
+    _dev_f32(x, "x")
+    _dev_f32(residual, "residual")
+    n_tokens = x.shape[0] if x.dim() == 2 else 1
+    if out is None:
+        out = torch.empty_like(residual)
+    need = fmoe_tiered_workspace_bytes(L, n_tokens)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    nbytes = ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else need
+    _ok(lib().fmoe_moe_layer_tiered_device(cache.handle, layer, ctypes.byref(L.c()), n_tokens, _ptr(x),
+                                           _ptr(residual), _ptr(out), _ptr(topk_idx), _ptr(topk_w), _ptr(ws),
+                                           nbytes, _stream(stream)),
+        "fmoe_moe_layer_tiered_device")
     return out
 
 

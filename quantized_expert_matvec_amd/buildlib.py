@@ -11,7 +11,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(_HERE)
-SOURCES = ["csrc/kernels_q4.hip", "csrc/kernels_q2.hip", "csrc/kernels.hip", "csrc/kernels_forms.hip", "csrc/scratch.hip", "csrc/api.cpp",
+SOURCES = ["csrc/kernels_q4.hip", "csrc/kernels_q2.hip", "csrc/kernels.hip", "csrc/kernels_forms.hip", "csrc/scratch.hip", "csrc/tier_kernels.hip", "csrc/api.cpp",
            "csrc/pack.cpp"]
 OUT = os.path.join(_HERE, "libfmoe.so")
 BUILD_DIR = os.path.join(ROOT, "_build", "fmoe")

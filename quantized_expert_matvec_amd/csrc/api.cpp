@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <new>
+#include <unordered_map>
 #include <vector>
 
 #include "../../include/fmoe.h"
@@ -421,12 +422,33 @@ struct fmoe_cache {
   int32_t *idx_host;             // pinned host: routing read-back [kMaxTokens * kMaxTopK]
   fmoe::ExpertCache lru;
   int64_t lookups = 0, bytes = 0;
+  // where the policy runs: 0 not yet, 1 on the host (lru), 2 on the device (the state below)
+  int mode = 0;
+  bool dev_init = false;         // the device state initialised (by the first device-policy call)
+  fmoe::TierHdr *hdr;            // device: counters and the current call's copy count
+  int64_t *key;                  // device: [n_slots] (layer, expert) held, -1 empty
+  uint64_t *last;                // device: [n_slots] last use
+  int32_t *jobs;                 // device: [2 * kMaxExperts] the current call's copies
+  std::unordered_map<const void *, const void *> bank_dev;  // host bank -> its device-visible address
   fmoe_cache(int n) : lru(n) {}
 };
 
 namespace {
 size_t cache_table_offset(int bits, int hidden, int inter, int n_slots) {
   return round_up((size_t)n_slots * expert_bytes(bits, hidden, inter), 256);
+}
+// the device policy's state, after the table: header, keys, last uses, copy jobs
+struct CacheState {
+  size_t hdr, key, last, jobs, end;
+};
+CacheState cache_state(int bits, int hidden, int inter, int n_experts, int n_slots) {
+  CacheState c;
+  c.hdr = cache_table_offset(bits, hidden, inter, n_slots) + round_up(sizeof(void *) * (size_t)n_experts, 256);
+  c.key = c.hdr + round_up(sizeof(fmoe::TierHdr), 256);
+  c.last = c.key + round_up(sizeof(int64_t) * (size_t)n_slots, 256);
+  c.jobs = c.last + round_up(sizeof(uint64_t) * (size_t)n_slots, 256);
+  c.end = c.jobs + round_up(sizeof(int32_t) * 2 * kMaxExperts, 256);
+  return c;
 }
 }  // namespace
 
@@ -436,7 +458,7 @@ size_t fmoe_cache_device_bytes(int bits, int hidden, int inter, int group, int n
   if (check_expert_shape(bits, hidden, inter, group) != FMOE_OK || n_slots < 1 || n_experts < 1 ||
       n_experts > kMaxExperts)
     return 0;
-  return cache_table_offset(bits, hidden, inter, n_slots) + round_up(sizeof(void *) * (size_t)n_experts, 256);
+  return cache_state(bits, hidden, inter, n_experts, n_slots).end;
 }
 
 fmoe_status fmoe_cache_create(int bits, int hidden, int inter, int group, int n_experts, int n_slots,
@@ -462,6 +484,12 @@ fmoe_status fmoe_cache_create(int bits, int hidden, int inter, int group, int n_
   c->table = (const uint8_t **)((uint8_t *)device_buf + cache_table_offset(bits, hidden, inter, n_slots));
   c->table_host = nullptr;  // (pinned host buffers: allocated by the first tiered call)
   c->idx_host = nullptr;
+  const CacheState cs = cache_state(bits, hidden, inter, n_experts, n_slots);
+  uint8_t *b = (uint8_t *)device_buf;
+  c->hdr = (fmoe::TierHdr *)(b + cs.hdr);
+  c->key = (int64_t *)(b + cs.key);
+  c->last = (uint64_t *)(b + cs.last);
+  c->jobs = (int32_t *)(b + cs.jobs);
   *out = c;
   return FMOE_OK;
 }
@@ -476,6 +504,16 @@ void fmoe_cache_destroy(fmoe_cache *c) {
 fmoe_status fmoe_cache_get_stats(const fmoe_cache *c, int64_t *lookups, int64_t *hits, int64_t *misses,
                                  int64_t *bytes_copied) {
   if (!c) return FMOE_ERR_NULL;
+  if (c->mode == 2) {
+    fmoe::TierHdr h;
+    if (hipDeviceSynchronize() != hipSuccess || hipMemcpy(&h, c->hdr, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess)
+      return FMOE_ERR_LAUNCH;
+    if (lookups) *lookups = h.lookups;
+    if (hits) *hits = h.hits;
+    if (misses) *misses = h.misses;
+    if (bytes_copied) *bytes_copied = h.bytes;
+    return FMOE_OK;
+  }
   if (lookups) *lookups = c->lookups;
   if (hits) *hits = c->lru.hits();
   if (misses) *misses = c->lru.misses();
@@ -486,6 +524,7 @@ fmoe_status fmoe_cache_get_stats(const fmoe_cache *c, int64_t *lookups, int64_t 
 fmoe_status fmoe_cache_plan(fmoe_cache *c, int layer, const int32_t *experts, int n, int32_t *slot_out,
                             int32_t *miss_out) {
   if (!c || !experts || !slot_out || !miss_out) return FMOE_ERR_NULL;
+  if (c->mode == 2) return FMOE_ERR_SHAPE;  // (the cache's policy runs on the device)
   if (layer < 0 || n < 1) return FMOE_ERR_BATCH;
   std::vector<int32_t> sorted(experts, experts + n);
   std::sort(sorted.begin(), sorted.end());
@@ -493,6 +532,7 @@ fmoe_status fmoe_cache_plan(fmoe_cache *c, int layer, const int32_t *experts, in
     if (sorted[i] < 0 || sorted[i] >= c->n_experts || (i > 0 && sorted[i] == sorted[i - 1])) return FMOE_ERR_ROUTING;
   if (n > c->n_slots) return FMOE_ERR_WORKSPACE;
   c->lookups += n;
+  c->mode = 1;
   return c->lru.plan(layer, experts, n, slot_out, miss_out) ? FMOE_OK : FMOE_ERR_WORKSPACE;
 }
 
@@ -501,9 +541,13 @@ size_t fmoe_tiered_workspace_bytes(const fmoe_layer *L, int n_tokens) {
   return layer_ws(n_tokens, L->n_experts, L->top_k, L->hidden, L->inter, true).total;
 }
 
-fmoe_status fmoe_moe_layer_tiered(fmoe_cache *c, int layer, const fmoe_layer *L, int n_tokens, const float *x,
-                                  const float *residual, float *out, int32_t *topk_idx, float *topk_w, void *ws,
-                                  size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+// The arguments of a tiered layer call (either policy).
+fmoe_status tiered_check(const fmoe_cache *c, int layer, const fmoe_layer *L, int n_tokens, const float *x,
+                         const float *residual, const float *out, const int32_t *topk_idx, const float *topk_w,
+                         const void *ws, size_t ws_bytes) {
   if (!c) return FMOE_ERR_NULL;
   fmoe_status st = check_layer(L);
   if (st != FMOE_OK) return st;
@@ -524,6 +568,19 @@ fmoe_status fmoe_moe_layer_tiered(fmoe_cache *c, int layer, const fmoe_layer *L,
       (residual != out && overlap(residual, ab, out, ab)) || overlap(topk_idx, kb, residual, ab) ||
       overlap(topk_w, kb, residual, ab) || overlap(topk_idx, kb, x, ab) || overlap(topk_w, kb, x, ab))
     return FMOE_ERR_ALIAS;
+  return FMOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+fmoe_status fmoe_moe_layer_tiered(fmoe_cache *c, int layer, const fmoe_layer *L, int n_tokens, const float *x,
+                                  const float *residual, float *out, int32_t *topk_idx, float *topk_w, void *ws,
+                                  size_t ws_bytes, void *stream) {
+  fmoe_status st = tiered_check(c, layer, L, n_tokens, x, residual, out, topk_idx, topk_w, ws, ws_bytes);
+  if (st != FMOE_OK) return st;
+  if (c->mode == 2) return FMOE_ERR_SHAPE;  // (the cache's policy runs on the device)
+  c->mode = 1;
   if (!c->table_host) {
     if (hipHostMalloc((void **)&c->table_host, sizeof(void *) * (size_t)c->n_experts, hipHostMallocDefault) !=
         hipSuccess) {
@@ -571,6 +628,62 @@ fmoe_status fmoe_moe_layer_tiered(fmoe_cache *c, int layer, const fmoe_layer *L,
                      hipMemcpyHostToDevice, s) != hipSuccess)
     return FMOE_ERR_LAUNCH;
   // 3. the experts from their slots, and the combine
+  return launch_group_experts(g, s) == hipSuccess ? FMOE_OK : FMOE_ERR_LAUNCH;
+}
+
+fmoe_status fmoe_moe_layer_tiered_device(fmoe_cache *c, int layer, const fmoe_layer *L, int n_tokens,
+                                         const float *x, const float *residual, float *out, int32_t *topk_idx,
+                                         float *topk_w, void *ws, size_t ws_bytes, void *stream) {
+  fmoe_status st = tiered_check(c, layer, L, n_tokens, x, residual, out, topk_idx, topk_w, ws, ws_bytes);
+  if (st != FMOE_OK) return st;
+  if (c->mode == 1) return FMOE_ERR_SHAPE;  // (the cache's policy runs on the host)
+  const int S = n_tokens * L->top_k;
+  if (c->n_slots > kMaxTierSlots || std::min(S, L->n_experts) > c->n_slots) return FMOE_ERR_WORKSPACE;
+  // the bank's device-visible address, looked up once per bank (so that calls under
+  // graph capture make no runtime query)
+  const void *bank = nullptr;
+  const auto it = c->bank_dev.find(L->bank);
+  if (it != c->bank_dev.end()) {
+    bank = it->second;
+  } else {
+    void *d = nullptr;
+    if (hipHostGetDevicePointer(&d, (void *)L->bank, 0) != hipSuccess || !d) {
+      (void)hipGetLastError();  // (not left for the next launch check to report)
+      return FMOE_ERR_LAUNCH;
+    }
+    c->bank_dev[L->bank] = d;
+    bank = d;
+  }
+  hipStream_t s = as_stream(stream);
+  if (!c->dev_init) {
+    // the first call initialises the state (every slot empty, counters zero): not
+    // inside a graph capture, whose replays would each start from an empty cache
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cap) != hipSuccess) return FMOE_ERR_LAUNCH;
+    if (cap != hipStreamCaptureStatusNone) return FMOE_ERR_WORKSPACE;
+    if (launch_tier_init(c->hdr, c->key, c->n_slots, s) != hipSuccess) return FMOE_ERR_LAUNCH;
+    c->dev_init = true;
+  }
+  c->mode = 2;
+  GroupArgs g = group_args(L, n_tokens, x, -1.f, residual, out, topk_idx, topk_w, (uint8_t *)ws);
+  g.expert_ptr = c->table;
+  // the routing, the plan and the copies it needs, then the experts from their slots
+  TierPlanArgs p{};
+  p.idx = g.idx;
+  p.S = S;
+  p.E = L->n_experts;
+  p.layer = layer;
+  p.n_slots = c->n_slots;
+  p.stride = c->stride;
+  p.slots = c->slots;
+  p.table = c->table;
+  p.key = c->key;
+  p.last = c->last;
+  p.hdr = c->hdr;
+  p.jobs = c->jobs;
+  if (launch_group_route(g, s) != hipSuccess || launch_tier_plan(p, s) != hipSuccess ||
+      launch_tier_copy(c->hdr, c->jobs, (const uint8_t *)bank, c->slots, c->stride, s) != hipSuccess)
+    return FMOE_ERR_LAUNCH;
   return launch_group_experts(g, s) == hipSuccess ? FMOE_OK : FMOE_ERR_LAUNCH;
 }
 

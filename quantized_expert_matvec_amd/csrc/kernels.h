@@ -115,6 +115,35 @@ hipError_t launch_read_xor(const void *buf, size_t bytes, uint32_t *out, hipStre
 // scratch.hip), looked up once per device.
 hipError_t scratch_device_ptr(void **out);
 
+// The host-memory expert tier's cache state in device memory, for the policy run
+// on the GPU (tier_kernels.hip): per slot the (layer, expert) key it holds (-1:
+// empty) and its last-use clock; the counters; the copies the current call needs.
+struct TierHdr {
+  uint64_t clock, call;
+  int64_t lookups, hits, misses, bytes;
+  int32_t njobs, pad;
+};
+struct TierPlanArgs {
+  const int32_t *idx;      // [S] the call's routing (expert of each slot)
+  int S, E, layer, n_slots;
+  size_t stride;           // bytes per expert blob
+  uint8_t *slots;          // n_slots blobs
+  const uint8_t **table;   // [E] blob address of each chosen expert (written)
+  int64_t *key;            // [n_slots]
+  uint64_t *last;          // [n_slots]
+  TierHdr *hdr;
+  int32_t *jobs;           // [2 * kMaxExperts]: (slot, expert) of each miss, in the call's order
+};
+// The state of an empty cache: every key -1, the header zero.
+hipError_t launch_tier_init(TierHdr *hdr, int64_t *key, int n_slots, hipStream_t s);
+// One workgroup: the least-recently-used plan of one call (the rules of the host
+// policy, expert_cache.h), the table of the chosen experts' blobs and the copy jobs.
+hipError_t launch_tier_plan(const TierPlanArgs &a, hipStream_t s);
+// The copies the plan asked for, read straight from the pinned host bank
+// (host_bank: its device-visible address).
+hipError_t launch_tier_copy(const TierHdr *hdr, const int32_t *jobs, const uint8_t *host_bank, uint8_t *slots,
+                            size_t stride, hipStream_t s);
+
 // Device packer: record r of the matrix goes to blob + rec_offset + r * rec_stride.
 hipError_t launch_pack_matrix(int bits, int rows, int cols, const uint8_t *codes, const uint16_t *scale,
                               const uint16_t *bias, uint8_t *blob, size_t rec_stride, size_t rec_offset,

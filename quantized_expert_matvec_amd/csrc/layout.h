@@ -21,6 +21,7 @@ constexpr int kBlock = 256;  // threads per block everywhere: 4 wavefronts
 constexpr int kMaxTopK = 16;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTokens = 256;
+constexpr int kMaxTierSlots = 65536;  // slots of a cache whose policy runs on the GPU
 constexpr int kDigStride = 52;  // u32 words per 64-column group of x in digit form
 constexpr size_t kScratchBytes = (size_t)4 << 20;  // static workspace of fmoe_moe_layer_noalloc (per GPU)
 

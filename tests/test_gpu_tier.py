@@ -30,11 +30,11 @@ def tiered_layer(seed, layer, bits, n_exp, k, hidden, inter, dev):
     return qem.Layer(R, g, host_bank, sh, n_exp, k, hidden, inter, bits)
 
 
-def run_and_check(device, cache, layer_id, L, OL, X, what):
+def run_and_check(device, cache, layer_id, L, OL, X, what, fn=qem.fmoe_moe_layer_tiered):
     B = X.shape[0]
     idx = torch.full((B, OL.k), -1, dtype=torch.int32, device=device)
     w = torch.zeros((B, OL.k), dtype=torch.float32, device=device)
-    out = qem.fmoe_moe_layer_tiered(cache, layer_id, L, to_dev(X, device), to_dev(X, device), topk_idx=idx, topk_w=w)
+    out = fn(cache, layer_id, L, to_dev(X, device), to_dev(X, device), topk_idx=idx, topk_w=w)
     torch.cuda.synchronize()
     got, gi, gw = out.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
     for t in range(B):
@@ -108,3 +108,103 @@ def test_tiered_too_many_experts_for_the_slots(device):
     assert ei.value.status == 7
     torch.cuda.synchronize()
     cache.close()
+
+
+# --------------------------------------------------------------------------- the policy on the GPU
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_tiered_device_equals_host_policy(device, bits):
+    """The same calls through two caches, one planned on the host and one on the GPU (no
+    host synchronisation): every output and routing equal bit for bit, the counters equal
+    after every call, and the device-planned outputs against the oracle."""
+    hidden, inter, n_exp, k, n_slots = 1024, 512, 32, 4, 10
+    print(f"tiered device policy q{bits}", flush=True)
+    layers = [tiered_layer(81, l, bits, n_exp, k, hidden, inter, device) for l in range(2)]
+    OLs = [OracleLayer(81, l, bits, n_exp, k, hidden, inter) for l in range(2)]
+    host = qem.ExpertCache(bits, hidden, inter, n_exp, n_slots, device)
+    dev = qem.ExpertCache(bits, hidden, inter, n_exp, n_slots, device)
+    calls = [(0, 1, 0), (0, 1, 0), (1, 1, 1), (0, 2, 2), (1, 2, 3), (1, 1, 4), (0, 1, 2), (0, 1, 5), (1, 2, 6)]
+    for c, (layer_id, B, xi) in enumerate(calls):
+        X = to_dev(synth.activations(81, synth.T_X, xi, B, hidden), device)
+        ih = torch.full((B, k), -1, dtype=torch.int32, device=device)
+        idv = torch.full((B, k), -1, dtype=torch.int32, device=device)
+        oh = qem.fmoe_moe_layer_tiered(host, layer_id, layers[layer_id], X, X, topk_idx=ih)
+        od = qem.fmoe_moe_layer_tiered_device(dev, layer_id, layers[layer_id], X, X, topk_idx=idv)
+        torch.cuda.synchronize()
+        assert torch.equal(ih, idv) and torch.equal(oh, od), c
+        assert host.stats() == dev.stats(), (c, host.stats(), dev.stats())
+    run_and_check(device, dev, 0, layers[0], OLs[0], synth.activations(81, synth.T_X, 7, 2, hidden),
+                  "device policy", fn=qem.fmoe_moe_layer_tiered_device)
+    # a cache is driven by one policy
+    with pytest.raises(qem.FmoeError) as ei:
+        qem.fmoe_moe_layer_tiered(dev, 0, layers[0], X, X)
+    assert ei.value.status == 2
+    with pytest.raises(qem.FmoeError) as ei:
+        qem.fmoe_moe_layer_tiered_device(host, 0, layers[0], X, X)
+    assert ei.value.status == 2
+    torch.cuda.synchronize()
+    host.close()
+    dev.close()
+
+
+def test_tiered_device_full_size(device):
+    """The workload's layer (q4, 512 experts of 6.75 MiB in pinned host memory) through a
+    64-slot cache planned on the GPU: three tokens, then the first again (all hits), each
+    against the oracle."""
+    hidden, inter, n_exp, k, bits = 4096, 1024, 512, 4, 4
+    L = tiered_layer(synth.SEED, 40, bits, n_exp, k, hidden, inter, device)
+    OL = OracleLayer(synth.SEED, 40, bits, n_exp, k, hidden, inter)
+    cache = qem.ExpertCache(bits, hidden, inter, n_exp, 64, device)
+    X = synth.activations(synth.SEED, synth.T_X, 9100, 3, hidden)
+    fn = qem.fmoe_moe_layer_tiered_device
+    for t in range(3):
+        run_and_check(device, cache, 0, L, OL, X[t:t + 1], f"device policy, full size token {t}", fn=fn)
+    before = cache.stats()
+    run_and_check(device, cache, 0, L, OL, X[0:1], "device policy, full size token 0 again", fn=fn)
+    after = cache.stats()
+    assert after["misses"] == before["misses"] and after["hits"] == before["hits"] + k
+    assert after["bytes_copied"] == after["misses"] * qem.fmoe_expert_bytes(bits, hidden, inter)
+    cache.close()
+
+
+def test_tiered_device_graph_replays(device):
+    """Two tiered layers planned on the GPU, captured once in a HIP graph after an eager
+    first call, replayed on new tokens with eager work between the replays: every replay's
+    outputs and the counters equal those of the same calls made eagerly on a twin cache
+    (the cache's state lives on the device and carries over from replay to replay)."""
+    hidden, inter, n_exp, k, bits, n_slots = 1024, 256, 32, 4, 4, 8
+    layers = [tiered_layer(83, l, bits, n_exp, k, hidden, inter, device) for l in range(2)]
+    xs = [to_dev(synth.activations(83, synth.T_X, i, 1, hidden), device) for i in range(4)]
+    A = qem.ExpertCache(bits, hidden, inter, n_exp, n_slots, device)
+    T = qem.ExpertCache(bits, hidden, inter, n_exp, n_slots, device)
+    ws = [torch.empty(qem.fmoe_tiered_workspace_bytes(layers[0], 1), dtype=torch.uint8, device=device)
+          for _ in range(2)]
+    x_in = torch.empty_like(xs[0])
+    outs = [torch.empty_like(xs[0]) for _ in range(2)]
+    refs = [torch.empty_like(xs[0]) for _ in range(2)]
+
+    def calls(cache, x, o):
+        for l in range(2):
+            qem.fmoe_moe_layer_tiered_device(cache, l, layers[l], x, x, out=o[l], ws=ws[l])
+
+    x_in.copy_(xs[0])
+    calls(A, x_in, outs)  # eager: initialises A's state
+    calls(T, xs[0], refs)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls(A, x_in, outs)
+    for r in (1, 2, 1, 3):
+        for o in outs:
+            o.fill_(float("nan"))
+        x_in.copy_(xs[r])
+        g.replay()
+        torch.cuda.synchronize()
+        calls(T, xs[r], refs)
+        torch.cuda.synchronize()
+        for l in range(2):
+            assert torch.equal(outs[l], refs[l]), (r, l)
+        assert A.stats() == T.stats(), (r, A.stats(), T.stats())
+    del g
+    A.close()
+    T.close()
