@@ -79,6 +79,8 @@ def parse():
                         "sizes in expert slots ('pages' = the pages' page-cache share of the bank, 35 of 209 GB); "
                         "one JSON line each, plus one for a repeated token (every expert a hit)")
     p.add_argument("--tier-layers", type=int, default=8, help="layers whose routed banks sit in pinned host memory")
+    p.add_argument("--tier-policy", choices=["host", "device", "both"], default="both",
+                   help="where the host-memory tier's cache policy runs")
     p.add_argument("--timeline", action="store_true",
                    help="print device-clock stamps of a few layers' kernels inside the graph-captured stack "
                         "instead of timing")
@@ -177,19 +179,53 @@ def tier(a):
             h, h2 = h2, h
         torch.cuda.synchronize()
 
+    # the policy on the GPU: the layers' calls need no host synchronisation, so a step is
+    # captured once in a graph (after an eager step that initialises the cache's state)
+    # and replayed; a step copies its tokens into the graph's input first
+    hin = torch.empty_like(h)
+    hbuf = [torch.empty_like(h) for _ in range(2)]
+
+    def dev_calls(cache):
+        cur = hin
+        for l in range(n_layers):
+            qem.fmoe_rms_scale(cur, x)
+            nxt = hbuf[l & 1]
+            qem.fmoe_moe_layer_tiered_device(cache, l, layers[l], x, cur, out=nxt, ws=ws)
+            cur = nxt
+
+    graphs = {}
+
+    def step_dev(cache, h0):
+        hin.copy_(h0)
+        g = graphs.get(id(cache))
+        if g is None:
+            dev_calls(cache)  # eager (the first call of each layer initialises or warms)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                dev_calls(cache)
+            graphs[id(cache)] = g
+            hin.copy_(h0)
+        g.replay()
+        torch.cuda.synchronize()
+
     total_slots = n_layers * E
     sizes = []
     for t in a.tier_slots.split(","):
         t = t.strip()
         sizes.append(max(K * B, round(total_slots * 35 / 209)) if t == "pages" else int(t))
-    for n_slots, repeat in [(n, False) for n in sizes] + [(max(sizes), True)]:
+    policies = ["host", "device"] if a.tier_policy == "both" else [a.tier_policy]
+    for policy, n_slots, repeat in [(p, n, False) for p in policies for n in sizes] + \
+                                   [(p, max(sizes), True) for p in policies]:
         buf_bytes = qem.fmoe_cache_device_bytes(bits, H, I, E, n_slots)
         cache = qem.ExpertCache(bits, H, I, E, n_slots, dev)
+        run_step = step if policy == "host" else step_dev
         warm = a.warmup + (1 if repeat else int(np.ceil(2 * n_slots / (K * B * n_layers))))
-        log(f"bench: tier {n_slots} slots{' (repeated token)' if repeat else ''}: {warm} warm-up steps")
+        log(f"bench: tier ({policy} policy) {n_slots} slots{' (repeated token)' if repeat else ''}: "
+            f"{warm} warm-up steps")
         tok = 0
         for s in range(warm):
-            step(cache, tokens(0 if repeat else tok))
+            run_step(cache, tokens(0 if repeat else tok))
             tok += 1
         st0 = cache.stats()
         times = []
@@ -197,7 +233,7 @@ def tier(a):
             h0 = tokens(0 if repeat else tok)
             torch.cuda.synchronize()
             t1 = time.perf_counter()
-            step(cache, h0)
+            run_step(cache, h0)
             times.append(time.perf_counter() - t1)
             tok += 1
         st1 = cache.stats()
@@ -207,11 +243,13 @@ def tier(a):
         us_layer = float(np.sum(times) * 1e6 / (a.steps * n_layers))
         rec = {
             "metric": f"µs per MoE layer, routed experts in host memory behind an HBM cache "
-                      f"(top-{K} + shared, {bits}-bit, B={B})",
+                      f"(top-{K} + shared, {bits}-bit, B={B}, policy on the {policy})",
             "value": round(us_layer, 2), "unit": "us/layer", "higher_is_better": False,
             "steps": a.steps, "warmup": warm,
             "config": {"workload": f"moe_stack_q{bits}_B{B}_host_tier", "layers": n_layers, "batch": B,
                        "experts": E, "top_k": K, "hidden": H, "inter": I, "group": 64,
+                       "policy": "host (one read-back per layer)" if policy == "host"
+                       else "device (no host synchronisation; a step is one graph replay)",
                        "cache_slots": n_slots, "cache_share_of_bank": round(n_slots / total_slots, 4),
                        "cache_GB": round(buf_bytes / 1e9, 2), "host_bank_GB": round(n_layers * bank_bytes / 1e9, 2),
                        "tokens": "one token repeated" if repeat else "fresh synthetic tokens each step"},
@@ -224,6 +262,7 @@ def tier(a):
             "data": "synthetic (seeded; random-init weights of the workload's shapes)",
         }
         print(json.dumps(rec, ensure_ascii=False), flush=True)
+        graphs.pop(id(cache), None)
         cache.close()
         del cache
         torch.cuda.empty_cache()
