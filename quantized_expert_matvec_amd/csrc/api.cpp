@@ -122,52 +122,56 @@ GroupArgs group_args(const fmoe_layer *L, int B, const float *x, float rms_eps, 
 // trace: device-clock stamps of the layer's kernels (layout in fmoe.h), or null.
 // form >= 0 (one token): the dequant-form build of the layer kernels (launch_layer_form),
 // with x in fp32 in the workspace's d_shared region, which the one-token kernels leave unused.
+// The one-token kernels' arguments for token x of layer L (workspace ws laid out by
+// layer_ws for one token).
+LayerArgs one_token_args(const fmoe_layer *L, const float *x, float rms_eps, const float *residual, float *out,
+                         int32_t *topk_idx, float *topk_w, uint8_t *ws) {
+  const LayerWs w = layer_ws(1, L->n_experts, L->top_k, L->hidden, L->inter, false);
+  const int H = L->hidden, I = L->inter;
+  LayerArgs a{};
+  a.router = L->router;
+  a.shared_gate = L->shared_gate;
+  a.bank = (const uint8_t *)L->bank;
+  a.shared = (const uint8_t *)L->shared;
+  a.E = L->n_experts;
+  a.K = L->top_k;
+  a.H = H;
+  a.I = I;
+  a.bits = L->bits;
+  a.expert_stride = expert_bytes(L->bits, H, I);
+  a.gateup_bytes = gateup_bytes(L->bits, H, I);
+  a.x = x;
+  a.rms_eps = rms_eps;
+  a.residual = residual;
+  a.out = out;
+  a.topk_idx_out = topk_idx;
+  a.topk_w_out = topk_w;
+  a.logits = (float *)(ws + w.logits);
+  a.sigma = (float *)(ws + w.sigma);
+  a.ws_idx = (int32_t *)(ws + w.topk_idx);
+  a.ws_w = (float *)(ws + w.topk_w);
+  a.h_shared = (float *)(ws + w.h_shared);
+  a.h_routed = (float *)(ws + w.h_routed);
+  a.d_shared = (float *)(ws + w.d_shared);
+  a.xdig = (uint32_t *)(ws + w.xdig);
+  return a;
+}
+
 fmoe_status layer_enqueue(const fmoe_layer *L, int B, const float *x, float rms_eps, const float *residual,
                           float *out, int32_t *topk_idx, float *topk_w, uint8_t *ws, hipStream_t s,
                           int phases = 7, uint64_t *trace = nullptr, int form = -1) {
-  const LayerWs w = layer_ws(B, L->n_experts, L->top_k, L->hidden, L->inter, B > 1);
-  const int H = L->hidden, I = L->inter, E = L->n_experts, K = L->top_k;
   if (B > 1) {
     GroupArgs g = group_args(L, B, x, rms_eps, residual, out, topk_idx, topk_w, ws);
     g.trace = trace;
     return launch_group(g, s, phases) == hipSuccess ? FMOE_OK : FMOE_ERR_LAUNCH;
   }
-  for (int t = 0; t < B; ++t) {
-    LayerArgs a{};
-    a.router = L->router;
-    a.shared_gate = L->shared_gate;
-    a.bank = (const uint8_t *)L->bank;
-    a.shared = (const uint8_t *)L->shared;
-    a.E = E;
-    a.K = K;
-    a.H = H;
-    a.I = I;
-    a.bits = L->bits;
-    a.expert_stride = expert_bytes(L->bits, H, I);
-    a.gateup_bytes = gateup_bytes(L->bits, H, I);
-    a.x = x + (size_t)t * H;
-    a.rms_eps = rms_eps;
-    a.residual = residual + (size_t)t * H;
-    a.out = out + (size_t)t * H;
-    a.topk_idx_out = topk_idx ? topk_idx + (size_t)t * K : nullptr;
-    a.topk_w_out = topk_w ? topk_w + (size_t)t * K : nullptr;
-    a.logits = (float *)(ws + w.logits) + (size_t)t * logit_stride(E);
-    a.sigma = (float *)(ws + w.sigma) + t;
-    a.ws_idx = (int32_t *)(ws + w.topk_idx) + (size_t)t * K;
-    a.ws_w = (float *)(ws + w.topk_w) + (size_t)t * K;
-    a.h_shared = (float *)(ws + w.h_shared) + (size_t)t * I;
-    a.h_routed = (float *)(ws + w.h_routed) + (size_t)t * K * I;
-    a.d_shared = (float *)(ws + w.d_shared) + (size_t)t * H;
-    a.xdig = (uint32_t *)(ws + w.xdig);
-    a.trace = trace;
-    if (form >= 0) {
-      a.xs = (float *)(ws + w.d_shared) + (size_t)t * H;
-      if (launch_layer_form(a, form, s) != hipSuccess) return FMOE_ERR_LAUNCH;
-      continue;
-    }
-    if (launch_layer(a, s, phases) != hipSuccess) return FMOE_ERR_LAUNCH;
+  LayerArgs a = one_token_args(L, x, rms_eps, residual, out, topk_idx, topk_w, ws);
+  a.trace = trace;
+  if (form >= 0) {
+    a.xs = a.d_shared;  // (the workspace's d_shared region holds x in fp32 for the form builds)
+    return launch_layer_form(a, form, s) == hipSuccess ? FMOE_OK : FMOE_ERR_LAUNCH;
   }
-  return FMOE_OK;
+  return launch_layer(a, s, phases) == hipSuccess ? FMOE_OK : FMOE_ERR_LAUNCH;
 }
 
 }  // namespace
@@ -538,7 +542,9 @@ fmoe_status fmoe_cache_plan(fmoe_cache *c, int layer, const int32_t *experts, in
 
 size_t fmoe_tiered_workspace_bytes(const fmoe_layer *L, int n_tokens) {
   if (fmoe_workspace_bytes(L, n_tokens) == 0) return 0;
-  return layer_ws(n_tokens, L->n_experts, L->top_k, L->hidden, L->inter, true).total;
+  const size_t g = layer_ws(n_tokens, L->n_experts, L->top_k, L->hidden, L->inter, true).total;
+  // (one token: either kernels' workspace, for the two policies' calls)
+  return n_tokens == 1 ? std::max(g, layer_ws(1, L->n_experts, L->top_k, L->hidden, L->inter, false).total) : g;
 }
 
 }  // extern "C"
@@ -665,11 +671,7 @@ fmoe_status fmoe_moe_layer_tiered_device(fmoe_cache *c, int layer, const fmoe_la
     c->dev_init = true;
   }
   c->mode = 2;
-  GroupArgs g = group_args(L, n_tokens, x, -1.f, residual, out, topk_idx, topk_w, (uint8_t *)ws);
-  g.expert_ptr = c->table;
-  // the routing, the plan and the copies it needs, then the experts from their slots
   TierPlanArgs p{};
-  p.idx = g.idx;
   p.S = S;
   p.E = L->n_experts;
   p.layer = layer;
@@ -681,6 +683,23 @@ fmoe_status fmoe_moe_layer_tiered_device(fmoe_cache *c, int layer, const fmoe_la
   p.last = c->last;
   p.hdr = c->hdr;
   p.jobs = c->jobs;
+  if (n_tokens == 1) {
+    // one token: the one-token kernels, the routed experts through the table: the
+    // router, the top-K alone, the plan and its copies, then gate/up and down
+    LayerArgs a = one_token_args(L, x, -1.f, residual, out, topk_idx, topk_w, (uint8_t *)ws);
+    a.bank = c->slots;  // (read only where no routed expert is chosen yet: any valid blob)
+    a.expert_ptr = c->table;
+    p.idx = a.ws_idx;
+    if (launch_layer(a, s, 1) != hipSuccess || launch_route1(a.logits, a.E, a.K, a.ws_idx, a.ws_w, s) != hipSuccess ||
+        launch_tier_plan(p, s) != hipSuccess ||
+        launch_tier_copy(c->hdr, c->jobs, (const uint8_t *)bank, c->slots, c->stride, s) != hipSuccess)
+      return FMOE_ERR_LAUNCH;
+    return launch_layer_ptr(a, s, 6) == hipSuccess ? FMOE_OK : FMOE_ERR_LAUNCH;
+  }
+  GroupArgs g = group_args(L, n_tokens, x, -1.f, residual, out, topk_idx, topk_w, (uint8_t *)ws);
+  g.expert_ptr = c->table;
+  // the routing, the plan and the copies it needs, then the experts from their slots
+  p.idx = g.idx;
   if (launch_group_route(g, s) != hipSuccess || launch_tier_plan(p, s) != hipSuccess ||
       launch_tier_copy(c->hdr, c->jobs, (const uint8_t *)bank, c->slots, c->stride, s) != hipSuccess)
     return FMOE_ERR_LAUNCH;

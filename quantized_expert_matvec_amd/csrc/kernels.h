@@ -43,6 +43,9 @@ struct LayerArgs {
   // optional per-workgroup timestamps (device, 100 MHz clock) for profiling:
   // [phase][kTraceBlocks workgroups][kTraceSlots]; null in normal use
   uint64_t *trace;
+  // launch_layer_ptr: routed expert e's blob at expert_ptr[e] (device array [E]; entries
+  // needed only for the chosen experts); bank then only needs one readable blob
+  const uint8_t *const *expert_ptr;
 };
 constexpr int kTraceSlots = 8;
 constexpr int kTraceBlocks = 4096;  // workgroups recorded per phase
@@ -101,6 +104,10 @@ hipError_t launch_group_experts(const GroupArgs &a, hipStream_t s);
 // down + weighted combine + residual. Three launches, no host synchronisation.
 // phases: bit p set = enqueue kernel p+1 (7 = the whole layer).
 hipError_t launch_layer(const LayerArgs &a, hipStream_t s, int phases = 7);
+// Phases 2 and 3 (or any of the three) with the routed experts through a.expert_ptr.
+hipError_t launch_layer_ptr(const LayerArgs &a, hipStream_t s, int phases);
+// One token's top-K from the router kernel's logits into idx / w (K entries each).
+hipError_t launch_route1(const float *logits, int E, int K, int32_t *idx, float *w, hipStream_t s);
 // The same layer (one token, hidden 4096, inter 1024, top_k <= 4, n_experts <= 512) with
 // the per-weight arithmetic of its gate/up and down projections in dequant form `form`
 // (forms.h); a.xs must hold H floats of workspace.

@@ -21,6 +21,13 @@ extern template hipError_t gateup_b<2>(const uint8_t *, int, int, const float *,
 extern template hipError_t layer_b<4>(const LayerArgs &, hipStream_t, int);
 extern template hipError_t layer_b<2>(const LayerArgs &, hipStream_t, int);
 template <int BITS>
+hipError_t layer_ptr_b(const LayerArgs &, hipStream_t, int);
+extern template hipError_t layer_ptr_b<4>(const LayerArgs &, hipStream_t, int);
+extern template hipError_t layer_ptr_b<2>(const LayerArgs &, hipStream_t, int);
+template <int BITS>
+hipError_t route1_b(const float *, int, int, int32_t *, float *, hipStream_t);
+extern template hipError_t route1_b<4>(const float *, int, int, int32_t *, float *, hipStream_t);
+template <int BITS>
 hipError_t group_b(const GroupArgs &, hipStream_t, int);
 extern template hipError_t group_b<4>(const GroupArgs &, hipStream_t, int);
 extern template hipError_t group_b<2>(const GroupArgs &, hipStream_t, int);
@@ -171,6 +178,14 @@ hipError_t launch_read_xor(const void *buf, size_t bytes, uint32_t *out, hipStre
 
 hipError_t launch_layer(const LayerArgs &a, hipStream_t s, int phases) {
   return a.bits == 4 ? dev::layer_b<4>(a, s, phases) : dev::layer_b<2>(a, s, phases);
+}
+
+hipError_t launch_layer_ptr(const LayerArgs &a, hipStream_t s, int phases) {
+  return a.bits == 4 ? dev::layer_ptr_b<4>(a, s, phases) : dev::layer_ptr_b<2>(a, s, phases);
+}
+
+hipError_t launch_route1(const float *logits, int E, int K, int32_t *idx, float *w, hipStream_t s) {
+  return dev::route1_b<4>(logits, E, K, idx, w, s);
 }
 
 hipError_t launch_group(const GroupArgs &a, hipStream_t s, int phases) {

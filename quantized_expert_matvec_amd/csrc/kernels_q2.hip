@@ -7,6 +7,7 @@ namespace dev {
 template hipError_t qmatvec_b<2>(const uint8_t *, int, int, const float *, float *, hipStream_t);
 template hipError_t gateup_b<2>(const uint8_t *, int, int, const float *, float *, hipStream_t);
 template hipError_t layer_b<2>(const LayerArgs &, hipStream_t, int);
+template hipError_t layer_ptr_b<2>(const LayerArgs &, hipStream_t, int);
 template hipError_t group_b<2>(const GroupArgs &, hipStream_t, int);
 template hipError_t group_route_b<2>(const GroupArgs &, hipStream_t);
 template hipError_t group_experts_b<2>(const GroupArgs &, hipStream_t);

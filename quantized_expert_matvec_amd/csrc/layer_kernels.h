@@ -855,6 +855,7 @@ struct Phase2Args {
   float *h_shared;
   const float *xs;           // the form variants (FORM >= 0): x in fp32 [hidden] instead of xdig
   uint64_t *trace;
+  const uint8_t *const *expert_ptr;  // PTR builds: expert e's blob at expert_ptr[e] (the tier's table)
 };
 
 // Phase 2. Routed blocks stage the logits and x (in digit form), derive the
@@ -866,8 +867,15 @@ struct Phase2Args {
 // wavefront (gateup_iters(top_k)). FORM >= 0 (comparison builds): x in fp32
 // (a.xs) and the per-weight arithmetic of partial_form<FORM> instead of the digit
 // form's integer dot products.
-template <int BITS, int NGHP, int GI, int FORM = -1>
+template <int BITS, int NGHP, int GI, int FORM = -1, bool PTR = false>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void k_phase2(const Phase2Args a) {
+  // the blob of routed expert e: in the bank, or (PTR) where the table says
+  auto blob = [&](int e) -> const uint8_t * {
+    if constexpr (PTR)
+      return a.expert_ptr[e];
+    else
+      return a.bank + (size_t)e * a.stride;
+  };
   constexpr int RPIH = kWave / NGHP;
   constexpr bool DIG = FORM < 0;
   constexpr int D4 = DIG ? (NGHP * kDigStride / 4 + kBlock - 1) / kBlock : (NGHP * 16 + kBlock - 1) / kBlock;
@@ -948,7 +956,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       // unconditional, so that the staging's wait counts the x loads only (every
       // routed wavefront is active: waves_per_slot * K is a whole number of
       // workgroups, and each wavefront's pairs lie inside its expert)
-      P.issue(a.bank + (size_t)sidx[slot] * a.stride, a.ng, pair0);
+      P.issue(blob(sidx[slot]), a.ng, pair0);
       x_store(xst);
       __syncthreads();
       trace_mark(a.trace, 1);
@@ -961,7 +969,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       trace_mark(a.trace, 1);
       block_topk(lg, a.E, bslot + 1, tks, sidx, sw);
       trace_mark(a.trace, 2);
-      if (active) P.issue(a.bank + (size_t)sidx[slot] * a.stride, a.ng, pair0);
+      if (active) P.issue(blob(sidx[slot]), a.ng, pair0);
     }
     if (wv == (a.K - 1) * a.waves_per_slot && lane < a.K) {
       const int sel = sidx[lane];
@@ -1073,6 +1081,7 @@ struct Phase3Args {
   const float *residual;
   float *out;
   uint64_t *trace;
+  const uint8_t *const *expert_ptr;  // PTR builds: expert e's blob at expert_ptr[e] (the tier's table)
 };
 
 // Phase 3: out_i = residual_i + sum_k w_k (down_k . h_k)_i + sigma (down_s . h_s)_i.
@@ -1087,7 +1096,7 @@ struct Phase3Args {
 // combining lanes through LDS.
 // FORM >= 0 (comparison builds, at most four slots): the per-weight arithmetic of
 // partial_form<FORM> instead of group_partial.
-template <int BITS, int NGIP, int KPAD, int FORM = -1>
+template <int BITS, int NGIP, int KPAD, int FORM = -1, bool PTR = false>
 __global__ __launch_bounds__(kP3Block) void k_phase3(const Phase3Args a) {
   constexpr int kP3Iters = down_iters(KPAD);
   constexpr int SLOTS = KPAD * NGIP;
@@ -1171,7 +1180,10 @@ __global__ __launch_bounds__(kP3Block) void k_phase3(const Phase3Args a) {
 #pragma unroll
   for (int m = 0; m < SPL; ++m) {
     asm volatile("" : "+v"(sel[m]));  // (keeps the address arithmetic, and its wait, here)
-    base[m] = a.bank + (size_t)sel[m] * a.stride + a.gu_bytes;
+    if constexpr (PTR)
+      base[m] = a.expert_ptr[sel[m]] + a.gu_bytes;
+    else
+      base[m] = a.bank + (size_t)sel[m] * a.stride + a.gu_bytes;
   }
   Chunk<BITS> c[kP3Iters][SPL];
   uint32_t sb[kP3Iters][SPL];
@@ -1316,7 +1328,7 @@ struct Dispatch {
     return hipGetLastError();
   }
 
-  template <int NGH, int NGI, int KPAD, int FORM = -1>
+  template <int NGH, int NGI, int KPAD, int FORM = -1, bool PTR = false>
   static hipError_t phase3(const LayerArgs &L, const LayerGeom<BITS, NGH, NGI> &G, hipStream_t s) {
     Phase3Args p3{};
     p3.bank = L.bank;
@@ -1334,7 +1346,8 @@ struct Dispatch {
     p3.residual = L.residual;
     p3.out = L.out;
     p3.trace = L.trace ? L.trace + (size_t)2 * kTraceBlocks * kTraceSlots : nullptr;
-    hipLaunchKernelGGL((k_phase3<BITS, NGI, KPAD, FORM>), dim3(G.n3), dim3(kP3Block), 0, s, p3);
+    p3.expert_ptr = L.expert_ptr;
+    hipLaunchKernelGGL((k_phase3<BITS, NGI, KPAD, FORM, PTR>), dim3(G.n3), dim3(kP3Block), 0, s, p3);
     return hipGetLastError();
   }
 
@@ -1361,7 +1374,7 @@ struct Dispatch {
     return hipGetLastError();
   }
 
-  template <int NGH, int NGI, int FORM = -1>
+  template <int NGH, int NGI, int FORM = -1, bool PTR = false>
   static hipError_t phase2(const LayerArgs &L, const LayerGeom<BITS, NGH, NGI> &G, hipStream_t s) {
     const bool has_shared = L.shared != nullptr;
     Phase2Args p2{};
@@ -1384,44 +1397,46 @@ struct Dispatch {
     p2.h_shared = L.h_shared;
     p2.xs = L.xs;
     p2.trace = L.trace ? L.trace + (size_t)kTraceBlocks * kTraceSlots : nullptr;
+    p2.expert_ptr = L.expert_ptr;
     static_assert(gateup_iters(4) == 2 && gateup_iters(5) == 4, "the builds below");
     const dim3 grid(G.n2r + G.n2s);
     if (L.K <= 4)
-      hipLaunchKernelGGL((k_phase2<BITS, NGH, 2, FORM>), grid, dim3(kBlock), 0, s, p2);
+      hipLaunchKernelGGL((k_phase2<BITS, NGH, 2, FORM, PTR>), grid, dim3(kBlock), 0, s, p2);
     else if constexpr (FORM < 0)
-      hipLaunchKernelGGL((k_phase2<BITS, NGH, 4>), grid, dim3(kBlock), 0, s, p2);
+      hipLaunchKernelGGL((k_phase2<BITS, NGH, 4, -1, PTR>), grid, dim3(kBlock), 0, s, p2);
     else
       return hipErrorInvalidValue;  // (the form builds take at most four slots)
     return hipGetLastError();
   }
 
-  template <int NGH, int NGI>
+  template <int NGH, int NGI, bool PTR = false>
   static hipError_t phase3k(const LayerArgs &L, const LayerGeom<BITS, NGH, NGI> &G, hipStream_t s) {
-    if (L.K <= 1) return phase3<NGH, NGI, 1>(L, G, s);
-    if (L.K <= 2) return phase3<NGH, NGI, 2>(L, G, s);
-    if (L.K <= 4) return phase3<NGH, NGI, 4>(L, G, s);
-    if (L.K <= 8) return phase3<NGH, NGI, 8>(L, G, s);
-    return phase3<NGH, NGI, 16>(L, G, s);
+    if (L.K <= 1) return phase3<NGH, NGI, 1, -1, PTR>(L, G, s);
+    if (L.K <= 2) return phase3<NGH, NGI, 2, -1, PTR>(L, G, s);
+    if (L.K <= 4) return phase3<NGH, NGI, 4, -1, PTR>(L, G, s);
+    if (L.K <= 8) return phase3<NGH, NGI, 8, -1, PTR>(L, G, s);
+    return phase3<NGH, NGI, 16, -1, PTR>(L, G, s);
   }
 
-  template <int NGH, int NGI>
+  // PTR: the routed experts' blobs through L.expert_ptr (the tier's table)
+  template <int NGH, int NGI, bool PTR = false>
   static hipError_t layer(const LayerArgs &L, hipStream_t s, int phases) {
     const LayerGeom<BITS, NGH, NGI> G(L, BITS);
     hipError_t err = hipSuccess;
     if (phases & 1) err = phase1<NGH, NGI>(L, G, s);
-    if (err == hipSuccess && (phases & 2)) err = phase2<NGH, NGI>(L, G, s);
-    if (err == hipSuccess && (phases & 4)) err = phase3k<NGH, NGI>(L, G, s);
+    if (err == hipSuccess && (phases & 2)) err = phase2<NGH, NGI, -1, PTR>(L, G, s);
+    if (err == hipSuccess && (phases & 4)) err = phase3k<NGH, NGI, PTR>(L, G, s);
     return err;
   }
 
-  template <int NGH>
+  template <int NGH, bool PTR = false>
   static hipError_t layer_h(const LayerArgs &L, hipStream_t s, int phases) {
     switch (pad_groups(L.I / kGroup)) {
-      case 4: return layer<NGH, 4>(L, s, phases);
-      case 8: return layer<NGH, 8>(L, s, phases);
-      case 16: return layer<NGH, 16>(L, s, phases);
-      case 32: return layer<NGH, 32>(L, s, phases);
-      case 64: return layer<NGH, 64>(L, s, phases);
+      case 4: return layer<NGH, 4, PTR>(L, s, phases);
+      case 8: return layer<NGH, 8, PTR>(L, s, phases);
+      case 16: return layer<NGH, 16, PTR>(L, s, phases);
+      case 32: return layer<NGH, 32, PTR>(L, s, phases);
+      case 64: return layer<NGH, 64, PTR>(L, s, phases);
       default: return hipErrorInvalidValue;
     }
   }
@@ -1440,6 +1455,39 @@ hipError_t gateup_b(const uint8_t *gu, int hidden, int inter, const float *x, fl
 template <int BITS>
 hipError_t layer_b(const LayerArgs &L, hipStream_t s, int phases) {
   FMOE_NG_SWITCH(pad_groups(L.H / kGroup), Dispatch<BITS>::template layer_h, L, s, phases)
+}
+
+// The layer's kernels with the routed experts' blobs through L.expert_ptr.
+template <int BITS>
+hipError_t layer_ptr_b(const LayerArgs &L, hipStream_t s, int phases) {
+  switch (pad_groups(L.H / kGroup)) {
+    case 4: return Dispatch<BITS>::template layer_h<4, true>(L, s, phases);
+    case 8: return Dispatch<BITS>::template layer_h<8, true>(L, s, phases);
+    case 16: return Dispatch<BITS>::template layer_h<16, true>(L, s, phases);
+    case 32: return Dispatch<BITS>::template layer_h<32, true>(L, s, phases);
+    case 64: return Dispatch<BITS>::template layer_h<64, true>(L, s, phases);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// One token's routing alone (its top-K from the router kernel's logits, which carry
+// the RMS factor already): ws_idx / ws_w, as the gate/up kernel derives them.
+template <int BITS>
+__global__ __launch_bounds__(kWave) void k_route1(const float *logits, int E, int K, int32_t *idx, float *w) {
+  __shared__ TopkLds tk;
+  int mi;
+  float mw;
+  wave_topk_lds(logits, E, K, 1.f, tk, mi, mw);
+  if (lane_id() < K) {
+    idx[lane_id()] = mi;
+    w[lane_id()] = mw;
+  }
+}
+
+template <int BITS>
+hipError_t route1_b(const float *logits, int E, int K, int32_t *idx, float *w, hipStream_t s) {
+  hipLaunchKernelGGL(k_route1<BITS>, dim3(1), dim3(kWave), 0, s, logits, E, K, idx, w);
+  return hipGetLastError();
 }
 
 }  // namespace dev

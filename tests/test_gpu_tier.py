@@ -115,8 +115,10 @@ def test_tiered_too_many_experts_for_the_slots(device):
 @pytest.mark.parametrize("bits", [4, 2])
 def test_tiered_device_equals_host_policy(device, bits):
     """The same calls through two caches, one planned on the host and one on the GPU (no
-    host synchronisation): every output and routing equal bit for bit, the counters equal
-    after every call, and the device-planned outputs against the oracle."""
+    host synchronisation): the routing equal, the outputs equal bit for bit for batches
+    (the same grouped kernels) and to rounding for one token (the device-planned call
+    takes the one-token kernels), the counters equal after every call, and the
+    device-planned outputs against the oracle."""
     hidden, inter, n_exp, k, n_slots = 1024, 512, 32, 4, 10
     print(f"tiered device policy q{bits}", flush=True)
     layers = [tiered_layer(81, l, bits, n_exp, k, hidden, inter, device) for l in range(2)]
@@ -131,10 +133,16 @@ def test_tiered_device_equals_host_policy(device, bits):
         oh = qem.fmoe_moe_layer_tiered(host, layer_id, layers[layer_id], X, X, topk_idx=ih)
         od = qem.fmoe_moe_layer_tiered_device(dev, layer_id, layers[layer_id], X, X, topk_idx=idv)
         torch.cuda.synchronize()
-        assert torch.equal(ih, idv) and torch.equal(oh, od), c
+        assert torch.equal(ih, idv), c
+        if B > 1:
+            assert torch.equal(oh, od), c
+        else:
+            a, b = oh.cpu().numpy().astype(np.float64), od.cpu().numpy().astype(np.float64)
+            assert np.abs(a - b).max() <= 1e-5 * np.abs(a).max(), c
         assert host.stats() == dev.stats(), (c, host.stats(), dev.stats())
-    run_and_check(device, dev, 0, layers[0], OLs[0], synth.activations(81, synth.T_X, 7, 2, hidden),
-                  "device policy", fn=qem.fmoe_moe_layer_tiered_device)
+    for B in (1, 2):
+        run_and_check(device, dev, 0, layers[0], OLs[0], synth.activations(81, synth.T_X, 7, B, hidden),
+                      f"device policy B={B}", fn=qem.fmoe_moe_layer_tiered_device)
     # a cache is driven by one policy
     with pytest.raises(qem.FmoeError) as ei:
         qem.fmoe_moe_layer_tiered(dev, 0, layers[0], X, X)
