@@ -669,6 +669,13 @@ __global__ __launch_bounds__(kBlock) void k_expert_gateup(const uint8_t *__restr
 // wavefront, whose workgroups each stage all of h for a quarter of the rows)
 __host__ __device__ constexpr int gateup_iters(int K) { return K <= 4 ? 2 : 4; }
 __host__ __device__ constexpr int down_iters(int kpad) { return kpad <= 4 ? 4 : 2; }
+// Slots per down lane group for top_k slots: top_k rounded up to a power of two, or
+// 12 for 9..12 slots when a row's lane groups then fill whole wavefronts (12 x the
+// inter groups a multiple of 64, at most 32 groups: inter 1024 or 2048), which spares
+// a quarter of the lanes' loads and arithmetic at top_k 10 against 16 slots.
+__host__ __device__ constexpr int down_slots(int K, int ngi_pad) {
+  return K <= 1 ? 1 : K <= 2 ? 2 : K <= 4 ? 4 : K <= 8 ? 8 : (K <= 12 && (ngi_pad == 16 || ngi_pad == 32)) ? 12 : 16;
+}
 constexpr int kP3Block = 256;      // threads per down + combine workgroup
 constexpr int kP3Waves = kP3Block / kWave;
 
@@ -1087,7 +1094,7 @@ struct Phase3Args {
 // Phase 3: out_i = residual_i + sum_k w_k (down_k . h_k)_i + sigma (down_s . h_s)_i.
 // Routed: lanes are (slot k, group j) pairs, so one cross-lane sum adds the K
 // experts' weighted partials of a row together; each lane keeps its slot's h
-// slice. KPAD = top_k rounded up to a power of two, NGIP = the inter groups ngi
+// slice. KPAD = down_slots(top_k, NGIP) (top_k rounded up to a power of two, or 12), NGIP = the inter groups ngi
 // rounded up to a power of two (lanes of slots past top_k or groups past ngi stay
 // idle). The routed h vectors are staged in LDS when they fit (KPAD * NGIP <=
 // 128), group j of slot k in row k ngi + j. Shared: the same wavefront's rows,
@@ -1289,8 +1296,7 @@ struct LayerGeom {
     wps = (L.I / RPIH + GI - 1) / GI;
     n2r = blocks_for((long)wps * L.K);
     n2s = sh ? blocks_for(wps) : 0;
-    kpad = 1;
-    while (kpad < L.K) kpad <<= 1;
+    kpad = down_slots(L.K, NGI);
     const int DI = down_iters(kpad);
     const int slots = kpad * NGI;
     const int seg = slots < kWave ? slots : kWave;
@@ -1415,6 +1421,9 @@ struct Dispatch {
     if (L.K <= 2) return phase3<NGH, NGI, 2, -1, PTR>(L, G, s);
     if (L.K <= 4) return phase3<NGH, NGI, 4, -1, PTR>(L, G, s);
     if (L.K <= 8) return phase3<NGH, NGI, 8, -1, PTR>(L, G, s);
+    if constexpr (down_slots(12, NGI) == 12) {
+      if (L.K <= 12) return phase3<NGH, NGI, 12, -1, PTR>(L, G, s);
+    }
     return phase3<NGH, NGI, 16, -1, PTR>(L, G, s);
   }
 

@@ -44,10 +44,10 @@ def _check(device, OL, L, X, RES, what):
 
 @pytest.mark.parametrize("bits", [4, 2])
 @pytest.mark.parametrize("hidden,inter,k", [(1024, 512, 9), (1024, 512, 10), (1024, 1024, 16), (2048, 256, 10),
-                                            (768, 2048, 12)])
+                                            (768, 2048, 12), (1024, 1024, 9), (512, 1024, 12), (1024, 2048, 10)])
 def test_wide_topk_small(device, bits, hidden, inter, k):
-    """top_k 9..16: the one-token kernels (16 slots per down lane group) token by token,
-    then the same tokens grouped (routed inside the gate/up kernel)."""
+    """top_k 9..16: the one-token kernels (12 or 16 slots per down lane group) token by
+    token, then the same tokens grouped (routed inside the gate/up kernel)."""
     n_exp = 48
     print(f"wide top-k q{bits} hidden={hidden} inter={inter} k={k}", flush=True)
     L = host_layer(71, 0, bits, n_exp, k, hidden, inter, device)
