@@ -505,11 +505,13 @@ __device__ __forceinline__ void router_tile(const GroupArgs &a, float (*part)[kR
     for (int u = 0; u < U; ++u) {
       if (st + u >= steps) break;  // (uniform)
       const float4 r0 = ra[u][0], r1 = ra[u][1], x0 = xa[u][0], x1 = xa[u][1];
-      const int nx = min(st + U + u, steps - 1);  // (past the end: the last step again, unused)
-      ra[u][0] = rp[8 * nx];
-      ra[u][1] = rp[8 * nx + 1];
-      xa[u][0] = xp[8 * nx];
-      xa[u][1] = xp[8 * nx + 1];
+      if (st + U < steps) {  // (uniform: no requests past the part's last step)
+        const int nx = min(st + U + u, steps - 1);  // (past the end: the last step again, unused)
+        ra[u][0] = rp[8 * nx];
+        ra[u][1] = rp[8 * nx + 1];
+        xa[u][0] = xp[8 * nx];
+        xa[u][1] = xp[8 * nx + 1];
+      }
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r0.x, x0.x, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r0.y, x0.y, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r0.z, x0.z, acc, 0, 0, 0);
