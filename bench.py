@@ -701,11 +701,13 @@ def versions(torch):
 
 
 def kernels_per_layer(B, K):
-    """Launches of one layer: 3 for one token; grouped, 4, or 6 with the routing kernels
-    (more than 8 tokens)."""
+    """Launches of one layer: 3 for one token; grouped, 4, plus the top-K kernel above 8
+    tokens (or 128 slots), plus the grouping kernel above 64 slots."""
     if B == 1:
         return 3
-    return 6 if B > 8 else 4
+    if B <= 8 and B * K <= 128:
+        return 4
+    return 5 if B * K <= 64 else 6
 
 
 def group_phase_bytes(phase, d_routed, eb, gub, E, H, I, K, B):

@@ -911,12 +911,11 @@ struct __attribute__((aligned(16))) RouteSmallLds {
 // kTokBlock. The slots are placed in rank order in LDS, and each
 // block-opening position writes its block, numbered by the block-opening
 // positions below it. Returns NB.
-__device__ __forceinline__ int route_small(const GroupArgs &a, RouteSmallLds &R, int *blk, bool writer) {
-  static_assert(kTokBlock * kMaxTopK <= kWave, "every batch of at most kTokBlock tokens: one slot per lane");
+// The grouping alone, from the slots' experts in R.sidx (S <= 64; written and
+// synchronised by the caller); the writer stores the table G. Returns NB.
+__device__ __forceinline__ int group_ranked(const GroupArgs &a, RouteSmallLds &R, int *blk, bool writer) {
   const int lane = lane_id();
   const int S = a.B * a.K;
-  route_topk(a, R.sidx, R.tk, writer);
-  __syncthreads();
   if (wave_in_block() == 0) {
     const bool live = lane < S;
     const int e = live ? R.sidx[lane] : kMaxExperts;
@@ -972,6 +971,21 @@ __device__ __forceinline__ int route_small(const GroupArgs &a, RouteSmallLds &R,
   }
   __syncthreads();
   return R.nb;
+}
+
+__device__ __forceinline__ int route_small(const GroupArgs &a, RouteSmallLds &R, int *blk, bool writer) {
+  static_assert(kTokBlock * kMaxTopK <= kWave, "every batch of at most kTokBlock tokens: one slot per lane");
+  route_topk(a, R.sidx, R.tk, writer);
+  __syncthreads();
+  return group_ranked(a, R, blk, writer);
+}
+
+// The grouping of at most 64 slots from the routing kernel's indices (a.idx).
+__device__ __forceinline__ int group_from_idx(const GroupArgs &a, RouteSmallLds &R, int *blk, bool writer) {
+  const int S = a.B * a.K;
+  if ((int)threadIdx.x < S) R.sidx[threadIdx.x] = a.idx[threadIdx.x];
+  __syncthreads();
+  return group_ranked(a, R, blk, writer);
 }
 
 // ------------------------------------------------------------------ routing kernels (large batches)
@@ -1126,7 +1140,7 @@ __global__ __launch_bounds__(kGThreads) void k_group(const GroupArgs a) {
 // the routing and the grouping table already (large batches); otherwise every
 // workgroup derives them itself when it meets its first routed item (route_small
 // for batches of at most kTokBlock tokens, block_route for the others).
-template <int BITS, int NGH, bool PRE, bool FULL, bool TABLE>
+template <int BITS, int NGH, bool PRE, bool FULL, bool TABLE, bool IDX = false>
 __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
   // (NGH: the hidden groups ng rounded up to a power of two; FULL: ng == NGH)
   const int ng = FULL ? NGH : a.H / kGroup, ngi = a.I / kGroup;
@@ -1164,6 +1178,7 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
   using MR = MfmaRows<BITS, NGH, 1, FULL>;
   constexpr bool pre = PRE;  // (launched for batches of at most kTokBlock tokens)
   static_assert(sizeof(RouteSmallLds) <= sizeof(wlds), "routing scratch of a small batch fits the chunk regions");
+  static_assert(sizeof(RouteSmallLds) <= sizeof(xl), "grouping scratch fits the staging buffer");
   if (pre && wv >= a.B) {  // (B <= kTokBlock < kGWaves: at least four such wavefronts)
     const int nst = (kGWaves - a.B) * kWave, st = (int)threadIdx.x - a.B * kWave;
     const int units = kParts * a.B * ng * 4;
@@ -1210,6 +1225,8 @@ __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
       if (NB < 0) {
         if constexpr (TABLE)
           NB = __builtin_amdgcn_readfirstlane(a.groups[1]);
+        else if constexpr (IDX)
+          NB = group_from_idx(a, *reinterpret_cast<RouteSmallLds *>(xl), blk, writer);
         else if constexpr (PRE)
           NB = route_small(a, *reinterpret_cast<RouteSmallLds *>(&wlds[0][0]), blk, writer);
         else
@@ -1467,13 +1484,22 @@ struct GroupDispatch {
       const dim3 grid(std::min((shb + S) * (a.I / kGroup), cu_count()));
       const bool full = a.H == NGH * kGroup;
       if (S > kRouteSlots || a.B > kRouteTokens) {
-        // large batches: the routing kernels first, then gate/up from the table
+        // large batches: the top-K kernel first; with at most 64 slots every gate/up
+        // workgroup groups them itself from the indices (one wavefront's ranking),
+        // else the grouping kernel writes the table first
         launch_topk(a, s);
-        hipLaunchKernelGGL(k_group<BITS>, dim3(1), dim3(kGThreads), 0, s, a);
-        if (full)
-          hipLaunchKernelGGL((k_g2<BITS, NGH, false, true, true>), grid, dim3(kGThreads), 0, s, a);
-        else
-          hipLaunchKernelGGL((k_g2<BITS, NGH, false, false, true>), grid, dim3(kGThreads), 0, s, a);
+        if (S <= kWave) {
+          if (full)
+            hipLaunchKernelGGL((k_g2<BITS, NGH, false, true, false, true>), grid, dim3(kGThreads), 0, s, a);
+          else
+            hipLaunchKernelGGL((k_g2<BITS, NGH, false, false, false, true>), grid, dim3(kGThreads), 0, s, a);
+        } else {
+          hipLaunchKernelGGL(k_group<BITS>, dim3(1), dim3(kGThreads), 0, s, a);
+          if (full)
+            hipLaunchKernelGGL((k_g2<BITS, NGH, false, true, true>), grid, dim3(kGThreads), 0, s, a);
+          else
+            hipLaunchKernelGGL((k_g2<BITS, NGH, false, false, true>), grid, dim3(kGThreads), 0, s, a);
+        }
       } else if (a.B <= kTokBlock && full) {
         hipLaunchKernelGGL((k_g2<BITS, NGH, true, true, false>), grid, dim3(kGThreads), 0, s, a);
       } else if (a.B <= kTokBlock) {
