@@ -323,8 +323,11 @@ fmoe_status fmoe_moe_layer_tiered(fmoe_cache *c, int layer, const fmoe_layer *L,
  * experts' slot addresses and the list of misses; a second kernel copies each
  * missing blob from L->bank, read directly over the bus (L->bank must be pinned host
  * memory the device can address: hipHostMalloc or a pinned torch tensor); then the
- * experts and the combine, as fmoe_moe_layer_tiered. For the same sequence of calls
- * the slots, counters and results equal the host policy's. A cache is driven by one
+ * experts and the combine, as fmoe_moe_layer_tiered for several tokens, and with the
+ * one-token kernels of fmoe_moe_layer for one token (the routed blobs read through the
+ * cache's table). For the same sequence of calls the slots, counters and routing equal
+ * the host policy's, the results too for several tokens (to rounding for one token,
+ * where the host-planned call takes the grouped kernels). A cache is driven by one
  * policy: FMOE_ERR_SHAPE if fmoe_cache_plan or fmoe_moe_layer_tiered used it before
  * (and they return FMOE_ERR_SHAPE on a cache this call used). The first such call on
  * a cache initialises its device state (every slot empty) on `stream` and must not be
