@@ -376,8 +376,8 @@ def timeline_grouped(np, rec, us, q):
     r = rec[2]
     print(f"  {names[2]:28s} {len(r):4d} wg  start {q(r[:, 0])}  end {q(r[:, 3])}", flush=True)
     gaps = [us(rec[k + 1][:, 0].min()) - us(rec[k][:, 3 if k == 0 else 7].max()) for k in range(2)]
-    print(f"  last end -> next kernel's first start: router -> gate/up {gaps[0]:.2f} (routing kernels "
-          f"between them above 8 tokens), gate/up -> down {gaps[1]:.2f}; first start -> last down end "
+    print(f"  last end -> next kernel's first start: router -> gate/up {gaps[0]:.2f} (the top-K "
+          f"kernel between them above 8 tokens, and the grouping kernel above 64 slots), gate/up -> down {gaps[1]:.2f}; first start -> last down end "
           f"{us(rec[2][:, 3].max()):.2f} (the combine follows)", flush=True)
 
 
