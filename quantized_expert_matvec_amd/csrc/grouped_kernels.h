@@ -62,6 +62,11 @@ constexpr int kRouteSlots = kRouteTokens * kMaxTopK;  // 128: every batch of at 
 // expert used by more tokens (the shared expert, mostly) gives several items,
 // which run on different compute units and re-read its rows (from the caches).
 constexpr int kTokBlock = 4;
+// Batches of up to kDownOneTile tokens run the down kernel with one 128-row tile per
+// workgroup (more, smaller workgroups: the last ones end sooner), larger ones with two
+// tiles per staging of h (60-layer q4 stack, one tile against two: 8 tokens 60.4 / 62.9
+// us per layer, 12 tokens 74.0 / 74.7, 16 tokens 84.3 / 84.4).
+constexpr int kDownOneTile = 16;
 constexpr int kParts = 3;       // signed 8-bit digit planes of a value's integer form
 constexpr int kGThreads = 512;  // workgroup of the matrix-core kernels: 8 wavefronts
 constexpr int kGWaves = kGThreads / kWave;
@@ -1522,9 +1527,9 @@ struct GroupDispatch {
     if (phases & 4) {
       const bool full = a.I == NGI * kGroup;
       const dim3 g1((shb + S) * (a.H / 128)), g2((shb + S) * (a.H / 256));
-      if (a.B <= kTokBlock && full)
+      if (a.B <= kDownOneTile && full)
         hipLaunchKernelGGL((k_g3<BITS, NGI, 1, true>), g1, dim3(kGThreads), 0, s, a);
-      else if (a.B <= kTokBlock)
+      else if (a.B <= kDownOneTile)
         hipLaunchKernelGGL((k_g3<BITS, NGI, 1, false>), g1, dim3(kGThreads), 0, s, a);
       else if (full)
         hipLaunchKernelGGL((k_g3<BITS, NGI, 2, true>), g2, dim3(kGThreads), 0, s, a);
