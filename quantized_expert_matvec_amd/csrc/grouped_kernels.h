@@ -22,7 +22,8 @@
 // are those of the X_j (at most 2^-22 of the group's largest magnitude) and of
 // the fp32 combination.
 //
-// Four launches:
+// Four launches (above 8 tokens, the top-K kernel, and above 64 slots the grouping
+// kernel, before g2):
 //   g1  router rows . x of every token (fp32 rows held in registers, VALU, the
 //       tokens' x through LDS), unscaled; other workgroups prepare each token's
 //       x for the matrix cores: RMS factor, per group the digit planes, the
@@ -34,7 +35,7 @@
 //       (top-K of every token, the distinct experts in ascending id and, for
 //       each, the ascending list of the slots (token t, choice k; slot = t*K + k)
 //       routed to it); the shared expert's workgroups need none and stream at once
-//   g3  down of (shared expert or distinct expert, 256 rows): per token
+//   g3  down of (shared expert or distinct expert, 128 or 256 rows): per token
 //       sigma * (D_s h) into d_shared, per slot w * (D h) into partial[slot]
 //   g4  out = residual + the K per-slot outputs in slot order + sigma * shared
 #pragma once
@@ -48,8 +49,10 @@ namespace fmoe {
 namespace dev {
 
 // Slots (token, choice) that the gate/up kernel's own routing handles (one thread
-// per slot): batches with more, or with more than kRouteTokens tokens, are routed
-// by the routing kernels before it (k_topk, k_group) and read the grouping table.
+// per slot): batches with more, or with more than kRouteTokens tokens, take their
+// top-Ks from the top-K kernel before it (k_topk); the gate/up workgroups then group
+// at most 64 slots themselves (group_from_idx), and read the table the grouping
+// kernel (k_group) writes for more.
 // Every gate/up workgroup that routes for itself reads all the batch's logits
 // (B x the router's slabs x 2 KB): from 16 tokens that traffic, and the top-Ks
 // of two tokens per wavefront, cost more than the two extra launches (same-build
@@ -1142,9 +1145,10 @@ __global__ __launch_bounds__(kGThreads) void k_group(const GroupArgs a) {
 // inter dimension) of one item's expert, for the item's tokens / slots.
 // Wavefront w holds rows 16w .. 16w + 15. h vectors: slot s at index s,
 // shared-expert token t at index S + t. TABLE: the routing kernels have written
-// the routing and the grouping table already (large batches); otherwise every
-// workgroup derives them itself when it meets its first routed item (route_small
-// for batches of at most kTokBlock tokens, block_route for the others).
+// the routing and the grouping table already (large batches); IDX: the top-K kernel
+// has written the routing and every workgroup groups the slots (at most 64) itself;
+// otherwise every workgroup derives both when it meets its first routed item
+// (route_small for batches of at most kTokBlock tokens, block_route for the others).
 template <int BITS, int NGH, bool PRE, bool FULL, bool TABLE, bool IDX = false>
 __global__ __launch_bounds__(kGThreads) void k_g2(const GroupArgs a) {
   // (NGH: the hidden groups ng rounded up to a power of two; FULL: ng == NGH)
